@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the wave-index hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input: build the index
+of the layer (segmented spherical k-means, finalise, permuted K/V) and run the workload's
+decode steps against it (score, select, exact + estimate, merge). Inputs are resident in HBM
+before timing starts. Between decode calls a 512 MiB buffer is written so that each call
+reads its data from HBM rather than from the 256 MB Infinity Cache; the decode figures come
+from HIP events around each call (the flush is outside them) and the per-kernel figures from
+events the library records between its kernels.
+
+Prints one JSON line. `value` is decode-attention tokens/s of the layer (batch / median time
+of one decode call); the index-build rate and achieved HBM bandwidth are extra fields.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama128k")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="decode calls per step (default: the workload's)")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-decode-steps", type=int, default=3)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): the wave index path here is single-GPU; see DESIGN.md for how it "
+              "would shard.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_vector_index_amd as wi
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wi.library()
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    nds = args.decode_steps or w.steps
+    w = w.with_(steps=nds)
+    B, H, Hq, G, d = w.batch, w.n_kv_heads, w.n_q_heads, w.group, 128
+    L0, C, nr, T = w.context, w.n_clusters, w.n_retrieve, w.n_iters
+    print(f"[bench] workload {w.name}: B={B} Hq={Hq} Hkv={H} L0={L0} S={w.segment_size} "
+          f"C={C} T={T} n_r={nr} decode steps={nds}", file=sys.stderr, flush=True)
+
+    t = time.time()
+    x = synth.generate_layer(w)
+    print(f"[bench] generated inputs in {time.time() - t:.1f}s", file=sys.stderr, flush=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    k, v = dev(x.k), dev(x.v)
+    q = dev(x.q)                                              # [steps, B, Hq, d]
+    k_out, v_out = torch.zeros_like(k), torch.zeros_like(v)
+    k_out[:, :, L0:] = k[:, :, L0:]                           # decode-appended rows
+    v_out[:, :, L0:] = v[:, :, L0:]
+    bp = wi.wave_build_params(B, Hq, H, d, L0, w.capacity, w.segment_size,
+                              w.clusters_per_segment, T, w.n_sink, w.n_recent)
+    bws = torch.empty(wi.wave_index_workspace_size(bp), dtype=torch.uint8, device="cuda")
+    idx = wi.alloc_index(B, H, C, L0, optional=False)
+    scale = 1.0 / math.sqrt(d)
+    dps = [wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
+                                 w.n_recent, nr, scale) for s in range(nds)]
+    dws = torch.empty(wi.wave_decode_workspace_size(dps[0]), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+    sel = torch.empty(nds, B, H, max(nr, 1), dtype=torch.int32, device="cuda")
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    n_build_ev = 3 * T + 4
+    def events(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in ev:
+            e.record()
+        return ev
+
+    def one_step(bev, dev_):
+        wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws,
+                            events=None if bev is None else [e.cuda_event for e in bev])
+        for s in range(nds):
+            if flush is not None:
+                flush.fill_(s & 255)
+            wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, out, lse, sel[s], dws,
+                                     events=None if dev_ is None else
+                                     [e.cuda_event for e in dev_[s]])
+
+    for _ in range(args.warmup):
+        one_step(None, None)
+    torch.cuda.synchronize()
+    bevs = [events(n_build_ev) for _ in range(args.steps)]
+    devs = [[events(4) for _ in range(nds)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(bevs[i], devs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---- per-kernel durations (ms) from the library's kernel-boundary events
+    el = lambda a, b: a.elapsed_time(b)  # noqa: E731
+    build_ms = [el(b[0], b[-1]) for b in bevs]
+    # build kernel order: norms, seeds, then per pass assign, sort, [update]; finalise, steady
+    assign_ms, sort_ms, update_ms = [], [], []
+    for b in bevs:
+        i = 2
+        for p in range(T):
+            assign_ms.append(el(b[i], b[i + 1]))
+            sort_ms.append(el(b[i + 1], b[i + 2]))
+            i += 2
+            if p < T - 1:
+                update_ms.append(el(b[i], b[i + 1]))
+                i += 1
+        fin_ms = el(b[i], b[i + 1])
+    call_ms = [el(e[0], e[3]) for st in devs for e in st]
+    stream_ms = [el(e[0], e[1]) for st in devs for e in st]
+    select_ms = [el(e[1], e[2]) for st in devs for e in st]
+    retr_ms = [el(e[2], e[3]) for st in devs for e in st]
+    med = statistics.median
+
+    # ---- algorithmic work (per decode call and per assignment launch)
+    csize = idx.cluster_size.cpu().numpy()
+    selh = sel.cpu().numpy()
+    e_tok = []
+    for s in range(nds):
+        steady = w.n_sink + w.n_recent + s + 1
+        tot = 0
+        for b in range(B):
+            for g in range(H):
+                ids = selh[s, b, g, :nr]
+                ids = ids[ids >= 0]
+                tot += steady + int(csize[b, g, ids].sum())
+        e_tok.append(tot / (B * H))
+    E = float(np.mean(e_tok))
+    per_bh = 2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d
+    call_bytes = per_bh * B * H
+    steady_tok = w.n_sink + w.n_recent + (nds + 1) / 2.0
+    stream_bytes = (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * steady_tok + 2 * G * d) * B * H
+    n_idx = [max(0, min((s + 1) * w.segment_size, L0 - w.n_recent) - max(s * w.segment_size,
+                                                                           w.n_sink))
+             for s in range(w.n_segments)]
+    assign_flop = sum(2.0 * n * w.clusters_per_segment * d for n in n_idx) * B * H
+
+    decode_tok_s = B / (med(call_ms) * 1e-3)
+    build_tok_s = B * L0 / (med(build_ms) * 1e-3)
+    call_gbs = call_bytes / (med(call_ms) * 1e-3) / 1e9
+    stream_gbs = stream_bytes / (med(stream_ms) * 1e-3) / 1e9
+    assign_tfs = assign_flop / (statistics.mean(assign_ms) * 1e-3) / 1e12
+    per_step = {"assign": T * statistics.mean(assign_ms),
+                "decode_stream": nds * statistics.mean(stream_ms),
+                "decode_select": nds * statistics.mean(select_ms),
+                "decode_retrieved": nds * statistics.mean(retr_ms)}
+    dominant = max(per_step, key=per_step.get)
+    roof_assign = {"kernel": "k_assign", "bound": "mfma", "achieved": round(assign_tfs, 2),
+                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                   "frac": round(assign_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                   "flop_per_launch": assign_flop,
+                   "avg_launch_us": round(statistics.mean(assign_ms) * 1e3, 2)}
+    roof_stream = {"kernel": "k_decode_stream", "bound": "hbm", "achieved": round(stream_gbs, 1),
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": round(stream_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                   "bytes_per_launch": stream_bytes,
+                   "avg_launch_us": round(med(stream_ms) * 1e3, 2)}
+    roof = roof_assign if dominant == "assign" else roof_stream
+
+    res = {
+        "metric": "decode attn tokens/s + achieved HBM GB/s at 128K/1M ctx; index-build tok/s",
+        "value": round(decode_tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded topic-structured RoPE keys, Gaussian values)",
+        "config": {"workload": w.name, "batch": B, "context": L0, "n_q_heads": Hq,
+                   "n_kv_heads": H, "head_dim": d, "segment_size": w.segment_size,
+                   "clusters": C, "iters": T, "steady": [w.n_sink, w.n_recent],
+                   "n_retrieve": nr, "decode_steps": nds, "cache_flush": flush is not None},
+        "decode_call_us": round(med(call_ms) * 1e3, 2),
+        "decode_hbm_GBps": round(call_gbs, 1),
+        "decode_hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4),
+        "decode_bytes_per_call": call_bytes,
+        "exact_tokens_per_kv_head": round(E, 1),
+        "index_build_tok_s": round(build_tok_s, 1),
+        "index_build_ms": round(med(build_ms), 3),
+        "kernel_us": {"assign": round(statistics.mean(assign_ms) * 1e3, 2),
+                      "sort": round(statistics.mean(sort_ms) * 1e3, 2),
+                      "update": round(statistics.mean(update_ms) * 1e3, 2) if update_ms else None,
+                      "finalise": round(fin_ms * 1e3, 2),
+                      "decode_stream": round(med(stream_ms) * 1e3, 2),
+                      "decode_select": round(med(select_ms) * 1e3, 2),
+                      "decode_retrieved": round(med(retr_ms) * 1e3, 2)},
+        "dominant_kernel": dominant,
+        "roofline": roof,
+        "roofline_assign": roof_assign,
+        "roofline_decode_stream": roof_stream,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_decode_steps)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, x, n_steps):
+    """The oracle, untuned, on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import wave_oracle as wo
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    print("[bench] cpu baseline: oracle build of one (head, segment)", file=sys.stderr,
+          flush=True)
+    g = 0
+    lo, hi = wo.segment_ranges(w.context, w.segment_size, w.n_sink, w.n_recent)[0]
+    K0 = wo.bf16_to_f64(x.k[0, g, lo:hi])
+    t = time.perf_counter()
+    wo.cluster_segment(K0, w.clusters_per_segment, w.n_iters)
+    t_seg = time.perf_counter() - t
+    build_tok_s = (hi - lo) / t_seg
+    # decode sample: one KV head, index built by the oracle with one pass (decode cost does
+    # not depend on the pass count), a few steps, scaled to all KV heads of the batch
+    print("[bench] cpu baseline: oracle decode sample", file=sys.stderr, flush=True)
+    hidx, ko, vo = wo.build_head(x.k[0, g], x.v[0, g], w.context, w.segment_size,
+                                 w.clusters_per_segment, 1, w.n_sink, w.n_recent)
+    kc = np.concatenate([ko, x.k[0, g, w.context:]])
+    vc = np.concatenate([vo, x.v[0, g, w.context:]])
+    G = w.group
+    t = time.perf_counter()
+    for s in range(n_steps):
+        wo.decode_group(x.q[s][0, g * G:(g + 1) * G], kc, vc, hidx, w.context,
+                        w.context + s + 1, w.n_sink, w.n_recent, w.n_retrieve)
+    t_head = (time.perf_counter() - t) / n_steps
+    step_s = t_head * w.n_kv_heads * w.batch
+    return {"value": round(1.0 / step_s, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"decode: {n_steps} steps of KV head 0 (index built by the oracle, 1 "
+                       f"pass), scaled x{w.n_kv_heads * w.batch} to all KV heads; build: one "
+                       f"{hi - lo}-token segment, {w.n_iters} passes"),
+            "index_build_tok_s": round(build_tok_s, 1)}
+
+
+if __name__ == "__main__":
+    main()

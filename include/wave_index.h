@@ -1,0 +1,199 @@
+/*
+ * wave_index.h -- C ABI of the MI355X (gfx950) wave-index library.
+ *
+ * The library implements the data-parallel hot path of RetroInfer's wave index
+ * ("Attention-aWare VEctor index"): building the index with segmented spherical k-means
+ * over each KV head's keys, and the per-step tripartite decode attention that combines
+ * exact attention over the steady and retrieval zones with a centroid estimate of the
+ * estimation zone.
+ *
+ * Sources (web summaries of the RetroInfer paper, arXiv 2505.02922):
+ *   - abstract (chatpaper.ai): wave index = tripartite attention approximation,
+ *     accuracy-bounded attention estimation, segmented clustering;
+ *   - gist.science/de, section 2A; gist.science/fr, section 2A; gist.science/zh,
+ *     section 2A: the three zones, centroids plus precomputed value sums for the
+ *     estimate with a Jensen lower bound, spherical k-means (fr), segment-local
+ *     clustering that exploits RoPE locality (zh);
+ *   - gist.science/zh section 3: a retrieval budget of about 1.8 % of the clusters.
+ *
+ * Conventions shared by every entry point
+ *   - Layout. bf16 tensors are IEEE bfloat16 (round to nearest even). K/V caches are
+ *     [B, Hkv, Lcap, d] row-major (one 2*d-byte row per token); query head h uses KV head
+ *     h / G with G = Hq / Hkv. Only d = 128 is supported.
+ *   - Ownership. The caller allocates and owns every buffer (device memory), including the
+ *     workspace, whose size the *_workspace_size functions report. The library allocates
+ *     no device memory and keeps no state between calls.
+ *   - Asynchrony. Compute entry points validate their arguments on the host, enqueue
+ *     kernels on `stream` and return; outputs are valid once the stream has reached them.
+ *     Calls that share a workspace must not overlap.
+ *   - Errors. Invalid arguments are reported before anything is enqueued; a failed kernel
+ *     launch returns WAVE_ERR_HIP. Nothing is written on error.
+ */
+#ifndef WAVE_INDEX_H
+#define WAVE_INDEX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WAVE_OK = 0,
+  WAVE_ERR_INVALID_ARG = 1,  /* a size, count or pointer is out of range or null */
+  WAVE_ERR_UNSUPPORTED = 2,  /* a valid shape this build does not implement (d != 128, G > 8) */
+  WAVE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the reported size */
+  WAVE_ERR_ALIAS = 4,        /* an output buffer overlaps an input buffer */
+  WAVE_ERR_HIP = 5           /* a HIP launch or runtime call failed */
+} wave_status;
+
+/* ------------------------------------------------------------------------------------
+ * Index build: segmented spherical k-means over the keys of each (batch element, KV head)
+ * ------------------------------------------------------------------------------------
+ * Positions [0, n_sink) and [seq_len - n_recent, seq_len) form the steady zone and are not
+ * clustered. The indexed positions of segment s are [s*S, (s+1)*S) intersected with
+ * [n_sink, seq_len - n_recent). Each segment has clusters_per_segment clusters (global id
+ * s * clusters_per_segment + j), so C = ceil(seq_len / S) * clusters_per_segment.
+ * Spherical k-means (gist.science/fr section 2A) per segment: unit keys x = k/||k||; seeds
+ * mu_j = bf16(x at local point j*floor(n_s/k_seg)) (first n_s points if n_s < k_seg; the
+ * remaining clusters stay empty); n_iters passes of "assign each point to the centroid of
+ * largest cosine (lowest id on ties), then mu_j = bf16(normalised sum of its unit points)"
+ * (an empty cluster keeps its centroid; the last pass is not followed by an update).
+ * From the final labels: size n_j, mean raw key bf16(sum k / n_j), value sum bf16(sum v)
+ * (gist.science/zh section 2A: centroids and precomputed value sums), and a segment-local
+ * permutation of K and V into cluster order (ascending cluster id, ascending position
+ * inside a cluster) so that every cluster's tokens are contiguous.
+ */
+typedef struct {
+  int32_t batch;                 /* B >= 1 */
+  int32_t n_q_heads;             /* Hq, a multiple of n_kv_heads (only checked, not used) */
+  int32_t n_kv_heads;            /* Hkv >= 1 */
+  int32_t head_dim;              /* d; must be 128 */
+  int64_t seq_len;               /* L0 >= 1: tokens indexed, rows [0, L0) of k and v */
+  int64_t kv_capacity;           /* Lcap >= L0: row stride (in tokens) of k, v, k_out, v_out */
+  int32_t segment_size;          /* S, 1..16384 */
+  int32_t clusters_per_segment;  /* k_seg, 1..min(S, 2048) */
+  int32_t n_iters;               /* T, 1..1000 assignment passes */
+  int32_t n_sink;                /* >= 0 */
+  int32_t n_recent;              /* >= 0, n_sink + n_recent <= L0 */
+} wave_build_params;
+
+/* The index of one layer. All arrays are device memory, indexed [B, Hkv, ...]. */
+typedef struct {
+  void* centroid_mean;     /* bf16 [B, Hkv, C, d]: mean raw key of each cluster (0 if empty) */
+  void* value_sum;         /* bf16 [B, Hkv, C, d]: sum of the cluster's value rows (0 if empty) */
+  int32_t* cluster_size;   /* [B, Hkv, C]: n_j */
+  int32_t* cluster_offset; /* [B, Hkv, C]: first row of cluster j in k_out / v_out */
+  int32_t* labels;         /* optional [B, Hkv, L0]: global cluster id per position, -1 steady */
+  int32_t* perm;           /* optional [B, Hkv, L0]: perm[row] = source position of k_out row */
+  void* last_centroids;    /* optional bf16 [B, Hkv, C, d]: unit centroids of the last pass */
+  float* objective;        /* optional [B, Hkv]: sum over clusters of ||sum of unit points|| */
+} wave_index;
+
+/* Bytes of workspace wave_index_build needs for these parameters (host only). */
+wave_status wave_index_workspace_size(const wave_build_params* p, size_t* bytes);
+
+/* Build the index of one layer.
+ *   k, v         bf16 [B, Hkv, Lcap, d] inputs; rows [0, L0) are read.
+ *   k_out, v_out bf16 [B, Hkv, Lcap, d] outputs: rows [0, L0) receive the permuted cache
+ *                (steady rows unchanged); rows [L0, Lcap) are not touched. They must not
+ *                overlap k or v (WAVE_ERR_ALIAS).
+ *   idx          output arrays (the optional ones may be NULL).
+ *   workspace    device memory of at least wave_index_workspace_size bytes (no clearing
+ *                needed). */
+wave_status wave_index_build(const wave_build_params* p, const void* k, const void* v,
+                             void* k_out, void* v_out, const wave_index* idx,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Tripartite decode attention (one step, one layer)
+ * ------------------------------------------------------------------------------------
+ * For every batch element b and query head h (KV head g = h / G), with scale = p->scale:
+ *   s_j = scale * q_h . centroid_mean_j for non-empty clusters, and the group score
+ *   s^_j = mean over the G heads of KV head g. The retrieval zone R is the n_retrieve
+ *   clusters of largest s^_j (ties to the lower id; all non-empty clusters if fewer).
+ *   Exact zone E = [0, n_sink) U [index_len - n_recent, seq_len) U the rows of R's clusters
+ *   (the steady zone of the summaries, section 2A, plus the tokens appended since the
+ *   build). Estimation zone U = the other non-empty clusters.
+ *   out_h = (sum_E e^{a_i} v_i + sum_U e^{s_j} V_j) / (sum_E e^{a_i} + sum_U n_j e^{s_j}),
+ *   a_i = scale * q_h . k_i, V_j = value_sum_j; lse_h = log of the denominator.
+ * Accumulation is fp32 over bf16 inputs.
+ */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;  /* head_dim must be 128; G <= 8 */
+  int64_t seq_len;       /* L: rows [0, L) of the cache are attended (L0 <= L <= Lcap) */
+  int64_t index_len;     /* L0: rows covered by the index */
+  int64_t kv_capacity;   /* Lcap: row stride of the caches */
+  int32_t n_clusters;    /* C >= 1 */
+  int32_t n_sink;        /* as in the build */
+  int32_t n_recent;      /* as in the build; the recent zone extends to L */
+  int32_t n_retrieve;    /* 0 <= n_r <= C: clusters attended exactly */
+  float scale;           /* > 0, usually 1/sqrt(d) */
+} wave_decode_params;
+
+/* Bytes of decode workspace for these parameters (host only). */
+wave_status wave_decode_workspace_size(const wave_decode_params* p, size_t* bytes);
+
+/* One decode step.
+ *   q          bf16 [B, Hq, d]
+ *   k_cache, v_cache  bf16 [B, Hkv, Lcap, d]: k_out / v_out of the build, with decode
+ *              tokens appended at rows [L0, L)
+ *   idx        the build's index (only the four required arrays are read)
+ *   out        fp32 [B, Hq, d]
+ *   lse        optional fp32 [B, Hq]
+ *   selected   optional int32 [B, Hkv, n_retrieve]: R in ascending id order, -1 padded
+ *   workspace  at least wave_decode_workspace_size bytes (no clearing needed; it only
+ *              depends on the shape, so one workspace serves every step up to Lcap). */
+wave_status wave_decode_attention(const wave_decode_params* p, const void* q,
+                                  const void* k_cache, const void* v_cache,
+                                  const wave_index* idx, float* out, float* lse,
+                                  int32_t* selected, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* Dense decode attention over all L rows (the "full attention" the summaries compare
+ * against, section 4). Same parameters; the index fields of p are ignored. */
+wave_status wave_dense_decode_attention(const wave_decode_params* p, const void* q,
+                                        const void* k_cache, const void* v_cache, float* out,
+                                        float* lse, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Tracing: kernel-boundary events
+ * ------------------------------------------------------------------------------------
+ * The *_traced variants behave exactly like their plain counterparts and additionally
+ * record caller-created HIP events on `stream`: events[i] right before the i-th kernel of
+ * the call is enqueued and one more after the last, so kernel i spans events[i] to
+ * events[i + 1]. At most `capacity` events are recorded; `recorded` returns the count.
+ * Kernel order, build: key norms (if any indexed token), seeds, then per pass: assign,
+ * sort, and (all passes but the last) update; then finalise, steady-row copy (if
+ * n_sink + n_recent > 0), objective (if requested). Decode: stream, select, retrieved.
+ */
+typedef struct {
+  hipEvent_t* events;   /* capacity events created by the caller (hipEventCreate) */
+  int32_t capacity;
+  int32_t recorded;     /* out */
+} wave_trace;
+
+wave_status wave_index_build_traced(const wave_build_params* p, const void* k, const void* v,
+                                    void* k_out, void* v_out, const wave_index* idx,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    wave_trace* trace);
+
+wave_status wave_decode_attention_traced(const wave_decode_params* p, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const wave_index* idx, float* out, float* lse,
+                                         int32_t* selected, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream,
+                                         wave_trace* trace);
+
+/* Static, human-readable name of a status code. */
+const char* wave_status_string(wave_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAVE_INDEX_H */

@@ -1,0 +1,221 @@
+"""Python binding of libwave_index (MI355X wave index): argument marshalling only.
+
+Every computation runs in the HIP library; this module only converts torch tensors (device
+memory) and the current HIP stream into the C ABI's plain pointers, and raises on error.
+The names mirror the C entry points declared in include/wave_index.h. PyTorch serves as
+the device-memory allocator and stream provider.
+
+If the compiled library is missing, importing the package still works but every call
+raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+__all__ = [
+    "WaveError", "wave_build_params", "wave_index", "wave_decode_params", "library",
+    "wave_status_string", "wave_index_workspace_size", "wave_index_build",
+    "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
+    "IndexTensors", "alloc_index", "EXPORTED_SYMBOLS", "LIB_PATH", "wave_trace",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libwave_index.so")
+EXPORTED_SYMBOLS = (
+    "wave_status_string", "wave_index_workspace_size", "wave_index_build",
+    "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
+    "wave_index_build_traced", "wave_decode_attention_traced",
+)
+STATUS = {0: "WAVE_OK", 1: "WAVE_ERR_INVALID_ARG", 2: "WAVE_ERR_UNSUPPORTED",
+          3: "WAVE_ERR_WORKSPACE", 4: "WAVE_ERR_ALIAS", 5: "WAVE_ERR_HIP"}
+
+
+class WaveError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        self.name = STATUS.get(code, str(code))
+        super().__init__(f"{fn}: {self.name} ({wave_status_string(code)})")
+
+
+class wave_build_params(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("seq_len", ctypes.c_int64), ("kv_capacity", ctypes.c_int64),
+                ("segment_size", ctypes.c_int32), ("clusters_per_segment", ctypes.c_int32),
+                ("n_iters", ctypes.c_int32), ("n_sink", ctypes.c_int32),
+                ("n_recent", ctypes.c_int32)]
+
+
+class wave_index(ctypes.Structure):
+    _fields_ = [("centroid_mean", ctypes.c_void_p), ("value_sum", ctypes.c_void_p),
+                ("cluster_size", ctypes.c_void_p), ("cluster_offset", ctypes.c_void_p),
+                ("labels", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("last_centroids", ctypes.c_void_p), ("objective", ctypes.c_void_p)]
+
+
+class wave_decode_params(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("seq_len", ctypes.c_int64), ("index_len", ctypes.c_int64),
+                ("kv_capacity", ctypes.c_int64), ("n_clusters", ctypes.c_int32),
+                ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+                ("n_retrieve", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class wave_trace(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", ctypes.c_int32),
+                ("recorded", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libwave_index.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.wave_status_string.restype = ctypes.c_char_p
+        lib.wave_status_string.argtypes = [ctypes.c_int]
+        lib.wave_index_workspace_size.argtypes = [P(wave_build_params), P(sz)]
+        lib.wave_index_build.argtypes = [P(wave_build_params), vp, vp, vp, vp, P(wave_index),
+                                         vp, sz, vp]
+        lib.wave_decode_workspace_size.argtypes = [P(wave_decode_params), P(sz)]
+        lib.wave_decode_attention.argtypes = [P(wave_decode_params), vp, vp, vp, P(wave_index),
+                                              vp, vp, vp, vp, sz, vp]
+        lib.wave_dense_decode_attention.argtypes = [P(wave_decode_params), vp, vp, vp, vp, vp,
+                                                    vp, sz, vp]
+        lib.wave_index_build_traced.argtypes = lib.wave_index_build.argtypes + [P(wave_trace)]
+        lib.wave_decode_attention_traced.argtypes = (lib.wave_decode_attention.argtypes
+                                                     + [P(wave_trace)])
+        for name in EXPORTED_SYMBOLS[1:]:
+            getattr(lib, name).restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(fn: str, code: int) -> None:
+    if code != 0:
+        raise WaveError(fn, code)
+
+
+def wave_status_string(code: int) -> str:
+    return library().wave_status_string(code).decode()
+
+
+def wave_index_workspace_size(p: wave_build_params) -> int:
+    n = ctypes.c_size_t(0)
+    _check("wave_index_workspace_size", library().wave_index_workspace_size(ctypes.byref(p),
+                                                                             ctypes.byref(n)))
+    return n.value
+
+
+def wave_decode_workspace_size(p: wave_decode_params) -> int:
+    n = ctypes.c_size_t(0)
+    _check("wave_decode_workspace_size", library().wave_decode_workspace_size(ctypes.byref(p),
+                                                                               ctypes.byref(n)))
+    return n.value
+
+
+@dataclass
+class IndexTensors:
+    """Device tensors of one layer's index, in the library layout."""
+    centroid_mean: object      # bf16 [B, Hkv, C, d]
+    value_sum: object          # bf16 [B, Hkv, C, d]
+    cluster_size: object       # int32 [B, Hkv, C]
+    cluster_offset: object     # int32 [B, Hkv, C]
+    labels: object = None      # int32 [B, Hkv, L0]
+    perm: object = None        # int32 [B, Hkv, L0]
+    last_centroids: object = None
+    objective: object = None   # float32 [B, Hkv]
+
+    def c_struct(self) -> wave_index:
+        return wave_index(*[_ptr(getattr(self, f)) for f, _ in wave_index._fields_])
+
+
+def alloc_index(batch: int, n_kv_heads: int, n_clusters: int, seq_len: int, device="cuda",
+                optional: bool = True) -> IndexTensors:
+    import torch
+    B, H, C, d = batch, n_kv_heads, n_clusters, 128
+    e = dict(device=device)
+    return IndexTensors(
+        torch.empty(B, H, C, d, dtype=torch.bfloat16, **e),
+        torch.empty(B, H, C, d, dtype=torch.bfloat16, **e),
+        torch.empty(B, H, C, dtype=torch.int32, **e),
+        torch.empty(B, H, C, dtype=torch.int32, **e),
+        torch.empty(B, H, seq_len, dtype=torch.int32, **e) if optional else None,
+        torch.empty(B, H, seq_len, dtype=torch.int32, **e) if optional else None,
+        torch.empty(B, H, C, d, dtype=torch.bfloat16, **e) if optional else None,
+        torch.empty(B, H, dtype=torch.float32, **e) if optional else None,
+    )
+
+
+def _trace(events):
+    arr = (ctypes.c_void_p * len(events))(*events)
+    return wave_trace(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), len(events), 0), arr
+
+
+def wave_index_build(p: wave_build_params, k, v, k_out, v_out, index: IndexTensors, workspace,
+                     stream=None, events=None) -> int:
+    """Enqueue the index build (see wave_index_build in include/wave_index.h).
+
+    With `events` (a list of hipEvent_t handles) the traced variant records kernel-boundary
+    events; returns the number recorded (0 without events)."""
+    idx = index.c_struct()
+    args = (ctypes.byref(p), _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out), ctypes.byref(idx),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if events is None:
+        _check("wave_index_build", library().wave_index_build(*args))
+        return 0
+    tr, keep = _trace(events)
+    _check("wave_index_build_traced", library().wave_index_build_traced(*args, ctypes.byref(tr)))
+    return tr.recorded
+
+
+def wave_decode_attention(p: wave_decode_params, q, k_cache, v_cache, index: IndexTensors, out,
+                          lse=None, selected=None, workspace=None, stream=None,
+                          events=None) -> int:
+    """Enqueue one tripartite decode step (see include/wave_index.h); `events` as for
+    wave_index_build."""
+    idx = index.c_struct()
+    args = (ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(idx), _ptr(out),
+            _ptr(lse), _ptr(selected), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    if events is None:
+        _check("wave_decode_attention", library().wave_decode_attention(*args))
+        return 0
+    tr, keep = _trace(events)
+    _check("wave_decode_attention_traced",
+           library().wave_decode_attention_traced(*args, ctypes.byref(tr)))
+    return tr.recorded
+
+
+def wave_dense_decode_attention(p: wave_decode_params, q, k_cache, v_cache, out, lse=None,
+                                workspace=None, stream=None) -> None:
+    """Enqueue dense (full) decode attention over all seq_len rows."""
+    _check("wave_dense_decode_attention", library().wave_dense_decode_attention(
+        ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def default_scale(head_dim: int = 128) -> float:
+    return 1.0 / math.sqrt(head_dim)

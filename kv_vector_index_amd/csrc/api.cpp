@@ -1,0 +1,419 @@
+// C ABI of the wave-index library: argument validation, workspace layout, launch order.
+// Nothing here allocates device memory or synchronises; kernels are enqueued on the
+// caller's stream.
+#include "../../include/wave_index.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "wave_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Carves aligned sub-buffers out of one workspace; with base == nullptr it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
+// ---------------------------------------------------------------- build
+
+struct BuildShape {
+  int nseg, C;
+  int64_t BH, cache_elems;  // elements of one [B, Hkv, Lcap, d] cache
+};
+
+wave_status check_build(const wave_build_params* p, BuildShape* sh) {
+  if (!p) return WAVE_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->n_kv_heads < 1 || p->n_q_heads < 1) return WAVE_ERR_INVALID_ARG;
+  if (p->n_q_heads % p->n_kv_heads) return WAVE_ERR_INVALID_ARG;
+  if (p->head_dim != wave::kHeadDim) return p->head_dim > 0 ? WAVE_ERR_UNSUPPORTED
+                                                            : WAVE_ERR_INVALID_ARG;
+  if (p->seq_len < 1 || p->kv_capacity < p->seq_len) return WAVE_ERR_INVALID_ARG;
+  if (p->seq_len > (int64_t)1 << 30) return WAVE_ERR_UNSUPPORTED;
+  if (p->segment_size < 1 || p->clusters_per_segment < 1) return WAVE_ERR_INVALID_ARG;
+  if (p->clusters_per_segment > p->segment_size) return WAVE_ERR_INVALID_ARG;
+  if (p->segment_size > 16384 || p->clusters_per_segment > 2048) return WAVE_ERR_UNSUPPORTED;
+  if (p->n_iters < 1 || p->n_iters > 1000) return WAVE_ERR_INVALID_ARG;
+  if (p->n_sink < 0 || p->n_recent < 0) return WAVE_ERR_INVALID_ARG;
+  if ((int64_t)p->n_sink + p->n_recent > p->seq_len) return WAVE_ERR_INVALID_ARG;
+  const int64_t nseg = (p->seq_len + p->segment_size - 1) / p->segment_size;
+  const int64_t C = nseg * p->clusters_per_segment;
+  if (C > INT32_MAX / 2) return WAVE_ERR_UNSUPPORTED;
+  int64_t bh, rows, elems;
+  if (!mul_ok(p->batch, p->n_kv_heads, &bh) || !mul_ok(bh, p->kv_capacity, &rows) ||
+      !mul_ok(rows, wave::kHeadDim, &elems) || elems > INT64_MAX / 4)
+    return WAVE_ERR_INVALID_ARG;
+  sh->nseg = (int)nseg;
+  sh->C = (int)C;
+  sh->BH = bh;
+  sh->cache_elems = elems;
+  return WAVE_OK;
+}
+
+// Workspace of the build; returns its size (and fills a when base != nullptr).
+size_t layout_build(const wave_build_params* p, const BuildShape& sh, void* base,
+                    wave::BuildArgs* a) {
+  Carver cv(base);
+  const size_t BH = (size_t)sh.BH, L0 = (size_t)p->seq_len, C = (size_t)sh.C;
+  float* inv = cv.take<float>(BH * L0);
+  uint16_t* mu0 = cv.take<uint16_t>(BH * C * wave::kHeadDim);
+  uint16_t* mu1 = cv.take<uint16_t>(BH * C * wave::kHeadDim);
+  int32_t* lab = cv.take<int32_t>(BH * L0);
+  int32_t* order = cv.take<int32_t>(BH * L0);
+  int32_t* cstart = cv.take<int32_t>(BH * sh.nseg * (size_t)(p->clusters_per_segment + 1));
+  float* cnorm = cv.take<float>(BH * C);
+  if (a) {
+    a->inv_norm = inv;
+    a->mu[0] = mu0;
+    a->mu[1] = mu1;
+    a->lab = lab;
+    a->order = order;
+    a->cstart = cstart;
+    a->cnorm = cnorm;
+  }
+  return cv.off;
+}
+
+// ---------------------------------------------------------------- decode
+
+struct DecodeShape {
+  int G, nEst, nSteadyMax, nB, nBDense, rcap;
+  int64_t BH, cache_elems;
+};
+
+int clampi(int64_t x, int lo, int hi) { return (int)(x < lo ? lo : (x > hi ? hi : x)); }
+
+wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
+  if (!p) return WAVE_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->n_kv_heads < 1 || p->n_q_heads < 1) return WAVE_ERR_INVALID_ARG;
+  if (p->n_q_heads % p->n_kv_heads) return WAVE_ERR_INVALID_ARG;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (G > wave::kMaxGroup) return WAVE_ERR_UNSUPPORTED;
+  if (p->head_dim != wave::kHeadDim) return p->head_dim > 0 ? WAVE_ERR_UNSUPPORTED
+                                                            : WAVE_ERR_INVALID_ARG;
+  if (p->index_len < 1 || p->seq_len < p->index_len || p->kv_capacity < p->seq_len)
+    return WAVE_ERR_INVALID_ARG;
+  if (p->kv_capacity > (int64_t)1 << 30) return WAVE_ERR_UNSUPPORTED;
+  if (p->n_clusters < 1 || p->n_clusters > INT32_MAX / 2) return WAVE_ERR_INVALID_ARG;
+  if (p->n_sink < 0 || p->n_recent < 0) return WAVE_ERR_INVALID_ARG;
+  if ((int64_t)p->n_sink + p->n_recent > p->index_len) return WAVE_ERR_INVALID_ARG;
+  if (p->n_retrieve < 0 || p->n_retrieve > p->n_clusters) return WAVE_ERR_INVALID_ARG;
+  if (!(p->scale > 0.f) || !isfinite(p->scale)) return WAVE_ERR_INVALID_ARG;
+  int64_t bh, rows, elems;
+  if (!mul_ok(p->batch, p->n_kv_heads, &bh) || !mul_ok(bh, p->kv_capacity, &rows) ||
+      !mul_ok(rows, wave::kHeadDim, &elems) || elems > INT64_MAX / 4)
+    return WAVE_ERR_INVALID_ARG;
+  sh->G = G;
+  sh->BH = bh;
+  sh->cache_elems = elems;
+  sh->nEst = (p->n_clusters + wave::kEstChunk - 1) / wave::kEstChunk;
+  const int64_t steady_max = (int64_t)p->n_sink + p->n_recent + (p->kv_capacity - p->index_len);
+  sh->nSteadyMax = (int)((steady_max + wave::kTokChunk - 1) / wave::kTokChunk);
+  // retrieved-token workgroups: about 256 tokens each at the average cluster size
+  const int64_t indexed = p->index_len - p->n_sink - p->n_recent;
+  const int64_t avg = indexed > p->n_clusters ? indexed / p->n_clusters : 1;
+  sh->nB = clampi(((int64_t)p->n_retrieve * avg + 255) / 256, 1, 64);
+  sh->nBDense = clampi((p->kv_capacity + 1023) / 1024, 1, 512);
+  sh->rcap = p->n_retrieve > 0 ? p->n_retrieve : 1;
+  return WAVE_OK;
+}
+
+size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* base,
+                     wave::DecodeArgs* a) {
+  Carver cv(base);
+  const size_t BH = (size_t)sh.BH, G = (size_t)sh.G, PS = wave::kPartStride;
+  const int nAmax = sh.nEst + sh.nSteadyMax;
+  const int nBmax = sh.nB > sh.nBDense ? sh.nB : sh.nBDense;
+  uint32_t* counter = cv.take<uint32_t>(BH);
+  int32_t* nsel = cv.take<int32_t>(BH);
+  int32_t* ntok = cv.take<int32_t>(BH);
+  float* shat = cv.take<float>(BH * (size_t)p->n_clusters);
+  float* partA = cv.take<float>(BH * (size_t)nAmax * G * PS);
+  float* mergedA = cv.take<float>(BH * G * PS);
+  float* partB = cv.take<float>(BH * (size_t)nBmax * G * PS);
+  int32_t* sel = cv.take<int32_t>(BH * (size_t)sh.rcap);
+  int32_t* slots = cv.take<int32_t>(BH * (size_t)p->index_len);
+  if (a) {
+    a->counter = counter;
+    a->nsel = nsel;
+    a->ntok = ntok;
+    a->shat = shat;
+    a->partA = partA;
+    a->mergedA = mergedA;
+    a->partB = partB;
+    a->sel = sel;
+    a->slots = slots;
+  }
+  return cv.off;
+}
+
+void fill_decode_shape(const wave_decode_params* p, const DecodeShape& sh, wave::DecodeArgs* a) {
+  a->B = p->batch;
+  a->Hq = p->n_q_heads;
+  a->Hkv = p->n_kv_heads;
+  a->G = sh.G;
+  a->L = p->seq_len;
+  a->L0 = p->index_len;
+  a->Lcap = p->kv_capacity;
+  a->C = p->n_clusters;
+  a->n_sink = p->n_sink;
+  a->n_recent = p->n_recent;
+  a->n_retrieve = p->n_retrieve;
+  a->rcap = sh.rcap;
+  a->scale = p->scale;
+  a->scale_log2 = p->scale * wave::kLog2eHost;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wave_status_string(wave_status s) {
+  switch (s) {
+    case WAVE_OK: return "ok";
+    case WAVE_ERR_INVALID_ARG: return "invalid argument";
+    case WAVE_ERR_UNSUPPORTED: return "unsupported shape";
+    case WAVE_ERR_WORKSPACE: return "workspace missing or too small";
+    case WAVE_ERR_ALIAS: return "output buffer overlaps an input buffer";
+    case WAVE_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+wave_status wave_index_workspace_size(const wave_build_params* p, size_t* bytes) {
+  if (!bytes) return WAVE_ERR_INVALID_ARG;
+  BuildShape sh;
+  wave_status st = check_build(p, &sh);
+  if (st != WAVE_OK) return st;
+  *bytes = layout_build(p, sh, nullptr, nullptr);
+  return WAVE_OK;
+}
+
+namespace {
+
+wave_status build_impl(const wave_build_params* p, const void* k, const void* v, void* k_out,
+                       void* v_out, const wave_index* idx, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, wave::Tracer* tr) {
+  BuildShape sh;
+  wave_status st = check_build(p, &sh);
+  if (st != WAVE_OK) return st;
+  if (!k || !v || !k_out || !v_out || !idx || !idx->centroid_mean || !idx->value_sum ||
+      !idx->cluster_size || !idx->cluster_offset)
+    return WAVE_ERR_INVALID_ARG;
+  const size_t need = layout_build(p, sh, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return WAVE_ERR_WORKSPACE;
+  const size_t cache_bytes = (size_t)sh.cache_elems * 2;
+  const size_t L0 = (size_t)p->seq_len, BH = (size_t)sh.BH, C = (size_t)sh.C;
+  const size_t meta_bytes = BH * C * wave::kHeadDim * 2;
+  // outputs must not overlap the inputs (k, v) or each other
+  const void* outs[] = {k_out, v_out, idx->centroid_mean, idx->value_sum, idx->cluster_size,
+                        idx->cluster_offset, idx->labels, idx->perm, idx->last_centroids,
+                        idx->objective, workspace};
+  const size_t out_sz[] = {cache_bytes, cache_bytes, meta_bytes, meta_bytes, BH * C * 4,
+                           BH * C * 4, BH * L0 * 4, BH * L0 * 4, meta_bytes, BH * 4,
+                           workspace_bytes};
+  const int nout = sizeof(outs) / sizeof(outs[0]);
+  for (int i = 0; i < nout; ++i) {
+    if (!outs[i]) continue;
+    if (overlaps(outs[i], out_sz[i], k, cache_bytes) || overlaps(outs[i], out_sz[i], v, cache_bytes))
+      return WAVE_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (outs[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return WAVE_ERR_ALIAS;
+  }
+
+  wave::BuildArgs a{};
+  layout_build(p, sh, workspace, &a);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.k_out = static_cast<uint16_t*>(k_out);
+  a.v_out = static_cast<uint16_t*>(v_out);
+  a.cmean = static_cast<uint16_t*>(idx->centroid_mean);
+  a.vsum = static_cast<uint16_t*>(idx->value_sum);
+  a.csize = idx->cluster_size;
+  a.coff = idx->cluster_offset;
+  a.labels = idx->labels;
+  a.perm = idx->perm;
+  a.last_mu = static_cast<uint16_t*>(idx->last_centroids);
+  a.objective = idx->objective;
+  a.B = p->batch;
+  a.Hkv = p->n_kv_heads;
+  a.L0 = p->seq_len;
+  a.Lcap = p->kv_capacity;
+  a.S = p->segment_size;
+  a.kseg = p->clusters_per_segment;
+  a.nseg = sh.nseg;
+  a.C = sh.C;
+  a.T = p->n_iters;
+  a.n_sink = p->n_sink;
+  a.n_recent = p->n_recent;
+  a.idx_lo = p->n_sink;
+  a.idx_hi = p->seq_len - p->n_recent;
+  return wave::launch_build(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
+}
+
+}  // namespace
+
+wave_status wave_index_build(const wave_build_params* p, const void* k, const void* v,
+                             void* k_out, void* v_out, const wave_index* idx, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return build_impl(p, k, v, k_out, v_out, idx, workspace, workspace_bytes, stream, nullptr);
+}
+
+wave_status wave_index_build_traced(const wave_build_params* p, const void* k, const void* v,
+                                    void* k_out, void* v_out, const wave_index* idx,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    wave_trace* trace) {
+  if (!trace || (trace->capacity > 0 && !trace->events)) return WAVE_ERR_INVALID_ARG;
+  wave::Tracer tr{trace->events, trace->capacity, 0};
+  const wave_status st =
+      build_impl(p, k, v, k_out, v_out, idx, workspace, workspace_bytes, stream, &tr);
+  trace->recorded = tr.n;
+  return st;
+}
+
+wave_status wave_decode_workspace_size(const wave_decode_params* p, size_t* bytes) {
+  if (!bytes) return WAVE_ERR_INVALID_ARG;
+  DecodeShape sh;
+  wave_status st = check_decode(p, &sh);
+  if (st != WAVE_OK) return st;
+  *bytes = layout_decode(p, sh, nullptr, nullptr);
+  return WAVE_OK;
+}
+
+namespace {
+
+wave_status decode_impl(const wave_decode_params* p, const void* q, const void* k_cache,
+                        const void* v_cache, const wave_index* idx, float* out, float* lse,
+                        int32_t* selected, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, wave::Tracer* tr) {
+  DecodeShape sh;
+  wave_status st = check_decode(p, &sh);
+  if (st != WAVE_OK) return st;
+  if (!q || !k_cache || !v_cache || !idx || !idx->centroid_mean || !idx->value_sum ||
+      !idx->cluster_size || !idx->cluster_offset || !out)
+    return WAVE_ERR_INVALID_ARG;
+  const size_t need = layout_decode(p, sh, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return WAVE_ERR_WORKSPACE;
+  const size_t BH = (size_t)sh.BH, C = (size_t)p->n_clusters;
+  const size_t cache_bytes = (size_t)sh.cache_elems * 2;
+  const size_t qb = (size_t)p->batch * p->n_q_heads * wave::kHeadDim;
+  const void* ins[] = {q, k_cache, v_cache, idx->centroid_mean, idx->value_sum,
+                       idx->cluster_size, idx->cluster_offset};
+  const size_t in_sz[] = {qb * 2, cache_bytes, cache_bytes, BH * C * wave::kHeadDim * 2,
+                          BH * C * wave::kHeadDim * 2, BH * C * 4, BH * C * 4};
+  const void* outs[] = {out, lse, selected, workspace};
+  const size_t out_sz[] = {qb * 4, (size_t)p->batch * p->n_q_heads * 4,
+                           BH * (size_t)p->n_retrieve * 4, workspace_bytes};
+  for (int i = 0; i < 4; ++i) {
+    if (!outs[i]) continue;
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return WAVE_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return WAVE_ERR_ALIAS;
+  }
+  wave::DecodeArgs a{};
+  layout_decode(p, sh, workspace, &a);
+  fill_decode_shape(p, sh, &a);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.cmean = static_cast<const uint16_t*>(idx->centroid_mean);
+  a.vsum = static_cast<const uint16_t*>(idx->value_sum);
+  a.csize = idx->cluster_size;
+  a.coff = idx->cluster_offset;
+  a.out = out;
+  a.lse = lse;
+  a.selected = p->n_retrieve > 0 ? selected : nullptr;
+  const int64_t n_steady = (int64_t)p->n_sink + p->n_recent + (p->seq_len - p->index_len);
+  a.nEst = sh.nEst;
+  a.nSteady = (int)((n_steady + wave::kTokChunk - 1) / wave::kTokChunk);
+  a.nA = a.nEst + a.nSteady;
+  a.nB = sh.nB;
+  return wave::launch_decode(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
+}
+
+}  // namespace
+
+wave_status wave_decode_attention(const wave_decode_params* p, const void* q, const void* k_cache,
+                                  const void* v_cache, const wave_index* idx, float* out,
+                                  float* lse, int32_t* selected, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(p, q, k_cache, v_cache, idx, out, lse, selected, workspace,
+                     workspace_bytes, stream, nullptr);
+}
+
+wave_status wave_decode_attention_traced(const wave_decode_params* p, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const wave_index* idx, float* out, float* lse,
+                                         int32_t* selected, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream,
+                                         wave_trace* trace) {
+  if (!trace || (trace->capacity > 0 && !trace->events)) return WAVE_ERR_INVALID_ARG;
+  wave::Tracer tr{trace->events, trace->capacity, 0};
+  const wave_status st = decode_impl(p, q, k_cache, v_cache, idx, out, lse, selected, workspace,
+                                     workspace_bytes, stream, &tr);
+  trace->recorded = tr.n;
+  return st;
+}
+
+wave_status wave_dense_decode_attention(const wave_decode_params* p, const void* q,
+                                        const void* k_cache, const void* v_cache, float* out,
+                                        float* lse, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  DecodeShape sh;
+  wave_status st = check_decode(p, &sh);
+  if (st != WAVE_OK) return st;
+  if (!q || !k_cache || !v_cache || !out) return WAVE_ERR_INVALID_ARG;
+  const size_t need = layout_decode(p, sh, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return WAVE_ERR_WORKSPACE;
+  const size_t cache_bytes = (size_t)sh.cache_elems * 2;
+  const size_t qb = (size_t)p->batch * p->n_q_heads * wave::kHeadDim;
+  const void* ins[] = {q, k_cache, v_cache};
+  const size_t in_sz[] = {qb * 2, cache_bytes, cache_bytes};
+  const void* outs[] = {out, lse, workspace};
+  const size_t out_sz[] = {qb * 4, (size_t)p->batch * p->n_q_heads * 4, workspace_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (!outs[i]) continue;
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return WAVE_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (outs[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return WAVE_ERR_ALIAS;
+  }
+  wave::DecodeArgs a{};
+  layout_decode(p, sh, workspace, &a);
+  fill_decode_shape(p, sh, &a);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.out = out;
+  a.lse = lse;
+  a.nB = sh.nBDense;
+  return wave::launch_dense_decode(a, stream, nullptr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,522 @@
+// Wave-index build: segmented spherical k-means over each KV head's keys (gfx950).
+//
+// The summaries of RetroInfer build the index during prefill by clustering the keys of each
+// segment of the context locally (gist.science de/fr/zh, section 2A "segmented
+// clustering"; the zh summary ties it to RoPE's positional locality), with spherical
+// k-means (fr, section 2A), and keep per-cluster centroids and precomputed value sums for
+// the estimation zone (zh, section 2A).
+//
+// Per (b, kv-head, segment), T passes of
+//   assign: a_i = argmax_j k_i . mu_j  (the positive factor 1/||k_i|| of the cosine does not
+//           change the argmax, so the contraction runs on the raw bf16 keys) -- a dense
+//           [points x 128] x [128 x k_seg] product on bf16 MFMA (v_mfma_f32_32x32x16_bf16)
+//           with the argmax fused into the epilogue;
+//   sort:   stable counting sort of the labels (one workgroup per segment, wave ballots
+//           give each point its rank among equal labels) -- no atomics on data, so every
+//           later sum runs in a fixed order and the build is bitwise reproducible;
+//   update: mu_j = bf16(u_j / ||u_j||), u_j = sum of the members' unit keys, summed in
+//           position order by 16 lanes per row (empty clusters keep mu_j).
+// Then finalise: sizes, offsets, mean raw key and value sum per cluster, and the
+// cluster-contiguous permutation of K and V (each row read once, written once), so that
+// decode reads a retrieved cluster as one contiguous run of rows.
+#include <algorithm>
+
+#include "wave_common.h"
+#include "wave_kernels.h"
+
+namespace wave {
+
+struct Seg {
+  int64_t lo, hi;  // indexed positions [lo, hi) of the segment
+};
+
+__device__ __forceinline__ Seg seg_range(const BuildArgs& a, int s) {
+  int64_t lo = max((int64_t)s * a.S, a.idx_lo);
+  int64_t hi = min((int64_t)(s + 1) * a.S, a.idx_hi);
+  if (hi < lo) hi = lo;
+  return {lo, hi};
+}
+
+// usable clusters of a segment with n points: all k_seg, or one per point if fewer
+__device__ __forceinline__ int n_valid_clusters(const BuildArgs& a, int64_t n) {
+  return n >= a.kseg ? a.kseg : (int)n;
+}
+
+// ------------------------------------------------------------------------------------
+// norms of the indexed keys: inv_norm = 1/||k|| (0 for a zero key)
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_norms(BuildArgs a) {
+  const int bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, grp = (threadIdx.x >> 4), c = lane & 15;
+  const int64_t n = a.idx_hi - a.idx_lo;
+  for (int64_t i = (int64_t)blockIdx.x * 16 + grp; i < n; i += (int64_t)gridDim.x * 16) {
+    const int64_t p = a.idx_lo + i;
+    const u32x4 kr = ld16(a.k + ((size_t)bh * a.Lcap + p) * kHeadDim + c * 8);
+    float ss = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float x0 = bf_lo(kr[d]), x1 = bf_hi(kr[d]);
+      ss += x0 * x0 + x1 * x1;
+    }
+    ss = sum16(ss);
+    if (c == 0) a.inv_norm[(size_t)bh * a.L0 + p] = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// seeds: mu_j = bf16(unit key of local point j * floor(n_s / k_seg)); first n_s points
+// if the segment is short, zero rows for the clusters that stay empty
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_seeds(BuildArgs a, uint16_t* __restrict__ mu) {
+  const int s = blockIdx.y, bh = blockIdx.z;
+  const int grp = threadIdx.x >> 4, c = threadIdx.x & 15;
+  const Seg sg = seg_range(a, s);
+  const int64_t n = sg.hi - sg.lo;
+  const int j = blockIdx.x * 16 + grp;
+  if (j >= a.kseg) return;
+  u32x4 out = {0, 0, 0, 0};
+  int64_t p = -1;
+  if (n >= a.kseg) p = sg.lo + (int64_t)j * (n / a.kseg);
+  else if (j < n) p = sg.lo + j;
+  if (p >= 0) {
+    const u32x4 kr = ld16(a.k + ((size_t)bh * a.Lcap + p) * kHeadDim + c * 8);
+    const float inv = a.inv_norm[(size_t)bh * a.L0 + p];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) out[d] = pack_bf2(bf_lo(kr[d]) * inv, bf_hi(kr[d]) * inv);
+  }
+  st16(mu + ((size_t)bh * a.C + (size_t)s * a.kseg + j) * kHeadDim + c * 8, out);
+}
+
+// ------------------------------------------------------------------------------------
+// assignment on MFMA
+// ------------------------------------------------------------------------------------
+constexpr int kAsgWaves = 4;
+constexpr int kAsgNB = 2;                                  // 32-point column blocks per wave
+constexpr int kAsgPoints = kAsgWaves * kAsgNB * 32;        // points per workgroup
+constexpr int kAsgTile = 128;                              // centroids per LDS tile
+constexpr int kAsgLdsStride = kRowBytes + 16;              // padded row: no bank conflicts
+
+__global__ __launch_bounds__(256) void k_assign(BuildArgs a, const uint16_t* __restrict__ mu) {
+  const int blk = blockIdx.x, s = blockIdx.y, bh = blockIdx.z;
+  const Seg sg = seg_range(a, s);
+  const int64_t n = sg.hi - sg.lo;
+  if ((int64_t)blk * kAsgPoints >= n) return;
+  const int nvalid = n_valid_clusters(a, n);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+
+  __shared__ __attribute__((aligned(16))) unsigned char s_mu[kAsgTile * kAsgLdsStride];
+
+  // B operands: this wave's points, 32 per column block. Lane holds elements
+  // k = 16*kk + 8*half + [0, 8) of point (col) for every 16-wide k step kk.
+  bf16x8 bq[kAsgNB][8];
+  int64_t pidx[kAsgNB];
+#pragma unroll
+  for (int nb = 0; nb < kAsgNB; ++nb) {
+    pidx[nb] = (int64_t)blk * kAsgPoints + wave * (kAsgNB * 32) + nb * 32 + col;
+    const bool ok = pidx[nb] < n;
+    const uint16_t* row = a.k + ((size_t)bh * a.Lcap + sg.lo + (ok ? pidx[nb] : 0)) * kHeadDim;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4 v = ok ? ld16(row + kk * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      bq[nb][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  float best[kAsgNB];
+  int bidx[kAsgNB];
+#pragma unroll
+  for (int nb = 0; nb < kAsgNB; ++nb) {
+    best[nb] = kNegInf;
+    bidx[nb] = 0;
+  }
+
+  const uint16_t* mus = mu + ((size_t)bh * a.C + (size_t)s * a.kseg) * kHeadDim;
+  for (int t0 = 0; t0 < nvalid; t0 += kAsgTile) {
+    __syncthreads();
+    // stage centroids [t0, t0 + 128) (zero rows past k_seg)
+    for (int q = tid; q < kAsgTile * 16; q += 256) {
+      const int r = q >> 4, ch = q & 15;
+      u32x4 v = {0, 0, 0, 0};
+      if (t0 + r < a.kseg) v = ld16(mus + (size_t)(t0 + r) * kHeadDim + ch * 8);
+      *reinterpret_cast<u32x4*>(s_mu + r * kAsgLdsStride + ch * 16) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < kAsgTile / 32; ++rb) {
+      const int m0 = t0 + rb * 32;
+      if (m0 >= nvalid) break;
+      floatx16 acc[kAsgNB];
+#pragma unroll
+      for (int nb = 0; nb < kAsgNB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        // A operand: centroid row (m0 + col), elements 16*kk + 8*half + [0, 8)
+        const bf16x8 am = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(s_mu + (rb * 32 + col) * kAsgLdsStride +
+                                                     (kk * 2 + half) * 16));
+#pragma unroll
+        for (int nb = 0; nb < kAsgNB; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bq[nb][kk], acc[nb], 0, 0, 0);
+      }
+      // D[m][n]: lane holds column n = col and rows m = 8*(i/4) + 4*half + i%4 (increasing
+      // in i), so a strict '>' keeps the lowest centroid id among equal scores
+#pragma unroll
+      for (int nb = 0; nb < kAsgNB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + 8 * (i >> 2) + 4 * half + (i & 3);
+          const float v = acc[nb][i];
+          if (m < nvalid && v > best[nb]) {
+            best[nb] = v;
+            bidx[nb] = m;
+          }
+        }
+    }
+  }
+  // the two half-waves hold disjoint centroid rows of the same points
+#pragma unroll
+  for (int nb = 0; nb < kAsgNB; ++nb) {
+    const float ov = __shfl_xor(best[nb], 32);
+    const int oi = __shfl_xor(bidx[nb], 32);
+    if (ov > best[nb] || (ov == best[nb] && oi < bidx[nb])) {
+      best[nb] = ov;
+      bidx[nb] = oi;
+    }
+    if (half == 0 && pidx[nb] < n) a.lab[(size_t)bh * a.L0 + sg.lo + pidx[nb]] = bidx[nb];
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// stable counting sort of a segment's labels: order = local point ids by (label, position)
+// ------------------------------------------------------------------------------------
+constexpr int kSortThreads = 1024;
+constexpr int kSortWaves = kSortThreads / 64;
+constexpr int kMaxSeg = 16384;
+constexpr int kMaxKseg = 2048;
+
+__device__ __forceinline__ uint32_t scan1024_excl(uint32_t x, uint32_t* s_tmp, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t v = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) s_tmp[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t t = lane < kSortWaves ? s_tmp[lane] : 0u;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const uint32_t y = __shfl_up(t, off);
+      if (lane >= off) t += y;
+    }
+    if (lane < kSortWaves) s_tmp[lane] = t;
+  }
+  __syncthreads();
+  const uint32_t before = wave > 0 ? s_tmp[wave - 1] : 0u;
+  total = s_tmp[kSortWaves - 1];
+  __syncthreads();
+  return v - x + before;
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_sort(BuildArgs a) {
+  const int s = blockIdx.x, bh = blockIdx.y;
+  const Seg sg = seg_range(a, s);
+  const int n = (int)(sg.hi - sg.lo);
+  const int K = a.kseg;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  __shared__ uint16_t s_lab[kMaxSeg];
+  __shared__ uint16_t s_hist[kSortWaves][kMaxKseg];
+  __shared__ uint32_t s_start[kMaxKseg + 1];
+  __shared__ uint32_t s_run[kMaxKseg];
+  __shared__ uint32_t s_tmp[32];
+
+  const int32_t* lab = a.lab + (size_t)bh * a.L0 + sg.lo;
+  for (int i = tid; i < n; i += kSortThreads) s_lab[i] = (uint16_t)lab[i];
+  for (int j = tid; j < K; j += kSortThreads) {
+    s_run[j] = 0u;
+    s_start[j] = 0u;
+  }
+  for (int q = tid; q < kSortWaves * K; q += kSortThreads) s_hist[q / K][q % K] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kSortThreads) atomicAdd(&s_start[s_lab[i]], 1u);
+  __syncthreads();
+  // exclusive scan of the counts; thread t owns clusters [t*per, (t+1)*per)
+  {
+    const int per = (K + kSortThreads - 1) / kSortThreads;
+    const int j0 = min(K, tid * per), j1 = min(K, j0 + per);
+    uint32_t loc = 0;
+    for (int j = j0; j < j1; ++j) loc += s_start[j];
+    uint32_t total;
+    uint32_t run = scan1024_excl(loc, s_tmp, total);
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t c = s_start[j];
+      s_start[j] = run;
+      run += c;
+    }
+    if (tid == 0) s_start[K] = total;
+  }
+  __syncthreads();
+  int32_t* cst = a.cstart + ((size_t)bh * a.nseg + s) * (K + 1);
+  for (int j = tid; j <= K; j += kSortThreads) cst[j] = (int32_t)s_start[j];
+
+  int32_t* order = a.order + (size_t)bh * a.L0 + sg.lo;
+  const int nbits = 32 - __clz(max(K - 1, 1));
+  for (int r0 = 0; r0 < n; r0 += kSortThreads) {
+    const int i = r0 + tid;
+    const bool ok = i < n;
+    const uint32_t l = ok ? s_lab[i] : 0u;
+    // lanes of this wave holding the same label (ballot over the label bits)
+    uint64_t peers = __ballot(ok);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t bb = __ballot(ok && ((l >> bit) & 1u));
+      peers &= ((l >> bit) & 1u) ? bb : ~bb;
+    }
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+    const uint32_t cnt = (uint32_t)__popcll(peers);
+    if (ok && rank == 0) s_hist[wave][l] = (uint16_t)cnt;
+    __syncthreads();
+    if (ok) {
+      uint32_t pos = s_start[l] + s_run[l] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_hist[w][l];
+      order[pos] = i;
+    }
+    __syncthreads();
+    if (ok && rank == 0) {
+      atomicAdd(&s_run[l], cnt);
+      s_hist[wave][l] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// update: mu_j = bf16(u_j / ||u_j||), u_j = sum of member unit keys (position order)
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_update(BuildArgs a, const uint16_t* __restrict__ mu_in,
+                                                uint16_t* __restrict__ mu_out) {
+  const int s = blockIdx.y, bh = blockIdx.z;
+  const int grp = threadIdx.x >> 4, c = threadIdx.x & 15;
+  const int j = blockIdx.x * 16 + grp;
+  if (j >= a.kseg) return;
+  const Seg sg = seg_range(a, s);
+  const int32_t* cst = a.cstart + ((size_t)bh * a.nseg + s) * (a.kseg + 1);
+  const int cs = cst[j], ce = cst[j + 1];
+  const int32_t* order = a.order + (size_t)bh * a.L0 + sg.lo;
+  const size_t krow0 = (size_t)bh * a.Lcap;
+  const float* inv = a.inv_norm + (size_t)bh * a.L0;
+  float u[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) u[d] = 0.f;
+  for (int r = cs; r < ce; r += 4) {
+    u32x4 kr[4];
+    float iv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (r + e < ce) {
+        const int64_t p = sg.lo + order[r + e];
+        kr[e] = ld16(a.k + (krow0 + p) * kHeadDim + c * 8);
+        iv[e] = inv[p];
+      } else {
+        kr[e] = u32x4{0, 0, 0, 0};
+        iv[e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        u[2 * d] += bf_lo(kr[e][d]) * iv[e];
+        u[2 * d + 1] += bf_hi(kr[e][d]) * iv[e];
+      }
+  }
+  const size_t mrow = ((size_t)bh * a.C + (size_t)s * a.kseg + j) * kHeadDim + c * 8;
+  u32x4 out;
+  if (ce > cs) {
+    float ss = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) ss += u[d] * u[d];
+    ss = sum16(ss);
+    const float nrm = sqrtf(ss);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      out[d] = nrm > 0.f ? pack_bf2(u[2 * d] / nrm, u[2 * d + 1] / nrm) : 0u;
+  } else {
+    out = ld16(mu_in + mrow);
+  }
+  st16(mu_out + mrow, out);
+}
+
+// ------------------------------------------------------------------------------------
+// finalise: sizes, offsets, mean key, value sum, permuted K/V rows, labels, perm
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_finalise(BuildArgs a) {
+  const int s = blockIdx.y, bh = blockIdx.z;
+  const int grp = threadIdx.x >> 4, c = threadIdx.x & 15;
+  const int j = blockIdx.x * 16 + grp;
+  if (j >= a.kseg) return;
+  const Seg sg = seg_range(a, s);
+  const int32_t* cst = a.cstart + ((size_t)bh * a.nseg + s) * (a.kseg + 1);
+  const int cs = cst[j], ce = cst[j + 1];
+  const int32_t* order = a.order + (size_t)bh * a.L0 + sg.lo;
+  const size_t row0 = (size_t)bh * a.Lcap;
+  const float* inv = a.inv_norm + (size_t)bh * a.L0;
+  const int gid = s * a.kseg + j;
+  float uk[8], ux[8], uv[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) uk[d] = ux[d] = uv[d] = 0.f;
+  for (int r = cs; r < ce; r += 4) {
+    u32x4 kr[4], vr[4];
+    float iv[4];
+    int64_t pp[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (r + e < ce) {
+        pp[e] = sg.lo + order[r + e];
+        kr[e] = ld16(a.k + (row0 + pp[e]) * kHeadDim + c * 8);
+        vr[e] = ld16(a.v + (row0 + pp[e]) * kHeadDim + c * 8);
+        iv[e] = inv[pp[e]];
+      } else {
+        pp[e] = -1;
+        kr[e] = vr[e] = u32x4{0, 0, 0, 0};
+        iv[e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (pp[e] < 0) continue;
+      const int64_t slot = sg.lo + r + e;
+      st16(a.k_out + (row0 + slot) * kHeadDim + c * 8, kr[e]);
+      st16(a.v_out + (row0 + slot) * kHeadDim + c * 8, vr[e]);
+      if (c == 0 && a.perm) a.perm[(size_t)bh * a.L0 + slot] = (int32_t)pp[e];
+      if (c == 1 && a.labels) a.labels[(size_t)bh * a.L0 + pp[e]] = gid;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float k0 = bf_lo(kr[e][d]), k1 = bf_hi(kr[e][d]);
+        uk[2 * d] += k0;
+        uk[2 * d + 1] += k1;
+        ux[2 * d] += k0 * iv[e];
+        ux[2 * d + 1] += k1 * iv[e];
+        uv[2 * d] += bf_lo(vr[e][d]);
+        uv[2 * d + 1] += bf_hi(vr[e][d]);
+      }
+    }
+  }
+  const int cnt = ce - cs;
+  const size_t crow = ((size_t)bh * a.C + gid) * kHeadDim + c * 8;
+  u32x4 cm = {0, 0, 0, 0}, vs = {0, 0, 0, 0};
+  if (cnt > 0) {
+    const float fn = (float)cnt;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      cm[d] = pack_bf2(uk[2 * d] / fn, uk[2 * d + 1] / fn);
+      vs[d] = pack_bf2(uv[2 * d], uv[2 * d + 1]);
+    }
+  }
+  st16(a.cmean + crow, cm);
+  st16(a.vsum + crow, vs);
+  float ss = 0.f;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) ss += ux[d] * ux[d];
+  ss = sum16(ss);
+  if (c == 0) {
+    a.csize[(size_t)bh * a.C + gid] = cnt;
+    a.coff[(size_t)bh * a.C + gid] = (int32_t)(sg.lo + cs);
+    a.cnorm[(size_t)bh * a.C + gid] = sqrtf(ss);
+  }
+}
+
+// steady rows stay in place: copy them, label -1, perm = identity
+__global__ __launch_bounds__(256) void k_steady(BuildArgs a) {
+  const int bh = blockIdx.y;
+  const int grp = threadIdx.x >> 4, c = threadIdx.x & 15;
+  const int64_t n = (int64_t)a.n_sink + a.n_recent;
+  for (int64_t t = (int64_t)blockIdx.x * 16 + grp; t < n; t += (int64_t)gridDim.x * 16) {
+    const int64_t p = t < a.n_sink ? t : a.L0 - a.n_recent + (t - a.n_sink);
+    const size_t row = ((size_t)bh * a.Lcap + p) * kHeadDim + c * 8;
+    st16(a.k_out + row, ld16(a.k + row));
+    st16(a.v_out + row, ld16(a.v + row));
+    if (c == 0 && a.perm) a.perm[(size_t)bh * a.L0 + p] = (int32_t)p;
+    if (c == 1 && a.labels) a.labels[(size_t)bh * a.L0 + p] = -1;
+  }
+}
+
+// objective J = sum over clusters of ||u_j|| (fixed summation order)
+__global__ __launch_bounds__(256) void k_objective(BuildArgs a) {
+  const int bh = blockIdx.x;
+  __shared__ float s_part[256];
+  float acc = 0.f;
+  for (int j = threadIdx.x; j < a.C; j += 256) acc += a.cnorm[(size_t)bh * a.C + j];
+  s_part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) s_part[threadIdx.x] += s_part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.objective[bh] = s_part[0];
+}
+
+// ------------------------------------------------------------------------------------
+hipError_t launch_build(const BuildArgs& a, hipStream_t st, Tracer* tr) {
+  const int BH = a.B * a.Hkv;
+  const int64_t nidx = a.idx_hi - a.idx_lo;
+  const dim3 gseg((a.kseg + 15) / 16, a.nseg, BH);
+  hipError_t e;
+#define WAVE_CHECK()                          \
+  do {                                        \
+    e = hipGetLastError();                    \
+    if (e != hipSuccess) return e;            \
+  } while (0)
+  if (nidx > 0) {
+    const int nb = (int)std::min<int64_t>((nidx + 15) / 16, 4096);
+    Tracer::mark(tr, st);
+    hipLaunchKernelGGL(k_norms, dim3(nb, BH), dim3(256), 0, st, a);
+    WAVE_CHECK();
+  }
+  Tracer::mark(tr, st);
+  hipLaunchKernelGGL(k_seeds, gseg, dim3(256), 0, st, a, a.mu[0]);
+  WAVE_CHECK();
+  const dim3 gasg((a.S + kAsgPoints - 1) / kAsgPoints, a.nseg, BH);
+  for (int t = 1; t <= a.T; ++t) {
+    const uint16_t* cur = a.mu[(t - 1) & 1];
+    Tracer::mark(tr, st);
+    hipLaunchKernelGGL(k_assign, gasg, dim3(256), 0, st, a, cur);
+    WAVE_CHECK();
+    Tracer::mark(tr, st);
+    hipLaunchKernelGGL(k_sort, dim3(a.nseg, BH), dim3(kSortThreads), 0, st, a);
+    WAVE_CHECK();
+    if (t < a.T) {
+      Tracer::mark(tr, st);
+      hipLaunchKernelGGL(k_update, gseg, dim3(256), 0, st, a, cur, a.mu[t & 1]);
+      WAVE_CHECK();
+    }
+  }
+  Tracer::mark(tr, st);
+  hipLaunchKernelGGL(k_finalise, gseg, dim3(256), 0, st, a);
+  WAVE_CHECK();
+  if (a.n_sink + a.n_recent > 0) {
+    const int nb = (int)std::min<int64_t>(((int64_t)a.n_sink + a.n_recent + 15) / 16, 1024);
+    Tracer::mark(tr, st);
+    hipLaunchKernelGGL(k_steady, dim3(nb, BH), dim3(256), 0, st, a);
+    WAVE_CHECK();
+  }
+  if (a.objective) {
+    Tracer::mark(tr, st);
+    hipLaunchKernelGGL(k_objective, dim3(BH), dim3(256), 0, st, a);
+    WAVE_CHECK();
+  }
+  if (a.last_mu) {
+    e = hipMemcpyAsync(a.last_mu, a.mu[(a.T - 1) & 1],
+                       (size_t)BH * a.C * kHeadDim * sizeof(uint16_t), hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return e;
+  }
+#undef WAVE_CHECK
+  Tracer::mark(tr, st);
+  return hipSuccess;
+}
+
+}  // namespace wave

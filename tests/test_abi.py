@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every symbol its header declares, and validates arguments
+on the host (no GPU work is enqueued by any call in this file)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import kv_vector_index_amd as wi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wave_index.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(wi.LIB_PATH),
+                                reason="libwave_index.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:wave_status|const char\*)\s+(wave_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(wi.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", wi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    lib = wi.library()
+    for f in declared_functions():
+        assert getattr(lib, f) is not None
+
+
+def test_status_strings():
+    assert wi.wave_status_string(0) == "ok"
+    assert "workspace" in wi.wave_status_string(3)
+    assert wi.wave_status_string(99) == "unknown status"
+
+
+def build_params(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, seq_len=4096,
+                kv_capacity=4112, segment_size=4096, clusters_per_segment=256, n_iters=5,
+                n_sink=4, n_recent=64)
+    base.update(kw)
+    return wi.wave_build_params(**base)
+
+
+def decode_params(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, seq_len=4097,
+                index_len=4096, kv_capacity=4112, n_clusters=256, n_sink=4, n_recent=64,
+                n_retrieve=6, scale=128 ** -0.5)
+    base.update(kw)
+    return wi.wave_decode_params(**base)
+
+
+def test_workspace_sizes_are_positive_and_grow_with_the_problem():
+    a = wi.wave_index_workspace_size(build_params())
+    b = wi.wave_index_workspace_size(build_params(batch=2))
+    assert 0 < a < b
+    c = wi.wave_decode_workspace_size(decode_params())
+    d = wi.wave_decode_workspace_size(decode_params(batch=3))
+    assert 0 < c < d
+    # independent of the current length: one workspace serves every decode step
+    assert wi.wave_decode_workspace_size(decode_params(seq_len=4100)) == c
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), 2), (dict(head_dim=0), 1), (dict(n_q_heads=30), 1),
+    (dict(batch=0), 1), (dict(seq_len=0), 1), (dict(kv_capacity=100), 1),
+    (dict(clusters_per_segment=5000), 1), (dict(segment_size=32768, clusters_per_segment=8), 2),
+    (dict(clusters_per_segment=4096, segment_size=8192), 2), (dict(n_iters=0), 1),
+    (dict(n_sink=-1), 1), (dict(n_sink=3000, n_recent=2000), 1),
+])
+def test_build_validation(kw, code):
+    with pytest.raises(wi.WaveError) as e:
+        wi.wave_index_workspace_size(build_params(**kw))
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), 2), (dict(n_q_heads=36, n_kv_heads=4), 2), (dict(n_q_heads=33), 1),
+    (dict(seq_len=4000), 1), (dict(seq_len=5000), 1), (dict(n_retrieve=-1), 1),
+    (dict(n_retrieve=257), 1), (dict(scale=0.0), 1), (dict(scale=float("nan")), 1),
+    (dict(n_clusters=0), 1), (dict(n_sink=4000, n_recent=200), 1),
+])
+def test_decode_validation(kw, code):
+    with pytest.raises(wi.WaveError) as e:
+        wi.wave_decode_workspace_size(decode_params(**kw))
+    assert e.value.code == code
+
+
+def test_build_rejects_null_small_workspace_and_aliasing_before_any_launch():
+    """Pointer checks run on the host before anything is enqueued (fake addresses are never
+    dereferenced because every call here fails validation)."""
+    lib = wi.library()
+    p = build_params()
+    ws = wi.wave_index_workspace_size(p)
+    cache = 1 * 8 * 4112 * 128 * 2
+    K, V, KO, VO, WS = 1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40
+    idx = wi.wave_index(6 << 40, 7 << 40, 8 << 40, 9 << 40, None, None, None, None)
+    call = lambda *a: lib.wave_index_build(ctypes.byref(p), *a)  # noqa: E731
+    assert call(None, V, KO, VO, ctypes.byref(idx), WS, ws, None) == 1
+    assert call(K, V, KO, VO, ctypes.byref(idx), WS, ws - 1, None) == 3
+    assert call(K, V, KO, VO, ctypes.byref(idx), None, ws, None) == 3
+    assert call(K, V, K + cache // 2, VO, ctypes.byref(idx), WS, ws, None) == 4
+    assert call(K, V, KO, KO + 256, ctypes.byref(idx), WS, ws, None) == 4
+    bad = wi.wave_index(6 << 40, None, 8 << 40, 9 << 40, None, None, None, None)
+    assert call(K, V, KO, VO, ctypes.byref(bad), WS, ws, None) == 1
+
+
+def test_decode_rejects_null_small_workspace_and_aliasing_before_any_launch():
+    lib = wi.library()
+    p = decode_params()
+    ws = wi.wave_decode_workspace_size(p)
+    Q, K, V, OUT, WS = 1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40
+    idx = wi.wave_index(6 << 40, 7 << 40, 8 << 40, 9 << 40, None, None, None, None)
+    call = lambda *a: lib.wave_decode_attention(ctypes.byref(p), *a)  # noqa: E731
+    assert call(Q, K, V, ctypes.byref(idx), None, None, None, WS, ws, None) == 1
+    assert call(Q, K, V, ctypes.byref(idx), OUT, None, None, WS, ws - 256, None) == 3
+    assert call(Q, K, V, ctypes.byref(idx), K + 512, None, None, WS, ws, None) == 4
+    assert call(Q, K, V, ctypes.byref(idx), OUT, OUT + 64, None, WS, ws, None) == 4
+    dense = lib.wave_dense_decode_attention
+    assert dense(ctypes.byref(p), Q, K, V, None, None, WS, ws, None) == 1
+    assert dense(ctypes.byref(p), Q, K, V, OUT, None, None, ws, None) == 3

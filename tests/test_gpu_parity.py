@@ -1,0 +1,279 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+All inputs come from the seeded generator (synth); every expected value comes from the oracle
+run on the CPU. Tolerances follow the protocol in wave_testlib.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import wave_oracle as wo
+import wave_testlib as tl
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = synth.WORKLOADS["tiny"]
+    x = synth.generate_layer(w)
+    layer = tl.Layer(x.k, x.v, w.context, w.segment_size, w.clusters_per_segment, w.n_iters,
+                     w.n_sink, w.n_recent, w.n_q_heads)
+    return w, x, layer
+
+
+def test_tiny_build_is_stepwise_identical_to_the_oracle(tiny):
+    """Every pass of every head: labels = oracle assignment from the GPU's own centroids
+    (ties 1e-4); next centroids = oracle update of those labels (1 bf16 ulp); seeds = oracle
+    seeds (1 ulp)."""
+    w, x, layer = tiny
+    K = wo.bf16_to_f64(x.k)
+    mus, labs = [], []
+    for t in range(1, w.n_iters + 1):
+        say(f"[tiny build] n_iters={t}")
+        idx = layer.build(T=t)
+        mus.append(tl.to_np16(idx.last_centroids))     # mu^(t-1)
+        labs.append(idx.labels.cpu().numpy())           # a^(t)
+    nflip = 0
+    for b in range(layer.B):
+        for g in range(layer.H):
+            for s, (lo, hi) in enumerate(tl.segment_ranges(layer)):
+                k = layer.kseg
+                Xhat = wo.normalise_rows(K[b, g, lo:hi])
+                seeds, nv = wo.kmeans_seeds(Xhat, k)
+                assert tl.bf16_close(mus[0][b, g, s * k:(s + 1) * k], seeds) <= 1
+                for t in range(w.n_iters):
+                    mu_prev = mus[t][b, g, s * k:(s + 1) * k]
+                    got = labs[t][b, g, lo:hi] - s * k
+                    nflip += tl.check_assignment(Xhat, mu_prev, nv, got)
+                    if t + 1 < w.n_iters:
+                        u = wo.kmeans_cluster_sums(Xhat, got, k)
+                        ref = wo.kmeans_update(u, np.bincount(got, minlength=k), mu_prev)
+                        d = tl.bf16_close(mus[t + 1][b, g, s * k:(s + 1) * k], ref)
+                        assert d <= 1, (b, g, s, t, d)
+    say(f"[tiny build] label differences resolved as ties: {nflip}")
+
+
+def test_tiny_index_matches_the_oracle_given_the_gpu_labels(tiny):
+    """Sizes, offsets, permutation and permuted rows bit-exact; means / value sums within
+    1 bf16 ulp; objective within 1e-4 relative; build bitwise reproducible."""
+    w, x, layer = tiny
+    say("[tiny index] build")
+    idx = layer.build()
+    k_out1 = tl.to_np16(layer.k_out)
+    again = layer.build()
+    assert np.array_equal(tl.to_np16(layer.k_out), k_out1)
+    for f in ("centroid_mean", "value_sum", "last_centroids"):
+        assert np.array_equal(tl.to_np16(getattr(idx, f)), tl.to_np16(getattr(again, f))), f
+    for f in ("cluster_size", "cluster_offset", "labels", "perm", "objective"):
+        assert np.array_equal(getattr(idx, f).cpu().numpy(), getattr(again, f).cpu().numpy()), f
+    labels = idx.labels.cpu().numpy()
+    k_out, v_out = tl.to_np16(layer.k_out), tl.to_np16(layer.v_out)
+    obj = idx.objective.cpu().numpy()
+    for b in range(layer.B):
+        for g in range(layer.H):
+            ref, ko, vo = wo.build_head(x.k[b, g], x.v[b, g], layer.L0, layer.S, layer.kseg,
+                                        w.n_iters, layer.n_sink, layer.n_recent,
+                                        labels_override=labels[b, g])
+            hi = tl.head_index(idx, b, g)
+            assert np.array_equal(hi.size, ref.size)
+            assert np.array_equal(hi.offset, ref.offset)
+            assert np.array_equal(hi.perm, ref.perm)
+            assert np.array_equal(hi.labels, ref.labels)
+            assert np.array_equal(k_out[b, g, :layer.L0], ko)
+            assert np.array_equal(v_out[b, g, :layer.L0], vo)
+            assert tl.bf16_close(hi.centroid_mean, ref.centroid_mean) <= 1
+            assert tl.bf16_close(hi.value_sum, ref.value_sum) <= 1
+            assert obj[b, g] == pytest.approx(ref.objective.sum(), rel=1e-4)
+
+
+def test_tiny_objective_close_to_the_oracle_run(tiny):
+    """The GPU's k-means (its own trajectory) reaches the oracle's own objective within 1e-4."""
+    w, x, layer = tiny
+    idx = layer.build()
+    obj = idx.objective.cpu().numpy()
+    for g in range(layer.H):
+        ref, _, _ = wo.build_head(x.k[0, g], x.v[0, g], layer.L0, layer.S, layer.kseg,
+                                  w.n_iters, layer.n_sink, layer.n_recent)
+        assert obj[0, g] == pytest.approx(ref.objective.sum(), rel=1e-4)
+
+
+def test_tiny_decode_every_step(tiny):
+    """16 decode steps, all heads: selection (ties 1e-4), outputs and lse within 2e-3."""
+    w, x, layer = tiny
+    idx = layer.build()
+    worst = 0.0
+    for s in range(w.steps):
+        L = layer.L0 + s + 1
+        say(f"[tiny decode] step {s} L={L} n_r={w.n_retrieve}")
+        out, lse, sel = layer.decode(idx, x.q[s], L, w.n_retrieve)
+        worst = max(worst, tl.oracle_decode_check(layer, idx, x.q[s], L, w.n_retrieve, out,
+                                                  lse, sel))
+    say(f"[tiny decode] worst row error {worst:.2e}")
+
+
+def test_decode_on_an_oracle_built_index(tiny):
+    """The index layout is the contract: an index built by the oracle and uploaded gives the
+    oracle's decode result on the GPU."""
+    t = tl.torch()
+    w, x, layer = tiny
+    lay = wo.build_layer(x.k, x.v, layer.L0, layer.S, layer.kseg, 2, layer.n_sink,
+                         layer.n_recent)
+    idx = wi_index_from_oracle(lay)
+    layer.k_out[:, :, :layer.L0] = tl.to_dev(lay.k_out)
+    layer.v_out[:, :, :layer.L0] = tl.to_dev(lay.v_out)
+    layer.k_out[:, :, layer.L0:] = layer.k[:, :, layer.L0:]
+    layer.v_out[:, :, layer.L0:] = layer.v[:, :, layer.L0:]
+    t.cuda.synchronize()
+    for s in (0, 7):
+        L = layer.L0 + s + 1
+        say(f"[oracle index decode] step {s}")
+        out, lse, sel = layer.decode(idx, x.q[s], L, 9)
+        tl.oracle_decode_check(layer, idx, x.q[s], L, 9, out, lse, sel)
+
+
+def wi_index_from_oracle(lay):
+    import kv_vector_index_amd as wi
+    t = tl.torch()
+    st = lambda f: lay.stacked(f)  # noqa: E731
+    return wi.IndexTensors(
+        tl.to_dev(st("centroid_mean")), tl.to_dev(st("value_sum")),
+        t.from_numpy(st("size").astype(np.int32)).cuda(),
+        t.from_numpy(st("offset").astype(np.int32)).cuda(),
+        t.from_numpy(st("labels").astype(np.int32)).cuda(),
+        t.from_numpy(st("perm").astype(np.int32)).cuda(),
+        tl.to_dev(st("last_centroids")), None)
+
+
+def test_retrieve_all_equals_dense_equals_full_attention(tiny):
+    w, x, layer = tiny
+    idx = layer.build()
+    L = layer.L0 + 5
+    say("[retrieve-all] decode + dense")
+    out, lse, _ = layer.decode(idx, x.q[4], L, layer.C)
+    dout, dlse, _ = layer.decode(idx, x.q[4], L, 0, dense=True)
+    kc, vc = tl.to_np16(layer.k_out), tl.to_np16(layer.v_out)
+    G = layer.Hq // layer.H
+    for g in range(layer.H):
+        ref, rlse = wo.full_attention(x.q[4][0, g * G:(g + 1) * G], kc[0, g], vc[0, g], L)
+        assert tl.row_rel_err(out[0, g * G:(g + 1) * G], ref) <= tl.OUT_TOL
+        assert tl.row_rel_err(dout[0, g * G:(g + 1) * G], ref) <= tl.OUT_TOL
+        assert np.all(np.abs(dlse[0, g * G:(g + 1) * G] - rlse) <= tl.OUT_TOL)
+        assert np.all(np.abs(lse[0, g * G:(g + 1) * G] - rlse) <= tl.OUT_TOL)
+
+
+def test_zero_query_gives_the_mean_value(tiny):
+    """q = 0: every logit is 0. Against the oracle on the same index (2e-3), and against the
+    closed form mean(v) within the error the bf16 value sums allow (each stored sum carries
+    a relative rounding error up to 2^-9, so 1e-2 of the row scale), with lse = ln L."""
+    w, x, layer = tiny
+    idx = layer.build()
+    L = layer.L0 + 3
+    q0 = np.zeros_like(x.q[0])
+    for n_r in (0, 6):
+        say(f"[zero query] n_r={n_r}")
+        out, lse, sel = layer.decode(idx, q0, L, n_r)
+        tl.oracle_decode_check(layer, idx, q0, L, n_r, out, lse, sel)
+        vmean = wo.bf16_to_f64(tl.to_np16(layer.v_out)[:, :, :L]).mean(axis=2)  # [B, H, d]
+        G = layer.Hq // layer.H
+        assert tl.row_rel_err(out, np.repeat(vmean, G, axis=1)) <= 1e-2
+        assert np.all(np.abs(lse - np.log(L)) <= 1e-4)
+
+
+CASES = {
+    # name: (ragged_layer kwargs, decode budgets)
+    "gqa4_ragged": (dict(), (0, 5, 40)),
+    "mha_g1": (dict(H=2, Hq=2), (3,)),
+    "qwen_g7_batch2": (dict(B=2, H=2, Hq=14, L0=600, S=200, kseg=13), (4, 26)),
+    "short_last_segment": (dict(L0=530, S=256, kseg=40, n_recent=3), (7,)),
+    "no_steady_zone": (dict(n_sink=0, n_recent=0, steps=1), (2,)),
+    "one_cluster_per_segment": (dict(kseg=1, S=128), (1,)),
+    "singletons": (dict(L0=300, S=64, kseg=64, n_sink=1, n_recent=2), (0, 11)),
+    "many_clusters": (dict(L0=2200, S=1024, kseg=300, T=4), (12, 300)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_shapes_and_edge_cases(case):
+    kw, budgets = CASES[case]
+    rng = np.random.default_rng(abs(hash(case)) % 2 ** 32)
+    layer, q = tl.ragged_layer(rng, **kw)
+    say(f"[edge {case}] build B={layer.B} H={layer.H} Hq={layer.Hq} L0={layer.L0} "
+        f"S={layer.S} kseg={layer.kseg}")
+    idx = layer.build()
+    labels = idx.labels.cpu().numpy()
+    K = wo.bf16_to_f64(layer.k_np)
+    last = tl.to_np16(idx.last_centroids)
+    for b in range(layer.B):
+        for g in range(layer.H):
+            for s, (lo, hi) in enumerate(tl.segment_ranges(layer)):
+                k = layer.kseg
+                Xhat = wo.normalise_rows(K[b, g, lo:hi])
+                tl.check_assignment(Xhat, last[b, g, s * k:(s + 1) * k], tl.n_valid(k, hi - lo),
+                                    labels[b, g, lo:hi] - s * k)
+            ref, ko, _ = wo.build_head(layer.k_np[b, g], layer.v_np[b, g], layer.L0, layer.S,
+                                       layer.kseg, layer.T, layer.n_sink, layer.n_recent,
+                                       labels_override=labels[b, g])
+            hi_ = tl.head_index(idx, b, g)
+            assert np.array_equal(hi_.size, ref.size) and np.array_equal(hi_.offset, ref.offset)
+            assert np.array_equal(hi_.perm, ref.perm)
+            assert np.array_equal(tl.to_np16(layer.k_out)[b, g, :layer.L0], ko)
+            assert tl.bf16_close(hi_.centroid_mean, ref.centroid_mean) <= 1
+            assert tl.bf16_close(hi_.value_sum, ref.value_sum) <= 1
+    for s in range(q.shape[0]):
+        L = layer.L0 + s + 1
+        for n_r in budgets:
+            n_r = min(n_r, layer.C)
+            say(f"[edge {case}] decode step {s} n_r={n_r}")
+            out, lse, sel = layer.decode(idx, q[s], L, n_r)
+            tl.oracle_decode_check(layer, idx, q[s], L, n_r, out, lse, sel)
+        dout, dlse, _ = layer.decode(idx, q[s], L, 0, dense=True)
+        kc, vc = tl.to_np16(layer.k_out), tl.to_np16(layer.v_out)
+        G = layer.Hq // layer.H
+        for b in range(layer.B):
+            for g in range(layer.H):
+                ref, _ = wo.full_attention(q[s][b, g * G:(g + 1) * G], kc[b, g], vc[b, g], L)
+                assert tl.row_rel_err(dout[b, g * G:(g + 1) * G], ref) <= tl.OUT_TOL
+
+
+@pytest.mark.slow
+def test_llama128k_sampled_parity():
+    """Full 128K single-layer workload, launched as the bench launches it: sampled segments
+    checked step-wise at the last pass and through the finalise, and two decode steps checked
+    on every head."""
+    w = synth.WORKLOADS["llama128k"]
+    say("[128k] generate")
+    x = synth.generate_layer(w, rows=w.context + 2)
+    layer = tl.Layer(x.k, x.v, w.context, w.segment_size, w.clusters_per_segment, w.n_iters,
+                     w.n_sink, w.n_recent, w.n_q_heads)
+    say("[128k] build")
+    idx = layer.build()
+    labels = idx.labels.cpu().numpy()
+    last = tl.to_np16(idx.last_centroids)
+    k_out = tl.to_np16(layer.k_out)
+    segs = tl.segment_ranges(layer)
+    rng = np.random.default_rng(5)
+    for (g, s) in [(0, 0), (3, 7), (7, len(segs) - 1)] + [
+            (int(rng.integers(8)), int(rng.integers(len(segs)))) for _ in range(3)]:
+        lo, hi = segs[s]
+        k = layer.kseg
+        say(f"[128k] check head {g} segment {s}")
+        Xhat = wo.normalise_rows(wo.bf16_to_f64(x.k[0, g, lo:hi]))
+        tl.check_assignment(Xhat, last[0, g, s * k:(s + 1) * k], tl.n_valid(k, hi - lo),
+                            labels[0, g, lo:hi] - s * k)
+        size, off, order = wo.finalise_segment(lo, labels[0, g, lo:hi] - s * k, k)
+        assert np.array_equal(idx.cluster_size[0, g, s * k:(s + 1) * k].cpu().numpy(), size)
+        assert np.array_equal(idx.cluster_offset[0, g, s * k:(s + 1) * k].cpu().numpy(), off)
+        assert np.array_equal(k_out[0, g, lo:hi], x.k[0, g, order])
+    for s in range(2):
+        L = layer.L0 + s + 1
+        say(f"[128k] decode step {s}")
+        out, lse, sel = layer.decode(idx, x.q[s], L, w.n_retrieve)
+        tl.oracle_decode_check(layer, idx, x.q[s], L, w.n_retrieve, out, lse, sel)
