@@ -86,7 +86,7 @@ def main():
     scale = 1.0 / math.sqrt(d)
     dps = [wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
                                  w.n_recent, nr, scale) for s in range(nds)]
-    dws = torch.empty(wi.wave_decode_workspace_size(dps[0]), dtype=torch.uint8, device="cuda")
+    dws = wi.alloc_decode_workspace(dps[0])
     out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
     lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
     sel = torch.empty(nds, B, H, max(nr, 1), dtype=torch.int32, device="cuda")
@@ -113,7 +113,7 @@ def main():
         one_step(None, None)
     torch.cuda.synchronize()
     bevs = [events(n_build_ev) for _ in range(args.steps)]
-    devs = [[events(4) for _ in range(nds)] for _ in range(args.steps)]
+    devs = [[events(2) for _ in range(nds)] for _ in range(args.steps)]
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
@@ -138,10 +138,7 @@ def main():
                 update_ms.append(el(b[i], b[i + 1]))
                 i += 1
         fin_ms = el(b[i], b[i + 1])
-    call_ms = [el(e[0], e[3]) for st in devs for e in st]
-    stream_ms = [el(e[0], e[1]) for st in devs for e in st]
-    select_ms = [el(e[1], e[2]) for st in devs for e in st]
-    retr_ms = [el(e[2], e[3]) for st in devs for e in st]
+    call_ms = [el(e[0], e[1]) for st in devs for e in st]   # one persistent decode kernel
     med = statistics.median
 
     # ---- algorithmic work (per decode call and per assignment launch)
@@ -160,8 +157,6 @@ def main():
     E = float(np.mean(e_tok))
     per_bh = 2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d
     call_bytes = per_bh * B * H
-    steady_tok = w.n_sink + w.n_recent + (nds + 1) / 2.0
-    stream_bytes = (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * steady_tok + 2 * G * d) * B * H
     n_idx = [max(0, min((s + 1) * w.segment_size, L0 - w.n_recent) - max(s * w.segment_size,
                                                                            w.n_sink))
              for s in range(w.n_segments)]
@@ -170,24 +165,22 @@ def main():
     decode_tok_s = B / (med(call_ms) * 1e-3)
     build_tok_s = B * L0 / (med(build_ms) * 1e-3)
     call_gbs = call_bytes / (med(call_ms) * 1e-3) / 1e9
-    stream_gbs = stream_bytes / (med(stream_ms) * 1e-3) / 1e9
     assign_tfs = assign_flop / (statistics.mean(assign_ms) * 1e-3) / 1e12
-    per_step = {"assign": T * statistics.mean(assign_ms),
-                "decode_stream": nds * statistics.mean(stream_ms),
-                "decode_select": nds * statistics.mean(select_ms),
-                "decode_retrieved": nds * statistics.mean(retr_ms)}
+    per_step = {"k_assign": T * statistics.mean(assign_ms),
+                "k_decode": nds * statistics.mean(call_ms)}
     dominant = max(per_step, key=per_step.get)
     roof_assign = {"kernel": "k_assign", "bound": "mfma", "achieved": round(assign_tfs, 2),
                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                    "frac": round(assign_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None,
                    "flop_per_launch": assign_flop,
                    "avg_launch_us": round(statistics.mean(assign_ms) * 1e3, 2)}
-    roof_stream = {"kernel": "k_decode_stream", "bound": "hbm", "achieved": round(stream_gbs, 1),
+    roof_decode = {"kernel": "k_decode", "bound": "hbm", "achieved": round(call_gbs, 1),
                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                   "frac": round(stream_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                   "bytes_per_launch": stream_bytes,
-                   "avg_launch_us": round(med(stream_ms) * 1e3, 2)}
-    roof = roof_assign if dominant == "assign" else roof_stream
+                   "frac": round(call_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                   "bytes_per_launch": call_bytes,
+                   "avg_launch_us": round(statistics.mean(call_ms) * 1e3, 2),
+                   "median_launch_us": round(med(call_ms) * 1e3, 2)}
+    roof = roof_assign if dominant == "k_assign" else roof_decode
 
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s at 128K/1M ctx; index-build tok/s",
@@ -210,13 +203,11 @@ def main():
                       "sort": round(statistics.mean(sort_ms) * 1e3, 2),
                       "update": round(statistics.mean(update_ms) * 1e3, 2) if update_ms else None,
                       "finalise": round(fin_ms * 1e3, 2),
-                      "decode_stream": round(med(stream_ms) * 1e3, 2),
-                      "decode_select": round(med(select_ms) * 1e3, 2),
-                      "decode_retrieved": round(med(retr_ms) * 1e3, 2)},
+                      "decode": round(med(call_ms) * 1e3, 2)},
         "dominant_kernel": dominant,
         "roofline": roof,
         "roofline_assign": roof_assign,
-        "roofline_decode_stream": roof_stream,
+        "roofline_decode": roof_decode,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_decode_steps)

@@ -137,6 +137,16 @@ typedef struct {
 /* Bytes of decode workspace for these parameters (host only). */
 wave_status wave_decode_workspace_size(const wave_decode_params* p, size_t* bytes);
 
+/* Prepare a decode workspace: zero its control words (enqueued on stream, by a kernel, so
+ * it may be captured in a graph). Needed once after allocating the workspace and again
+ * before reusing it with a different batch, n_kv_heads, n_clusters, kv_capacity,
+ * index_len or n_retrieve; every decode call that completes leaves the control words
+ * zero again, so consecutive steps of one shape need no further preparation. The size
+ * (wave_decode_workspace_size) does not depend on seq_len, so one workspace serves every
+ * step up to kv_capacity. */
+wave_status wave_decode_workspace_init(const wave_decode_params* p, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
 /* One decode step.
  *   q          bf16 [B, Hq, d]
  *   k_cache, v_cache  bf16 [B, Hkv, Lcap, d]: k_out / v_out of the build, with decode
@@ -145,8 +155,8 @@ wave_status wave_decode_workspace_size(const wave_decode_params* p, size_t* byte
  *   out        fp32 [B, Hq, d]
  *   lse        optional fp32 [B, Hq]
  *   selected   optional int32 [B, Hkv, n_retrieve]: R in ascending id order, -1 padded
- *   workspace  at least wave_decode_workspace_size bytes (no clearing needed; it only
- *              depends on the shape, so one workspace serves every step up to Lcap). */
+ *   workspace  at least wave_decode_workspace_size bytes, prepared once with
+ *              wave_decode_workspace_init (see there). */
 wave_status wave_decode_attention(const wave_decode_params* p, const void* q,
                                   const void* k_cache, const void* v_cache,
                                   const wave_index* idx, float* out, float* lse,

@@ -102,7 +102,7 @@ size_t layout_build(const wave_build_params* p, const BuildShape& sh, void* base
 // ---------------------------------------------------------------- decode
 
 struct DecodeShape {
-  int G, nEst, nSteadyMax, nB, nBDense, rcap;
+  int G, nS, nStMax, nB, nBDense, rcap;
   int64_t BH, cache_elems;
 };
 
@@ -119,7 +119,7 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   if (p->index_len < 1 || p->seq_len < p->index_len || p->kv_capacity < p->seq_len)
     return WAVE_ERR_INVALID_ARG;
   if (p->kv_capacity > (int64_t)1 << 30) return WAVE_ERR_UNSUPPORTED;
-  if (p->n_clusters < 1 || p->n_clusters > INT32_MAX / 2) return WAVE_ERR_INVALID_ARG;
+  if (p->n_clusters < 1 || p->n_clusters > (1 << 26)) return WAVE_ERR_INVALID_ARG;
   if (p->n_sink < 0 || p->n_recent < 0) return WAVE_ERR_INVALID_ARG;
   if ((int64_t)p->n_sink + p->n_recent > p->index_len) return WAVE_ERR_INVALID_ARG;
   if (p->n_retrieve < 0 || p->n_retrieve > p->n_clusters) return WAVE_ERR_INVALID_ARG;
@@ -128,46 +128,63 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   if (!mul_ok(p->batch, p->n_kv_heads, &bh) || !mul_ok(bh, p->kv_capacity, &rows) ||
       !mul_ok(rows, wave::kHeadDim, &elems) || elems > INT64_MAX / 4)
     return WAVE_ERR_INVALID_ARG;
+  if (bh > 65536) return WAVE_ERR_UNSUPPORTED;
   sh->G = G;
   sh->BH = bh;
   sh->cache_elems = elems;
-  sh->nEst = (p->n_clusters + wave::kEstChunk - 1) / wave::kEstChunk;
+  sh->nS = (p->n_clusters + wave::kChunk - 1) / wave::kChunk;
   const int64_t steady_max = (int64_t)p->n_sink + p->n_recent + (p->kv_capacity - p->index_len);
-  sh->nSteadyMax = (int)((steady_max + wave::kTokChunk - 1) / wave::kTokChunk);
-  // retrieved-token workgroups: about 256 tokens each at the average cluster size
+  sh->nStMax = (int)((steady_max + wave::kTokChunk - 1) / wave::kTokChunk);
+  // retrieved-token work items: about 256 tokens each at the average cluster size
   const int64_t indexed = p->index_len - p->n_sink - p->n_recent;
   const int64_t avg = indexed > p->n_clusters ? indexed / p->n_clusters : 1;
-  sh->nB = clampi(((int64_t)p->n_retrieve * avg + 255) / 256, 1, 64);
+  sh->nB = clampi(((int64_t)p->n_retrieve * avg + wave::kTokPerItem - 1) / wave::kTokPerItem,
+                  1, 256);
   sh->nBDense = clampi((p->kv_capacity + 1023) / 1024, 1, 512);
   sh->rcap = p->n_retrieve > 0 ? p->n_retrieve : 1;
   return WAVE_OK;
 }
 
+// Decode workspace: control words first (they must be zero when a call starts), then data.
+// Returns the total size; *ctl_bytes receives the size of the control region.
 size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* base,
-                     wave::DecodeArgs* a) {
+                     wave::DecodeArgs* a, size_t* ctl_bytes = nullptr) {
   Carver cv(base);
-  const size_t BH = (size_t)sh.BH, G = (size_t)sh.G, PS = wave::kPartStride;
-  const int nAmax = sh.nEst + sh.nSteadyMax;
-  const int nBmax = sh.nB > sh.nBDense ? sh.nB : sh.nBDense;
-  uint32_t* counter = cv.take<uint32_t>(BH);
-  int32_t* nsel = cv.take<int32_t>(BH);
-  int32_t* ntok = cv.take<int32_t>(BH);
-  float* shat = cv.take<float>(BH * (size_t)p->n_clusters);
-  float* partA = cv.take<float>(BH * (size_t)nAmax * G * PS);
-  float* mergedA = cv.take<float>(BH * G * PS);
-  float* partB = cv.take<float>(BH * (size_t)nBmax * G * PS);
+  const size_t BH = (size_t)sh.BH, G = (size_t)sh.G, C = (size_t)p->n_clusters;
+  wave::DecodeCtl* ctl = cv.take<wave::DecodeCtl>(1);
+  uint32_t* score_done = cv.take<uint32_t>(BH);
+  uint32_t* part_done = cv.take<uint32_t>(BH);
+  uint32_t* sel_ready = cv.take<uint32_t>(BH);
+  uint32_t* chunk_ready = cv.take<uint32_t>(BH * sh.nS);
+  uint32_t* hist = cv.take<uint32_t>(BH * wave::kHistBins);
+  if (ctl_bytes) *ctl_bytes = cv.off;
+  const size_t nP = (size_t)sh.nStMax + sh.nS + sh.nB;
+  const size_t nPmax = nP > (size_t)sh.nBDense ? nP : (size_t)sh.nBDense;
+  float* scores = cv.take<float>(BH * C * G);
+  float* shat = cv.take<float>(BH * C);
+  uint32_t* cand_key = cv.take<uint32_t>(BH * C);
+  int32_t* cand_id = cv.take<int32_t>(BH * C);
   int32_t* sel = cv.take<int32_t>(BH * (size_t)sh.rcap);
   int32_t* slots = cv.take<int32_t>(BH * (size_t)p->index_len);
+  int32_t* nsel = cv.take<int32_t>(BH);
+  int32_t* ntok = cv.take<int32_t>(BH);
+  float* part = cv.take<float>(BH * nPmax * G * wave::kPartStride);
   if (a) {
-    a->counter = counter;
-    a->nsel = nsel;
-    a->ntok = ntok;
+    a->ctl = ctl;
+    a->score_done = score_done;
+    a->part_done = part_done;
+    a->sel_ready = sel_ready;
+    a->chunk_ready = chunk_ready;
+    a->hist = hist;
+    a->scores = scores;
     a->shat = shat;
-    a->partA = partA;
-    a->mergedA = mergedA;
-    a->partB = partB;
+    a->cand_key = cand_key;
+    a->cand_id = cand_id;
     a->sel = sel;
     a->slots = slots;
+    a->nsel = nsel;
+    a->ntok = ntok;
+    a->part = part;
   }
   return cv.off;
 }
@@ -350,14 +367,34 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   a.lse = lse;
   a.selected = p->n_retrieve > 0 ? selected : nullptr;
   const int64_t n_steady = (int64_t)p->n_sink + p->n_recent + (p->seq_len - p->index_len);
-  a.nEst = sh.nEst;
-  a.nSteady = (int)((n_steady + wave::kTokChunk - 1) / wave::kTokChunk);
-  a.nA = a.nEst + a.nSteady;
+  a.nS = sh.nS;
+  a.nSt = (int)((n_steady + wave::kTokChunk - 1) / wave::kTokChunk);
   a.nB = sh.nB;
+  a.nP = a.nSt + a.nS + a.nB;
+  a.total_items = (uint32_t)(sh.BH * (2 * (int64_t)a.nS + a.nSt + a.nB));
+  a.local_select = p->n_clusters <= wave::kLocalSelMax ? 1 : 0;
+  if (a.local_select) {
+    const size_t per = ((size_t)p->n_clusters + wave::kDecThreads - 1) / wave::kDecThreads;
+    const size_t keys = per * wave::kDecThreads;
+    a.dyn_lds = (keys + (keys + 1) / 2 + 3 * (size_t)wave::kWin) * sizeof(uint32_t);
+  } else {
+    a.dyn_lds = 0;
+  }
   return wave::launch_decode(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
 }
 
 }  // namespace
+
+wave_status wave_decode_workspace_init(const wave_decode_params* p, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  DecodeShape sh;
+  wave_status st = check_decode(p, &sh);
+  if (st != WAVE_OK) return st;
+  size_t ctl_bytes = 0;
+  const size_t need = layout_decode(p, sh, nullptr, nullptr, &ctl_bytes);
+  if (!workspace || workspace_bytes < need) return WAVE_ERR_WORKSPACE;
+  return wave::launch_zero(workspace, ctl_bytes, stream) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
+}
 
 wave_status wave_decode_attention(const wave_decode_params* p, const void* q, const void* k_cache,
                                   const void* v_cache, const wave_index* idx, float* out,
@@ -413,6 +450,7 @@ wave_status wave_dense_decode_attention(const wave_decode_params* p, const void*
   a.out = out;
   a.lse = lse;
   a.nB = sh.nBDense;
+  a.nP = sh.nBDense;
   return wave::launch_dense_decode(a, stream, nullptr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
 }
 

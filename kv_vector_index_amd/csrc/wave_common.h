@@ -71,4 +71,18 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Data exchanged between workgroups of one kernel: device-coherent (sc1) loads and stores,
+// seen consistently by every XCD without writing back or invalidating whole L2 caches.
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's earlier vector-memory operations have completed (device-coherent
+// stores acknowledged); also a compiler barrier for memory accesses.
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace wave

@@ -125,6 +125,11 @@ def test_decode_rejects_null_small_workspace_and_aliasing_before_any_launch():
     assert call(Q, K, V, ctypes.byref(idx), OUT, None, None, WS, ws - 256, None) == 3
     assert call(Q, K, V, ctypes.byref(idx), K + 512, None, None, WS, ws, None) == 4
     assert call(Q, K, V, ctypes.byref(idx), OUT, OUT + 64, None, WS, ws, None) == 4
+    init = lib.wave_decode_workspace_init
+    assert init(ctypes.byref(p), None, ws, None) == 3
+    assert init(ctypes.byref(p), WS, ws - 1, None) == 3
+    bad = decode_params(n_retrieve=-1)
+    assert init(ctypes.byref(bad), WS, ws, None) == 1
     dense = lib.wave_dense_decode_attention
     assert dense(ctypes.byref(p), Q, K, V, None, None, WS, ws, None) == 1
     assert dense(ctypes.byref(p), Q, K, V, OUT, None, None, ws, None) == 3

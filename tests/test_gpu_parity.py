@@ -107,16 +107,34 @@ def test_tiny_objective_close_to_the_oracle_run(tiny):
 
 def test_tiny_decode_every_step(tiny):
     """16 decode steps, all heads: selection (ties 1e-4), outputs and lse within 2e-3."""
+    import kv_vector_index_amd as wi
     w, x, layer = tiny
     idx = layer.build()
     worst = 0.0
+    # one workspace for every step: each call must leave its control words cleared
+    ws = wi.alloc_decode_workspace(layer.decode_params(layer.L0 + 1, w.n_retrieve))
     for s in range(w.steps):
         L = layer.L0 + s + 1
         say(f"[tiny decode] step {s} L={L} n_r={w.n_retrieve}")
-        out, lse, sel = layer.decode(idx, x.q[s], L, w.n_retrieve)
+        out, lse, sel = layer.decode(idx, x.q[s], L, w.n_retrieve, ws=ws)
         worst = max(worst, tl.oracle_decode_check(layer, idx, x.q[s], L, w.n_retrieve, out,
                                                   lse, sel))
     say(f"[tiny decode] worst row error {worst:.2e}")
+
+
+def test_workspace_reuse_across_budgets(tiny):
+    """A workspace re-prepared for another budget gives the same results as a fresh one."""
+    import kv_vector_index_amd as wi
+    w, x, layer = tiny
+    idx = layer.build()
+    L = layer.L0 + 2
+    ws = wi.alloc_decode_workspace(layer.decode_params(L, 11))   # sized for the largest
+    for n_r in (3, 11, 3, 0, 11):
+        wi.wave_decode_workspace_init(layer.decode_params(L, n_r), ws)
+        out, lse, sel = layer.decode(idx, x.q[1], L, n_r, ws=ws)
+        out2, lse2, sel2 = layer.decode(idx, x.q[1], L, n_r)
+        assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+        assert np.array_equal(sel, sel2)
 
 
 def test_decode_on_an_oracle_built_index(tiny):

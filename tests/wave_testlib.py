@@ -108,7 +108,7 @@ class Layer:
         t = torch()
         p = self.decode_params(L, n_r)
         if ws is None:
-            ws = t.empty(wi.wave_decode_workspace_size(p), dtype=t.uint8, device="cuda")
+            ws = wi.alloc_decode_workspace(p)
         q = to_dev(q_np)
         out = t.empty(self.B, self.Hq, 128, dtype=t.float32, device="cuda")
         lse = t.empty(self.B, self.Hq, dtype=t.float32, device="cuda")
