@@ -93,6 +93,8 @@ def main():
     flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
 
     n_build_ev = 3 * T + 4
+    # decode kernels: stream, [select when C > 16384], retrieve (one event before each + end)
+    n_dec_ev = 3 if C <= 16384 else 4
     def events(n):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for e in ev:
@@ -113,7 +115,7 @@ def main():
         one_step(None, None)
     torch.cuda.synchronize()
     bevs = [events(n_build_ev) for _ in range(args.steps)]
-    devs = [[events(2) for _ in range(nds)] for _ in range(args.steps)]
+    devs = [[events(n_dec_ev) for _ in range(nds)] for _ in range(args.steps)]
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
@@ -138,7 +140,10 @@ def main():
                 update_ms.append(el(b[i], b[i + 1]))
                 i += 1
         fin_ms = el(b[i], b[i + 1])
-    call_ms = [el(e[0], e[1]) for st in devs for e in st]   # one persistent decode kernel
+    call_ms = [el(e[0], e[-1]) for st in devs for e in st]
+    stream_ms = [el(e[0], e[1]) for st in devs for e in st]
+    select_ms = [el(e[1], e[2]) for st in devs for e in st] if n_dec_ev == 4 else []
+    retrieve_ms = [el(e[-2], e[-1]) for st in devs for e in st]
     med = statistics.median
 
     # ---- algorithmic work (per decode call and per assignment launch)
@@ -157,6 +162,10 @@ def main():
     E = float(np.mean(e_tok))
     per_bh = 2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d
     call_bytes = per_bh * B * H
+    # the stream kernel's share: centroids, sizes, unretrieved value sums, steady rows, q
+    steady_mean = w.n_sink + w.n_recent + (nds + 1) / 2
+    stream_bytes = (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * steady_mean
+                    + 2 * G * d) * B * H
     n_idx = [max(0, min((s + 1) * w.segment_size, L0 - w.n_recent) - max(s * w.segment_size,
                                                                            w.n_sink))
              for s in range(w.n_segments)]
@@ -166,21 +175,28 @@ def main():
     build_tok_s = B * L0 / (med(build_ms) * 1e-3)
     call_gbs = call_bytes / (med(call_ms) * 1e-3) / 1e9
     assign_tfs = assign_flop / (statistics.mean(assign_ms) * 1e-3) / 1e12
+    stream_gbs = stream_bytes / (statistics.mean(stream_ms) * 1e-3) / 1e9
     per_step = {"k_assign": T * statistics.mean(assign_ms),
-                "k_decode": nds * statistics.mean(call_ms)}
+                "k_dec_stream": nds * statistics.mean(stream_ms),
+                "k_dec_retrieve": nds * statistics.mean(retrieve_ms)}
     dominant = max(per_step, key=per_step.get)
     roof_assign = {"kernel": "k_assign", "bound": "mfma", "achieved": round(assign_tfs, 2),
                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                    "frac": round(assign_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None,
                    "flop_per_launch": assign_flop,
                    "avg_launch_us": round(statistics.mean(assign_ms) * 1e3, 2)}
-    roof_decode = {"kernel": "k_decode", "bound": "hbm", "achieved": round(call_gbs, 1),
-                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    roof_decode = {"kernel": "decode call (all kernels)", "bound": "hbm",
+                   "achieved": round(call_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                    "frac": round(call_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                    "bytes_per_launch": call_bytes,
                    "avg_launch_us": round(statistics.mean(call_ms) * 1e3, 2),
                    "median_launch_us": round(med(call_ms) * 1e3, 2)}
-    roof = roof_assign if dominant == "k_assign" else roof_decode
+    roof_stream = {"kernel": "k_dec_stream", "bound": "hbm", "achieved": round(stream_gbs, 1),
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": round(stream_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                   "bytes_per_launch": stream_bytes,
+                   "avg_launch_us": round(statistics.mean(stream_ms) * 1e3, 2)}
+    roof = {"k_assign": roof_assign, "k_dec_stream": roof_stream}.get(dominant, roof_decode)
 
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s at 128K/1M ctx; index-build tok/s",
@@ -203,11 +219,16 @@ def main():
                       "sort": round(statistics.mean(sort_ms) * 1e3, 2),
                       "update": round(statistics.mean(update_ms) * 1e3, 2) if update_ms else None,
                       "finalise": round(fin_ms * 1e3, 2),
-                      "decode": round(med(call_ms) * 1e3, 2)},
+                      "decode_call": round(med(call_ms) * 1e3, 2),
+                      "dec_stream": round(statistics.mean(stream_ms) * 1e3, 2),
+                      "dec_select": round(statistics.mean(select_ms) * 1e3, 2) if select_ms
+                      else None,
+                      "dec_retrieve": round(statistics.mean(retrieve_ms) * 1e3, 2)},
         "dominant_kernel": dominant,
         "roofline": roof,
         "roofline_assign": roof_assign,
         "roofline_decode": roof_decode,
+        "roofline_dec_stream": roof_stream,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_decode_steps)

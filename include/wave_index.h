@@ -134,18 +134,11 @@ typedef struct {
   float scale;           /* > 0, usually 1/sqrt(d) */
 } wave_decode_params;
 
-/* Bytes of decode workspace for these parameters (host only). */
+/* Bytes of decode workspace for these parameters (host only). The workspace needs no
+ * clearing or other preparation, and a workspace of this size also serves any call whose
+ * parameters need no more (the size does not depend on seq_len, so one workspace serves
+ * every step up to kv_capacity). Calls that share a workspace must not overlap in time. */
 wave_status wave_decode_workspace_size(const wave_decode_params* p, size_t* bytes);
-
-/* Prepare a decode workspace: zero its control words (enqueued on stream, by a kernel, so
- * it may be captured in a graph). Needed once after allocating the workspace and again
- * before reusing it with a different batch, n_kv_heads, n_clusters, kv_capacity,
- * index_len or n_retrieve; every decode call that completes leaves the control words
- * zero again, so consecutive steps of one shape need no further preparation. The size
- * (wave_decode_workspace_size) does not depend on seq_len, so one workspace serves every
- * step up to kv_capacity. */
-wave_status wave_decode_workspace_init(const wave_decode_params* p, void* workspace,
-                                       size_t workspace_bytes, hipStream_t stream);
 
 /* One decode step.
  *   q          bf16 [B, Hq, d]
@@ -155,8 +148,8 @@ wave_status wave_decode_workspace_init(const wave_decode_params* p, void* worksp
  *   out        fp32 [B, Hq, d]
  *   lse        optional fp32 [B, Hq]
  *   selected   optional int32 [B, Hkv, n_retrieve]: R in ascending id order, -1 padded
- *   workspace  at least wave_decode_workspace_size bytes, prepared once with
- *              wave_decode_workspace_init (see there). */
+ *   workspace  at least wave_decode_workspace_size bytes (no clearing needed).
+ * n_clusters is at most 65536 (WAVE_ERR_UNSUPPORTED above). */
 wave_status wave_decode_attention(const wave_decode_params* p, const void* q,
                                   const void* k_cache, const void* v_cache,
                                   const wave_index* idx, float* out, float* lse,
@@ -179,7 +172,8 @@ wave_status wave_dense_decode_attention(const wave_decode_params* p, const void*
  * events[i + 1]. At most `capacity` events are recorded; `recorded` returns the count.
  * Kernel order, build: key norms (if any indexed token), seeds, then per pass: assign,
  * sort, and (all passes but the last) update; then finalise, steady-row copy (if
- * n_sink + n_recent > 0), objective (if requested). Decode: stream, select, retrieved.
+ * n_sink + n_recent > 0), objective (if requested). Decode: stream, select (only when
+ * n_clusters > 16384), retrieve.
  */
 typedef struct {
   hipEvent_t* events;   /* capacity events created by the caller (hipEventCreate) */

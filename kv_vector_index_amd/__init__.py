@@ -20,14 +20,14 @@ __all__ = [
     "wave_status_string", "wave_index_workspace_size", "wave_index_build",
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
     "IndexTensors", "alloc_index", "EXPORTED_SYMBOLS", "LIB_PATH", "wave_trace",
-    "wave_decode_workspace_init", "alloc_decode_workspace",
+    "alloc_decode_workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libwave_index.so")
 EXPORTED_SYMBOLS = (
     "wave_status_string", "wave_index_workspace_size", "wave_index_build",
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
-    "wave_index_build_traced", "wave_decode_attention_traced", "wave_decode_workspace_init",
+    "wave_index_build_traced", "wave_decode_attention_traced",
 )
 STATUS = {0: "WAVE_OK", 1: "WAVE_ERR_INVALID_ARG", 2: "WAVE_ERR_UNSUPPORTED",
           3: "WAVE_ERR_WORKSPACE", 4: "WAVE_ERR_ALIAS", 5: "WAVE_ERR_HIP"}
@@ -89,7 +89,6 @@ def library() -> ctypes.CDLL:
         lib.wave_index_build.argtypes = [P(wave_build_params), vp, vp, vp, vp, P(wave_index),
                                          vp, sz, vp]
         lib.wave_decode_workspace_size.argtypes = [P(wave_decode_params), P(sz)]
-        lib.wave_decode_workspace_init.argtypes = [P(wave_decode_params), vp, sz, vp]
         lib.wave_decode_attention.argtypes = [P(wave_decode_params), vp, vp, vp, P(wave_index),
                                               vp, vp, vp, vp, sz, vp]
         lib.wave_dense_decode_attention.argtypes = [P(wave_decode_params), vp, vp, vp, vp, vp,
@@ -136,19 +135,10 @@ def wave_decode_workspace_size(p: wave_decode_params) -> int:
     return n.value
 
 
-def wave_decode_workspace_init(p: wave_decode_params, workspace, stream=None) -> None:
-    """Zero the control words of a decode workspace (once per allocation / shape)."""
-    _check("wave_decode_workspace_init", library().wave_decode_workspace_init(
-        ctypes.byref(p), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
-
-
 def alloc_decode_workspace(p: wave_decode_params, device="cuda"):
-    """A decode workspace for this shape, ready for use (allocated with torch, prepared)."""
+    """A decode workspace for this shape (allocated with torch; needs no clearing)."""
     import torch
-    ws = torch.empty(wave_decode_workspace_size(p), dtype=torch.uint8, device=device)
-    wave_decode_workspace_init(p, ws)
-    return ws
+    return torch.empty(wave_decode_workspace_size(p), dtype=torch.uint8, device=device)
 
 
 @dataclass

@@ -119,7 +119,8 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   if (p->index_len < 1 || p->seq_len < p->index_len || p->kv_capacity < p->seq_len)
     return WAVE_ERR_INVALID_ARG;
   if (p->kv_capacity > (int64_t)1 << 30) return WAVE_ERR_UNSUPPORTED;
-  if (p->n_clusters < 1 || p->n_clusters > (1 << 26)) return WAVE_ERR_INVALID_ARG;
+  if (p->n_clusters < 1) return WAVE_ERR_INVALID_ARG;
+  if (p->n_clusters > wave::kMaxClusters) return WAVE_ERR_UNSUPPORTED;
   if (p->n_sink < 0 || p->n_recent < 0) return WAVE_ERR_INVALID_ARG;
   if ((int64_t)p->n_sink + p->n_recent > p->index_len) return WAVE_ERR_INVALID_ARG;
   if (p->n_retrieve < 0 || p->n_retrieve > p->n_clusters) return WAVE_ERR_INVALID_ARG;
@@ -145,45 +146,28 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   return WAVE_OK;
 }
 
-// Decode workspace: control words first (they must be zero when a call starts), then data.
-// Returns the total size; *ctl_bytes receives the size of the control region.
+// Decode workspace (no preparation needed: the stream kernel clears the arrival counters
+// of the retrieve kernel in every call). Returns the total size.
 size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* base,
-                     wave::DecodeArgs* a, size_t* ctl_bytes = nullptr) {
+                     wave::DecodeArgs* a) {
   Carver cv(base);
   const size_t BH = (size_t)sh.BH, G = (size_t)sh.G, C = (size_t)p->n_clusters;
-  wave::DecodeCtl* ctl = cv.take<wave::DecodeCtl>(1);
-  uint32_t* score_done = cv.take<uint32_t>(BH);
-  uint32_t* part_done = cv.take<uint32_t>(BH);
-  uint32_t* sel_ready = cv.take<uint32_t>(BH);
-  uint32_t* chunk_ready = cv.take<uint32_t>(BH * sh.nS);
-  uint32_t* hist = cv.take<uint32_t>(BH * wave::kHistBins);
-  if (ctl_bytes) *ctl_bytes = cv.off;
   const size_t nP = (size_t)sh.nStMax + sh.nS + sh.nB;
   const size_t nPmax = nP > (size_t)sh.nBDense ? nP : (size_t)sh.nBDense;
+  uint32_t* counter = cv.take<uint32_t>(BH);
   float* scores = cv.take<float>(BH * C * G);
   float* shat = cv.take<float>(BH * C);
-  uint32_t* cand_key = cv.take<uint32_t>(BH * C);
-  int32_t* cand_id = cv.take<int32_t>(BH * C);
-  int32_t* sel = cv.take<int32_t>(BH * (size_t)sh.rcap);
-  int32_t* slots = cv.take<int32_t>(BH * (size_t)p->index_len);
-  int32_t* nsel = cv.take<int32_t>(BH);
-  int32_t* ntok = cv.take<int32_t>(BH);
+  int32_t* sel_id = cv.take<int32_t>(BH * (size_t)sh.rcap);
+  int32_t* sel_tok = cv.take<int32_t>(BH * ((size_t)sh.rcap + 1));
+  int32_t* sel_n = cv.take<int32_t>(BH);
   float* part = cv.take<float>(BH * nPmax * G * wave::kPartStride);
   if (a) {
-    a->ctl = ctl;
-    a->score_done = score_done;
-    a->part_done = part_done;
-    a->sel_ready = sel_ready;
-    a->chunk_ready = chunk_ready;
-    a->hist = hist;
+    a->counter = counter;
     a->scores = scores;
     a->shat = shat;
-    a->cand_key = cand_key;
-    a->cand_id = cand_id;
-    a->sel = sel;
-    a->slots = slots;
-    a->nsel = nsel;
-    a->ntok = ntok;
+    a->sel_id = sel_id;
+    a->sel_tok = sel_tok;
+    a->sel_n = sel_n;
     a->part = part;
   }
   return cv.off;
@@ -371,30 +355,23 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   a.nSt = (int)((n_steady + wave::kTokChunk - 1) / wave::kTokChunk);
   a.nB = sh.nB;
   a.nP = a.nSt + a.nS + a.nB;
-  a.total_items = (uint32_t)(sh.BH * (2 * (int64_t)a.nS + a.nSt + a.nB));
   a.local_select = p->n_clusters <= wave::kLocalSelMax ? 1 : 0;
+  const size_t per = ((size_t)p->n_clusters + wave::kDecThreads - 1) / wave::kDecThreads;
+  const size_t keys = per * wave::kDecThreads;
+  const size_t win = 3 * (size_t)wave::kWin * sizeof(uint32_t);
   if (a.local_select) {
-    const size_t per = ((size_t)p->n_clusters + wave::kDecThreads - 1) / wave::kDecThreads;
-    const size_t keys = per * wave::kDecThreads;
-    a.dyn_lds = (keys + (keys + 1) / 2 + 3 * (size_t)wave::kWin) * sizeof(uint32_t);
+    // 32-bit keys and 16-bit sizes of every cluster, then the window
+    a.lds_retrieve = keys * sizeof(uint32_t) + (keys + 1) / 2 * sizeof(uint32_t) + win;
+    a.lds_select = 0;
   } else {
-    a.dyn_lds = 0;
+    a.lds_retrieve = win;
+    // top 16 bits of every key, then the candidate keys
+    a.lds_select = (keys + 1) / 2 * sizeof(uint32_t) + (size_t)wave::kCandLds * sizeof(uint32_t);
   }
   return wave::launch_decode(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
 }
 
 }  // namespace
-
-wave_status wave_decode_workspace_init(const wave_decode_params* p, void* workspace,
-                                       size_t workspace_bytes, hipStream_t stream) {
-  DecodeShape sh;
-  wave_status st = check_decode(p, &sh);
-  if (st != WAVE_OK) return st;
-  size_t ctl_bytes = 0;
-  const size_t need = layout_decode(p, sh, nullptr, nullptr, &ctl_bytes);
-  if (!workspace || workspace_bytes < need) return WAVE_ERR_WORKSPACE;
-  return wave::launch_zero(workspace, ctl_bytes, stream) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
-}
 
 wave_status wave_decode_attention(const wave_decode_params* p, const void* q, const void* k_cache,
                                   const void* v_cache, const wave_index* idx, float* out,

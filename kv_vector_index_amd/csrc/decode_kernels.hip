@@ -9,26 +9,24 @@
 // sums V_j, one query head's output is
 //     out = (sum_E e^{a_i} v_i + sum_U e^{s_j} V_j) / (sum_E e^{a_i} + sum_U n_j e^{s_j}).
 //
-// MI355X design: one persistent kernel per call. Workgroups take work items from an atomic
-// ticket, in this order:
-//   1. score      (b, kv-head, 256 clusters): stream the centroid rows once, store each query
-//                 head's logit and the group-mean score, add the scores to a histogram of
-//                 their ordered bit patterns. The workgroup that finishes the last score item
-//                 of a (b, kv-head) runs the exact top-n_r selection for it right away
-//                 (histogram -> candidate bin -> refinement in LDS; ties to the lower id) and
-//                 publishes the retrieved ids and their token list.
-//   2. steady     exact attention over the steady zone (no dependency).
-//   3. estimate   (b, kv-head, 256 clusters): stream the value sums and fold the estimate of
-//                 ALL non-empty clusters into a partial softmax; it waits only for its own
-//                 score item. Streaming every value sum (instead of only the unretrieved
-//                 ones) lets this run while the selection is still being made.
-//   4. retrieved  waits for the selection, attends the retrieved tokens exactly and removes
-//                 the estimate terms that step 3 added for the retrieved clusters.
-// The workgroup that writes the last partial of a (b, kv-head) merges its partials by
-// log-sum-exp into out / lse. Every wait is on an item with a smaller ticket, which a running
-// workgroup has already claimed, so the waits always end; each wait is also bounded.
-// Rows are read 16 lanes per 256-byte row (4 rows per wave instruction, fully coalesced);
-// each K/V row is shared by the G query heads of its group.
+// MI355X design, two compact kernels per call (a third, the published select, only for
+// indexes with more than kLocalSelMax clusters per head):
+//   stream    one workgroup per 128 clusters or 128 steady tokens of a (b, kv-head): stream
+//             the centroid rows, value-sum rows and sizes once (HBM-bound), store each query
+//             head's logit and the group-mean score, and fold the estimate of ALL non-empty
+//             clusters (or the exact steady tokens) into one partial softmax state.
+//   retrieve  nB workgroups per (b, kv-head). Each recomputes the same exact top-n_r
+//             selection from the group scores staged in LDS (histogram of their ordered bit
+//             patterns, then refinement; ties to the lower id), attends its share of the
+//             retrieved tokens exactly (a retrieved cluster is a contiguous run of cache rows
+//             in the index layout) and removes the estimate terms the stream kernel added for
+//             the retrieved clusters. The last workgroup of a (b, kv-head) merges all partials
+//             by log-sum-exp into out / lse.
+// Streaming every value sum in the first kernel (rather than only the unretrieved ones after
+// the selection) keeps the selection off the critical path of the big reads. Rows are read
+// 16 lanes per 256-byte row (4 rows per wave instruction, fully coalesced) and each K/V row
+// is shared by the G query heads of its group. Both kernels stay small: the instruction
+// cache is shared by neighbouring CUs, and large fused kernels run far slower.
 #include "wave_common.h"
 #include "wave_kernels.h"
 
@@ -226,32 +224,6 @@ __device__ __forceinline__ uint32_t scan_excl(uint32_t x, ScanTmp& tmp, uint32_t
   return before + v - x;
 }
 
-// Bounded wait until *flag != 0 (thread 0 polls; the block then acquires).
-__device__ __forceinline__ void wait_flag(const DecodeArgs& a, const uint32_t* flag) {
-  if (threadIdx.x == 0) {
-    uint32_t spins = 0;
-    while (ld_dev(flag) == 0u) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > (1u << 20)) {  // about a second: a missing producer, never expected
-        atomicOr(&a.ctl->error, 1u);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// Data published through flags and counters is written with device-coherent stores
-// (st_dev) and read with device-coherent loads (ld_dev); draining each wave's stores
-// before the flag update orders the data before the flag for every reader.
-
-// Publish this block's device-coherent writes, then set *flag.
-__device__ __forceinline__ void publish_flag(uint32_t* flag) {
-  drain_vmem();
-  __syncthreads();
-  if (threadIdx.x == 0) st_dev(flag, 1u);
-}
-
 // Publish this block's device-coherent writes and count one more arrival on *counter;
 // true (in every thread) for the block that brings it to n.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n) {
@@ -262,191 +234,6 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n) {
   __syncthreads();
   return s_last != 0u;
 }
-
-// ------------------------------------------------------------------------------------
-// selection of the retrieval zone for one (b, kv-head), by one workgroup
-// ------------------------------------------------------------------------------------
-constexpr int kSweep = 32;                     // ids per thread per sweep
-constexpr int kSweepIds = kSweep * kDecThreads;
-
-// group scores [j0, j0 + kSweep) as ordered keys (0 past the end); scalar loads, all issued
-// before use (rows of these arrays need not be 16-byte aligned)
-__device__ __forceinline__ void load_keys(const float* shat, int C, int j0,
-                                          uint32_t (&key)[kSweep]) {
-  float v[kSweep];
-#pragma unroll
-  for (int i = 0; i < kSweep; ++i) v[i] = (j0 + i < C) ? ld_dev(shat + j0 + i) : kNegInf;
-#pragma unroll
-  for (int i = 0; i < kSweep; ++i) key[i] = order_key(v[i]);
-}
-
-__device__ __forceinline__ void do_select(const DecodeArgs& a, int bh, uint32_t* s_buf) {
-  const int tid = threadIdx.x;
-  __shared__ ScanTmp tmp;
-  __shared__ uint32_t s_h[256];
-  __shared__ uint32_t s_b[2];
-  const int C = a.C;
-  const float* shat = a.shat + (size_t)bh * C;
-
-  // ---- pass 1: the histogram the score items built (thread t owns the top bins first)
-  uint32_t* H = a.hist + (size_t)bh * kHistBins;
-  uint32_t h[16];
-  const int hb0 = kHistBins - 16 * (tid + 1);    // bins hb0 .. hb0+15, visited descending
-#pragma unroll
-  for (int i = 0; i < 16; ++i) h[i] = ld_dev(H + hb0 + i);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) st_dev(H + hb0 + i, 0u);
-  uint32_t loc = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) loc += h[i];
-  uint32_t ne;
-  const uint32_t above_me = scan_excl(loc, tmp, &ne);
-  const uint32_t nr = min((uint32_t)a.n_retrieve, ne);
-
-  // Selection = {key > T} plus the keq lowest ids with key == T.
-  uint32_t T, keq;
-  if (nr == ne) {
-    T = 0u;            // every non-empty cluster (keys > 0)
-    keq = 0u;
-  } else if (nr == 0) {
-    T = 0xffffffffu;   // nothing
-    keq = 0u;
-  } else {
-    uint32_t run = above_me;
-#pragma unroll
-    for (int i = 15; i >= 0; --i) {
-      if (run < nr && run + h[i] >= nr) {
-        s_b[0] = (uint32_t)(hb0 + i);
-        s_b[1] = run;
-      }
-      run += h[i];
-    }
-    __syncthreads();
-    const uint32_t bstar = s_b[0];
-    uint32_t need = nr - s_b[1];
-    __syncthreads();
-    // ---- pass 2: candidates = keys in bin bstar, ascending id order
-    uint32_t* ckey = a.cand_key + (size_t)bh * C;
-    int32_t* cid = a.cand_id + (size_t)bh * C;
-    uint32_t n_c = 0;
-    for (int base = 0; base < C; base += kSweepIds) {
-      const int j0 = base + tid * kSweep;
-      uint32_t key[kSweep];
-      load_keys(shat, C, j0, key);
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int i = 0; i < kSweep; ++i) cnt += (key[i] != 0u && (key[i] >> kHistShift) == bstar);
-      uint32_t tot;
-      uint32_t pos = n_c + scan_excl(cnt, tmp, &tot);
-#pragma unroll
-      for (int i = 0; i < kSweep; ++i) {
-        if (key[i] != 0u && (key[i] >> kHistShift) == bstar) {
-          st_dev(ckey + pos, key[i]);
-          st_dev(cid + pos, j0 + i);
-          if (pos < (uint32_t)kCandLds) s_buf[pos] = key[i];
-          ++pos;
-        }
-      }
-      n_c += tot;
-    }
-    const bool staged = n_c <= (uint32_t)kCandLds;
-    drain_vmem();  // candidates may be re-read from global memory below
-    __syncthreads();
-    // ---- refine inside the bin: the need-th largest candidate key (256 bins per round)
-    uint32_t lo = bstar << kHistShift, hi = lo | ((1u << kHistShift) - 1u);
-    for (;;) {
-      if (lo == hi) break;
-      const uint32_t width = (uint32_t)(((uint64_t)hi - lo + 1 + 255) / 256);
-      s_h[tid] = 0u;
-      __syncthreads();
-      for (uint32_t i = tid; i < n_c; i += kDecThreads) {
-        const uint32_t k = staged ? s_buf[i] : ld_dev(ckey + i);
-        if (k >= lo && k <= hi) atomicAdd(&s_h[(k - lo) / width], 1u);
-      }
-      __syncthreads();
-      const uint32_t cnt = s_h[255 - tid];
-      uint32_t tot;
-      const uint32_t incl = scan_excl(cnt, tmp, &tot) + cnt;
-      if (incl >= need && incl - cnt < need) {
-        s_b[0] = 255u - tid;
-        s_b[1] = incl - cnt;
-      }
-      __syncthreads();
-      const uint32_t b2 = s_b[0], above = s_b[1];
-      __syncthreads();
-      need -= above;
-      const uint64_t nlo = (uint64_t)lo + (uint64_t)b2 * width;
-      const uint64_t nhi = min((uint64_t)hi, nlo + width - 1);
-      lo = (uint32_t)nlo;
-      hi = (uint32_t)nhi;
-      if (width == 1) break;
-    }
-    T = lo;
-    keq = need;
-  }
-
-  // ---- pass 3: ordered compaction of the retrieved ids and their token list
-  const int32_t* csize = a.csize + (size_t)bh * C;
-  const int32_t* coff = a.coff + (size_t)bh * C;
-  int32_t* sel = a.sel + (size_t)bh * a.rcap;
-  int32_t* slots = a.slots + (size_t)bh * a.L0;
-  uint32_t eq_run = 0, sel_run = 0, tok_run = 0;
-  for (int base = 0; base < C; base += kSweepIds) {
-    const int j0 = base + tid * kSweep;
-    uint32_t key[kSweep];
-    load_keys(shat, C, j0, key);
-    int32_t sz[kSweep];
-#pragma unroll
-    for (int i = 0; i < kSweep; ++i) sz[i] = (j0 + i < C) ? csize[j0 + i] : 0;
-    uint32_t n_eq = 0;
-#pragma unroll
-    for (int i = 0; i < kSweep; ++i) n_eq += (T != 0u && key[i] == T);
-    uint32_t tot_eq;
-    uint32_t e = eq_run + scan_excl(n_eq, tmp, &tot_eq);
-    uint32_t n_sel = 0, n_tok = 0, take = 0u;  // take: bit i = id j0 + i retrieved
-#pragma unroll
-    for (int i = 0; i < kSweep; ++i) {
-      bool t = key[i] > T;
-      if (T != 0u && key[i] == T) {
-        t = e < keq;
-        ++e;
-      }
-      take |= (t ? 1u : 0u) << i;
-      n_sel += t;
-      n_tok += t ? (uint32_t)sz[i] : 0u;
-    }
-    uint32_t tot_sel, tot_tok;
-    uint32_t ps = sel_run + scan_excl(n_sel, tmp, &tot_sel);
-    uint32_t pt = tok_run + scan_excl(n_tok, tmp, &tot_tok);
-    while (take) {  // few ids per thread; sizes and offsets re-read from memory
-      const int i = __builtin_ctz(take);
-      take &= take - 1u;
-      const int j = j0 + i;
-      if (ps < (uint32_t)a.rcap) st_dev(sel + ps, j);
-      if (a.selected && ps < (uint32_t)a.n_retrieve)
-        a.selected[(size_t)bh * a.n_retrieve + ps] = j;
-      ++ps;
-      const int n = csize[j], o = coff[j];
-      for (int r = 0; r < n && pt + r < (uint32_t)a.L0; ++r) st_dev(slots + pt + r, o + r);
-      pt += (uint32_t)n;
-    }
-    eq_run += tot_eq;
-    sel_run += tot_sel;
-    tok_run += tot_tok;
-  }
-  if (a.selected)
-    for (int r = (int)sel_run + tid; r < a.n_retrieve; r += kDecThreads)
-      a.selected[(size_t)bh * a.n_retrieve + r] = -1;
-  if (tid == 0) {
-    st_dev(a.nsel + bh, (int32_t)min(sel_run, (uint32_t)a.rcap));
-    st_dev(a.ntok + bh, (int32_t)min(tok_run, (uint32_t)a.L0));
-  }
-  publish_flag(a.sel_ready + bh);
-}
-
-// ------------------------------------------------------------------------------------
-// work items
-// ------------------------------------------------------------------------------------
 
 // Merge the n partials of one (b, kv-head) into out / lse.
 template <int G>
@@ -473,157 +260,9 @@ __device__ __forceinline__ void final_merge(const DecodeArgs& a, int bh, const f
   }
 }
 
-template <int G>
-__device__ __forceinline__ void finish_partial(const DecodeArgs& a, int bh, Online<G>& st,
-                                               int p) {
-  float* parts = a.part + (size_t)bh * a.nP * G * kPartStride;
-  write_block_partial<G>(st, parts + (size_t)p * G * kPartStride);
-  if (arrive_last(a.part_done + bh, (uint32_t)a.nP)) {
-    final_merge<G>(a, bh, parts, a.nP);
-    if (a.local_select)  // every reader of this head's histogram is done: clear it
-      for (int i = threadIdx.x; i < kHistBins; i += kDecThreads)
-        st_dev(a.hist + (size_t)bh * kHistBins + i, 0u);
-  }
-}
 
-template <int G>
-__device__ __forceinline__ void item_score(const DecodeArgs& a, int bh, int c, uint32_t* s_buf) {
-  const int b = bh / a.Hkv, g = bh % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = lane >> 4, cc = lane & 15;
-  u32x4 q[G];
-  load_q<G>(a, b, g, cc, q);
-  for (int i = tid; i < kHistBins; i += kDecThreads) s_buf[i] = 0u;
-  __syncthreads();
-  const size_t base = (size_t)bh * a.C;
-  const int wbeg = c * kChunk + wave * (kChunk / 4);
-  const int wend = min(a.C, wbeg + kChunk / 4);
-  const float sl2 = a.scale_log2;
-  // two tiles of 4 rows per row group in flight (8 rows, 32 per wave)
-  for (int t = wbeg; t < wend; t += 32) {
-    u32x4 kr[8];
-    int32_t n[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = t + 4 * i + grp;
-      if (j < wend) {
-        kr[i] = ld16_stream(a.cmean + (base + j) * kHeadDim + cc * 8);
-        n[i] = a.csize[base + j];
-      } else {
-        kr[i] = u32x4{0, 0, 0, 0};
-        n[i] = -1;
-      }
-    }
-    float s[8][G];
-    row_logits<G, 8>(q, kr, 1.f, s);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = t + 4 * i + grp;
-      if (n[i] < 0) continue;
-      float mean = 0.f;
-#pragma unroll
-      for (int h = 0; h < G; ++h) mean += s[i][h] * a.scale;
-      mean = mean / (float)G;
-      const float sh = n[i] > 0 ? mean : kNegInf;
-      if (cc < G) {
-        float mine = s[i][0];
-#pragma unroll
-        for (int h = 1; h < G; ++h) mine = (cc == h) ? s[i][h] : mine;
-        st_dev(a.scores + (base + j) * G + cc, mine * sl2);
-      }
-      if (cc == 0) {
-        st_dev(a.shat + base + j, sh);
-        const uint32_t key = order_key(sh);
-        if (key) atomicAdd(&s_buf[key >> kHistShift], 1u);
-      }
-    }
-  }
-  __syncthreads();
-  uint32_t* H = a.hist + (size_t)bh * kHistBins;
-  for (int i = tid; i < kHistBins; i += kDecThreads)
-    if (s_buf[i]) atomicAdd(&H[i], s_buf[i]);
-  publish_flag(a.chunk_ready + (size_t)bh * a.nS + c);
-  if (arrive_last(a.score_done + bh, (uint32_t)a.nS) && !a.local_select) do_select(a, bh, s_buf);
-}
-
-template <int G>
-__device__ __forceinline__ void item_steady(const DecodeArgs& a, int bh, int i_item) {
-  const int b = bh / a.Hkv, g = bh % a.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = lane >> 4, cc = lane & 15;
-  u32x4 q[G];
-  load_q<G>(a, b, g, cc, q);
-  Online<G> st;
-  st.init();
-  const int64_t n_steady = (int64_t)a.n_sink + a.n_recent + (a.L - a.L0);
-  const int64_t wbeg = (int64_t)i_item * kTokChunk + wave * (kTokChunk / 4);
-  const int64_t wend = min(n_steady, wbeg + kTokChunk / 4);
-  const size_t base = (size_t)bh * a.Lcap;
-  for (int64_t t = wbeg; t < wend; t += 32) {
-    u32x4 kr[8], vr[8];
-    float w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t tt = t + 4 * i + grp;
-      if (tt < wend) {
-        const size_t row = (base + steady_row(a, tt)) * kHeadDim + cc * 8;
-        kr[i] = ld16_stream(a.k + row);
-        vr[i] = ld16_stream(a.v + row);
-        w[i] = 1.f;
-      } else {
-        kr[i] = vr[i] = u32x4{0, 0, 0, 0};
-        w[i] = 0.f;
-      }
-    }
-    float s[8][G];
-    row_logits<G, 8>(q, kr, a.scale_log2, s);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (w[i] == 0.f)
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
-    fold_rows<G, 8>(st, s, w, vr, 1.f);
-  }
-  finish_partial<G>(a, bh, st, i_item);
-}
-
-template <int G>
-__device__ __forceinline__ void item_estimate(const DecodeArgs& a, int bh, int c) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = lane >> 4, cc = lane & 15;
-  wait_flag(a, a.chunk_ready + (size_t)bh * a.nS + c);
-  Online<G> st;
-  st.init();
-  const size_t base = (size_t)bh * a.C;
-  const int wbeg = c * kChunk + wave * (kChunk / 4);
-  const int wend = min(a.C, wbeg + kChunk / 4);
-  for (int t = wbeg; t < wend; t += 32) {
-    u32x4 vr[8];
-    float w[8], s[8][G];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = t + 4 * i + grp;
-      if (j < wend) {
-        vr[i] = ld16_stream(a.vsum + (base + j) * kHeadDim + cc * 8);
-        w[i] = (float)a.csize[base + j];
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = ld_dev(a.scores + (base + j) * G + h);
-      } else {
-        vr[i] = u32x4{0, 0, 0, 0};
-        w[i] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (w[i] == 0.f)
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
-    fold_rows<G, 8>(st, s, w, vr, 1.f);
-  }
-  finish_partial<G>(a, bh, st, a.nSt + c);
-}
-
-// Exact attention over the rows given by row_of(t) for t in [wb, we) (rows are cache rows).
+// Exact attention over the rows row_of(t), t in [wb, we) (cache rows), 8 rows per row group
+// in flight.
 template <int G, typename RowOf>
 __device__ __forceinline__ void attend_rows(const DecodeArgs& a, int bh, const u32x4 (&q)[G],
                                             Online<G>& st, int64_t wb, int64_t we, RowOf row_of) {
@@ -661,8 +300,8 @@ __device__ __forceinline__ void attend_rows(const DecodeArgs& a, int bh, const u
   }
 }
 
-// Remove the estimate terms of the clusters id_of(k), k in [wb, we), from the state: the
-// same stored logits, weight -n_j and value -V_j (the estimate items added them).
+// Remove the estimate terms of the clusters id_of(k), k in [wb, we): the same stored logits,
+// weight -n_j and value -V_j (the stream kernel added them).
 template <int G, typename IdOf>
 __device__ __forceinline__ void remove_estimates(const DecodeArgs& a, int bh, Online<G>& st,
                                                  int wb, int we, IdOf id_of) {
@@ -683,7 +322,7 @@ __device__ __forceinline__ void remove_estimates(const DecodeArgs& a, int bh, On
         vr[i] = ld16(a.vsum + (base + jr[i]) * kHeadDim + cc * 8);
         wt[i] = -(float)a.csize[base + jr[i]];
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = ld_dev(a.scores + (base + jr[i]) * G + h);
+        for (int h = 0; h < G; ++h) s[i][h] = a.scores[(base + jr[i]) * G + h];
       } else {
         vr[i] = u32x4{0, 0, 0, 0};
         wt[i] = 0.f;
@@ -695,218 +334,328 @@ __device__ __forceinline__ void remove_estimates(const DecodeArgs& a, int bh, On
   }
 }
 
-// Retrieved item, published selection (many clusters): the select of the last score item
-// listed the retrieved ids and their cache rows.
+// ------------------------------------------------------------------------------------
+// kernel 1: stream (scores + estimate of every cluster, and the steady zone)
+// ------------------------------------------------------------------------------------
 template <int G>
-__device__ __forceinline__ void item_retrieved_published(const DecodeArgs& a, int bh, int w_item) {
-  const int b = bh / a.Hkv, g = bh % a.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, cc = lane & 15;
+__global__ __launch_bounds__(kDecThreads) void k_dec_stream(DecodeArgs a) {
+  const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, cc = lane & 15;
+  if (blockIdx.x == 0 && blockIdx.y == 0)  // arrival counters of the retrieve kernel
+    for (int i = tid; i < a.B * a.Hkv; i += kDecThreads) a.counter[i] = 0u;
   u32x4 q[G];
   load_q<G>(a, b, g, cc, q);
-  wait_flag(a, a.sel_ready + bh);
   Online<G> st;
   st.init();
-  const int nB = a.nB;
-  const int64_t ntok = ld_dev(a.ntok + bh);
-  const int64_t t0 = ntok * w_item / nB, t1 = ntok * (w_item + 1) / nB;
-  const int32_t* slots = a.slots + (size_t)bh * a.L0;
-  attend_rows<G>(a, bh, q, st, t0 + (t1 - t0) * wave / 4, t0 + (t1 - t0) * (wave + 1) / 4,
-                 [&](int64_t t) { return ld_dev(slots + t); });
-  const int ns = ld_dev(a.nsel + bh);
-  const int k0 = (int)((int64_t)ns * w_item / nB), k1 = (int)((int64_t)ns * (w_item + 1) / nB);
-  const int32_t* sel = a.sel + (size_t)bh * a.rcap;
-  remove_estimates<G>(a, bh, st, k0 + (k1 - k0) * wave / 4, k0 + (k1 - k0) * (wave + 1) / 4,
-                      [&](int k) { return ld_dev(sel + k); });
-  finish_partial<G>(a, bh, st, a.nSt + a.nS + w_item);
+  if ((int)blockIdx.x < a.nS) {
+    const size_t base = (size_t)bh * a.C;
+    const int wbeg = blockIdx.x * kChunk + wave * (kChunk / 4);
+    const int wend = min(a.C, wbeg + kChunk / 4);
+    const float sl2 = a.scale_log2;
+    for (int t = wbeg; t < wend; t += 32) {
+      u32x4 kr[8], vr[8];
+      int32_t n[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = t + 4 * i + grp;
+        if (j < wend) {
+          const size_t row = (base + j) * kHeadDim + cc * 8;
+          kr[i] = ld16_stream(a.cmean + row);
+          vr[i] = ld16_stream(a.vsum + row);
+          n[i] = a.csize[base + j];
+        } else {
+          kr[i] = vr[i] = u32x4{0, 0, 0, 0};
+          n[i] = -1;
+        }
+      }
+      float s[8][G], w[8];
+      row_logits<G, 8>(q, kr, 1.f, s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = t + 4 * i + grp;
+        if (n[i] >= 0) {
+          float mean = 0.f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) mean += s[i][h] * a.scale;
+          mean = mean / (float)G;
+          if (cc == 0) a.shat[base + j] = n[i] > 0 ? mean : kNegInf;
+          if (cc < G) {
+            float mine = s[i][0];
+#pragma unroll
+            for (int h = 1; h < G; ++h) mine = (cc == h) ? s[i][h] : mine;
+            a.scores[(base + j) * G + cc] = mine * sl2;
+          }
+        }
+        w[i] = n[i] > 0 ? (float)n[i] : 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[i][h] = n[i] > 0 ? s[i][h] * sl2 : kNegInf;
+      }
+      fold_rows<G, 8>(st, s, w, vr, 1.f);
+    }
+  } else {
+    const int64_t n_steady = (int64_t)a.n_sink + a.n_recent + (a.L - a.L0);
+    const int64_t wbeg = (int64_t)(blockIdx.x - a.nS) * kTokChunk + wave * (kTokChunk / 4);
+    const int64_t wend = min(n_steady, wbeg + kTokChunk / 4);
+    attend_rows<G>(a, bh, q, st, wbeg, wend, [&](int64_t t) { return steady_row(a, t); });
+  }
+  write_block_partial<G>(st, a.part + ((size_t)bh * a.nP + blockIdx.x) * G * kPartStride);
 }
 
-// Bounded wait until *counter >= n (thread 0 polls; the block then proceeds).
-__device__ __forceinline__ void wait_count(const DecodeArgs& a, const uint32_t* counter,
-                                           uint32_t n) {
-  if (threadIdx.x == 0) {
-    uint32_t spins = 0;
-    while (ld_dev(counter) < n) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > (1u << 20)) {  // about a second: a missing producer, never expected
-        atomicOr(&a.ctl->error, 1u);
-        break;
-      }
-    }
+// ------------------------------------------------------------------------------------
+// selection helpers (one workgroup)
+// ------------------------------------------------------------------------------------
+
+// From an LDS histogram of the top 12 key bits: the number of non-empty clusters ne, the
+// size nr of the selection, and (if 0 < nr < ne) the bin holding its smallest key and how
+// many keys of that bin belong to the selection.
+__device__ __forceinline__ void hist_cut(const uint32_t* s_hist, uint32_t n_req, ScanTmp& tmp,
+                                         uint32_t* s_b, uint32_t& ne, uint32_t& nr,
+                                         uint32_t& bstar, uint32_t& need) {
+  const int tid = threadIdx.x;
+  const int hb0 = kHistBins - 16 * (tid + 1);  // this thread's bins, visited descending
+  uint32_t h[16], loc = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    h[i] = s_hist[hb0 + i];
+    loc += h[i];
   }
+  const uint32_t above_me = scan_excl(loc, tmp, &ne);
+  nr = min(n_req, ne);
+  bstar = 0u;
+  need = 0u;
+  if (nr == 0u || nr == ne) return;
+  uint32_t run = above_me;
+#pragma unroll
+  for (int i = 15; i >= 0; --i) {
+    if (run < nr && run + h[i] >= nr) {
+      s_b[0] = (uint32_t)(hb0 + i);
+      s_b[1] = run;
+    }
+    run += h[i];
+  }
+  __syncthreads();
+  bstar = s_b[0];
+  need = nr - s_b[1];
   __syncthreads();
 }
 
-// Retrieved item, local selection (up to kLocalSelMax clusters): every retrieved item of a
-// (b, kv-head) recomputes the same exact selection from the histogram and the group scores
-// staged in LDS as soon as the head's score items are done, then attends its share of the
-// selected tokens. This saves the round trips of publishing a list and waiting for it.
-// Dynamic LDS (words): keys [per][256] (entry (i, t) = cluster t*per + i, so that thread t
-// walks its own ids without bank conflicts), sizes u16 [per][256], then three windows of
-// kWin words.
-template <int G>
-__device__ __forceinline__ void item_retrieved_local(const DecodeArgs& a, int bh, int w_item,
-                                                     uint32_t* dyn) {
-  const int b = bh / a.Hkv, g = bh % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cc = lane & 15;
-  const int C = a.C;
-  const int per = (C + kDecThreads - 1) / kDecThreads;
-  uint32_t* s_key = dyn;
-  uint16_t* s_sz = reinterpret_cast<uint16_t*>(dyn + per * kDecThreads);
-  uint32_t* wp = dyn + per * kDecThreads + (per * kDecThreads + 1) / 2;
-  uint32_t* wn = wp + kWin;
-  int32_t* wo = reinterpret_cast<int32_t*>(wn + kWin);
-  __shared__ ScanTmp tmp;
-  __shared__ uint32_t s_h[256];
-  __shared__ uint32_t s_b[2];
-  u32x4 q[G];
-  load_q<G>(a, b, g, cc, q);
-  wait_count(a, a.score_done + bh, (uint32_t)a.nS);
-  const size_t cb = (size_t)bh * C;
-
-  // ---- one round trip: histogram, group scores and sizes
-  const uint32_t* H = a.hist + (size_t)bh * kHistBins;
-  const int hb0 = kHistBins - 16 * (tid + 1);  // this thread's bins, visited descending
-  uint32_t h[16];
+// Narrow [lo, hi] to the need-th largest key (256 equal-width bins per round over the keys
+// key_at(k), k in [0, n), that fall inside). On return lo == hi == that key and need = how
+// many keys equal to it belong to the selection.
+template <typename KeyAt>
+__device__ __forceinline__ void refine(KeyAt key_at, int n, uint32_t& lo, uint32_t& hi,
+                                       uint32_t& need, ScanTmp& tmp, uint32_t* s_h,
+                                       uint32_t* s_b) {
+  const int tid = threadIdx.x;
+  for (;;) {
+    if (lo == hi) return;
+    const uint32_t width = (uint32_t)(((uint64_t)hi - lo + 1 + 255) / 256);
+    s_h[tid] = 0u;
+    __syncthreads();
+    for (int k0 = tid; k0 < n; k0 += 8 * kDecThreads) {
+      uint32_t kk[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) h[i] = ld_dev(H + hb0 + i);
-  for (int i0 = 0; i0 < per; i0 += 16) {
-    float v[16];
-    int32_t z[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = tid * per + i0 + e;
-      const bool ok = (i0 + e < per) && j < C;
-      v[e] = ok ? ld_dev(a.shat + cb + j) : kNegInf;
-      z[e] = ok ? a.csize[cb + j] : 0;
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (i0 + e < per) {
-        s_key[(i0 + e) * kDecThreads + tid] = order_key(v[e]);
-        s_sz[(i0 + e) * kDecThreads + tid] = (uint16_t)z[e];
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + e * kDecThreads;
+        kk[e] = k < n ? key_at(k) : 0u;
       }
-  }
-  uint32_t loc = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) loc += h[i];
-  uint32_t ne;
-  const uint32_t above_me = scan_excl(loc, tmp, &ne);  // also publishes the LDS stores
-  const uint32_t nr = min((uint32_t)a.n_retrieve, ne);
-
-  // ---- threshold: selection = {key > T} plus the keq lowest ids with key == T
-  uint32_t T, keq;
-  if (nr == ne) {
-    T = 0u;
-    keq = 0u;
-  } else if (nr == 0) {
-    T = 0xffffffffu;
-    keq = 0u;
-  } else {
-    uint32_t run = above_me;
-#pragma unroll
-    for (int i = 15; i >= 0; --i) {
-      if (run < nr && run + h[i] >= nr) {
-        s_b[0] = (uint32_t)(hb0 + i);
-        s_b[1] = run;
-      }
-      run += h[i];
+      for (int e = 0; e < 8; ++e)
+        if (kk[e] != 0u && kk[e] >= lo && kk[e] <= hi) atomicAdd(&s_h[(kk[e] - lo) / width], 1u);
     }
     __syncthreads();
-    uint32_t lo = s_b[0] << kHistShift, need = nr - s_b[1];
-    uint32_t hi = lo | ((1u << kHistShift) - 1u);
-    __syncthreads();
-    for (;;) {  // 256 bins per round over the keys inside [lo, hi]
-      if (lo == hi) break;
-      const uint32_t width = (uint32_t)(((uint64_t)hi - lo + 1 + 255) / 256);
-      s_h[tid] = 0u;
-      __syncthreads();
-      for (int i = 0; i < per; ++i) {
-        const uint32_t k = s_key[i * kDecThreads + tid];
-        if (k >= lo && k <= hi) atomicAdd(&s_h[(k - lo) / width], 1u);
-      }
-      __syncthreads();
-      const uint32_t cnt = s_h[255 - tid];
-      uint32_t tot;
-      const uint32_t incl = scan_excl(cnt, tmp, &tot) + cnt;
-      if (incl >= need && incl - cnt < need) {
-        s_b[0] = 255u - tid;
-        s_b[1] = incl - cnt;
-      }
-      __syncthreads();
-      const uint32_t b2 = s_b[0], above = s_b[1];
-      __syncthreads();
-      need -= above;
-      const uint64_t nlo = (uint64_t)lo + (uint64_t)b2 * width;
-      const uint64_t nhi = min((uint64_t)hi, nlo + width - 1);
-      lo = (uint32_t)nlo;
-      hi = (uint32_t)nhi;
-      if (width == 1) break;
+    const uint32_t cnt = s_h[255 - tid];
+    uint32_t tot;
+    const uint32_t incl = scan_excl(cnt, tmp, &tot) + cnt;
+    if (incl >= need && incl - cnt < need) {
+      s_b[0] = 255u - tid;
+      s_b[1] = incl - cnt;
     }
-    T = lo;
-    keq = need;
+    __syncthreads();
+    const uint32_t b2 = s_b[0], above = s_b[1];
+    __syncthreads();
+    need -= above;
+    const uint64_t nlo = (uint64_t)lo + (uint64_t)b2 * width;
+    const uint64_t nhi = min((uint64_t)hi, nlo + width - 1);
+    lo = (uint32_t)nlo;
+    hi = (uint32_t)nhi;
+    if (width == 1) return;
   }
+}
 
-  // ---- ranks and token offsets of this thread's retrieved ids (ascending id order)
-  uint32_t n_eq = 0;
-  for (int i = 0; i < per; ++i) n_eq += (T != 0u && s_key[i * kDecThreads + tid] == T);
-  uint32_t tot;
-  const uint32_t eq0 = scan_excl(n_eq, tmp, &tot);
-  // walk(f): f(rank, token offset, size, id) for each retrieved id of this thread
-  auto walk = [&](uint32_t r, uint32_t p, auto f) {
-    uint32_t e = eq0;
-    for (int i = 0; i < per; ++i) {
-      const uint32_t k = s_key[i * kDecThreads + tid];
-      bool take = k > T;
-      if (T != 0u && k == T) {
+// Visit this thread's ids (thread t owns ids t*per + i, i < per, stored in LDS at
+// i * 256 + t) in ascending order, with whether each belongs to the selection
+// {key > T} + {the keq lowest ids with key == T} (e counts the keys == T seen so far).
+template <typename F>
+__device__ __forceinline__ void walk_ids(const uint32_t* s_key, int per, uint32_t T,
+                                         uint32_t keq, uint32_t e, F f) {
+  const int tid = threadIdx.x;
+  for (int i0 = 0; i0 < per; i0 += 8) {
+    uint32_t kk[8];
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) kk[e2] = (i0 + e2 < per) ? s_key[(i0 + e2) * kDecThreads + tid] : 0u;
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) {
+      if (i0 + e2 >= per) break;
+      bool take = kk[e2] > T;
+      if (T != 0u && kk[e2] == T) {
         take = e < keq;
         ++e;
       }
-      if (take) {
-        const uint32_t n = s_sz[i * kDecThreads + tid];
-        f(r, p, n, tid * per + i);
-        ++r;
-        p += n;
-      }
+      f(i0 + e2, take);
     }
-  };
-  uint32_t my_sel = 0, my_tok = 0;
-  walk(0u, 0u, [&](uint32_t, uint32_t, uint32_t n, int) {
-    ++my_sel;
-    my_tok += n;
-  });
-  uint32_t nsel, ntok;
-  const uint32_t r0 = scan_excl(my_sel, tmp, &nsel);
-  const uint32_t p0 = scan_excl(my_tok, tmp, &ntok);
-  if (w_item == 0 && a.selected) {
-    walk(r0, p0, [&](uint32_t r, uint32_t, uint32_t, int j) {
-      if (r < (uint32_t)a.n_retrieve) a.selected[(size_t)bh * a.n_retrieve + r] = j;
-    });
-    for (int r = (int)nsel + tid; r < a.n_retrieve; r += kDecThreads)
-      a.selected[(size_t)bh * a.n_retrieve + r] = -1;
   }
+}
+
+// ------------------------------------------------------------------------------------
+// kernel 2: retrieve (selection, exact retrieved tokens, estimate removal, final merge)
+// ------------------------------------------------------------------------------------
+template <int G>
+__global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
+  extern __shared__ uint32_t s_dyn[];
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ ScanTmp tmp;
+  __shared__ uint32_t s_h[256];
+  __shared__ uint32_t s_b[2];
+  const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv, w_item = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cc = lane & 15;
+  const int C = a.C, nB = a.nB;
+  const size_t cb = (size_t)bh * C;
+  const int per = (C + kDecThreads - 1) / kDecThreads;
+  const int nkeys = a.local_select ? per * kDecThreads : 0;
+  uint32_t* s_key = s_dyn;                                       // [per][256]
+  uint16_t* s_sz = reinterpret_cast<uint16_t*>(s_dyn + nkeys);   // [per][256]
+  uint32_t* wp = s_dyn + nkeys + (nkeys + 1) / 2;                // window: token starts
+  uint32_t* wn = wp + kWin;                                      //         sizes
+  int32_t* wo = reinterpret_cast<int32_t*>(wn + kWin);           //         ids / cache rows
+  u32x4 q[G];
+  load_q<G>(a, b, g, cc, q);
+
+  uint32_t nsel, ntok, T = 0u, keq = 0u, eq0 = 0u, r0 = 0u, p0 = 0u;
+  if (a.local_select) {
+    // ---- group scores and sizes into LDS (one round trip), histogram of the keys
+    for (int i = tid; i < kHistBins; i += kDecThreads) s_hist[i] = 0u;
+    __syncthreads();
+    for (int i0 = 0; i0 < per; i0 += 16) {
+      float v[16];
+      int32_t z[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = tid * per + i0 + e;
+        const bool ok = (i0 + e < per) && j < C;
+        v[e] = ok ? a.shat[cb + j] : kNegInf;
+        z[e] = ok ? a.csize[cb + j] : 0;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (i0 + e < per) {
+          const uint32_t key = order_key(v[e]);
+          s_key[(i0 + e) * kDecThreads + tid] = key;
+          s_sz[(i0 + e) * kDecThreads + tid] = (uint16_t)z[e];
+          if (key) atomicAdd(&s_hist[key >> kHistShift], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t ne, nr, bstar, need;
+    hist_cut(s_hist, (uint32_t)a.n_retrieve, tmp, s_b, ne, nr, bstar, need);
+    if (nr == ne) {
+      T = 0u;            // every non-empty cluster (keys > 0)
+    } else if (nr == 0) {
+      T = 0xffffffffu;   // nothing
+    } else {
+      uint32_t lo = bstar << kHistShift, hi = lo | ((1u << kHistShift) - 1u);
+      refine([&](int k) { return s_key[k]; }, nkeys, lo, hi, need, tmp, s_h, s_b);
+      T = lo;
+      keq = need;
+    }
+    // ---- ranks and token offsets of this thread's retrieved ids
+    uint32_t n_eq = 0, tot;
+    for (int i = 0; i < per; ++i) n_eq += (T != 0u && s_key[i * kDecThreads + tid] == T);
+    eq0 = scan_excl(n_eq, tmp, &tot);
+    uint32_t my_sel = 0, my_tok = 0;
+    walk_ids(s_key, per, T, keq, eq0, [&](int i, bool take) {
+      if (take) {
+        ++my_sel;
+        my_tok += s_sz[i * kDecThreads + tid];
+      }
+    });
+    r0 = scan_excl(my_sel, tmp, &nsel);
+    p0 = scan_excl(my_tok, tmp, &ntok);
+    if (w_item == 0 && a.selected) {
+      uint32_t r = r0;
+      walk_ids(s_key, per, T, keq, eq0, [&](int i, bool take) {
+        if (take) {
+          if (r < (uint32_t)a.n_retrieve) a.selected[(size_t)bh * a.n_retrieve + r] = tid * per + i;
+          ++r;
+        }
+      });
+      for (int r2 = (int)nsel + tid; r2 < a.n_retrieve; r2 += kDecThreads)
+        a.selected[(size_t)bh * a.n_retrieve + r2] = -1;
+    }
+  } else {
+    nsel = (uint32_t)a.sel_n[bh];
+    ntok = (uint32_t)a.sel_tok[(size_t)bh * (a.rcap + 1) + nsel];
+  }
+
   Online<G> st;
   st.init();
-  const int nB = a.nB;
-  // tokens [T0, T1) of the selection belong to this item; clusters [R0, R1) overlap them
+  const int32_t* stok = a.sel_tok + (size_t)bh * (a.rcap + 1);
+  const int32_t* sid = a.sel_id + (size_t)bh * a.rcap;
+  // tokens [T0, T1) of the selection belong to this workgroup; clusters [R0, R1) overlap them
   const uint32_t T0 = (uint32_t)((uint64_t)ntok * w_item / nB);
   const uint32_t T1 = (uint32_t)((uint64_t)ntok * (w_item + 1) / nB);
-  uint32_t c_before = 0, c_upto = 0;
-  walk(r0, p0, [&](uint32_t, uint32_t p, uint32_t n, int) {
-    c_before += (p + n <= T0);
-    c_upto += (p < T1);
-  });
   uint32_t R0, R1;
-  scan_excl(c_before, tmp, &R0);
-  scan_excl(c_upto, tmp, &R1);
-  for (uint32_t Rw = R0; Rw < R1; Rw += kWin) {
-    const uint32_t cnt = min((uint32_t)kWin, R1 - Rw);
-    walk(r0, p0, [&](uint32_t r, uint32_t p, uint32_t n, int j) {
-      if (r >= Rw && r < Rw + cnt) {
-        wp[r - Rw] = p;
-        wn[r - Rw] = n;
-        wo[r - Rw] = j;
+  if (a.local_select) {
+    uint32_t c_before = 0, c_upto = 0, p = p0;
+    walk_ids(s_key, per, T, keq, eq0, [&](int i, bool take) {
+      if (take) {
+        const uint32_t n = s_sz[i * kDecThreads + tid];
+        c_before += (p + n <= T0);
+        c_upto += (p < T1);
+        p += n;
       }
     });
+    scan_excl(c_before, tmp, &R0);
+    scan_excl(c_upto, tmp, &R1);
+  } else {
+    // first cluster ending after T0, first cluster starting at or after T1 (binary search)
+    uint32_t lo = 0, hi = nsel;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if ((uint32_t)stok[mid + 1] <= T0) lo = mid + 1; else hi = mid;
+    }
+    R0 = lo;
+    hi = nsel;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if ((uint32_t)stok[mid] < T1) lo = mid + 1; else hi = mid;
+    }
+    R1 = lo;
+  }
+  for (uint32_t Rw = R0; Rw < R1; Rw += kWin) {
+    const uint32_t cnt = min((uint32_t)kWin, R1 - Rw);
+    if (a.local_select) {
+      uint32_t r = r0, p = p0;
+      walk_ids(s_key, per, T, keq, eq0, [&](int i, bool take) {
+        if (take) {
+          const uint32_t n = s_sz[i * kDecThreads + tid];
+          if (r >= Rw && r < Rw + cnt) {
+            wp[r - Rw] = p;
+            wn[r - Rw] = n;
+            wo[r - Rw] = tid * per + i;
+          }
+          ++r;
+          p += n;
+        }
+      });
+    } else {
+      for (uint32_t i = tid; i < cnt; i += kDecThreads) {
+        wp[i] = (uint32_t)stok[Rw + i];
+        wn[i] = (uint32_t)(stok[Rw + i + 1] - stok[Rw + i]);
+        wo[i] = sid[Rw + i];
+      }
+    }
     __syncthreads();
     for (uint32_t i = tid; i < cnt; i += kDecThreads) wo[i] = a.coff[cb + wo[i]];
     __syncthreads();
@@ -923,73 +672,179 @@ __device__ __forceinline__ void item_retrieved_local(const DecodeArgs& a, int bh
                    });
     __syncthreads();
   }
-  // the estimate terms of the selected clusters [K0, K1) (by rank) are removed here
+  // the estimate terms of the retrieved clusters [K0, K1) (by rank) are removed here
   const uint32_t K0 = (uint32_t)((uint64_t)nsel * w_item / nB);
   const uint32_t K1 = (uint32_t)((uint64_t)nsel * (w_item + 1) / nB);
   for (uint32_t Kw = K0; Kw < K1; Kw += kWin) {
     const uint32_t cnt = min((uint32_t)kWin, K1 - Kw);
-    walk(r0, p0, [&](uint32_t r, uint32_t, uint32_t, int j) {
-      if (r >= Kw && r < Kw + cnt) wo[r - Kw] = j;
-    });
+    if (a.local_select) {
+      uint32_t r = r0;
+      walk_ids(s_key, per, T, keq, eq0, [&](int i, bool take) {
+        if (take) {
+          if (r >= Kw && r < Kw + cnt) wo[r - Kw] = tid * per + i;
+          ++r;
+        }
+      });
+    } else {
+      for (uint32_t i = tid; i < cnt; i += kDecThreads) wo[i] = sid[Kw + i];
+    }
     __syncthreads();
     remove_estimates<G>(a, bh, st, (int)(cnt * wave / 4), (int)(cnt * (wave + 1) / 4),
                         [&](int k) { return wo[k]; });
     __syncthreads();
   }
-  finish_partial<G>(a, bh, st, a.nSt + a.nS + w_item);
+  float* parts = a.part + (size_t)bh * a.nP * G * kPartStride;
+  write_block_partial<G>(st, parts + (size_t)(a.nS + a.nSt + w_item) * G * kPartStride);
+  if (arrive_last(a.counter + bh, (uint32_t)nB)) final_merge<G>(a, bh, parts, a.nP);
 }
 
 // ------------------------------------------------------------------------------------
-// the persistent decode kernel
+// published select (more than kLocalSelMax clusters per head): one workgroup per
+// (b, kv-head) selects and lists the retrieved ids and their token offsets. LDS holds the
+// top 16 bits of every key; full keys are re-read only around the cut.
 // ------------------------------------------------------------------------------------
-template <int G>
-__global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
-  __shared__ uint32_t s_buf[kHistBins];
+__global__ __launch_bounds__(kDecThreads) void k_dec_select(DecodeArgs a) {
   extern __shared__ uint32_t s_dyn[];
-  __shared__ uint32_t s_ticket;
-  const int BH = a.B * a.Hkv;
-  const uint32_t nScore = (uint32_t)BH * a.nS;
-  const uint32_t nSteady = nScore + (uint32_t)BH * a.nSt;
-  const uint32_t nEst = nSteady + (uint32_t)BH * a.nS;
-  if (threadIdx.x == 0) s_ticket = atomicAdd(&a.ctl->ticket, 1u);
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ ScanTmp tmp;
+  __shared__ uint32_t s_h[256];
+  __shared__ uint32_t s_b[2];
+  const int bh = blockIdx.x, tid = threadIdx.x, C = a.C;
+  const size_t cb = (size_t)bh * C;
+  const float* shat = a.shat + cb;
+  const int per = (C + kDecThreads - 1) / kDecThreads;
+  uint16_t* s_top = reinterpret_cast<uint16_t*>(s_dyn);          // [per][256] key >> 16
+  uint32_t* s_cand = s_dyn + (per * kDecThreads + 1) / 2;        // [kCandLds]
+  for (int i = tid; i < kHistBins; i += kDecThreads) s_hist[i] = 0u;
   __syncthreads();
-  for (;;) {
-    const uint32_t t = s_ticket;
-    __syncthreads();
-    if (t >= a.total_items) break;
-    uint32_t next = 0;
-    if (threadIdx.x == 0) next = atomicAdd(&a.ctl->ticket, 1u);  // prefetch the next item
-    if (t < nScore) {
-      item_score<G>(a, (int)(t % BH), (int)(t / BH), s_buf);
-    } else if (t < nSteady) {
-      const uint32_t u = t - nScore;
-      item_steady<G>(a, (int)(u % BH), (int)(u / BH));
-    } else if (t < nEst) {
-      const uint32_t u = t - nSteady;
-      item_estimate<G>(a, (int)(u % BH), (int)(u / BH));
-    } else {
-      const uint32_t u = t - nEst;
-      if (a.local_select)
-        item_retrieved_local<G>(a, (int)(u % BH), (int)(u / BH), s_dyn);
-      else
-        item_retrieved_published<G>(a, (int)(u % BH), (int)(u / BH));
+  for (int i0 = 0; i0 < per; i0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = tid * per + i0 + e;
+      v[e] = ((i0 + e < per) && j < C) ? shat[j] : kNegInf;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) s_ticket = next;
-    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (i0 + e < per) {
+        const uint32_t key = order_key(v[e]);
+        s_top[(i0 + e) * kDecThreads + tid] = (uint16_t)(key >> 16);
+        if (key) atomicAdd(&s_hist[key >> kHistShift], 1u);
+      }
   }
-  // the last workgroup to leave returns the control words to zero for the next call
-  if (arrive_last(&a.ctl->exited, gridDim.x)) {
-    for (int i = threadIdx.x; i < BH; i += kDecThreads) {
-      a.score_done[i] = 0u;
-      a.part_done[i] = 0u;
-      a.sel_ready[i] = 0u;
+  __syncthreads();
+  uint32_t ne, nr, bstar, need;
+  hist_cut(s_hist, (uint32_t)a.n_retrieve, tmp, s_b, ne, nr, bstar, need);
+  uint32_t T = 0u, keq = 0u;
+  if (nr == 0) {
+    T = 0xffffffffu;
+  } else if (nr < ne) {
+    // second level on the 16-bit keys: which of the 16 sub-bins of bstar holds the cut
+    s_h[tid] = 0u;
+    __syncthreads();
+    for (int i = 0; i < per; ++i) {
+      const uint32_t t16 = s_top[i * kDecThreads + tid];
+      if ((t16 >> 4) == bstar) atomicAdd(&s_h[t16 & 15u], 1u);
     }
-    for (int i = threadIdx.x; i < BH * a.nS; i += kDecThreads) a.chunk_ready[i] = 0u;
-    if (threadIdx.x == 0) {
-      a.ctl->ticket = 0u;
-      a.ctl->exited = 0u;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t run = 0;
+      for (int sb = 15; sb >= 0; --sb) {
+        if (run < need && run + s_h[sb] >= need) {
+          s_b[0] = (bstar << 4) | (uint32_t)sb;
+          s_b[1] = need - run;
+        }
+        run += s_h[sb];
+      }
     }
+    __syncthreads();
+    const uint32_t b16 = s_b[0];
+    need = s_b[1];
+    __syncthreads();
+    // candidates: full keys of the ids whose top 16 bits equal b16
+    uint32_t cnt = 0;
+    for (int i = 0; i < per; ++i) cnt += s_top[i * kDecThreads + tid] == b16 && tid * per + i < C;
+    uint32_t n_c;
+    uint32_t pos = scan_excl(cnt, tmp, &n_c);
+    const bool staged = n_c <= (uint32_t)kCandLds;
+    if (staged)
+      for (int i = 0; i < per; ++i)
+        if (s_top[i * kDecThreads + tid] == b16 && tid * per + i < C)
+          s_cand[pos++] = order_key(shat[tid * per + i]);
+    __syncthreads();
+    uint32_t lo = b16 << 16, hi = lo | 0xffffu;
+    if (staged) {
+      refine([&](int k) { return s_cand[k]; }, (int)n_c, lo, hi, need, tmp, s_h, s_b);
+    } else {  // many equal top bits: read the full keys of every id again
+      refine([&](int k) {
+               const int j = (k % kDecThreads) * per + k / kDecThreads;
+               return j < C ? order_key(shat[j]) : 0u;
+             },
+             per * kDecThreads, lo, hi, need, tmp, s_h, s_b);
+    }
+    T = lo;
+    keq = need;
+  }
+  // ordered compaction: ranks, token offsets, ids
+  auto full_key = [&](int i) -> uint32_t {
+    const uint32_t t16 = s_top[i * kDecThreads + tid];
+    const int j = tid * per + i;
+    if (t16 != (T >> 16) || T == 0u || j >= C) return (uint32_t)t16 << 16;  // enough vs T
+    return order_key(shat[j]);
+  };
+  uint32_t n_eq = 0, tot;
+  for (int i = 0; i < per; ++i) n_eq += (T != 0u && full_key(i) == T);
+  uint32_t e = scan_excl(n_eq, tmp, &tot);
+  uint32_t my_sel = 0, my_tok = 0;
+  const uint32_t e0 = e;
+  for (int i = 0; i < per; ++i) {
+    const int j = tid * per + i;
+    if (j >= C) break;
+    const uint32_t k = full_key(i);
+    bool take = (T == 0u) ? (s_top[i * kDecThreads + tid] != 0u || order_key(shat[j]) != 0u)
+                          : k > T;
+    if (T != 0u && k == T) {
+      take = e < keq;
+      ++e;
+    }
+    if (take) {
+      ++my_sel;
+      my_tok += (uint32_t)a.csize[cb + j];
+    }
+  }
+  uint32_t nsel, ntok;
+  uint32_t r = scan_excl(my_sel, tmp, &nsel);
+  uint32_t p = scan_excl(my_tok, tmp, &ntok);
+  e = e0;
+  int32_t* sid = a.sel_id + (size_t)bh * a.rcap;
+  int32_t* stok = a.sel_tok + (size_t)bh * (a.rcap + 1);
+  for (int i = 0; i < per; ++i) {
+    const int j = tid * per + i;
+    if (j >= C) break;
+    const uint32_t k = full_key(i);
+    bool take = (T == 0u) ? (s_top[i * kDecThreads + tid] != 0u || order_key(shat[j]) != 0u)
+                          : k > T;
+    if (T != 0u && k == T) {
+      take = e < keq;
+      ++e;
+    }
+    if (take) {
+      if (r < (uint32_t)a.rcap) {
+        sid[r] = j;
+        stok[r] = (int32_t)p;
+      }
+      if (a.selected && r < (uint32_t)a.n_retrieve) a.selected[(size_t)bh * a.n_retrieve + r] = j;
+      ++r;
+      p += (uint32_t)a.csize[cb + j];
+    }
+  }
+  if (a.selected)
+    for (int r2 = (int)nsel + tid; r2 < a.n_retrieve; r2 += kDecThreads)
+      a.selected[(size_t)bh * a.n_retrieve + r2] = -1;
+  if (tid == 0) {
+    const uint32_t ns = min(nsel, (uint32_t)a.rcap);
+    a.sel_n[bh] = (int32_t)ns;
+    stok[ns] = (int32_t)ntok;
   }
 }
 
@@ -1043,25 +898,30 @@ __global__ __launch_bounds__(kDecThreads) void k_dense_merge(DecodeArgs a) {
   final_merge<G>(a, bh, a.part + (size_t)bh * a.nB * G * kPartStride, a.nB);
 }
 
-__global__ __launch_bounds__(256) void k_zero(uint32_t* p, size_t n_words) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n_words;
-       i += (size_t)gridDim.x * 256)
-    p[i] = 0u;
-}
 
 // ------------------------------------------------------------------------------------
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
-  const uint32_t grid = a.total_items < 2048u ? a.total_items : 2048u;
-  if (a.dyn_lds > 0) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<G>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)a.dyn_lds);
+  const int BH = a.B * a.Hkv;
+  Tracer::mark(tr, s);
+  hipLaunchKernelGGL(k_dec_stream<G>, dim3(a.nS + a.nSt, BH), dim3(kDecThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (!a.local_select) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_select),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)a.lds_select);
+    if (e != hipSuccess) return e;
+    Tracer::mark(tr, s);
+    hipLaunchKernelGGL(k_dec_select, dim3(BH), dim3(kDecThreads), a.lds_select, s, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_retrieve<G>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)a.lds_retrieve);
+  if (e != hipSuccess) return e;
   Tracer::mark(tr, s);
-  hipLaunchKernelGGL(k_decode<G>, dim3(grid), dim3(kDecThreads), a.dyn_lds, s, a);
-  const hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL(k_dec_retrieve<G>, dim3(a.nB, BH), dim3(kDecThreads), a.lds_retrieve, s, a);
+  e = hipGetLastError();
   Tracer::mark(tr, s);
   return e;
 }
@@ -1098,15 +958,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
 }
 hipError_t launch_dense_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   WAVE_DISPATCH_G(launch_dense_g, a, s, tr)
-}
-
-hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
-  const size_t words = bytes / 4;
-  if (words == 0) return hipSuccess;
-  const size_t blocks = (words + 255) / 256;
-  hipLaunchKernelGGL(k_zero, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s,
-                     static_cast<uint32_t*>(p), words);
-  return hipGetLastError();
 }
 
 }  // namespace wave

@@ -24,24 +24,16 @@ struct Tracer {
 
 // ---------------------------------------------------------------- decode
 constexpr int kDecThreads = 256;      // every decode workgroup: 4 waves
-constexpr int kChunk = 256;           // clusters per score / estimate work item
-constexpr int kTokChunk = 256;        // tokens per steady / dense work item
+constexpr int kChunk = 128;           // clusters per stream workgroup (one tile per wave)
+constexpr int kTokChunk = 128;        // tokens per steady workgroup
 constexpr int kPartStride = 132;      // floats per (partial, head): o[128], m, l, 2 pad
 constexpr int kHistBins = 4096;       // group-score histogram: top 12 bits of the ordered key
 constexpr int kHistShift = 20;
-constexpr int kCandLds = 4096;        // candidate keys staged in LDS by the select
-constexpr int kLocalSelMax = 16384;   // up to this many clusters, retrieved items select locally
-constexpr int kWin = 512;             // clusters per window of a retrieved item
-constexpr int kTokPerItem = 128;      // retrieved tokens per retrieved item (target)
-
-// Control words of the decode workspace. They must be zero when a call starts; every call
-// that completes returns them to zero (the last workgroup to leave clears them).
-struct DecodeCtl {
-  uint32_t ticket;   // next work item
-  uint32_t exited;   // workgroups that found no more work
-  uint32_t error;    // set if a bounded wait timed out (results then undefined)
-  uint32_t pad;
-};
+constexpr int kLocalSelMax = 16384;   // up to this many clusters, retrieve workgroups select
+constexpr int kMaxClusters = 65536;   // clusters per (b, kv-head) supported by the decode
+constexpr int kCandLds = 2048;        // candidate keys held in LDS by the published select
+constexpr int kWin = 512;             // clusters per window of a retrieve workgroup
+constexpr int kTokPerItem = 128;      // retrieved tokens per retrieve workgroup (target)
 
 struct DecodeArgs {
   // inputs
@@ -56,40 +48,29 @@ struct DecodeArgs {
   float* out;              // [B, Hq, d]
   float* lse;              // [B, Hq] or null
   int32_t* selected;       // [B, Hkv, n_retrieve] or null
-  // workspace: control words (zero between calls)
-  DecodeCtl* ctl;
-  uint32_t* score_done;    // [BH] score items finished
-  uint32_t* part_done;     // [BH] partials written
-  uint32_t* sel_ready;     // [BH] retrieval set published
-  uint32_t* chunk_ready;   // [BH, nS] scores of a chunk published
-  uint32_t* hist;          // [BH, kHistBins] group-score histogram (cleared by the select)
-  // workspace: data
+  // workspace
+  uint32_t* counter;       // [BH] retrieve-workgroup arrivals (cleared by the stream kernel)
   float* scores;           // [BH, C, G] log2-domain centroid logits of each query head
   float* shat;             // [BH, C] group-mean logits (natural units; -inf if empty)
-  uint32_t* cand_key;      // [BH, C] select candidates
-  int32_t* cand_id;
-  int32_t* sel;            // [BH, rcap] retrieved ids, ascending
-  int32_t* slots;          // [BH, L0] cache rows of the retrieved tokens, in sel order
-  int32_t* nsel;           // [BH]
-  int32_t* ntok;           // [BH]
-  float* part;             // [BH, nP, G, kPartStride]
+  float* part;             // [BH, nP, G, kPartStride] partial softmax states
+  int32_t* sel_id;         // [BH, rcap] published selection: ids in ascending order
+  int32_t* sel_tok;        // [BH, rcap + 1] token start of each retrieved cluster, then total
+  int32_t* sel_n;          // [BH] number of retrieved clusters
   // shape
   int B, Hq, Hkv, G;
   int64_t L, L0, Lcap;
   int C, n_sink, n_recent, n_retrieve, rcap;
-  int nS, nSt, nB, nP;     // items per (b, kv-head): score (= estimate), steady, retrieved
-  uint32_t total_items;
-  int local_select;        // 1: retrieved items select locally (C <= kLocalSelMax)
-  size_t dyn_lds;          // dynamic LDS bytes of the decode kernel
+  int nS, nSt, nB, nP;     // per (b, kv-head): stream chunks, steady chunks, retrieve groups
+  int local_select;        // 1: retrieve workgroups select themselves (C <= kLocalSelMax)
+  size_t lds_retrieve;     // dynamic LDS bytes of the retrieve kernel
+  size_t lds_select;       // dynamic LDS bytes of the published select kernel
   float scale, scale_log2;
 };
 
-// Enqueue one tripartite decode step (one persistent kernel). Returns the launch error.
+// Enqueue one tripartite decode step. Returns the first launch error.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
 // Enqueue dense decode over [0, L): split-K partials (part, nB per head) + merge.
 hipError_t launch_dense_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
-// Zero `bytes` bytes of device memory with a kernel (safe under stream capture).
-hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 
 // ---------------------------------------------------------------- build
 struct BuildArgs {

@@ -87,7 +87,7 @@ def test_build_validation(kw, code):
     (dict(head_dim=96), 2), (dict(n_q_heads=36, n_kv_heads=4), 2), (dict(n_q_heads=33), 1),
     (dict(seq_len=4000), 1), (dict(seq_len=5000), 1), (dict(n_retrieve=-1), 1),
     (dict(n_retrieve=257), 1), (dict(scale=0.0), 1), (dict(scale=float("nan")), 1),
-    (dict(n_clusters=0), 1), (dict(n_sink=4000, n_recent=200), 1),
+    (dict(n_clusters=0), 1), (dict(n_sink=4000, n_recent=200), 1), (dict(n_clusters=65537), 2),
 ])
 def test_decode_validation(kw, code):
     with pytest.raises(wi.WaveError) as e:
@@ -125,11 +125,9 @@ def test_decode_rejects_null_small_workspace_and_aliasing_before_any_launch():
     assert call(Q, K, V, ctypes.byref(idx), OUT, None, None, WS, ws - 256, None) == 3
     assert call(Q, K, V, ctypes.byref(idx), K + 512, None, None, WS, ws, None) == 4
     assert call(Q, K, V, ctypes.byref(idx), OUT, OUT + 64, None, WS, ws, None) == 4
-    init = lib.wave_decode_workspace_init
-    assert init(ctypes.byref(p), None, ws, None) == 3
-    assert init(ctypes.byref(p), WS, ws - 1, None) == 3
     bad = decode_params(n_retrieve=-1)
-    assert init(ctypes.byref(bad), WS, ws, None) == 1
+    assert lib.wave_decode_attention(ctypes.byref(bad), Q, K, V, ctypes.byref(idx), OUT, None,
+                                     None, WS, ws, None) == 1
     dense = lib.wave_dense_decode_attention
     assert dense(ctypes.byref(p), Q, K, V, None, None, WS, ws, None) == 1
     assert dense(ctypes.byref(p), Q, K, V, OUT, None, None, ws, None) == 3

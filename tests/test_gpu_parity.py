@@ -8,6 +8,7 @@ import sys
 import numpy as np
 import pytest
 
+import kv_vector_index_amd as wi
 import synth
 from oracle import wave_oracle as wo
 import wave_testlib as tl
@@ -123,14 +124,14 @@ def test_tiny_decode_every_step(tiny):
 
 
 def test_workspace_reuse_across_budgets(tiny):
-    """A workspace re-prepared for another budget gives the same results as a fresh one."""
+    """One workspace, sized for the largest budget and never cleared, serves calls with other
+    budgets and gives the same results as a fresh workspace each time."""
     import kv_vector_index_amd as wi
     w, x, layer = tiny
     idx = layer.build()
     L = layer.L0 + 2
     ws = wi.alloc_decode_workspace(layer.decode_params(L, 11))   # sized for the largest
     for n_r in (3, 11, 3, 0, 11):
-        wi.wave_decode_workspace_init(layer.decode_params(L, n_r), ws)
         out, lse, sel = layer.decode(idx, x.q[1], L, n_r, ws=ws)
         out2, lse2, sel2 = layer.decode(idx, x.q[1], L, n_r)
         assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
@@ -295,3 +296,58 @@ def test_llama128k_sampled_parity():
         say(f"[128k] decode step {s}")
         out, lse, sel = layer.decode(idx, x.q[s], L, w.n_retrieve)
         tl.oracle_decode_check(layer, idx, x.q[s], L, w.n_retrieve, out, lse, sel)
+
+
+def host_index_layer(rng, C, n_distinct, Hq=4, n_sink=3, n_recent=9, steps=1, p_empty=0.05):
+    """One KV head whose index is written on the host: cluster sizes 0..3, centroid means
+    drawn from only n_distinct bf16 vectors (so thousands of group scores tie exactly),
+    value sums = the bf16-rounded sums of the cluster's value rows."""
+    t = tl.torch()
+    size = rng.integers(1, 4, C).astype(np.int32)
+    size[rng.random(C) < p_empty] = 0
+    offset = (n_sink + np.concatenate([[0], np.cumsum(size)[:-1]])).astype(np.int32)
+    L0 = n_sink + int(size.sum()) + n_recent
+    Lcap = L0 + steps
+    k = tl.f32_bits(rng.standard_normal((1, 1, Lcap, 128)))
+    v = tl.f32_bits(rng.standard_normal((1, 1, Lcap, 128)))
+    protos = tl.f32_bits(rng.standard_normal((n_distinct, 128)) * 0.3)
+    cmean = protos[rng.integers(0, n_distinct, C)]
+    V = wo.bf16_to_f64(v[0, 0])
+    csum = np.zeros((C, 128))
+    owner = np.repeat(np.arange(C), size)
+    np.add.at(csum, owner, V[n_sink:n_sink + len(owner)])
+    vsum = wo.round_bf16(csum)
+    layer = tl.Layer(k, v, L0, L0, 1, 1, n_sink, n_recent, Hq)
+    layer.C = C
+    layer.k_out, layer.v_out = layer.k, layer.v
+    idx = wi.alloc_index(1, 1, C, L0)
+    idx.centroid_mean.copy_(tl.to_dev(cmean[None, None]))
+    idx.value_sum.copy_(tl.to_dev(vsum[None, None]))
+    idx.cluster_size.copy_(t.from_numpy(size[None, None]))
+    idx.cluster_offset.copy_(t.from_numpy(offset[None, None]))
+    idx.labels.zero_()
+    idx.perm.zero_()
+    idx.last_centroids.zero_()
+    q = tl.f32_bits(rng.standard_normal((steps, 1, Hq, 128)))
+    return layer, idx, q, size
+
+
+@pytest.mark.parametrize("C", [12000, 20000, 65536])
+def test_exact_score_ties_select_lowest_ids(C):
+    """Exactly tied group scores are broken towards the lower cluster id, both where each
+    retrieve workgroup selects for itself (C <= 16384) and where one workgroup per head
+    publishes the selection (larger C); the budgets put the cut inside a block of ties
+    thousands of clusters wide, and past the number of non-empty clusters."""
+    rng = np.random.default_rng(C)
+    layer, idx, q, size = host_index_layer(rng, C, n_distinct=5)
+    for n_r in (1, C // 50, C // 3, C):
+        say(f"[ties C={C}] n_r={n_r}")
+        out, lse, sel = layer.decode(idx, q[0], layer.L0 + 1, n_r)
+        hi = tl.head_index(idx, 0, 0)
+        free = wo.decode_group(q[0][0], tl.to_np16(layer.k)[0, 0], tl.to_np16(layer.v)[0, 0], hi,
+                               layer.L0, layer.L0 + 1, layer.n_sink, layer.n_recent, n_r)
+        got = sel[0, 0]
+        want = np.sort(free.selected)
+        assert np.array_equal(got[got >= 0], want), "tie-break differs from lowest-id order"
+        assert np.all(got[len(want):] == -1)
+        tl.oracle_decode_check(layer, idx, q[0], layer.L0 + 1, n_r, out, lse, sel)
