@@ -136,11 +136,12 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   sh->nS = (p->n_clusters + wave::kChunk - 1) / wave::kChunk;
   const int64_t steady_max = (int64_t)p->n_sink + p->n_recent + (p->kv_capacity - p->index_len);
   sh->nStMax = (int)((steady_max + wave::kTokChunk - 1) / wave::kTokChunk);
-  // retrieved-token work items: about 256 tokens each at the average cluster size
+  // retrieve workgroups: about kRowsPerItem virtual rows each (a retrieved cluster's tokens
+  // plus its estimate-removal row) at the average cluster size
   const int64_t indexed = p->index_len - p->n_sink - p->n_recent;
   const int64_t avg = indexed > p->n_clusters ? indexed / p->n_clusters : 1;
-  sh->nB = clampi(((int64_t)p->n_retrieve * avg + wave::kTokPerItem - 1) / wave::kTokPerItem,
-                  1, 256);
+  sh->nB = clampi(((int64_t)p->n_retrieve * (avg + 1) + wave::kRowsPerItem - 1) /
+                      wave::kRowsPerItem, 1, wave::kMaxRetrieveWG);
   sh->nBDense = clampi((p->kv_capacity + 1023) / 1024, 1, 512);
   sh->rcap = p->n_retrieve > 0 ? p->n_retrieve : 1;
   return WAVE_OK;
@@ -152,22 +153,29 @@ size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* b
                      wave::DecodeArgs* a) {
   Carver cv(base);
   const size_t BH = (size_t)sh.BH, G = (size_t)sh.G, C = (size_t)p->n_clusters;
+  const size_t Cp = (size_t)sh.nS * wave::kChunk;
   const size_t nP = (size_t)sh.nStMax + sh.nS + sh.nB;
   const size_t nPmax = nP > (size_t)sh.nBDense ? nP : (size_t)sh.nBDense;
   uint32_t* counter = cv.take<uint32_t>(BH);
   float* scores = cv.take<float>(BH * C * G);
-  float* shat = cv.take<float>(BH * C);
+  float* shat = cv.take<float>(BH * Cp);
+  float* mm = cv.take<float>(BH * sh.nS * 4);
   int32_t* sel_id = cv.take<int32_t>(BH * (size_t)sh.rcap);
-  int32_t* sel_tok = cv.take<int32_t>(BH * ((size_t)sh.rcap + 1));
+  int32_t* sel_ts = cv.take<int32_t>(BH * ((size_t)sh.rcap + 1));
+  int32_t* sel_coff = cv.take<int32_t>(BH * (size_t)sh.rcap);
   int32_t* sel_n = cv.take<int32_t>(BH);
+  int32_t* wg_r0 = cv.take<int32_t>(BH * (wave::kMaxRetrieveWG + 1));
   float* part = cv.take<float>(BH * nPmax * G * wave::kPartStride);
   if (a) {
     a->counter = counter;
     a->scores = scores;
     a->shat = shat;
+    a->mm = mm;
     a->sel_id = sel_id;
-    a->sel_tok = sel_tok;
+    a->sel_ts = sel_ts;
+    a->sel_coff = sel_coff;
     a->sel_n = sel_n;
+    a->wg_r0 = wg_r0;
     a->part = part;
   }
   return cv.off;
@@ -182,6 +190,7 @@ void fill_decode_shape(const wave_decode_params* p, const DecodeShape& sh, wave:
   a->L0 = p->index_len;
   a->Lcap = p->kv_capacity;
   a->C = p->n_clusters;
+  a->Cp = sh.nS * wave::kChunk;
   a->n_sink = p->n_sink;
   a->n_recent = p->n_recent;
   a->n_retrieve = p->n_retrieve;
@@ -355,19 +364,8 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   a.nSt = (int)((n_steady + wave::kTokChunk - 1) / wave::kTokChunk);
   a.nB = sh.nB;
   a.nP = a.nSt + a.nS + a.nB;
-  a.local_select = p->n_clusters <= wave::kLocalSelMax ? 1 : 0;
-  const size_t per = ((size_t)p->n_clusters + wave::kDecThreads - 1) / wave::kDecThreads;
-  const size_t keys = per * wave::kDecThreads;
-  const size_t win = 3 * (size_t)wave::kWin * sizeof(uint32_t);
-  if (a.local_select) {
-    // 32-bit keys and 16-bit sizes of every cluster, then the window
-    a.lds_retrieve = keys * sizeof(uint32_t) + (keys + 1) / 2 * sizeof(uint32_t) + win;
-    a.lds_select = 0;
-  } else {
-    a.lds_retrieve = win;
-    // top 16 bits of every key, then the candidate keys
-    a.lds_select = (keys + 1) / 2 * sizeof(uint32_t) + (size_t)wave::kCandLds * sizeof(uint32_t);
-  }
+  a.local_select =
+      (p->n_clusters <= wave::kLocalSelMax && p->n_retrieve <= wave::kSelMax) ? 1 : 0;
   return wave::launch_decode(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
 }
 

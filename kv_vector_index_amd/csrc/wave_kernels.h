@@ -24,17 +24,21 @@ struct Tracer {
 
 // ---------------------------------------------------------------- decode
 constexpr int kDecThreads = 256;      // every decode workgroup: 4 waves
-constexpr int kChunk = 128;           // clusters per stream workgroup (one tile per wave)
-constexpr int kTokChunk = 128;        // tokens per steady workgroup
+constexpr int kChunk = 128;           // clusters per stream workgroup (32 per wave)
+constexpr int kTokChunk = 128;        // steady tokens per stream workgroup
 constexpr int kPartStride = 132;      // floats per (partial, head): o[128], m, l, 2 pad
-constexpr int kHistBins = 4096;       // group-score histogram: top 12 bits of the ordered key
-constexpr int kHistShift = 20;
-constexpr int kLocalSelMax = 16384;   // up to this many clusters, retrieve workgroups select
+constexpr int kHistBins = 4096;       // value-range histogram of the group scores
+constexpr int kCand = 256;            // keys ranked exactly in the histogram bin of the cut
+constexpr int kLocalSelMax = 16384;   // retrieve workgroups select for themselves up to this C
+constexpr int kSelMax = 1024;         // ... and up to this many retrieved clusters
+constexpr int kKeySlices = kLocalSelMax / (4 * kDecThreads);  // float4 slices of 1024 ids
 constexpr int kMaxClusters = 65536;   // clusters per (b, kv-head) supported by the decode
-constexpr int kCandLds = 2048;        // candidate keys held in LDS by the published select
-constexpr int kWin = 512;             // clusters per window of a retrieve workgroup
-constexpr int kTokPerItem = 128;      // retrieved tokens per retrieve workgroup (target)
+constexpr int kMaxRetrieveWG = 256;   // retrieve workgroups per (b, kv-head)
+constexpr int kRowsPerItem = 128;     // retrieved rows per retrieve workgroup (target)
 
+// A retrieved cluster j of size n_j occupies n_j + 1 consecutive "virtual rows": its n_j
+// tokens, then one row that removes its centroid estimate (logit s_j, weight -n_j, value
+// -V_j) from the stream kernel's estimate over all clusters.
 struct DecodeArgs {
   // inputs
   const uint16_t* q;       // [B, Hq, d]
@@ -51,19 +55,20 @@ struct DecodeArgs {
   // workspace
   uint32_t* counter;       // [BH] retrieve-workgroup arrivals (cleared by the stream kernel)
   float* scores;           // [BH, C, G] log2-domain centroid logits of each query head
-  float* shat;             // [BH, C] group-mean logits (natural units; -inf if empty)
+  float* shat;             // [BH, Cp] group-mean logits (natural units; -inf: empty / pad)
+  float* mm;               // [BH, nS, 4] per stream chunk: min, max, count of finite shat
+  int32_t* sel_id;         // [BH, rcap] published selection (ascending ids)
+  int32_t* sel_ts;         // [BH, rcap + 1] first virtual row of each cluster, then total
+  int32_t* sel_coff;       // [BH, rcap] first cache row of each cluster
+  int32_t* sel_n;          // [BH]
+  int32_t* wg_r0;          // [BH, kMaxRetrieveWG + 1] first listed cluster of each workgroup
   float* part;             // [BH, nP, G, kPartStride] partial softmax states
-  int32_t* sel_id;         // [BH, rcap] published selection: ids in ascending order
-  int32_t* sel_tok;        // [BH, rcap + 1] token start of each retrieved cluster, then total
-  int32_t* sel_n;          // [BH] number of retrieved clusters
   // shape
   int B, Hq, Hkv, G;
   int64_t L, L0, Lcap;
-  int C, n_sink, n_recent, n_retrieve, rcap;
+  int C, Cp, n_sink, n_recent, n_retrieve, rcap;
   int nS, nSt, nB, nP;     // per (b, kv-head): stream chunks, steady chunks, retrieve groups
-  int local_select;        // 1: retrieve workgroups select themselves (C <= kLocalSelMax)
-  size_t lds_retrieve;     // dynamic LDS bytes of the retrieve kernel
-  size_t lds_select;       // dynamic LDS bytes of the published select kernel
+  int local_select;        // 1: retrieve workgroups select themselves
   float scale, scale_log2;
 };
 
