@@ -4,10 +4,13 @@
 One step = one pass of the whole hot path over one batch of synthetic input: build the index
 of the layer (segmented spherical k-means, finalise, permuted K/V) and run the workload's
 decode steps against it (score, select, exact + estimate, merge). Inputs are resident in HBM
-before timing starts. Between decode calls a 512 MiB buffer is written so that each call
-reads its data from HBM rather than from the 256 MB Infinity Cache; the decode figures come
-from HIP events around each call (the flush is outside them) and the per-kernel figures from
-events the library records between its kernels.
+before timing starts. Before each decode call a 512 MiB buffer is read (a reduction) so that
+the call finds its data in HBM rather than in the 256 MB Infinity Cache, as it would after
+the other layers of a model; the per-kernel figures come from HIP events that the library
+records between its kernels (the flush lies outside them).
+
+A 256 MiB device-to-device copy runs once before the warmup: its FETCH_SIZE / WRITE_SIZE
+counters calibrate the HBM-traffic figures taken from rocprofv3 runs of this script.
 
 Prints one JSON line. `value` is decode-attention tokens/s of the layer (batch / median time
 of one decode call); the index-build rate and achieved HBM bandwidth are extra fields.
@@ -90,11 +93,17 @@ def main():
     out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
     lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
     sel = torch.empty(nds, B, H, max(nr, 1), dtype=torch.int32, device="cuda")
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = None
+    if not args.no_flush:
+        flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")    # 512 MiB
+    calib = torch.empty(2, 64 << 20, dtype=torch.float32, device="cuda")     # 2 x 256 MiB
+    calib[1].copy_(calib[0])                                                 # calibration copy
 
-    n_build_ev = 3 * T + 4
-    # decode kernels: stream, [select when C > 16384], retrieve (one event before each + end)
-    n_dec_ev = 3 if C <= 16384 else 4
+    # start / end events of every kernel: build = norms, seeds, T x (assign, sort),
+    # (T - 1) x update, finalise, steady; decode = stream, [select], retrieve
+    n_build_ev = 2 * (3 * T + 3)
+    local = C <= 16384 and nr <= 1024
+    n_dec_ev = 4 if local else 6
     def events(n):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for e in ev:
@@ -106,7 +115,7 @@ def main():
                             events=None if bev is None else [e.cuda_event for e in bev])
         for s in range(nds):
             if flush is not None:
-                flush.fill_(s & 255)
+                flush.sum()
             wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, out, lse, sel[s], dws,
                                      events=None if dev_ is None else
                                      [e.cuda_event for e in dev_[s]])
@@ -125,78 +134,89 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # ---- per-kernel durations (ms) from the library's kernel-boundary events
+    # ---- per-kernel durations (ms) from the library's per-kernel start / end events
     el = lambda a, b: a.elapsed_time(b)  # noqa: E731
+    kd = lambda ev, i: el(ev[2 * i], ev[2 * i + 1])  # noqa: E731
     build_ms = [el(b[0], b[-1]) for b in bevs]
-    # build kernel order: norms, seeds, then per pass assign, sort, [update]; finalise, steady
-    assign_ms, sort_ms, update_ms = [], [], []
+    assign_ms, sort_ms, update_ms, fin_ms = [], [], [], []
     for b in bevs:
-        i = 2
+        i = 2                      # after norms, seeds
         for p in range(T):
-            assign_ms.append(el(b[i], b[i + 1]))
-            sort_ms.append(el(b[i + 1], b[i + 2]))
+            assign_ms.append(kd(b, i))
+            sort_ms.append(kd(b, i + 1))
             i += 2
             if p < T - 1:
-                update_ms.append(el(b[i], b[i + 1]))
+                update_ms.append(kd(b, i))
                 i += 1
-        fin_ms = el(b[i], b[i + 1])
+        fin_ms.append(kd(b, i))
     call_ms = [el(e[0], e[-1]) for st in devs for e in st]
-    stream_ms = [el(e[0], e[1]) for st in devs for e in st]
-    select_ms = [el(e[1], e[2]) for st in devs for e in st] if n_dec_ev == 4 else []
-    retrieve_ms = [el(e[-2], e[-1]) for st in devs for e in st]
+    stream_ms = [kd(e, 0) for st in devs for e in st]
+    select_ms = [kd(e, 1) for st in devs for e in st] if not local else []
+    retrieve_ms = [kd(e, n_dec_ev // 2 - 1) for st in devs for e in st]
     med = statistics.median
 
     # ---- algorithmic work (per decode call and per assignment launch)
     csize = idx.cluster_size.cpu().numpy()
     selh = sel.cpu().numpy()
-    e_tok = []
+    e_tok, r_tok = [], []
     for s in range(nds):
         steady = w.n_sink + w.n_recent + s + 1
-        tot = 0
+        tot = rt = 0
         for b in range(B):
             for g in range(H):
                 ids = selh[s, b, g, :nr]
                 ids = ids[ids >= 0]
+                rt += int(csize[b, g, ids].sum())
                 tot += steady + int(csize[b, g, ids].sum())
         e_tok.append(tot / (B * H))
-    E = float(np.mean(e_tok))
-    per_bh = 2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d
-    call_bytes = per_bh * B * H
-    # the stream kernel's share: centroids, sizes, unretrieved value sums, steady rows, q
+        r_tok.append(rt / (B * H))
+    E, Er = float(np.mean(e_tok)), float(np.mean(r_tok))
+    BH = B * H
+    # whole call: centroids + sizes, value sums of the unretrieved clusters, exact K/V rows,
+    # q in, out
+    call_bytes = (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d) * BH
+    # stream kernel: centroids, sizes, unretrieved value sums, steady rows, q
     steady_mean = w.n_sink + w.n_recent + (nds + 1) / 2
     stream_bytes = (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * steady_mean
-                    + 2 * G * d) * B * H
+                    + 2 * G * d) * BH
+    # retrieve kernel: retrieved K/V rows, the removed clusters' value sums, logits, sizes
+    # and offsets, the group scores it selects from, q, out
+    retrieve_bytes = (4 * d * Er + (2 * d + 4 * G + 8) * nr + 4 * C + 2 * G * d
+                      + 4 * G * d) * BH
     n_idx = [max(0, min((s + 1) * w.segment_size, L0 - w.n_recent) - max(s * w.segment_size,
                                                                            w.n_sink))
              for s in range(w.n_segments)]
-    assign_flop = sum(2.0 * n * w.clusters_per_segment * d for n in n_idx) * B * H
+    assign_flop = sum(2.0 * n * w.clusters_per_segment * d for n in n_idx) * BH
 
     decode_tok_s = B / (med(call_ms) * 1e-3)
     build_tok_s = B * L0 / (med(build_ms) * 1e-3)
     call_gbs = call_bytes / (med(call_ms) * 1e-3) / 1e9
-    assign_tfs = assign_flop / (statistics.mean(assign_ms) * 1e-3) / 1e12
-    stream_gbs = stream_bytes / (statistics.mean(stream_ms) * 1e-3) / 1e9
-    per_step = {"k_assign": T * statistics.mean(assign_ms),
-                "k_dec_stream": nds * statistics.mean(stream_ms),
-                "k_dec_retrieve": nds * statistics.mean(retrieve_ms)}
+    mean = statistics.mean
+    traffic = load_traffic()
+
+    def roof(kernel, bound, work, launches_ms, extra=None):
+        t = mean(launches_ms) * 1e-3
+        if bound == "mfma":
+            ach, peak, unit, key = work / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "flop_per_launch"
+        else:
+            ach, peak, unit, key = work / t / 1e9, HBM_PEAK_GBS, "GB/s", "bytes_per_launch"
+        r = {"kernel": kernel, "bound": bound, "achieved": round(ach, 2), "peak": peak,
+             "unit": unit, "frac": round(ach / peak, 4), "traffic": traffic.get(kernel),
+             key: work, "avg_launch_us": round(mean(launches_ms) * 1e3, 2)}
+        r.update(extra or {})
+        return r
+
+    roofs = {
+        "k_assign": roof("k_assign", "mfma", assign_flop, assign_ms),
+        "k_dec_stream": roof("k_dec_stream", "hbm", stream_bytes, stream_ms),
+        "k_dec_retrieve": roof("k_dec_retrieve", "hbm", retrieve_bytes, retrieve_ms),
+    }
+    per_step = {"k_assign": T * mean(assign_ms), "k_dec_stream": nds * mean(stream_ms),
+                "k_dec_retrieve": nds * mean(retrieve_ms)}
     dominant = max(per_step, key=per_step.get)
-    roof_assign = {"kernel": "k_assign", "bound": "mfma", "achieved": round(assign_tfs, 2),
-                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                   "frac": round(assign_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                   "flop_per_launch": assign_flop,
-                   "avg_launch_us": round(statistics.mean(assign_ms) * 1e3, 2)}
-    roof_decode = {"kernel": "decode call (all kernels)", "bound": "hbm",
-                   "achieved": round(call_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                   "frac": round(call_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                   "bytes_per_launch": call_bytes,
-                   "avg_launch_us": round(statistics.mean(call_ms) * 1e3, 2),
-                   "median_launch_us": round(med(call_ms) * 1e3, 2)}
-    roof_stream = {"kernel": "k_dec_stream", "bound": "hbm", "achieved": round(stream_gbs, 1),
-                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                   "frac": round(stream_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                   "bytes_per_launch": stream_bytes,
-                   "avg_launch_us": round(statistics.mean(stream_ms) * 1e3, 2)}
-    roof = {"k_assign": roof_assign, "k_dec_stream": roof_stream}.get(dominant, roof_decode)
+    roof_call = roof("decode call", "hbm", call_bytes, call_ms,
+                     {"median_launch_us": round(med(call_ms) * 1e3, 2)})
+    roof_call.pop("traffic")
 
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s at 128K/1M ctx; index-build tok/s",
@@ -209,30 +229,55 @@ def main():
                    "clusters": C, "iters": T, "steady": [w.n_sink, w.n_recent],
                    "n_retrieve": nr, "decode_steps": nds, "cache_flush": flush is not None},
         "decode_call_us": round(med(call_ms) * 1e3, 2),
+        "retrieved_tokens_per_kv_head": round(Er, 1),
         "decode_hbm_GBps": round(call_gbs, 1),
         "decode_hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4),
         "decode_bytes_per_call": call_bytes,
         "exact_tokens_per_kv_head": round(E, 1),
         "index_build_tok_s": round(build_tok_s, 1),
         "index_build_ms": round(med(build_ms), 3),
-        "kernel_us": {"assign": round(statistics.mean(assign_ms) * 1e3, 2),
+        "kernel_us": {"assign": round(mean(assign_ms) * 1e3, 2),
                       "sort": round(statistics.mean(sort_ms) * 1e3, 2),
                       "update": round(statistics.mean(update_ms) * 1e3, 2) if update_ms else None,
-                      "finalise": round(fin_ms * 1e3, 2),
+                      "finalise": round(statistics.mean(fin_ms) * 1e3, 2),
                       "decode_call": round(med(call_ms) * 1e3, 2),
                       "dec_stream": round(statistics.mean(stream_ms) * 1e3, 2),
                       "dec_select": round(statistics.mean(select_ms) * 1e3, 2) if select_ms
                       else None,
                       "dec_retrieve": round(statistics.mean(retrieve_ms) * 1e3, 2)},
         "dominant_kernel": dominant,
-        "roofline": roof,
-        "roofline_assign": roof_assign,
-        "roofline_decode": roof_decode,
-        "roofline_dec_stream": roof_stream,
+        "step_ms_by_kernel": {k: round(v, 3) for k, v in per_step.items()},
+        "roofline": roofs[dominant],
+        "roofline_by_kernel": roofs,
+        "roofline_decode_call": roof_call,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_decode_steps)
     print(json.dumps(res), flush=True)
+
+
+def kernel_sources_hash() -> str:
+    """Hash of the HIP sources: traffic figures are only valid for the kernels they measured."""
+    import hashlib
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "kv_vector_index_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic() -> dict:
+    """HBM bytes per launch of each kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by the calibration copy), if it was taken from the
+    current kernel sources; otherwise no figures."""
+    path = os.path.join(ROOT, "profiles", "traffic_llama128k.json")
+    if not os.path.exists(path):
+        return {}
+    t = json.load(open(path))
+    if t.get("sources_sha1") != kernel_sources_hash():
+        return {}
+    return t.get("bytes_per_launch", {})
 
 
 def cpu_baseline(w, x, n_steps):

@@ -164,16 +164,18 @@ wave_status wave_dense_decode_attention(const wave_decode_params* p, const void*
                                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
- * Tracing: kernel-boundary events
+ * Tracing: per-kernel timing events
  * ------------------------------------------------------------------------------------
- * The *_traced variants behave exactly like their plain counterparts and additionally
- * record caller-created HIP events on `stream`: events[i] right before the i-th kernel of
- * the call is enqueued and one more after the last, so kernel i spans events[i] to
- * events[i + 1]. At most `capacity` events are recorded; `recorded` returns the count.
+ * The *_traced variants behave exactly like their plain counterparts and additionally time
+ * their kernels with caller-created HIP events: events[2i] and events[2i + 1] are recorded
+ * at the start and at the end of the execution of the i-th kernel of the call (through
+ * hipExtLaunchKernel), so hipEventElapsedTime(events[2i], events[2i + 1]) is that kernel's
+ * duration. Kernels beyond capacity / 2 run untimed; `recorded` returns the number of events
+ * used (twice the number of timed kernels).
  * Kernel order, build: key norms (if any indexed token), seeds, then per pass: assign,
  * sort, and (all passes but the last) update; then finalise, steady-row copy (if
  * n_sink + n_recent > 0), objective (if requested). Decode: stream, select (only when
- * n_clusters > 16384), retrieve.
+ * n_clusters > 16384 or n_retrieve > 1024), retrieve. Dense decode: partial, merge.
  */
 typedef struct {
   hipEvent_t* events;   /* capacity events created by the caller (hipEventCreate) */

@@ -183,8 +183,9 @@ def wave_index_build(p: wave_build_params, k, v, k_out, v_out, index: IndexTenso
                      stream=None, events=None) -> int:
     """Enqueue the index build (see wave_index_build in include/wave_index.h).
 
-    With `events` (a list of hipEvent_t handles) the traced variant records kernel-boundary
-    events; returns the number recorded (0 without events)."""
+    With `events` (a list of created hipEvent_t handles) the traced variant times its
+    kernels: events 2i and 2i + 1 bracket the execution of kernel i; returns the number of
+    events used (0 without events)."""
     idx = index.c_struct()
     args = (ctypes.byref(p), _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out), ctypes.byref(idx),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))

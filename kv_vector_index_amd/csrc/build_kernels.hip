@@ -466,56 +466,34 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t st, Tracer* tr) {
   const int64_t nidx = a.idx_hi - a.idx_lo;
   const dim3 gseg((a.kseg + 15) / 16, a.nseg, BH);
   hipError_t e;
-#define WAVE_CHECK()                          \
-  do {                                        \
-    e = hipGetLastError();                    \
-    if (e != hipSuccess) return e;            \
+#define WAVE_TRY(X)                 \
+  do {                              \
+    e = (X);                        \
+    if (e != hipSuccess) return e;  \
   } while (0)
   if (nidx > 0) {
     const int nb = (int)std::min<int64_t>((nidx + 15) / 16, 4096);
-    Tracer::mark(tr, st);
-    hipLaunchKernelGGL(k_norms, dim3(nb, BH), dim3(256), 0, st, a);
-    WAVE_CHECK();
+    WAVE_TRY(launch(tr, k_norms, dim3(nb, BH), dim3(256), 0, st, a));
   }
-  Tracer::mark(tr, st);
-  hipLaunchKernelGGL(k_seeds, gseg, dim3(256), 0, st, a, a.mu[0]);
-  WAVE_CHECK();
+  WAVE_TRY(launch(tr, k_seeds, gseg, dim3(256), 0, st, a, a.mu[0]));
   const dim3 gasg((a.S + kAsgPoints - 1) / kAsgPoints, a.nseg, BH);
   for (int t = 1; t <= a.T; ++t) {
     const uint16_t* cur = a.mu[(t - 1) & 1];
-    Tracer::mark(tr, st);
-    hipLaunchKernelGGL(k_assign, gasg, dim3(256), 0, st, a, cur);
-    WAVE_CHECK();
-    Tracer::mark(tr, st);
-    hipLaunchKernelGGL(k_sort, dim3(a.nseg, BH), dim3(kSortThreads), 0, st, a);
-    WAVE_CHECK();
-    if (t < a.T) {
-      Tracer::mark(tr, st);
-      hipLaunchKernelGGL(k_update, gseg, dim3(256), 0, st, a, cur, a.mu[t & 1]);
-      WAVE_CHECK();
-    }
+    WAVE_TRY(launch(tr, k_assign, gasg, dim3(256), 0, st, a, cur));
+    WAVE_TRY(launch(tr, k_sort, dim3(a.nseg, BH), dim3(kSortThreads), 0, st, a));
+    if (t < a.T) WAVE_TRY(launch(tr, k_update, gseg, dim3(256), 0, st, a, cur, a.mu[t & 1]));
   }
-  Tracer::mark(tr, st);
-  hipLaunchKernelGGL(k_finalise, gseg, dim3(256), 0, st, a);
-  WAVE_CHECK();
+  WAVE_TRY(launch(tr, k_finalise, gseg, dim3(256), 0, st, a));
   if (a.n_sink + a.n_recent > 0) {
     const int nb = (int)std::min<int64_t>(((int64_t)a.n_sink + a.n_recent + 15) / 16, 1024);
-    Tracer::mark(tr, st);
-    hipLaunchKernelGGL(k_steady, dim3(nb, BH), dim3(256), 0, st, a);
-    WAVE_CHECK();
+    WAVE_TRY(launch(tr, k_steady, dim3(nb, BH), dim3(256), 0, st, a));
   }
-  if (a.objective) {
-    Tracer::mark(tr, st);
-    hipLaunchKernelGGL(k_objective, dim3(BH), dim3(256), 0, st, a);
-    WAVE_CHECK();
-  }
-  if (a.last_mu) {
-    e = hipMemcpyAsync(a.last_mu, a.mu[(a.T - 1) & 1],
-                       (size_t)BH * a.C * kHeadDim * sizeof(uint16_t), hipMemcpyDeviceToDevice, st);
-    if (e != hipSuccess) return e;
-  }
-#undef WAVE_CHECK
-  Tracer::mark(tr, st);
+  if (a.objective) WAVE_TRY(launch(tr, k_objective, dim3(BH), dim3(256), 0, st, a));
+  if (a.last_mu)
+    WAVE_TRY(hipMemcpyAsync(a.last_mu, a.mu[(a.T - 1) & 1],
+                            (size_t)BH * a.C * kHeadDim * sizeof(uint16_t),
+                            hipMemcpyDeviceToDevice, st));
+#undef WAVE_TRY
   return hipSuccess;
 }
 

@@ -1101,14 +1101,10 @@ __global__ __launch_bounds__(kDecThreads) void k_dense_merge(DecodeArgs a) {
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   const int BH = a.B * a.Hkv;
-  Tracer::mark(tr, s);
-  hipLaunchKernelGGL(k_dec_stream<G>, dim3(a.nS + a.nSt, BH), dim3(kDecThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(tr, k_dec_stream<G>, dim3(a.nS + a.nSt, BH), dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
   if (!a.local_select) {
-    Tracer::mark(tr, s);
-    hipLaunchKernelGGL(k_dec_select, dim3(BH), dim3(kDecThreads), 0, s, a);
-    e = hipGetLastError();
+    e = launch(tr, k_dec_select, dim3(BH), dim3(kDecThreads), 0, s, a);
     if (e != hipSuccess) return e;
   }
   // dynamic LDS of the retrieve kernel: the group scores when it selects for itself
@@ -1119,25 +1115,15 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr
   const size_t lds = a.local_select ? (size_t)(a.Cp + 4 * kDecThreads - 1) /
                                           (4 * kDecThreads) * (4 * kDecThreads) * sizeof(float)
                                     : 0;
-  Tracer::mark(tr, s);
-  hipLaunchKernelGGL(k_dec_retrieve<G>, dim3(a.nB, BH), dim3(kDecThreads), lds, s, a);
-  e = hipGetLastError();
-  Tracer::mark(tr, s);
-  return e;
+  return launch(tr, k_dec_retrieve<G>, dim3(a.nB, BH), dim3(kDecThreads), (uint32_t)lds, s, a);
 }
 
 template <int G>
 static hipError_t launch_dense_g(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   const int BH = a.B * a.Hkv;
-  Tracer::mark(tr, s);
-  hipLaunchKernelGGL(k_dense_partial<G>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(tr, k_dense_partial<G>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
-  Tracer::mark(tr, s);
-  hipLaunchKernelGGL(k_dense_merge<G>, dim3(BH), dim3(kDecThreads), 0, s, a);
-  e = hipGetLastError();
-  Tracer::mark(tr, s);
-  return e;
+  return launch(tr, k_dense_merge<G>, dim3(BH), dim3(kDecThreads), 0, s, a);
 }
 
 #define WAVE_DISPATCH_G(FN, A, S, T)          \

@@ -1,6 +1,7 @@
 // Device helpers shared by the wave-index kernels (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -84,5 +85,20 @@ __device__ __forceinline__ void st_dev(T* p, T v) {
 // Wait until this wave's earlier vector-memory operations have completed (device-coherent
 // stores acknowledged); also a compiler barrier for memory accesses.
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Enqueue a kernel; with a tracer that has room, its next two events time this kernel
+// (recorded at the start and the end of its execution). Returns the launch status.
+template <typename F, typename... Args>
+inline hipError_t launch(Tracer* tr, F kernel, dim3 grid, dim3 block, uint32_t lds,
+                         hipStream_t s, Args... args) {
+  if (tr && tr->ev && tr->n + 2 <= tr->cap) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, tr->ev[tr->n], tr->ev[tr->n + 1], 0u,
+                          args...);
+    tr->n += 2;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace wave

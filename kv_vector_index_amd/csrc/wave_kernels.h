@@ -12,14 +12,12 @@ constexpr int kRowBytes = 256;     // one bf16 row of d = 128
 constexpr int kMaxGroup = 8;       // largest GQA group (query heads per KV head)
 constexpr float kLog2eHost = 1.4426950408889634f;
 
-// Optional kernel-boundary events: mark() records the next caller-provided event on the
-// stream right before each kernel launch, and once after the last one.
+// Optional per-kernel timing events: the launch helper (wave_common.h) hands the next two
+// caller-provided events to hipExtLaunchKernel, which records them at the start and the end
+// of that kernel's execution.
 struct Tracer {
   hipEvent_t* ev;
   int cap, n;
-  static void mark(Tracer* t, hipStream_t s) {
-    if (t && t->ev && t->n < t->cap) (void)hipEventRecord(t->ev[t->n++], s);
-  }
 };
 
 // ---------------------------------------------------------------- decode

@@ -351,3 +351,54 @@ def test_exact_score_ties_select_lowest_ids(C):
         assert np.array_equal(got[got >= 0], want), "tie-break differs from lowest-id order"
         assert np.all(got[len(want):] == -1)
         tl.oracle_decode_check(layer, idx, q[0], layer.L0 + 1, n_r, out, lse, sel)
+
+
+def test_traced_calls_time_each_kernel_and_match_the_plain_calls(tiny):
+    """The traced variants give bit-identical results and time every kernel with one
+    start / end event pair (build: norms, seeds, passes x (assign, sort) + (passes - 1) x
+    update, finalise, steady, objective; decode: stream, retrieve)."""
+    t = tl.torch()
+    w, x, layer = tiny
+    T = 3
+    p = layer.build_params(T)
+    ws = t.empty(wi.wave_index_workspace_size(p), dtype=t.uint8, device="cuda")
+
+    def events(n):
+        ev = [t.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in ev:
+            e.record()
+        return ev
+
+    idx_a = wi.alloc_index(layer.B, layer.H, layer.C, layer.L0)
+    idx_b = wi.alloc_index(layer.B, layer.H, layer.C, layer.L0)
+    wi.wave_index_build(p, layer.k, layer.v, layer.k_out, layer.v_out, idx_a, ws)
+    ko_a = layer.k_out.clone()
+    n_build = 2 * (3 * T + 4)
+    bev = events(n_build + 4)                    # room to spare: only what is used is counted
+    got = wi.wave_index_build(p, layer.k, layer.v, layer.k_out, layer.v_out, idx_b, ws,
+                              events=[e.cuda_event for e in bev])
+    t.cuda.synchronize()
+    assert got == n_build
+    for f in ("centroid_mean", "value_sum", "cluster_size", "cluster_offset", "labels", "perm"):
+        assert t.equal(getattr(idx_a, f), getattr(idx_b, f)), f
+    assert t.equal(ko_a, layer.k_out)
+    durs = [bev[2 * i].elapsed_time(bev[2 * i + 1]) for i in range(n_build // 2)]
+    assert all(d > 0 for d in durs), durs
+    layer.k_out[:, :, layer.L0:] = layer.k[:, :, layer.L0:]
+    layer.v_out[:, :, layer.L0:] = layer.v[:, :, layer.L0:]
+    L, n_r = layer.L0 + 1, w.n_retrieve
+    dp = layer.decode_params(L, n_r)
+    q = tl.to_dev(x.q[0])
+    outs = []
+    for traced in (False, True):
+        out = t.empty(layer.B, layer.Hq, 128, dtype=t.float32, device="cuda")
+        dws = wi.alloc_decode_workspace(dp)
+        ev = events(6) if traced else None
+        n = wi.wave_decode_attention(dp, q, layer.k_out, layer.v_out, idx_b, out, None, None,
+                                     dws, events=None if ev is None else [e.cuda_event for e in ev])
+        t.cuda.synchronize()
+        if traced:
+            assert n == 4
+            assert ev[0].elapsed_time(ev[1]) > 0 and ev[2].elapsed_time(ev[3]) > 0
+        outs.append(out.cpu())
+    assert t.equal(outs[0], outs[1])
