@@ -9,8 +9,13 @@ the call finds its data in HBM rather than in the 256 MB Infinity Cache, as it w
 the other layers of a model; the per-kernel figures come from HIP events that the library
 records between its kernels (the flush lies outside them).
 
-A 256 MiB device-to-device copy runs once before the warmup: its FETCH_SIZE / WRITE_SIZE
-counters calibrate the HBM-traffic figures taken from rocprofv3 runs of this script.
+The timed steps run the plain entry points with HIP events around each call (call time =
+first kernel start to last kernel end, as the stream sees it); one more step runs the traced
+entry points, whose per-kernel start / end events give the kernel breakdown and rooflines
+(those events add a few microseconds around each kernel, so they are not used for the call
+time). A 256 MiB device-to-device copy runs once before the warmup: its FETCH_SIZE /
+WRITE_SIZE counters calibrate the HBM-traffic figures taken from rocprofv3 runs of this
+script.
 
 Prints one JSON line. `value` is decode-attention tokens/s of the layer (batch / median time
 of one decode call); the index-build rate and achieved HBM bandwidth are extra fields.
@@ -100,59 +105,73 @@ def main():
     calib[1].copy_(calib[0])                                                 # calibration copy
 
     # start / end events of every kernel: build = norms, seeds, T x (assign, sort),
-    # (T - 1) x update, finalise, steady; decode = stream, [select], retrieve
+    # (T - 1) x update, finalise, steady; decode = stream, select, retrieve
     n_build_ev = 2 * (3 * T + 3)
-    local = C <= 16384 and nr <= 1024
-    n_dec_ev = 4 if local else 6
+    n_dec_ev = 6
     def events(n):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for e in ev:
             e.record()
         return ev
 
-    def one_step(bev, dev_):
+    def one_step(bev, dev_, timed=None):
+        """One build + nds decode calls. bev / dev_: per-kernel event lists (traced pass);
+        timed: (build pair, [decode pairs]) of events around each call (untraced pass)."""
+        if timed:
+            timed[0][0].record()
         wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws,
                             events=None if bev is None else [e.cuda_event for e in bev])
+        if timed:
+            timed[0][1].record()
         for s in range(nds):
             if flush is not None:
                 flush.sum()
+            if timed:
+                timed[1][s][0].record()
             wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, out, lse, sel[s], dws,
                                      events=None if dev_ is None else
                                      [e.cuda_event for e in dev_[s]])
+            if timed:
+                timed[1][s][1].record()
 
     for _ in range(args.warmup):
         one_step(None, None)
     torch.cuda.synchronize()
-    bevs = [events(n_build_ev) for _ in range(args.steps)]
-    devs = [[events(n_dec_ev) for _ in range(nds)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
 
+    # ---- timed pass: untraced calls, HIP events around each call on the stream
+    pair = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
+    tev = [(pair(), [pair() for _ in range(nds)]) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(bevs[i], devs[i])
+        one_step(None, None, tev[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # ---- per-kernel durations (ms) from the library's per-kernel start / end events
     el = lambda a, b: a.elapsed_time(b)  # noqa: E731
+    build_ms = [el(*t[0]) for t in tev]
+    call_ms = [el(*c) for t in tev for c in t[1]]
+
+    # ---- traced pass (one step): each kernel's duration from its start / end events
+    bev = events(n_build_ev)
+    dev_ = [events(n_dec_ev) for _ in range(nds)]
+    torch.cuda.synchronize()
+    one_step(bev, dev_)
+    torch.cuda.synchronize()
     kd = lambda ev, i: el(ev[2 * i], ev[2 * i + 1])  # noqa: E731
-    build_ms = [el(b[0], b[-1]) for b in bevs]
     assign_ms, sort_ms, update_ms, fin_ms = [], [], [], []
-    for b in bevs:
-        i = 2                      # after norms, seeds
-        for p in range(T):
-            assign_ms.append(kd(b, i))
-            sort_ms.append(kd(b, i + 1))
-            i += 2
-            if p < T - 1:
-                update_ms.append(kd(b, i))
-                i += 1
-        fin_ms.append(kd(b, i))
-    call_ms = [el(e[0], e[-1]) for st in devs for e in st]
-    stream_ms = [kd(e, 0) for st in devs for e in st]
-    select_ms = [kd(e, 1) for st in devs for e in st] if not local else []
-    retrieve_ms = [kd(e, n_dec_ev // 2 - 1) for st in devs for e in st]
+    i = 2                          # after norms, seeds
+    for p in range(T):
+        assign_ms.append(kd(bev, i))
+        sort_ms.append(kd(bev, i + 1))
+        i += 2
+        if p < T - 1:
+            update_ms.append(kd(bev, i))
+            i += 1
+    fin_ms.append(kd(bev, i))
+    stream_ms = [kd(e, 0) for e in dev_]
+    select_ms = [kd(e, 1) for e in dev_]
+    retrieve_ms = [kd(e, 2) for e in dev_]
     med = statistics.median
 
     # ---- algorithmic work (per decode call and per assignment launch)
@@ -179,10 +198,12 @@ def main():
     steady_mean = w.n_sink + w.n_recent + (nds + 1) / 2
     stream_bytes = (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * steady_mean
                     + 2 * G * d) * BH
-    # retrieve kernel: retrieved K/V rows, the removed clusters' value sums, logits, sizes
-    # and offsets, the group scores it selects from, q, out
-    retrieve_bytes = (4 * d * Er + (2 * d + 4 * G + 8) * nr + 4 * C + 2 * G * d
-                      + 4 * G * d) * BH
+    # select kernel: the group scores, sizes and offsets of the retrieved clusters, and the
+    # published list (ids, first virtual row, first cache row)
+    select_bytes = (4 * C + 8 * nr + 12 * nr) * BH
+    # retrieve kernel: retrieved K/V rows, the removed clusters' value sums and logits, the
+    # list entries, q, out
+    retrieve_bytes = (4 * d * Er + (2 * d + 4 * G + 12) * nr + 2 * G * d + 4 * G * d) * BH
     n_idx = [max(0, min((s + 1) * w.segment_size, L0 - w.n_recent) - max(s * w.segment_size,
                                                                            w.n_sink))
              for s in range(w.n_segments)]
@@ -209,10 +230,11 @@ def main():
     roofs = {
         "k_assign": roof("k_assign", "mfma", assign_flop, assign_ms),
         "k_dec_stream": roof("k_dec_stream", "hbm", stream_bytes, stream_ms),
+        "k_dec_select": roof("k_dec_select", "hbm", select_bytes, select_ms),
         "k_dec_retrieve": roof("k_dec_retrieve", "hbm", retrieve_bytes, retrieve_ms),
     }
     per_step = {"k_assign": T * mean(assign_ms), "k_dec_stream": nds * mean(stream_ms),
-                "k_dec_retrieve": nds * mean(retrieve_ms)}
+                "k_dec_select": nds * mean(select_ms), "k_dec_retrieve": nds * mean(retrieve_ms)}
     dominant = max(per_step, key=per_step.get)
     roof_call = roof("decode call", "hbm", call_bytes, call_ms,
                      {"median_launch_us": round(med(call_ms) * 1e3, 2)})
@@ -242,8 +264,7 @@ def main():
                       "finalise": round(statistics.mean(fin_ms) * 1e3, 2),
                       "decode_call": round(med(call_ms) * 1e3, 2),
                       "dec_stream": round(statistics.mean(stream_ms) * 1e3, 2),
-                      "dec_select": round(statistics.mean(select_ms) * 1e3, 2) if select_ms
-                      else None,
+                      "dec_select": round(statistics.mean(select_ms) * 1e3, 2),
                       "dec_retrieve": round(statistics.mean(retrieve_ms) * 1e3, 2)},
         "dominant_kernel": dominant,
         "step_ms_by_kernel": {k: round(v, 3) for k, v in per_step.items()},

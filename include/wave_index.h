@@ -174,8 +174,8 @@ wave_status wave_dense_decode_attention(const wave_decode_params* p, const void*
  * used (twice the number of timed kernels).
  * Kernel order, build: key norms (if any indexed token), seeds, then per pass: assign,
  * sort, and (all passes but the last) update; then finalise, steady-row copy (if
- * n_sink + n_recent > 0), objective (if requested). Decode: stream, select (only when
- * n_clusters > 16384 or n_retrieve > 1024), retrieve. Dense decode: partial, merge.
+ * n_sink + n_recent > 0), objective (if requested). Decode: stream, select, retrieve.
+ * Dense decode: partial, merge.
  */
 typedef struct {
   hipEvent_t* events;   /* capacity events created by the caller (hipEventCreate) */

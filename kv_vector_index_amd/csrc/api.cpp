@@ -137,10 +137,11 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   const int64_t steady_max = (int64_t)p->n_sink + p->n_recent + (p->kv_capacity - p->index_len);
   sh->nStMax = (int)((steady_max + wave::kTokChunk - 1) / wave::kTokChunk);
   // retrieve workgroups: about kRowsPerItem virtual rows each (a retrieved cluster's tokens
-  // plus its estimate-removal row) at the average cluster size
+  // plus its estimate-removal row) at 1.5x the average cluster size (the retrieved clusters
+  // run larger than average)
   const int64_t indexed = p->index_len - p->n_sink - p->n_recent;
   const int64_t avg = indexed > p->n_clusters ? indexed / p->n_clusters : 1;
-  sh->nB = clampi(((int64_t)p->n_retrieve * (avg + 1) + wave::kRowsPerItem - 1) /
+  sh->nB = clampi(((int64_t)p->n_retrieve * (avg + 1) * 3 / 2 + wave::kRowsPerItem - 1) /
                       wave::kRowsPerItem, 1, wave::kMaxRetrieveWG);
   sh->nBDense = clampi((p->kv_capacity + 1023) / 1024, 1, 512);
   sh->rcap = p->n_retrieve > 0 ? p->n_retrieve : 1;
@@ -164,7 +165,7 @@ size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* b
   int32_t* sel_ts = cv.take<int32_t>(BH * ((size_t)sh.rcap + 1));
   int32_t* sel_coff = cv.take<int32_t>(BH * (size_t)sh.rcap);
   int32_t* sel_n = cv.take<int32_t>(BH);
-  int32_t* wg_r0 = cv.take<int32_t>(BH * (wave::kMaxRetrieveWG + 1));
+  int32_t* wg_info = cv.take<int32_t>(BH * wave::kMaxRetrieveWG * 4);
   float* part = cv.take<float>(BH * nPmax * G * wave::kPartStride);
   if (a) {
     a->counter = counter;
@@ -175,7 +176,7 @@ size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* b
     a->sel_ts = sel_ts;
     a->sel_coff = sel_coff;
     a->sel_n = sel_n;
-    a->wg_r0 = wg_r0;
+    a->wg_info = wg_info;
     a->part = part;
   }
   return cv.off;
@@ -364,8 +365,6 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   a.nSt = (int)((n_steady + wave::kTokChunk - 1) / wave::kTokChunk);
   a.nB = sh.nB;
   a.nP = a.nSt + a.nS + a.nB;
-  a.local_select =
-      (p->n_clusters <= wave::kLocalSelMax && p->n_retrieve <= wave::kSelMax) ? 1 : 0;
   return wave::launch_decode(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
 }
 

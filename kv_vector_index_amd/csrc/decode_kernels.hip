@@ -9,24 +9,26 @@
 // sums V_j, one query head's output is
 //     out = (sum_E e^{a_i} v_i + sum_U e^{s_j} V_j) / (sum_E e^{a_i} + sum_U n_j e^{s_j}).
 //
-// MI355X design, two small kernels per call (plus a one-workgroup-per-head select kernel
-// when an index has more than kLocalSelMax clusters per head or the budget exceeds kSelMax):
+// MI355X design, three small kernels per call:
 //   stream    one workgroup per 128 clusters or 128 steady tokens of a (b, kv-head): stream
 //             the centroid rows, value-sum rows and sizes once (HBM-bound), store each query
 //             head's logit and the group-mean score, and fold the estimate of ALL non-empty
 //             clusters (or the exact steady tokens) into one partial softmax state.
-//   retrieve  nB workgroups per (b, kv-head). Each recomputes the same exact top-n_r
-//             selection from the group scores held in registers (a histogram over the
-//             scores' value range, then an exact rank of the few keys in the bin of the cut;
-//             ties to the lower id), lists the retrieved clusters in LDS, and walks its share
-//             of their "virtual rows": every token of a retrieved cluster (exact attention;
-//             a retrieved cluster is a contiguous run of cache rows in the index layout) and
-//             one row per cluster that removes the estimate term the stream kernel added.
-//             Each workgroup also folds a share of the stream partials; the last workgroup
-//             of a (b, kv-head) merges the retrieve partials by log-sum-exp into out / lse.
+//   select    one 512-thread workgroup per (b, kv-head) finds the exact top-n_r clusters
+//             (ties to the lower id) from the group scores held in registers and publishes
+//             them in ascending id order, each with its first "virtual row" (see below) and
+//             first cache row, plus the first listed cluster of every retrieve workgroup.
+//   retrieve  nB workgroups per (b, kv-head) walk the virtual rows of the retrieved clusters:
+//             every token of a retrieved cluster (exact attention; a retrieved cluster is a
+//             contiguous run of cache rows in the index layout) and one row per cluster that
+//             removes the estimate term the stream kernel added. Each workgroup also folds a
+//             share of the stream partials; the last workgroup of a (b, kv-head) merges the
+//             retrieve partials by log-sum-exp into out / lse.
 // Rows are read 16 lanes per 256-byte row (4 rows per wave instruction, fully coalesced) and
 // each K/V row is shared by the G query heads of its group.
 #include <float.h>
+
+#include <type_traits>
 
 #include "wave_common.h"
 #include "wave_kernels.h"
@@ -182,19 +184,19 @@ __device__ __forceinline__ void write_block_partial(Online<G>& st, const float* 
 }
 
 // Log-sum-exp merge of the partials p0, p0 + step, ... (< n) of parts, for the head/dim
-// element idx = h * 128 + d; 8 partials in flight per round. DEV: device-coherent loads
-// (partials written by other workgroups of the same kernel).
-template <bool DEV>
+// element idx = h * 128 + d, NBATCH partials in flight per round. DEV: device-coherent loads
+// (partials written by other workgroups of the same kernel). NBATCH partials per round.
+template <bool DEV, int NBATCH = 8>
 __device__ __forceinline__ void merge_partials(const float* parts, int G, int idx, int p0,
                                                int step, int n, float& M, float& Ls, float& O) {
   const int h = idx >> 7, d = idx & 127;
   M = kNegInf;
   Ls = 0.f;
   O = 0.f;
-  for (int p = p0; p < n; p += 8 * step) {
-    float pm[8], pl[8], po[8];
+  for (int p = p0; p < n; p += NBATCH * step) {
+    float pm[NBATCH], pl[NBATCH], po[NBATCH];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NBATCH; ++k) {
       const int pk = p + k * step;
       const float* pp = parts + ((size_t)pk * G + h) * kPartStride;
       if (pk < n) {
@@ -208,13 +210,13 @@ __device__ __forceinline__ void merge_partials(const float* parts, int G, int id
     }
     float mx = M;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) mx = fmaxf(mx, pm[k]);
+    for (int k = 0; k < NBATCH; ++k) mx = fmaxf(mx, pm[k]);
     if (mx == kNegInf) continue;
     const float sc = fast_exp2(M - mx);
     O *= sc;
     Ls *= sc;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NBATCH; ++k) {
       const float f = fast_exp2(pm[k] - mx);
       O += f * po[k];
       Ls += f * pl[k];
@@ -281,14 +283,16 @@ __device__ __forceinline__ void attend_rows(const DecodeArgs& a, int bh, const u
 }
 
 // ------------------------------------------------------------------------------------
-// block-wide helpers (256 threads)
+// block-wide helpers for NT-thread workgroups
 // ------------------------------------------------------------------------------------
+template <int NT>
 struct ScanTmp {
-  uint32_t w[kDecThreads / 64];
+  uint32_t w[NT / 64];
 };
 
 // exclusive scan over the block; *total = block sum
-__device__ __forceinline__ uint32_t scan_excl(uint32_t x, ScanTmp& tmp, uint32_t* total) {
+template <int NT>
+__device__ __forceinline__ uint32_t scan_excl(uint32_t x, ScanTmp<NT>& tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t v = x;
 #pragma unroll
@@ -300,7 +304,7 @@ __device__ __forceinline__ uint32_t scan_excl(uint32_t x, ScanTmp& tmp, uint32_t
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kDecThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const uint32_t t = tmp.w[w];
     before += (w < wave) ? t : 0u;
     tot += t;
@@ -318,20 +322,40 @@ __device__ __forceinline__ uint32_t wave_prefix_small(uint32_t c, uint32_t& wave
   return __popcll(b0 & lt) + 2u * __popcll(b1 & lt) + 4u * __popcll(b2 & lt);
 }
 
+// Reductions over the 64 lanes of a wave without LDS: four DPP steps make each 16-lane row
+// uniform, then the four rows are read back as scalars. Every lane gets the result.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T x, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  auto mv = [](T v, auto ctrl) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                          decltype(ctrl)::value, 0xF, 0xF,
+                                                          false));
+  };
+  x = op(x, mv(x, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+  x = op(x, mv(x, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+  x = op(x, mv(x, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  x = op(x, mv(x, std::integral_constant<int, 0x140>{}));  // row_mirror
+  const int xi = __builtin_bit_cast(int, x);
+  const T r0 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(xi, 0));
+  const T r1 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(xi, 16));
+  const T r2 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(xi, 32));
+  const T r3 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(xi, 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
 struct Red3 {
   float mn, mx;
   uint32_t n;
 };
 
 // block min / max / count
+template <int NT>
 __device__ __forceinline__ Red3 block_red3(Red3 r, float (*s)[3]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    r.mn = fminf(r.mn, __shfl_xor(r.mn, off));
-    r.mx = fmaxf(r.mx, __shfl_xor(r.mx, off));
-    r.n += __shfl_xor(r.n, off);
-  }
+  r.mn = wave_reduce(r.mn, [](float a, float b) { return fminf(a, b); });
+  r.mx = wave_reduce(r.mx, [](float a, float b) { return fmaxf(a, b); });
+  r.n = wave_reduce(r.n, [](uint32_t a, uint32_t b) { return a + b; });
   if (lane == 0) {
     s[wave][0] = r.mn;
     s[wave][1] = r.mx;
@@ -340,13 +364,75 @@ __device__ __forceinline__ Red3 block_red3(Red3 r, float (*s)[3]) {
   __syncthreads();
   Red3 t{kPosInf, kNegInf, 0u};
 #pragma unroll
-  for (int w = 0; w < kDecThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     t.mn = fminf(t.mn, s[w][0]);
     t.mx = fmaxf(t.mx, s[w][1]);
     t.n += __float_as_uint(s[w][2]);
   }
   __syncthreads();
   return t;
+}
+
+// Ordered visit of nsl (<= NSMAX) slices of E entries per thread of an NT-thread block;
+// entry (slice i, thread t, element e) has order (i * NT + t) * E + e. hit(i, e) selects
+// entries; visit(i, e, rank) receives each selected entry with its rank in that order.
+// Returns the count. Slices are unrolled (i is a compile-time index for register data).
+template <int NT, int NSMAX, int E, typename Hit, typename Visit>
+__device__ __forceinline__ uint32_t ordered_visit(int nsl, Hit hit, Visit visit, uint32_t* wt) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NSMAX; ++i)
+    if (i < nsl) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) c += hit(i, e) ? 1u : 0u;
+      uint32_t t;
+      wave_prefix_small(c, t);
+      if (lane == 0) wt[i * NW + wave] = t;
+    }
+  __syncthreads();
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < NSMAX; ++i)
+    if (i < nsl) {
+      bool p[E];
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        p[e] = hit(i, e);
+        c += p[e] ? 1u : 0u;
+      }
+      uint32_t t;
+      uint32_t k = wave_prefix_small(c, t) + acc;
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t v = wt[i * NW + w];
+        k += w < wave ? v : 0u;
+        acc += v;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (p[e]) visit(i, e, k++);
+    }
+  __syncthreads();
+  return acc;
+}
+
+// Histogram increment with the lanes of a wave that hit the same bin combined first (wave
+// ballots over the BITS bits of the bin give each lane its peers), so a bin receives at most
+// one LDS atomic per wave instead of one per lane. Lanes with active = false take part in
+// the ballots only.
+template <int BITS>
+__device__ __forceinline__ void hist_add(uint32_t* hist, int bin, bool active) {
+  uint64_t peers = __ballot(active);
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const bool bit = (bin >> b) & 1;
+    const uint64_t m = __ballot(active && bit);
+    peers &= bit ? m : ~m;
+  }
+  const uint64_t below = (1ull << (threadIdx.x & 63)) - 1ull;
+  if (active && (peers & below) == 0) atomicAdd(&hist[bin], (uint32_t)__popcll(peers));
 }
 
 // Publish this block's device-coherent writes and count one more arrival on *counter;
@@ -365,18 +451,22 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n) {
 // { j : s^_j > Tkey or (s^_j == Tkey and j <= Tid) } for the n_r-th pair (Tkey, Tid) in
 // (score descending, id ascending) order. Empty clusters have s^ = -inf and never qualify.
 // ------------------------------------------------------------------------------------
+constexpr int kSelWaves = kSelThreads / 64;
+
 struct SelShared {
-  uint32_t hist[kHistBins];  // value-range histogram; reused for the LDS cluster lists
+  uint32_t hist[kHistBins];  // value-range histogram; then the selected ids
   float ck[kCand];
   int32_t ci[kCand];
-  uint32_t wt[kKeySlices * 4];
-  float red[4][3];
+  float cand_key[kCandMax];  // scores at or above the bound, ascending ids
+  int32_t cand_id[kCandMax];
+  uint32_t wt[kSelSlices * kSelWaves];
+  float red[kSelWaves][3];
+  int32_t wgr[kMaxRetrieveWG + 1];
   uint32_t u[4];
   float tkey;
   int32_t tid;
-  ScanTmp tmp;
+  ScanTmp<kSelThreads> tmp;
 };
-static_assert(3 * kSelMax + 1 <= kHistBins, "cluster lists must fit in the histogram space");
 
 __device__ __forceinline__ float4 neg4() { return make_float4(kNegInf, kNegInf, kNegInf, kNegInf); }
 
@@ -390,10 +480,10 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Histogram bins over a score range [lo, hi], monotone in the score (every step rounds
-// monotonically). Linear in the value when the range allows it; otherwise, and on every
-// narrowing round, linear in the order-preserving integer key. Either way lo lands in bin 0
-// and hi in a later bin, so each narrowing round strictly shrinks the candidate range.
+// Histogram bins (kHistBins) over a score range [lo, hi], monotone in the score (every step
+// rounds monotonically). Linear in the value when the range allows it; otherwise, and on
+// every narrowing round, linear in the order-preserving integer key. Either way lo lands in
+// bin 0 and hi in a later bin, so each narrowing round strictly shrinks the candidate range.
 struct Binner {
   float lo, inv;   // value mode: bin = (v - lo) * inv
   uint32_t klo;    // key mode:   bin = (key(v) - klo) * kinv
@@ -412,13 +502,17 @@ struct Binner {
   }
 };
 
-// Find (Tkey, Tid) given the block-uniform range [lo, hi] of finite scores and
-// need in [1, #finite]. each(f) visits every (score, id) this thread owns; tie_id(v, need)
-// returns the need-th lowest id whose score equals v (block-uniform).
-template <typename Each, typename TieId>
+// Find (Tkey, Tid) given the block-uniform range [lo, hi] of the candidate scores and
+// need in [1, #candidates]. each(f) visits every (score, id) this thread owns; tie_id(v,
+// need) returns the need-th lowest id whose score equals v (block-uniform). NB bins.
+template <int NB, typename Each, typename TieId>
 __device__ __forceinline__ void find_threshold(Each each, TieId tie_id, float lo, float hi,
                                                uint32_t need, SelShared& sh, float& Tkey,
                                                int& Tid) {
+  constexpr int NT = kSelThreads;
+  static_assert(NB <= kHistBins && (NB & (NB - 1)) == 0 && (NB % NT == 0 || NT % NB == 0),
+                "bins");
+  constexpr int BPT = NB >= NT ? NB / NT : 1;  // bins per thread (threads >= NB own none)
   const int tid = threadIdx.x;
   bool first = true;
   for (;;) {
@@ -427,27 +521,31 @@ __device__ __forceinline__ void find_threshold(Each each, TieId tie_id, float lo
       Tid = tie_id(lo, need);
       return;
     }
-    const Binner bin(lo, hi, first);
+    const Binner b4k(lo, hi, first);
+    auto bin = [&](float v) { return b4k(v) / (kHistBins / NB); };
     first = false;
-    for (int i = tid; i < kHistBins; i += kDecThreads) sh.hist[i] = 0u;
+    for (int i = tid; i < NB; i += NT) sh.hist[i] = 0u;
     __syncthreads();
+    constexpr int BITS = __builtin_ctz(NB);
     each([&](float v, int) {
-      if (v >= lo && v <= hi) atomicAdd(&sh.hist[bin(v)], 1u);
+      const bool in = v >= lo && v <= hi;
+      hist_add<BITS>(sh.hist, in ? bin(v) : 0, in);
     });
     __syncthreads();
-    // bin b* of the need-th largest score: thread t owns 16 bins, visited descending
-    const int hb0 = kHistBins - 16 * (tid + 1);
-    uint32_t hc[16], loc = 0;
+    // bin b* of the need-th largest score: thread t owns BPT bins, visited descending
+    const int hb0 = NB - BPT * (tid + 1);
+    const bool owns = NB >= NT || tid < NB;
+    uint32_t hc[BPT], loc = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      hc[i] = sh.hist[hb0 + i];
+    for (int i = 0; i < BPT; ++i) {
+      hc[i] = owns ? sh.hist[hb0 + i] : 0u;
       loc += hc[i];
     }
     uint32_t tot;
-    uint32_t run = scan_excl(loc, sh.tmp, &tot);
+    uint32_t run = scan_excl<NT>(loc, sh.tmp, &tot);
 #pragma unroll
-    for (int i = 15; i >= 0; --i) {
-      if (run < need && run + hc[i] >= need) {
+    for (int i = BPT - 1; i >= 0; --i) {
+      if (owns && run < need && run + hc[i] >= need) {
         sh.u[0] = (uint32_t)(hb0 + i);
         sh.u[1] = run;
       }
@@ -495,7 +593,7 @@ __device__ __forceinline__ void find_threshold(Each each, TieId tie_id, float lo
         r.mx = fmaxf(r.mx, v);
       }
     });
-    r = block_red3(r, sh.red);
+    r = block_red3<NT>(r, sh.red);
     lo = r.mn;
     hi = r.mx;
     need = need2;
@@ -667,34 +765,16 @@ __device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, cons
 
 template <int G>
 __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
-  extern __shared__ float s_key[];       // local select: the group scores, -inf padded
-  __shared__ SelShared sh;
   __shared__ float s_x[G][kPartStride];  // this workgroup's share of the stream partials
+  __shared__ int32_t l_ts[kWinR + 1], l_co[kWinR], l_id[kWinR];
   const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv, w_item = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cc = lane & 15;
   const int nB = a.nB, nSP = a.nS + a.nSt;
   float* parts = a.part + (size_t)bh * a.nP * G * kPartStride;
-  int32_t* l_ts = reinterpret_cast<int32_t*>(sh.hist);  // [kSelMax + 1]
-  int32_t* l_co = l_ts + kSelMax + 1;                      // [kSelMax]
-  int32_t* l_id = l_co + kSelMax;                          // [kSelMax]
-  const bool local = a.local_select != 0;
-  const int Cp = a.Cp, ns = (Cp + 4 * kDecThreads - 1) / (4 * kDecThreads);
-
-  // ---- group scores into LDS (coalesced float4; ids 4 * (i * 256 + tid) + e)
-  if (local) {
-    const float* shat = a.shat + (size_t)bh * Cp;
-    for (int i0 = 0; i0 < ns; i0 += 8) {
-      float4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j4 = 4 * ((i0 + u) * kDecThreads + tid);
-        v[u] = (i0 + u < ns && j4 < Cp) ? *reinterpret_cast<const float4*>(shat + j4) : neg4();
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (i0 + u < ns) *reinterpret_cast<float4*>(s_key + 4 * ((i0 + u) * kDecThreads + tid)) = v[u];
-    }
-  }
+  // ---- this workgroup's virtual rows [T0, T1) and listed clusters [r_lo, r_hi)
+  const int4 info = reinterpret_cast<const int4*>(a.wg_info)[(size_t)bh * kMaxRetrieveWG + w_item];
+  const int T0 = info.x, T1 = info.y, r_lo = info.z, r_hi = info.w;
+  const int32_t* g_ts = a.sel_ts + (size_t)bh * (a.rcap + 1);
   // ---- this workgroup's stream partials w_item, w_item + nB, ... merged into s_x
   for (int idx = tid; idx < G * 128; idx += kDecThreads) {
     float M, Ls, O;
@@ -706,189 +786,33 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
       s_x[h][129] = Ls;
     }
   }
-  __syncthreads();
-
-  int nsel, V;  // retrieved clusters, their virtual rows
-  int r_lo = 0, r_hi = 0;
-  if (local) {
-    auto each = [&](auto f) {
-      for (int i = 0; i < ns; ++i) {
-        const int j4 = 4 * (i * kDecThreads + tid);
-        const float4 x = *reinterpret_cast<const float4*>(s_key + j4);
-        f(x.x, j4);
-        f(x.y, j4 + 1);
-        f(x.z, j4 + 2);
-        f(x.w, j4 + 3);
-      }
-    };
-    // Ordered visit of the ids with pred(v, j) true (ids ascend with slice, then thread,
-    // then element): each is passed with its rank; returns the count.
-    auto ordered = [&](auto pred, auto visit) -> uint32_t {
-      for (int i = 0; i < ns; ++i) {
-        const int j4 = 4 * (i * kDecThreads + tid);
-        const float4 x = *reinterpret_cast<const float4*>(s_key + j4);
-        const uint32_t c = pred(x.x, j4) + pred(x.y, j4 + 1) + pred(x.z, j4 + 2) +
-                           pred(x.w, j4 + 3);
-        uint32_t wt;
-        wave_prefix_small(c, wt);
-        if (lane == 0) sh.wt[i * 4 + wave] = wt;
-      }
-      __syncthreads();
-      uint32_t acc = 0;
-      for (int i = 0; i < ns; ++i) {
-        const int j4 = 4 * (i * kDecThreads + tid);
-        const float4 x = *reinterpret_cast<const float4*>(s_key + j4);
-        const float e4[4] = {x.x, x.y, x.z, x.w};
-        bool p4[4];
-        uint32_t c = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p4[e] = pred(e4[e], j4 + e);
-          c += p4[e];
-        }
-        uint32_t wt;
-        uint32_t k = wave_prefix_small(c, wt) + acc;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t v = sh.wt[i * 4 + w];
-          k += w < wave ? v : 0u;
-          acc += v;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (p4[e]) visit(j4 + e, k++);
-      }
-      __syncthreads();
-      return acc;
-    };
-    auto tie_id = [&](float v, uint32_t need) -> int {
-      ordered([&](float x, int) { return x == v; },
-              [&](int j, uint32_t k) {
-                if (k + 1 == need) sh.tid = j;
-              });
-      const int r = sh.tid;
-      __syncthreads();
-      return r;
-    };
-    Red3 r{kPosInf, kNegInf, 0u};
-    each([&](float v, int) {
-      if (v != kNegInf) {
-        r.mn = fminf(r.mn, v);
-        r.mx = fmaxf(r.mx, v);
-        ++r.n;
-      }
-    });
-    r = block_red3(r, sh.red);
-    const uint32_t nr = min((uint32_t)a.n_retrieve, r.n);
-    float Tkey = kPosInf;
-    int Tid = -1;
-    if (nr == r.n && nr > 0) {
-      Tkey = kNegInf;  // every non-empty cluster
-    } else if (nr > 0) {
-      find_threshold(each, tie_id, r.mn, r.mx, nr, sh, Tkey, Tid);
-    }
-    // ---- ordered compaction of the selection into the LDS list (ascending ids)
-    nsel = (int)ordered([&](float v, int j) { return is_selected(v, j, Tkey, Tid); },
-                        [&](int j, uint32_t k) { l_id[k] = j; });
-    if (w_item == 0 && a.selected) {
-      int32_t* sel = a.selected + (size_t)bh * a.n_retrieve;
-      for (int i = tid; i < a.n_retrieve; i += kDecThreads) sel[i] = i < nsel ? l_id[i] : -1;
-    }
-    // ---- sizes and first cache rows of the listed clusters; virtual row starts
-    constexpr int kPer = kSelMax / kDecThreads;
-    const int per = (nsel + kDecThreads - 1) / kDecThreads;
-    int32_t sz[kPer], co[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int rr = tid * per + k;
-      if (k < per && rr < nsel) {
-        const size_t j = (size_t)bh * a.C + l_id[rr];
-        sz[k] = a.csize[j];
-        co[k] = a.coff[j];
-      } else {
-        sz[k] = -1;
-        co[k] = 0;
-      }
-    }
-    uint32_t my = 0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) my += sz[k] >= 0 ? (uint32_t)sz[k] + 1u : 0u;
-    uint32_t tot;
-    uint32_t pos = scan_excl(my, sh.tmp, &tot);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int rr = tid * per + k;
-      if (sz[k] >= 0) {
-        l_ts[rr] = (int)pos;
-        l_co[rr] = co[k];
-        pos += (uint32_t)sz[k] + 1u;
-      }
-    }
-    V = (int)tot;
-    if (tid == 0) l_ts[nsel] = V;
-    __syncthreads();
-  } else {
-    nsel = a.sel_n[bh];
-    V = a.sel_ts[(size_t)bh * (a.rcap + 1) + nsel];
-  }
-  const int T0 = (int)((int64_t)V * w_item / nB), T1 = (int)((int64_t)V * (w_item + 1) / nB);
-  if (T0 < T1) {
-    if (local) {  // listed clusters overlapping [T0, T1): binary searches in the LDS list
-      int lo = 0, hi = nsel - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (l_ts[mid] <= T0) lo = mid; else hi = mid - 1;
-      }
-      r_lo = lo;
-      hi = nsel - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (l_ts[mid] < T1) lo = mid; else hi = mid - 1;
-      }
-      r_hi = lo + 1;
-    } else {
-      const int32_t* r0 = a.wg_r0 + (size_t)bh * (kMaxRetrieveWG + 1);
-      r_lo = r0[w_item];
-      r_hi = w_item + 1 < nB ? min(nsel, r0[w_item + 1] + 1) : nsel;
-    }
-  }
-
   u32x4 q[G];
   load_q<G>(a, b, g, cc, q);
   Online<G> st;
   st.init();
-  if (local) {
-    if (T0 < T1) {
-      const int ts = max(T0, l_ts[r_lo]), te = min(T1, l_ts[r_hi]);
-      attend_virtual<G>(a, bh, q, st, ts + (te - ts) * wave / 4, ts + (te - ts) * (wave + 1) / 4,
-                        l_ts, l_co, l_id, r_lo, r_hi);
-    }
-  } else {
-    const size_t lb = (size_t)bh * a.rcap;
-    const int32_t* g_ts = a.sel_ts + (size_t)bh * (a.rcap + 1);
-    for (int rw = r_lo; rw < r_hi; rw += kSelMax) {
-      const int cnt = min(kSelMax, r_hi - rw);
-      for (int i = tid; i <= cnt; i += kDecThreads) {
-        l_ts[i] = g_ts[rw + i];
-        if (i < cnt) {
-          l_co[i] = a.sel_coff[lb + rw + i];
-          l_id[i] = a.sel_id[lb + rw + i];
-        }
+  const size_t lb = (size_t)bh * a.rcap;
+  for (int rw = r_lo; rw < r_hi; rw += kWinR) {
+    const int cnt = min(kWinR, r_hi - rw);
+    for (int i = tid; i <= cnt; i += kDecThreads) {
+      l_ts[i] = g_ts[rw + i];
+      if (i < cnt) {
+        l_co[i] = a.sel_coff[lb + rw + i];
+        l_id[i] = a.sel_id[lb + rw + i];
       }
-      __syncthreads();
-      const int ts = max(T0, l_ts[0]), te = min(T1, l_ts[cnt]);
-      if (ts < te)
-        attend_virtual<G>(a, bh, q, st, ts + (te - ts) * wave / 4,
-                          ts + (te - ts) * (wave + 1) / 4, l_ts, l_co, l_id, 0, cnt);
-      __syncthreads();
     }
+    __syncthreads();
+    const int ts = max(T0, l_ts[0]), te = min(T1, l_ts[cnt]);
+    if (ts < te)
+      attend_virtual<G>(a, bh, q, st, ts + (te - ts) * wave / 4, ts + (te - ts) * (wave + 1) / 4,
+                        l_ts, l_co, l_id, 0, cnt);
+    __syncthreads();
   }
   write_block_partial<G>(st, &s_x[0][0], parts + (size_t)(nSP + w_item) * G * kPartStride);
   if (arrive_last(a.counter + bh, (uint32_t)nB)) {
     const int bq = b * a.Hq + g * G;
     for (int idx = tid; idx < G * 128; idx += kDecThreads) {
       float M, Ls, O;
-      merge_partials<true>(parts, G, idx, nSP, 1, nSP + nB, M, Ls, O);
+      merge_partials<true, 32>(parts, G, idx, nSP, 1, nSP + nB, M, Ls, O);
       const int h = idx >> 7, d = idx & 127;
       a.out[(size_t)(bq + h) * kHeadDim + d] = O / Ls;
       if (d == 0 && a.lse) a.lse[bq + h] = (M + log2f(Ls)) * kLn2;
@@ -897,170 +821,253 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// published select (large indexes or budgets): one workgroup per (b, kv-head) selects and
-// lists the retrieved clusters (ids, first virtual row, first cache row) in the workspace,
-// plus the first listed cluster of every retrieve workgroup. Scores are streamed from the
-// workspace (L2-resident) on each pass.
+// select: one 512-thread workgroup per (b, kv-head). It finds the n_r-th (score, id) pair,
+// lists the retrieved clusters in ascending id order with their first virtual row and
+// first cache row, writes the `selected` output, and records the virtual rows and clusters
+// of every retrieve workgroup. The group scores (<= 65536, 128 per thread) stay in
+// registers; one CU's vector throughput bounds this kernel, so each step is O(scores):
+//   1. a lower bound of the n_r-th largest score: with q = ceil(n_r / 512), each thread's
+//      q-th largest score v_t; if u = ceil(n_r / q) threads have v_t >= b, at least
+//      u * q >= n_r scores are >= b. The bound is the 256-bin histogram bin (over the range
+//      of the v_t) holding the u-th largest v_t: every score in it or above qualifies.
+//   2. the qualifying scores (a few more than n_r), in ascending id order;
+//   3. the exact pair among them (value-range histogram, then an exact rank in the cut bin);
+//   4. ordered compaction, cluster sizes, prefix of the virtual rows.
+// Any step that cannot hold its data falls back to the same search over every score.
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kDecThreads) void k_dec_select(DecodeArgs a) {
+template <int NS>  // float4 score slices per thread (>= ceil(Cp / 2048))
+__global__ __launch_bounds__(kSelThreads) void k_dec_select(DecodeArgs a) {
+  constexpr int NT = kSelThreads;
   __shared__ SelShared sh;
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Cp = a.Cp, nsl = (Cp + 4 * kDecThreads - 1) / (4 * kDecThreads);
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int Cp = a.Cp, ns = (Cp + 4 * NT - 1) / (4 * NT);
   const float* shat = a.shat + (size_t)bh * Cp;
   const size_t cb = (size_t)bh * a.C;
-  auto each = [&](auto f) {
-    for (int i0 = 0; i0 < nsl; i0 += 4) {
-      float4 v[4];
+  float4 kf[NS];  // ids 4 * (i * NT + tid) + e
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j4 = 4 * ((i0 + u) * kDecThreads + tid);
-        v[u] = (i0 + u < nsl && j4 < Cp) ? *reinterpret_cast<const float4*>(shat + j4) : neg4();
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j4 = 4 * ((i0 + u) * kDecThreads + tid);
-        f(v[u].x, j4);
-        f(v[u].y, j4 + 1);
-        f(v[u].z, j4 + 2);
-        f(v[u].w, j4 + 3);
-      }
-    }
+  for (int i = 0; i < NS; ++i) {
+    const int j4 = 4 * (i * NT + tid);
+    kf[i] = (i < ns && j4 < Cp) ? *reinterpret_cast<const float4*>(shat + j4) : neg4();
+  }
+  auto key_at = [&](int i, int e) {
+    return e == 0 ? kf[i].x : e == 1 ? kf[i].y : e == 2 ? kf[i].z : kf[i].w;
   };
-  // slice-by-slice ordered search for the need-th lowest id whose score equals v
-  auto tie_id = [&](float v, uint32_t need) -> int {
-    uint32_t acc = 0;
-    for (int i = 0; i < nsl; ++i) {
-      const int j4 = 4 * (i * kDecThreads + tid);
-      const float4 x = j4 < Cp ? *reinterpret_cast<const float4*>(shat + j4) : neg4();
-      const uint32_t c = (x.x == v) + (x.y == v) + (x.z == v) + (x.w == v);
-      uint32_t wt;
-      uint32_t pre = wave_prefix_small(c, wt);
-      if (lane == 0) sh.wt[wave] = wt;
-      __syncthreads();
-      uint32_t before = 0, stot = 0;
+  auto id_of = [&](int i, int e) { return 4 * (i * NT + tid) + e; };
+  auto each_key = [&](auto f) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        stot += sh.wt[w];
-        before += w < wave ? sh.wt[w] : 0u;
+    for (int i = 0; i < NS; ++i)
+      if (i < ns) {
+        f(kf[i].x, id_of(i, 0));
+        f(kf[i].y, id_of(i, 1));
+        f(kf[i].z, id_of(i, 2));
+        f(kf[i].w, id_of(i, 3));
       }
-      pre += acc + before;
-      if (pre < need && need <= pre + c) {
-        const float e4[4] = {x.x, x.y, x.z, x.w};
-        uint32_t k = pre;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (e4[e] == v && ++k == need) sh.tid = j4 + e;
-      }
-      acc += stot;
-      __syncthreads();
-      if (acc >= need) break;
-    }
+  };
+  auto tie_key = [&](float v, uint32_t need) -> int {
+    ordered_visit<NT, NS, 4>(ns, [&](int i, int e) { return key_at(i, e) == v; },
+                                     [&](int i, int e, uint32_t k) {
+                                       if (k + 1 == need) sh.tid = id_of(i, e);
+                                     },
+                                     sh.wt);
     const int r = sh.tid;
     __syncthreads();
     return r;
   };
-  // range and count of the finite scores from the stream chunks' summaries
-  Red3 r{kPosInf, kNegInf, 0u};
-  for (int x = tid; x < a.nS; x += kDecThreads) {
-    const float* m = a.mm + ((size_t)bh * a.nS + x) * 4;
-    r.mn = fminf(r.mn, m[0]);
-    r.mx = fmaxf(r.mx, m[1]);
-    r.n += (uint32_t)m[2];
-  }
-  r = block_red3(r, sh.red);
-  const uint32_t nr = min((uint32_t)a.n_retrieve, r.n);
+  // ---- 1. the bound
+  const int nreq = a.n_retrieve;
+  const int q = min(4, max(1, (nreq + NT - 1) / NT));
+  float t0 = kNegInf, t1 = kNegInf, t2 = kNegInf, t3 = kNegInf;  // this thread's top 4
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (i < ns) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = key_at(i, e);
+        cnt += v != kNegInf ? 1u : 0u;
+        if (q > 1) {
+          t3 = fmaxf(t3, fminf(t2, v));
+          t2 = fmaxf(t2, fminf(t1, v));
+          t1 = fmaxf(t1, fminf(t0, v));
+        }
+        t0 = fmaxf(t0, v);
+      }
+    }
+  const float vq = q == 1 ? t0 : q == 2 ? t1 : q == 3 ? t2 : t3;
+  Red3 r{vq != kNegInf ? vq : kPosInf, vq, cnt};
+  r = block_red3<NT>(r, sh.red);  // range of the finite v_t, count of finite scores
+  const uint32_t ne = r.n, nr = min((uint32_t)nreq, ne);
   float Tkey = kPosInf;
   int Tid = -1;
-  if (nr == r.n && nr > 0) {
-    Tkey = kNegInf;
+  bool cand = false;
+  uint32_t m = 0;
+  auto keep = [&](int i, int e, uint32_t k) {
+    if (k < (uint32_t)kCandMax) {
+      sh.cand_key[k] = key_at(i, e);
+      sh.cand_id[k] = id_of(i, e);
+    }
+  };
+  if (nr > 0 && nr == ne) {
+    Tkey = kNegInf;  // every non-empty cluster
   } else if (nr > 0) {
-    find_threshold(each, tie_id, r.mn, r.mx, nr, sh, Tkey, Tid);
+    // the bound: the histogram bin (256 bins over the range of the finite v_t) that holds
+    // the u-th largest v_t; every score in that bin or above qualifies
+    const uint32_t u = (uint32_t)((nreq + q - 1) / q);
+    if (r.mx != kNegInf && r.mn < r.mx) {
+      const Binner vb(r.mn, r.mx, true);
+      auto b256 = [&](float v) { return vb(v) >> 4; };
+      if (tid < 256) sh.hist[tid] = 0u;
+      __syncthreads();
+      hist_add<8>(sh.hist, vq != kNegInf ? b256(vq) : 0, vq != kNegInf);
+      __syncthreads();
+      const uint32_t h = tid < 256 ? sh.hist[255 - tid] : 0u;  // thread t: bin 255 - t
+      uint32_t tot;
+      const uint32_t above = scan_excl<NT>(h, sh.tmp, &tot);
+      if (tid < 256 && above < u && above + h >= u) sh.u[0] = 255u - tid;
+      if (tid == 0 && tot < u) sh.u[0] = 0xffffffffu;  // fewer than u finite v_t
+      __syncthreads();
+      const uint32_t bb = sh.u[0];
+      __syncthreads();
+      if (bb != 0xffffffffu) {
+        // the smallest v_t in that bin (<= the u-th largest v_t) is the bound
+        Red3 rb{vq != kNegInf && b256(vq) == (int)bb ? vq : kPosInf, kNegInf, 0u};
+        rb = block_red3<NT>(rb, sh.red);
+        const float bound = rb.mn;
+        m = ordered_visit<NT, NS, 4>(
+            ns, [&](int i, int e) { return key_at(i, e) >= bound; }, keep, sh.wt);
+        cand = true;
+      }
+    } else if (r.mx != kNegInf) {  // all finite v_t are equal
+      m = ordered_visit<NT, NS, 4>(
+          ns,
+          [&](int i, int e) {
+            const float v = key_at(i, e);
+            return v != kNegInf && v >= r.mn;
+          },
+          keep, sh.wt);
+      cand = true;
+    }
+    // the candidates hold the whole selection iff at least nr scores reach the bound
+    cand = cand && m <= (uint32_t)kCandMax && m >= nr;
+    if (cand) {
+      // ---- 3. the exact pair among the candidates
+      const int nslc = (int)((m + NT - 1) / NT);
+      auto each_c = [&](auto f) {
+        for (int k = tid; k < (int)m; k += NT) f(sh.cand_key[k], sh.cand_id[k]);
+      };
+      auto tie_c = [&](float v, uint32_t need) -> int {
+        ordered_visit<NT, kCandMax / NT, 1>(
+            nslc,
+            [&](int i, int) {
+              const int k = i * NT + tid;
+              return k < (int)m && sh.cand_key[k] == v;
+            },
+            [&](int i, int, uint32_t k) {
+              if (k + 1 == need) sh.tid = sh.cand_id[i * NT + tid];
+            },
+            sh.wt);
+        const int res = sh.tid;
+        __syncthreads();
+        return res;
+      };
+      Red3 rc{kPosInf, kNegInf, 0u};
+      each_c([&](float v, int) {
+        rc.mn = fminf(rc.mn, v);
+        rc.mx = fmaxf(rc.mx, v);
+      });
+      rc = block_red3<NT>(rc, sh.red);
+      find_threshold<256>(each_c, tie_c, rc.mn, rc.mx, nr, sh, Tkey, Tid);
+    } else {
+      Red3 ra{kPosInf, kNegInf, 0u};
+      each_key([&](float v, int) {
+        if (v != kNegInf) {
+          ra.mn = fminf(ra.mn, v);
+          ra.mx = fmaxf(ra.mx, v);
+        }
+      });
+      ra = block_red3<NT>(ra, sh.red);
+      find_threshold<kHistBins>(each_key, tie_key, ra.mn, ra.mx, nr, sh, Tkey, Tid);
+    }
   }
-  // total virtual rows of the selection
-  uint32_t my = 0;
-  for (int i = 0; i < nsl; ++i) {
-    const int j4 = 4 * (i * kDecThreads + tid);
-    if (j4 >= a.C) break;
-    const float4 x = *reinterpret_cast<const float4*>(shat + j4);
-    const float e4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (j4 + e < a.C && is_selected(e4[e], j4 + e, Tkey, Tid))
-        my += (uint32_t)a.csize[cb + j4 + e] + 1u;
-  }
-  uint32_t V;
-  scan_excl(my, sh.tmp, &V);
-  // ordered compaction, one slice of 1024 ids at a time
-  const int nB = a.nB;
+  // ---- 4. the selection in ascending id order: published list, `selected`, LDS copy
   int32_t* sid = a.sel_id + (size_t)bh * a.rcap;
   int32_t* sts = a.sel_ts + (size_t)bh * (a.rcap + 1);
   int32_t* sco = a.sel_coff + (size_t)bh * a.rcap;
-  int32_t* r0 = a.wg_r0 + (size_t)bh * (kMaxRetrieveWG + 1);
   int32_t* selo = a.selected ? a.selected + (size_t)bh * a.n_retrieve : nullptr;
-  uint32_t rank = 0, row = 0;
-  for (int i = 0; i < nsl; ++i) {
-    const int j4 = 4 * (i * kDecThreads + tid);
-    const float4 x = j4 < Cp ? *reinterpret_cast<const float4*>(shat + j4) : neg4();
-    const float e4[4] = {x.x, x.y, x.z, x.w};
-    int32_t n4[4];
-    uint32_t c = 0, tok = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool s = j4 + e < a.C && is_selected(e4[e], j4 + e, Tkey, Tid);
-      n4[e] = s ? a.csize[cb + j4 + e] : -1;
-      c += s;
-      tok += s ? (uint32_t)n4[e] + 1u : 0u;
-    }
-    uint32_t wt;
-    const uint32_t pre = wave_prefix_small(c, wt);
-    uint32_t tp = tok;  // inclusive scan of tok over the wave
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(tp, off);
-      if (lane >= off) tp += y;
-    }
-    if (lane == 63) {
-      sh.wt[wave] = wt;
-      sh.wt[4 + wave] = tp;
-    }
-    __syncthreads();
-    uint32_t before_c = 0, before_t = 0, sc = 0, stk = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      sc += sh.wt[w];
-      stk += sh.wt[4 + w];
-      before_c += w < wave ? sh.wt[w] : 0u;
-      before_t += w < wave ? sh.wt[4 + w] : 0u;
-    }
-    __syncthreads();
-    uint32_t rr = rank + before_c + pre, ts = row + before_t + tp - tok;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (n4[e] >= 0) {
-        const int j = j4 + e;
-        sid[rr] = j;
-        sts[rr] = (int32_t)ts;
-        sco[rr] = a.coff[cb + j];
-        if (selo) selo[rr] = j;
-        // retrieve workgroups whose first virtual row falls in [ts, te)
-        const uint32_t te = ts + (uint32_t)n4[e] + 1u;
-        const int w0 = (int)(((uint64_t)ts * nB + V - 1) / V);
-        const int w1 = (int)(((uint64_t)te * nB + V - 1) / V);
-        for (int w = w0; w < w1; ++w) r0[w] = (int32_t)rr;
-        ++rr;
-        ts = te;
-      }
-    rank += sc;
-    row += stk;
+  int32_t* lst = reinterpret_cast<int32_t*>(sh.hist);  // the first kHistBins selected ids
+  auto put = [&](int j, uint32_t k) {
+    sid[k] = j;
+    if (selo) selo[k] = j;
+    if (k < (uint32_t)kHistBins) lst[k] = j;
+  };
+  uint32_t nsel;
+  if (cand) {
+    nsel = ordered_visit<NT, kCandMax / NT, 1>(
+        (int)((m + NT - 1) / NT),
+        [&](int i, int) {
+          const int k = i * NT + tid;
+          return k < (int)m && is_selected(sh.cand_key[k], sh.cand_id[k], Tkey, Tid);
+        },
+        [&](int i, int, uint32_t k) { put(sh.cand_id[i * NT + tid], k); }, sh.wt);
+  } else {
+    nsel = ordered_visit<NT, NS, 4>(
+        ns, [&](int i, int e) { return is_selected(key_at(i, e), id_of(i, e), Tkey, Tid); },
+        [&](int i, int e, uint32_t k) { put(id_of(i, e), k); }, sh.wt);
   }
   if (selo)
-    for (int i = (int)rank + tid; i < a.n_retrieve; i += kDecThreads) selo[i] = -1;
+    for (int i = (int)nsel + tid; i < a.n_retrieve; i += NT) selo[i] = -1;
+  // sizes and first rows of the listed clusters (thread t: ranks [t * per, (t + 1) * per))
+  auto listed = [&](int k) { return k < kHistBins ? lst[k] : ld_dev(sid + k); };
+  const int per = (int)((nsel + NT - 1) / NT), k0 = tid * per;
+  const int k1 = min((int)nsel, k0 + per);
+  int32_t sz4[4], co4[4];  // the first four of this thread's clusters
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    sz4[k] = co4[k] = 0;
+    if (k0 + k < k1) {
+      const int j = listed(k0 + k);
+      sz4[k] = a.csize[cb + j];
+      co4[k] = a.coff[cb + j];
+    }
+  }
+  uint32_t tok = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tok += k0 + k < k1 ? (uint32_t)sz4[k] + 1u : 0u;
+  for (int k = k0 + 4; k < k1; ++k) tok += (uint32_t)a.csize[cb + listed(k)] + 1u;
+  uint32_t V;
+  uint32_t pos = scan_excl<NT>(tok, sh.tmp, &V);
+  const int nB = a.nB;
+  auto emit = [&](int k, int32_t n, int32_t co) {
+    const uint32_t te = pos + (uint32_t)n + 1u;
+    sts[k] = (int32_t)pos;
+    sco[k] = co;
+    // retrieve workgroups whose first virtual row falls in [pos, te)
+    const int w0 = (int)(((uint64_t)pos * nB + V - 1) / V);
+    const int w1 = (int)(((uint64_t)te * nB + V - 1) / V);
+    for (int w = w0; w < w1; ++w) sh.wgr[w] = k;
+    pos = te;
+  };
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (k0 + k < k1) emit(k0 + k, sz4[k], co4[k]);
+  for (int k = k0 + 4; k < k1; ++k) {
+    const int j = listed(k);
+    emit(k, a.csize[cb + j], a.coff[cb + j]);
+  }
   if (tid == 0) {
-    a.sel_n[bh] = (int32_t)rank;
-    sts[rank] = (int32_t)V;
-    if (V == 0)
-      for (int w = 0; w < nB; ++w) r0[w] = 0;
-    r0[nB] = (int32_t)rank;
+    a.sel_n[bh] = (int32_t)nsel;
+    sts[nsel] = (int32_t)V;
+  }
+  __syncthreads();
+  // per retrieve workgroup: its virtual rows [T0, T1) and listed clusters [r_lo, r_hi)
+  if (tid < nB) {
+    const int T0 = (int)((uint64_t)V * tid / nB), T1 = (int)((uint64_t)V * (tid + 1) / nB);
+    int lo = 0, hi = 0;
+    if (T0 < T1) {
+      lo = sh.wgr[tid];
+      hi = tid + 1 < nB ? min((int)nsel, sh.wgr[tid + 1] + 1) : (int)nsel;
+    }
+    reinterpret_cast<int4*>(a.wg_info)[(size_t)bh * kMaxRetrieveWG + tid] = make_int4(T0, T1, lo, hi);
   }
 }
 
@@ -1103,19 +1110,12 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr
   const int BH = a.B * a.Hkv;
   hipError_t e = launch(tr, k_dec_stream<G>, dim3(a.nS + a.nSt, BH), dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
-  if (!a.local_select) {
-    e = launch(tr, k_dec_select, dim3(BH), dim3(kDecThreads), 0, s, a);
-    if (e != hipSuccess) return e;
-  }
-  // dynamic LDS of the retrieve kernel: the group scores when it selects for itself
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_dec_retrieve<G>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kLocalSelMax * (int)sizeof(float));
-  if (attr != hipSuccess) return attr;
-  const size_t lds = a.local_select ? (size_t)(a.Cp + 4 * kDecThreads - 1) /
-                                          (4 * kDecThreads) * (4 * kDecThreads) * sizeof(float)
-                                    : 0;
-  return launch(tr, k_dec_retrieve<G>, dim3(a.nB, BH), dim3(kDecThreads), (uint32_t)lds, s, a);
+  const int ns = (a.Cp + 4 * kSelThreads - 1) / (4 * kSelThreads);
+  auto sel = ns <= 1 ? k_dec_select<1> : ns <= 2 ? k_dec_select<2> : ns <= 4 ? k_dec_select<4>
+           : ns <= 8 ? k_dec_select<8> : ns <= 16 ? k_dec_select<16> : k_dec_select<32>;
+  e = launch(tr, sel, dim3(BH), dim3(kSelThreads), 0, s, a);
+  if (e != hipSuccess) return e;
+  return launch(tr, k_dec_retrieve<G>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
 }
 
 template <int G>

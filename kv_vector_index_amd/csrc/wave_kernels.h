@@ -27,11 +27,12 @@ constexpr int kTokChunk = 128;        // steady tokens per stream workgroup
 constexpr int kPartStride = 132;      // floats per (partial, head): o[128], m, l, 2 pad
 constexpr int kHistBins = 4096;       // value-range histogram of the group scores
 constexpr int kCand = 256;            // keys ranked exactly in the histogram bin of the cut
-constexpr int kLocalSelMax = 16384;   // retrieve workgroups select for themselves up to this C
-constexpr int kSelMax = 1024;         // ... and up to this many retrieved clusters
-constexpr int kKeySlices = kLocalSelMax / (4 * kDecThreads);  // float4 slices of 1024 ids
+constexpr int kCandMax = 2048;        // candidate scores kept after the bound
+constexpr int kSelThreads = 512;      // select workgroup (one per (b, kv-head))
 constexpr int kMaxClusters = 65536;   // clusters per (b, kv-head) supported by the decode
+constexpr int kSelSlices = kMaxClusters / (4 * kSelThreads);  // float4 scores per select thread
 constexpr int kMaxRetrieveWG = 256;   // retrieve workgroups per (b, kv-head)
+constexpr int kWinR = 1024;           // listed clusters staged per LDS window of a retrieve WG
 constexpr int kRowsPerItem = 128;     // retrieved rows per retrieve workgroup (target)
 
 // A retrieved cluster j of size n_j occupies n_j + 1 consecutive "virtual rows": its n_j
@@ -55,18 +56,17 @@ struct DecodeArgs {
   float* scores;           // [BH, C, G] log2-domain centroid logits of each query head
   float* shat;             // [BH, Cp] group-mean logits (natural units; -inf: empty / pad)
   float* mm;               // [BH, nS, 4] per stream chunk: min, max, count of finite shat
-  int32_t* sel_id;         // [BH, rcap] published selection (ascending ids)
+  int32_t* sel_id;         // [BH, rcap] the selection (ascending ids)
   int32_t* sel_ts;         // [BH, rcap + 1] first virtual row of each cluster, then total
   int32_t* sel_coff;       // [BH, rcap] first cache row of each cluster
   int32_t* sel_n;          // [BH]
-  int32_t* wg_r0;          // [BH, kMaxRetrieveWG + 1] first listed cluster of each workgroup
+  int32_t* wg_info;        // [BH, kMaxRetrieveWG, 4] per retrieve workgroup: T0, T1, r_lo, r_hi
   float* part;             // [BH, nP, G, kPartStride] partial softmax states
   // shape
   int B, Hq, Hkv, G;
   int64_t L, L0, Lcap;
   int C, Cp, n_sink, n_recent, n_retrieve, rcap;
   int nS, nSt, nB, nP;     // per (b, kv-head): stream chunks, steady chunks, retrieve groups
-  int local_select;        // 1: retrieve workgroups select themselves
   float scale, scale_log2;
 };
 

@@ -356,7 +356,7 @@ def test_exact_score_ties_select_lowest_ids(C):
 def test_traced_calls_time_each_kernel_and_match_the_plain_calls(tiny):
     """The traced variants give bit-identical results and time every kernel with one
     start / end event pair (build: norms, seeds, passes x (assign, sort) + (passes - 1) x
-    update, finalise, steady, objective; decode: stream, retrieve)."""
+    update, finalise, steady, objective; decode: stream, select, retrieve)."""
     t = tl.torch()
     w, x, layer = tiny
     T = 3
@@ -393,12 +393,12 @@ def test_traced_calls_time_each_kernel_and_match_the_plain_calls(tiny):
     for traced in (False, True):
         out = t.empty(layer.B, layer.Hq, 128, dtype=t.float32, device="cuda")
         dws = wi.alloc_decode_workspace(dp)
-        ev = events(6) if traced else None
+        ev = events(8) if traced else None
         n = wi.wave_decode_attention(dp, q, layer.k_out, layer.v_out, idx_b, out, None, None,
                                      dws, events=None if ev is None else [e.cuda_event for e in ev])
         t.cuda.synchronize()
         if traced:
-            assert n == 4
-            assert ev[0].elapsed_time(ev[1]) > 0 and ev[2].elapsed_time(ev[3]) > 0
+            assert n == 6
+            assert all(ev[2 * i].elapsed_time(ev[2 * i + 1]) > 0 for i in range(3))
         outs.append(out.cpu())
     assert t.equal(outs[0], outs[1])
