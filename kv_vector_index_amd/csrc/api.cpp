@@ -160,7 +160,6 @@ size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* b
   uint32_t* counter = cv.take<uint32_t>(BH);
   float* scores = cv.take<float>(BH * C * G);
   float* shat = cv.take<float>(BH * Cp);
-  float* mm = cv.take<float>(BH * sh.nS * 4);
   int32_t* sel_id = cv.take<int32_t>(BH * (size_t)sh.rcap);
   int32_t* sel_ts = cv.take<int32_t>(BH * ((size_t)sh.rcap + 1));
   int32_t* sel_coff = cv.take<int32_t>(BH * (size_t)sh.rcap);
@@ -171,7 +170,6 @@ size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* b
     a->counter = counter;
     a->scores = scores;
     a->shat = shat;
-    a->mm = mm;
     a->sel_id = sel_id;
     a->sel_ts = sel_ts;
     a->sel_coff = sel_coff;

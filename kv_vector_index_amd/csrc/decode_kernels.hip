@@ -67,34 +67,41 @@ __device__ __forceinline__ float vdim(const u32x4& v, int d) {
 
 // Fold R rows into the state. s2: log2-domain logits (-inf = skip row), w: denominator
 // weight of the row (1 for a token, n_j for a cluster estimate, -n_j to remove one),
-// sg: +1 / -1 multiplier of the value row.
+// sg: +1 / -1 multiplier of the value row. All weights first, then one pass over the 8
+// dims in which each value is unpacked from bf16 once and used by all G heads.
 template <int G, int R>
 __device__ __forceinline__ void fold_rows(Online<G>& st, const float (&s2)[R][G],
                                           const float (&w)[R], const u32x4 (&v)[R],
                                           const float (&sg)[R]) {
+  float alpha[G], p[G][R];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float tm = s2[0][h];
 #pragma unroll
     for (int i = 1; i < R; ++i) tm = fmaxf(tm, s2[i][h]);
     const float mn = fmaxf(st.m[h], tm);
-    if (mn == kNegInf) continue;
-    const float alpha = fast_exp2(st.m[h] - mn);
-    float p[R];
+    const bool none = mn == kNegInf;  // nothing folded yet and nothing in these rows
+    alpha[h] = none ? 1.f : fast_exp2(st.m[h] - mn);
     float ls = 0.f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      p[i] = fast_exp2(s2[i][h] - mn);
-      ls += w[i] * p[i];
-      p[i] *= sg[i];
+      const float e = none ? 0.f : fast_exp2(s2[i][h] - mn);
+      ls += w[i] * e;
+      p[h][i] = e * sg[i];
     }
-    st.l[h] = alpha * st.l[h] + ls;
+    st.l[h] = alpha[h] * st.l[h] + ls;
     st.m[h] = mn;
+  }
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      float acc = alpha * st.o[h][d];
+  for (int d = 0; d < 8; ++d) {
+    float vd[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) acc += p[i] * vdim(v[i], d);
+    for (int i = 0; i < R; ++i) vd[i] = vdim(v[i], d);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = alpha[h] * st.o[h][d];
+#pragma unroll
+      for (int i = 0; i < R; ++i) acc += p[h][i] * vd[i];
       st.o[h][d] = acc;
     }
   }
@@ -111,22 +118,36 @@ __device__ __forceinline__ void lse_pair(float m1, float m2, float& a1, float& a
   }
 }
 
+// The value of lane l ^ 16 (resp. l ^ 32), without LDS: the permlane swaps exchange
+// 16-lane rows 0 <-> 1 and 2 <-> 3 (resp. the two 32-lane halves) between two registers.
+__device__ __forceinline__ float xor16(float x) {
+  const int xi = __float_as_int(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  return __int_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float x) {
+  const int xi = __float_as_int(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __int_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // Combine the four 16-lane row groups of a wave; afterwards every lane holds the wave state.
 template <int G>
 __device__ __forceinline__ void merge_row_groups(Online<G>& st) {
 #pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
+  for (int step = 0; step < 2; ++step) {
+    auto other = [&](float x) { return step == 0 ? xor16(x) : xor32(x); };
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(st.m[h], off);
-      const float lo = __shfl_xor(st.l[h], off);
+      const float mo = other(st.m[h]);
+      const float lo = other(st.l[h]);
       float a1, a2, mn;
       lse_pair(st.m[h], mo, a1, a2, mn);
       st.m[h] = mn;
       st.l[h] = a1 * st.l[h] + a2 * lo;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        const float oo = __shfl_xor(st.o[h][d], off);
+        const float oo = other(st.o[h][d]);
         st.o[h][d] = a1 * st.o[h][d] + a2 * oo;
       }
     }
@@ -616,12 +637,10 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_stream(DecodeArgs a) {
   st.init();
   if ((int)blockIdx.x < a.nS) {
     constexpr int R = Rows<G>::R;
-    __shared__ float s_mm[kDecThreads / 64][3];
     const size_t base = (size_t)bh * a.C;
     float* shat = a.shat + (size_t)bh * a.Cp;
-    const int j0 = blockIdx.x * kChunk + wave * (kChunk / 4);  // this wave's 32 clusters
+    const int j0 = blockIdx.x * kChunk + wave * (kChunk / 4);  // this wave's clusters
     const float sl2 = a.scale_log2, gmean = a.scale / (float)G;
-    float mn = kPosInf, mx = kNegInf, cnt = 0.f;
     for (int t = j0; t < j0 + kChunk / 4; t += 4 * R) {
       u32x4 kr[R], vr[R];
       int32_t n[R];
@@ -632,7 +651,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_stream(DecodeArgs a) {
           const size_t row = (base + j) * kHeadDim + cc * 8;
           kr[i] = ld16_stream(a.cmean + row);
           vr[i] = ld16_stream(a.vsum + row);
-          n[i] = a.csize[base + j];
+          n[i] = __builtin_nontemporal_load(a.csize + base + j);
         } else {
           kr[i] = vr[i] = u32x4{0, 0, 0, 0};
           n[i] = -1;
@@ -649,11 +668,6 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_stream(DecodeArgs a) {
         for (int h = 0; h < G; ++h) sum += s[i][h];
         const float mean = sum * gmean;
         if (cc == 0) shat[j] = ok ? mean : kNegInf;
-        if (ok) {
-          mn = fminf(mn, mean);
-          mx = fmaxf(mx, mean);
-          cnt += 1.f;
-        }
         if (n[i] >= 0 && cc < G) {
           float mine = s[i][0];
 #pragma unroll
@@ -666,26 +680,6 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_stream(DecodeArgs a) {
         for (int h = 0; h < G; ++h) s[i][h] = ok ? s[i][h] * sl2 : kNegInf;
       }
       fold_rows<G, R>(st, s, w, vr, sg);
-    }
-    // min / max / count of this chunk's finite scores (the 16 lanes of a row group agree)
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, off));
-      mx = fmaxf(mx, __shfl_xor(mx, off));
-      cnt += __shfl_xor(cnt, off);
-    }
-    if (lane == 0) {
-      s_mm[wave][0] = mn;
-      s_mm[wave][1] = mx;
-      s_mm[wave][2] = cnt;
-    }
-    __syncthreads();
-    if (tid < 3) {
-      float r = s_mm[0][tid];
-#pragma unroll
-      for (int w = 1; w < kDecThreads / 64; ++w)
-        r = tid == 0 ? fminf(r, s_mm[w][0]) : tid == 1 ? fmaxf(r, s_mm[w][1]) : r + s_mm[w][2];
-      a.mm[((size_t)bh * a.nS + blockIdx.x) * 4 + tid] = r;
     }
   } else {
     const int64_t n_steady = (int64_t)a.n_sink + a.n_recent + (a.L - a.L0);

@@ -55,7 +55,6 @@ struct DecodeArgs {
   uint32_t* counter;       // [BH] retrieve-workgroup arrivals (cleared by the stream kernel)
   float* scores;           // [BH, C, G] log2-domain centroid logits of each query head
   float* shat;             // [BH, Cp] group-mean logits (natural units; -inf: empty / pad)
-  float* mm;               // [BH, nS, 4] per stream chunk: min, max, count of finite shat
   int32_t* sel_id;         // [BH, rcap] the selection (ascending ids)
   int32_t* sel_ts;         // [BH, rcap + 1] first virtual row of each cluster, then total
   int32_t* sel_coff;       // [BH, rcap] first cache row of each cluster
