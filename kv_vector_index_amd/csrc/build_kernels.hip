@@ -188,6 +188,193 @@ __global__ __launch_bounds__(256) void k_assign(BuildArgs a, const uint16_t* __r
   }
 }
 
+// Segment-resident variant (k_seg <= kA2MaxK): a 512-thread workgroup stages all centroids
+// of its segment in LDS once (k_seg x 272 B) and each wave loops over 64-point blocks of its
+// share of the segment's points. Per 32-centroid row block the argmax takes a max3 tree of
+// the 16 scores a lane holds and looks for the index only when that beats its running best
+// (rows in increasing id order, so a strict '>' still keeps the lowest id on ties).
+constexpr int kA2Threads = 512;
+constexpr int kA2Waves = kA2Threads / 64;
+constexpr int kA2MaxK = 512;
+
+__global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const uint16_t* __restrict__ mu,
+                                                           int nsplit) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_mu2[];
+  const int split = blockIdx.x, s = blockIdx.y, bh = blockIdx.z;
+  const Seg sg = seg_range(a, s);
+  const int64_t n = sg.hi - sg.lo;
+  if (n <= 0) return;
+  const int nvalid = n_valid_clusters(a, n);
+  const int kpad = (nvalid + 31) & ~31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const uint16_t* mus = mu + ((size_t)bh * a.C + (size_t)s * a.kseg) * kHeadDim;
+  // 16-byte chunks in batches of 8 per thread, all loads of a batch in flight together
+  // (rows clamp to the last valid one, padding rows are written as zero)
+  for (int q0 = 0; q0 < kpad * 16; q0 += 8 * kA2Threads) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = q0 + j * kA2Threads + tid, r = q >> 4, ch = q & 15;
+      v[j] = ld16(mus + (size_t)min(r, nvalid - 1) * kHeadDim + ch * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = q0 + j * kA2Threads + tid, r = q >> 4, ch = q & 15;
+      if (r >= nvalid) v[j] = u32x4{0, 0, 0, 0};
+      if (q < kpad * 16) *reinterpret_cast<u32x4*>(s_mu2 + r * kAsgLdsStride + ch * 16) = v[j];
+    }
+  }
+  // this split's points, in 64-point blocks (loads clamp to the last point: columns past the
+  // segment are scored but never written)
+  const int64_t nblk = (n + 63) / 64;
+  const int64_t b0 = nblk * split / nsplit, b1 = nblk * (split + 1) / nsplit;
+  int* s_next = reinterpret_cast<int*>(s_mu2 + kpad * kAsgLdsStride);
+  if (tid == 0) *s_next = (int)(b0 + kA2Waves);
+  __syncthreads();
+  auto load_block = [&](int64_t blk, bf16x8 (&bq)[2][8], float (&inv)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int64_t p = min(blk * 64 + nb * 32 + col, n - 1);
+      const uint16_t* row = a.k + ((size_t)bh * a.Lcap + sg.lo + p) * kHeadDim;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        bq[nb][kk] = __builtin_bit_cast(bf16x8, ld16_stream(row + kk * 16 + half * 8));
+      inv[nb] = a.inv_norm[(size_t)bh * a.L0 + sg.lo + p];
+    }
+  };
+  // row of the A operand (centroids) that this lane supplies for row block m0 and k step kk
+  // (rows clamp to the last padded one, so reads need no branch)
+  auto a_row = [&](int m0, int kk) {
+    const unsigned char* r = s_mu2 + min(m0 + col, kpad - 1) * kAsgLdsStride + half * 16;
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(r + kk * 32));
+  };
+  // The products k . mu of a point with unit centroids lie within +-||k|| (1 + 2^-8 for bf16
+  // rounding of mu), so starting the accumulation from 2 ||k|| makes every score a positive
+  // float whose bit pattern orders like its value. The low 4 bits of each score are then
+  // replaced by 15 - i for accumulator element i (rows ascend with i), so one unsigned max
+  // over a point's scores picks its best row and, among scores equal above those bits, the
+  // lowest row. The winner's cosine is thereby within 2^-17 of the best one (16 ulps of a
+  // value below 4 ||k||); only which of such near-equal centroids wins can change.
+  auto score_block = [&](int64_t blk, const bf16x8 (&bq)[2][8], const float (&inv)[2]) {
+    float bias[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) bias[nb] = inv[nb] > 0.f ? 2.f / inv[nb] : 1.f;
+    uint32_t best[2] = {0u, 0u};
+    int bblk[2] = {0, 0};
+    bf16x8 am[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) am[kk] = a_row(0, kk);
+    // products of row block m0; each A operand is refilled with the next row block's once
+    // its products are issued
+    auto products = [&](int m0, floatx16 (&acc)[2]) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nb][i] = bias[nb];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[kk], bq[nb][kk], acc[nb], 0, 0, 0);
+        am[kk] = a_row(m0 + 32, kk);
+      }
+    };
+    // best row of row block m0 per point; element i holds row m0 + 8 * (i / 4) + 4 * half +
+    // i % 4, and in the last block rows >= nvalid get key 0, below every biased score
+    auto pick = [&](int m0, const floatx16 (&acc)[2], bool last) {
+      const int lim = nvalid - m0 - 4 * half;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        uint32_t key[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) key[i] = (__float_as_uint(acc[nb][i]) & ~15u) | (15u - i);
+        if (last) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (8 * (i >> 2) + (i & 3) >= lim) key[i] = 0u;
+        }
+        uint32_t bm = max(max(key[0], key[1]), key[2]);
+        bm = max(max(bm, key[3]), key[4]);
+        bm = max(max(bm, key[5]), key[6]);
+        bm = max(max(bm, key[7]), key[8]);
+        bm = max(max(bm, key[9]), key[10]);
+        bm = max(max(bm, key[11]), key[12]);
+        bm = max(max(bm, key[13]), key[14]);
+        bm = max(bm, key[15]);
+        // strict: an equal key in a later block has a higher row
+        if (bm > best[nb]) {
+          best[nb] = bm;
+          bblk[nb] = m0;
+        }
+      }
+    };
+    // software pipeline over the row blocks: the products of block r are issued before the
+    // scores of block r - 1 are reduced, so the matrix core and the vector ALU overlap
+    const int nrb = kpad / 32;
+    // (each products + pick pair is one scheduling region, the compiler interleaving the
+    // reduction's ALU work between the 16 matrix products)
+    floatx16 acc0[2], acc1[2];
+    products(0, acc0);
+    int r = 1;
+    for (; r + 1 < nrb; r += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      products(32 * r, acc1);
+      pick(32 * (r - 1), acc0, false);
+      __builtin_amdgcn_sched_barrier(0);
+      products(32 * (r + 1), acc0);
+      pick(32 * r, acc1, false);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (r < nrb) {
+      products(32 * r, acc1);
+      pick(32 * (r - 1), acc0, false);
+      pick(32 * r, acc1, true);
+    } else {
+      pick(32 * (r - 1), acc0, true);
+    }
+    // the two half-waves hold disjoint centroid rows of the same points
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int i = 15 - (int)(best[nb] & 15u);
+      const uint32_t tv = best[nb] & ~15u;
+      const int idx = bblk[nb] + 8 * (i >> 2) + 4 * half + (i & 3);
+      const uint32_t ov = __shfl_xor(tv, 32);
+      const int oi = __shfl_xor(idx, 32);
+      const int pick = (ov > tv || (ov == tv && oi < idx)) ? oi : idx;
+      const int64_t p = blk * 64 + nb * 32 + col;
+      if (half == 0 && p < n) a.lab[(size_t)bh * a.L0 + sg.lo + p] = pick;
+    }
+  };
+  // Blocks b0 + wave go to the waves first; every later block goes to whichever wave asks
+  // next (a counter in LDS), so the waves of the workgroup, and with them the SIMDs, stay
+  // busy until its last block. A wave claims its next block when it starts the current one,
+  // and one plain load per 128-byte line of that next block, consumed only after the current
+  // block is scored, brings its keys into L2 meanwhile.
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(s_next, 1);
+    return (int64_t)__shfl(v, 0);
+  };
+  uint32_t touch = 0;
+  int64_t blk = b0 + wave;
+  while (blk < b1) {
+    const int64_t nxt = claim();
+    bf16x8 bq[2][8];
+    float inv[2];
+    load_block(blk, bq, inv);
+    const int64_t pn = min(nxt * 64 + lane, n - 1);
+    const uint32_t* nrow =
+        reinterpret_cast<const uint32_t*>(a.k + ((size_t)bh * a.Lcap + sg.lo + pn) * kHeadDim);
+    const uint32_t t0 = nrow[0], t1 = nrow[32];
+    score_block(blk, bq, inv);
+    touch ^= t0 ^ t1;
+    blk = nxt;
+  }
+  // (never true, nsplit >= 1: keeps the touching loads)
+  if (nsplit <= 0 && touch == 1u) a.lab[0] = 0;
+}
+
 // ------------------------------------------------------------------------------------
 // stable counting sort of a segment's labels: order = local point ids by (label, position)
 // ------------------------------------------------------------------------------------
@@ -477,9 +664,25 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t st, Tracer* tr) {
   }
   WAVE_TRY(launch(tr, k_seeds, gseg, dim3(256), 0, st, a, a.mu[0]));
   const dim3 gasg((a.S + kAsgPoints - 1) / kAsgPoints, a.nseg, BH);
+  // segment-resident assignment when a segment's centroids fit in LDS; enough splits of
+  // each segment to give every CU a workgroup
+  const bool seg_res = a.kseg <= kA2MaxK;
+  const int nsplit = std::max(1, std::min((a.S + 63) / 64, (256 + a.nseg * BH - 1) / (a.nseg * BH)));
+  // centroid rows, then the block counter
+  const size_t lds2 = (size_t)((std::min(a.kseg, a.S) + 31) & ~31) * kAsgLdsStride + 16;
+  if (seg_res) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&k_assign_seg), hipFuncAttributeMaxDynamicSharedMemorySize,
+        kA2MaxK * kAsgLdsStride + 16);
+    if (attr != hipSuccess) return attr;
+  }
   for (int t = 1; t <= a.T; ++t) {
     const uint16_t* cur = a.mu[(t - 1) & 1];
-    WAVE_TRY(launch(tr, k_assign, gasg, dim3(256), 0, st, a, cur));
+    if (seg_res)
+      WAVE_TRY(launch(tr, k_assign_seg, dim3(nsplit, a.nseg, BH), dim3(kA2Threads),
+                      (uint32_t)lds2, st, a, cur, nsplit));
+    else
+      WAVE_TRY(launch(tr, k_assign, gasg, dim3(256), 0, st, a, cur));
     WAVE_TRY(launch(tr, k_sort, dim3(a.nseg, BH), dim3(kSortThreads), 0, st, a));
     if (t < a.T) WAVE_TRY(launch(tr, k_update, gseg, dim3(256), 0, st, a, cur, a.mu[t & 1]));
   }

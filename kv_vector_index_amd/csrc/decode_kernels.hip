@@ -970,7 +970,7 @@ __global__ __launch_bounds__(kSelThreads) void k_dec_select(DecodeArgs a) {
         rc.mx = fmaxf(rc.mx, v);
       });
       rc = block_red3<NT>(rc, sh.red);
-      find_threshold<256>(each_c, tie_c, rc.mn, rc.mx, nr, sh, Tkey, Tid);
+      find_threshold<1024>(each_c, tie_c, rc.mn, rc.mx, nr, sh, Tkey, Tid);
     } else {
       Red3 ra{kPosInf, kNegInf, 0u};
       each_key([&](float v, int) {

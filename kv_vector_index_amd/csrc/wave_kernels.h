@@ -27,7 +27,7 @@ constexpr int kTokChunk = 128;        // steady tokens per stream workgroup
 constexpr int kPartStride = 132;      // floats per (partial, head): o[128], m, l, 2 pad
 constexpr int kHistBins = 4096;       // value-range histogram of the group scores
 constexpr int kCand = 256;            // keys ranked exactly in the histogram bin of the cut
-constexpr int kCandMax = 2048;        // candidate scores kept after the bound
+constexpr int kCandMax = 8192;        // candidate scores kept after the bound
 constexpr int kSelThreads = 512;      // select workgroup (one per (b, kv-head))
 constexpr int kMaxClusters = 65536;   // clusters per (b, kv-head) supported by the decode
 constexpr int kSelSlices = kMaxClusters / (4 * kSelThreads);  // float4 scores per select thread

@@ -216,6 +216,8 @@ CASES = {
     "one_cluster_per_segment": (dict(kseg=1, S=128), (1,)),
     "singletons": (dict(L0=300, S=64, kseg=64, n_sink=1, n_recent=2), (0, 11)),
     "many_clusters": (dict(L0=2200, S=1024, kseg=300, T=4), (12, 300)),
+    # more clusters per segment than the segment-resident assignment holds in LDS
+    "tiled_assignment": (dict(L0=1500, S=1024, kseg=600, T=2), (20,)),
 }
 
 
