@@ -105,9 +105,9 @@ def main():
     calib[1].copy_(calib[0])                                                 # calibration copy
 
     # start / end events of every kernel: build = norms, seeds, T x (assign, sort),
-    # (T - 1) x update, finalise, steady; decode = stream, select, retrieve
+    # (T - 1) x update, finalise, steady; decode = score, hist, gather, retrieve
     n_build_ev = 2 * (3 * T + 3)
-    n_dec_ev = 6
+    n_dec_ev = 8
     def events(n):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for e in ev:
@@ -169,9 +169,10 @@ def main():
             update_ms.append(kd(bev, i))
             i += 1
     fin_ms.append(kd(bev, i))
-    stream_ms = [kd(e, 0) for e in dev_]
-    select_ms = [kd(e, 1) for e in dev_]
-    retrieve_ms = [kd(e, 2) for e in dev_]
+    score_ms = [kd(e, 0) for e in dev_]
+    hist_ms = [kd(e, 1) for e in dev_]
+    gather_ms = [kd(e, 2) for e in dev_]
+    retrieve_ms = [kd(e, 3) for e in dev_]
     med = statistics.median
 
     # ---- algorithmic work (per decode call and per assignment launch)
@@ -194,13 +195,15 @@ def main():
     # whole call: centroids + sizes, value sums of the unretrieved clusters, exact K/V rows,
     # q in, out
     call_bytes = (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d) * BH
-    # stream kernel: centroids, sizes, unretrieved value sums, steady rows, q
+    # score kernel: centroids and sizes in; every head's logit and the group score out; q
+    score_bytes = (2 * C * d + 4 * C + 4 * C * G + 4 * C + 2 * G * d) * BH
+    # histogram kernel: the group scores
+    hist_bytes = 4 * C * BH
+    # gather kernel: the group scores (selection), every cluster's value sum, size and
+    # logits (estimate), the steady rows, q; the published list
     steady_mean = w.n_sink + w.n_recent + (nds + 1) / 2
-    stream_bytes = (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * steady_mean
-                    + 2 * G * d) * BH
-    # select kernel: the group scores, sizes and offsets of the retrieved clusters, and the
-    # published list (ids, first virtual row, first cache row)
-    select_bytes = (4 * C + 8 * nr + 12 * nr) * BH
+    gather_bytes = (4 * C + 2 * C * d + 4 * C + 4 * C * G + 4 * d * steady_mean + 2 * G * d
+                    + 8 * nr + 12 * nr) * BH
     # retrieve kernel: retrieved K/V rows, the removed clusters' value sums and logits, the
     # list entries, q, out
     retrieve_bytes = (4 * d * Er + (2 * d + 4 * G + 12) * nr + 2 * G * d + 4 * G * d) * BH
@@ -229,12 +232,14 @@ def main():
 
     roofs = {
         "k_assign": roof("k_assign", "mfma", assign_flop, assign_ms),
-        "k_dec_stream": roof("k_dec_stream", "hbm", stream_bytes, stream_ms),
-        "k_dec_select": roof("k_dec_select", "hbm", select_bytes, select_ms),
+        "k_dec_score": roof("k_dec_score", "hbm", score_bytes, score_ms),
+        "k_dec_hist": roof("k_dec_hist", "hbm", hist_bytes, hist_ms),
+        "k_dec_gather": roof("k_dec_gather", "hbm", gather_bytes, gather_ms),
         "k_dec_retrieve": roof("k_dec_retrieve", "hbm", retrieve_bytes, retrieve_ms),
     }
-    per_step = {"k_assign": T * mean(assign_ms), "k_dec_stream": nds * mean(stream_ms),
-                "k_dec_select": nds * mean(select_ms), "k_dec_retrieve": nds * mean(retrieve_ms)}
+    per_step = {"k_assign": T * mean(assign_ms), "k_dec_score": nds * mean(score_ms),
+                "k_dec_hist": nds * mean(hist_ms), "k_dec_gather": nds * mean(gather_ms),
+                "k_dec_retrieve": nds * mean(retrieve_ms)}
     dominant = max(per_step, key=per_step.get)
     roof_call = roof("decode call", "hbm", call_bytes, call_ms,
                      {"median_launch_us": round(med(call_ms) * 1e3, 2)})
@@ -263,8 +268,9 @@ def main():
                       "update": round(statistics.mean(update_ms) * 1e3, 2) if update_ms else None,
                       "finalise": round(statistics.mean(fin_ms) * 1e3, 2),
                       "decode_call": round(med(call_ms) * 1e3, 2),
-                      "dec_stream": round(statistics.mean(stream_ms) * 1e3, 2),
-                      "dec_select": round(statistics.mean(select_ms) * 1e3, 2),
+                      "dec_score": round(statistics.mean(score_ms) * 1e3, 2),
+                      "dec_hist": round(statistics.mean(hist_ms) * 1e3, 2),
+                      "dec_gather": round(statistics.mean(gather_ms) * 1e3, 2),
                       "dec_retrieve": round(statistics.mean(retrieve_ms) * 1e3, 2)},
         "dominant_kernel": dominant,
         "step_ms_by_kernel": {k: round(v, 3) for k, v in per_step.items()},

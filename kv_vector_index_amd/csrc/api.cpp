@@ -102,7 +102,7 @@ size_t layout_build(const wave_build_params* p, const BuildShape& sh, void* base
 // ---------------------------------------------------------------- decode
 
 struct DecodeShape {
-  int G, nS, nStMax, nB, nBDense, rcap;
+  int G, nS, nStMax, nH, nB, nG, nBDense, rcap;
   int64_t BH, cache_elems;
 };
 
@@ -143,21 +143,28 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   const int64_t avg = indexed > p->n_clusters ? indexed / p->n_clusters : 1;
   sh->nB = clampi(((int64_t)p->n_retrieve * (avg + 1) * 3 / 2 + wave::kRowsPerItem - 1) /
                       wave::kRowsPerItem, 1, wave::kMaxRetrieveWG);
+  sh->nH = (int)((sh->nS * (int64_t)wave::kChunk + wave::kSelSpan - 1) / wave::kSelSpan);
+  sh->nG = (sh->nB + wave::kMergeGroup - 1) / wave::kMergeGroup;
   sh->nBDense = clampi((p->kv_capacity + 1023) / 1024, 1, 512);
   sh->rcap = p->n_retrieve > 0 ? p->n_retrieve : 1;
   return WAVE_OK;
 }
 
-// Decode workspace (no preparation needed: the stream kernel clears the arrival counters
-// of the retrieve kernel in every call). Returns the total size.
+// Decode workspace (no preparation needed: the score kernel clears the histogram and the
+// counters in every call). Returns the total size.
 size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* base,
                      wave::DecodeArgs* a) {
   Carver cv(base);
   const size_t BH = (size_t)sh.BH, G = (size_t)sh.G, C = (size_t)p->n_clusters;
   const size_t Cp = (size_t)sh.nS * wave::kChunk;
-  const size_t nP = (size_t)sh.nStMax + sh.nS + sh.nB;
+  const size_t nP = (size_t)sh.nStMax + sh.nS + sh.nB + sh.nG;
   const size_t nPmax = nP > (size_t)sh.nBDense ? nP : (size_t)sh.nBDense;
-  uint32_t* counter = cv.take<uint32_t>(BH);
+  uint32_t* counter = cv.take<uint32_t>(BH * wave::kCtrStride);
+  uint32_t* hist = cv.take<uint32_t>(BH * wave::kHistBins);
+  float* smm = cv.take<float>(BH * (size_t)sh.nS * 2);
+  int32_t* sure = cv.take<int32_t>(BH * (size_t)sh.rcap);
+  float* tie_key = cv.take<float>(BH * C);
+  int32_t* tie_id = cv.take<int32_t>(BH * C);
   float* scores = cv.take<float>(BH * C * G);
   float* shat = cv.take<float>(BH * Cp);
   int32_t* sel_id = cv.take<int32_t>(BH * (size_t)sh.rcap);
@@ -168,6 +175,11 @@ size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* b
   float* part = cv.take<float>(BH * nPmax * G * wave::kPartStride);
   if (a) {
     a->counter = counter;
+    a->hist = hist;
+    a->smm = smm;
+    a->sure = sure;
+    a->tie_key = tie_key;
+    a->tie_id = tie_id;
     a->scores = scores;
     a->shat = shat;
     a->sel_id = sel_id;
@@ -361,8 +373,10 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   const int64_t n_steady = (int64_t)p->n_sink + p->n_recent + (p->seq_len - p->index_len);
   a.nS = sh.nS;
   a.nSt = (int)((n_steady + wave::kTokChunk - 1) / wave::kTokChunk);
+  a.nH = sh.nH;
   a.nB = sh.nB;
-  a.nP = a.nSt + a.nS + a.nB;
+  a.nG = sh.nG;
+  a.nP = a.nSt + a.nS + a.nB + a.nG;
   return wave::launch_decode(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
 }
 

@@ -394,51 +394,6 @@ __device__ __forceinline__ Red3 block_red3(Red3 r, float (*s)[3]) {
   return t;
 }
 
-// Ordered visit of nsl (<= NSMAX) slices of E entries per thread of an NT-thread block;
-// entry (slice i, thread t, element e) has order (i * NT + t) * E + e. hit(i, e) selects
-// entries; visit(i, e, rank) receives each selected entry with its rank in that order.
-// Returns the count. Slices are unrolled (i is a compile-time index for register data).
-template <int NT, int NSMAX, int E, typename Hit, typename Visit>
-__device__ __forceinline__ uint32_t ordered_visit(int nsl, Hit hit, Visit visit, uint32_t* wt) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < NSMAX; ++i)
-    if (i < nsl) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) c += hit(i, e) ? 1u : 0u;
-      uint32_t t;
-      wave_prefix_small(c, t);
-      if (lane == 0) wt[i * NW + wave] = t;
-    }
-  __syncthreads();
-  uint32_t acc = 0;
-#pragma unroll
-  for (int i = 0; i < NSMAX; ++i)
-    if (i < nsl) {
-      bool p[E];
-      uint32_t c = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        p[e] = hit(i, e);
-        c += p[e] ? 1u : 0u;
-      }
-      uint32_t t;
-      uint32_t k = wave_prefix_small(c, t) + acc;
-      for (int w = 0; w < NW; ++w) {
-        const uint32_t v = wt[i * NW + w];
-        k += w < wave ? v : 0u;
-        acc += v;
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (p[e]) visit(i, e, k++);
-    }
-  __syncthreads();
-  return acc;
-}
-
 // Histogram increment with the lanes of a wave that hit the same bin combined first (wave
 // ballots over the BITS bits of the bin give each lane its peers), so a bin receives at most
 // one LDS atomic per wave instead of one per lane. Lanes with active = false take part in
@@ -472,23 +427,6 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n) {
 // { j : s^_j > Tkey or (s^_j == Tkey and j <= Tid) } for the n_r-th pair (Tkey, Tid) in
 // (score descending, id ascending) order. Empty clusters have s^ = -inf and never qualify.
 // ------------------------------------------------------------------------------------
-constexpr int kSelWaves = kSelThreads / 64;
-
-struct SelShared {
-  uint32_t hist[kHistBins];  // value-range histogram; then the selected ids
-  float ck[kCand];
-  int32_t ci[kCand];
-  float cand_key[kCandMax];  // scores at or above the bound, ascending ids
-  int32_t cand_id[kCandMax];
-  uint32_t wt[kSelSlices * kSelWaves];
-  float red[kSelWaves][3];
-  int32_t wgr[kMaxRetrieveWG + 1];
-  uint32_t u[4];
-  float tkey;
-  int32_t tid;
-  ScanTmp<kSelThreads> tmp;
-};
-
 __device__ __forceinline__ float4 neg4() { return make_float4(kNegInf, kNegInf, kNegInf, kNegInf); }
 
 __device__ __forceinline__ bool is_selected(float v, int j, float tkey, int tid) {
@@ -505,6 +443,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // rounds monotonically). Linear in the value when the range allows it; otherwise, and on
 // every narrowing round, linear in the order-preserving integer key. Either way lo lands in
 // bin 0 and hi in a later bin, so each narrowing round strictly shrinks the candidate range.
+// The same (lo, hi) always gives the same bins, in every kernel.
 struct Binner {
   float lo, inv;   // value mode: bin = (v - lo) * inv
   uint32_t klo;    // key mode:   bin = (key(v) - klo) * kinv
@@ -523,69 +462,292 @@ struct Binner {
   }
 };
 
-// Find (Tkey, Tid) given the block-uniform range [lo, hi] of the candidate scores and
-// need in [1, #candidates]. each(f) visits every (score, id) this thread owns; tie_id(v,
-// need) returns the need-th lowest id whose score equals v (block-uniform). NB bins.
-template <int NB, typename Each, typename TieId>
-__device__ __forceinline__ void find_threshold(Each each, TieId tie_id, float lo, float hi,
-                                               uint32_t need, SelShared& sh, float& Tkey,
-                                               int& Tid) {
-  constexpr int NT = kSelThreads;
-  static_assert(NB <= kHistBins && (NB & (NB - 1)) == 0 && (NB % NT == 0 || NT % NB == 0),
-                "bins");
-  constexpr int BPT = NB >= NT ? NB / NT : 1;  // bins per thread (threads >= NB own none)
+// ------------------------------------------------------------------------------------
+// kernel 1: score (centroid logits of every cluster)
+// ------------------------------------------------------------------------------------
+// nS workgroups per (b, kv-head), 128 clusters each. The centroid rows and sizes are
+// streamed once; every query head's log2-domain logit goes to scores[], the group mean
+// (natural units) to shat[] (-inf for empty and padding clusters), and the chunk's finite
+// min / max to smm[]. Workgroup 0 of each (b, kv-head) also clears its histogram and
+// counters.
+template <int G>
+__global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
+  const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, cc = lane & 15;
+  if (blockIdx.x == 0) {
+    uint32_t* h = a.hist + (size_t)bh * kHistBins;
+    for (int i = tid; i < kHistBins; i += kDecThreads) h[i] = 0u;
+    if (tid < kCtrStride) a.counter[(size_t)bh * kCtrStride + tid] = 0u;
+  }
+  u32x4 q[G];
+  load_q<G>(a, b, g, cc, q);
+  {
+    constexpr int R = Rows<G>::R;
+    __shared__ float s_mm[kDecThreads / 64][2];
+    const size_t base = (size_t)bh * a.C;
+    float* shat = a.shat + (size_t)bh * a.Cp;
+    const int j0 = blockIdx.x * kChunk + wave * (kChunk / 4);  // this wave's clusters
+    const float sl2 = a.scale_log2, gmean = a.scale / (float)G;
+    float mn = kPosInf, mx = kNegInf;
+    for (int t = j0; t < j0 + kChunk / 4; t += 4 * R) {
+      u32x4 kr[R];
+      int32_t n[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int j = t + 4 * i + grp;
+        if (j < a.C) {
+          kr[i] = ld16_stream(a.cmean + (base + j) * kHeadDim + cc * 8);
+          n[i] = __builtin_nontemporal_load(a.csize + base + j);
+        } else {
+          kr[i] = u32x4{0, 0, 0, 0};
+          n[i] = -1;
+        }
+      }
+      float s[R][G];
+      row_logits<G, R>(q, kr, 1.f, s);
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int j = t + 4 * i + grp;
+        float sum = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) sum += s[i][h];
+        const float mean = sum * gmean;
+        const bool ok = n[i] > 0;
+        if (ok) {
+          mn = fminf(mn, mean);
+          mx = fmaxf(mx, mean);
+        }
+        if (cc == 0) shat[j] = ok ? mean : kNegInf;
+        if (n[i] >= 0 && cc < G) {
+          float mine = s[i][0];
+#pragma unroll
+          for (int h = 1; h < G; ++h) mine = (cc == h) ? s[i][h] : mine;
+          a.scores[(base + j) * G + cc] = mine * sl2;
+        }
+      }
+    }
+    mn = wave_reduce(mn, [](float x, float y) { return fminf(x, y); });
+    mx = wave_reduce(mx, [](float x, float y) { return fmaxf(x, y); });
+    if (lane == 0) {
+      s_mm[wave][0] = mn;
+      s_mm[wave][1] = mx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float* o = a.smm + ((size_t)bh * a.nS + blockIdx.x) * 2;
+      o[0] = fminf(fminf(s_mm[0][0], s_mm[1][0]), fminf(s_mm[2][0], s_mm[3][0]));
+      o[1] = fmaxf(fmaxf(s_mm[0][1], s_mm[1][1]), fmaxf(s_mm[2][1], s_mm[3][1]));
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// kernel 2: histogram of the group scores
+// ------------------------------------------------------------------------------------
+// Value-range bins over [min, max] of the head's finite group scores (from the score
+// kernel's per-chunk pairs); the same (lo, hi) and bins are recomputed by the gather kernel.
+__device__ __forceinline__ Red3 score_range(const DecodeArgs& a, int bh, float (*red)[3]) {
+  const float* mm = a.smm + (size_t)bh * a.nS * 2;
+  Red3 r{kPosInf, kNegInf, 0u};
+  for (int i = threadIdx.x; i < a.nS; i += kDecThreads) {
+    r.mn = fminf(r.mn, mm[2 * i]);
+    r.mx = fmaxf(r.mx, mm[2 * i + 1]);
+  }
+  return block_red3<kDecThreads>(r, red);
+}
+
+// nH workgroups per (b, kv-head), kSelSpan scores each, add their histogram into hist[].
+__global__ __launch_bounds__(kDecThreads) void k_dec_hist(DecodeArgs a) {
+  constexpr int NT = kDecThreads;
+  __shared__ uint32_t hs[kHistBins];
+  __shared__ float red[NT / 64][3];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const Red3 r = score_range(a, bh, red);
+  if (r.mx == kNegInf) return;  // no finite score in this head
+  for (int i = tid; i < kHistBins; i += NT) hs[i] = 0u;
+  __syncthreads();
+  const Binner bn(r.mn, r.mx, true);
+  const float* sh = a.shat + (size_t)bh * a.Cp;
+#pragma unroll
+  for (int k = 0; k < kSelSpan / (4 * NT); ++k) {
+    const int j4 = blockIdx.x * kSelSpan + k * 4 * NT + 4 * tid;
+    const float4 v = j4 < a.Cp ? *reinterpret_cast<const float4*>(sh + j4) : neg4();
+    hist_add<12>(hs, v.x != kNegInf ? bn(v.x) : 0, v.x != kNegInf);
+    hist_add<12>(hs, v.y != kNegInf ? bn(v.y) : 0, v.y != kNegInf);
+    hist_add<12>(hs, v.z != kNegInf ? bn(v.z) : 0, v.z != kNegInf);
+    hist_add<12>(hs, v.w != kNegInf ? bn(v.w) : 0, v.w != kNegInf);
+  }
+  __syncthreads();
+  uint32_t* gh = a.hist + (size_t)bh * kHistBins;
+  for (int i = tid; i < kHistBins; i += NT)
+    if (hs[i]) atomicAdd(gh + i, hs[i]);
+}
+
+// ------------------------------------------------------------------------------------
+// kernel 3: gather (the selection) and estimate (every cluster's centroid term)
+// ------------------------------------------------------------------------------------
+struct FinShared {
+  union {
+    uint32_t bits[kMaxClusters / 32];  // selection bitmap over cluster ids
+    uint32_t hist[kNarrowBins];        // histogram of a crowded cut bin
+  } u;
+  float ck[kCand];
+  int32_t ci[kCand];
+  int32_t wgr[kMaxRetrieveWG + 1];
+  float red[kDecThreads / 64][3];
+  ScanTmp<kDecThreads> tmp;
+  uint32_t v[4];
+  float tkey;
+  int32_t tid;
+  uint32_t base[2];
+};
+
+// The cut of a (b, kv-head): need = min(n_r, finite scores) and the histogram bin b* that
+// holds the need-th largest score (b* = kHistBins when need = 0), from the complete
+// histogram; every workgroup that calls this computes the same values.
+struct Cut {
+  float lo, hi;
+  int bstar;
+  uint32_t need;
+};
+__device__ Cut find_cut(const DecodeArgs& a, int bh, FinShared& sh) {
+  constexpr int NT = kDecThreads, BPT = kHistBins / NT;
   const int tid = threadIdx.x;
+  const Red3 r = score_range(a, bh, sh.red);
+  const uint32_t* gh = a.hist + (size_t)bh * kHistBins;
+  const int hb0 = kHistBins - BPT * (tid + 1);  // thread t's bins, visited from the top
+  uint32_t hc[BPT], loc = 0;
+  if (r.mx != kNegInf) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      hc[i] = gh[hb0 + i];
+      loc += hc[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) hc[i] = 0u;
+  }
+  uint32_t ne;
+  uint32_t run = scan_excl<NT>(loc, sh.tmp, &ne);
+  const uint32_t need = min((uint32_t)a.n_retrieve, ne);
+  if (tid == 0) sh.v[0] = kHistBins;
+  __syncthreads();
+#pragma unroll
+  for (int i = BPT - 1; i >= 0; --i) {
+    if (run < need && run + hc[i] >= need) sh.v[0] = (uint32_t)(hb0 + i);
+    run += hc[i];
+  }
+  __syncthreads();
+  Cut c{r.mn, r.mx, (int)sh.v[0], need};
+  __syncthreads();
+  return c;
+}
+
+// Set bit j of the selection bitmap.
+__device__ __forceinline__ void mark(FinShared& sh, int j) {
+  atomicOr(&sh.u.bits[j >> 5], 1u << (j & 31));
+}
+
+// The need-th lowest id among the n listed clusters whose score equals v (need >= 1).
+__device__ int nth_id_with_score(const float* tk, const int32_t* ti, uint32_t n, float v,
+                                 uint32_t need, FinShared& sh) {
+  constexpr int NT = kDecThreads, WPT = kMaxClusters / 32 / NT;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kMaxClusters / 32; i += NT) sh.u.bits[i] = 0u;
+  __syncthreads();
+  for (uint32_t k = tid; k < n; k += NT)
+    if (ld_dev(tk + k) == v) mark(sh, ld_dev(ti + k));
+  __syncthreads();
+  uint32_t w[WPT], c = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    w[i] = sh.u.bits[tid * WPT + i];
+    c += __popc(w[i]);
+  }
+  uint32_t tot;
+  uint32_t run = scan_excl<NT>(c, sh.tmp, &tot);
+  if (run < need && run + c >= need) {
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      uint32_t x = w[i];
+      while (x) {
+        const int bit = __builtin_ctz(x);
+        x &= x - 1u;
+        if (++run == need) sh.tid = (tid * WPT + i) * 32 + bit;
+      }
+    }
+  }
+  __syncthreads();
+  const int r = sh.tid;
+  __syncthreads();
+  return r;
+}
+
+// (Tkey, Tid): the need-th pair (score descending, id ascending) among the n listed
+// clusters of the cut bin (1 <= need < n). Value-range histograms narrow the range until
+// the bin holding the pair has at most kCand scores, which are then ranked exactly.
+__device__ void cut_pair(const float* tk, const int32_t* ti, uint32_t n, uint32_t need,
+                         FinShared& sh, float& Tkey, int& Tid) {
+  constexpr int NT = kDecThreads, BPT = kNarrowBins / NT;
+  const int tid = threadIdx.x;
+  Red3 r{kPosInf, kNegInf, 0u};
+  for (uint32_t k = tid; k < n; k += NT) {
+    const float v = ld_dev(tk + k);
+    r.mn = fminf(r.mn, v);
+    r.mx = fmaxf(r.mx, v);
+  }
+  r = block_red3<NT>(r, sh.red);
+  float lo = r.mn, hi = r.mx;
   bool first = true;
   for (;;) {
-    if (lo == hi) {  // every remaining candidate has the same score
+    if (lo == hi) {  // every remaining score is lo
       Tkey = lo;
-      Tid = tie_id(lo, need);
+      Tid = nth_id_with_score(tk, ti, n, lo, need, sh);
       return;
     }
     const Binner b4k(lo, hi, first);
-    auto bin = [&](float v) { return b4k(v) / (kHistBins / NB); };
     first = false;
-    for (int i = tid; i < NB; i += NT) sh.hist[i] = 0u;
+    auto bin = [&](float v) { return b4k(v) / (kHistBins / kNarrowBins); };
+    for (int i = tid; i < kNarrowBins; i += NT) sh.u.hist[i] = 0u;
     __syncthreads();
-    constexpr int BITS = __builtin_ctz(NB);
-    each([&](float v, int) {
-      const bool in = v >= lo && v <= hi;
-      hist_add<BITS>(sh.hist, in ? bin(v) : 0, in);
-    });
+    for (uint32_t k0 = 0; k0 < n; k0 += NT) {
+      const uint32_t k = k0 + tid;
+      const float v = k < n ? ld_dev(tk + k) : kNegInf;
+      const bool in = k < n && v >= lo && v <= hi;
+      hist_add<10>(sh.u.hist, in ? bin(v) : 0, in);
+    }
     __syncthreads();
-    // bin b* of the need-th largest score: thread t owns BPT bins, visited descending
-    const int hb0 = NB - BPT * (tid + 1);
-    const bool owns = NB >= NT || tid < NB;
+    const int hb0 = kNarrowBins - BPT * (tid + 1);
     uint32_t hc[BPT], loc = 0;
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
-      hc[i] = owns ? sh.hist[hb0 + i] : 0u;
+      hc[i] = sh.u.hist[hb0 + i];
       loc += hc[i];
     }
     uint32_t tot;
     uint32_t run = scan_excl<NT>(loc, sh.tmp, &tot);
 #pragma unroll
     for (int i = BPT - 1; i >= 0; --i) {
-      if (owns && run < need && run + hc[i] >= need) {
-        sh.u[0] = (uint32_t)(hb0 + i);
-        sh.u[1] = run;
+      if (run < need && run + hc[i] >= need) {
+        sh.v[0] = (uint32_t)(hb0 + i);
+        sh.v[1] = run;
       }
       run += hc[i];
     }
-    if (tid == 0) sh.u[2] = 0u;
+    if (tid == 0) sh.v[2] = 0u;
     __syncthreads();
-    const int bstar = (int)sh.u[0];
-    const uint32_t need2 = need - sh.u[1];
-    const uint32_t cnt = sh.hist[bstar];
+    const int bstar = (int)sh.v[0];
+    const uint32_t need2 = need - sh.v[1], cnt = sh.u.hist[bstar];
     if (cnt <= (uint32_t)kCand) {
-      // rank the keys of bin b* exactly
-      each([&](float v, int j) {
+      for (uint32_t k = tid; k < n; k += NT) {
+        const float v = ld_dev(tk + k);
         if (v >= lo && v <= hi && bin(v) == bstar) {
-          const uint32_t k = atomicAdd(&sh.u[2], 1u);
-          sh.ck[k] = v;
-          sh.ci[k] = j;
+          const uint32_t c = atomicAdd(&sh.v[2], 1u);
+          sh.ck[c] = v;
+          sh.ci[c] = ld_dev(ti + k);
         }
-      });
+      }
       __syncthreads();
       if (tid < (int)cnt) {
         const float mv = sh.ck[tid];
@@ -606,93 +768,260 @@ __device__ __forceinline__ void find_threshold(Each each, TieId tie_id, float lo
       __syncthreads();
       return;
     }
-    // too many keys in b*: narrow the range to that bin's keys and repeat
-    Red3 r{kPosInf, kNegInf, 0u};
-    each([&](float v, int) {
+    Red3 rb{kPosInf, kNegInf, 0u};
+    for (uint32_t k = tid; k < n; k += NT) {
+      const float v = ld_dev(tk + k);
       if (v >= lo && v <= hi && bin(v) == bstar) {
-        r.mn = fminf(r.mn, v);
-        r.mx = fmaxf(r.mx, v);
+        rb.mn = fminf(rb.mn, v);
+        rb.mx = fmaxf(rb.mx, v);
       }
-    });
-    r = block_red3<NT>(r, sh.red);
-    lo = r.mn;
-    hi = r.mx;
+    }
+    rb = block_red3<NT>(rb, sh.red);
+    lo = rb.mn;
+    hi = rb.mx;
     need = need2;
   }
 }
 
-// ------------------------------------------------------------------------------------
-// kernel 1: stream (scores + estimate of every cluster, and the steady zone)
-// ------------------------------------------------------------------------------------
+// The last gather workgroup of a (b, kv-head): the exact cut among the clusters of the cut
+// bin, the selection bitmap, and from it the published list in ascending id order (ids,
+// first virtual row, first cache row), `selected`, and each retrieve workgroup's share.
+__device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinShared& sh) {
+  constexpr int NT = kDecThreads, WPT = kMaxClusters / 32 / NT;
+  const int tid = threadIdx.x;
+  const size_t cb = (size_t)bh * a.C;
+  const uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
+  const uint32_t nsure = min(ld_dev(ctr + kCtrSure), (uint32_t)a.rcap);
+  const uint32_t ntie = min(ld_dev(ctr + kCtrTie), (uint32_t)a.C);
+  const float* tk = a.tie_key + cb;
+  const int32_t* ti = a.tie_id + cb;
+  float Tkey = kNegInf;  // default: every listed cluster of the cut bin
+  int Tid = 0x7fffffff;
+  if (need > nsure && need - nsure < ntie) cut_pair(tk, ti, ntie, need - nsure, sh, Tkey, Tid);
+  for (int i = tid; i < kMaxClusters / 32; i += NT) sh.u.bits[i] = 0u;
+  __syncthreads();
+  if (need > 0) {
+    const int32_t* su = a.sure + (size_t)bh * a.rcap;
+    for (uint32_t k = tid; k < nsure; k += NT) mark(sh, ld_dev(su + k));
+    for (uint32_t k = tid; k < ntie; k += NT) {
+      const int j = ld_dev(ti + k);
+      if (is_selected(ld_dev(tk + k), j, Tkey, Tid)) mark(sh, j);
+    }
+  }
+  __syncthreads();
+  // ordered compaction: thread t holds ids [t * 32 * WPT, (t + 1) * 32 * WPT), its ranks
+  // start at the exclusive scan of the counts (the list holds at most rcap clusters; the
+  // counts above make nsel = need <= rcap)
+  uint32_t w[WPT], c = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    w[i] = sh.u.bits[tid * WPT + i];
+    c += __popc(w[i]);
+  }
+  uint32_t nsel;
+  uint32_t k = scan_excl<NT>(c, sh.tmp, &nsel);  // (its barriers also end the bitmap reads)
+  nsel = min(nsel, (uint32_t)a.rcap);
+  int32_t* sid = a.sel_id + (size_t)bh * a.rcap;
+  int32_t* sts = a.sel_ts + (size_t)bh * (a.rcap + 1);
+  int32_t* sco = a.sel_coff + (size_t)bh * a.rcap;
+  int32_t* selo = a.selected ? a.selected + (size_t)bh * a.n_retrieve : nullptr;
+  int32_t* lst = reinterpret_cast<int32_t*>(sh.u.bits);  // the first kListLds listed ids
+  constexpr uint32_t kListLds = kMaxClusters / 32;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    uint32_t x = w[i];
+    while (x) {
+      const int j = (tid * WPT + i) * 32 + __builtin_ctz(x);
+      x &= x - 1u;
+      if (k < nsel) {
+        st_dev(sid + k, (int32_t)j);
+        if (selo) selo[k] = j;
+        if (k < kListLds) lst[k] = j;
+      }
+      ++k;
+    }
+  }
+  if (selo)
+    for (int i = (int)nsel + tid; i < a.n_retrieve; i += NT) selo[i] = -1;
+  __syncthreads();
+  // sizes and first rows: thread t takes ranks [t * per, (t + 1) * per), loads first
+  auto listed = [&](uint32_t r) { return r < kListLds ? lst[r] : ld_dev(sid + r); };
+  const uint32_t per = (nsel + NT - 1) / NT, r0 = tid * per, r1 = min(nsel, r0 + per);
+  int32_t sz4[4], co4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sz4[i] = co4[i] = 0;
+    if (r0 + i < r1) {
+      const int j = listed(r0 + i);
+      sz4[i] = a.csize[cb + j];
+      co4[i] = a.coff[cb + j];
+    }
+  }
+  uint32_t tok = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tok += r0 + i < r1 ? (uint32_t)sz4[i] + 1u : 0u;
+  for (uint32_t r = r0 + 4; r < r1; ++r) tok += (uint32_t)a.csize[cb + listed(r)] + 1u;
+  uint32_t V;
+  uint32_t pos = scan_excl<NT>(tok, sh.tmp, &V);
+  const int nB = a.nB;
+  auto emit = [&](uint32_t r, int32_t n, int32_t co) {
+    const uint32_t te = pos + (uint32_t)n + 1u;
+    sts[r] = (int32_t)pos;
+    sco[r] = co;
+    // retrieve workgroups whose first virtual row falls in [pos, te)
+    const int w0 = (int)(((uint64_t)pos * nB + V - 1) / V);
+    const int w1 = (int)(((uint64_t)te * nB + V - 1) / V);
+    for (int wi = w0; wi < w1; ++wi) sh.wgr[wi] = (int32_t)r;
+    pos = te;
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (r0 + i < r1) emit(r0 + i, sz4[i], co4[i]);
+  for (uint32_t r = r0 + 4; r < r1; ++r) {
+    const int j = listed(r);
+    emit(r, a.csize[cb + j], a.coff[cb + j]);
+  }
+  if (tid == 0) {
+    a.sel_n[bh] = (int32_t)nsel;
+    sts[nsel] = (int32_t)V;
+  }
+  __syncthreads();
+  // per retrieve workgroup: its virtual rows [T0, T1) and listed clusters [r_lo, r_hi)
+  for (int wi = tid; wi < nB; wi += NT) {
+    const int T0 = (int)((uint64_t)V * wi / nB), T1 = (int)((uint64_t)V * (wi + 1) / nB);
+    int lo = 0, hi = 0;
+    if (T0 < T1) {
+      lo = sh.wgr[wi];
+      hi = wi + 1 < nB ? min((int)nsel, sh.wgr[wi + 1] + 1) : (int)nsel;
+    }
+    reinterpret_cast<int4*>(a.wg_info)[(size_t)bh * kMaxRetrieveWG + wi] = make_int4(T0, T1, lo, hi);
+  }
+}
+
+// Workgroups [0, nH) of a (b, kv-head) list the clusters of their kSelSpan scores that lie
+// above the cut bin (all selected) or in it (ranked by the last workgroup to arrive, which
+// then publishes the selection). Workgroups [nH, nH + nS) fold the centroid estimate of
+// their 128 clusters (weight n_j, logit s_j, value sum V_j) into partial slot c = x - nH;
+// workgroups [nH + nS, nH + nS + nSt) attend exactly to 128 steady tokens each, into
+// partial slot nS + (x - nH - nS).
 template <int G>
-__global__ __launch_bounds__(kDecThreads) void k_dec_stream(DecodeArgs a) {
-  const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = lane >> 4, cc = lane & 15;
-  if (blockIdx.x == 0 && blockIdx.y == 0)  // arrival counters of the retrieve kernel
-    for (int i = tid; i < a.B * a.Hkv; i += kDecThreads) a.counter[i] = 0u;
-  u32x4 q[G];
-  load_q<G>(a, b, g, cc, q);
-  Online<G> st;
-  st.init();
-  if ((int)blockIdx.x < a.nS) {
+__global__ __launch_bounds__(kDecThreads) void k_dec_gather(DecodeArgs a) {
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  if ((int)blockIdx.x >= a.nH + a.nS) {
+    const int b = bh / a.Hkv, g = bh % a.Hkv, wave = tid >> 6, cc = tid & 15;
+    u32x4 q[G];
+    load_q<G>(a, b, g, cc, q);
+    Online<G> st;
+    st.init();
+    const int s = blockIdx.x - a.nH - a.nS;
+    const int64_t n_steady = (int64_t)a.n_sink + a.n_recent + (a.L - a.L0);
+    const int64_t wbeg = (int64_t)s * kTokChunk + wave * (kTokChunk / 4);
+    const int64_t wend = min(n_steady, wbeg + kTokChunk / 4);
+    attend_rows<G>(a, bh, q, st, wbeg, wend, [&](int64_t t) { return steady_row(a, t); });
+    write_block_partial<G>(st, nullptr,
+                           a.part + ((size_t)bh * a.nP + a.nS + s) * G * kPartStride);
+    return;
+  }
+  if ((int)blockIdx.x >= a.nH) {
+    const int c = blockIdx.x - a.nH;
+    const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, cc = lane & 15;
     constexpr int R = Rows<G>::R;
+    Online<G> st;
+    st.init();
     const size_t base = (size_t)bh * a.C;
-    float* shat = a.shat + (size_t)bh * a.Cp;
-    const int j0 = blockIdx.x * kChunk + wave * (kChunk / 4);  // this wave's clusters
-    const float sl2 = a.scale_log2, gmean = a.scale / (float)G;
+    const int j0 = c * kChunk + wave * (kChunk / 4);
     for (int t = j0; t < j0 + kChunk / 4; t += 4 * R) {
-      u32x4 kr[R], vr[R];
+      u32x4 vr[R];
       int32_t n[R];
+      float s2[R][G], w[R], sg[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int j = t + 4 * i + grp;
         if (j < a.C) {
-          const size_t row = (base + j) * kHeadDim + cc * 8;
-          kr[i] = ld16_stream(a.cmean + row);
-          vr[i] = ld16_stream(a.vsum + row);
+          vr[i] = ld16_stream(a.vsum + (base + j) * kHeadDim + cc * 8);
           n[i] = __builtin_nontemporal_load(a.csize + base + j);
+          const float* sp = a.scores + (base + j) * G;
+#pragma unroll
+          for (int h = 0; h < G; ++h) s2[i][h] = sp[h];
         } else {
-          kr[i] = vr[i] = u32x4{0, 0, 0, 0};
-          n[i] = -1;
+          vr[i] = u32x4{0, 0, 0, 0};
+          n[i] = 0;
+#pragma unroll
+          for (int h = 0; h < G; ++h) s2[i][h] = kNegInf;
         }
       }
-      float s[R][G], w[R], sg[R];
-      row_logits<G, R>(q, kr, 1.f, s);
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const int j = t + 4 * i + grp;
         const bool ok = n[i] > 0;
-        float sum = 0.f;
-#pragma unroll
-        for (int h = 0; h < G; ++h) sum += s[i][h];
-        const float mean = sum * gmean;
-        if (cc == 0) shat[j] = ok ? mean : kNegInf;
-        if (n[i] >= 0 && cc < G) {
-          float mine = s[i][0];
-#pragma unroll
-          for (int h = 1; h < G; ++h) mine = (cc == h) ? s[i][h] : mine;
-          a.scores[(base + j) * G + cc] = mine * sl2;
-        }
         w[i] = ok ? (float)n[i] : 0.f;
         sg[i] = 1.f;
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = ok ? s[i][h] * sl2 : kNegInf;
+        for (int h = 0; h < G; ++h) s2[i][h] = ok ? s2[i][h] : kNegInf;
       }
-      fold_rows<G, R>(st, s, w, vr, sg);
+      fold_rows<G, R>(st, s2, w, vr, sg);
     }
-  } else {
-    const int64_t n_steady = (int64_t)a.n_sink + a.n_recent + (a.L - a.L0);
-    const int64_t wbeg = (int64_t)(blockIdx.x - a.nS) * kTokChunk + wave * (kTokChunk / 4);
-    const int64_t wend = min(n_steady, wbeg + kTokChunk / 4);
-    attend_rows<G>(a, bh, q, st, wbeg, wend, [&](int64_t t) { return steady_row(a, t); });
+    write_block_partial<G>(st, nullptr, a.part + ((size_t)bh * a.nP + c) * G * kPartStride);
+    return;
   }
-  write_block_partial<G>(st, nullptr,
-                         a.part + ((size_t)bh * a.nP + blockIdx.x) * G * kPartStride);
+  __shared__ FinShared sh;
+  const Cut cut = find_cut(a, bh, sh);
+  uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
+  if (cut.need > 0) {
+    constexpr int E = kSelSpan / kDecThreads;  // scores per thread
+    const Binner bn(cut.lo, cut.hi, true);
+    const float* shv = a.shat + (size_t)bh * a.Cp;
+    float v[E];
+    int bv[E];
+    uint32_t ns = 0, nt = 0;
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) {
+      const int j4 = blockIdx.x * kSelSpan + k * 4 * kDecThreads + 4 * tid;
+      const float4 v4 = j4 < a.Cp ? *reinterpret_cast<const float4*>(shv + j4) : neg4();
+      v[4 * k] = v4.x;
+      v[4 * k + 1] = v4.y;
+      v[4 * k + 2] = v4.z;
+      v[4 * k + 3] = v4.w;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      bv[e] = v[e] != kNegInf ? bn(v[e]) : -1;
+      ns += bv[e] > cut.bstar ? 1u : 0u;
+      nt += bv[e] == cut.bstar ? 1u : 0u;
+    }
+    // one reservation per workgroup and list
+    uint32_t tns, tnt;
+    uint32_t ps = scan_excl<kDecThreads>(ns, sh.tmp, &tns);
+    uint32_t pt = scan_excl<kDecThreads>(nt, sh.tmp, &tnt);
+    if (tid == 0) {
+      sh.base[0] = tns ? atomicAdd(ctr + kCtrSure, tns) : 0u;
+      sh.base[1] = tnt ? atomicAdd(ctr + kCtrTie, tnt) : 0u;
+    }
+    __syncthreads();
+    ps += sh.base[0];
+    pt += sh.base[1];
+    int32_t* su = a.sure + (size_t)bh * a.rcap;
+    float* tk = a.tie_key + (size_t)bh * a.C;
+    int32_t* ti = a.tie_id + (size_t)bh * a.C;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = blockIdx.x * kSelSpan + (e >> 2) * 4 * kDecThreads + 4 * tid + (e & 3);
+      if (bv[e] > cut.bstar) {
+        if (ps < (uint32_t)a.rcap) st_dev(su + ps, (int32_t)j);
+        ++ps;
+      } else if (bv[e] == cut.bstar) {
+        if (pt < (uint32_t)a.C) {
+          st_dev(tk + pt, v[e]);
+          st_dev(ti + pt, (int32_t)j);
+        }
+        ++pt;
+      }
+    }
+  }
+  if (arrive_last(ctr + kCtrGather, (uint32_t)a.nH)) finish_select(a, bh, cut.need, sh);
 }
 
 // ------------------------------------------------------------------------------------
-// kernel 2: retrieve
+// kernel 4: retrieve
 // ------------------------------------------------------------------------------------
 
 // Exact attention and estimate removal over the virtual rows [wb, we) of the listed
@@ -757,9 +1086,12 @@ __device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, cons
   }
 }
 
+// nB workgroups per (b, kv-head): each takes a share of the estimate and steady partials
+// and its virtual rows, and writes one partial. The last of every kMergeGroup workgroups
+// merges their partials; the last of those merges writes out / lse.
 template <int G>
 __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
-  __shared__ float s_x[G][kPartStride];  // this workgroup's share of the stream partials
+  __shared__ float s_x[G][kPartStride];  // this workgroup's share of the earlier partials
   __shared__ int32_t l_ts[kWinR + 1], l_co[kWinR], l_id[kWinR];
   const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv, w_item = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cc = lane & 15;
@@ -769,7 +1101,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   const int4 info = reinterpret_cast<const int4*>(a.wg_info)[(size_t)bh * kMaxRetrieveWG + w_item];
   const int T0 = info.x, T1 = info.y, r_lo = info.z, r_hi = info.w;
   const int32_t* g_ts = a.sel_ts + (size_t)bh * (a.rcap + 1);
-  // ---- this workgroup's stream partials w_item, w_item + nB, ... merged into s_x
+  // ---- the estimate / steady partials w_item, w_item + nB, ... merged into s_x
   for (int idx = tid; idx < G * 128; idx += kDecThreads) {
     float M, Ls, O;
     merge_partials<false>(parts, G, idx, w_item, nB, nSP, M, Ls, O);
@@ -802,266 +1134,34 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
     __syncthreads();
   }
   write_block_partial<G>(st, &s_x[0][0], parts + (size_t)(nSP + w_item) * G * kPartStride);
-  if (arrive_last(a.counter + bh, (uint32_t)nB)) {
-    const int bq = b * a.Hq + g * G;
-    for (int idx = tid; idx < G * 128; idx += kDecThreads) {
-      float M, Ls, O;
-      merge_partials<true, 32>(parts, G, idx, nSP, 1, nSP + nB, M, Ls, O);
-      const int h = idx >> 7, d = idx & 127;
+  uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
+  const int grp = w_item / kMergeGroup, g0 = grp * kMergeGroup, gn = min(kMergeGroup, nB - g0);
+  if (!arrive_last(ctr + kCtrGroup + grp, (uint32_t)gn)) return;
+  const int bq = b * a.Hq + g * G;
+  const bool single = a.nG == 1;
+  float* gp = parts + (size_t)(nSP + nB + grp) * G * kPartStride;
+  for (int idx = tid; idx < G * 128; idx += kDecThreads) {
+    float M, Ls, O;
+    merge_partials<true, kMergeGroup>(parts, G, idx, nSP + g0, 1, nSP + g0 + gn, M, Ls, O);
+    const int h = idx >> 7, d = idx & 127;
+    if (single) {
       a.out[(size_t)(bq + h) * kHeadDim + d] = O / Ls;
       if (d == 0 && a.lse) a.lse[bq + h] = (M + log2f(Ls)) * kLn2;
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------
-// select: one 512-thread workgroup per (b, kv-head). It finds the n_r-th (score, id) pair,
-// lists the retrieved clusters in ascending id order with their first virtual row and
-// first cache row, writes the `selected` output, and records the virtual rows and clusters
-// of every retrieve workgroup. The group scores (<= 65536, 128 per thread) stay in
-// registers; one CU's vector throughput bounds this kernel, so each step is O(scores):
-//   1. a lower bound of the n_r-th largest score: with q = ceil(n_r / 512), each thread's
-//      q-th largest score v_t; if u = ceil(n_r / q) threads have v_t >= b, at least
-//      u * q >= n_r scores are >= b. The bound is the 256-bin histogram bin (over the range
-//      of the v_t) holding the u-th largest v_t: every score in it or above qualifies.
-//   2. the qualifying scores (a few more than n_r), in ascending id order;
-//   3. the exact pair among them (value-range histogram, then an exact rank in the cut bin);
-//   4. ordered compaction, cluster sizes, prefix of the virtual rows.
-// Any step that cannot hold its data falls back to the same search over every score.
-// ------------------------------------------------------------------------------------
-template <int NS>  // float4 score slices per thread (>= ceil(Cp / 2048))
-__global__ __launch_bounds__(kSelThreads) void k_dec_select(DecodeArgs a) {
-  constexpr int NT = kSelThreads;
-  __shared__ SelShared sh;
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int Cp = a.Cp, ns = (Cp + 4 * NT - 1) / (4 * NT);
-  const float* shat = a.shat + (size_t)bh * Cp;
-  const size_t cb = (size_t)bh * a.C;
-  float4 kf[NS];  // ids 4 * (i * NT + tid) + e
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int j4 = 4 * (i * NT + tid);
-    kf[i] = (i < ns && j4 < Cp) ? *reinterpret_cast<const float4*>(shat + j4) : neg4();
-  }
-  auto key_at = [&](int i, int e) {
-    return e == 0 ? kf[i].x : e == 1 ? kf[i].y : e == 2 ? kf[i].z : kf[i].w;
-  };
-  auto id_of = [&](int i, int e) { return 4 * (i * NT + tid) + e; };
-  auto each_key = [&](auto f) {
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      if (i < ns) {
-        f(kf[i].x, id_of(i, 0));
-        f(kf[i].y, id_of(i, 1));
-        f(kf[i].z, id_of(i, 2));
-        f(kf[i].w, id_of(i, 3));
-      }
-  };
-  auto tie_key = [&](float v, uint32_t need) -> int {
-    ordered_visit<NT, NS, 4>(ns, [&](int i, int e) { return key_at(i, e) == v; },
-                                     [&](int i, int e, uint32_t k) {
-                                       if (k + 1 == need) sh.tid = id_of(i, e);
-                                     },
-                                     sh.wt);
-    const int r = sh.tid;
-    __syncthreads();
-    return r;
-  };
-  // ---- 1. the bound
-  const int nreq = a.n_retrieve;
-  const int q = min(4, max(1, (nreq + NT - 1) / NT));
-  float t0 = kNegInf, t1 = kNegInf, t2 = kNegInf, t3 = kNegInf;  // this thread's top 4
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int i = 0; i < NS; ++i)
-    if (i < ns) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = key_at(i, e);
-        cnt += v != kNegInf ? 1u : 0u;
-        if (q > 1) {
-          t3 = fmaxf(t3, fminf(t2, v));
-          t2 = fmaxf(t2, fminf(t1, v));
-          t1 = fmaxf(t1, fminf(t0, v));
-        }
-        t0 = fmaxf(t0, v);
-      }
-    }
-  const float vq = q == 1 ? t0 : q == 2 ? t1 : q == 3 ? t2 : t3;
-  Red3 r{vq != kNegInf ? vq : kPosInf, vq, cnt};
-  r = block_red3<NT>(r, sh.red);  // range of the finite v_t, count of finite scores
-  const uint32_t ne = r.n, nr = min((uint32_t)nreq, ne);
-  float Tkey = kPosInf;
-  int Tid = -1;
-  bool cand = false;
-  uint32_t m = 0;
-  auto keep = [&](int i, int e, uint32_t k) {
-    if (k < (uint32_t)kCandMax) {
-      sh.cand_key[k] = key_at(i, e);
-      sh.cand_id[k] = id_of(i, e);
-    }
-  };
-  if (nr > 0 && nr == ne) {
-    Tkey = kNegInf;  // every non-empty cluster
-  } else if (nr > 0) {
-    // the bound: the histogram bin (256 bins over the range of the finite v_t) that holds
-    // the u-th largest v_t; every score in that bin or above qualifies
-    const uint32_t u = (uint32_t)((nreq + q - 1) / q);
-    if (r.mx != kNegInf && r.mn < r.mx) {
-      const Binner vb(r.mn, r.mx, true);
-      auto b256 = [&](float v) { return vb(v) >> 4; };
-      if (tid < 256) sh.hist[tid] = 0u;
-      __syncthreads();
-      hist_add<8>(sh.hist, vq != kNegInf ? b256(vq) : 0, vq != kNegInf);
-      __syncthreads();
-      const uint32_t h = tid < 256 ? sh.hist[255 - tid] : 0u;  // thread t: bin 255 - t
-      uint32_t tot;
-      const uint32_t above = scan_excl<NT>(h, sh.tmp, &tot);
-      if (tid < 256 && above < u && above + h >= u) sh.u[0] = 255u - tid;
-      if (tid == 0 && tot < u) sh.u[0] = 0xffffffffu;  // fewer than u finite v_t
-      __syncthreads();
-      const uint32_t bb = sh.u[0];
-      __syncthreads();
-      if (bb != 0xffffffffu) {
-        // the smallest v_t in that bin (<= the u-th largest v_t) is the bound
-        Red3 rb{vq != kNegInf && b256(vq) == (int)bb ? vq : kPosInf, kNegInf, 0u};
-        rb = block_red3<NT>(rb, sh.red);
-        const float bound = rb.mn;
-        m = ordered_visit<NT, NS, 4>(
-            ns, [&](int i, int e) { return key_at(i, e) >= bound; }, keep, sh.wt);
-        cand = true;
-      }
-    } else if (r.mx != kNegInf) {  // all finite v_t are equal
-      m = ordered_visit<NT, NS, 4>(
-          ns,
-          [&](int i, int e) {
-            const float v = key_at(i, e);
-            return v != kNegInf && v >= r.mn;
-          },
-          keep, sh.wt);
-      cand = true;
-    }
-    // the candidates hold the whole selection iff at least nr scores reach the bound
-    cand = cand && m <= (uint32_t)kCandMax && m >= nr;
-    if (cand) {
-      // ---- 3. the exact pair among the candidates
-      const int nslc = (int)((m + NT - 1) / NT);
-      auto each_c = [&](auto f) {
-        for (int k = tid; k < (int)m; k += NT) f(sh.cand_key[k], sh.cand_id[k]);
-      };
-      auto tie_c = [&](float v, uint32_t need) -> int {
-        ordered_visit<NT, kCandMax / NT, 1>(
-            nslc,
-            [&](int i, int) {
-              const int k = i * NT + tid;
-              return k < (int)m && sh.cand_key[k] == v;
-            },
-            [&](int i, int, uint32_t k) {
-              if (k + 1 == need) sh.tid = sh.cand_id[i * NT + tid];
-            },
-            sh.wt);
-        const int res = sh.tid;
-        __syncthreads();
-        return res;
-      };
-      Red3 rc{kPosInf, kNegInf, 0u};
-      each_c([&](float v, int) {
-        rc.mn = fminf(rc.mn, v);
-        rc.mx = fmaxf(rc.mx, v);
-      });
-      rc = block_red3<NT>(rc, sh.red);
-      find_threshold<1024>(each_c, tie_c, rc.mn, rc.mx, nr, sh, Tkey, Tid);
     } else {
-      Red3 ra{kPosInf, kNegInf, 0u};
-      each_key([&](float v, int) {
-        if (v != kNegInf) {
-          ra.mn = fminf(ra.mn, v);
-          ra.mx = fmaxf(ra.mx, v);
-        }
-      });
-      ra = block_red3<NT>(ra, sh.red);
-      find_threshold<kHistBins>(each_key, tie_key, ra.mn, ra.mx, nr, sh, Tkey, Tid);
+      st_dev(gp + h * kPartStride + d, O);
+      if (d == 0) {
+        st_dev(gp + h * kPartStride + 128, M);
+        st_dev(gp + h * kPartStride + 129, Ls);
+      }
     }
   }
-  // ---- 4. the selection in ascending id order: published list, `selected`, LDS copy
-  int32_t* sid = a.sel_id + (size_t)bh * a.rcap;
-  int32_t* sts = a.sel_ts + (size_t)bh * (a.rcap + 1);
-  int32_t* sco = a.sel_coff + (size_t)bh * a.rcap;
-  int32_t* selo = a.selected ? a.selected + (size_t)bh * a.n_retrieve : nullptr;
-  int32_t* lst = reinterpret_cast<int32_t*>(sh.hist);  // the first kHistBins selected ids
-  auto put = [&](int j, uint32_t k) {
-    sid[k] = j;
-    if (selo) selo[k] = j;
-    if (k < (uint32_t)kHistBins) lst[k] = j;
-  };
-  uint32_t nsel;
-  if (cand) {
-    nsel = ordered_visit<NT, kCandMax / NT, 1>(
-        (int)((m + NT - 1) / NT),
-        [&](int i, int) {
-          const int k = i * NT + tid;
-          return k < (int)m && is_selected(sh.cand_key[k], sh.cand_id[k], Tkey, Tid);
-        },
-        [&](int i, int, uint32_t k) { put(sh.cand_id[i * NT + tid], k); }, sh.wt);
-  } else {
-    nsel = ordered_visit<NT, NS, 4>(
-        ns, [&](int i, int e) { return is_selected(key_at(i, e), id_of(i, e), Tkey, Tid); },
-        [&](int i, int e, uint32_t k) { put(id_of(i, e), k); }, sh.wt);
-  }
-  if (selo)
-    for (int i = (int)nsel + tid; i < a.n_retrieve; i += NT) selo[i] = -1;
-  // sizes and first rows of the listed clusters (thread t: ranks [t * per, (t + 1) * per))
-  auto listed = [&](int k) { return k < kHistBins ? lst[k] : ld_dev(sid + k); };
-  const int per = (int)((nsel + NT - 1) / NT), k0 = tid * per;
-  const int k1 = min((int)nsel, k0 + per);
-  int32_t sz4[4], co4[4];  // the first four of this thread's clusters
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    sz4[k] = co4[k] = 0;
-    if (k0 + k < k1) {
-      const int j = listed(k0 + k);
-      sz4[k] = a.csize[cb + j];
-      co4[k] = a.coff[cb + j];
-    }
-  }
-  uint32_t tok = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) tok += k0 + k < k1 ? (uint32_t)sz4[k] + 1u : 0u;
-  for (int k = k0 + 4; k < k1; ++k) tok += (uint32_t)a.csize[cb + listed(k)] + 1u;
-  uint32_t V;
-  uint32_t pos = scan_excl<NT>(tok, sh.tmp, &V);
-  const int nB = a.nB;
-  auto emit = [&](int k, int32_t n, int32_t co) {
-    const uint32_t te = pos + (uint32_t)n + 1u;
-    sts[k] = (int32_t)pos;
-    sco[k] = co;
-    // retrieve workgroups whose first virtual row falls in [pos, te)
-    const int w0 = (int)(((uint64_t)pos * nB + V - 1) / V);
-    const int w1 = (int)(((uint64_t)te * nB + V - 1) / V);
-    for (int w = w0; w < w1; ++w) sh.wgr[w] = k;
-    pos = te;
-  };
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    if (k0 + k < k1) emit(k0 + k, sz4[k], co4[k]);
-  for (int k = k0 + 4; k < k1; ++k) {
-    const int j = listed(k);
-    emit(k, a.csize[cb + j], a.coff[cb + j]);
-  }
-  if (tid == 0) {
-    a.sel_n[bh] = (int32_t)nsel;
-    sts[nsel] = (int32_t)V;
-  }
-  __syncthreads();
-  // per retrieve workgroup: its virtual rows [T0, T1) and listed clusters [r_lo, r_hi)
-  if (tid < nB) {
-    const int T0 = (int)((uint64_t)V * tid / nB), T1 = (int)((uint64_t)V * (tid + 1) / nB);
-    int lo = 0, hi = 0;
-    if (T0 < T1) {
-      lo = sh.wgr[tid];
-      hi = tid + 1 < nB ? min((int)nsel, sh.wgr[tid + 1] + 1) : (int)nsel;
-    }
-    reinterpret_cast<int4*>(a.wg_info)[(size_t)bh * kMaxRetrieveWG + tid] = make_int4(T0, T1, lo, hi);
+  if (single || !arrive_last(ctr + kCtrFinal, (uint32_t)a.nG)) return;
+  for (int idx = tid; idx < G * 128; idx += kDecThreads) {
+    float M, Ls, O;
+    merge_partials<true, kMergeGroup>(parts, G, idx, nSP + nB, 1, nSP + nB + a.nG, M, Ls, O);
+    const int h = idx >> 7, d = idx & 127;
+    a.out[(size_t)(bq + h) * kHeadDim + d] = O / Ls;
+    if (d == 0 && a.lse) a.lse[bq + h] = (M + log2f(Ls)) * kLn2;
   }
 }
 
@@ -1102,12 +1202,11 @@ __global__ __launch_bounds__(kDecThreads) void k_dense_merge(DecodeArgs a) {
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   const int BH = a.B * a.Hkv;
-  hipError_t e = launch(tr, k_dec_stream<G>, dim3(a.nS + a.nSt, BH), dim3(kDecThreads), 0, s, a);
+  hipError_t e = launch(tr, k_dec_score<G>, dim3(a.nS, BH), dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
-  const int ns = (a.Cp + 4 * kSelThreads - 1) / (4 * kSelThreads);
-  auto sel = ns <= 1 ? k_dec_select<1> : ns <= 2 ? k_dec_select<2> : ns <= 4 ? k_dec_select<4>
-           : ns <= 8 ? k_dec_select<8> : ns <= 16 ? k_dec_select<16> : k_dec_select<32>;
-  e = launch(tr, sel, dim3(BH), dim3(kSelThreads), 0, s, a);
+  e = launch(tr, k_dec_hist, dim3(a.nH, BH), dim3(kDecThreads), 0, s, a);
+  if (e != hipSuccess) return e;
+  e = launch(tr, k_dec_gather<G>, dim3(a.nH + a.nS + a.nSt, BH), dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
   return launch(tr, k_dec_retrieve<G>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
 }

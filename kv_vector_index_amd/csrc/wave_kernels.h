@@ -22,22 +22,29 @@ struct Tracer {
 
 // ---------------------------------------------------------------- decode
 constexpr int kDecThreads = 256;      // every decode workgroup: 4 waves
-constexpr int kChunk = 128;           // clusters per stream workgroup (32 per wave)
-constexpr int kTokChunk = 128;        // steady tokens per stream workgroup
+constexpr int kChunk = 128;           // clusters per score / estimate workgroup (32 per wave)
+constexpr int kTokChunk = 128;        // steady tokens per steady workgroup
 constexpr int kPartStride = 132;      // floats per (partial, head): o[128], m, l, 2 pad
+constexpr int kSelSpan = 2048;        // group scores per histogram / gather workgroup
 constexpr int kHistBins = 4096;       // value-range histogram of the group scores
-constexpr int kCand = 256;            // keys ranked exactly in the histogram bin of the cut
-constexpr int kCandMax = 8192;        // candidate scores kept after the bound
-constexpr int kSelThreads = 512;      // select workgroup (one per (b, kv-head))
+constexpr int kNarrowBins = 1024;     // histogram of a crowded cut bin's scores
+constexpr int kCand = 256;            // scores ranked exactly in LDS
 constexpr int kMaxClusters = 65536;   // clusters per (b, kv-head) supported by the decode
-constexpr int kSelSlices = kMaxClusters / (4 * kSelThreads);  // float4 scores per select thread
 constexpr int kMaxRetrieveWG = 256;   // retrieve workgroups per (b, kv-head)
+constexpr int kMergeGroup = 16;       // retrieve partials merged per first-level merge
 constexpr int kWinR = 1024;           // listed clusters staged per LDS window of a retrieve WG
 constexpr int kRowsPerItem = 128;     // retrieved rows per retrieve workgroup (target)
+// per (b, kv-head) counters, cleared by the score kernel in every call
+constexpr int kCtrStride = 32;
+constexpr int kCtrGather = 1;         // gather workgroups arrived
+constexpr int kCtrSure = 2;           // clusters above the cut bin listed so far
+constexpr int kCtrTie = 3;            // clusters in the cut bin listed so far
+constexpr int kCtrFinal = 4;          // first-level merges arrived
+constexpr int kCtrGroup = 8;          // + group: retrieve workgroups of that group arrived
 
 // A retrieved cluster j of size n_j occupies n_j + 1 consecutive "virtual rows": its n_j
 // tokens, then one row that removes its centroid estimate (logit s_j, weight -n_j, value
-// -V_j) from the stream kernel's estimate over all clusters.
+// -V_j) from the estimate over all clusters.
 struct DecodeArgs {
   // inputs
   const uint16_t* q;       // [B, Hq, d]
@@ -52,7 +59,12 @@ struct DecodeArgs {
   float* lse;              // [B, Hq] or null
   int32_t* selected;       // [B, Hkv, n_retrieve] or null
   // workspace
-  uint32_t* counter;       // [BH] retrieve-workgroup arrivals (cleared by the stream kernel)
+  uint32_t* counter;       // [BH, kCtrStride]
+  uint32_t* hist;          // [BH, kHistBins] value-range histogram of the group scores
+  float* smm;              // [BH, nS, 2] min and max finite group score of each chunk
+  int32_t* sure;           // [BH, rcap] clusters above the cut bin (arrival order)
+  float* tie_key;          // [BH, C] clusters in the cut bin (arrival order): score, id
+  int32_t* tie_id;
   float* scores;           // [BH, C, G] log2-domain centroid logits of each query head
   float* shat;             // [BH, Cp] group-mean logits (natural units; -inf: empty / pad)
   int32_t* sel_id;         // [BH, rcap] the selection (ascending ids)
@@ -65,11 +77,14 @@ struct DecodeArgs {
   int B, Hq, Hkv, G;
   int64_t L, L0, Lcap;
   int C, Cp, n_sink, n_recent, n_retrieve, rcap;
-  int nS, nSt, nB, nP;     // per (b, kv-head): stream chunks, steady chunks, retrieve groups
+  // per (b, kv-head): estimate chunks, steady chunks, select workgroups, retrieve
+  // workgroups, first-level merge groups, partial slots (estimate, steady, retrieve, merge)
+  int nS, nSt, nH, nB, nG, nP;
   float scale, scale_log2;
 };
 
-// Enqueue one tripartite decode step. Returns the first launch error.
+// Enqueue one tripartite decode step (score, histogram, gather, retrieve kernels). Returns
+// the first launch error.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
 // Enqueue dense decode over [0, L): split-K partials (part, nB per head) + merge.
 hipError_t launch_dense_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
