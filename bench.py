@@ -199,11 +199,11 @@ def main():
     score_bytes = (2 * C * d + 4 * C + 4 * C * G + 4 * C + 2 * G * d) * BH
     # histogram kernel: the group scores
     hist_bytes = 4 * C * BH
-    # gather kernel: the group scores (selection), every cluster's value sum, size and
-    # logits (estimate), the steady rows, q; the published list
+    # gather kernel: the group scores (selection) and the published list; every cluster's
+    # value sum, size and logits (estimate); the steady rows; q
     steady_mean = w.n_sink + w.n_recent + (nds + 1) / 2
-    gather_bytes = (4 * C + 2 * C * d + 4 * C + 4 * C * G + 4 * d * steady_mean + 2 * G * d
-                    + 8 * nr + 12 * nr) * BH
+    gather_bytes = (4 * C + 8 * nr + 12 * nr + 2 * C * d + 4 * C + 4 * C * G
+                    + 4 * d * steady_mean + 2 * G * d) * BH
     # retrieve kernel: retrieved K/V rows, the removed clusters' value sums and logits, the
     # list entries, q, out
     retrieve_bytes = (4 * d * Er + (2 * d + 4 * G + 12) * nr + 2 * G * d + 4 * G * d) * BH

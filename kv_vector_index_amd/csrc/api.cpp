@@ -4,6 +4,8 @@
 #include "../../include/wave_index.h"
 
 #include <math.h>
+
+#include <algorithm>
 #include <string.h>
 
 #include "wave_kernels.h"
@@ -102,7 +104,7 @@ size_t layout_build(const wave_build_params* p, const BuildShape& sh, void* base
 // ---------------------------------------------------------------- decode
 
 struct DecodeShape {
-  int G, nS, nStMax, nH, nB, nG, nBDense, rcap;
+  int G, nS, nSW, nEW, nStMax, nH, nB, nG, nBDense, rcap;
   int64_t BH, cache_elems;
 };
 
@@ -141,10 +143,16 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   // run larger than average)
   const int64_t indexed = p->index_len - p->n_sink - p->n_recent;
   const int64_t avg = indexed > p->n_clusters ? indexed / p->n_clusters : 1;
+  // and at most about four workgroups per CU over all (b, kv-heads), so that they all run
+  // in one round
+  const int nb_cap = clampi(wave::kRetrieveWGPerCall / bh, 1, wave::kMaxRetrieveWG);
   sh->nB = clampi(((int64_t)p->n_retrieve * (avg + 1) * 3 / 2 + wave::kRowsPerItem - 1) /
-                      wave::kRowsPerItem, 1, wave::kMaxRetrieveWG);
-  sh->nH = (int)((sh->nS * (int64_t)wave::kChunk + wave::kSelSpan - 1) / wave::kSelSpan);
+                      wave::kRowsPerItem, 1, nb_cap);
+  // score / estimate workgroups: a few per CU over all (b, kv-heads), looping over chunks
+  sh->nSW = clampi(wave::kScoreWGPerCall / bh, 1, sh->nS);
+  sh->nEW = sh->nS;
   sh->nG = (sh->nB + wave::kMergeGroup - 1) / wave::kMergeGroup;
+  sh->nH = (int)((sh->nS * (int64_t)wave::kChunk + wave::kSelSpan - 1) / wave::kSelSpan);
   sh->nBDense = clampi((p->kv_capacity + 1023) / 1024, 1, 512);
   sh->rcap = p->n_retrieve > 0 ? p->n_retrieve : 1;
   return WAVE_OK;
@@ -157,11 +165,11 @@ size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* b
   Carver cv(base);
   const size_t BH = (size_t)sh.BH, G = (size_t)sh.G, C = (size_t)p->n_clusters;
   const size_t Cp = (size_t)sh.nS * wave::kChunk;
-  const size_t nP = (size_t)sh.nStMax + sh.nS + sh.nB + sh.nG;
+  const size_t nP = (size_t)sh.nEW + sh.nStMax + sh.nB + sh.nG;
   const size_t nPmax = nP > (size_t)sh.nBDense ? nP : (size_t)sh.nBDense;
   uint32_t* counter = cv.take<uint32_t>(BH * wave::kCtrStride);
   uint32_t* hist = cv.take<uint32_t>(BH * wave::kHistBins);
-  float* smm = cv.take<float>(BH * (size_t)sh.nS * 2);
+  float* smm = cv.take<float>(BH * (size_t)sh.nSW * 2);
   int32_t* sure = cv.take<int32_t>(BH * (size_t)sh.rcap);
   float* tie_key = cv.take<float>(BH * C);
   int32_t* tie_id = cv.take<int32_t>(BH * C);
@@ -373,10 +381,12 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   const int64_t n_steady = (int64_t)p->n_sink + p->n_recent + (p->seq_len - p->index_len);
   a.nS = sh.nS;
   a.nSt = (int)((n_steady + wave::kTokChunk - 1) / wave::kTokChunk);
+  a.nSW = sh.nSW;
+  a.nEW = sh.nEW;
   a.nH = sh.nH;
   a.nB = sh.nB;
   a.nG = sh.nG;
-  a.nP = a.nSt + a.nS + a.nB + a.nG;
+  a.nP = a.nEW + a.nSt + a.nB + a.nG;
   return wave::launch_decode(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
 }
 

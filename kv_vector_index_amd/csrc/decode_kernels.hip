@@ -465,13 +465,26 @@ struct Binner {
 // ------------------------------------------------------------------------------------
 // kernel 1: score (centroid logits of every cluster)
 // ------------------------------------------------------------------------------------
-// nS workgroups per (b, kv-head), 128 clusters each. The centroid rows and sizes are
-// streamed once; every query head's log2-domain logit goes to scores[], the group mean
-// (natural units) to shat[] (-inf for empty and padding clusters), and the chunk's finite
-// min / max to smm[]. Workgroup 0 of each (b, kv-head) also clears its histogram and
-// counters.
+// Clusters [c0, c1) of a workgroup, a contiguous share of the nS chunks of 128 clusters of
+// its (b, kv-head) split over nw workgroups.
+struct Share {
+  int c0, c1;
+};
+__device__ __forceinline__ Share chunk_share(int nS, int nw, int w) {
+  const int k0 = (int)((int64_t)nS * w / nw), k1 = (int)((int64_t)nS * (w + 1) / nw);
+  return {k0 * kChunk, k1 * kChunk};
+}
+
+// nSW workgroups per (b, kv-head), each over a share of the clusters in steps of 16R rows
+// (4R per wave), the rows of the next step loaded while the current step is scored. The
+// centroid rows and sizes are streamed once; every query head's log2-domain logit goes to
+// scores[], the group mean (natural units) to shat[] (-inf for empty and padding clusters),
+// and the workgroup's finite min / max to smm[]. Workgroup 0 of each (b, kv-head) also
+// clears its histogram and counters.
 template <int G>
 __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
+  constexpr int R = Rows<G>::R;
+  __shared__ float s_mm[kDecThreads / 64][2];
   const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, cc = lane & 15;
@@ -482,63 +495,72 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
   }
   u32x4 q[G];
   load_q<G>(a, b, g, cc, q);
-  {
-    constexpr int R = Rows<G>::R;
-    __shared__ float s_mm[kDecThreads / 64][2];
-    const size_t base = (size_t)bh * a.C;
-    float* shat = a.shat + (size_t)bh * a.Cp;
-    const int j0 = blockIdx.x * kChunk + wave * (kChunk / 4);  // this wave's clusters
-    const float sl2 = a.scale_log2, gmean = a.scale / (float)G;
-    float mn = kPosInf, mx = kNegInf;
-    for (int t = j0; t < j0 + kChunk / 4; t += 4 * R) {
-      u32x4 kr[R];
-      int32_t n[R];
+  const size_t base = (size_t)bh * a.C;
+  float* shat = a.shat + (size_t)bh * a.Cp;
+  const float sl2 = a.scale_log2, gmean = a.scale / (float)G;
+  const Share sh = chunk_share(a.nS, a.nSW, blockIdx.x);
+  // (unconditional loads, masked afterwards: straight-line loads let the compiler wait for
+  // exactly the step in use while the next one is in flight; rows past the share re-read
+  // its last row, already cached)
+  const int jmax = min(a.C, sh.c1) - 1;
+  auto load = [&](int t, u32x4 (&kr)[R], int32_t (&n)[R]) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int j = t + 4 * i + grp;
-        if (j < a.C) {
-          kr[i] = ld16_stream(a.cmean + (base + j) * kHeadDim + cc * 8);
-          n[i] = __builtin_nontemporal_load(a.csize + base + j);
-        } else {
-          kr[i] = u32x4{0, 0, 0, 0};
-          n[i] = -1;
-        }
+    for (int i = 0; i < R; ++i) {
+      const int j = t + 4 * i + grp;
+      const size_t jc = base + min(j, jmax);
+      kr[i] = ld16_stream(a.cmean + jc * kHeadDim + cc * 8);
+      n[i] = __builtin_nontemporal_load(a.csize + jc);
+      if (j >= a.C || t >= sh.c1) n[i] = -1;
+    }
+  };
+  float mn = kPosInf, mx = kNegInf;
+  u32x4 kr[R];
+  int32_t n[R];
+  int t = sh.c0 + wave * 4 * R;  // this wave's first row of each step
+  load(t, kr, n);
+  for (; t < sh.c1; t += 16 * R) {
+    u32x4 kn[R];
+    int32_t nn[R];
+    load(t + 16 * R, kn, nn);
+    float s[R][G];
+    row_logits<G, R>(q, kr, 1.f, s);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int j = t + 4 * i + grp;
+      float sum = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) sum += s[i][h];
+      const float mean = sum * gmean;
+      const bool ok = n[i] > 0;
+      if (ok) {
+        mn = fminf(mn, mean);
+        mx = fmaxf(mx, mean);
       }
-      float s[R][G];
-      row_logits<G, R>(q, kr, 1.f, s);
+      if (cc == 0) shat[j] = ok ? mean : kNegInf;
+      if (n[i] >= 0 && cc < G) {
+        float mine = s[i][0];
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int j = t + 4 * i + grp;
-        float sum = 0.f;
-#pragma unroll
-        for (int h = 0; h < G; ++h) sum += s[i][h];
-        const float mean = sum * gmean;
-        const bool ok = n[i] > 0;
-        if (ok) {
-          mn = fminf(mn, mean);
-          mx = fmaxf(mx, mean);
-        }
-        if (cc == 0) shat[j] = ok ? mean : kNegInf;
-        if (n[i] >= 0 && cc < G) {
-          float mine = s[i][0];
-#pragma unroll
-          for (int h = 1; h < G; ++h) mine = (cc == h) ? s[i][h] : mine;
-          a.scores[(base + j) * G + cc] = mine * sl2;
-        }
+        for (int h = 1; h < G; ++h) mine = (cc == h) ? s[i][h] : mine;
+        a.scores[(base + j) * G + cc] = mine * sl2;
       }
     }
-    mn = wave_reduce(mn, [](float x, float y) { return fminf(x, y); });
-    mx = wave_reduce(mx, [](float x, float y) { return fmaxf(x, y); });
-    if (lane == 0) {
-      s_mm[wave][0] = mn;
-      s_mm[wave][1] = mx;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      kr[i] = kn[i];
+      n[i] = nn[i];
     }
-    __syncthreads();
-    if (tid == 0) {
-      float* o = a.smm + ((size_t)bh * a.nS + blockIdx.x) * 2;
-      o[0] = fminf(fminf(s_mm[0][0], s_mm[1][0]), fminf(s_mm[2][0], s_mm[3][0]));
-      o[1] = fmaxf(fmaxf(s_mm[0][1], s_mm[1][1]), fmaxf(s_mm[2][1], s_mm[3][1]));
-    }
+  }
+  mn = wave_reduce(mn, [](float x, float y) { return fminf(x, y); });
+  mx = wave_reduce(mx, [](float x, float y) { return fmaxf(x, y); });
+  if (lane == 0) {
+    s_mm[wave][0] = mn;
+    s_mm[wave][1] = mx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float* o = a.smm + ((size_t)bh * a.nSW + blockIdx.x) * 2;
+    o[0] = fminf(fminf(s_mm[0][0], s_mm[1][0]), fminf(s_mm[2][0], s_mm[3][0]));
+    o[1] = fmaxf(fmaxf(s_mm[0][1], s_mm[1][1]), fmaxf(s_mm[2][1], s_mm[3][1]));
   }
 }
 
@@ -546,11 +568,11 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
 // kernel 2: histogram of the group scores
 // ------------------------------------------------------------------------------------
 // Value-range bins over [min, max] of the head's finite group scores (from the score
-// kernel's per-chunk pairs); the same (lo, hi) and bins are recomputed by the gather kernel.
+// workgroups' pairs); the same (lo, hi) and bins are recomputed by the gather kernel.
 __device__ __forceinline__ Red3 score_range(const DecodeArgs& a, int bh, float (*red)[3]) {
-  const float* mm = a.smm + (size_t)bh * a.nS * 2;
+  const float* mm = a.smm + (size_t)bh * a.nSW * 2;
   Red3 r{kPosInf, kNegInf, 0u};
-  for (int i = threadIdx.x; i < a.nS; i += kDecThreads) {
+  for (int i = threadIdx.x; i < a.nSW; i += kDecThreads) {
     r.mn = fminf(r.mn, mm[2 * i]);
     r.mx = fmaxf(r.mx, mm[2 * i + 1]);
   }
@@ -834,7 +856,7 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
       const int j = (tid * WPT + i) * 32 + __builtin_ctz(x);
       x &= x - 1u;
       if (k < nsel) {
-        st_dev(sid + k, (int32_t)j);
+        sid[k] = j;
         if (selo) selo[k] = j;
         if (k < kListLds) lst[k] = j;
       }
@@ -845,7 +867,7 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
     for (int i = (int)nsel + tid; i < a.n_retrieve; i += NT) selo[i] = -1;
   __syncthreads();
   // sizes and first rows: thread t takes ranks [t * per, (t + 1) * per), loads first
-  auto listed = [&](uint32_t r) { return r < kListLds ? lst[r] : ld_dev(sid + r); };
+  auto listed = [&](uint32_t r) { return r < kListLds ? lst[r] : sid[r]; };
   const uint32_t per = (nsel + NT - 1) / NT, r0 = tid * per, r1 = min(nsel, r0 + per);
   int32_t sz4[4], co4[4];
 #pragma unroll
@@ -898,69 +920,85 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
   }
 }
 
-// Workgroups [0, nH) of a (b, kv-head) list the clusters of their kSelSpan scores that lie
+// One-dimensional grid, by role (so the selection workgroups of every (b, kv-head) are
+// dispatched first): nH per (b, kv-head) list the clusters of their kSelSpan scores that lie
 // above the cut bin (all selected) or in it (ranked by the last workgroup to arrive, which
-// then publishes the selection). Workgroups [nH, nH + nS) fold the centroid estimate of
-// their 128 clusters (weight n_j, logit s_j, value sum V_j) into partial slot c = x - nH;
-// workgroups [nH + nS, nH + nS + nSt) attend exactly to 128 steady tokens each, into
-// partial slot nS + (x - nH - nS).
+// then publishes the selection); then nEW = nS per (b, kv-head) fold the centroid estimate
+// of a chunk of 128 clusters each (weight n_j, logit s_j, value sum V_j) into partial slot
+// e; then nSt per (b, kv-head) attend exactly to 128 steady tokens each, into partial slot
+// nEW + s. The value-sum stream of the estimate does not depend on the selection and runs
+// beside it.
 template <int G>
 __global__ __launch_bounds__(kDecThreads) void k_dec_gather(DecodeArgs a) {
-  const int bh = blockIdx.y, tid = threadIdx.x;
-  if ((int)blockIdx.x >= a.nH + a.nS) {
-    const int b = bh / a.Hkv, g = bh % a.Hkv, wave = tid >> 6, cc = tid & 15;
-    u32x4 q[G];
-    load_q<G>(a, b, g, cc, q);
-    Online<G> st;
-    st.init();
-    const int s = blockIdx.x - a.nH - a.nS;
-    const int64_t n_steady = (int64_t)a.n_sink + a.n_recent + (a.L - a.L0);
-    const int64_t wbeg = (int64_t)s * kTokChunk + wave * (kTokChunk / 4);
-    const int64_t wend = min(n_steady, wbeg + kTokChunk / 4);
-    attend_rows<G>(a, bh, q, st, wbeg, wend, [&](int64_t t) { return steady_row(a, t); });
-    write_block_partial<G>(st, nullptr,
-                           a.part + ((size_t)bh * a.nP + a.nS + s) * G * kPartStride);
-    return;
+  const int BH = a.B * a.Hkv, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, cc = lane & 15;
+  int x = blockIdx.x, bh;
+  if (x < a.nH * BH) {
+    bh = x / a.nH;
+    x -= bh * a.nH;
+  } else if (x < (a.nH + a.nEW) * BH) {
+    x -= a.nH * BH;
+    bh = x / a.nEW;
+    x = a.nH + (x - bh * a.nEW);
+  } else {
+    x -= (a.nH + a.nEW) * BH;
+    bh = x / a.nSt;
+    x = a.nH + a.nEW + (x - bh * a.nSt);
   }
-  if ((int)blockIdx.x >= a.nH) {
-    const int c = blockIdx.x - a.nH;
-    const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, cc = lane & 15;
-    constexpr int R = Rows<G>::R;
+  if (x >= a.nH) {
+    const int b = bh / a.Hkv, g = bh % a.Hkv;
     Online<G> st;
     st.init();
-    const size_t base = (size_t)bh * a.C;
-    const int j0 = c * kChunk + wave * (kChunk / 4);
-    for (int t = j0; t < j0 + kChunk / 4; t += 4 * R) {
-      u32x4 vr[R];
-      int32_t n[R];
-      float s2[R][G], w[R], sg[R];
+    int slot;
+    if (x < a.nH + a.nEW) {
+      // ---- estimate: chunk e of 128 clusters, 4R rows per wave and step
+      const int e = x - a.nH;
+      constexpr int R = Rows<G>::R;
+      const size_t base = (size_t)bh * a.C;
+      const int j0 = e * kChunk + wave * (kChunk / 4);
+      for (int t = j0; t < j0 + kChunk / 4; t += 4 * R) {
+        u32x4 vr[R];
+        int32_t n[R];
+        float s2[R][G], w[R], sg[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int j = t + 4 * i + grp;
-        if (j < a.C) {
-          vr[i] = ld16_stream(a.vsum + (base + j) * kHeadDim + cc * 8);
-          n[i] = __builtin_nontemporal_load(a.csize + base + j);
-          const float* sp = a.scores + (base + j) * G;
+        for (int i = 0; i < R; ++i) {
+          const int j = t + 4 * i + grp;
+          if (j < a.C) {
+            vr[i] = ld16_stream(a.vsum + (base + j) * kHeadDim + cc * 8);
+            n[i] = __builtin_nontemporal_load(a.csize + base + j);
+            const float* sp = a.scores + (base + j) * G;
 #pragma unroll
-          for (int h = 0; h < G; ++h) s2[i][h] = sp[h];
-        } else {
-          vr[i] = u32x4{0, 0, 0, 0};
-          n[i] = 0;
+            for (int h = 0; h < G; ++h) s2[i][h] = sp[h];
+          } else {
+            vr[i] = u32x4{0, 0, 0, 0};
+            n[i] = 0;
 #pragma unroll
-          for (int h = 0; h < G; ++h) s2[i][h] = kNegInf;
+            for (int h = 0; h < G; ++h) s2[i][h] = kNegInf;
+          }
         }
-      }
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const bool ok = n[i] > 0;
-        w[i] = ok ? (float)n[i] : 0.f;
-        sg[i] = 1.f;
+        for (int i = 0; i < R; ++i) {
+          const bool ok = n[i] > 0;
+          w[i] = ok ? (float)n[i] : 0.f;
+          sg[i] = 1.f;
 #pragma unroll
-        for (int h = 0; h < G; ++h) s2[i][h] = ok ? s2[i][h] : kNegInf;
+          for (int h = 0; h < G; ++h) s2[i][h] = ok ? s2[i][h] : kNegInf;
+        }
+        fold_rows<G, R>(st, s2, w, vr, sg);
       }
-      fold_rows<G, R>(st, s2, w, vr, sg);
+      slot = e;
+    } else {
+      // ---- steady: 128 tokens
+      const int s = x - a.nH - a.nEW;
+      u32x4 q[G];
+      load_q<G>(a, b, g, cc, q);
+      const int64_t n_steady = (int64_t)a.n_sink + a.n_recent + (a.L - a.L0);
+      const int64_t wbeg = (int64_t)s * kTokChunk + wave * (kTokChunk / 4);
+      const int64_t wend = min(n_steady, wbeg + kTokChunk / 4);
+      attend_rows<G>(a, bh, q, st, wbeg, wend, [&](int64_t t) { return steady_row(a, t); });
+      slot = a.nEW + s;
     }
-    write_block_partial<G>(st, nullptr, a.part + ((size_t)bh * a.nP + c) * G * kPartStride);
+    write_block_partial<G>(st, nullptr, a.part + ((size_t)bh * a.nP + slot) * G * kPartStride);
     return;
   }
   __shared__ FinShared sh;
@@ -975,7 +1013,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gather(DecodeArgs a) {
     uint32_t ns = 0, nt = 0;
 #pragma unroll
     for (int k = 0; k < E / 4; ++k) {
-      const int j4 = blockIdx.x * kSelSpan + k * 4 * kDecThreads + 4 * tid;
+      const int j4 = x * kSelSpan + k * 4 * kDecThreads + 4 * tid;
       const float4 v4 = j4 < a.Cp ? *reinterpret_cast<const float4*>(shv + j4) : neg4();
       v[4 * k] = v4.x;
       v[4 * k + 1] = v4.y;
@@ -1004,7 +1042,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gather(DecodeArgs a) {
     int32_t* ti = a.tie_id + (size_t)bh * a.C;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int j = blockIdx.x * kSelSpan + (e >> 2) * 4 * kDecThreads + 4 * tid + (e & 3);
+      const int j = x * kSelSpan + (e >> 2) * 4 * kDecThreads + 4 * tid + (e & 3);
       if (bv[e] > cut.bstar) {
         if (ps < (uint32_t)a.rcap) st_dev(su + ps, (int32_t)j);
         ++ps;
@@ -1033,7 +1071,7 @@ __device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, cons
                                                Online<G>& st, int wb, int we, const int32_t* ts,
                                                const int32_t* co, const int32_t* id, int r_lo,
                                                int r_hi) {
-  constexpr int R = Rows<G>::R;
+  constexpr int R = Rows<G>::R / 2;  // (register budget: four retrieve workgroups per CU)
   constexpr int GX = G > 4 ? G - 4 : 1;
   const int lane = threadIdx.x & 63, grp = lane >> 4, cc = lane & 15;
   const size_t kb = (size_t)bh * a.Lcap, cb = (size_t)bh * a.C;
@@ -1095,7 +1133,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   __shared__ int32_t l_ts[kWinR + 1], l_co[kWinR], l_id[kWinR];
   const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv, w_item = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cc = lane & 15;
-  const int nB = a.nB, nSP = a.nS + a.nSt;
+  const int nB = a.nB, nSP = a.nEW + a.nSt;
   float* parts = a.part + (size_t)bh * a.nP * G * kPartStride;
   // ---- this workgroup's virtual rows [T0, T1) and listed clusters [r_lo, r_hi)
   const int4 info = reinterpret_cast<const int4*>(a.wg_info)[(size_t)bh * kMaxRetrieveWG + w_item];
@@ -1142,7 +1180,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   float* gp = parts + (size_t)(nSP + nB + grp) * G * kPartStride;
   for (int idx = tid; idx < G * 128; idx += kDecThreads) {
     float M, Ls, O;
-    merge_partials<true, kMergeGroup>(parts, G, idx, nSP + g0, 1, nSP + g0 + gn, M, Ls, O);
+    merge_partials<true, 8>(parts, G, idx, nSP + g0, 1, nSP + g0 + gn, M, Ls, O);
     const int h = idx >> 7, d = idx & 127;
     if (single) {
       a.out[(size_t)(bq + h) * kHeadDim + d] = O / Ls;
@@ -1158,7 +1196,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   if (single || !arrive_last(ctr + kCtrFinal, (uint32_t)a.nG)) return;
   for (int idx = tid; idx < G * 128; idx += kDecThreads) {
     float M, Ls, O;
-    merge_partials<true, kMergeGroup>(parts, G, idx, nSP + nB, 1, nSP + nB + a.nG, M, Ls, O);
+    merge_partials<true, 8>(parts, G, idx, nSP + nB, 1, nSP + nB + a.nG, M, Ls, O);
     const int h = idx >> 7, d = idx & 127;
     a.out[(size_t)(bq + h) * kHeadDim + d] = O / Ls;
     if (d == 0 && a.lse) a.lse[bq + h] = (M + log2f(Ls)) * kLn2;
@@ -1202,11 +1240,12 @@ __global__ __launch_bounds__(kDecThreads) void k_dense_merge(DecodeArgs a) {
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   const int BH = a.B * a.Hkv;
-  hipError_t e = launch(tr, k_dec_score<G>, dim3(a.nS, BH), dim3(kDecThreads), 0, s, a);
+  hipError_t e = launch(tr, k_dec_score<G>, dim3(a.nSW, BH), dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
   e = launch(tr, k_dec_hist, dim3(a.nH, BH), dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
-  e = launch(tr, k_dec_gather<G>, dim3(a.nH + a.nS + a.nSt, BH), dim3(kDecThreads), 0, s, a);
+  e = launch(tr, k_dec_gather<G>, dim3((a.nH + a.nEW + a.nSt) * BH), dim3(kDecThreads), 0, s,
+             a);
   if (e != hipSuccess) return e;
   return launch(tr, k_dec_retrieve<G>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
 }

@@ -34,9 +34,12 @@ constexpr int kMaxRetrieveWG = 256;   // retrieve workgroups per (b, kv-head)
 constexpr int kMergeGroup = 16;       // retrieve partials merged per first-level merge
 constexpr int kWinR = 1024;           // listed clusters staged per LDS window of a retrieve WG
 constexpr int kRowsPerItem = 128;     // retrieved rows per retrieve workgroup (target)
+constexpr int kRetrieveWGPerCall = 1024;  // retrieve workgroups of one call (at most, about)
+// score workgroups of one call (about): three resident per CU, one round
+constexpr int kScoreWGPerCall = 768;
 // per (b, kv-head) counters, cleared by the score kernel in every call
 constexpr int kCtrStride = 32;
-constexpr int kCtrGather = 1;         // gather workgroups arrived
+constexpr int kCtrGather = 1;         // select workgroups of the gather kernel arrived
 constexpr int kCtrSure = 2;           // clusters above the cut bin listed so far
 constexpr int kCtrTie = 3;            // clusters in the cut bin listed so far
 constexpr int kCtrFinal = 4;          // first-level merges arrived
@@ -61,7 +64,7 @@ struct DecodeArgs {
   // workspace
   uint32_t* counter;       // [BH, kCtrStride]
   uint32_t* hist;          // [BH, kHistBins] value-range histogram of the group scores
-  float* smm;              // [BH, nS, 2] min and max finite group score of each chunk
+  float* smm;              // [BH, nSW, 2] min and max finite group score per score WG
   int32_t* sure;           // [BH, rcap] clusters above the cut bin (arrival order)
   float* tie_key;          // [BH, C] clusters in the cut bin (arrival order): score, id
   int32_t* tie_id;
@@ -77,9 +80,10 @@ struct DecodeArgs {
   int B, Hq, Hkv, G;
   int64_t L, L0, Lcap;
   int C, Cp, n_sink, n_recent, n_retrieve, rcap;
-  // per (b, kv-head): estimate chunks, steady chunks, select workgroups, retrieve
-  // workgroups, first-level merge groups, partial slots (estimate, steady, retrieve, merge)
-  int nS, nSt, nH, nB, nG, nP;
+  // per (b, kv-head): chunks of 128 clusters, score workgroups, estimate workgroups (one per
+  // chunk), steady workgroups, histogram / select workgroups, retrieve workgroups, their
+  // merge groups, partial slots (estimate, steady, retrieve, merge)
+  int nS, nSW, nEW, nSt, nH, nB, nG, nP;
   float scale, scale_log2;
 };
 
