@@ -18,7 +18,10 @@ WRITE_SIZE counters calibrate the HBM-traffic figures taken from rocprofv3 runs 
 script.
 
 Prints one JSON line. `value` is decode-attention tokens/s of the layer (batch / median time
-of one decode call); the index-build rate and achieved HBM bandwidth are extra fields.
+of one decode call); the index-build rate and achieved HBM bandwidth are extra fields. A
+long-context leg (default: the 1M-token layer) then builds that layer's index once and times
+16 decode calls the same way (`long_context`: call time, HBM bandwidth on the algorithmic
+bytes, build time).
 """
 from __future__ import annotations
 
@@ -48,6 +51,8 @@ def parse():
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-decode-steps", type=int, default=3)
+    ap.add_argument("--long-context", default="llama1m",
+                    help="also time decode calls at this workload's context ('none': skip)")
     return ap.parse_args()
 
 
@@ -77,27 +82,7 @@ def main():
     print(f"[bench] workload {w.name}: B={B} Hq={Hq} Hkv={H} L0={L0} S={w.segment_size} "
           f"C={C} T={T} n_r={nr} decode steps={nds}", file=sys.stderr, flush=True)
 
-    t = time.time()
-    x = synth.generate_layer(w)
-    print(f"[bench] generated inputs in {time.time() - t:.1f}s", file=sys.stderr, flush=True)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
-        torch.bfloat16).cuda()
-    k, v = dev(x.k), dev(x.v)
-    q = dev(x.q)                                              # [steps, B, Hq, d]
-    k_out, v_out = torch.zeros_like(k), torch.zeros_like(v)
-    k_out[:, :, L0:] = k[:, :, L0:]                           # decode-appended rows
-    v_out[:, :, L0:] = v[:, :, L0:]
-    bp = wi.wave_build_params(B, Hq, H, d, L0, w.capacity, w.segment_size,
-                              w.clusters_per_segment, T, w.n_sink, w.n_recent)
-    bws = torch.empty(wi.wave_index_workspace_size(bp), dtype=torch.uint8, device="cuda")
-    idx = wi.alloc_index(B, H, C, L0, optional=False)
-    scale = 1.0 / math.sqrt(d)
-    dps = [wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
-                                 w.n_recent, nr, scale) for s in range(nds)]
-    dws = wi.alloc_decode_workspace(dps[0])
-    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
-    lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
-    sel = torch.empty(nds, B, H, max(nr, 1), dtype=torch.int32, device="cuda")
+    x, k, v, q, k_out, v_out, bp, bws, idx, dps, dws, out, lse, sel = setup(w, nds)
     flush = None
     if not args.no_flush:
         flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")    # 512 MiB
@@ -176,25 +161,9 @@ def main():
     med = statistics.median
 
     # ---- algorithmic work (per decode call and per assignment launch)
-    csize = idx.cluster_size.cpu().numpy()
-    selh = sel.cpu().numpy()
-    e_tok, r_tok = [], []
-    for s in range(nds):
-        steady = w.n_sink + w.n_recent + s + 1
-        tot = rt = 0
-        for b in range(B):
-            for g in range(H):
-                ids = selh[s, b, g, :nr]
-                ids = ids[ids >= 0]
-                rt += int(csize[b, g, ids].sum())
-                tot += steady + int(csize[b, g, ids].sum())
-        e_tok.append(tot / (B * H))
-        r_tok.append(rt / (B * H))
-    E, Er = float(np.mean(e_tok)), float(np.mean(r_tok))
+    E, Er = exact_rows(w, idx, sel, nds)
     BH = B * H
-    # whole call: centroids + sizes, value sums of the unretrieved clusters, exact K/V rows,
-    # q in, out
-    call_bytes = (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d) * BH
+    call_bytes = decode_call_bytes(w, E)
     # score kernel: centroids and sizes in; every head's logit and the group score out; q
     score_bytes = (2 * C * d + 4 * C + 4 * C * G + 4 * C + 2 * G * d) * BH
     # histogram kernel: the group scores
@@ -278,10 +247,123 @@ def main():
         "roofline_by_kernel": roofs,
         "roofline_decode_call": roof_call,
     }
+    if args.long_context != "none":
+        del k, v, q, k_out, v_out, bws, idx, dws, flush, calib
+        torch.cuda.empty_cache()
+        res["long_context"] = long_context(args.long_context, 16, 2, not args.no_flush)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_decode_steps)
     print(json.dumps(res), flush=True)
 
+
+
+def setup(w, nds):
+    """Synthetic layer of workload w resident on the GPU, index and decode buffers."""
+    import numpy as np
+    import torch
+
+    import kv_vector_index_amd as wi
+    import synth
+
+    B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, 128
+    L0, C, nr = w.context, w.n_clusters, w.n_retrieve
+    t = time.time()
+    x = synth.generate_layer(w)
+    print(f"[bench] generated {w.name} inputs in {time.time() - t:.1f}s", file=sys.stderr,
+          flush=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    k, v = dev(x.k), dev(x.v)
+    q = dev(x.q)                                              # [steps, B, Hq, d]
+    k_out, v_out = torch.zeros_like(k), torch.zeros_like(v)
+    k_out[:, :, L0:] = k[:, :, L0:]                           # decode-appended rows
+    v_out[:, :, L0:] = v[:, :, L0:]
+    bp = wi.wave_build_params(B, Hq, H, d, L0, w.capacity, w.segment_size,
+                              w.clusters_per_segment, w.n_iters, w.n_sink, w.n_recent)
+    bws = torch.empty(wi.wave_index_workspace_size(bp), dtype=torch.uint8, device="cuda")
+    idx = wi.alloc_index(B, H, C, L0, optional=False)
+    scale = 1.0 / math.sqrt(d)
+    dps = [wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
+                                 w.n_recent, nr, scale) for s in range(nds)]
+    dws = wi.alloc_decode_workspace(dps[0])
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+    sel = torch.empty(nds, B, H, max(nr, 1), dtype=torch.int32, device="cuda")
+    return x, k, v, q, k_out, v_out, bp, bws, idx, dps, dws, out, lse, sel
+
+
+def exact_rows(w, idx, sel, nds):
+    """Mean exact rows (steady + retrieved tokens) and retrieved tokens per (b, kv-head)
+    over the decode calls, from the published selections and the cluster sizes."""
+    import numpy as np
+
+    B, H, nr = w.batch, w.n_kv_heads, w.n_retrieve
+    csize = idx.cluster_size.cpu().numpy()
+    selh = sel.cpu().numpy()
+    e_tok, r_tok = [], []
+    for s in range(nds):
+        steady = w.n_sink + w.n_recent + s + 1
+        tot = rt = 0
+        for b in range(B):
+            for g in range(H):
+                ids = selh[s, b, g, :nr]
+                ids = ids[ids >= 0]
+                rt += int(csize[b, g, ids].sum())
+                tot += steady + int(csize[b, g, ids].sum())
+        e_tok.append(tot / (B * H))
+        r_tok.append(rt / (B * H))
+    return float(np.mean(e_tok)), float(np.mean(r_tok))
+
+
+def decode_call_bytes(w, E):
+    """Algorithmic HBM bytes of one decode call: centroids and sizes, the value sums of the
+    unretrieved clusters, the exact K/V rows (E per (b, kv-head)), q in and out."""
+    C, nr, G, d = w.n_clusters, w.n_retrieve, w.group, 128
+    BH = w.batch * w.n_kv_heads
+    return (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d) * BH
+
+
+def long_context(name, n_calls, n_warm, use_flush):
+    """Decode at a long context: one build of the index, then n_calls timed decode calls
+    (HIP events around each call; cache flush before each, as in the main measurement)."""
+    import torch
+
+    import kv_vector_index_amd as wi
+    import synth
+
+    w = synth.WORKLOADS[name].with_(steps=n_warm + n_calls)
+    nds = n_warm + n_calls
+    x, k, v, q, k_out, v_out, bp, bws, idx, dps, dws, out, lse, sel = setup(w, nds)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda") if use_flush else None
+    ev = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
+    wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws)     # warm
+    be = ev()
+    be[0].record()
+    wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws)
+    be[1].record()
+    calls = [ev() for _ in range(nds)]
+    for s in range(nds):
+        if flush is not None:
+            flush.sum()
+        calls[s][0].record()
+        wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, out, lse, sel[s], dws)
+        calls[s][1].record()
+    torch.cuda.synchronize()
+    build_ms = be[0].elapsed_time(be[1])
+    call_ms = statistics.median(c[0].elapsed_time(c[1]) for c in calls[n_warm:])
+    E, Er = exact_rows(w, idx, sel, nds)
+    nbytes = decode_call_bytes(w, E)
+    gbs = nbytes / (call_ms * 1e-3) / 1e9
+    return {"workload": w.name, "batch": w.batch, "context": w.context,
+            "clusters": w.n_clusters, "n_retrieve": w.n_retrieve,
+            "steady": [w.n_sink, w.n_recent], "decode_calls": n_calls,
+            "decode_call_us": round(call_ms * 1e3, 2),
+            "decode_tok_s": round(w.batch / (call_ms * 1e-3), 1),
+            "decode_bytes_per_call": nbytes, "decode_hbm_GBps": round(gbs, 1),
+            "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "retrieved_tokens_per_kv_head": round(Er, 1),
+            "index_build_ms": round(build_ms, 3),
+            "index_build_tok_s": round(w.batch * w.context / (build_ms * 1e-3), 1)}
 
 def kernel_sources_hash() -> str:
     """Hash of the HIP sources: traffic figures are only valid for the kernels they measured."""
