@@ -90,9 +90,11 @@ def main():
     calib[1].copy_(calib[0])                                                 # calibration copy
 
     # start / end events of every kernel: build = norms, seeds, T x (assign, sort),
-    # (T - 1) x update, finalise, steady; decode = score, hist, gather, retrieve
+    # (T - 1) x update, finalise, steady; decode = score, [histogram: heads of more than 16384
+    # clusters], gather, retrieve
     n_build_ev = 2 * (3 * T + 3)
     n_dec_ev = 8
+    dec_recorded = []
     def events(n):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for e in ev:
@@ -113,9 +115,11 @@ def main():
                 flush.sum()
             if timed:
                 timed[1][s][0].record()
-            wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, out, lse, sel[s], dws,
-                                     events=None if dev_ is None else
-                                     [e.cuda_event for e in dev_[s]])
+            n_ev = wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, out, lse, sel[s], dws,
+                                            events=None if dev_ is None else
+                                            [e.cuda_event for e in dev_[s]])
+            if dev_ is not None:
+                dec_recorded.append(n_ev)
             if timed:
                 timed[1][s][1].record()
 
@@ -154,10 +158,12 @@ def main():
             update_ms.append(kd(bev, i))
             i += 1
     fin_ms.append(kd(bev, i))
+    has_hist = dec_recorded[0] == 8
+    assert all(n == dec_recorded[0] for n in dec_recorded) and dec_recorded[0] in (6, 8)
     score_ms = [kd(e, 0) for e in dev_]
-    hist_ms = [kd(e, 1) for e in dev_]
-    gather_ms = [kd(e, 2) for e in dev_]
-    retrieve_ms = [kd(e, 3) for e in dev_]
+    hist_ms = [kd(e, 1) for e in dev_] if has_hist else []
+    gather_ms = [kd(e, 1 + has_hist) for e in dev_]
+    retrieve_ms = [kd(e, 2 + has_hist) for e in dev_]
     med = statistics.median
 
     # ---- algorithmic work (per decode call and per assignment launch)
@@ -166,9 +172,10 @@ def main():
     call_bytes = decode_call_bytes(w, E)
     # score kernel: centroids and sizes in; every head's logit and the group score out; q
     score_bytes = (2 * C * d + 4 * C + 4 * C * G + 4 * C + 2 * G * d) * BH
-    # histogram kernel: the group scores
+    # histogram kernel (large heads): the group scores
     hist_bytes = 4 * C * BH
-    # gather kernel: the group scores (selection) and the published list; every cluster's
+    # gather kernel: the group scores (selection: each selection workgroup reads its own share;
+    # the histogram's re-reads of the head's scores hit L2) and the published list; every cluster's
     # value sum, size and logits (estimate); the steady rows; q
     steady_mean = w.n_sink + w.n_recent + (nds + 1) / 2
     gather_bytes = (4 * C + 8 * nr + 12 * nr + 2 * C * d + 4 * C + 4 * C * G
@@ -202,12 +209,13 @@ def main():
     roofs = {
         "k_assign": roof("k_assign", "mfma", assign_flop, assign_ms),
         "k_dec_score": roof("k_dec_score", "hbm", score_bytes, score_ms),
-        "k_dec_hist": roof("k_dec_hist", "hbm", hist_bytes, hist_ms),
+        **({"k_dec_hist": roof("k_dec_hist", "hbm", hist_bytes, hist_ms)} if has_hist else {}),
         "k_dec_gather": roof("k_dec_gather", "hbm", gather_bytes, gather_ms),
         "k_dec_retrieve": roof("k_dec_retrieve", "hbm", retrieve_bytes, retrieve_ms),
     }
     per_step = {"k_assign": T * mean(assign_ms), "k_dec_score": nds * mean(score_ms),
-                "k_dec_hist": nds * mean(hist_ms), "k_dec_gather": nds * mean(gather_ms),
+                **({"k_dec_hist": nds * mean(hist_ms)} if has_hist else {}),
+                "k_dec_gather": nds * mean(gather_ms),
                 "k_dec_retrieve": nds * mean(retrieve_ms)}
     dominant = max(per_step, key=per_step.get)
     roof_call = roof("decode call", "hbm", call_bytes, call_ms,
@@ -238,7 +246,8 @@ def main():
                       "finalise": round(statistics.mean(fin_ms) * 1e3, 2),
                       "decode_call": round(med(call_ms) * 1e3, 2),
                       "dec_score": round(statistics.mean(score_ms) * 1e3, 2),
-                      "dec_hist": round(statistics.mean(hist_ms) * 1e3, 2),
+                      **({"dec_hist": round(statistics.mean(hist_ms) * 1e3, 2)}
+                         if has_hist else {}),
                       "dec_gather": round(statistics.mean(gather_ms) * 1e3, 2),
                       "dec_retrieve": round(statistics.mean(retrieve_ms) * 1e3, 2)},
         "dominant_kernel": dominant,

@@ -158,8 +158,8 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   return WAVE_OK;
 }
 
-// Decode workspace (no preparation needed: the score kernel clears the histogram and the
-// counters in every call). Returns the total size.
+// Decode workspace (no preparation needed: the score kernel clears the counters in every
+// call). Returns the total size.
 size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* base,
                      wave::DecodeArgs* a) {
   Carver cv(base);
@@ -168,8 +168,8 @@ size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* b
   const size_t nP = (size_t)sh.nEW + sh.nStMax + sh.nB + sh.nG;
   const size_t nPmax = nP > (size_t)sh.nBDense ? nP : (size_t)sh.nBDense;
   uint32_t* counter = cv.take<uint32_t>(BH * wave::kCtrStride);
-  uint32_t* hist = cv.take<uint32_t>(BH * wave::kHistBins);
   float* smm = cv.take<float>(BH * (size_t)sh.nSW * 2);
+  uint32_t* hist = cv.take<uint32_t>(BH * wave::kHistBins);
   int32_t* sure = cv.take<int32_t>(BH * (size_t)sh.rcap);
   float* tie_key = cv.take<float>(BH * C);
   int32_t* tie_id = cv.take<int32_t>(BH * C);
@@ -183,8 +183,8 @@ size_t layout_decode(const wave_decode_params* p, const DecodeShape& sh, void* b
   float* part = cv.take<float>(BH * nPmax * G * wave::kPartStride);
   if (a) {
     a->counter = counter;
-    a->hist = hist;
     a->smm = smm;
+    a->hist = hist;
     a->sure = sure;
     a->tie_key = tie_key;
     a->tie_id = tie_id;
@@ -384,6 +384,7 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   a.nSW = sh.nSW;
   a.nEW = sh.nEW;
   a.nH = sh.nH;
+  a.hist_kernel = sh.nS * wave::kChunk > wave::kFusedHistMax ? 1 : 0;
   a.nB = sh.nB;
   a.nG = sh.nG;
   a.nP = a.nEW + a.nSt + a.nB + a.nG;

@@ -480,7 +480,7 @@ __device__ __forceinline__ Share chunk_share(int nS, int nw, int w) {
 // centroid rows and sizes are streamed once; every query head's log2-domain logit goes to
 // scores[], the group mean (natural units) to shat[] (-inf for empty and padding clusters),
 // and the workgroup's finite min / max to smm[]. Workgroup 0 of each (b, kv-head) also
-// clears its histogram and counters.
+// clears its counters (and its histogram, for the histogram kernel).
 template <int G>
 __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
   constexpr int R = Rows<G>::R;
@@ -489,9 +489,11 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, cc = lane & 15;
   if (blockIdx.x == 0) {
-    uint32_t* h = a.hist + (size_t)bh * kHistBins;
-    for (int i = tid; i < kHistBins; i += kDecThreads) h[i] = 0u;
     if (tid < kCtrStride) a.counter[(size_t)bh * kCtrStride + tid] = 0u;
+    if (a.hist_kernel) {
+      uint32_t* h = a.hist + (size_t)bh * kHistBins;
+      for (int i = tid; i < kHistBins; i += kDecThreads) h[i] = 0u;
+    }
   }
   u32x4 q[G];
   load_q<G>(a, b, g, cc, q);
@@ -565,10 +567,10 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// kernel 2: histogram of the group scores
+// the head's score range, from the score workgroups' min / max pairs
 // ------------------------------------------------------------------------------------
-// Value-range bins over [min, max] of the head's finite group scores (from the score
-// workgroups' pairs); the same (lo, hi) and bins are recomputed by the gather kernel.
+// Value-range bins over [min, max] of the head's finite group scores; every selection
+// workgroup of the head recomputes the same (lo, hi) and bins.
 __device__ __forceinline__ Red3 score_range(const DecodeArgs& a, int bh, float (*red)[3]) {
   const float* mm = a.smm + (size_t)bh * a.nSW * 2;
   Red3 r{kPosInf, kNegInf, 0u};
@@ -579,7 +581,8 @@ __device__ __forceinline__ Red3 score_range(const DecodeArgs& a, int bh, float (
   return block_red3<kDecThreads>(r, red);
 }
 
-// nH workgroups per (b, kv-head), kSelSpan scores each, add their histogram into hist[].
+// Histogram kernel (heads of more than kFusedHistMax clusters): nH workgroups per (b,
+// kv-head), kSelSpan scores each, add their histogram into hist[].
 __global__ __launch_bounds__(kDecThreads) void k_dec_hist(DecodeArgs a) {
   constexpr int NT = kDecThreads;
   __shared__ uint32_t hs[kHistBins];
@@ -613,6 +616,7 @@ struct FinShared {
   union {
     uint32_t bits[kMaxClusters / 32];  // selection bitmap over cluster ids
     uint32_t hist[kNarrowBins];        // histogram of a crowded cut bin
+    uint32_t full[kHistBins];          // histogram of all the head's scores
   } u;
   float ck[kCand];
   int32_t ci[kCand];
@@ -626,8 +630,10 @@ struct FinShared {
 };
 
 // The cut of a (b, kv-head): need = min(n_r, finite scores) and the histogram bin b* that
-// holds the need-th largest score (b* = kHistBins when need = 0), from the complete
-// histogram; every workgroup that calls this computes the same values.
+// holds the need-th largest score (b* = kHistBins when need = 0). The histogram of all the
+// head's scores comes from the histogram kernel for large heads; for heads of at most
+// kFusedHistMax clusters every selection workgroup builds it in LDS (the scores were just
+// written and sit in L2). Every selection workgroup of the head computes the same values.
 struct Cut {
   float lo, hi;
   int bstar;
@@ -637,18 +643,31 @@ __device__ Cut find_cut(const DecodeArgs& a, int bh, FinShared& sh) {
   constexpr int NT = kDecThreads, BPT = kHistBins / NT;
   const int tid = threadIdx.x;
   const Red3 r = score_range(a, bh, sh.red);
-  const uint32_t* gh = a.hist + (size_t)bh * kHistBins;
+  if (a.hist_kernel) {
+    const uint32_t* gh = a.hist + (size_t)bh * kHistBins;
+    for (int i = tid; i < kHistBins; i += NT) sh.u.full[i] = r.mx != kNegInf ? gh[i] : 0u;
+  } else {
+    for (int i = tid; i < kHistBins; i += NT) sh.u.full[i] = 0u;
+  }
+  __syncthreads();
+  if (!a.hist_kernel && r.mx != kNegInf) {
+    const Binner bn(r.mn, r.mx, true);
+    const float4* sh4 = reinterpret_cast<const float4*>(a.shat + (size_t)bh * a.Cp);
+    for (int i = tid; i < a.Cp / 4; i += NT) {
+      const float4 v = sh4[i];
+      if (v.x != kNegInf) atomicAdd(&sh.u.full[bn(v.x)], 1u);
+      if (v.y != kNegInf) atomicAdd(&sh.u.full[bn(v.y)], 1u);
+      if (v.z != kNegInf) atomicAdd(&sh.u.full[bn(v.z)], 1u);
+      if (v.w != kNegInf) atomicAdd(&sh.u.full[bn(v.w)], 1u);
+    }
+  }
+  __syncthreads();
   const int hb0 = kHistBins - BPT * (tid + 1);  // thread t's bins, visited from the top
   uint32_t hc[BPT], loc = 0;
-  if (r.mx != kNegInf) {
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      hc[i] = gh[hb0 + i];
-      loc += hc[i];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) hc[i] = 0u;
+  for (int i = 0; i < BPT; ++i) {
+    hc[i] = sh.u.full[hb0 + i];
+    loc += hc[i];
   }
   uint32_t ne;
   uint32_t run = scan_excl<NT>(loc, sh.tmp, &ne);
@@ -1242,8 +1261,10 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr
   const int BH = a.B * a.Hkv;
   hipError_t e = launch(tr, k_dec_score<G>, dim3(a.nSW, BH), dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
-  e = launch(tr, k_dec_hist, dim3(a.nH, BH), dim3(kDecThreads), 0, s, a);
-  if (e != hipSuccess) return e;
+  if (a.hist_kernel) {
+    e = launch(tr, k_dec_hist, dim3(a.nH, BH), dim3(kDecThreads), 0, s, a);
+    if (e != hipSuccess) return e;
+  }
   e = launch(tr, k_dec_gather<G>, dim3((a.nH + a.nEW + a.nSt) * BH), dim3(kDecThreads), 0, s,
              a);
   if (e != hipSuccess) return e;

@@ -25,8 +25,9 @@ constexpr int kDecThreads = 256;      // every decode workgroup: 4 waves
 constexpr int kChunk = 128;           // clusters per score / estimate workgroup (32 per wave)
 constexpr int kTokChunk = 128;        // steady tokens per steady workgroup
 constexpr int kPartStride = 132;      // floats per (partial, head): o[128], m, l, 2 pad
-constexpr int kSelSpan = 2048;        // group scores per histogram / gather workgroup
+constexpr int kSelSpan = 2048;        // group scores listed per selection workgroup
 constexpr int kHistBins = 4096;       // value-range histogram of the group scores
+constexpr int kFusedHistMax = 16384;  // larger heads get the histogram kernel
 constexpr int kNarrowBins = 1024;     // histogram of a crowded cut bin's scores
 constexpr int kCand = 256;            // scores ranked exactly in LDS
 constexpr int kMaxClusters = 65536;   // clusters per (b, kv-head) supported by the decode
@@ -63,8 +64,8 @@ struct DecodeArgs {
   int32_t* selected;       // [B, Hkv, n_retrieve] or null
   // workspace
   uint32_t* counter;       // [BH, kCtrStride]
-  uint32_t* hist;          // [BH, kHistBins] value-range histogram of the group scores
   float* smm;              // [BH, nSW, 2] min and max finite group score per score WG
+  uint32_t* hist;          // [BH, kHistBins] histogram of the group scores (large heads)
   int32_t* sure;           // [BH, rcap] clusters above the cut bin (arrival order)
   float* tie_key;          // [BH, C] clusters in the cut bin (arrival order): score, id
   int32_t* tie_id;
@@ -81,13 +82,15 @@ struct DecodeArgs {
   int64_t L, L0, Lcap;
   int C, Cp, n_sink, n_recent, n_retrieve, rcap;
   // per (b, kv-head): chunks of 128 clusters, score workgroups, estimate workgroups (one per
-  // chunk), steady workgroups, histogram / select workgroups, retrieve workgroups, their
+  // chunk), steady workgroups, selection workgroups, retrieve workgroups, their
   // merge groups, partial slots (estimate, steady, retrieve, merge)
   int nS, nSW, nEW, nSt, nH, nB, nG, nP;
   float scale, scale_log2;
+  int hist_kernel;         // 1: the histogram kernel runs (Cp > kFusedHistMax)
 };
 
-// Enqueue one tripartite decode step (score, histogram, gather, retrieve kernels). Returns
+// Enqueue one tripartite decode step (score, histogram for large heads, gather, retrieve
+// kernels). Returns
 // the first launch error.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
 // Enqueue dense decode over [0, L): split-K partials (part, nB per head) + merge.

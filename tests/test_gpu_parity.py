@@ -400,7 +400,7 @@ def test_traced_calls_time_each_kernel_and_match_the_plain_calls(tiny):
                                      dws, events=None if ev is None else [e.cuda_event for e in ev])
         t.cuda.synchronize()
         if traced:
-            assert n == 8
+            assert n == 6
             assert all(ev[2 * i].elapsed_time(ev[2 * i + 1]) > 0 for i in range(3))
         outs.append(out.cpu())
     assert t.equal(outs[0], outs[1])
