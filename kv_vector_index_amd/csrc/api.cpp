@@ -151,7 +151,10 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   // score / estimate workgroups: a few per CU over all (b, kv-heads), looping over chunks
   sh->nSW = clampi(wave::kScoreWGPerCall / bh, 1, sh->nS);
   sh->nEW = sh->nS;
-  sh->nG = (sh->nB + wave::kMergeGroup - 1) / wave::kMergeGroup;
+  // retrieve merge groups: one merge of all partials for up to two groups' worth, else
+  // groups of about kMergeGroup and a second level
+  sh->nG = sh->nB <= 2 * wave::kMergeGroup
+               ? 1 : (sh->nB + wave::kMergeGroup - 1) / wave::kMergeGroup;
   sh->nH = (int)((sh->nS * (int64_t)wave::kChunk + wave::kSelSpan - 1) / wave::kSelSpan);
   sh->nBDense = clampi((p->kv_capacity + 1023) / 1024, 1, 512);
   sh->rcap = p->n_retrieve > 0 ? p->n_retrieve : 1;

@@ -9,21 +9,24 @@
 // sums V_j, one query head's output is
 //     out = (sum_E e^{a_i} v_i + sum_U e^{s_j} V_j) / (sum_E e^{a_i} + sum_U n_j e^{s_j}).
 //
-// MI355X design, three small kernels per call:
-//   stream    one workgroup per 128 clusters or 128 steady tokens of a (b, kv-head): stream
-//             the centroid rows, value-sum rows and sizes once (HBM-bound), store each query
-//             head's logit and the group-mean score, and fold the estimate of ALL non-empty
-//             clusters (or the exact steady tokens) into one partial softmax state.
-//   select    one 512-thread workgroup per (b, kv-head) finds the exact top-n_r clusters
-//             (ties to the lower id) from the group scores held in registers and publishes
-//             them in ascending id order, each with its first "virtual row" (see below) and
-//             first cache row, plus the first listed cluster of every retrieve workgroup.
+// MI355X design, three kernels per call (four for heads of more than kFusedHistMax clusters):
+//   score     a few workgroups per CU stream the centroid rows and sizes once (HBM-bound),
+//             store each query head's logit, the group-mean score and each workgroup's
+//             score range.
+//   [hist]    large heads only: a value-range histogram of the group scores.
+//   gather    selection workgroups find the exact top-n_r clusters (ties to the lower id)
+//             from a 4096-bin histogram over the head's score range and an exact rank of
+//             the cut bin, and the last of a head publishes them in ascending id order with
+//             each cluster's first "virtual row" (see below) and first cache row, and each
+//             retrieve workgroup's share; in the same launch, estimate workgroups fold the
+//             centroid term of ALL non-empty clusters (value sums streamed beside the
+//             selection) and steady workgroups attend to the sink and recent tokens.
 //   retrieve  nB workgroups per (b, kv-head) walk the virtual rows of the retrieved clusters:
 //             every token of a retrieved cluster (exact attention; a retrieved cluster is a
 //             contiguous run of cache rows in the index layout) and one row per cluster that
-//             removes the estimate term the stream kernel added. Each workgroup also folds a
-//             share of the stream partials; the last workgroup of a (b, kv-head) merges the
-//             retrieve partials by log-sum-exp into out / lse.
+//             removes the estimate term added above. Each workgroup also folds a share of the
+//             estimate and steady partials; partials are merged by log-sum-exp in one or two
+//             levels into out / lse.
 // Rows are read 16 lanes per 256-byte row (4 rows per wave instruction, fully coalesced) and
 // each K/V row is shared by the G query heads of its group.
 #include <float.h>
@@ -616,7 +619,7 @@ struct FinShared {
   union {
     uint32_t bits[kMaxClusters / 32];  // selection bitmap over cluster ids
     uint32_t hist[kNarrowBins];        // histogram of a crowded cut bin
-    uint32_t full[kHistBins];          // histogram of all the head's scores
+    uint32_t full[kHistBins + 1];      // histogram of all the head's scores (+ a spare bin)
   } u;
   float ck[kCand];
   int32_t ci[kCand];
@@ -647,18 +650,42 @@ __device__ Cut find_cut(const DecodeArgs& a, int bh, FinShared& sh) {
     const uint32_t* gh = a.hist + (size_t)bh * kHistBins;
     for (int i = tid; i < kHistBins; i += NT) sh.u.full[i] = r.mx != kNegInf ? gh[i] : 0u;
   } else {
-    for (int i = tid; i < kHistBins; i += NT) sh.u.full[i] = 0u;
+    for (int i = tid; i <= kHistBins; i += NT) sh.u.full[i] = 0u;
   }
   __syncthreads();
   if (!a.hist_kernel && r.mx != kNegInf) {
+    // (Cp <= kFusedHistMax: at most 16 float4 per thread, all loaded before any is binned)
+    constexpr int NV = kFusedHistMax / 4 / NT;
     const Binner bn(r.mn, r.mx, true);
     const float4* sh4 = reinterpret_cast<const float4*>(a.shat + (size_t)bh * a.Cp);
-    for (int i = tid; i < a.Cp / 4; i += NT) {
-      const float4 v = sh4[i];
-      if (v.x != kNegInf) atomicAdd(&sh.u.full[bn(v.x)], 1u);
-      if (v.y != kNegInf) atomicAdd(&sh.u.full[bn(v.y)], 1u);
-      if (v.z != kNegInf) atomicAdd(&sh.u.full[bn(v.z)], 1u);
-      if (v.w != kNegInf) atomicAdd(&sh.u.full[bn(v.w)], 1u);
+    float4 v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {  // (clamped, unconditional loads: issued together)
+      const int i = k * NT + tid;
+      v[k] = sh4[min(i, a.Cp / 4 - 1)];
+      if (i >= a.Cp / 4) v[k] = neg4();
+    }
+    // (no branch per score: -inf, i.e. empty and padding clusters, goes to the spare bin;
+    // the binning mode is the same for the whole head)
+    const int nk = (a.Cp / 4 + NT - 1) / NT;
+    auto add = [&](auto bin) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        if (k >= nk) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = e == 0 ? v[k].x : e == 1 ? v[k].y : e == 2 ? v[k].z : v[k].w;
+          atomicAdd(&sh.u.full[x != kNegInf ? bin(x) : kHistBins], 1u);
+        }
+      }
+    };
+    if (bn.by_value) {
+      add([&](float x) {
+        const float t = (x - bn.lo) * bn.inv;
+        return t >= (float)(kHistBins - 1) ? kHistBins - 1 : (int)t;
+      });
+    } else {
+      add([&](float x) { return bn(x); });
     }
   }
   __syncthreads();
@@ -868,6 +895,9 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
   int32_t* selo = a.selected ? a.selected + (size_t)bh * a.n_retrieve : nullptr;
   int32_t* lst = reinterpret_cast<int32_t*>(sh.u.bits);  // the first kListLds listed ids
   constexpr uint32_t kListLds = kMaxClusters / 32;
+  // the ids go to LDS here; to the published list with the rest of each cluster's entry
+  // below, except where the list is longer than the LDS copy (then all of it goes now)
+  const bool long_list = nsel > kListLds;
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
     uint32_t x = w[i];
@@ -875,25 +905,23 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
       const int j = (tid * WPT + i) * 32 + __builtin_ctz(x);
       x &= x - 1u;
       if (k < nsel) {
-        sid[k] = j;
-        if (selo) selo[k] = j;
         if (k < kListLds) lst[k] = j;
+        if (long_list) sid[k] = j;
       }
       ++k;
     }
   }
-  if (selo)
-    for (int i = (int)nsel + tid; i < a.n_retrieve; i += NT) selo[i] = -1;
   __syncthreads();
   // sizes and first rows: thread t takes ranks [t * per, (t + 1) * per), loads first
   auto listed = [&](uint32_t r) { return r < kListLds ? lst[r] : sid[r]; };
   const uint32_t per = (nsel + NT - 1) / NT, r0 = tid * per, r1 = min(nsel, r0 + per);
-  int32_t sz4[4], co4[4];
+  int32_t sz4[4], co4[4], id4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sz4[i] = co4[i] = 0;
+    sz4[i] = co4[i] = id4[i] = 0;
     if (r0 + i < r1) {
       const int j = listed(r0 + i);
+      id4[i] = j;
       sz4[i] = a.csize[cb + j];
       co4[i] = a.coff[cb + j];
     }
@@ -905,8 +933,10 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
   uint32_t V;
   uint32_t pos = scan_excl<NT>(tok, sh.tmp, &V);
   const int nB = a.nB;
-  auto emit = [&](uint32_t r, int32_t n, int32_t co) {
+  auto emit = [&](uint32_t r, int j, int32_t n, int32_t co) {
     const uint32_t te = pos + (uint32_t)n + 1u;
+    if (!long_list) sid[r] = j;
+    if (selo) selo[r] = j;
     sts[r] = (int32_t)pos;
     sco[r] = co;
     // retrieve workgroups whose first virtual row falls in [pos, te)
@@ -917,11 +947,13 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
   };
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    if (r0 + i < r1) emit(r0 + i, sz4[i], co4[i]);
+    if (r0 + i < r1) emit(r0 + i, id4[i], sz4[i], co4[i]);
   for (uint32_t r = r0 + 4; r < r1; ++r) {
     const int j = listed(r);
-    emit(r, a.csize[cb + j], a.coff[cb + j]);
+    emit(r, j, a.csize[cb + j], a.coff[cb + j]);
   }
+  if (selo)
+    for (int i = (int)nsel + tid; i < a.n_retrieve; i += NT) selo[i] = -1;
   if (tid == 0) {
     a.sel_n[bh] = (int32_t)nsel;
     sts[nsel] = (int32_t)V;
@@ -1020,6 +1052,9 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gather(DecodeArgs a) {
     write_block_partial<G>(st, nullptr, a.part + ((size_t)bh * a.nP + slot) * G * kPartStride);
     return;
   }
+  // the selection is the latency-critical chain of the call: its waves issue ahead of the
+  // estimate and steady waves that share their SIMDs
+  __builtin_amdgcn_s_setprio(3);
   __shared__ FinShared sh;
   const Cut cut = find_cut(a, bh, sh);
   uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
@@ -1144,8 +1179,9 @@ __device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, cons
 }
 
 // nB workgroups per (b, kv-head): each takes a share of the estimate and steady partials
-// and its virtual rows, and writes one partial. The last of every kMergeGroup workgroups
-// merges their partials; the last of those merges writes out / lse.
+// and its virtual rows, and writes one partial. The last of each of the nG merge groups
+// merges its partials (nG = 1: straight into out / lse); the last of those merges writes
+// out / lse.
 template <int G>
 __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   __shared__ float s_x[G][kPartStride];  // this workgroup's share of the earlier partials
@@ -1192,7 +1228,8 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   }
   write_block_partial<G>(st, &s_x[0][0], parts + (size_t)(nSP + w_item) * G * kPartStride);
   uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
-  const int grp = w_item / kMergeGroup, g0 = grp * kMergeGroup, gn = min(kMergeGroup, nB - g0);
+  const int gsz = (nB + a.nG - 1) / a.nG;  // retrieve partials per merge group
+  const int grp = w_item / gsz, g0 = grp * gsz, gn = min(gsz, nB - g0);
   if (!arrive_last(ctr + kCtrGroup + grp, (uint32_t)gn)) return;
   const int bq = b * a.Hq + g * G;
   const bool single = a.nG == 1;
