@@ -478,19 +478,22 @@ __device__ __forceinline__ Share chunk_share(int nS, int nw, int w) {
   return {k0 * kChunk, k1 * kChunk};
 }
 
-// nSW workgroups per (b, kv-head), each over a share of the clusters in steps of 16R rows
-// (4R per wave), the rows of the next step loaded while the current step is scored. The
-// centroid rows and sizes are streamed once; every query head's log2-domain logit goes to
-// scores[], the group mean (natural units) to shat[] (-inf for empty and padding clusters),
-// and the workgroup's finite min / max to smm[]. Workgroup 0 of each (b, kv-head) also
-// clears its counters (and its histogram, for the histogram kernel).
+// nSW workgroups per (b, kv-head), each over a share of the clusters in steps of 128 (32 per
+// wave), the centroids of the next step loaded while the current step is scored. The logits
+// of the G heads are a dense product [16 x 128] . [128 x 16] per 16 clusters on
+// v_mfma_f32_16x16x32_bf16 (A: the group's query rows, zero beyond G; B: 16 centroids, four
+// lanes of 16 bytes per 64 bytes of a row; D: lane l < 16 holds heads 0..3 of cluster l,
+// lane 16 + l heads 4..7). Every query head's log2-domain logit goes to scores[], the group
+// mean (natural units) to shat[] (-inf for empty and padding clusters), and the
+// workgroup's finite min / max to smm[]. Workgroup 0 of each (b, kv-head) also clears its
+// counters (and its histogram, for the histogram kernel).
 template <int G>
 __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
-  constexpr int R = Rows<G>::R;
+  typedef __attribute__((ext_vector_type(4))) float floatx4;
   __shared__ float s_mm[kDecThreads / 64][2];
   const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = lane >> 4, cc = lane & 15;
+  const int col = lane & 15, kg = lane >> 4;  // MFMA column (cluster) and k group
   if (blockIdx.x == 0) {
     if (tid < kCtrStride) a.counter[(size_t)bh * kCtrStride + tid] = 0u;
     if (a.hist_kernel) {
@@ -498,62 +501,77 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
       for (int i = tid; i < kHistBins; i += kDecThreads) h[i] = 0u;
     }
   }
-  u32x4 q[G];
-  load_q<G>(a, b, g, cc, q);
+  // A operand: query head `col` (zero beyond G), dims 32 s + 8 kg .. + 7 for k step s
+  bf16x8 qa[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    u32x4 v = {0, 0, 0, 0};
+    if (col < G)
+      v = ld16(a.q + ((size_t)(b * a.Hq + g * G + col) * kHeadDim + st * 32 + kg * 8));
+    qa[st] = __builtin_bit_cast(bf16x8, v);
+  }
   const size_t base = (size_t)bh * a.C;
   float* shat = a.shat + (size_t)bh * a.Cp;
   const float sl2 = a.scale_log2, gmean = a.scale / (float)G;
   const Share sh = chunk_share(a.nS, a.nSW, blockIdx.x);
-  // (unconditional loads, masked afterwards: straight-line loads let the compiler wait for
-  // exactly the step in use while the next one is in flight; rows past the share re-read
-  // its last row, already cached)
+  // B operands of the wave's 32 clusters of a step (two groups of 16): row t + 16 u + col,
+  // dims 32 s + 8 kg; unconditional loads from a clamped row (rows past the share re-read
+  // its last row, already cached), so the compiler waits for exactly the step in use
   const int jmax = min(a.C, sh.c1) - 1;
-  auto load = [&](int t, u32x4 (&kr)[R], int32_t (&n)[R]) {
+  auto load = [&](int t, u32x4 (&kb)[2][4]) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int j = t + 4 * i + grp;
-      const size_t jc = base + min(j, jmax);
-      kr[i] = ld16_stream(a.cmean + jc * kHeadDim + cc * 8);
-      n[i] = __builtin_nontemporal_load(a.csize + jc);
-      if (j >= a.C || t >= sh.c1) n[i] = -1;
+    for (int u = 0; u < 2; ++u) {
+      const size_t row = base + min(t + 16 * u + col, jmax);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        kb[u][st] = ld16_stream(a.cmean + row * kHeadDim + st * 32 + kg * 8);
     }
   };
   float mn = kPosInf, mx = kNegInf;
-  u32x4 kr[R];
-  int32_t n[R];
-  int t = sh.c0 + wave * 4 * R;  // this wave's first row of each step
-  load(t, kr, n);
-  for (; t < sh.c1; t += 16 * R) {
-    u32x4 kn[R];
-    int32_t nn[R];
-    load(t + 16 * R, kn, nn);
-    float s[R][G];
-    row_logits<G, R>(q, kr, 1.f, s);
+  u32x4 kb[2][4];
+  int t = sh.c0 + wave * 32;  // this wave's first cluster of each step
+  load(t, kb);
+  for (; t < sh.c1; t += 128) {
+    u32x4 kn[2][4];
+    load(t + 128, kn);
+    int32_t n[2] = {-1, -1};
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int j = t + 4 * i + grp;
+    for (int u = 0; u < 2; ++u) {
+      const int j = t + 16 * u + col;
+      if (kg == 0 && j < a.C) n[u] = __builtin_nontemporal_load(a.csize + base + j);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      floatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], __builtin_bit_cast(bf16x8, kb[u][st]),
+                                                    d, 0, 0, 0);
+      // lane kg * 16 + col: heads 4 kg + i of cluster t + 16 u + col
+      const int j = t + 16 * u + col;
       float sum = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) sum += s[i][h];
-      const float mean = sum * gmean;
-      const bool ok = n[i] > 0;
-      if (ok) {
-        mn = fminf(mn, mean);
-        mx = fmaxf(mx, mean);
-      }
-      if (cc == 0) shat[j] = ok ? mean : kNegInf;
-      if (n[i] >= 0 && cc < G) {
-        float mine = s[i][0];
+      for (int i = 0; i < 4; ++i) sum += (4 * kg + i < G) ? d[i] : 0.f;
+      if (G > 4) sum += __shfl_xor(sum, 16);  // heads 4..7 from lane col + 16
+      if (j < a.C && kg < (G + 3) / 4) {
 #pragma unroll
-        for (int h = 1; h < G; ++h) mine = (cc == h) ? s[i][h] : mine;
-        a.scores[(base + j) * G + cc] = mine * sl2;
+        for (int i = 0; i < 4; ++i)
+          if (4 * kg + i < G) a.scores[(base + j) * G + 4 * kg + i] = d[i] * sl2;
+      }
+      if (kg == 0) {
+        const float mean = sum * gmean;
+        const bool ok = n[u] > 0;
+        if (ok) {
+          mn = fminf(mn, mean);
+          mx = fmaxf(mx, mean);
+        }
+        shat[j] = ok ? mean : kNegInf;
       }
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      kr[i] = kn[i];
-      n[i] = nn[i];
-    }
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) kb[u][st] = kn[u][st];
   }
   mn = wave_reduce(mn, [](float x, float y) { return fminf(x, y); });
   mx = wave_reduce(mx, [](float x, float y) { return fmaxf(x, y); });
@@ -1118,50 +1136,58 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gather(DecodeArgs a) {
 
 // Exact attention and estimate removal over the virtual rows [wb, we) of the listed
 // clusters [r_lo, r_hi) (LDS lists: first virtual row ts[] with ts[r_hi] = end, first cache
-// row co[], cluster id id[]). A removal row carries weight -n_j (wt < 0); its stored logits
-// travel in the registers of its (unused) key row, and in kx for heads 4..7.
+// row co[], cluster id id[]). A removal row carries weight -n_j (wt < 0) and the cluster's
+// stored logits.
 template <int G>
 __device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, const u32x4 (&q)[G],
                                                Online<G>& st, int wb, int we, const int32_t* ts,
                                                const int32_t* co, const int32_t* id, int r_lo,
                                                int r_hi) {
   constexpr int R = Rows<G>::R / 2;  // (register budget: four retrieve workgroups per CU)
-  constexpr int GX = G > 4 ? G - 4 : 1;
   const int lane = threadIdx.x & 63, grp = lane >> 4, cc = lane & 15;
   const size_t kb = (size_t)bh * a.Lcap, cb = (size_t)bh * a.C;
+  // the listed cluster holding this lane's current virtual row: found once by bisection,
+  // then advanced (a lane's rows only increase, and clusters span about 17 rows)
+  int cur = r_lo;
+  {
+    const int t0 = min(wb + grp, we - 1);
+    int hi = r_hi - 1;
+    while (cur < hi) {
+      const int mid = (cur + hi + 1) >> 1;
+      if (ts[mid] <= t0) cur = mid; else hi = mid - 1;
+    }
+  }
+  // every row issues the same loads (no branch, so the R rows' loads are in flight
+  // together): a key row (a token row; for a removal row with G = 4, its cluster's four
+  // logits in the same 16 bytes, else the cluster's first row), a value row (the token's,
+  // or the cluster's value sum) and, for G != 4, the cluster's logits
+  constexpr bool kPacked = G == 4;
+  constexpr int GS = kPacked ? 1 : G;
   for (int t = wb; t < we; t += 4 * R) {
     u32x4 kr[R], vr[R];
-    float wt[R], kx[R][GX];
+    float wt[R], sc[R][GS];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int tt = t + 4 * i + grp;
-      kr[i] = vr[i] = u32x4{0, 0, 0, 0};
-      wt[i] = 0.f;
+      const bool valid = tt < we;
+      if (valid)
+        while (cur + 1 < r_hi && ts[cur + 1] <= tt) ++cur;
+      const int lo = cur;
+      const int off = tt - ts[lo], n = ts[lo + 1] - ts[lo] - 1;
+      const bool token = valid && off < n;
+      const size_t krow = (kb + co[lo] + (token ? off : 0)) * kHeadDim + cc * 8;
+      const size_t j = cb + id[lo];
+      const float* sp = a.scores + j * G;
+      if constexpr (kPacked) {
+        kr[i] = ld16_stream(token ? static_cast<const void*>(a.k + krow)
+                                  : static_cast<const void*>(sp));
+      } else {
+        kr[i] = ld16_stream(a.k + krow);
 #pragma unroll
-      for (int h = 0; h < GX; ++h) kx[i][h] = 0.f;
-      if (tt < we) {
-        int lo = r_lo, hi = r_hi - 1;  // the listed cluster holding virtual row tt
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (ts[mid] <= tt) lo = mid; else hi = mid - 1;
-        }
-        const int off = tt - ts[lo], n = ts[lo + 1] - ts[lo] - 1;
-        if (off < n) {
-          const size_t row = (kb + co[lo] + off) * kHeadDim + cc * 8;
-          kr[i] = ld16_stream(a.k + row);
-          vr[i] = ld16_stream(a.v + row);
-          wt[i] = 1.f;
-        } else {
-          const size_t j = cb + id[lo];
-          vr[i] = ld16(a.vsum + j * kHeadDim + cc * 8);
-          const float* sp = a.scores + j * G;
-#pragma unroll
-          for (int h = 0; h < G && h < 4; ++h) kr[i][h] = __float_as_uint(sp[h]);
-#pragma unroll
-          for (int h = 4; h < G; ++h) kx[i][h - 4] = sp[h];
-          wt[i] = -(float)n;
-        }
+        for (int h = 0; h < GS; ++h) sc[i][h] = sp[h];
       }
+      vr[i] = ld16_stream(token ? a.v + krow : a.vsum + j * kHeadDim + cc * 8);
+      wt[i] = token ? 1.f : (valid ? -(float)n : 0.f);
     }
     float s[R][G], sg[R];
     row_logits<G, R>(q, kr, a.scale_log2, s);
@@ -1170,7 +1196,7 @@ __device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, cons
       sg[i] = wt[i] < 0.f ? -1.f : 1.f;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float rs = h < 4 ? __uint_as_float(kr[i][h < 4 ? h : 0]) : kx[i][h < 4 ? 0 : h - 4];
+        const float rs = kPacked ? __uint_as_float(kr[i][h & 3]) : sc[i][kPacked ? 0 : h];
         s[i][h] = wt[i] < 0.f ? rs : (wt[i] == 0.f ? kNegInf : s[i][h]);
       }
     }
@@ -1236,7 +1262,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   float* gp = parts + (size_t)(nSP + nB + grp) * G * kPartStride;
   for (int idx = tid; idx < G * 128; idx += kDecThreads) {
     float M, Ls, O;
-    merge_partials<true, 8>(parts, G, idx, nSP + g0, 1, nSP + g0 + gn, M, Ls, O);
+    merge_partials<true, 2 * kMergeGroup>(parts, G, idx, nSP + g0, 1, nSP + g0 + gn, M, Ls, O);
     const int h = idx >> 7, d = idx & 127;
     if (single) {
       a.out[(size_t)(bq + h) * kHeadDim + d] = O / Ls;
@@ -1252,7 +1278,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   if (single || !arrive_last(ctr + kCtrFinal, (uint32_t)a.nG)) return;
   for (int idx = tid; idx < G * 128; idx += kDecThreads) {
     float M, Ls, O;
-    merge_partials<true, 8>(parts, G, idx, nSP + nB, 1, nSP + nB + a.nG, M, Ls, O);
+    merge_partials<true, 2 * kMergeGroup>(parts, G, idx, nSP + nB, 1, nSP + nB + a.nG, M, Ls, O);
     const int h = idx >> 7, d = idx & 127;
     a.out[(size_t)(bq + h) * kHeadDim + d] = O / Ls;
     if (d == 0 && a.lse) a.lse[bq + h] = (M + log2f(Ls)) * kLn2;
