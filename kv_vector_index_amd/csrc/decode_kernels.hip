@@ -635,10 +635,14 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_hist(DecodeArgs a) {
 // ------------------------------------------------------------------------------------
 struct FinShared {
   union {
-    uint32_t bits[kMaxClusters / 32];  // selection bitmap over cluster ids
+    struct {
+      uint32_t bits[kMaxClusters / 32];  // selection bitmap over cluster ids
+      uint32_t nzw[kMaxClusters / 32];   // non-empty words: index | first rank << 11
+    };
     uint32_t hist[kNarrowBins];        // histogram of a crowded cut bin
     uint32_t full[kHistBins + 1];      // histogram of all the head's scores (+ a spare bin)
   } u;
+  int32_t lst[kMaxClusters / 32];      // the first kMaxClusters / 32 listed ids
   float ck[kCand];
   int32_t ci[kCand];
   int32_t wgr[kMaxRetrieveWG + 1];
@@ -895,38 +899,52 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
     }
   }
   __syncthreads();
-  // ordered compaction: thread t holds ids [t * 32 * WPT, (t + 1) * 32 * WPT), its ranks
-  // start at the exclusive scan of the counts (the list holds at most rcap clusters; the
-  // counts above make nsel = need <= rcap)
-  uint32_t w[WPT], c = 0;
+  // ordered compaction: thread t counts words [t * WPT, (t + 1) * WPT); exclusive scans of
+  // the counts give each word's first rank and each non-empty word's place in a compact
+  // list; then one lane per bit of the listed words (two words per wave instruction)
+  // writes its id at its rank, whatever the spread of the selected ids (the list holds at
+  // most rcap clusters; the counts above make nsel = need <= rcap)
+  uint32_t c = 0, nz = 0;
+  uint32_t wcnt[WPT];
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
-    w[i] = sh.u.bits[tid * WPT + i];
-    c += __popc(w[i]);
+    wcnt[i] = __popc(sh.u.bits[tid * WPT + i]);
+    c += wcnt[i];
+    nz += wcnt[i] != 0u ? 1u : 0u;
   }
-  uint32_t nsel;
-  uint32_t k = scan_excl<NT>(c, sh.tmp, &nsel);  // (its barriers also end the bitmap reads)
+  uint32_t nsel, nnz;
+  uint32_t k = scan_excl<NT>(c, sh.tmp, &nsel);
+  uint32_t z = scan_excl<NT>(nz, sh.tmp, &nnz);
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    if (wcnt[i]) sh.u.nzw[z++] = (uint32_t)(tid * WPT + i) | (k << 11);
+    k += wcnt[i];
+  }
   nsel = min(nsel, (uint32_t)a.rcap);
   int32_t* sid = a.sel_id + (size_t)bh * a.rcap;
   int32_t* sts = a.sel_ts + (size_t)bh * (a.rcap + 1);
   int32_t* sco = a.sel_coff + (size_t)bh * a.rcap;
   int32_t* selo = a.selected ? a.selected + (size_t)bh * a.n_retrieve : nullptr;
-  int32_t* lst = reinterpret_cast<int32_t*>(sh.u.bits);  // the first kListLds listed ids
+  int32_t* lst = sh.lst;
   constexpr uint32_t kListLds = kMaxClusters / 32;
   // the ids go to LDS here; to the published list with the rest of each cluster's entry
   // below, except where the list is longer than the LDS copy (then all of it goes now)
   const bool long_list = nsel > kListLds;
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    uint32_t x = w[i];
-    while (x) {
-      const int j = (tid * WPT + i) * 32 + __builtin_ctz(x);
-      x &= x - 1u;
-      if (k < nsel) {
-        if (k < kListLds) lst[k] = j;
-        if (long_list) sid[k] = j;
+  __syncthreads();
+  {
+    const int lane = tid & 63, wave = tid >> 6, bit = lane & 31;
+    for (int q = 2 * wave + (lane >> 5); q < (int)nnz; q += 2 * (NT / 64)) {
+      const uint32_t e = sh.u.nzw[q];
+      const int word = (int)(e & 2047u);
+      const uint32_t x = sh.u.bits[word];
+      if ((x >> bit) & 1u) {
+        const uint32_t r = (e >> 11) + __popc(x & ((1u << bit) - 1u));
+        const int j = word * 32 + bit;
+        if (r < nsel) {
+          if (r < kListLds) lst[r] = j;
+          if (long_list) sid[r] = j;
+        }
       }
-      ++k;
     }
   }
   __syncthreads();
