@@ -90,7 +90,7 @@ def main():
     calib[1].copy_(calib[0])                                                 # calibration copy
 
     # start / end events of every kernel: build = norms, seeds, T x (assign, sort),
-    # (T - 1) x update, finalise, steady; decode = score, [histogram: heads of more than 16384
+    # (T - 1) x update, finalise, steady; decode = score, [histogram: heads of more than 8192
     # clusters], gather, retrieve
     n_build_ev = 2 * (3 * T + 3)
     n_dec_ev = 8

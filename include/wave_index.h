@@ -175,7 +175,7 @@ wave_status wave_dense_decode_attention(const wave_decode_params* p, const void*
  * Kernel order, build: key norms (if any indexed token), seeds, then per pass: assign,
  * sort, and (all passes but the last) update; then finalise, steady-row copy (if
  * n_sink + n_recent > 0), objective (if requested). Decode: score, histogram (only when
- * n_clusters > 16384), gather, retrieve.
+ * n_clusters > 8192), gather, retrieve.
  * Dense decode: partial, merge.
  */
 typedef struct {

@@ -155,7 +155,10 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   // groups of about kMergeGroup and a second level
   sh->nG = sh->nB <= 2 * wave::kMergeGroup
                ? 1 : (sh->nB + wave::kMergeGroup - 1) / wave::kMergeGroup;
-  sh->nH = (int)((sh->nS * (int64_t)wave::kChunk + wave::kSelSpan - 1) / wave::kSelSpan);
+  // selection workgroups per (b, kv-head): one for heads of at most kLocalSelectMax clusters
+  // (it holds all of the head's scores), else one per kSelSpan scores
+  const int64_t cp = (int64_t)sh->nS * wave::kChunk;
+  sh->nH = cp <= wave::kLocalSelectMax ? 1 : (int)((cp + wave::kSelSpan - 1) / wave::kSelSpan);
   sh->nBDense = clampi((p->kv_capacity + 1023) / 1024, 1, 512);
   sh->rcap = p->n_retrieve > 0 ? p->n_retrieve : 1;
   return WAVE_OK;
@@ -387,7 +390,7 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   a.nSW = sh.nSW;
   a.nEW = sh.nEW;
   a.nH = sh.nH;
-  a.hist_kernel = sh.nS * wave::kChunk > wave::kFusedHistMax ? 1 : 0;
+  a.hist_kernel = sh.nS * wave::kChunk > wave::kLocalSelectMax ? 1 : 0;
   a.nB = sh.nB;
   a.nG = sh.nG;
   a.nP = a.nEW + a.nSt + a.nB + a.nG;

@@ -9,16 +9,20 @@
 // sums V_j, one query head's output is
 //     out = (sum_E e^{a_i} v_i + sum_U e^{s_j} V_j) / (sum_E e^{a_i} + sum_U n_j e^{s_j}).
 //
-// MI355X design, three kernels per call (four for heads of more than kFusedHistMax clusters):
+// MI355X design, three kernels per call (four for heads of more than kLocalSelectMax clusters):
 //   score     a few workgroups per CU stream the centroid rows and sizes once (HBM-bound),
 //             store each query head's logit, the group-mean score and each workgroup's
 //             score range.
 //   [hist]    large heads only: a value-range histogram of the group scores.
-//   gather    selection workgroups find the exact top-n_r clusters (ties to the lower id)
-//             from a 4096-bin histogram over the head's score range and an exact rank of
-//             the cut bin, and the last of a head publishes them in ascending id order with
-//             each cluster's first "virtual row" (see below) and first cache row, and each
-//             retrieve workgroup's share; in the same launch, estimate workgroups fold the
+//   gather    the selection finds the exact top-n_r clusters (ties to the lower id) from a
+//             4096-bin histogram over the head's score range and an exact rank of the cut
+//             bin: for heads of at most kLocalSelectMax clusters one workgroup does it all
+//             with the head's scores in registers; larger heads have one workgroup per
+//             2048 scores listing the clusters above and in the cut bin, and the last of a
+//             head ranks the cut bin. Either way the selection is published in ascending id
+//             order with each cluster's first "virtual row" (see below) and first cache
+//             row, and each retrieve workgroup's share; in the same launch, estimate
+//             workgroups fold the
 //             centroid term of ALL non-empty clusters (value sums streamed beside the
 //             selection) and steady workgroups attend to the sink and recent tokens.
 //   retrieve  nB workgroups per (b, kv-head) walk the virtual rows of the retrieved clusters:
@@ -314,16 +318,30 @@ struct ScanTmp {
   uint32_t w[NT / 64];
 };
 
+// Inclusive scan over the 64 lanes of a wave: four DPP row shifts (lanes shifted in from
+// outside the 16-lane row read 0) scan each row, then the three lower rows' totals are read
+// back as scalars and added to the rows above them.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+  auto shr = [](uint32_t v, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, decltype(ctrl)::value, 0xF, 0xF,
+                                                 true);
+  };
+  x += shr(x, std::integral_constant<int, 0x111>{});  // row_shr:1
+  x += shr(x, std::integral_constant<int, 0x112>{});  // row_shr:2
+  x += shr(x, std::integral_constant<int, 0x114>{});  // row_shr:4
+  x += shr(x, std::integral_constant<int, 0x118>{});  // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // exclusive scan over the block; *total = block sum
 template <int NT>
 __device__ __forceinline__ uint32_t scan_excl(uint32_t x, ScanTmp<NT>& tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t v = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
+  const uint32_t v = wave_scan_incl(x);
   if (lane == 63) tmp.w[wave] = v;
   __syncthreads();
   uint32_t before = 0, tot = 0;
@@ -397,11 +415,20 @@ __device__ __forceinline__ Red3 block_red3(Red3 r, float (*s)[3]) {
   return t;
 }
 
+// LDS histograms whose bins are scanned in runs of 2^SHIFT per thread keep one spare word
+// after every run, so that the threads of a wave read their runs from distinct banks.
+template <int SHIFT>
+__device__ __forceinline__ int padded(int bin) {
+  return bin + (bin >> SHIFT);
+}
+constexpr int kFullPad = 4;    // full histogram (kHistBins): runs of 16 bins
+constexpr int kNarrowPad = 2;  // narrowing histogram (kNarrowBins): runs of 4 bins
+
 // Histogram increment with the lanes of a wave that hit the same bin combined first (wave
 // ballots over the BITS bits of the bin give each lane its peers), so a bin receives at most
 // one LDS atomic per wave instead of one per lane. Lanes with active = false take part in
-// the ballots only.
-template <int BITS>
+// the ballots only. PAD: the histogram's padding shift (31: none).
+template <int BITS, int PAD = 31>
 __device__ __forceinline__ void hist_add(uint32_t* hist, int bin, bool active) {
   uint64_t peers = __ballot(active);
 #pragma unroll
@@ -411,7 +438,7 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, int bin, bool active) {
     peers &= bit ? m : ~m;
   }
   const uint64_t below = (1ull << (threadIdx.x & 63)) - 1ull;
-  if (active && (peers & below) == 0) atomicAdd(&hist[bin], (uint32_t)__popcll(peers));
+  if (active && (peers & below) == 0) atomicAdd(&hist[padded<PAD>(bin)], (uint32_t)__popcll(peers));
 }
 
 // Publish this block's device-coherent writes and count one more arrival on *counter;
@@ -602,7 +629,7 @@ __device__ __forceinline__ Red3 score_range(const DecodeArgs& a, int bh, float (
   return block_red3<kDecThreads>(r, red);
 }
 
-// Histogram kernel (heads of more than kFusedHistMax clusters): nH workgroups per (b,
+// Histogram kernel (heads of more than kLocalSelectMax clusters): nH workgroups per (b,
 // kv-head), kSelSpan scores each, add their histogram into hist[].
 __global__ __launch_bounds__(kDecThreads) void k_dec_hist(DecodeArgs a) {
   constexpr int NT = kDecThreads;
@@ -639,8 +666,9 @@ struct FinShared {
       uint32_t bits[kMaxClusters / 32];  // selection bitmap over cluster ids
       uint32_t nzw[kMaxClusters / 32];   // non-empty words: index | first rank << 11
     };
-    uint32_t hist[kNarrowBins];        // histogram of a crowded cut bin
-    uint32_t full[kHistBins + 1];      // histogram of all the head's scores (+ a spare bin)
+    uint32_t hist[kNarrowBins + kNarrowBins / 4];  // histogram of a crowded cut bin (padded)
+    uint32_t full[kHistBins + 1 + kHistBins / 16 + 1];  // all the head's scores (+ a spare
+                                                        // bin; padded)
   } u;
   int32_t lst[kMaxClusters / 32];      // the first kMaxClusters / 32 listed ids
   float ck[kCand];
@@ -654,68 +682,28 @@ struct FinShared {
   uint32_t base[2];
 };
 
-// The cut of a (b, kv-head): need = min(n_r, finite scores) and the histogram bin b* that
-// holds the need-th largest score (b* = kHistBins when need = 0). The histogram of all the
-// head's scores comes from the histogram kernel for large heads; for heads of at most
-// kFusedHistMax clusters every selection workgroup builds it in LDS (the scores were just
-// written and sit in L2). Every selection workgroup of the head computes the same values.
+// The cut of a (b, kv-head) of more than kLocalSelectMax clusters: need = min(n_r, finite
+// scores) and the histogram bin b* that holds the need-th largest score (b* = kHistBins when
+// need = 0), from the histogram kernel's histogram of all the head's scores. Every selection
+// workgroup of the head computes the same values.
 struct Cut {
   float lo, hi;
   int bstar;
   uint32_t need;
 };
-__device__ Cut find_cut(const DecodeArgs& a, int bh, FinShared& sh) {
+__device__ __forceinline__ Cut find_cut(const DecodeArgs& a, int bh, FinShared& sh) {
   constexpr int NT = kDecThreads, BPT = kHistBins / NT;
   const int tid = threadIdx.x;
   const Red3 r = score_range(a, bh, sh.red);
-  if (a.hist_kernel) {
-    const uint32_t* gh = a.hist + (size_t)bh * kHistBins;
-    for (int i = tid; i < kHistBins; i += NT) sh.u.full[i] = r.mx != kNegInf ? gh[i] : 0u;
-  } else {
-    for (int i = tid; i <= kHistBins; i += NT) sh.u.full[i] = 0u;
-  }
-  __syncthreads();
-  if (!a.hist_kernel && r.mx != kNegInf) {
-    // (Cp <= kFusedHistMax: at most 16 float4 per thread, all loaded before any is binned)
-    constexpr int NV = kFusedHistMax / 4 / NT;
-    const Binner bn(r.mn, r.mx, true);
-    const float4* sh4 = reinterpret_cast<const float4*>(a.shat + (size_t)bh * a.Cp);
-    float4 v[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {  // (clamped, unconditional loads: issued together)
-      const int i = k * NT + tid;
-      v[k] = sh4[min(i, a.Cp / 4 - 1)];
-      if (i >= a.Cp / 4) v[k] = neg4();
-    }
-    // (no branch per score: -inf, i.e. empty and padding clusters, goes to the spare bin;
-    // the binning mode is the same for the whole head)
-    const int nk = (a.Cp / 4 + NT - 1) / NT;
-    auto add = [&](auto bin) {
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        if (k >= nk) break;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = e == 0 ? v[k].x : e == 1 ? v[k].y : e == 2 ? v[k].z : v[k].w;
-          atomicAdd(&sh.u.full[x != kNegInf ? bin(x) : kHistBins], 1u);
-        }
-      }
-    };
-    if (bn.by_value) {
-      add([&](float x) {
-        const float t = (x - bn.lo) * bn.inv;
-        return t >= (float)(kHistBins - 1) ? kHistBins - 1 : (int)t;
-      });
-    } else {
-      add([&](float x) { return bn(x); });
-    }
-  }
+  const uint32_t* gh = a.hist + (size_t)bh * kHistBins;
+  for (int i = tid; i < kHistBins; i += NT)
+    sh.u.full[padded<kFullPad>(i)] = r.mx != kNegInf ? gh[i] : 0u;
   __syncthreads();
   const int hb0 = kHistBins - BPT * (tid + 1);  // thread t's bins, visited from the top
   uint32_t hc[BPT], loc = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    hc[i] = sh.u.full[hb0 + i];
+    hc[i] = sh.u.full[padded<kFullPad>(hb0 + i)];
     loc += hc[i];
   }
   uint32_t ne;
@@ -739,20 +727,15 @@ __device__ __forceinline__ void mark(FinShared& sh, int j) {
   atomicOr(&sh.u.bits[j >> 5], 1u << (j & 31));
 }
 
-// The need-th lowest id among the n listed clusters whose score equals v (need >= 1).
-__device__ int nth_id_with_score(const float* tk, const int32_t* ti, uint32_t n, float v,
-                                 uint32_t need, FinShared& sh) {
+// The id of the need-th set bit (need >= 1, at most the number of set bits) of the bitmap
+// words [0, nwords) of sh.u.bits, in every thread.
+__device__ __forceinline__ int nth_bit(FinShared& sh, int nwords, uint32_t need) {
   constexpr int NT = kDecThreads, WPT = kMaxClusters / 32 / NT;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kMaxClusters / 32; i += NT) sh.u.bits[i] = 0u;
-  __syncthreads();
-  for (uint32_t k = tid; k < n; k += NT)
-    if (ld_dev(tk + k) == v) mark(sh, ld_dev(ti + k));
-  __syncthreads();
   uint32_t w[WPT], c = 0;
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
-    w[i] = sh.u.bits[tid * WPT + i];
+    w[i] = tid * WPT + i < nwords ? sh.u.bits[tid * WPT + i] : 0u;
     c += __popc(w[i]);
   }
   uint32_t tot;
@@ -772,6 +755,17 @@ __device__ int nth_id_with_score(const float* tk, const int32_t* ti, uint32_t n,
   const int r = sh.tid;
   __syncthreads();
   return r;
+}
+
+// The need-th lowest id among the n listed clusters whose score equals v (need >= 1).
+__device__ int nth_id_with_score(const float* tk, const int32_t* ti, uint32_t n, float v,
+                                 uint32_t need, FinShared& sh) {
+  for (int i = threadIdx.x; i < kMaxClusters / 32; i += kDecThreads) sh.u.bits[i] = 0u;
+  __syncthreads();
+  for (uint32_t k = threadIdx.x; k < n; k += kDecThreads)
+    if (ld_dev(tk + k) == v) mark(sh, ld_dev(ti + k));
+  __syncthreads();
+  return nth_bit(sh, kMaxClusters / 32, need);
 }
 
 // (Tkey, Tid): the need-th pair (score descending, id ascending) among the n listed
@@ -799,20 +793,20 @@ __device__ void cut_pair(const float* tk, const int32_t* ti, uint32_t n, uint32_
     const Binner b4k(lo, hi, first);
     first = false;
     auto bin = [&](float v) { return b4k(v) / (kHistBins / kNarrowBins); };
-    for (int i = tid; i < kNarrowBins; i += NT) sh.u.hist[i] = 0u;
+    for (int i = tid; i < kNarrowBins + kNarrowBins / 4; i += NT) sh.u.hist[i] = 0u;
     __syncthreads();
     for (uint32_t k0 = 0; k0 < n; k0 += NT) {
       const uint32_t k = k0 + tid;
       const float v = k < n ? ld_dev(tk + k) : kNegInf;
       const bool in = k < n && v >= lo && v <= hi;
-      hist_add<10>(sh.u.hist, in ? bin(v) : 0, in);
+      hist_add<10, kNarrowPad>(sh.u.hist, in ? bin(v) : 0, in);
     }
     __syncthreads();
     const int hb0 = kNarrowBins - BPT * (tid + 1);
     uint32_t hc[BPT], loc = 0;
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
-      hc[i] = sh.u.hist[hb0 + i];
+      hc[i] = sh.u.hist[padded<kNarrowPad>(hb0 + i)];
       loc += hc[i];
     }
     uint32_t tot;
@@ -828,7 +822,7 @@ __device__ void cut_pair(const float* tk, const int32_t* ti, uint32_t n, uint32_
     if (tid == 0) sh.v[2] = 0u;
     __syncthreads();
     const int bstar = (int)sh.v[0];
-    const uint32_t need2 = need - sh.v[1], cnt = sh.u.hist[bstar];
+    const uint32_t need2 = need - sh.v[1], cnt = sh.u.hist[padded<kNarrowPad>(bstar)];
     if (cnt <= (uint32_t)kCand) {
       for (uint32_t k = tid; k < n; k += NT) {
         const float v = ld_dev(tk + k);
@@ -873,99 +867,97 @@ __device__ void cut_pair(const float* tk, const int32_t* ti, uint32_t n, uint32_
   }
 }
 
-// The last gather workgroup of a (b, kv-head): the exact cut among the clusters of the cut
-// bin, the selection bitmap, and from it the published list in ascending id order (ids,
-// first virtual row, first cache row), `selected`, and each retrieve workgroup's share.
-__device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinShared& sh) {
+// Publish the selection marked in the bitmap sh.u.bits (bits of clusters [0, C)) of a (b,
+// kv-head): the list in ascending id order (ids, first virtual row, first cache row),
+// `selected`, the list length, and each retrieve workgroup's virtual rows and listed
+// clusters. Every thread of the workgroup takes part.
+__device__ __forceinline__ void publish_selection(const DecodeArgs& a, int bh, FinShared& sh) {
   constexpr int NT = kDecThreads, WPT = kMaxClusters / 32 / NT;
   const int tid = threadIdx.x;
   const size_t cb = (size_t)bh * a.C;
-  const uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
-  const uint32_t nsure = min(ld_dev(ctr + kCtrSure), (uint32_t)a.rcap);
-  const uint32_t ntie = min(ld_dev(ctr + kCtrTie), (uint32_t)a.C);
-  const float* tk = a.tie_key + cb;
-  const int32_t* ti = a.tie_id + cb;
-  float Tkey = kNegInf;  // default: every listed cluster of the cut bin
-  int Tid = 0x7fffffff;
-  if (need > nsure && need - nsure < ntie) cut_pair(tk, ti, ntie, need - nsure, sh, Tkey, Tid);
-  for (int i = tid; i < kMaxClusters / 32; i += NT) sh.u.bits[i] = 0u;
-  __syncthreads();
-  if (need > 0) {
-    const int32_t* su = a.sure + (size_t)bh * a.rcap;
-    for (uint32_t k = tid; k < nsure; k += NT) mark(sh, ld_dev(su + k));
-    for (uint32_t k = tid; k < ntie; k += NT) {
-      const int j = ld_dev(ti + k);
-      if (is_selected(ld_dev(tk + k), j, Tkey, Tid)) mark(sh, j);
-    }
-  }
-  __syncthreads();
-  // ordered compaction: thread t counts words [t * WPT, (t + 1) * WPT); exclusive scans of
-  // the counts give each word's first rank and each non-empty word's place in a compact
-  // list; then one lane per bit of the listed words (two words per wave instruction)
-  // writes its id at its rank, whatever the spread of the selected ids (the list holds at
-  // most rcap clusters; the counts above make nsel = need <= rcap)
-  uint32_t c = 0, nz = 0;
-  uint32_t wcnt[WPT];
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    wcnt[i] = __popc(sh.u.bits[tid * WPT + i]);
-    c += wcnt[i];
-    nz += wcnt[i] != 0u ? 1u : 0u;
-  }
-  uint32_t nsel, nnz;
-  uint32_t k = scan_excl<NT>(c, sh.tmp, &nsel);
-  uint32_t z = scan_excl<NT>(nz, sh.tmp, &nnz);
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    if (wcnt[i]) sh.u.nzw[z++] = (uint32_t)(tid * WPT + i) | (k << 11);
-    k += wcnt[i];
-  }
-  nsel = min(nsel, (uint32_t)a.rcap);
+  const int nwords = (a.C + 31) / 32;
   int32_t* sid = a.sel_id + (size_t)bh * a.rcap;
   int32_t* sts = a.sel_ts + (size_t)bh * (a.rcap + 1);
   int32_t* sco = a.sel_coff + (size_t)bh * a.rcap;
   int32_t* selo = a.selected ? a.selected + (size_t)bh * a.n_retrieve : nullptr;
   int32_t* lst = sh.lst;
   constexpr uint32_t kListLds = kMaxClusters / 32;
-  // the ids go to LDS here; to the published list with the rest of each cluster's entry
-  // below, except where the list is longer than the LDS copy (then all of it goes now)
-  const bool long_list = nsel > kListLds;
-  __syncthreads();
-  {
-    const int lane = tid & 63, wave = tid >> 6, bit = lane & 31;
-    for (int q = 2 * wave + (lane >> 5); q < (int)nnz; q += 2 * (NT / 64)) {
+  // ordered compaction of the bitmap into ranks: the ids go to LDS here, and to the
+  // published list with the rest of each cluster's entry below, except where the list is
+  // longer than the LDS copy (then all of it goes now). The selection counts make
+  // nsel = need <= rcap.
+  uint32_t nsel;
+  bool long_list;
+  auto put = [&](uint32_t r, int j) {
+    if (r < nsel) {
+      if (r < kListLds) lst[r] = j;
+      if (long_list) sid[r] = j;
+    }
+  };
+  if (nwords <= NT) {
+    // one word per thread: an exclusive scan of the counts gives each word's first rank
+    uint32_t x = tid < nwords ? sh.u.bits[tid] : 0u;
+    uint32_t r = scan_excl<NT>(__popc(x), sh.tmp, &nsel);
+    nsel = min(nsel, (uint32_t)a.rcap);
+    long_list = nsel > kListLds;
+    while (x) {
+      put(r++, tid * 32 + __builtin_ctz(x));
+      x &= x - 1u;
+    }
+  } else {
+    // thread t counts words [t * WPT, (t + 1) * WPT); exclusive scans of the counts give
+    // each word's first rank and each non-empty word's place in a compact list, and one
+    // lane per listed word writes its ids at consecutive ranks
+    uint32_t c = 0, nz = 0;
+    uint32_t wcnt[WPT];
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int w = tid * WPT + i;
+      wcnt[i] = w < nwords ? __popc(sh.u.bits[w]) : 0u;
+      c += wcnt[i];
+      nz += wcnt[i] != 0u ? 1u : 0u;
+    }
+    uint32_t nnz;
+    uint32_t k = scan_excl<NT>(c, sh.tmp, &nsel);
+    uint32_t z = scan_excl<NT>(nz, sh.tmp, &nnz);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      if (wcnt[i]) sh.u.nzw[z++] = (uint32_t)(tid * WPT + i) | (k << 11);
+      k += wcnt[i];
+    }
+    nsel = min(nsel, (uint32_t)a.rcap);
+    long_list = nsel > kListLds;
+    __syncthreads();
+    for (int q = tid; q < (int)nnz; q += NT) {
       const uint32_t e = sh.u.nzw[q];
-      const int word = (int)(e & 2047u);
-      const uint32_t x = sh.u.bits[word];
-      if ((x >> bit) & 1u) {
-        const uint32_t r = (e >> 11) + __popc(x & ((1u << bit) - 1u));
-        const int j = word * 32 + bit;
-        if (r < nsel) {
-          if (r < kListLds) lst[r] = j;
-          if (long_list) sid[r] = j;
-        }
+      const int j0 = (int)(e & 2047u) * 32;
+      uint32_t x = sh.u.bits[e & 2047u], r = e >> 11;
+      while (x) {
+        put(r++, j0 + __builtin_ctz(x));
+        x &= x - 1u;
       }
     }
   }
   __syncthreads();
   // sizes and first rows: thread t takes ranks [t * per, (t + 1) * per), loads first
   auto listed = [&](uint32_t r) { return r < kListLds ? lst[r] : sid[r]; };
+  constexpr int RB = 8;  // ranks per thread whose loads are issued together
   const uint32_t per = (nsel + NT - 1) / NT, r0 = tid * per, r1 = min(nsel, r0 + per);
-  int32_t sz4[4], co4[4], id4[4];
+  int32_t szb[RB], cob[RB], idb[RB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sz4[i] = co4[i] = id4[i] = 0;
+  for (int i = 0; i < RB; ++i) {
+    szb[i] = cob[i] = idb[i] = 0;
     if (r0 + i < r1) {
       const int j = listed(r0 + i);
-      id4[i] = j;
-      sz4[i] = a.csize[cb + j];
-      co4[i] = a.coff[cb + j];
+      idb[i] = j;
+      szb[i] = a.csize[cb + j];
+      cob[i] = a.coff[cb + j];
     }
   }
   uint32_t tok = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) tok += r0 + i < r1 ? (uint32_t)sz4[i] + 1u : 0u;
-  for (uint32_t r = r0 + 4; r < r1; ++r) tok += (uint32_t)a.csize[cb + listed(r)] + 1u;
+  for (int i = 0; i < RB; ++i) tok += r0 + i < r1 ? (uint32_t)szb[i] + 1u : 0u;
+  for (uint32_t r = r0 + RB; r < r1; ++r) tok += (uint32_t)a.csize[cb + listed(r)] + 1u;
   uint32_t V;
   uint32_t pos = scan_excl<NT>(tok, sh.tmp, &V);
   const int nB = a.nB;
@@ -982,9 +974,9 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
     pos = te;
   };
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (r0 + i < r1) emit(r0 + i, id4[i], sz4[i], co4[i]);
-  for (uint32_t r = r0 + 4; r < r1; ++r) {
+  for (int i = 0; i < RB; ++i)
+    if (r0 + i < r1) emit(r0 + i, idb[i], szb[i], cob[i]);
+  for (uint32_t r = r0 + RB; r < r1; ++r) {
     const int j = listed(r);
     emit(r, j, a.csize[cb + j], a.coff[cb + j]);
   }
@@ -1007,6 +999,314 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
   }
 }
 
+
+// The last gather workgroup of a (b, kv-head): the exact cut among the clusters of the cut
+// bin, the selection bitmap, and from it the published list in ascending id order (ids,
+// first virtual row, first cache row), `selected`, and each retrieve workgroup's share.
+__device__ __forceinline__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinShared& sh) {
+  constexpr int NT = kDecThreads;
+  const int tid = threadIdx.x;
+  const size_t cb = (size_t)bh * a.C;
+  const uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
+  const uint32_t nsure = min(ld_dev(ctr + kCtrSure), (uint32_t)a.rcap);
+  const uint32_t ntie = min(ld_dev(ctr + kCtrTie), (uint32_t)a.C);
+  const float* tk = a.tie_key + cb;
+  const int32_t* ti = a.tie_id + cb;
+  float Tkey = kNegInf;  // default: every listed cluster of the cut bin
+  int Tid = 0x7fffffff;
+  if (need > nsure && need - nsure < ntie) cut_pair(tk, ti, ntie, need - nsure, sh, Tkey, Tid);
+  for (int i = tid; i < (a.C + 31) / 32; i += NT) sh.u.bits[i] = 0u;
+  __syncthreads();
+  if (need > 0) {
+    const int32_t* su = a.sure + (size_t)bh * a.rcap;
+    for (uint32_t k = tid; k < nsure; k += NT) mark(sh, ld_dev(su + k));
+    for (uint32_t k = tid; k < ntie; k += NT) {
+      const int j = ld_dev(ti + k);
+      if (is_selected(ld_dev(tk + k), j, Tkey, Tid)) mark(sh, j);
+    }
+  }
+  __syncthreads();
+  publish_selection(a, bh, sh);
+}
+
+// ------------------------------------------------------------------------------------
+// selection of a (b, kv-head) of at most kLocalSelectMax clusters by one workgroup, from
+// registers: thread t holds the group scores of clusters 4i .. 4i + 3 for i = k * NT + t
+// ------------------------------------------------------------------------------------
+constexpr int kLocalV = kLocalSelectMax / 4 / kDecThreads;  // float4 of scores per thread
+
+// f(score, cluster id) for every register score of the first nk float4
+template <typename F>
+__device__ __forceinline__ void for_local(const float4 (&v)[kLocalV], int nk, F f) {
+#pragma unroll
+  for (int k = 0; k < kLocalV; ++k) {  // (a guard, not an early exit: the loop unrolls)
+    if (k < nk) {
+      const int j = 4 * (k * kDecThreads + (int)threadIdx.x);
+      // (opaque copies: each pass recomputes what it derives from a score, rather than
+      // the compiler keeping one pass's values live into the next)
+      float x0 = v[k].x, x1 = v[k].y, x2 = v[k].z, x3 = v[k].w;
+      asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
+      f(x0, j);
+      f(x1, j + 1);
+      f(x2, j + 2);
+      f(x3, j + 3);
+    }
+  }
+}
+
+// OR over each aligned group of 8 lanes (every lane of the group gets it): two quad
+// permutations make each quad uniform, then the half-row mirror pairs the two quads.
+__device__ __forceinline__ uint32_t or8_lanes(uint32_t w) {
+  auto mv = [](uint32_t v, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  w |= mv(w, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  w |= mv(w, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  w |= mv(w, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  return w;
+}
+
+// sh.u.bits words [0, nk * NT / 8), whole: bit j set where pick(score, j). A thread's four
+// clusters are one nibble of a word, so eight lanes OR their nibbles into one word.
+template <typename Pick>
+__device__ __forceinline__ void local_bitmap(const float4 (&v)[kLocalV], int nk, FinShared& sh,
+                                             Pick pick) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < kLocalV; ++k) {
+    if (k < nk) {
+      const int i = k * kDecThreads + tid;
+      float x0 = v[k].x, x1 = v[k].y, x2 = v[k].z, x3 = v[k].w;
+      asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
+      const uint32_t nib = (pick(x0, 4 * i) ? 1u : 0u) | (pick(x1, 4 * i + 1) ? 2u : 0u) |
+                           (pick(x2, 4 * i + 2) ? 4u : 0u) | (pick(x3, 4 * i + 3) ? 8u : 0u);
+      const uint32_t w = or8_lanes(nib << (4 * (tid & 7)));
+      if ((tid & 7) == 0) sh.u.bits[i >> 3] = w;
+    }
+  }
+}
+
+// The bin of sh.v[0] holding the need-th largest of the counts hist[0, NBINS) visited from
+// the top, and in sh.v[1] the count above it (1 <= need <= the total). Ends on a barrier.
+template <int NBINS, int PAD>
+__device__ __forceinline__ void cut_bin(const uint32_t* hist, uint32_t need, FinShared& sh) {
+  constexpr int NT = kDecThreads, BPT = NBINS / NT;
+  static_assert(BPT == 1 << PAD, "one padding word per thread's run of bins");
+  const int tid = threadIdx.x;
+  const int hb0 = NBINS - BPT * (tid + 1);  // thread t's bins, visited from the top
+  uint32_t hc[BPT], loc = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    hc[i] = hist[padded<PAD>(hb0 + i)];
+    loc += hc[i];
+  }
+  uint32_t tot;
+  uint32_t run = scan_excl<NT>(loc, sh.tmp, &tot);
+#pragma unroll
+  for (int i = BPT - 1; i >= 0; --i) {
+    if (run < need && run + hc[i] >= need) {
+      sh.v[0] = (uint32_t)(hb0 + i);
+      sh.v[1] = run;
+    }
+    run += hc[i];
+  }
+  __syncthreads();
+}
+
+// (Tkey, Tid): the need-th pair (score descending, id ascending) among the register scores
+// in [lo, hi] (1 <= need < their count), narrowed as cut_pair narrows a listed cut bin.
+__device__ __forceinline__ void cut_pair_local(const float4 (&v)[kLocalV], int nk, int nwords, float lo,
+                               float hi, uint32_t need, FinShared& sh, float& Tkey, int& Tid) {
+  const int tid = threadIdx.x;
+  bool first = true;
+  for (;;) {
+    if (lo == hi) {  // every remaining score is lo
+      Tkey = lo;
+      local_bitmap(v, nk, sh, [&](float x, int) { return x == lo; });
+      __syncthreads();
+      Tid = nth_bit(sh, nwords, need);
+      return;
+    }
+    const Binner b4k(lo, hi, first);
+    first = false;
+    auto bin = [&](float x) { return b4k(x) / (kHistBins / kNarrowBins); };
+    for (int i = tid; i < kNarrowBins + kNarrowBins / 4; i += kDecThreads) sh.u.hist[i] = 0u;
+    if (tid == 0) sh.v[2] = 0u;
+    __syncthreads();
+    for_local(v, nk, [&](float x, int) {
+      if (x >= lo && x <= hi) atomicAdd(&sh.u.hist[padded<kNarrowPad>(bin(x))], 1u);
+    });
+    __syncthreads();
+    cut_bin<kNarrowBins, kNarrowPad>(sh.u.hist, need, sh);
+    const int bstar = (int)sh.v[0];
+    const uint32_t need2 = need - sh.v[1], cnt = sh.u.hist[padded<kNarrowPad>(bstar)];
+    if (cnt <= (uint32_t)kCand) {
+      for_local(v, nk, [&](float x, int j) {
+        if (x >= lo && x <= hi && bin(x) == bstar) {
+          const uint32_t c = atomicAdd(&sh.v[2], 1u);
+          sh.ck[c] = x;
+          sh.ci[c] = j;
+        }
+      });
+      __syncthreads();
+      if (tid < (int)cnt) {
+        const float mv = sh.ck[tid];
+        const int mj = sh.ci[tid];
+        uint32_t rank = 0;
+        for (uint32_t c = 0; c < cnt; ++c) {
+          const float cv = sh.ck[c];
+          rank += (cv > mv || (cv == mv && sh.ci[c] < mj)) ? 1u : 0u;
+        }
+        if (rank == need2 - 1) {
+          sh.tkey = mv;
+          sh.tid = mj;
+        }
+      }
+      __syncthreads();
+      Tkey = sh.tkey;
+      Tid = sh.tid;
+      __syncthreads();
+      return;
+    }
+    Red3 rb{kPosInf, kNegInf, 0u};
+    for_local(v, nk, [&](float x, int) {
+      const bool in = x >= lo && x <= hi && bin(x) == bstar;
+      rb.mn = in ? fminf(rb.mn, x) : rb.mn;
+      rb.mx = in ? fmaxf(rb.mx, x) : rb.mx;
+    });
+    rb = block_red3<kDecThreads>(rb, sh.red);
+    lo = rb.mn;
+    hi = rb.mx;
+    need = need2;
+  }
+}
+
+// The selection of a (b, kv-head) of at most kLocalSelectMax clusters, whole, in one
+// workgroup: the head's scores are loaded once into registers; a value-range histogram
+// over their [min, max] gives the cut bin b* (the bin of the need-th largest score) and the
+// count above it, then the need2-th pair (Tkey, Tid) of b* in (score descending, id
+// ascending) order: an exact rank when b* holds at most kCand scores, else narrowing
+// histograms over the same registers. Since the bins are monotone in the score, the
+// selection is then { j : s_j > Tkey or (s_j == Tkey and j <= Tid) }; the bitmap goes from the
+// registers to LDS and is published as the other selection path publishes it.
+__device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinShared& sh) {
+  constexpr int NT = kDecThreads;
+  const int tid = threadIdx.x;
+  const int n4 = a.Cp / 4, nk = (n4 + NT - 1) / NT, nwords = (a.C + 31) / 32;
+  const float4* sh4 = reinterpret_cast<const float4*>(a.shat + (size_t)bh * a.Cp);
+  float4 v[kLocalV];
+#pragma unroll
+  for (int k = 0; k < kLocalV; ++k) {  // (clamped, unconditional loads: issued together)
+    const int i = k * NT + tid;
+    v[k] = sh4[min(i, n4 - 1)];
+    if (i >= n4) v[k] = neg4();
+  }
+  for (int i = tid; i < kHistBins + 1 + kHistBins / 16 + 1; i += NT) sh.u.full[i] = 0u;
+  if (tid == 0) sh.v[2] = 0u;
+  Red3 r{kPosInf, kNegInf, 0u};
+  for_local(v, nk, [&](float x, int) {
+    const bool f = x != kNegInf;
+    r.mn = f ? fminf(r.mn, x) : r.mn;
+    r.mx = fmaxf(r.mx, x);
+    r.n += f ? 1u : 0u;
+  });
+  r = block_red3<NT>(r, sh.red);  // (its barriers also end the clearing above)
+  const uint32_t need = min((uint32_t)a.n_retrieve, r.n);
+  float Tkey = kPosInf;  // need = 0: nothing selected
+  int Tid = 0;
+  if (need > 0) {
+    // bins (-inf, i.e. empty and padding clusters, to the spare bin), kept two per register
+    const Binner bn(r.mn, r.mx, true);
+    uint32_t bins[2 * kLocalV];
+#pragma unroll
+    for (int k = 0; k < kLocalV; ++k) {
+      bins[2 * k] = bins[2 * k + 1] = 0u;
+      if (k < nk) {
+        float x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        asm volatile("" : "+v"(x4[0]), "+v"(x4[1]), "+v"(x4[2]), "+v"(x4[3]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = x4[e];
+          int b;
+          if (bn.by_value) {  // (the mode is the same for the whole head)
+            const float t = (x - bn.lo) * bn.inv;
+            b = t >= (float)(kHistBins - 1) ? kHistBins - 1 : (int)t;
+          } else {
+            b = bn(x);
+          }
+          b = x != kNegInf ? b : kHistBins;
+          atomicAdd(&sh.u.full[padded<kFullPad>(b)], 1u);
+          bins[2 * k + (e >> 1)] |= (uint32_t)b << (16 * (e & 1));
+        }
+      }
+    }
+    auto bin_of = [&](int k, int e) { return (int)((bins[2 * k + (e >> 1)] >> (16 * (e & 1))) & 0xffffu); };
+    __syncthreads();
+    cut_bin<kHistBins, kFullPad>(sh.u.full, need, sh);
+    const int bstar = (int)sh.v[0];
+    const uint32_t need2 = need - sh.v[1], cnt = sh.u.full[padded<kFullPad>(bstar)];
+    if (cnt <= (uint32_t)kCand) {
+      // rank the scores of b* exactly (need2 = cnt gives its last pair: all of b* is taken)
+#pragma unroll
+      for (int k = 0; k < kLocalV; ++k) {
+        if (k < nk) {
+          const float x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (bin_of(k, e) == bstar) {
+              const uint32_t c = atomicAdd(&sh.v[2], 1u);
+              sh.ck[c] = x4[e];
+              sh.ci[c] = 4 * (k * NT + tid) + e;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < (int)cnt) {
+        const float mv = sh.ck[tid];
+        const int mj = sh.ci[tid];
+        uint32_t rank = 0;
+        for (uint32_t c = 0; c < cnt; ++c) {
+          const float cv = sh.ck[c];
+          rank += (cv > mv || (cv == mv && sh.ci[c] < mj)) ? 1u : 0u;
+        }
+        if (rank == need2 - 1) {
+          sh.tkey = mv;
+          sh.tid = mj;
+        }
+      }
+      __syncthreads();
+      Tkey = sh.tkey;
+      Tid = sh.tid;
+    } else {
+      Red3 rb{kPosInf, kNegInf, 0u};
+#pragma unroll
+      for (int k = 0; k < kLocalV; ++k) {
+        if (k < nk) {
+          const float x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool in = bin_of(k, e) == bstar;
+            rb.mn = in ? fminf(rb.mn, x4[e]) : rb.mn;
+            rb.mx = in ? fmaxf(rb.mx, x4[e]) : rb.mx;
+          }
+        }
+      }
+      rb = block_red3<NT>(rb, sh.red);
+      if (need2 == cnt) {  // all of b*
+        Tkey = rb.mn;
+        Tid = 0x7fffffff;
+      } else {
+        cut_pair_local(v, nk, nwords, rb.mn, rb.mx, need2, sh, Tkey, Tid);
+      }
+    }
+  }
+  __syncthreads();
+  local_bitmap(v, nk, sh, [&](float x, int j) { return x > Tkey || (x == Tkey && j <= Tid); });
+  __syncthreads();
+  publish_selection(a, bh, sh);
+}
+
 // One-dimensional grid, by role (so the selection workgroups of every (b, kv-head) are
 // dispatched first): nH per (b, kv-head) list the clusters of their kSelSpan scores that lie
 // above the cut bin (all selected) or in it (ranked by the last workgroup to arrive, which
@@ -1016,7 +1316,7 @@ __device__ void finish_select(const DecodeArgs& a, int bh, uint32_t need, FinSha
 // nEW + s. The value-sum stream of the estimate does not depend on the selection and runs
 // beside it.
 template <int G>
-__global__ __launch_bounds__(kDecThreads) void k_dec_gather(DecodeArgs a) {
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_gather(DecodeArgs a) {
   const int BH = a.B * a.Hkv, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, cc = lane & 15;
   int x = blockIdx.x, bh;
@@ -1092,6 +1392,10 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gather(DecodeArgs a) {
   // estimate and steady waves that share their SIMDs
   __builtin_amdgcn_s_setprio(3);
   __shared__ FinShared sh;
+  if (!a.hist_kernel) {
+    select_local(a, bh, sh);
+    return;
+  }
   const Cut cut = find_cut(a, bh, sh);
   uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
   if (cut.need > 0) {

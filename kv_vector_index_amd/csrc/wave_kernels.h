@@ -27,7 +27,10 @@ constexpr int kTokChunk = 128;        // steady tokens per steady workgroup
 constexpr int kPartStride = 132;      // floats per (partial, head): o[128], m, l, 2 pad
 constexpr int kSelSpan = 2048;        // group scores listed per selection workgroup
 constexpr int kHistBins = 4096;       // value-range histogram of the group scores
-constexpr int kFusedHistMax = 16384;  // larger heads get the histogram kernel
+// heads of at most this many clusters are selected by one workgroup holding all their
+// scores in registers; larger heads get the histogram kernel and one selection workgroup
+// per kSelSpan scores
+constexpr int kLocalSelectMax = 8192;
 constexpr int kNarrowBins = 1024;     // histogram of a crowded cut bin's scores
 constexpr int kCand = 256;            // scores ranked exactly in LDS
 constexpr int kMaxClusters = 65536;   // clusters per (b, kv-head) supported by the decode
@@ -86,7 +89,7 @@ struct DecodeArgs {
   // merge groups, partial slots (estimate, steady, retrieve, merge)
   int nS, nSW, nEW, nSt, nH, nB, nG, nP;
   float scale, scale_log2;
-  int hist_kernel;         // 1: the histogram kernel runs (Cp > kFusedHistMax)
+  int hist_kernel;         // 1: the histogram kernel runs (Cp > kLocalSelectMax)
 };
 
 // Enqueue one tripartite decode step (score, histogram for large heads, gather, retrieve

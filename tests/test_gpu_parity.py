@@ -300,20 +300,26 @@ def test_llama128k_sampled_parity():
         tl.oracle_decode_check(layer, idx, x.q[s], L, w.n_retrieve, out, lse, sel)
 
 
-def host_index_layer(rng, C, n_distinct, Hq=4, n_sink=3, n_recent=9, steps=1, p_empty=0.05):
+def host_index_layer(rng, C, n_distinct, Hq=4, n_sink=3, n_recent=9, steps=1, p_empty=0.05,
+                     cmean_f32=None, nonempty=()):
     """One KV head whose index is written on the host: cluster sizes 0..3, centroid means
-    drawn from only n_distinct bf16 vectors (so thousands of group scores tie exactly),
-    value sums = the bf16-rounded sums of the cluster's value rows."""
+    drawn from only n_distinct bf16 vectors (so thousands of group scores tie exactly) or
+    given (cmean_f32, exactly representable in bf16), value sums = the bf16-rounded sums of
+    the cluster's value rows."""
     t = tl.torch()
     size = rng.integers(1, 4, C).astype(np.int32)
     size[rng.random(C) < p_empty] = 0
+    size[list(nonempty)] = np.maximum(size[list(nonempty)], 1)
     offset = (n_sink + np.concatenate([[0], np.cumsum(size)[:-1]])).astype(np.int32)
     L0 = n_sink + int(size.sum()) + n_recent
     Lcap = L0 + steps
     k = tl.f32_bits(rng.standard_normal((1, 1, Lcap, 128)))
     v = tl.f32_bits(rng.standard_normal((1, 1, Lcap, 128)))
-    protos = tl.f32_bits(rng.standard_normal((n_distinct, 128)) * 0.3)
-    cmean = protos[rng.integers(0, n_distinct, C)]
+    if cmean_f32 is None:
+        protos = tl.f32_bits(rng.standard_normal((n_distinct, 128)) * 0.3)
+        cmean = protos[rng.integers(0, n_distinct, C)]
+    else:
+        cmean = tl.f32_bits(cmean_f32)
     V = wo.bf16_to_f64(v[0, 0])
     csum = np.zeros((C, 128))
     owner = np.repeat(np.arange(C), size)
@@ -334,12 +340,13 @@ def host_index_layer(rng, C, n_distinct, Hq=4, n_sink=3, n_recent=9, steps=1, p_
     return layer, idx, q, size
 
 
-@pytest.mark.parametrize("C", [12000, 20000, 65536])
+@pytest.mark.parametrize("C", [3000, 8192, 12000, 65536])
 def test_exact_score_ties_select_lowest_ids(C):
-    """Exactly tied group scores are broken towards the lower cluster id, both where each
-    retrieve workgroup selects for itself (C <= 16384) and where one workgroup per head
-    publishes the selection (larger C); the budgets put the cut inside a block of ties
-    thousands of clusters wide, and past the number of non-empty clusters."""
+    """Exactly tied group scores are broken towards the lower cluster id, both where one
+    workgroup selects a whole head from registers (C <= 8192) and where several workgroups
+    per head list candidates and the last ranks them (larger C); the budgets put the cut
+    inside a block of ties thousands of clusters wide, and past the number of non-empty
+    clusters."""
     rng = np.random.default_rng(C)
     layer, idx, q, size = host_index_layer(rng, C, n_distinct=5)
     for n_r in (1, C // 50, C // 3, C):
@@ -351,6 +358,46 @@ def test_exact_score_ties_select_lowest_ids(C):
         got = sel[0, 0]
         want = np.sort(free.selected)
         assert np.array_equal(got[got >= 0], want), "tie-break differs from lowest-id order"
+        assert np.all(got[len(want):] == -1)
+        tl.oracle_decode_check(layer, idx, q[0], layer.L0 + 1, n_r, out, lse, sel)
+
+
+@pytest.mark.parametrize("C,skew", [(6000, 0.0), (8192, 0.93), (30000, 0.0), (65536, 0.93)])
+def test_crowded_cut_bin_is_ranked_exactly(C, skew):
+    """Thousands of distinct group scores in the cut bin, so the cut pair is found after one
+    to three narrowing rounds (C <= 8192: from one workgroup's registers; larger C: from the
+    listed candidates); with skew most clusters share the top two score components and
+    differ only in the third. The scores are exact in fp32 in any summation order (query
+    e0 + 2^-8 e1 + 2^-16 e2 in every head, centroids with few-bit bf16 values in [1, 2) in
+    dims 0..2, zero elsewhere, so every score is a 22-bit fraction; one non-empty outlier of
+    64 stretches the histogram range so that the rest fall in a few of its bins) and
+    distinct scores stay distinct through the scaling, so the selection must equal the
+    oracle's exactly, ties to the lower id."""
+    rng = np.random.default_rng(C + int(skew * 100))
+    cm = np.zeros((C, 128), np.float32)
+    k0 = np.where(rng.random(C) < skew, 0, rng.integers(0, 16, C))
+    k1 = np.where(rng.random(C) < skew, 0, rng.integers(0, 128, C))
+    cm[:, 0] = 1.0 + k0 / 128.0
+    cm[:, 1] = 1.0 + k1 / 128.0
+    cm[:, 2] = 1.0 + rng.integers(0, 32, C) / 32.0
+    j_out = int(rng.integers(0, C))
+    cm[j_out, 0] = 64.0
+    layer, idx, _, size = host_index_layer(rng, C, 0, cmean_f32=cm, p_empty=0.02,
+                                           nonempty=(j_out,))
+    qv = np.zeros((1, 1, layer.Hq, 128), np.float32)
+    qv[..., 0] = 1.0
+    qv[..., 1] = 2.0 ** -8
+    qv[..., 2] = 2.0 ** -16
+    q = tl.f32_bits(qv)
+    hi = tl.head_index(idx, 0, 0)
+    for n_r in (C // 50, C // 7, C // 2):
+        say(f"[crowded C={C} skew={skew}] n_r={n_r}")
+        out, lse, sel = layer.decode(idx, q[0], layer.L0 + 1, n_r)
+        free = wo.decode_group(q[0][0], tl.to_np16(layer.k)[0, 0], tl.to_np16(layer.v)[0, 0], hi,
+                               layer.L0, layer.L0 + 1, layer.n_sink, layer.n_recent, n_r)
+        got = sel[0, 0]
+        want = np.sort(free.selected)
+        assert np.array_equal(got[got >= 0], want), "selection differs from the exact ranking"
         assert np.all(got[len(want):] == -1)
         tl.oracle_decode_check(layer, idx, q[0], layer.L0 + 1, n_r, out, lse, sel)
 
