@@ -253,6 +253,99 @@ __device__ __forceinline__ void merge_partials(const float* parts, int G, int id
   }
 }
 
+// Eight (two) floats of a partial: device-coherent 64-bit loads when DEV (partials written by
+// other workgroups of the same kernel), else plain loads.
+template <bool DEV>
+__device__ __forceinline__ float2 part_ld2(const float* p) {
+  if constexpr (DEV) {
+    const uint64_t u = ld_dev(reinterpret_cast<const uint64_t*>(p));
+    return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+  } else {
+    return *reinterpret_cast<const float2*>(p);
+  }
+}
+template <bool DEV>
+__device__ __forceinline__ float4 part_ld4(const float* p) {
+  const float2 a = part_ld2<DEV>(p), b = part_ld2<DEV>(p + 2);
+  return make_float4(a.x, a.y, b.x, b.y);
+}
+
+// Log-sum-exp merge of the n partials in slots p0, p0 + step, ... of parts ([slot][G]
+// [kPartStride]) by the whole workgroup, in one round of loads when n <= 2 MB: item i
+// (thread t % 128, then further items for G > 4) takes head i / 32 and dims 4 (i % 32) ..
+// + 3; the two halves of the workgroup take the even and the odd partials, each loading all
+// of its partials before combining them, and meet in LDS. emit(h, d4, M, L, o) runs in the
+// first half (M in log2 units, o unnormalised).
+template <int G, bool DEV, int MB, typename Emit>
+__device__ __forceinline__ void merge_block(const float* parts, int p0, int step, int n,
+                                            Emit emit) {
+  __shared__ float xh[128][6];
+  const int tid = threadIdx.x, half = tid >> 7, item = tid & 127;
+  for (int it0 = 0; it0 < G * 32; it0 += 128) {
+    const int it = it0 + item;
+    const bool live = it < G * 32;
+    const int h = live ? it >> 5 : 0, d4 = (it & 31) * 4;
+    float M = kNegInf, L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = half; k0 < n; k0 += 2 * MB) {
+      float2 ml[MB];
+      float4 ov[MB];
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {  // (clamped, unconditional loads: issued together)
+        const int k = min(k0 + 2 * b, n - 1);
+        const float* pp = parts + ((size_t)(p0 + k * step) * G + h) * kPartStride;
+        ml[b] = part_ld2<DEV>(pp + 128);
+        ov[b] = part_ld4<DEV>(pp + d4);
+        if (k0 + 2 * b >= n) ml[b].x = kNegInf;
+      }
+      float mx = M;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) mx = fmaxf(mx, ml[b].x);
+      if (mx != kNegInf) {
+        const float sc = fast_exp2(M - mx);
+        L *= sc;
+        o.x *= sc;
+        o.y *= sc;
+        o.z *= sc;
+        o.w *= sc;
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          const float f = fast_exp2(ml[b].x - mx);
+          L += f * ml[b].y;
+          o.x += f * ov[b].x;
+          o.y += f * ov[b].y;
+          o.z += f * ov[b].z;
+          o.w += f * ov[b].w;
+        }
+        M = mx;
+      }
+    }
+    if (half == 1) {
+      xh[item][0] = M;
+      xh[item][1] = L;
+      xh[item][2] = o.x;
+      xh[item][3] = o.y;
+      xh[item][4] = o.z;
+      xh[item][5] = o.w;
+    }
+    __syncthreads();
+    if (half == 0 && live) {
+      const float M2 = xh[item][0], mx = fmaxf(M, M2);
+      if (mx != kNegInf) {
+        const float f1 = fast_exp2(M - mx), f2 = fast_exp2(M2 - mx);
+        L = f1 * L + f2 * xh[item][1];
+        o.x = f1 * o.x + f2 * xh[item][2];
+        o.y = f1 * o.y + f2 * xh[item][3];
+        o.z = f1 * o.z + f2 * xh[item][4];
+        o.w = f1 * o.w + f2 * xh[item][5];
+        M = mx;
+      }
+      emit(h, d4, M, L, o);
+    }
+    __syncthreads();
+  }
+}
+
 template <int G>
 __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int g, int c, u32x4 (&q)[G]) {
 #pragma unroll
@@ -1582,29 +1675,30 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   const int bq = b * a.Hq + g * G;
   const bool single = a.nG == 1;
   float* gp = parts + (size_t)(nSP + nB + grp) * G * kPartStride;
-  for (int idx = tid; idx < G * 128; idx += kDecThreads) {
-    float M, Ls, O;
-    merge_partials<true, 2 * kMergeGroup>(parts, G, idx, nSP + g0, 1, nSP + g0 + gn, M, Ls, O);
-    const int h = idx >> 7, d = idx & 127;
-    if (single) {
-      a.out[(size_t)(bq + h) * kHeadDim + d] = O / Ls;
-      if (d == 0 && a.lse) a.lse[bq + h] = (M + log2f(Ls)) * kLn2;
-    } else {
-      st_dev(gp + h * kPartStride + d, O);
-      if (d == 0) {
-        st_dev(gp + h * kPartStride + 128, M);
-        st_dev(gp + h * kPartStride + 129, Ls);
-      }
+  auto write_out = [&](int h, int d4, float M, float L, float4 o) {
+    float* op = a.out + (size_t)(bq + h) * kHeadDim + d4;
+    const float r = 1.f / L;
+    *reinterpret_cast<float4*>(op) = make_float4(o.x * r, o.y * r, o.z * r, o.w * r);
+    if (d4 == 0 && a.lse) a.lse[bq + h] = (M + log2f(L)) * kLn2;
+  };
+  if (single) {
+    merge_block<G, true, kMergeBatch>(parts, nSP + g0, 1, gn, write_out);
+    return;
+  }
+  merge_block<G, true, kMergeBatch>(parts, nSP + g0, 1, gn,
+                                    [&](int h, int d4, float M, float L, float4 o) {
+    float* q = gp + h * kPartStride + d4;
+    st_dev(q, o.x);
+    st_dev(q + 1, o.y);
+    st_dev(q + 2, o.z);
+    st_dev(q + 3, o.w);
+    if (d4 == 0) {
+      st_dev(gp + h * kPartStride + 128, M);
+      st_dev(gp + h * kPartStride + 129, L);
     }
-  }
-  if (single || !arrive_last(ctr + kCtrFinal, (uint32_t)a.nG)) return;
-  for (int idx = tid; idx < G * 128; idx += kDecThreads) {
-    float M, Ls, O;
-    merge_partials<true, 2 * kMergeGroup>(parts, G, idx, nSP + nB, 1, nSP + nB + a.nG, M, Ls, O);
-    const int h = idx >> 7, d = idx & 127;
-    a.out[(size_t)(bq + h) * kHeadDim + d] = O / Ls;
-    if (d == 0 && a.lse) a.lse[bq + h] = (M + log2f(Ls)) * kLn2;
-  }
+  });
+  if (!arrive_last(ctr + kCtrFinal, (uint32_t)a.nG)) return;
+  merge_block<G, true, kMergeBatch>(parts, nSP + nB, 1, a.nG, write_out);
 }
 
 // ------------------------------------------------------------------------------------

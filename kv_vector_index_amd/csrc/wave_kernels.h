@@ -36,6 +36,7 @@ constexpr int kCand = 256;            // scores ranked exactly in LDS
 constexpr int kMaxClusters = 65536;   // clusters per (b, kv-head) supported by the decode
 constexpr int kMaxRetrieveWG = 256;   // retrieve workgroups per (b, kv-head)
 constexpr int kMergeGroup = 16;       // retrieve partials per first-level merge (about)
+constexpr int kMergeBatch = 14;       // partials per half-workgroup and round of loads in a merge
 constexpr int kWinR = 1024;           // listed clusters staged per LDS window of a retrieve WG
 constexpr int kRowsPerItem = 128;     // retrieved rows per retrieve workgroup (target)
 constexpr int kRetrieveWGPerCall = 1024;  // retrieve workgroups of one call (at most, about)
