@@ -1180,9 +1180,10 @@ __device__ __forceinline__ void local_bitmap(const float4 (&v)[kLocalV], int nk,
 }
 
 // The bin of sh.v[0] holding the need-th largest of the counts hist[0, NBINS) visited from
-// the top, and in sh.v[1] the count above it (1 <= need <= the total). Ends on a barrier.
+// the top, and in sh.v[1] the count above it, with need = min(want, the total) (returned;
+// nothing is written when it is 0). Ends on a barrier.
 template <int NBINS, int PAD>
-__device__ __forceinline__ void cut_bin(const uint32_t* hist, uint32_t need, FinShared& sh) {
+__device__ __forceinline__ uint32_t cut_bin(const uint32_t* hist, uint32_t want, FinShared& sh) {
   constexpr int NT = kDecThreads, BPT = NBINS / NT;
   static_assert(BPT == 1 << PAD, "one padding word per thread's run of bins");
   const int tid = threadIdx.x;
@@ -1195,6 +1196,7 @@ __device__ __forceinline__ void cut_bin(const uint32_t* hist, uint32_t need, Fin
   }
   uint32_t tot;
   uint32_t run = scan_excl<NT>(loc, sh.tmp, &tot);
+  const uint32_t need = min(want, tot);
 #pragma unroll
   for (int i = BPT - 1; i >= 0; --i) {
     if (run < need && run + hc[i] >= need) {
@@ -1204,6 +1206,7 @@ __device__ __forceinline__ void cut_bin(const uint32_t* hist, uint32_t need, Fin
     run += hc[i];
   }
   __syncthreads();
+  return need;
 }
 
 // (Tkey, Tid): the need-th pair (score descending, id ascending) among the register scores
@@ -1294,65 +1297,72 @@ __device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinSha
     v[k] = sh4[min(i, n4 - 1)];
     if (i >= n4) v[k] = neg4();
   }
-  for (int i = tid; i < kHistBins + 1 + kHistBins / 16 + 1; i += NT) sh.u.full[i] = 0u;
+  {
+    uint4* z = reinterpret_cast<uint4*>(sh.u.full);
+    constexpr int NZ = (kHistBins + 1 + kHistBins / 16 + 1 + 3) / 4;
+    for (int i = tid; i < NZ; i += NT) z[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   if (tid == 0) sh.v[2] = 0u;
-  Red3 r{kPosInf, kNegInf, 0u};
-  for_local(v, nk, [&](float x, int) {
-    const bool f = x != kNegInf;
-    r.mn = f ? fminf(r.mn, x) : r.mn;
-    r.mx = fmaxf(r.mx, x);
-    r.n += f ? 1u : 0u;
-  });
-  r = block_red3<NT>(r, sh.red);  // (its barriers also end the clearing above)
-  const uint32_t need = min((uint32_t)a.n_retrieve, r.n);
-  float Tkey = kPosInf;  // need = 0: nothing selected
+  // the head's finite score range from the score workgroups' (min, max) pairs, read while
+  // the scores are in flight (its barriers also end the clearing above)
+  const Red3 r = score_range(a, bh, sh.red);
+  float Tkey = kPosInf;  // nothing selected (no finite score, or n_r = 0)
   int Tid = 0;
-  if (need > 0) {
+  uint32_t need = 0;
+  if (r.mx != kNegInf && a.n_retrieve > 0) {
     // bins (-inf, i.e. empty and padding clusters, to the spare bin), kept two per register
     const Binner bn(r.mn, r.mx, true);
     uint32_t bins[2 * kLocalV];
+    auto bin_pass = [&](auto binf) {
 #pragma unroll
-    for (int k = 0; k < kLocalV; ++k) {
-      bins[2 * k] = bins[2 * k + 1] = 0u;
-      if (k < nk) {
-        float x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-        asm volatile("" : "+v"(x4[0]), "+v"(x4[1]), "+v"(x4[2]), "+v"(x4[3]));
+      for (int k = 0; k < kLocalV; ++k) {
+        bins[2 * k] = bins[2 * k + 1] = 0u;
+        if (k < nk) {
+          float x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+          asm volatile("" : "+v"(x4[0]), "+v"(x4[1]), "+v"(x4[2]), "+v"(x4[3]));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = x4[e];
-          int b;
-          if (bn.by_value) {  // (the mode is the same for the whole head)
-            const float t = (x - bn.lo) * bn.inv;
-            b = t >= (float)(kHistBins - 1) ? kHistBins - 1 : (int)t;
-          } else {
-            b = bn(x);
+          for (int e = 0; e < 4; ++e) {
+            const int b = x4[e] != kNegInf ? binf(x4[e]) : kHistBins;
+            atomicAdd(&sh.u.full[padded<kFullPad>(b)], 1u);
+            bins[2 * k + (e >> 1)] |= (uint32_t)b << (16 * (e & 1));
           }
-          b = x != kNegInf ? b : kHistBins;
-          atomicAdd(&sh.u.full[padded<kFullPad>(b)], 1u);
-          bins[2 * k + (e >> 1)] |= (uint32_t)b << (16 * (e & 1));
         }
       }
+    };
+    if (bn.by_value) {  // (the mode is the same for the whole head)
+      bin_pass([&](float x) {
+        const float t = (x - bn.lo) * bn.inv;
+        return t >= (float)(kHistBins - 1) ? kHistBins - 1 : (int)t;
+      });
+    } else {
+      bin_pass([&](float x) { return bn(x); });
     }
     auto bin_of = [&](int k, int e) { return (int)((bins[2 * k + (e >> 1)] >> (16 * (e & 1))) & 0xffffu); };
     __syncthreads();
-    cut_bin<kHistBins, kFullPad>(sh.u.full, need, sh);
+    need = cut_bin<kHistBins, kFullPad>(sh.u.full, (uint32_t)a.n_retrieve, sh);
     const int bstar = (int)sh.v[0];
     const uint32_t need2 = need - sh.v[1], cnt = sh.u.full[padded<kFullPad>(bstar)];
     if (cnt <= (uint32_t)kCand) {
-      // rank the scores of b* exactly (need2 = cnt gives its last pair: all of b* is taken)
+      // rank the scores of b* exactly (need2 = cnt gives its last pair: all of b* is taken);
+      // a mask of this thread's scores in b* first, then one LDS slot per set bit
+      uint32_t m = 0;
 #pragma unroll
-      for (int k = 0; k < kLocalV; ++k) {
-        if (k < nk) {
-          const float x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+      for (int k = 0; k < kLocalV; ++k)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (bin_of(k, e) == bstar) {
-              const uint32_t c = atomicAdd(&sh.v[2], 1u);
-              sh.ck[c] = x4[e];
-              sh.ci[c] = 4 * (k * NT + tid) + e;
-            }
-          }
+        for (int e = 0; e < 4; ++e)
+          m |= (k < nk && bin_of(k, e) == bstar) ? 1u << (4 * k + e) : 0u;
+      while (m) {
+        const int q = __builtin_ctz(m);
+        m &= m - 1u;
+        const uint32_t c = atomicAdd(&sh.v[2], 1u);
+        float x = 0.f;  // (picked by selects: registers are not indexed dynamically)
+#pragma unroll
+        for (int k = 0; k < kLocalV; ++k) {
+          x = (q >> 2) == k ? ((q & 3) == 0 ? v[k].x : (q & 3) == 1 ? v[k].y
+                                : (q & 3) == 2 ? v[k].z : v[k].w) : x;
         }
+        sh.ck[c] = x;
+        sh.ci[c] = 4 * ((q >> 2) * NT + tid) + (q & 3);
       }
       __syncthreads();
       if (tid < (int)cnt) {
