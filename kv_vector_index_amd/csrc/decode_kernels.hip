@@ -635,10 +635,11 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
   const float sl2 = a.scale_log2, gmean = a.scale / (float)G;
   const Share sh = chunk_share(a.nS, a.nSW, blockIdx.x);
   // B operands of the wave's 32 clusters of a step (two groups of 16): row t + 16 u + col,
-  // dims 32 s + 8 kg; unconditional loads from a clamped row (rows past the share re-read
-  // its last row, already cached), so the compiler waits for exactly the step in use
+  // dims 32 s + 8 kg, and the clusters' sizes; unconditional loads from a clamped row (rows
+  // past the share re-read its last row, already cached), issued a step ahead and in the
+  // order they are used, so the compiler waits for exactly the step in use
   const int jmax = min(a.C, sh.c1) - 1;
-  auto load = [&](int t, u32x4 (&kb)[2][4]) {
+  auto load = [&](int t, u32x4 (&kb)[2][4], int32_t (&n)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const size_t row = base + min(t + 16 * u + col, jmax);
@@ -646,20 +647,19 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
       for (int st = 0; st < 4; ++st)
         kb[u][st] = ld16_stream(a.cmean + row * kHeadDim + st * 32 + kg * 8);
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      n[u] = __builtin_nontemporal_load(a.csize + base + min(t + 16 * u + col, jmax));
   };
   float mn = kPosInf, mx = kNegInf;
   u32x4 kb[2][4];
+  int32_t n[2];
   int t = sh.c0 + wave * 32;  // this wave's first cluster of each step
-  load(t, kb);
+  load(t, kb, n);
   for (; t < sh.c1; t += 128) {
     u32x4 kn[2][4];
-    load(t + 128, kn);
-    int32_t n[2] = {-1, -1};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = t + 16 * u + col;
-      if (kg == 0 && j < a.C) n[u] = __builtin_nontemporal_load(a.csize + base + j);
-    }
+    int32_t nn[2];
+    load(t + 128, kn, nn);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       floatx4 d = {0.f, 0.f, 0.f, 0.f};
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
       }
       if (kg == 0) {
         const float mean = sum * gmean;
-        const bool ok = n[u] > 0;
+        const bool ok = j < a.C && n[u] > 0;
         if (ok) {
           mn = fminf(mn, mean);
           mx = fmaxf(mx, mean);
@@ -689,9 +689,11 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
+      n[u] = nn[u];
 #pragma unroll
       for (int st = 0; st < 4; ++st) kb[u][st] = kn[u][st];
+    }
   }
   mn = wave_reduce(mn, [](float x, float y) { return fminf(x, y); });
   mx = wave_reduce(mx, [](float x, float y) { return fmaxf(x, y); });
@@ -1411,29 +1413,31 @@ __device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinSha
 }
 
 // One-dimensional grid, by role (so the selection workgroups of every (b, kv-head) are
-// dispatched first): nH per (b, kv-head) list the clusters of their kSelSpan scores that lie
-// above the cut bin (all selected) or in it (ranked by the last workgroup to arrive, which
-// then publishes the selection); then nEW = nS per (b, kv-head) fold the centroid estimate
-// of a chunk of 128 clusters each (weight n_j, logit s_j, value sum V_j) into partial slot
-// e; then nSt per (b, kv-head) attend exactly to 128 steady tokens each, into partial slot
-// nEW + s. The value-sum stream of the estimate does not depend on the selection and runs
-// beside it.
+// dispatched first): nH per (b, kv-head) select (one for heads of at most kLocalSelectMax
+// clusters, which selects and publishes alone; else one per kSelSpan scores, listing the
+// clusters above and in the cut bin, the last of them ranking the cut bin and publishing);
+// then nSt per (b, kv-head) attend exactly to 128 steady tokens each, into partial slot
+// nEW + s; then nEW = nS per (b, kv-head) fold the centroid estimate of a chunk of 128
+// clusters each (weight n_j, logit s_j, value sum V_j) into partial slot e. The value-sum
+// stream of the estimate does not depend on the selection and runs beside it.
 template <int G>
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_gather(DecodeArgs a) {
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 1))) void k_dec_gather(DecodeArgs a) {
   const int BH = a.B * a.Hkv, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, cc = lane & 15;
+  // (roles in dispatch order: selection, steady, estimate; x below numbers a head's
+  // workgroups as selection [0, nH), estimate [nH, nH + nEW), steady after those)
   int x = blockIdx.x, bh;
   if (x < a.nH * BH) {
     bh = x / a.nH;
     x -= bh * a.nH;
-  } else if (x < (a.nH + a.nEW) * BH) {
+  } else if (x < (a.nH + a.nSt) * BH) {
     x -= a.nH * BH;
-    bh = x / a.nEW;
-    x = a.nH + (x - bh * a.nEW);
-  } else {
-    x -= (a.nH + a.nEW) * BH;
     bh = x / a.nSt;
     x = a.nH + a.nEW + (x - bh * a.nSt);
+  } else {
+    x -= (a.nH + a.nSt) * BH;
+    bh = x / a.nEW;
+    x = a.nH + (x - bh * a.nEW);
   }
   if (x >= a.nH) {
     const int b = bh / a.Hkv, g = bh % a.Hkv;
