@@ -162,8 +162,10 @@ __device__ __forceinline__ void merge_row_groups(Online<G>& st) {
 }
 
 // Combine the waves of the workgroup (and, if xp is not null, one more partial
-// [G][kPartStride] held in LDS) and write one partial [G][kPartStride] to dst.
-template <int G>
+// [G][kPartStride] held in LDS) and write one partial [G][kPartStride] to dst: with
+// device-coherent stores when DEV (read by other workgroups of the same kernel), else plain
+// stores (read by a later kernel).
+template <int G, bool DEV = true>
 __device__ __forceinline__ void write_block_partial(Online<G>& st, const float* xp,
                                                     float* __restrict__ dst) {
   constexpr int W = kDecThreads / 64;
@@ -202,10 +204,18 @@ __device__ __forceinline__ void write_block_partial(Online<G>& st, const float* 
         l += s * x[129];
       }
     }
-    st_dev(dst + h * kPartStride + d, o);
-    if (d == 0) {
-      st_dev(dst + h * kPartStride + 128, M);
-      st_dev(dst + h * kPartStride + 129, l);
+    if constexpr (DEV) {
+      st_dev(dst + h * kPartStride + d, o);
+      if (d == 0) {
+        st_dev(dst + h * kPartStride + 128, M);
+        st_dev(dst + h * kPartStride + 129, l);
+      }
+    } else {
+      dst[h * kPartStride + d] = o;
+      if (d == 0) {
+        dst[h * kPartStride + 128] = M;
+        dst[h * kPartStride + 129] = l;
+      }
     }
   }
   __syncthreads();
@@ -1492,7 +1502,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
       attend_rows<G>(a, bh, q, st, wbeg, wend, [&](int64_t t) { return steady_row(a, t); });
       slot = a.nEW + s;
     }
-    write_block_partial<G>(st, nullptr, a.part + ((size_t)bh * a.nP + slot) * G * kPartStride);
+    write_block_partial<G, false>(st, nullptr,
+                                  a.part + ((size_t)bh * a.nP + slot) * G * kPartStride);
     return;
   }
   // the selection is the latency-critical chain of the call: its waves issue ahead of the
