@@ -18,10 +18,13 @@ WRITE_SIZE counters calibrate the HBM-traffic figures taken from rocprofv3 runs 
 script.
 
 Prints one JSON line. `value` is decode-attention tokens/s of the layer (batch / median time
-of one decode call); the index-build rate and achieved HBM bandwidth are extra fields. A
-long-context leg (default: the 1M-token layer) then builds that layer's index once and times
-16 decode calls the same way (`long_context`: call time, HBM bandwidth on the algorithmic
-bytes, build time).
+of one decode call); the index-build rate and achieved HBM bandwidth are extra fields, with
+p10 / p90 of the call time and, as a reference, the bandwidth of a streaming read on the same
+GPU (torch's reduction over the flush buffer). A batched leg (default: batch 8 at 122 880
+tokens) builds that layer's index once and times wave decode calls and dense flash-decode
+calls over the same resident KV (`batched`, with the speedup). A long-context leg (default:
+the 1M-token layer) then builds that layer's index once and times 16 decode calls the same
+way (`long_context`: call time, HBM bandwidth on the algorithmic bytes, build time).
 """
 from __future__ import annotations
 
@@ -53,6 +56,9 @@ def parse():
     ap.add_argument("--cpu-decode-steps", type=int, default=3)
     ap.add_argument("--long-context", default="llama1m",
                     help="also time decode calls at this workload's context ('none': skip)")
+    ap.add_argument("--batched", default="llama122k_b8",
+                    help="also time wave and dense decode calls of this (batched) workload on "
+                         "the same resident KV ('none': skip)")
     return ap.parse_args()
 
 
@@ -256,9 +262,28 @@ def main():
         "roofline_by_kernel": roofs,
         "roofline_decode_call": roof_call,
     }
-    if args.long_context != "none":
-        del k, v, q, k_out, v_out, bws, idx, dws, flush, calib
+    if flush is not None:
+        # a streaming-read reference on this GPU: torch's reduction over the flush buffer
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+        for e in sev:
+            e[0].record()
+            flush.sum()
+            e[1].record()
+        torch.cuda.synchronize()
+        st_ms = med([e[0].elapsed_time(e[1]) for e in sev[1:]])
+        st_gbs = flush.numel() * 4 / (st_ms * 1e-3) / 1e9
+        res["stream_read"] = {"kernel": "torch sum over 512 MiB (one read)",
+                              "GBps": round(st_gbs, 1),
+                              "decode_hbm_frac_of_stream": round(call_gbs / st_gbs, 4)}
+    cs = sorted(call_ms)
+    res["decode_call_us_p10_p90"] = [round(cs[int(0.1 * (len(cs) - 1))] * 1e3, 2),
+                                     round(cs[int(0.9 * (len(cs) - 1))] * 1e3, 2)]
+    del k, v, q, k_out, v_out, bws, idx, dws, flush, calib
+    torch.cuda.empty_cache()
+    if args.batched != "none":
+        res["batched"] = batched_vs_dense(args.batched, 8, 2, not args.no_flush)
         torch.cuda.empty_cache()
+    if args.long_context != "none":
         res["long_context"] = long_context(args.long_context, 16, 2, not args.no_flush)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_decode_steps)
@@ -373,6 +398,67 @@ def long_context(name, n_calls, n_warm, use_flush):
             "retrieved_tokens_per_kv_head": round(Er, 1),
             "index_build_ms": round(build_ms, 3),
             "index_build_tok_s": round(w.batch * w.context / (build_ms * 1e-3), 1)}
+
+def batched_vs_dense(name, n_calls, n_warm, use_flush):
+    """A batched workload's decode against dense flash-decode over the same resident KV: one
+    index build, then n_calls timed wave calls and n_calls timed dense calls (all L rows of
+    every head; HIP events around each call, cache flush before each)."""
+    import torch
+
+    import kv_vector_index_amd as wi
+    import synth
+
+    w = synth.WORKLOADS[name].with_(steps=n_warm + n_calls)
+    nds = n_warm + n_calls
+    x, k, v, q, k_out, v_out, bp, bws, idx, dps, dws, out, lse, sel = setup(w, nds)
+    print(f"[bench] batched leg {w.name}: B={w.batch} L0={w.context} C={w.n_clusters} "
+          f"n_r={w.n_retrieve}", file=sys.stderr, flush=True)
+    be = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    be[0].record()
+    wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws)
+    be[1].record()
+    torch.cuda.synchronize()
+    del x, k, v, bws
+    torch.cuda.empty_cache()
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda") if use_flush else None
+    ev = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
+
+    def timed(call):
+        pairs = [ev() for _ in range(nds)]
+        for s in range(nds):
+            if flush is not None:
+                flush.sum()
+            pairs[s][0].record()
+            call(s)
+            pairs[s][1].record()
+        torch.cuda.synchronize()
+        return statistics.median(p[0].elapsed_time(p[1]) for p in pairs[n_warm:])
+
+    wave_ms = timed(lambda s: wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, out,
+                                                       lse, sel[s], dws))
+    dense_ms = timed(lambda s: wi.wave_dense_decode_attention(dps[s], q[s], k_out, v_out, out,
+                                                              lse, dws))
+    E, Er = exact_rows(w, idx, sel, nds)
+    nbytes = decode_call_bytes(w, E)
+    BH, G, d = w.batch * w.n_kv_heads, w.group, 128
+    L_mid = w.context + (nds + 1) / 2
+    dense_bytes = (4 * d * L_mid + 2 * G * d + 4 * G * d) * BH
+    gbs, dgbs = nbytes / (wave_ms * 1e-3) / 1e9, dense_bytes / (dense_ms * 1e-3) / 1e9
+    build_ms = be[0].elapsed_time(be[1])
+    return {"workload": w.name, "batch": w.batch, "context": w.context,
+            "clusters": w.n_clusters, "n_retrieve": w.n_retrieve, "decode_calls": n_calls,
+            "decode_call_us": round(wave_ms * 1e3, 2),
+            "decode_tok_s": round(w.batch / (wave_ms * 1e-3), 1),
+            "decode_bytes_per_call": nbytes, "decode_hbm_GBps": round(gbs, 1),
+            "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "dense_call_us": round(dense_ms * 1e3, 2),
+            "dense_tok_s": round(w.batch / (dense_ms * 1e-3), 1),
+            "dense_bytes_per_call": dense_bytes, "dense_hbm_GBps": round(dgbs, 1),
+            "dense_hbm_frac": round(dgbs / HBM_PEAK_GBS, 4),
+            "speedup_vs_dense": round(dense_ms / wave_ms, 2),
+            "index_build_ms": round(build_ms, 3),
+            "index_build_tok_s": round(w.batch * w.context / (build_ms * 1e-3), 1)}
+
 
 def kernel_sources_hash() -> str:
     """Hash of the HIP sources: traffic figures are only valid for the kernels they measured."""
