@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--cpu-decode-steps", type=int, default=3)
     ap.add_argument("--long-context", default="llama1m",
                     help="also time decode calls at this workload's context ('none': skip)")
+    ap.add_argument("--accuracy", default="qwen256k",
+                    help="error of the wave decode against exact (dense) attention over this "
+                         "workload's cluster-size x budget grid ('none': skip)")
     ap.add_argument("--batched", default="llama122k_b8",
                     help="also time wave and dense decode calls of this (batched) workload on "
                          "the same resident KV ('none': skip)")
@@ -283,6 +286,9 @@ def main():
     if args.batched != "none":
         res["batched"] = batched_vs_dense(args.batched, 8, 2, not args.no_flush)
         torch.cuda.empty_cache()
+    if args.accuracy != "none":
+        res["accuracy"] = accuracy_grid(args.accuracy, 4)
+        torch.cuda.empty_cache()
     if args.long_context != "none":
         res["long_context"] = long_context(args.long_context, 16, 2, not args.no_flush)
     if not args.no_cpu_baseline:
@@ -458,6 +464,91 @@ def batched_vs_dense(name, n_calls, n_warm, use_flush):
             "speedup_vs_dense": round(dense_ms / wave_ms, 2),
             "index_build_ms": round(build_ms, 3),
             "index_build_tok_s": round(w.batch * w.context / (build_ms * 1e-3), 1)}
+
+
+def accuracy_grid(name, nds, cluster_sizes=(8, 16, 32),
+                  budgets=(0.005, 0.01, 0.018, 0.04, 1.0)):
+    """Error of the wave decode against exact attention (the dense decode over all L rows,
+    itself checked against the oracle's full attention in the tests) on one layer of the
+    workload, for each cluster size (one index build each) and retrieval budget: relative
+    l2 error ||o - o_exact|| / ||o_exact|| per (b, q head, step), mean / p99 / max (budget
+    1.0 retrieves every cluster: exact up to rounding, a check of the comparison). With it,
+    the share of the exact softmax mass that falls on the exactly attended rows (steady and
+    retrieved), for the first KV group of batch element 0 at the first step. An accuracy
+    report of the approximation, not a parity claim."""
+    import numpy as np
+    import torch
+
+    import kv_vector_index_amd as wi
+    import synth
+
+    base = synth.WORKLOADS[name].with_(steps=nds)
+    B, H, Hq, d = base.batch, base.n_kv_heads, base.n_q_heads, 128
+    L0 = base.context
+    t = time.time()
+    x = synth.generate_layer(base)
+    print(f"[bench] accuracy leg {name}: generated inputs in {time.time() - t:.1f}s",
+          file=sys.stderr, flush=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    k, v, q = dev(x.k), dev(x.v), dev(x.q)
+    del x
+    k_out, v_out = torch.zeros_like(k), torch.zeros_like(v)
+    k_out[:, :, L0:] = k[:, :, L0:]
+    v_out[:, :, L0:] = v[:, :, L0:]
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    ref = torch.empty(nds, B, Hq, d, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    grid = []
+    for cs in cluster_sizes:
+        w = base.with_(cluster_size=cs)
+        C = w.n_clusters
+        bp = wi.wave_build_params(B, Hq, H, d, L0, w.capacity, w.segment_size,
+                                  w.clusters_per_segment, w.n_iters, w.n_sink, w.n_recent)
+        bws = torch.empty(wi.wave_index_workspace_size(bp), dtype=torch.uint8, device="cuda")
+        idx = wi.alloc_index(B, H, C, L0, optional=False)
+        wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws)
+        del bws
+        for s in range(nds):
+            p = wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
+                                      w.n_recent, 0, scale)
+            ws = wi.alloc_decode_workspace(p)
+            wi.wave_dense_decode_attention(p, q[s], k_out, v_out, ref[s], None, ws)
+        G = Hq // H
+        for beta in budgets:
+            nr = int(math.ceil(beta * C - 1e-9))
+            errs = []
+            sel = torch.empty(B, H, nr, dtype=torch.int32, device="cuda")
+            for s in range(nds):
+                p = wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
+                                          w.n_recent, nr, scale)
+                ws = wi.alloc_decode_workspace(p)
+                wi.wave_decode_attention(p, q[s], k_out, v_out, idx, out, None,
+                                         sel if s == 0 else None, ws)
+                e = (out - ref[s]).norm(dim=-1) / ref[s].norm(dim=-1)
+                errs.append(e.flatten())
+            e = torch.cat(errs).double().cpu().numpy()
+            # exact softmax mass on the exactly attended rows: batch 0, KV group 0, step 0
+            L = L0 + 1
+            mask = torch.zeros(L, dtype=torch.bool, device="cuda")
+            mask[:w.n_sink] = True
+            mask[L0 - w.n_recent:L] = True
+            ids = sel[0, 0].cpu().numpy()
+            off = idx.cluster_offset[0, 0].cpu().numpy()
+            size = idx.cluster_size[0, 0].cpu().numpy()
+            for j in ids[ids >= 0]:
+                mask[int(off[j]):int(off[j]) + int(size[j])] = True
+            logits = (k_out[0, 0, :L].float() @ q[0][0, :G].float().T) * scale  # [L, G]
+            mass = torch.softmax(logits, dim=0)[mask].sum(dim=0).mean().item()
+            grid.append({"cluster_size": cs, "clusters": C, "budget": beta, "n_retrieve": nr,
+                         "rel_l2_mean": float(f"{e.mean():.3e}"),
+                         "rel_l2_p99": float(f"{np.percentile(e, 99):.3e}"),
+                         "rel_l2_max": float(f"{e.max():.3e}"),
+                         "exact_zone_mass": round(mass, 4)})
+        del idx
+        torch.cuda.empty_cache()
+    return {"workload": name, "batch": B, "context": L0, "n_q_heads": Hq, "n_kv_heads": H,
+            "decode_steps": nds, "reference": "dense decode over all L rows", "grid": grid}
 
 
 def kernel_sources_hash() -> str:
