@@ -1648,7 +1648,10 @@ __device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, cons
 // and its virtual rows, and writes one partial. The last of each of the nG merge groups
 // merges its partials (nG = 1: straight into out / lse); the last of those merges writes
 // out / lse.
-template <int G>
+// XM1: the estimate / steady partials of the workgroup's share merged in one round of loads
+// (every (head, dim) element of a thread at once: a few more registers, for launches small
+// enough to be resident at three workgroups per CU); else element by element.
+template <int G, bool XM1>
 __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   __shared__ float s_x[G][kPartStride];  // this workgroup's share of the earlier partials
   __shared__ int32_t l_ts[kWinR + 1], l_co[kWinR], l_id[kWinR];
@@ -1661,14 +1664,35 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   const int T0 = info.x, T1 = info.y, r_lo = info.z, r_hi = info.w;
   const int32_t* g_ts = a.sel_ts + (size_t)bh * (a.rcap + 1);
   // ---- the estimate / steady partials w_item, w_item + nB, ... merged into s_x
-  for (int idx = tid; idx < G * 128; idx += kDecThreads) {
-    float M, Ls, O;
-    merge_partials<false>(parts, G, idx, w_item, nB, nSP, M, Ls, O);
-    const int h = idx >> 7, d = idx & 127;
-    s_x[h][d] = O;
-    if (d == 0) {
-      s_x[h][128] = M;
-      s_x[h][129] = Ls;
+  if constexpr (XM1) {
+    constexpr int IPT = (G * 128 + kDecThreads - 1) / kDecThreads;
+    float M[IPT], Ls[IPT], O[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i)
+      merge_partials<false, 4>(parts, G, min(tid + i * kDecThreads, G * 128 - 1), w_item, nB,
+                               nSP, M[i], Ls[i], O[i]);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int idx = tid + i * kDecThreads;
+      if (idx < G * 128) {
+        const int h = idx >> 7, d = idx & 127;
+        s_x[h][d] = O[i];
+        if (d == 0) {
+          s_x[h][128] = M[i];
+          s_x[h][129] = Ls[i];
+        }
+      }
+    }
+  } else {
+    for (int idx = tid; idx < G * 128; idx += kDecThreads) {
+      float M, Ls, O;
+      merge_partials<false>(parts, G, idx, w_item, nB, nSP, M, Ls, O);
+      const int h = idx >> 7, d = idx & 127;
+      s_x[h][d] = O;
+      if (d == 0) {
+        s_x[h][128] = M;
+        s_x[h][129] = Ls;
+      }
     }
   }
   u32x4 q[G];
@@ -1772,7 +1796,9 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr
   e = launch(tr, k_dec_gather<G>, dim3((a.nH + a.nEW + a.nSt) * BH), dim3(kDecThreads), 0, s,
              a);
   if (e != hipSuccess) return e;
-  return launch(tr, k_dec_retrieve<G>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
+  if (a.nB * BH <= 3 * kCUs)
+    return launch(tr, k_dec_retrieve<G, true>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
+  return launch(tr, k_dec_retrieve<G, false>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
 }
 
 template <int G>

@@ -39,6 +39,7 @@ constexpr int kMergeGroup = 16;       // retrieve partials per first-level merge
 constexpr int kMergeBatch = 14;       // partials per half-workgroup and round of loads in a merge
 constexpr int kWinR = 1024;           // listed clusters staged per LDS window of a retrieve WG
 constexpr int kRowsPerItem = 128;     // retrieved rows per retrieve workgroup (target)
+constexpr int kCUs = 256;              // compute units of an MI355X
 constexpr int kRetrieveWGPerCall = 1024;  // retrieve workgroups of one call (at most, about)
 // score workgroups of one call (about): three resident per CU, one round
 constexpr int kScoreWGPerCall = 768;

@@ -218,6 +218,9 @@ CASES = {
     "many_clusters": (dict(L0=2200, S=1024, kseg=300, T=4), (12, 300)),
     # more clusters per segment than the segment-resident assignment holds in LDS
     "tiled_assignment": (dict(L0=1500, S=1024, kseg=600, T=2), (20,)),
+    # 32 (b, kv-head) x 28 retrieve workgroups: more than three per CU, so the retrieve
+    # kernel merges its share of the earlier partials element by element
+    "wide_retrieve_grid": (dict(B=4, H=8, Hq=32, L0=3000, S=1024, kseg=64, steps=1), (150,)),
 }
 
 
