@@ -1471,8 +1471,14 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
             vr[i] = ld16_stream(a.vsum + (base + j) * kHeadDim + cc * 8);
             n[i] = __builtin_nontemporal_load(a.csize + base + j);
             const float* sp = a.scores + (base + j) * G;
+            if constexpr (G == 4) {  // (one 16-byte load: rows of four logits are aligned)
+              const u32x4 l4 = ld16(sp);
 #pragma unroll
-            for (int h = 0; h < G; ++h) s2[i][h] = sp[h];
+              for (int h = 0; h < 4; ++h) s2[i][h] = __uint_as_float(l4[h]);
+            } else {
+#pragma unroll
+              for (int h = 0; h < G; ++h) s2[i][h] = sp[h];
+            }
           } else {
             vr[i] = u32x4{0, 0, 0, 0};
             n[i] = 0;
