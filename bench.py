@@ -530,14 +530,15 @@ def accuracy_grid(name, nds, cluster_sizes=(8, 16, 32),
             e = torch.cat(errs).double().cpu().numpy()
             # exact softmax mass on the exactly attended rows: batch 0, KV group 0, step 0
             L = L0 + 1
-            mask = torch.zeros(L, dtype=torch.bool, device="cuda")
-            mask[:w.n_sink] = True
-            mask[L0 - w.n_recent:L] = True
+            m_np = np.zeros(L, dtype=bool)  # (built on the host, copied once)
+            m_np[:w.n_sink] = True
+            m_np[L0 - w.n_recent:L] = True
             ids = sel[0, 0].cpu().numpy()
             off = idx.cluster_offset[0, 0].cpu().numpy()
             size = idx.cluster_size[0, 0].cpu().numpy()
             for j in ids[ids >= 0]:
-                mask[int(off[j]):int(off[j]) + int(size[j])] = True
+                m_np[int(off[j]):int(off[j]) + int(size[j])] = True
+            mask = torch.from_numpy(m_np).cuda()
             logits = (k_out[0, 0, :L].float() @ q[0][0, :G].float().T) * scale  # [L, G]
             mass = torch.softmax(logits, dim=0)[mask].sum(dim=0).mean().item()
             grid.append({"cluster_size": cs, "clusters": C, "budget": beta, "n_retrieve": nr,
