@@ -165,11 +165,12 @@ __device__ __forceinline__ void merge_row_groups(Online<G>& st) {
 // [G][kPartStride] held in LDS) and write one partial [G][kPartStride] to dst: with
 // device-coherent stores when DEV (read by other workgroups of the same kernel), else plain
 // stores (read by a later kernel).
+// sm: LDS exchange [waves][G][kPartStride] (write_block_partial below brings its own).
 template <int G, bool DEV = true>
-__device__ __forceinline__ void write_block_partial(Online<G>& st, const float* xp,
-                                                    float* __restrict__ dst) {
+__device__ __forceinline__ void write_block_partial_in(Online<G>& st, const float* xp,
+                                                       float* __restrict__ dst,
+                                                       float (*sm)[G][kPartStride]) {
   constexpr int W = kDecThreads / 64;
-  __shared__ float sm[W][G][kPartStride];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   merge_row_groups<G>(st);
   if (lane < 16) {
@@ -219,6 +220,13 @@ __device__ __forceinline__ void write_block_partial(Online<G>& st, const float* 
     }
   }
   __syncthreads();
+}
+
+template <int G, bool DEV = true>
+__device__ __forceinline__ void write_block_partial(Online<G>& st, const float* xp,
+                                                    float* __restrict__ dst) {
+  __shared__ float sm[kDecThreads / 64][G][kPartStride];
+  write_block_partial_in<G, DEV>(st, xp, dst, sm);
 }
 
 // Log-sum-exp merge of the partials p0, p0 + step, ... (< n) of parts, for the head/dim
@@ -785,6 +793,17 @@ struct FinShared {
   float tkey;
   int32_t tid;
   uint32_t base[2];
+};
+
+// LDS of an estimate workgroup's second chunk (groups of four heads), staged by direct
+// global-to-LDS loads: the value sums in the register layout of the first chunk (per wave
+// and step, 4 rows x 256 B, lane l at byte 16 l), then the clusters' four logits and sizes
+// (waves 0-1 fill the first copy, waves 2-3 a second one that is not read: every wave issues
+// the same loads, so none of them sits behind a branch).
+struct EstStage {
+  uint32_t rows[kChunk * kHeadDim / 2];  // 128 rows x 256 B
+  float logit[2][kChunk][4];
+  int32_t size[2][kChunk];
 };
 
 // The cut of a (b, kv-head) of more than kLocalSelectMax clusters: need = min(n_r, finite
@@ -1433,6 +1452,13 @@ __device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinSha
 template <int G>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 1))) void k_dec_gather(DecodeArgs a) {
   const int BH = a.B * a.Hkv, tid = threadIdx.x;
+  // (roles use different workgroups: one LDS block serves the selection, an estimate
+  // workgroup's staged chunk and the partial exchange of the estimate and steady roles)
+  __shared__ union {
+    FinShared f;
+    typename std::conditional<G == 4, EstStage, int>::type est;
+    float sm[kDecThreads / 64][G][kPartStride];
+  } lds;
   const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, cc = lane & 15;
   // (roles in dispatch order: selection, steady, estimate; x below numbers a head's
   // workgroups as selection [0, nH), estimate [nH, nH + nEW), steady after those)
@@ -1455,30 +1481,29 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
     st.init();
     int slot;
     if (x < a.nH + a.nEW) {
-      // ---- estimate: chunk e of 128 clusters, 4R rows per wave and step
       const int e = x - a.nH;
       constexpr int R = Rows<G>::R;
       const size_t base = (size_t)bh * a.C;
-      const int j0 = e * kChunk + wave * (kChunk / 4);
-      for (int t = j0; t < j0 + kChunk / 4; t += 4 * R) {
+      if constexpr (G == 4) {
+        // ---- estimate: chunks e nEC (and e nEC + 1 when nEC = 2) of 128 clusters. The
+        // first chunk's rows go to registers (4R rows per wave, one step); the second one is
+        // staged in LDS by direct loads issued after them, so folding the first waits for
+        // the first only; then the second is folded from LDS.
+        const int cA = e * a.nEC, cB = min(cA + a.nEC - 1, a.nS - 1);
+        const bool hasB = cB > cA;
+        const int j0 = cA * kChunk + wave * (kChunk / 4);
         u32x4 vr[R];
         int32_t n[R];
         float s2[R][G], w[R], sg[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          const int j = t + 4 * i + grp;
+          const int j = j0 + 4 * i + grp;
           if (j < a.C) {
             vr[i] = ld16_stream(a.vsum + (base + j) * kHeadDim + cc * 8);
             n[i] = __builtin_nontemporal_load(a.csize + base + j);
-            const float* sp = a.scores + (base + j) * G;
-            if constexpr (G == 4) {  // (one 16-byte load: rows of four logits are aligned)
-              const u32x4 l4 = ld16(sp);
+            const u32x4 l4 = ld16(a.scores + (base + j) * G);
 #pragma unroll
-              for (int h = 0; h < 4; ++h) s2[i][h] = __uint_as_float(l4[h]);
-            } else {
-#pragma unroll
-              for (int h = 0; h < G; ++h) s2[i][h] = sp[h];
-            }
+            for (int h = 0; h < 4; ++h) s2[i][h] = __uint_as_float(l4[h]);
           } else {
             vr[i] = u32x4{0, 0, 0, 0};
             n[i] = 0;
@@ -1486,15 +1511,84 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
             for (int h = 0; h < G; ++h) s2[i][h] = kNegInf;
           }
         }
+        {
+          // (unconditional: without a second chunk these re-read the first, never folded;
+          // rows past the head clamp to its last cluster and are masked when folded)
+          typedef __attribute__((address_space(3))) void* lds_ptr;
+          const int jb = cB * kChunk + wave * (kChunk / 4);
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const bool ok = n[i] > 0;
-          w[i] = ok ? (float)n[i] : 0.f;
-          sg[i] = 1.f;
-#pragma unroll
-          for (int h = 0; h < G; ++h) s2[i][h] = ok ? s2[i][h] : kNegInf;
+          for (int i = 0; i < R; ++i) {
+            const size_t row = base + min(jb + 4 * i + grp, a.C - 1);
+            __builtin_amdgcn_global_load_lds(a.vsum + row * kHeadDim + cc * 8,
+                                             (lds_ptr)&lds.est.rows[(wave * R + i) * 256], 16,
+                                             0, 0);
+          }
+          const int r0 = (wave & 1) * 64;
+          const size_t rc = base + min(cB * kChunk + r0 + lane, a.C - 1);
+          __builtin_amdgcn_global_load_lds(a.scores + rc * G,
+                                           (lds_ptr)&lds.est.logit[wave >> 1][r0][0], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(a.csize + rc, (lds_ptr)&lds.est.size[wave >> 1][r0],
+                                           4, 0, 0);
         }
-        fold_rows<G, R>(st, s2, w, vr, sg);
+        auto fold = [&]() {
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const bool ok = n[i] > 0;
+            w[i] = ok ? (float)n[i] : 0.f;
+            sg[i] = 1.f;
+#pragma unroll
+            for (int h = 0; h < G; ++h) s2[i][h] = ok ? s2[i][h] : kNegInf;
+          }
+          fold_rows<G, R>(st, s2, w, vr, sg);
+        };
+        fold();
+        drain_vmem();  // (the staged chunk is in LDS once this wave's loads have completed)
+        __syncthreads();
+        if (hasB) {
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const int rl = wave * (kChunk / 4) + 4 * i + grp, j = cB * kChunk + rl;
+            vr[i] = *reinterpret_cast<const u32x4*>(&lds.est.rows[(wave * R + i) * 256 + lane * 4]);
+            n[i] = j < a.C ? lds.est.size[0][rl] : 0;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) s2[i][h] = lds.est.logit[0][rl][h];
+          }
+          fold();
+        }
+        __syncthreads();  // (the partial exchange below reuses the staging LDS)
+      } else {
+        // ---- estimate: chunk e of 128 clusters, 4R rows per wave and step
+        const int j0 = e * kChunk + wave * (kChunk / 4);
+        for (int t = j0; t < j0 + kChunk / 4; t += 4 * R) {
+          u32x4 vr[R];
+          int32_t n[R];
+          float s2[R][G], w[R], sg[R];
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const int j = t + 4 * i + grp;
+            if (j < a.C) {
+              vr[i] = ld16_stream(a.vsum + (base + j) * kHeadDim + cc * 8);
+              n[i] = __builtin_nontemporal_load(a.csize + base + j);
+              const float* sp = a.scores + (base + j) * G;
+#pragma unroll
+              for (int h = 0; h < G; ++h) s2[i][h] = sp[h];
+            } else {
+              vr[i] = u32x4{0, 0, 0, 0};
+              n[i] = 0;
+#pragma unroll
+              for (int h = 0; h < G; ++h) s2[i][h] = kNegInf;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const bool ok = n[i] > 0;
+            w[i] = ok ? (float)n[i] : 0.f;
+            sg[i] = 1.f;
+#pragma unroll
+            for (int h = 0; h < G; ++h) s2[i][h] = ok ? s2[i][h] : kNegInf;
+          }
+          fold_rows<G, R>(st, s2, w, vr, sg);
+        }
       }
       slot = e;
     } else {
@@ -1508,14 +1602,15 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
       attend_rows<G>(a, bh, q, st, wbeg, wend, [&](int64_t t) { return steady_row(a, t); });
       slot = a.nEW + s;
     }
-    write_block_partial<G, false>(st, nullptr,
-                                  a.part + ((size_t)bh * a.nP + slot) * G * kPartStride);
+    write_block_partial_in<G, false>(st, nullptr,
+                                     a.part + ((size_t)bh * a.nP + slot) * G * kPartStride,
+                                     lds.sm);
     return;
   }
   // the selection is the latency-critical chain of the call: its waves issue ahead of the
   // estimate and steady waves that share their SIMDs
   __builtin_amdgcn_s_setprio(3);
-  __shared__ FinShared sh;
+  FinShared& sh = lds.f;
   if (!a.hist_kernel) {
     select_local(a, bh, sh);
     return;

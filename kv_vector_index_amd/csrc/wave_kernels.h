@@ -90,6 +90,7 @@ struct DecodeArgs {
   // chunk), steady workgroups, selection workgroups, retrieve workgroups, their
   // merge groups, partial slots (estimate, steady, retrieve, merge)
   int nS, nSW, nEW, nSt, nH, nB, nG, nP;
+  int nEC;                 // chunks per estimate workgroup (2 for groups of four heads)
   float scale, scale_log2;
   int hist_kernel;         // 1: the histogram kernel runs (Cp > kLocalSelectMax)
 };
