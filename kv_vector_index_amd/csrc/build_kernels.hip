@@ -15,7 +15,8 @@
 //           give each point its rank among equal labels) -- no atomics on data, so every
 //           later sum runs in a fixed order and the build is bitwise reproducible;
 //   update: mu_j = bf16(u_j / ||u_j||), u_j = sum of the members' unit keys, summed in
-//           position order by 16 lanes per row (empty clusters keep mu_j).
+//           position order by 16 lanes per row, 16 member rows in flight at a time (empty
+//           clusters keep mu_j).
 // Then finalise: sizes, offsets, mean raw key and value sum per cluster, and the
 // cluster-contiguous permutation of K and V (each row read once, written once), so that
 // decode reads a retrieved cluster as one contiguous run of rows.
@@ -499,22 +500,22 @@ __global__ __launch_bounds__(256) void k_update(BuildArgs a, const uint16_t* __r
   float u[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) u[d] = 0.f;
-  for (int r = cs; r < ce; r += 4) {
-    u32x4 kr[4];
-    float iv[4];
+  // members in batches of 16: lane c of the group loads the batch's c-th member index, and
+  // then all 16 rows are loaded at once (a batch past the last member repeats it with
+  // weight 0), so a batch costs two dependent memory round trips
+  for (int r = cs; r < ce; r += 16) {
+    const int nm = min(16, ce - r);
+    const int mine = order[r + min(c, nm - 1)];
+    u32x4 kr[16];
+    float iv[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (r + e < ce) {
-        const int64_t p = sg.lo + order[r + e];
-        kr[e] = ld16(a.k + (krow0 + p) * kHeadDim + c * 8);
-        iv[e] = inv[p];
-      } else {
-        kr[e] = u32x4{0, 0, 0, 0};
-        iv[e] = 0.f;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int64_t p = sg.lo + __shfl(mine, min(e, nm - 1), 16);
+      kr[e] = ld16(a.k + (krow0 + p) * kHeadDim + c * 8);
+      iv[e] = e < nm ? inv[p] : 0.f;
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 16; ++e)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         u[2 * d] += bf_lo(kr[e][d]) * iv[e];
@@ -556,26 +557,25 @@ __global__ __launch_bounds__(256) void k_finalise(BuildArgs a) {
   float uk[8], ux[8], uv[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) uk[d] = ux[d] = uv[d] = 0.f;
-  for (int r = cs; r < ce; r += 4) {
-    u32x4 kr[4], vr[4];
-    float iv[4];
-    int64_t pp[4];
+  // members in batches of 8, as in the update: the batch's member indices in one load,
+  // then all its key and value rows at once (a batch past the last member repeats it, and
+  // the repeats are skipped)
+  for (int r = cs; r < ce; r += 8) {
+    const int nm = min(8, ce - r);
+    const int mine = order[r + min(c & 7, nm - 1)];
+    u32x4 kr[8], vr[8];
+    float iv[8];
+    int64_t pp[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (r + e < ce) {
-        pp[e] = sg.lo + order[r + e];
-        kr[e] = ld16(a.k + (row0 + pp[e]) * kHeadDim + c * 8);
-        vr[e] = ld16(a.v + (row0 + pp[e]) * kHeadDim + c * 8);
-        iv[e] = inv[pp[e]];
-      } else {
-        pp[e] = -1;
-        kr[e] = vr[e] = u32x4{0, 0, 0, 0};
-        iv[e] = 0.f;
-      }
+    for (int e = 0; e < 8; ++e) {
+      pp[e] = sg.lo + __shfl(mine, min(e, nm - 1), 16);
+      kr[e] = ld16(a.k + (row0 + pp[e]) * kHeadDim + c * 8);
+      vr[e] = ld16(a.v + (row0 + pp[e]) * kHeadDim + c * 8);
+      iv[e] = inv[pp[e]];
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (pp[e] < 0) continue;
+    for (int e = 0; e < 8; ++e) {
+      if (e >= nm) continue;
       const int64_t slot = sg.lo + r + e;
       st16(a.k_out + (row0 + slot) * kHeadDim + c * 8, kr[e]);
       st16(a.v_out + (row0 + slot) * kHeadDim + c * 8, vr[e]);
