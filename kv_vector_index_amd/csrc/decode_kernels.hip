@@ -749,16 +749,23 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_hist(DecodeArgs a) {
   __shared__ uint32_t hs[kHistBins];
   __shared__ float red[NT / 64][3];
   const int bh = blockIdx.y, tid = threadIdx.x;
+  // (the scores are loaded before the range is reduced: one memory round trip for both)
+  constexpr int K4 = kSelSpan / (4 * NT);
+  const float* sh = a.shat + (size_t)bh * a.Cp;
+  float4 sv[K4];
+#pragma unroll
+  for (int k = 0; k < K4; ++k) {
+    const int j4 = blockIdx.x * kSelSpan + k * 4 * NT + 4 * tid;
+    sv[k] = j4 < a.Cp ? *reinterpret_cast<const float4*>(sh + j4) : neg4();
+  }
   const Red3 r = score_range(a, bh, red);
   if (r.mx == kNegInf) return;  // no finite score in this head
   for (int i = tid; i < kHistBins; i += NT) hs[i] = 0u;
   __syncthreads();
   const Binner bn(r.mn, r.mx, true);
-  const float* sh = a.shat + (size_t)bh * a.Cp;
 #pragma unroll
-  for (int k = 0; k < kSelSpan / (4 * NT); ++k) {
-    const int j4 = blockIdx.x * kSelSpan + k * 4 * NT + 4 * tid;
-    const float4 v = j4 < a.Cp ? *reinterpret_cast<const float4*>(sh + j4) : neg4();
+  for (int k = 0; k < K4; ++k) {
+    const float4 v = sv[k];
     hist_add<12>(hs, v.x != kNegInf ? bn(v.x) : 0, v.x != kNegInf);
     hist_add<12>(hs, v.y != kNegInf ? bn(v.y) : 0, v.y != kNegInf);
     hist_add<12>(hs, v.z != kNegInf ? bn(v.z) : 0, v.z != kNegInf);
@@ -818,10 +825,15 @@ struct Cut {
 __device__ __forceinline__ Cut find_cut(const DecodeArgs& a, int bh, FinShared& sh) {
   constexpr int NT = kDecThreads, BPT = kHistBins / NT;
   const int tid = threadIdx.x;
-  const Red3 r = score_range(a, bh, sh.red);
+  // (the histogram is loaded before the range is reduced: one memory round trip for both)
   const uint32_t* gh = a.hist + (size_t)bh * kHistBins;
-  for (int i = tid; i < kHistBins; i += NT)
-    sh.u.full[padded<kFullPad>(i)] = r.mx != kNegInf ? gh[i] : 0u;
+  uint32_t hv[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) hv[i] = gh[tid + i * NT];
+  const Red3 r = score_range(a, bh, sh.red);
+#pragma unroll
+  for (int i = 0; i < BPT; ++i)
+    sh.u.full[padded<kFullPad>(tid + i * NT)] = r.mx != kNegInf ? hv[i] : 0u;
   __syncthreads();
   const int hb0 = kHistBins - BPT * (tid + 1);  // thread t's bins, visited from the top
   uint32_t hc[BPT], loc = 0;
@@ -1615,24 +1627,26 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
     select_local(a, bh, sh);
     return;
   }
+  // (this workgroup's scores are loaded before the cut is found: their round trip
+  // overlaps the cut's)
+  constexpr int E = kSelSpan / kDecThreads;  // scores per thread
+  const float* shv = a.shat + (size_t)bh * a.Cp;
+  float v[E];
+#pragma unroll
+  for (int k = 0; k < E / 4; ++k) {
+    const int j4 = x * kSelSpan + k * 4 * kDecThreads + 4 * tid;
+    const float4 v4 = j4 < a.Cp ? *reinterpret_cast<const float4*>(shv + j4) : neg4();
+    v[4 * k] = v4.x;
+    v[4 * k + 1] = v4.y;
+    v[4 * k + 2] = v4.z;
+    v[4 * k + 3] = v4.w;
+  }
   const Cut cut = find_cut(a, bh, sh);
   uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
   if (cut.need > 0) {
-    constexpr int E = kSelSpan / kDecThreads;  // scores per thread
     const Binner bn(cut.lo, cut.hi, true);
-    const float* shv = a.shat + (size_t)bh * a.Cp;
-    float v[E];
     int bv[E];
     uint32_t ns = 0, nt = 0;
-#pragma unroll
-    for (int k = 0; k < E / 4; ++k) {
-      const int j4 = x * kSelSpan + k * 4 * kDecThreads + 4 * tid;
-      const float4 v4 = j4 < a.Cp ? *reinterpret_cast<const float4*>(shv + j4) : neg4();
-      v[4 * k] = v4.x;
-      v[4 * k + 1] = v4.y;
-      v[4 * k + 2] = v4.z;
-      v[4 * k + 3] = v4.w;
-    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       bv[e] = v[e] != kNegInf ? bn(v[e]) : -1;
