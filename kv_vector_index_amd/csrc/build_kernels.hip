@@ -210,29 +210,10 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const uint16_t* mus = mu + ((size_t)bh * a.C + (size_t)s * a.kseg) * kHeadDim;
-  // 16-byte chunks in batches of 8 per thread, all loads of a batch in flight together
-  // (rows clamp to the last valid one, padding rows are written as zero)
-  for (int q0 = 0; q0 < kpad * 16; q0 += 8 * kA2Threads) {
-    u32x4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = q0 + j * kA2Threads + tid, r = q >> 4, ch = q & 15;
-      v[j] = ld16(mus + (size_t)min(r, nvalid - 1) * kHeadDim + ch * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = q0 + j * kA2Threads + tid, r = q >> 4, ch = q & 15;
-      if (r >= nvalid) v[j] = u32x4{0, 0, 0, 0};
-      if (q < kpad * 16) *reinterpret_cast<u32x4*>(s_mu2 + r * kAsgLdsStride + ch * 16) = v[j];
-    }
-  }
   // this split's points, in 64-point blocks (loads clamp to the last point: columns past the
   // segment are scored but never written)
   const int64_t nblk = (n + 63) / 64;
   const int64_t b0 = nblk * split / nsplit, b1 = nblk * (split + 1) / nsplit;
-  int* s_next = reinterpret_cast<int*>(s_mu2 + kpad * kAsgLdsStride);
-  if (tid == 0) *s_next = (int)(b0 + kA2Waves);
-  __syncthreads();
   auto load_block = [&](int64_t blk, bf16x8 (&bq)[2][8], float (&inv)[2]) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -244,6 +225,31 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
       inv[nb] = a.inv_norm[(size_t)bh * a.L0 + sg.lo + p];
     }
   };
+  // the wave's first key block is loaded before the centroids are staged, so that both
+  // take one memory round trip
+  int64_t blk = b0 + wave;
+  bf16x8 bq[2][8];
+  float inv[2];
+  if (blk < b1) load_block(blk, bq, inv);
+  // the centroids: 16-byte chunks, up to 16 per thread with all their loads in flight
+  // together (rows clamp to the last valid one, padding rows are written as zero)
+  for (int q0 = 0; q0 < kpad * 16; q0 += 16 * kA2Threads) {
+    u32x4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int q = q0 + j * kA2Threads + tid, r = min(q >> 4, kpad - 1), ch = q & 15;
+      v[j] = ld16(mus + (size_t)min(r, nvalid - 1) * kHeadDim + ch * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int q = q0 + j * kA2Threads + tid, r = q >> 4, ch = q & 15;
+      if (r >= nvalid) v[j] = u32x4{0, 0, 0, 0};
+      if (q < kpad * 16) *reinterpret_cast<u32x4*>(s_mu2 + r * kAsgLdsStride + ch * 16) = v[j];
+    }
+  }
+  int* s_next = reinterpret_cast<int*>(s_mu2 + kpad * kAsgLdsStride);
+  if (tid == 0) *s_next = (int)(b0 + kA2Waves);
+  __syncthreads();
   // row of the A operand (centroids) that this lane supplies for row block m0 and k step kk
   // (rows clamp to the last padded one, so reads need no branch)
   auto a_row = [&](int m0, int kk) {
@@ -358,12 +364,8 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
     return (int64_t)__shfl(v, 0);
   };
   uint32_t touch = 0;
-  int64_t blk = b0 + wave;
   while (blk < b1) {
     const int64_t nxt = claim();
-    bf16x8 bq[2][8];
-    float inv[2];
-    load_block(blk, bq, inv);
     const int64_t pn = min(nxt * 64 + lane, n - 1);
     const uint32_t* nrow =
         reinterpret_cast<const uint32_t*>(a.k + ((size_t)bh * a.Lcap + sg.lo + pn) * kHeadDim);
@@ -371,6 +373,7 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
     score_block(blk, bq, inv);
     touch ^= t0 ^ t1;
     blk = nxt;
+    if (blk < b1) load_block(blk, bq, inv);
   }
   // (never true, nsplit >= 1: keeps the touching loads)
   if (nsplit <= 0 && touch == 1u) a.lab[0] = 0;
