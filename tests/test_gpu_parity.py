@@ -303,6 +303,46 @@ def test_llama128k_sampled_parity():
         tl.oracle_decode_check(layer, idx, x.q[s], L, w.n_retrieve, out, lse, sel)
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["llama1m", "llama122k_b8", "qwen256k"])
+def test_full_size_sampled_parity(name):
+    """The other full-size layers that bench.py times (1M tokens; batch 8 at 122 880; the
+    Qwen-shaped batch 4 at 262 144 with seven query heads per KV head), launched as the bench
+    launches them: three sampled (b, kv-head, segment) triples checked at the last pass and
+    through the finalise, and one decode step checked on four sampled (b, kv-head) pairs."""
+    w = synth.WORKLOADS[name]
+    say(f"[{name}] generate")
+    x = synth.generate_layer(w, rows=w.context + 1)
+    layer = tl.Layer(x.k, x.v, w.context, w.segment_size, w.clusters_per_segment, w.n_iters,
+                     w.n_sink, w.n_recent, w.n_q_heads)
+    say(f"[{name}] build")
+    idx = layer.build()
+    segs = tl.segment_ranges(layer)
+    k = layer.kseg
+    rng = np.random.default_rng(11)
+    picks = [(0, 0, 0), (layer.B - 1, layer.H - 1, len(segs) - 1),
+             (int(rng.integers(layer.B)), int(rng.integers(layer.H)), int(rng.integers(len(segs))))]
+    for (b, g, s) in picks:
+        lo, hi = segs[s]
+        say(f"[{name}] check b {b} head {g} segment {s}")
+        labels = idx.labels[b, g, lo:hi].cpu().numpy() - s * k
+        Xhat = wo.normalise_rows(wo.bf16_to_f64(x.k[b, g, lo:hi]))
+        last = tl.to_np16(idx.last_centroids[b, g, s * k:(s + 1) * k])
+        tl.check_assignment(Xhat, last, tl.n_valid(k, hi - lo), labels)
+        size, off, order = wo.finalise_segment(lo, labels, k)
+        assert np.array_equal(idx.cluster_size[b, g, s * k:(s + 1) * k].cpu().numpy(), size)
+        assert np.array_equal(idx.cluster_offset[b, g, s * k:(s + 1) * k].cpu().numpy(), off)
+        assert np.array_equal(tl.to_np16(layer.k_out[b, g, lo:hi]), x.k[b, g, order])
+    say(f"[{name}] decode")
+    L = layer.L0 + 1
+    out, lse, sel = layer.decode(idx, x.q[0], L, w.n_retrieve)
+    heads = {(0, 0), (layer.B - 1, layer.H - 1),
+             (int(rng.integers(layer.B)), int(rng.integers(layer.H))),
+             (int(rng.integers(layer.B)), int(rng.integers(layer.H)))}
+    worst = tl.oracle_decode_check(layer, idx, x.q[0], L, w.n_retrieve, out, lse, sel, heads=heads)
+    say(f"[{name}] worst relative error {worst:.2e}")
+
+
 def host_index_layer(rng, C, n_distinct, Hq=4, n_sink=3, n_recent=9, steps=1, p_empty=0.05,
                      cmean_f32=None, nonempty=()):
     """One KV head whose index is written on the host: cluster sizes 0..3, centroid means
