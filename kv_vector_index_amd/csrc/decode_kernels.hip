@@ -1763,9 +1763,10 @@ __device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, cons
 // and its virtual rows, and writes one partial. The last of each of the nG merge groups
 // merges its partials (nG = 1: straight into out / lse); the last of those merges writes
 // out / lse.
-// XM1: the estimate / steady partials of the workgroup's share merged in one round of loads
-// (every (head, dim) element of a thread at once: a few more registers, for launches small
-// enough to be resident at three workgroups per CU); else element by element.
+// XM1: the estimate / steady partials of the workgroup's share loaded in one round for every
+// (head, dim) element of a thread before the attend and merged after it (more registers, for
+// launches small enough to be resident at three workgroups per CU); else merged element by
+// element before the attend.
 template <int G, bool XM1>
 __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   __shared__ float s_x[G][kPartStride];  // this workgroup's share of the earlier partials
@@ -1778,24 +1779,23 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
   const int4 info = reinterpret_cast<const int4*>(a.wg_info)[(size_t)bh * kMaxRetrieveWG + w_item];
   const int T0 = info.x, T1 = info.y, r_lo = info.z, r_hi = info.w;
   const int32_t* g_ts = a.sel_ts + (size_t)bh * (a.rcap + 1);
-  // ---- the estimate / steady partials w_item, w_item + nB, ... merged into s_x
+  // ---- the estimate / steady partials w_item, w_item + nB, ... merged into s_x. XM1: the
+  // first XB of them are loaded here for every (head, dim) element of the thread and merged
+  // after the attend, so that their round trip overlaps it.
+  constexpr int IPT = XM1 ? (G * 128 + kDecThreads - 1) / kDecThreads : 1;
+  constexpr int XB = 4;
+  float xm[IPT][XB], xl[IPT][XB], xo[IPT][XB];
   if constexpr (XM1) {
-    constexpr int IPT = (G * 128 + kDecThreads - 1) / kDecThreads;
-    float M[IPT], Ls[IPT], O[IPT];
-#pragma unroll
-    for (int i = 0; i < IPT; ++i)
-      merge_partials<false, 4>(parts, G, min(tid + i * kDecThreads, G * 128 - 1), w_item, nB,
-                               nSP, M[i], Ls[i], O[i]);
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      const int idx = tid + i * kDecThreads;
-      if (idx < G * 128) {
-        const int h = idx >> 7, d = idx & 127;
-        s_x[h][d] = O[i];
-        if (d == 0) {
-          s_x[h][128] = M[i];
-          s_x[h][129] = Ls[i];
-        }
+      const int idx = min(tid + i * kDecThreads, G * 128 - 1), h = idx >> 7, d = idx & 127;
+#pragma unroll
+      for (int k = 0; k < XB; ++k) {
+        const int pk = w_item + k * nB;
+        const float* pp = parts + ((size_t)pk * G + h) * kPartStride;
+        xm[i][k] = pk < nSP ? pp[128] : kNegInf;
+        xl[i][k] = pk < nSP ? pp[129] : 0.f;
+        xo[i][k] = pk < nSP ? pp[d] : 0.f;
       }
     }
   } else {
@@ -1831,6 +1831,42 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
                         l_ts, l_co, l_id, 0, cnt);
     __syncthreads();
   }
+  if constexpr (XM1) {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int idx = tid + i * kDecThreads;
+      float M = kNegInf;
+#pragma unroll
+      for (int k = 0; k < XB; ++k) M = fmaxf(M, xm[i][k]);
+      float Ls = 0.f, O = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int k = 0; k < XB; ++k) {
+          const float f = fast_exp2(xm[i][k] - M);
+          O += f * xo[i][k];
+          Ls += f * xl[i][k];
+        }
+      }
+      if (w_item + XB * nB < nSP) {  // more than XB partials for this workgroup
+        float M2, L2, O2, a1, a2, mn;
+        merge_partials<false, 4>(parts, G, min(idx, G * 128 - 1), w_item + XB * nB, nB, nSP, M2,
+                                 L2, O2);
+        lse_pair(M, M2, a1, a2, mn);
+        O = a1 * O + a2 * O2;
+        Ls = a1 * Ls + a2 * L2;
+        M = mn;
+      }
+      if (idx < G * 128) {
+        const int h = idx >> 7, d = idx & 127;
+        s_x[h][d] = O;
+        if (d == 0) {
+          s_x[h][128] = M;
+          s_x[h][129] = Ls;
+        }
+      }
+    }
+  }
+  // (the barrier inside makes s_x visible before it is read)
   write_block_partial<G>(st, &s_x[0][0], parts + (size_t)(nSP + w_item) * G * kPartStride);
   uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
   const int gsz = (nB + a.nG - 1) / a.nG;  // retrieve partials per merge group
