@@ -24,7 +24,9 @@ GPU (torch's reduction over the flush buffer). A batched leg (default: batch 8 a
 tokens) builds that layer's index once and times wave decode calls and dense flash-decode
 calls over the same resident KV (`batched`, with the speedup). A long-context leg (default:
 the 1M-token layer) then builds that layer's index once and times 16 decode calls the same
-way (`long_context`: call time, HBM bandwidth on the algorithmic bytes, build time).
+way (`long_context`: call time, HBM bandwidth on the algorithmic bytes, build time). An
+extension leg (default: the 128K layer) times the extension of an index built for one
+segment fewer tokens to the full context against a full build (`extend`).
 """
 from __future__ import annotations
 
@@ -59,6 +61,9 @@ def parse():
     ap.add_argument("--accuracy", default="qwen256k",
                     help="error of the wave decode against exact (dense) attention over this "
                          "workload's cluster-size x budget grid ('none': skip)")
+    ap.add_argument("--extend", default="llama128k",
+                    help="time the extension of this workload's index by one segment of new "
+                         "tokens against a full build ('none': skip)")
     ap.add_argument("--batched", default="llama122k_b8",
                     help="also time wave and dense decode calls of this (batched) workload on "
                          "the same resident KV ('none': skip)")
@@ -283,6 +288,9 @@ def main():
                                      round(cs[int(0.9 * (len(cs) - 1))] * 1e3, 2)]
     del k, v, q, k_out, v_out, bws, idx, dws, flush, calib
     torch.cuda.empty_cache()
+    if args.extend != "none":
+        res["extend"] = extend_leg(args.extend, 5)
+        torch.cuda.empty_cache()
     if args.batched != "none":
         res["batched"] = batched_vs_dense(args.batched, 8, 2, not args.no_flush)
         torch.cuda.empty_cache()
@@ -404,6 +412,61 @@ def long_context(name, n_calls, n_warm, use_flush):
             "retrieved_tokens_per_kv_head": round(Er, 1),
             "index_build_ms": round(build_ms, 3),
             "index_build_tok_s": round(w.batch * w.context / (build_ms * 1e-3), 1)}
+
+def extend_leg(name, n_rep):
+    """Index extension: a workload's index built for its context minus one segment, then
+    extended to the full context (wave_index_extend: the last, partly indexed segment and
+    the new one are clustered, the rest is copied), against a full build of the same
+    context. Median of n_rep timed calls each (HIP events), after one untimed call."""
+    import numpy as np
+    import torch
+
+    import kv_vector_index_amd as wi
+    import synth
+
+    w = synth.WORKLOADS[name]
+    B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, 128
+    L0, S, K = w.context, w.segment_size, w.clusters_per_segment
+    prev_len = L0 - S
+    x = synth.generate_layer(w, rows=L0 + 1)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    k, v = dev(x.k), dev(x.v)
+    del x
+    k_out, v_out = torch.zeros_like(k), torch.zeros_like(v)
+
+    def params(n):
+        return wi.wave_build_params(B, Hq, H, d, n, L0 + 1, S, K, w.n_iters, w.n_sink,
+                                    w.n_recent)
+
+    bp_prev, bp = params(prev_len), params(L0)
+    ws = torch.empty(wi.wave_index_workspace_size(bp), dtype=torch.uint8, device="cuda")
+    C_prev, C = -(-prev_len // S) * K, -(-L0 // S) * K
+    prev = wi.alloc_index(B, H, C_prev, prev_len, optional=False)
+    idx = wi.alloc_index(B, H, C, L0, optional=False)
+    wi.wave_index_build(bp_prev, k, v, k_out, v_out, prev, ws)
+
+    def timed(call):
+        call()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_rep)]
+        for e in ev:
+            e[0].record()
+            call()
+            e[1].record()
+        torch.cuda.synchronize()
+        return statistics.median(e[0].elapsed_time(e[1]) for e in ev)
+
+    ext_ms = timed(lambda: wi.wave_index_extend(bp, prev_len, k, v, k_out, v_out, prev, idx,
+                                                ws))
+    k_full, v_full = torch.zeros_like(k), torch.zeros_like(v)
+    full_ms = timed(lambda: wi.wave_index_build(bp, k, v, k_full, v_full, idx, ws))
+    s0 = (prev_len - w.n_recent) // S
+    return {"workload": w.name, "prev_len": prev_len, "seq_len": L0,
+            "segments_built": -(-L0 // S) - s0, "segments_total": -(-L0 // S),
+            "extend_ms": round(ext_ms, 3), "full_build_ms": round(full_ms, 3),
+            "speedup_vs_full_build": round(full_ms / ext_ms, 2),
+            "new_tok_s": round(B * (L0 - prev_len) / (ext_ms * 1e-3), 1)}
+
 
 def batched_vs_dense(name, n_calls, n_warm, use_flush):
     """A batched workload's decode against dense flash-decode over the same resident KV: one

@@ -108,6 +108,30 @@ wave_status wave_index_build(const wave_build_params* p, const void* k, const vo
                              void* k_out, void* v_out, const wave_index* idx,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Extend an index after tokens were appended: the index prev was built (or extended) for
+ * prev_seq_len tokens with the same parameters otherwise; idx receives the index for
+ * p->seq_len tokens (its arrays sized for that length, not overlapping prev's).
+ * Clustering is segment-local (gist.science de/fr/zh, section 2A, "segmented clustering"),
+ * so the segments whose indexed range is unchanged keep their clusters: with
+ * s0 = floor((prev_seq_len - n_recent) / S), clusters [0, s0 k_seg) and the labels / perm
+ * of positions [0, s0 S) are copied from prev, and segments [s0, nseg) are built from k, v
+ * as wave_index_build builds them. The result equals wave_index_build for p->seq_len.
+ *   k, v         bf16 [B, Hkv, Lcap, d]: the tokens in their original order for rows
+ *                [s0 S, seq_len) (rows before are not read)
+ *   k_out, v_out the cache of the earlier build, extended in place: rows [s0 S, seq_len)
+ *                are written as a build writes them, rows [n_sink, s0 S) are not touched
+ *   prev         the earlier index (only read; its optional arrays are copied when idx has
+ *                them too)
+ *   idx          output; idx->objective must be NULL (WAVE_ERR_UNSUPPORTED), since the
+ *                objective needs every cluster's pass sums
+ *   workspace    as for wave_index_build with p.
+ * WAVE_ERR_INVALID_ARG when prev_seq_len < n_sink + n_recent or > p->seq_len;
+ * WAVE_ERR_ALIAS when prev overlaps an output. */
+wave_status wave_index_extend(const wave_build_params* p, int64_t prev_seq_len, const void* k,
+                              const void* v, void* k_out, void* v_out, const wave_index* prev,
+                              const wave_index* idx, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------
  * Tripartite decode attention (one step, one layer)
  * ------------------------------------------------------------------------------------

@@ -17,7 +17,7 @@ from dataclasses import dataclass
 
 __all__ = [
     "WaveError", "wave_build_params", "wave_index", "wave_decode_params", "library",
-    "wave_status_string", "wave_index_workspace_size", "wave_index_build",
+    "wave_status_string", "wave_index_workspace_size", "wave_index_build", "wave_index_extend",
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
     "IndexTensors", "alloc_index", "EXPORTED_SYMBOLS", "LIB_PATH", "wave_trace",
     "alloc_decode_workspace",
@@ -25,7 +25,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libwave_index.so")
 EXPORTED_SYMBOLS = (
-    "wave_status_string", "wave_index_workspace_size", "wave_index_build",
+    "wave_status_string", "wave_index_workspace_size", "wave_index_build", "wave_index_extend",
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
     "wave_index_build_traced", "wave_decode_attention_traced",
 )
@@ -88,6 +88,8 @@ def library() -> ctypes.CDLL:
         lib.wave_index_workspace_size.argtypes = [P(wave_build_params), P(sz)]
         lib.wave_index_build.argtypes = [P(wave_build_params), vp, vp, vp, vp, P(wave_index),
                                          vp, sz, vp]
+        lib.wave_index_extend.argtypes = [P(wave_build_params), ctypes.c_int64, vp, vp, vp, vp,
+                                          P(wave_index), P(wave_index), vp, sz, vp]
         lib.wave_decode_workspace_size.argtypes = [P(wave_decode_params), P(sz)]
         lib.wave_decode_attention.argtypes = [P(wave_decode_params), vp, vp, vp, P(wave_index),
                                               vp, vp, vp, vp, sz, vp]
@@ -177,6 +179,17 @@ def alloc_index(batch: int, n_kv_heads: int, n_clusters: int, seq_len: int, devi
 def _trace(events):
     arr = (ctypes.c_void_p * len(events))(*events)
     return wave_trace(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), len(events), 0), arr
+
+
+def wave_index_extend(p: wave_build_params, prev_seq_len: int, k, v, k_out, v_out,
+                      prev: IndexTensors, index: IndexTensors, workspace, stream=None) -> None:
+    """Enqueue the extension of `prev` (built for prev_seq_len tokens) to p.seq_len tokens
+    into `index` (see wave_index_extend in include/wave_index.h)."""
+    pi, ni = prev.c_struct(), index.c_struct()
+    _check("wave_index_extend", library().wave_index_extend(
+        ctypes.byref(p), int(prev_seq_len), _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out),
+        ctypes.byref(pi), ctypes.byref(ni), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def wave_index_build(p: wave_build_params, k, v, k_out, v_out, index: IndexTensors, workspace,

@@ -254,9 +254,12 @@ wave_status wave_index_workspace_size(const wave_build_params* p, size_t* bytes)
 
 namespace {
 
+// prev != nullptr: an extension of the index prev built for prev_len tokens (segments before
+// the first one whose indexed range grew are copied from it, the rest are built).
 wave_status build_impl(const wave_build_params* p, const void* k, const void* v, void* k_out,
                        void* v_out, const wave_index* idx, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream, wave::Tracer* tr) {
+                       size_t workspace_bytes, hipStream_t stream, wave::Tracer* tr,
+                       const wave_index* prev = nullptr, int64_t prev_len = 0) {
   BuildShape sh;
   wave_status st = check_build(p, &sh);
   if (st != WAVE_OK) return st;
@@ -311,6 +314,51 @@ wave_status build_impl(const wave_build_params* p, const void* k, const void* v,
   a.n_recent = p->n_recent;
   a.idx_lo = p->n_sink;
   a.idx_hi = p->seq_len - p->n_recent;
+  a.seg0 = 0;
+  if (prev) {
+    // the earlier index: prev_len tokens, the same segments and clusters per segment
+    if (prev_len < (int64_t)p->n_sink + p->n_recent || prev_len > p->seq_len)
+      return WAVE_ERR_INVALID_ARG;
+    if (!prev->centroid_mean || !prev->value_sum || !prev->cluster_size ||
+        !prev->cluster_offset)
+      return WAVE_ERR_INVALID_ARG;
+    if (idx->objective) return WAVE_ERR_UNSUPPORTED;  // needs every cluster's pass sums
+    const int64_t S = p->segment_size, K = p->clusters_per_segment;
+    const int64_t nseg_prev = (prev_len + S - 1) / S, C_prev = nseg_prev * K;
+    const int seg0 = (int)((prev_len - p->n_recent) / S);
+    const size_t prev_meta = BH * (size_t)C_prev * wave::kHeadDim * 2;
+    const void* ins[] = {prev->centroid_mean, prev->value_sum, prev->cluster_size,
+                         prev->cluster_offset, prev->labels, prev->perm, prev->last_centroids};
+    const size_t in_sz[] = {prev_meta, prev_meta, BH * C_prev * 4, BH * C_prev * 4,
+                            BH * (size_t)prev_len * 4, BH * (size_t)prev_len * 4, prev_meta};
+    for (int i = 0; i < 7; ++i)
+      for (int j = 0; j < nout; ++j)
+        if (ins[i] && outs[j] && overlaps(ins[i], in_sz[i], outs[j], out_sz[j]))
+          return WAVE_ERR_ALIAS;
+    // clusters of segments [0, seg0) and positions [0, seg0 S) keep the earlier index's
+    // values (the optional arrays when both indexes have them)
+    wave::CopyArgs c{};
+    c.BH = (int)BH;
+    const int64_t nc = (int64_t)seg0 * K, np = std::min<int64_t>((int64_t)seg0 * S, prev_len);
+    auto add = [&](const void* src, void* dst, int64_t words, int64_t ss, int64_t ds) {
+      if (src && dst && words > 0)
+        c.blk[c.n++] = {static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), words,
+                        ss, ds};
+    };
+    constexpr int64_t kRowWords = wave::kHeadDim / 2;
+    add(prev->centroid_mean, idx->centroid_mean, nc * kRowWords, C_prev * kRowWords,
+        (int64_t)C * kRowWords);
+    add(prev->value_sum, idx->value_sum, nc * kRowWords, C_prev * kRowWords,
+        (int64_t)C * kRowWords);
+    add(prev->cluster_size, idx->cluster_size, nc, C_prev, C);
+    add(prev->cluster_offset, idx->cluster_offset, nc, C_prev, C);
+    add(prev->last_centroids, idx->last_centroids, nc * kRowWords, C_prev * kRowWords,
+        (int64_t)C * kRowWords);
+    add(prev->labels, idx->labels, np, prev_len, (int64_t)L0);
+    add(prev->perm, idx->perm, np, prev_len, (int64_t)L0);
+    if (wave::launch_copy_blocks(c, stream, tr) != hipSuccess) return WAVE_ERR_HIP;
+    a.seg0 = seg0;
+  }
   return wave::launch_build(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
 }
 
@@ -320,6 +368,15 @@ wave_status wave_index_build(const wave_build_params* p, const void* k, const vo
                              void* k_out, void* v_out, const wave_index* idx, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
   return build_impl(p, k, v, k_out, v_out, idx, workspace, workspace_bytes, stream, nullptr);
+}
+
+wave_status wave_index_extend(const wave_build_params* p, int64_t prev_seq_len, const void* k,
+                              const void* v, void* k_out, void* v_out, const wave_index* prev,
+                              const wave_index* idx, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  if (!prev) return WAVE_ERR_INVALID_ARG;
+  return build_impl(p, k, v, k_out, v_out, idx, workspace, workspace_bytes, stream, nullptr,
+                    prev, prev_seq_len);
 }
 
 wave_status wave_index_build_traced(const wave_build_params* p, const void* k, const void* v,

@@ -49,9 +49,9 @@ __device__ __forceinline__ int n_valid_clusters(const BuildArgs& a, int64_t n) {
 __global__ __launch_bounds__(256) void k_norms(BuildArgs a) {
   const int bh = blockIdx.y;
   const int lane = threadIdx.x & 63, grp = (threadIdx.x >> 4), c = lane & 15;
-  const int64_t n = a.idx_hi - a.idx_lo;
+  const int64_t lo = max(a.idx_lo, (int64_t)a.seg0 * a.S), n = a.idx_hi - lo;
   for (int64_t i = (int64_t)blockIdx.x * 16 + grp; i < n; i += (int64_t)gridDim.x * 16) {
-    const int64_t p = a.idx_lo + i;
+    const int64_t p = lo + i;
     const u32x4 kr = ld16(a.k + ((size_t)bh * a.Lcap + p) * kHeadDim + c * 8);
     float ss = 0.f;
 #pragma unroll
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void k_norms(BuildArgs a) {
 // if the segment is short, zero rows for the clusters that stay empty
 // ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_seeds(BuildArgs a, uint16_t* __restrict__ mu) {
-  const int s = blockIdx.y, bh = blockIdx.z;
+  const int s = a.seg0 + blockIdx.y, bh = blockIdx.z;
   const int grp = threadIdx.x >> 4, c = threadIdx.x & 15;
   const Seg sg = seg_range(a, s);
   const int64_t n = sg.hi - sg.lo;
@@ -98,7 +98,7 @@ constexpr int kAsgTile = 128;                              // centroids per LDS 
 constexpr int kAsgLdsStride = kRowBytes + 16;              // padded row: no bank conflicts
 
 __global__ __launch_bounds__(256) void k_assign(BuildArgs a, const uint16_t* __restrict__ mu) {
-  const int blk = blockIdx.x, s = blockIdx.y, bh = blockIdx.z;
+  const int blk = blockIdx.x, s = a.seg0 + blockIdx.y, bh = blockIdx.z;
   const Seg sg = seg_range(a, s);
   const int64_t n = sg.hi - sg.lo;
   if ((int64_t)blk * kAsgPoints >= n) return;
@@ -201,7 +201,7 @@ constexpr int kA2MaxK = 512;
 __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const uint16_t* __restrict__ mu,
                                                            int nsplit) {
   extern __shared__ __attribute__((aligned(16))) unsigned char s_mu2[];
-  const int split = blockIdx.x, s = blockIdx.y, bh = blockIdx.z;
+  const int split = blockIdx.x, s = a.seg0 + blockIdx.y, bh = blockIdx.z;
   const Seg sg = seg_range(a, s);
   const int64_t n = sg.hi - sg.lo;
   if (n <= 0) return;
@@ -414,7 +414,7 @@ __device__ __forceinline__ uint32_t scan1024_excl(uint32_t x, uint32_t* s_tmp, u
 }
 
 __global__ __launch_bounds__(kSortThreads) void k_sort(BuildArgs a) {
-  const int s = blockIdx.x, bh = blockIdx.y;
+  const int s = a.seg0 + blockIdx.x, bh = blockIdx.y;
   const Seg sg = seg_range(a, s);
   const int n = (int)(sg.hi - sg.lo);
   const int K = a.kseg;
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(BuildArgs a) {
 // ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_update(BuildArgs a, const uint16_t* __restrict__ mu_in,
                                                 uint16_t* __restrict__ mu_out) {
-  const int s = blockIdx.y, bh = blockIdx.z;
+  const int s = a.seg0 + blockIdx.y, bh = blockIdx.z;
   const int grp = threadIdx.x >> 4, c = threadIdx.x & 15;
   const int j = blockIdx.x * 16 + grp;
   if (j >= a.kseg) return;
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256) void k_update(BuildArgs a, const uint16_t* __r
 // finalise: sizes, offsets, mean key, value sum, permuted K/V rows, labels, perm
 // ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_finalise(BuildArgs a) {
-  const int s = blockIdx.y, bh = blockIdx.z;
+  const int s = a.seg0 + blockIdx.y, bh = blockIdx.z;
   const int grp = threadIdx.x >> 4, c = threadIdx.x & 15;
   const int j = blockIdx.x * 16 + grp;
   if (j >= a.kseg) return;
@@ -650,11 +650,32 @@ __global__ __launch_bounds__(256) void k_objective(BuildArgs a) {
   if (threadIdx.x == 0) a.objective[bh] = s_part[0];
 }
 
+// blocks of an earlier index copied into a larger one: blockIdx.y = (b, kv-head), z = block
+__global__ __launch_bounds__(256) void k_copy_blocks(CopyArgs c) {
+  const CopyBlock& b = c.blk[blockIdx.z];
+  const int bh = blockIdx.y;
+  const uint32_t* src = b.src + (size_t)bh * b.src_stride;
+  uint32_t* dst = b.dst + (size_t)bh * b.dst_stride;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < b.words;
+       i += (int64_t)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy_blocks(const CopyArgs& c, hipStream_t st, Tracer* tr) {
+  if (c.n <= 0) return hipSuccess;
+  int64_t most = 0;
+  for (int i = 0; i < c.n; ++i) most = std::max(most, c.blk[i].words);
+  const int nx = (int)std::max<int64_t>(1, std::min<int64_t>((most + 255) / 256, 1024));
+  return launch(tr, k_copy_blocks, dim3(nx, c.BH, c.n), dim3(256), 0, st, c);
+}
+
 // ------------------------------------------------------------------------------------
 hipError_t launch_build(const BuildArgs& a, hipStream_t st, Tracer* tr) {
   const int BH = a.B * a.Hkv;
-  const int64_t nidx = a.idx_hi - a.idx_lo;
-  const dim3 gseg((a.kseg + 15) / 16, a.nseg, BH);
+  // segments [seg0, nseg) are built (seg0 > 0: an extension of an earlier index)
+  const int nsb = a.nseg - a.seg0;
+  const int64_t nidx = a.idx_hi - std::max(a.idx_lo, (int64_t)a.seg0 * a.S);
+  const dim3 gseg((a.kseg + 15) / 16, nsb, BH);
   hipError_t e;
 #define WAVE_TRY(X)                 \
   do {                              \
@@ -666,11 +687,11 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t st, Tracer* tr) {
     WAVE_TRY(launch(tr, k_norms, dim3(nb, BH), dim3(256), 0, st, a));
   }
   WAVE_TRY(launch(tr, k_seeds, gseg, dim3(256), 0, st, a, a.mu[0]));
-  const dim3 gasg((a.S + kAsgPoints - 1) / kAsgPoints, a.nseg, BH);
+  const dim3 gasg((a.S + kAsgPoints - 1) / kAsgPoints, nsb, BH);
   // segment-resident assignment when a segment's centroids fit in LDS; enough splits of
   // each segment to give every CU a workgroup
   const bool seg_res = a.kseg <= kA2MaxK;
-  const int nsplit = std::max(1, std::min((a.S + 63) / 64, (256 + a.nseg * BH - 1) / (a.nseg * BH)));
+  const int nsplit = std::max(1, std::min((a.S + 63) / 64, (256 + nsb * BH - 1) / (nsb * BH)));
   // centroid rows, then the block counter
   const size_t lds2 = (size_t)((std::min(a.kseg, a.S) + 31) & ~31) * kAsgLdsStride + 16;
   if (seg_res) {
@@ -682,11 +703,11 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t st, Tracer* tr) {
   for (int t = 1; t <= a.T; ++t) {
     const uint16_t* cur = a.mu[(t - 1) & 1];
     if (seg_res)
-      WAVE_TRY(launch(tr, k_assign_seg, dim3(nsplit, a.nseg, BH), dim3(kA2Threads),
+      WAVE_TRY(launch(tr, k_assign_seg, dim3(nsplit, nsb, BH), dim3(kA2Threads),
                       (uint32_t)lds2, st, a, cur, nsplit));
     else
       WAVE_TRY(launch(tr, k_assign, gasg, dim3(256), 0, st, a, cur));
-    WAVE_TRY(launch(tr, k_sort, dim3(a.nseg, BH), dim3(kSortThreads), 0, st, a));
+    WAVE_TRY(launch(tr, k_sort, dim3(nsb, BH), dim3(kSortThreads), 0, st, a));
     if (t < a.T) WAVE_TRY(launch(tr, k_update, gseg, dim3(256), 0, st, a, cur, a.mu[t & 1]));
   }
   WAVE_TRY(launch(tr, k_finalise, gseg, dim3(256), 0, st, a));
@@ -695,10 +716,13 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t st, Tracer* tr) {
     WAVE_TRY(launch(tr, k_steady, dim3(nb, BH), dim3(256), 0, st, a));
   }
   if (a.objective) WAVE_TRY(launch(tr, k_objective, dim3(BH), dim3(256), 0, st, a));
-  if (a.last_mu)
-    WAVE_TRY(hipMemcpyAsync(a.last_mu, a.mu[(a.T - 1) & 1],
-                            (size_t)BH * a.C * kHeadDim * sizeof(uint16_t),
-                            hipMemcpyDeviceToDevice, st));
+  if (a.last_mu) {
+    // clusters [seg0 k_seg, C) of every (b, kv-head): the ones this call built
+    const size_t row = kHeadDim * sizeof(uint16_t), c0 = (size_t)a.seg0 * a.kseg;
+    WAVE_TRY(hipMemcpy2DAsync(a.last_mu + c0 * kHeadDim, (size_t)a.C * row,
+                              a.mu[(a.T - 1) & 1] + c0 * kHeadDim, (size_t)a.C * row,
+                              (a.C - c0) * row, BH, hipMemcpyDeviceToDevice, st));
+  }
 #undef WAVE_TRY
   return hipSuccess;
 }

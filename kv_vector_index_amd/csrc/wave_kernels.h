@@ -128,7 +128,23 @@ struct BuildArgs {
   int64_t L0, Lcap;
   int S, kseg, nseg, C, T, n_sink, n_recent;
   int64_t idx_lo, idx_hi;  // indexed positions [idx_lo, idx_hi)
+  int seg0;                // first segment built (an extension keeps the segments before it)
 };
+
+// One contiguous block of 4-byte words per (b, kv-head) copied from an earlier index into
+// a larger one (src and dst strides in words per head).
+struct CopyBlock {
+  const uint32_t* src;
+  uint32_t* dst;
+  int64_t words, src_stride, dst_stride;
+};
+constexpr int kMaxCopyBlocks = 8;
+struct CopyArgs {
+  CopyBlock blk[kMaxCopyBlocks];
+  int n, BH;
+};
+// Enqueue the copy of the blocks (one kernel).
+hipError_t launch_copy_blocks(const CopyArgs& c, hipStream_t stream, Tracer* tr);
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream, Tracer* tr);
 

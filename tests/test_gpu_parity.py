@@ -343,6 +343,64 @@ def test_full_size_sampled_parity(name):
     say(f"[{name}] worst relative error {worst:.2e}")
 
 
+@pytest.mark.parametrize("prev_len", [20, 1041, 1100, 1700, 3000])
+def test_extension_equals_the_full_build(prev_len):
+    """An index built for prev_len tokens and extended to 3000 equals the index built for
+    3000 directly, bit for bit (clustering is segment-local and the build deterministic), and
+    so does the extended cache. prev_len 20 = n_sink + n_recent (an empty index); 1041 puts
+    the earlier indexed range on a segment boundary; 1100 and 1700 end it inside a segment
+    (rebuilt); 3000 extends by nothing. Two batch elements and KV heads exercise the cluster
+    and position strides, which differ between the two lengths."""
+    t = tl.torch()
+    rng = np.random.default_rng(17)
+    full, _ = tl.ragged_layer(rng, B=2, H=2, Hq=4, L0=3000, steps=2, S=512, kseg=32, T=3,
+                              n_sink=3, n_recent=17)
+    idx_full = full.build()
+    idx_full.objective = None
+    prev = tl.Layer(full.k_np, full.v_np, prev_len, full.S, full.kseg, full.T, full.n_sink,
+                    full.n_recent, full.Hq)
+    idx_prev = prev.build()
+    idx_new = wi.alloc_index(full.B, full.H, full.C, full.L0)
+    idx_new.objective = None
+    p = full.build_params()
+    ws = t.empty(wi.wave_index_workspace_size(p), dtype=t.uint8, device="cuda")
+    wi.wave_index_extend(p, prev_len, full.k, full.v, prev.k_out, prev.v_out, idx_prev, idx_new,
+                         ws)
+    t.cuda.synchronize()
+    for f in ("centroid_mean", "value_sum", "cluster_size", "cluster_offset", "labels", "perm",
+              "last_centroids"):
+        a, b = getattr(idx_new, f), getattr(idx_full, f)
+        assert t.equal(a.view(t.int16) if a.dtype == t.bfloat16 else a,
+                       b.view(t.int16) if b.dtype == t.bfloat16 else b), f
+    L0 = full.L0
+    assert t.equal(prev.k_out[:, :, :L0].view(t.int16), full.k_out[:, :, :L0].view(t.int16))
+    assert t.equal(prev.v_out[:, :, :L0].view(t.int16), full.v_out[:, :, :L0].view(t.int16))
+
+
+def test_extension_rejects_bad_arguments():
+    """An earlier length out of range, an objective output, and an index that overlaps the
+    earlier one are refused before anything is enqueued."""
+    t = tl.torch()
+    rng = np.random.default_rng(18)
+    full, _ = tl.ragged_layer(rng, B=1, H=1, Hq=2, L0=1200, steps=1, S=256, kseg=16, T=2,
+                              n_sink=3, n_recent=17)
+    idx_prev = full.build()
+    p = full.build_params()
+    ws = t.empty(wi.wave_index_workspace_size(p), dtype=t.uint8, device="cuda")
+    out = wi.alloc_index(1, 1, full.C, full.L0)
+    with pytest.raises(wi.WaveError, match="UNSUPPORTED"):  # objective requested
+        wi.wave_index_extend(p, 600, full.k, full.v, full.k_out, full.v_out, idx_prev, out, ws)
+    out.objective = None
+    for bad in (10, 1201):
+        with pytest.raises(wi.WaveError, match="INVALID_ARG"):
+            wi.wave_index_extend(p, bad, full.k, full.v, full.k_out, full.v_out, idx_prev, out,
+                                 ws)
+    idx_prev.objective = None
+    with pytest.raises(wi.WaveError, match="ALIAS"):
+        wi.wave_index_extend(p, 600, full.k, full.v, full.k_out, full.v_out, idx_prev,
+                             idx_prev, ws)
+
+
 def host_index_layer(rng, C, n_distinct, Hq=4, n_sink=3, n_recent=9, steps=1, p_empty=0.05,
                      cmean_f32=None, nonempty=()):
     """One KV head whose index is written on the host: cluster sizes 0..3, centroid means
