@@ -75,8 +75,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}): the wave index path here is single-GPU; see DESIGN.md for how it "
-              "would shard.", file=sys.stderr, flush=True)
+              f"{world}): the wave index path here runs on one GPU (it would shard by (batch, "
+              "KV head), each GPU holding its heads' cache and index).", file=sys.stderr,
+              flush=True)
         sys.exit(2)
 
     import numpy as np
