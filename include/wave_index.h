@@ -44,7 +44,8 @@ extern "C" {
 typedef enum {
   WAVE_OK = 0,
   WAVE_ERR_INVALID_ARG = 1,  /* a size, count or pointer is out of range or null */
-  WAVE_ERR_UNSUPPORTED = 2,  /* a valid shape the library does not implement (d != 128, G > 8) */
+  WAVE_ERR_UNSUPPORTED = 2,  /* a valid request the library does not implement (d != 128,
+                                G > 8, an objective output of an extension) */
   WAVE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the reported size */
   WAVE_ERR_ALIAS = 4,        /* an output buffer overlaps an input buffer */
   WAVE_ERR_HIP = 5           /* a HIP launch or runtime call failed */
