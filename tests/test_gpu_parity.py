@@ -377,6 +377,32 @@ def test_extension_equals_the_full_build(prev_len):
     assert t.equal(prev.v_out[:, :, :L0].view(t.int16), full.v_out[:, :, :L0].view(t.int16))
 
 
+def test_extension_with_tiled_assignment():
+    """The extension through the other assignment kernel (k_seg > 512 centroids per segment:
+    LDS tiles of 128 centroids) and a group of seven query heads."""
+    t = tl.torch()
+    rng = np.random.default_rng(19)
+    full, _ = tl.ragged_layer(rng, B=1, H=2, Hq=14, L0=2600, steps=1, S=1024, kseg=600, T=2,
+                              n_sink=3, n_recent=17)
+    idx_full = full.build()
+    prev = tl.Layer(full.k_np, full.v_np, 1500, full.S, full.kseg, full.T, full.n_sink,
+                    full.n_recent, full.Hq)
+    idx_prev = prev.build()
+    idx_new = wi.alloc_index(full.B, full.H, full.C, full.L0)
+    idx_new.objective = None
+    p = full.build_params()
+    ws = t.empty(wi.wave_index_workspace_size(p), dtype=t.uint8, device="cuda")
+    wi.wave_index_extend(p, 1500, full.k, full.v, prev.k_out, prev.v_out, idx_prev, idx_new, ws)
+    t.cuda.synchronize()
+    for f in ("centroid_mean", "value_sum", "cluster_size", "cluster_offset", "labels", "perm",
+              "last_centroids"):
+        a, b = getattr(idx_new, f), getattr(idx_full, f)
+        assert t.equal(a.view(t.int16) if a.dtype == t.bfloat16 else a,
+                       b.view(t.int16) if b.dtype == t.bfloat16 else b), f
+    assert t.equal(prev.k_out[:, :, :full.L0].view(t.int16),
+                   full.k_out[:, :, :full.L0].view(t.int16))
+
+
 def test_extension_rejects_bad_arguments():
     """An earlier length out of range, an objective output, and an index that overlaps the
     earlier one are refused before anything is enqueued."""
