@@ -114,6 +114,31 @@ def test_build_rejects_null_small_workspace_and_aliasing_before_any_launch():
     assert call(K, V, KO, VO, ctypes.byref(bad), WS, ws, None) == 1
 
 
+def test_extend_validates_before_any_launch():
+    """The extension's own checks (earlier length, earlier index, objective output, overlap
+    with the earlier index) run on the host before anything is enqueued."""
+    lib = wi.library()
+    p = build_params()
+    ws = wi.wave_index_workspace_size(p)
+    K, V, KO, VO, WS = 1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40
+    idx = wi.wave_index(6 << 40, 7 << 40, 8 << 40, 9 << 40, None, None, None, None)
+    prev = wi.wave_index(10 << 40, 11 << 40, 12 << 40, 13 << 40, None, None, None, None)
+    lo = p.n_sink + p.n_recent
+
+    def call(n, pr, ix):
+        return lib.wave_index_extend(ctypes.byref(p), n, K, V, KO, VO,
+                                     ctypes.byref(pr) if pr is not None else None,
+                                     ctypes.byref(ix), WS, ws, None)
+    assert call(lo, None, idx) == 1                      # no earlier index
+    assert call(lo - 1, prev, idx) == 1                  # shorter than the steady zone
+    assert call(p.seq_len + 1, prev, idx) == 1           # longer than the new length
+    no_size = wi.wave_index(10 << 40, 11 << 40, None, 13 << 40, None, None, None, None)
+    assert call(lo, no_size, idx) == 1                   # an earlier required array missing
+    with_obj = wi.wave_index(6 << 40, 7 << 40, 8 << 40, 9 << 40, None, None, None, 14 << 40)
+    assert call(lo, prev, with_obj) == 2                 # objective output
+    assert call(lo, idx, idx) == 4                       # earlier index overlaps the output
+
+
 def test_decode_rejects_null_small_workspace_and_aliasing_before_any_launch():
     lib = wi.library()
     p = decode_params()
