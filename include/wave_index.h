@@ -118,14 +118,18 @@ wave_status wave_index_build(const wave_build_params* p, const void* k, const vo
  * of positions [0, s0 S) are copied from prev, and segments [s0, nseg) are built from k, v
  * as wave_index_build builds them. The result equals wave_index_build for p->seq_len.
  *   k, v         bf16 [B, Hkv, Lcap, d]: the tokens in their original order for rows
- *                [s0 S, seq_len) (rows before are not read)
- *   k_out, v_out the cache of the earlier build, extended in place: rows [s0 S, seq_len)
- *                are written as a build writes them, rows [n_sink, s0 S) are not touched
- *   prev         the earlier index (only read; its optional arrays are copied when idx has
- *                them too)
+ *                [max(s0 S, n_sink), seq_len) (rows before, the sink rows included, are
+ *                not read)
+ *   k_out, v_out the cache of the earlier build, extended in place: rows
+ *                [max(s0 S, n_sink), seq_len) are written as a build writes them, rows
+ *                [0, max(s0 S, n_sink)) (the sink rows included) are not touched
+ *   prev         the earlier index (only read). Each optional array of idx (labels, perm,
+ *                last_centroids) is copied from prev's for the unchanged segments, so prev
+ *                must have it too (WAVE_ERR_INVALID_ARG otherwise)
  *   idx          output; idx->objective must be NULL (WAVE_ERR_UNSUPPORTED), since the
  *                objective needs every cluster's pass sums
  *   workspace    as for wave_index_build with p.
+ * An extension by nothing (prev_seq_len = seq_len) is valid; it copies prev into idx.
  * WAVE_ERR_INVALID_ARG when prev_seq_len < n_sink + n_recent or > p->seq_len;
  * WAVE_ERR_ALIAS when prev overlaps an output. */
 wave_status wave_index_extend(const wave_build_params* p, int64_t prev_seq_len, const void* k,

@@ -323,6 +323,10 @@ wave_status build_impl(const wave_build_params* p, const void* k, const void* v,
         !prev->cluster_offset)
       return WAVE_ERR_INVALID_ARG;
     if (idx->objective) return WAVE_ERR_UNSUPPORTED;  // needs every cluster's pass sums
+    // an optional output is copied from the earlier index for the unchanged segments
+    if ((idx->labels && !prev->labels) || (idx->perm && !prev->perm) ||
+        (idx->last_centroids && !prev->last_centroids))
+      return WAVE_ERR_INVALID_ARG;
     const int64_t S = p->segment_size, K = p->clusters_per_segment;
     const int64_t nseg_prev = (prev_len + S - 1) / S, C_prev = nseg_prev * K;
     const int seg0 = (int)((prev_len - p->n_recent) / S);
@@ -358,6 +362,7 @@ wave_status build_impl(const wave_build_params* p, const void* k, const void* v,
     add(prev->perm, idx->perm, np, prev_len, (int64_t)L0);
     if (wave::launch_copy_blocks(c, stream, tr) != hipSuccess) return WAVE_ERR_HIP;
     a.seg0 = seg0;
+    a.extend = 1;
   }
   return wave::launch_build(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
 }

@@ -620,7 +620,9 @@ __global__ __launch_bounds__(256) void k_finalise(BuildArgs a) {
   }
 }
 
-// steady rows stay in place: copy them, label -1, perm = identity
+// steady rows stay in place: copy them, label -1, perm = identity. An extension leaves the
+// sink rows of k_out / v_out as the earlier build wrote them (and does not read them from k,
+// v), and still writes their labels and perm.
 __global__ __launch_bounds__(256) void k_steady(BuildArgs a) {
   const int bh = blockIdx.y;
   const int grp = threadIdx.x >> 4, c = threadIdx.x & 15;
@@ -628,8 +630,10 @@ __global__ __launch_bounds__(256) void k_steady(BuildArgs a) {
   for (int64_t t = (int64_t)blockIdx.x * 16 + grp; t < n; t += (int64_t)gridDim.x * 16) {
     const int64_t p = t < a.n_sink ? t : a.L0 - a.n_recent + (t - a.n_sink);
     const size_t row = ((size_t)bh * a.Lcap + p) * kHeadDim + c * 8;
-    st16(a.k_out + row, ld16(a.k + row));
-    st16(a.v_out + row, ld16(a.v + row));
+    if (!(a.extend && t < a.n_sink)) {
+      st16(a.k_out + row, ld16(a.k + row));
+      st16(a.v_out + row, ld16(a.v + row));
+    }
     if (c == 0 && a.perm) a.perm[(size_t)bh * a.L0 + p] = (int32_t)p;
     if (c == 1 && a.labels) a.labels[(size_t)bh * a.L0 + p] = -1;
   }
@@ -682,6 +686,9 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t st, Tracer* tr) {
     e = (X);                        \
     if (e != hipSuccess) return e;  \
   } while (0)
+  // an extension by nothing (n_recent = 0 and an unchanged length that ends a segment)
+  // builds no segment: only the steady rows' labels and perm below
+  if (nsb > 0) {
   if (nidx > 0) {
     const int nb = (int)std::min<int64_t>((nidx + 15) / 16, 4096);
     WAVE_TRY(launch(tr, k_norms, dim3(nb, BH), dim3(256), 0, st, a));
@@ -711,12 +718,13 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t st, Tracer* tr) {
     if (t < a.T) WAVE_TRY(launch(tr, k_update, gseg, dim3(256), 0, st, a, cur, a.mu[t & 1]));
   }
   WAVE_TRY(launch(tr, k_finalise, gseg, dim3(256), 0, st, a));
+  }
   if (a.n_sink + a.n_recent > 0) {
     const int nb = (int)std::min<int64_t>(((int64_t)a.n_sink + a.n_recent + 15) / 16, 1024);
     WAVE_TRY(launch(tr, k_steady, dim3(nb, BH), dim3(256), 0, st, a));
   }
   if (a.objective) WAVE_TRY(launch(tr, k_objective, dim3(BH), dim3(256), 0, st, a));
-  if (a.last_mu) {
+  if (a.last_mu && nsb > 0) {
     // clusters [seg0 k_seg, C) of every (b, kv-head): the ones this call built
     const size_t row = kHeadDim * sizeof(uint16_t), c0 = (size_t)a.seg0 * a.kseg;
     WAVE_TRY(hipMemcpy2DAsync(a.last_mu + c0 * kHeadDim, (size_t)a.C * row,

@@ -129,6 +129,7 @@ struct BuildArgs {
   int S, kseg, nseg, C, T, n_sink, n_recent;
   int64_t idx_lo, idx_hi;  // indexed positions [idx_lo, idx_hi)
   int seg0;                // first segment built (an extension keeps the segments before it)
+  int extend;              // 1: an extension (the sink rows of k_out are already in place)
 };
 
 // One contiguous block of 4-byte words per (b, kv-head) copied from an earlier index into

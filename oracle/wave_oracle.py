@@ -208,6 +208,22 @@ def finalise_segment(lo: int, local_labels: np.ndarray, k_seg: int):
     return size, offset, np.asarray(order, dtype=np.int64)
 
 
+def cluster_stats(K: np.ndarray, V: np.ndarray, lo: int, local_labels: np.ndarray,
+                  k_seg: int) -> tuple[np.ndarray, np.ndarray]:
+    """Mean raw key and value sum of each cluster of the segment whose points start at
+    position lo (K, V: fp64 rows indexed by absolute position), both bf16 (reading R1, R11;
+    gist.science/zh §2A: centroids plus precomputed value sums). Empty clusters are zero."""
+    d = K.shape[1]
+    cmean = np.zeros((k_seg, d), dtype=np.uint16)
+    vsum = np.zeros((k_seg, d), dtype=np.uint16)
+    for j in range(k_seg):
+        members = lo + np.nonzero(local_labels == j)[0]
+        if len(members):
+            cmean[j] = round_bf16(K[members].sum(axis=0) / len(members))
+            vsum[j] = round_bf16(V[members].sum(axis=0))
+    return cmean, vsum
+
+
 def build_head(Kb: np.ndarray, Vb: np.ndarray, L0: int, S: int, k_seg: int, n_iters: int,
                n_sink: int, n_recent: int, labels_override: np.ndarray | None = None,
                ) -> tuple[HeadIndex, np.ndarray, np.ndarray]:
@@ -247,11 +263,7 @@ def build_head(Kb: np.ndarray, Vb: np.ndarray, L0: int, S: int, k_seg: int, n_it
         size[base:base + k_seg] = sz
         offset[base:base + k_seg] = off
         perm[lo:hi] = order
-        for j in range(k_seg):
-            members = lo + np.nonzero(loc == j)[0]
-            if len(members):
-                cmean[base + j] = round_bf16(K[members].sum(axis=0) / len(members))
-                vsum[base + j] = round_bf16(V[members].sum(axis=0))
+        cmean[base:base + k_seg], vsum[base:base + k_seg] = cluster_stats(K, V, lo, loc, k_seg)
     K_out = Kb[:L0][perm]
     V_out = Vb[:L0][perm]
     return HeadIndex(cmean, vsum, size, offset, labels, perm, last, obj), K_out, V_out

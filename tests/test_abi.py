@@ -137,6 +137,11 @@ def test_extend_validates_before_any_launch():
     with_obj = wi.wave_index(6 << 40, 7 << 40, 8 << 40, 9 << 40, None, None, None, 14 << 40)
     assert call(lo, prev, with_obj) == 2                 # objective output
     assert call(lo, idx, idx) == 4                       # earlier index overlaps the output
+    # an optional output of idx must exist in prev (it is copied for the unchanged segments)
+    for field, addr in (("labels", 15 << 40), ("perm", 16 << 40), ("last_centroids", 17 << 40)):
+        want = wi.wave_index(6 << 40, 7 << 40, 8 << 40, 9 << 40, None, None, None, None)
+        setattr(want, field, addr)
+        assert call(lo, prev, want) == 1, field
 
 
 def test_decode_rejects_null_small_workspace_and_aliasing_before_any_launch():

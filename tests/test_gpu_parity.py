@@ -4,6 +4,7 @@ All inputs come from the seeded generator (synth); every expected value comes fr
 run on the CPU. Tolerances follow the protocol in wave_testlib.
 """
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -227,9 +228,10 @@ CASES = {
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_shapes_and_edge_cases(case):
     kw, budgets = CASES[case]
-    rng = np.random.default_rng(abs(hash(case)) % 2 ** 32)
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
     layer, q = tl.ragged_layer(rng, **kw)
-    say(f"[edge {case}] build B={layer.B} H={layer.H} Hq={layer.Hq} L0={layer.L0} "
+    say(f"[edge {case}] seed {zlib.crc32(case.encode())} build B={layer.B} H={layer.H} "
+        f"Hq={layer.Hq} L0={layer.L0} "
         f"S={layer.S} kseg={layer.kseg}")
     idx = layer.build()
     labels = idx.labels.cpu().numpy()
@@ -270,32 +272,27 @@ def test_shapes_and_edge_cases(case):
 @pytest.mark.slow
 def test_llama128k_sampled_parity():
     """Full 128K single-layer workload, launched as the bench launches it: sampled segments
-    checked step-wise at the last pass and through the finalise, and two decode steps checked
-    on every head."""
+    checked at the last pass and through the finalise (labels, sizes, offsets, permuted rows,
+    centroid means, value sums), the objective of three heads over all their segments, one
+    k-means update step on the sampled segments (a build with one pass fewer), and two decode
+    steps checked on every head."""
     w = synth.WORKLOADS["llama128k"]
     say("[128k] generate")
     x = synth.generate_layer(w, rows=w.context + 2)
     layer = tl.Layer(x.k, x.v, w.context, w.segment_size, w.clusters_per_segment, w.n_iters,
                      w.n_sink, w.n_recent, w.n_q_heads)
+    say("[128k] build with one pass fewer")
+    idx_prev = layer.build(T=w.n_iters - 1)
     say("[128k] build")
     idx = layer.build()
-    labels = idx.labels.cpu().numpy()
-    last = tl.to_np16(idx.last_centroids)
-    k_out = tl.to_np16(layer.k_out)
-    segs = tl.segment_ranges(layer)
+    nseg = layer.nseg
     rng = np.random.default_rng(5)
-    for (g, s) in [(0, 0), (3, 7), (7, len(segs) - 1)] + [
-            (int(rng.integers(8)), int(rng.integers(len(segs)))) for _ in range(3)]:
-        lo, hi = segs[s]
-        k = layer.kseg
-        say(f"[128k] check head {g} segment {s}")
-        Xhat = wo.normalise_rows(wo.bf16_to_f64(x.k[0, g, lo:hi]))
-        tl.check_assignment(Xhat, last[0, g, s * k:(s + 1) * k], tl.n_valid(k, hi - lo),
-                            labels[0, g, lo:hi] - s * k)
-        size, off, order = wo.finalise_segment(lo, labels[0, g, lo:hi] - s * k, k)
-        assert np.array_equal(idx.cluster_size[0, g, s * k:(s + 1) * k].cpu().numpy(), size)
-        assert np.array_equal(idx.cluster_offset[0, g, s * k:(s + 1) * k].cpu().numpy(), off)
-        assert np.array_equal(k_out[0, g, lo:hi], x.k[0, g, order])
+    picks = [(0, 0, 0), (0, 3, 7), (0, 7, nseg - 1)] + [
+        (0, int(rng.integers(8)), int(rng.integers(nseg))) for _ in range(3)]
+    say(f"[128k] check segments {picks}")
+    tl.check_segments(layer, idx, picks, objective_heads=[(0, 0), (0, 3), (0, 7)])
+    say("[128k] check one update step")
+    tl.check_update_step(layer, idx_prev, idx, picks)
     for s in range(2):
         L = layer.L0 + s + 1
         say(f"[128k] decode step {s}")
@@ -309,30 +306,27 @@ def test_full_size_sampled_parity(name):
     """The other full-size layers that bench.py times (1M tokens; batch 8 at 122 880; the
     Qwen-shaped batch 4 at 262 144 with seven query heads per KV head), launched as the bench
     launches them: three sampled (b, kv-head, segment) triples checked at the last pass and
-    through the finalise, and one decode step checked on four sampled (b, kv-head) pairs."""
+    through the finalise (labels, sizes, offsets, permuted rows, centroid means, value sums),
+    one update step there, the objective of one head over all its segments, and one decode
+    step checked on four sampled (b, kv-head) pairs."""
     w = synth.WORKLOADS[name]
     say(f"[{name}] generate")
     x = synth.generate_layer(w, rows=w.context + 1)
     layer = tl.Layer(x.k, x.v, w.context, w.segment_size, w.clusters_per_segment, w.n_iters,
                      w.n_sink, w.n_recent, w.n_q_heads)
+    say(f"[{name}] build with one pass fewer")
+    idx_prev = layer.build(T=w.n_iters - 1)
     say(f"[{name}] build")
     idx = layer.build()
-    segs = tl.segment_ranges(layer)
-    k = layer.kseg
+    nseg = layer.nseg
     rng = np.random.default_rng(11)
-    picks = [(0, 0, 0), (layer.B - 1, layer.H - 1, len(segs) - 1),
-             (int(rng.integers(layer.B)), int(rng.integers(layer.H)), int(rng.integers(len(segs))))]
-    for (b, g, s) in picks:
-        lo, hi = segs[s]
-        say(f"[{name}] check b {b} head {g} segment {s}")
-        labels = idx.labels[b, g, lo:hi].cpu().numpy() - s * k
-        Xhat = wo.normalise_rows(wo.bf16_to_f64(x.k[b, g, lo:hi]))
-        last = tl.to_np16(idx.last_centroids[b, g, s * k:(s + 1) * k])
-        tl.check_assignment(Xhat, last, tl.n_valid(k, hi - lo), labels)
-        size, off, order = wo.finalise_segment(lo, labels, k)
-        assert np.array_equal(idx.cluster_size[b, g, s * k:(s + 1) * k].cpu().numpy(), size)
-        assert np.array_equal(idx.cluster_offset[b, g, s * k:(s + 1) * k].cpu().numpy(), off)
-        assert np.array_equal(tl.to_np16(layer.k_out[b, g, lo:hi]), x.k[b, g, order])
+    picks = [(0, 0, 0), (layer.B - 1, layer.H - 1, nseg - 1),
+             (int(rng.integers(layer.B)), int(rng.integers(layer.H)), int(rng.integers(nseg)))]
+    say(f"[{name}] check segments {picks}")
+    tl.check_segments(layer, idx, picks, objective_heads=[picks[2][:2]])
+    say(f"[{name}] check one update step")
+    tl.check_update_step(layer, idx_prev, idx, picks)
+    del idx_prev
     say(f"[{name}] decode")
     L = layer.L0 + 1
     out, lse, sel = layer.decode(idx, x.q[0], L, w.n_retrieve)
@@ -343,20 +337,13 @@ def test_full_size_sampled_parity(name):
     say(f"[{name}] worst relative error {worst:.2e}")
 
 
-@pytest.mark.parametrize("prev_len", [20, 1041, 1100, 1700, 3000])
-def test_extension_equals_the_full_build(prev_len):
-    """An index built for prev_len tokens and extended to 3000 equals the index built for
-    3000 directly, bit for bit (clustering is segment-local and the build deterministic), and
-    so does the extended cache. prev_len 20 = n_sink + n_recent (an empty index); 1041 puts
-    the earlier indexed range on a segment boundary; 1100 and 1700 end it inside a segment
-    (rebuilt); 3000 extends by nothing. Two batch elements and KV heads exercise the cluster
-    and position strides, which differ between the two lengths."""
+def extend_and_check(full, idx_full, prev_len, n_q_steps=1, q=None):
+    """Build an index for prev_len tokens, extend it to full.L0 with the rows that the
+    extension documents as unread (before max(s0 S, n_sink)) overwritten with other data,
+    and check the result: bit for bit equal to the full build idx_full (index and cache), and
+    against the oracle on every segment (labels from the GPU's last centroids, sizes,
+    offsets, permuted rows, means, value sums) and on one decode step."""
     t = tl.torch()
-    rng = np.random.default_rng(17)
-    full, _ = tl.ragged_layer(rng, B=2, H=2, Hq=4, L0=3000, steps=2, S=512, kseg=32, T=3,
-                              n_sink=3, n_recent=17)
-    idx_full = full.build()
-    idx_full.objective = None
     prev = tl.Layer(full.k_np, full.v_np, prev_len, full.S, full.kseg, full.T, full.n_sink,
                     full.n_recent, full.Hq)
     idx_prev = prev.build()
@@ -364,8 +351,13 @@ def test_extension_equals_the_full_build(prev_len):
     idx_new.objective = None
     p = full.build_params()
     ws = t.empty(wi.wave_index_workspace_size(p), dtype=t.uint8, device="cuda")
-    wi.wave_index_extend(p, prev_len, full.k, full.v, prev.k_out, prev.v_out, idx_prev, idx_new,
-                         ws)
+    s0 = (prev_len - full.n_recent) // full.S
+    lim = max(s0 * full.S, full.n_sink)
+    k_in, v_in = full.k.clone(), full.v.clone()
+    k_in[:, :, :lim] = -k_in[:, :, :lim].flip(2)    # other data in the rows not read
+    v_in[:, :, :lim] = -v_in[:, :, :lim].flip(2)
+    say(f"[extend] prev_len={prev_len} s0={s0} rows not read [0, {lim})")
+    wi.wave_index_extend(p, prev_len, k_in, v_in, prev.k_out, prev.v_out, idx_prev, idx_new, ws)
     t.cuda.synchronize()
     for f in ("centroid_mean", "value_sum", "cluster_size", "cluster_offset", "labels", "perm",
               "last_centroids"):
@@ -375,6 +367,46 @@ def test_extension_equals_the_full_build(prev_len):
     L0 = full.L0
     assert t.equal(prev.k_out[:, :, :L0].view(t.int16), full.k_out[:, :, :L0].view(t.int16))
     assert t.equal(prev.v_out[:, :, :L0].view(t.int16), full.v_out[:, :, :L0].view(t.int16))
+    # against the oracle: the extended index and cache as a layer of L0 tokens
+    ext = tl.Layer.__new__(tl.Layer)
+    ext.__dict__.update(full.__dict__)
+    ext.k_out, ext.v_out = prev.k_out, prev.v_out
+    picks = [(b, g, s) for b in range(full.B) for g in range(full.H) for s in range(full.nseg)]
+    tl.check_segments(ext, idx_new, picks)
+    if q is not None:
+        L = L0 + 1
+        n_r = max(1, full.C // 20)
+        out, lse, sel = ext.decode(idx_new, q[0], L, n_r)
+        tl.oracle_decode_check(ext, idx_new, q[0], L, n_r, out, lse, sel)
+
+
+@pytest.mark.parametrize("prev_len", [20, 1041, 1100, 1700, 3000])
+def test_extension_equals_the_full_build_and_the_oracle(prev_len):
+    """An index built for prev_len tokens and extended to 3000 equals the index built for
+    3000 directly, bit for bit (clustering is segment-local and the build deterministic), and
+    so does the extended cache; the extended index matches the oracle. prev_len 20 =
+    n_sink + n_recent (an empty index); 1041 puts the earlier indexed range on a segment
+    boundary; 1100 and 1700 end it inside a segment (rebuilt); 3000 extends by nothing. Two
+    batch elements and KV heads exercise the cluster and position strides, which differ
+    between the two lengths."""
+    rng = np.random.default_rng(17)
+    full, q = tl.ragged_layer(rng, B=2, H=2, Hq=4, L0=3000, steps=2, S=512, kseg=32, T=3,
+                              n_sink=3, n_recent=17)
+    idx_full = full.build()
+    idx_full.objective = None
+    extend_and_check(full, idx_full, prev_len, q=q)
+
+
+def test_extension_by_nothing_without_a_steady_zone():
+    """n_sink = n_recent = 0 and an unchanged length that ends a segment: no segment is
+    rebuilt (the first one to build would be past the last); the call copies the earlier
+    index and still equals the full build."""
+    rng = np.random.default_rng(23)
+    full, q = tl.ragged_layer(rng, B=1, H=2, Hq=4, L0=1024, steps=1, S=512, kseg=16, T=2,
+                              n_sink=0, n_recent=0)
+    idx_full = full.build()
+    idx_full.objective = None
+    extend_and_check(full, idx_full, 1024, q=q)
 
 
 def test_extension_with_tiled_assignment():

@@ -6,7 +6,9 @@ the oracle with itself: the expected values come from hand arithmetic, from a li
 mathematics (Jensen's inequality, spherical k-means monotonicity) or from brute force on
 tiny inputs.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -71,78 +73,54 @@ def test_round_bf16_is_single_rounding_from_fp64():
 
 
 # ------------------------------------------------------------------------------------------
-# Hand-worked example (d = 4): every number below was derived by hand; see the comments.
+# Hand-worked example (d = 4): inputs and every expected value, with the derivation, are in
+# tests/golden/hand_worked_d4.json (derived by hand from the method's definitions; the pages
+# print no numeric example).
 # ------------------------------------------------------------------------------------------
-#
-# L0 = 10, one sink (position 0), one recent token (position 9), one segment (S = 16) whose
-# indexed points are positions 1..8, k_seg = 2 clusters, T = 2 passes.
-# Seeds sit at stride floor(8/2) = 4: local points 0 and 4 = positions 1 and 5, i.e. the unit
-# vectors e1 and e2.
-# Pass 1 (cosine with e1 / e2):
-#   pos1 (1,0,0,0): 1 / 0 -> 0        pos2 (3,4,0,0): .6 / .8 -> 1
-#   pos3 (4,3,0,0): .8 / .6 -> 0      pos4 (2,0,0,0): 1 / 0 -> 0
-#   pos5 (0,1,0,0): 0 / 1 -> 1        pos6 (0,2,0,0): 0 / 1 -> 1
-#   pos7 (1,1,0,0): s / s -> TIE -> 0 (lowest id)      pos8 (0,3,0,4): 0 / .6 -> 1
-# Update: u_0 = e1 + (.8,.6) + e1 + (s,s) = (2.8+s, .6+s, 0, 0), ||u_0|| = 3.74276984...
-#         u_1 = (.6,.8) + e2 + e2 + (0,.6,0,.8) = (.6, 3.4, 0, .8), ||u_1|| = sqrt(12.56)
-#   mu_0 = (.93703512, .34923515, 0, 0) -> bf16 (240/256, 179/512, 0, 0)
-#   mu_1 = (.16929979, .95936550, 0, .22573306) -> bf16 (173/1024, 246/256, 0, 231/1024)
-# Pass 2 keeps every label (e.g. pos2: .842188 vs .870117; pos7: .910124 vs .798948), so the
-# final labels equal pass 1's, last_centroids = mu^(1), and J = ||u_0|| + ||u_1||.
-# Statistics: cluster 0 = positions {1,3,4,7}: mean key (8,4,0,0)/4 = (2,1,0,0);
-#             cluster 1 = positions {2,5,6,8}: mean key (3,10,0,4)/4 = (.75,2.5,0,1).
-# With V[p] = (p, 1, 0, -1): value sums (15,4,0,-4) and (21,4,0,-4).
-# Layout: slots 1..4 hold positions 1,3,4,7 (cluster 0), slots 5..8 hold 2,5,6,8 (cluster 1).
-#
-# Decode at L = 11 (token 10 appended), q = (1,0,0,0), scale 1/sqrt(4) = 0.5, n_r = 1:
-#   s_0 = .5 * 2 = 1, s_1 = .5 * .75 = .375 -> cluster 0 retrieved, cluster 1 estimated.
-#   exact logits: pos0 (0,0,0,1) -> 0, pos9 (0,1,1,0) -> 0, pos10 (-2,0,0,0) -> -1,
-#                 members pos1 -> .5, pos3 -> 2, pos4 -> 1, pos7 -> .5
-#   estimate: numerator e^.375 * (21,4,0,-4), denominator 4 e^.375
-#   out = (4.143251575005814, 1, 0, -1); lse = 3.072351847528056
-#   (exact attention over all 11 tokens gives out_0 = 3.735741576864432, lse 3.146492167457256;
-#    the wave estimate's lse is lower, as Jensen's inequality requires.)
 
-S2 = 1 / math.sqrt(2)
-GOLD_K = np.array([[0, 0, 0, 1], [1, 0, 0, 0], [3, 4, 0, 0], [4, 3, 0, 0], [2, 0, 0, 0],
-                   [0, 1, 0, 0], [0, 2, 0, 0], [1, 1, 0, 0], [0, 3, 0, 4], [0, 1, 1, 0],
-                   [-2, 0, 0, 0]], dtype=np.float64)
-GOLD_V = np.array([[p, 1, 0, -1] for p in range(11)], dtype=np.float64)
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked_d4.json")))
+GOLD_K = np.array(GOLD["inputs"]["K"], dtype=np.float64)
+GOLD_V = np.array(GOLD["inputs"]["V"], dtype=np.float64)
+GX = GOLD["expected"]
 
 
 def golden_index():
-    return wo.build_head(bits(GOLD_K), bits(GOLD_V), L0=10, S=16, k_seg=2, n_iters=2,
-                         n_sink=1, n_recent=1)
+    i = GOLD["inputs"]
+    L0 = i["L0"]
+    return wo.build_head(bits(GOLD_K), bits(GOLD_V), L0=L0, S=i["S"], k_seg=i["k_seg"],
+                         n_iters=i["n_iters"], n_sink=i["n_sink"], n_recent=i["n_recent"])
 
 
 def test_golden_build():
     idx, K_out, V_out = golden_index()
-    assert idx.labels.tolist() == [-1, 0, 1, 0, 0, 1, 1, 0, 1, -1]
-    assert idx.size.tolist() == [4, 4]
-    assert idx.offset.tolist() == [1, 5]
-    assert idx.perm.tolist() == [0, 1, 3, 4, 7, 2, 5, 6, 8, 9]
-    assert np.array_equal(vals(idx.centroid_mean), [[2, 1, 0, 0], [0.75, 2.5, 0, 1]])
-    assert np.array_equal(vals(idx.value_sum), [[15, 4, 0, -4], [21, 4, 0, -4]])
-    assert np.array_equal(vals(idx.last_centroids),
-                          [[240 / 256, 179 / 512, 0, 0], [173 / 1024, 246 / 256, 0, 231 / 1024]])
-    assert idx.objective[0] == pytest.approx(3.7427698449234788 + math.sqrt(12.56), rel=1e-13)
-    assert np.array_equal(K_out, bits(GOLD_K[[0, 1, 3, 4, 7, 2, 5, 6, 8, 9]]))
-    assert np.array_equal(V_out, bits(GOLD_V[[0, 1, 3, 4, 7, 2, 5, 6, 8, 9]]))
+    assert idx.labels.tolist() == GX["labels"]
+    assert idx.size.tolist() == GX["size"]
+    assert idx.offset.tolist() == GX["offset"]
+    assert idx.perm.tolist() == GX["perm"]
+    assert np.array_equal(vals(idx.centroid_mean), GX["centroid_mean"])
+    assert np.array_equal(vals(idx.value_sum), GX["value_sum"])
+    assert np.array_equal(vals(idx.last_centroids), GX["last_centroids"])
+    assert idx.objective[0] == pytest.approx(GX["objective"], rel=1e-13)
+    assert np.array_equal(K_out, bits(GOLD_K[GX["perm"]]))
+    assert np.array_equal(V_out, bits(GOLD_V[GX["perm"]]))
 
 
 def test_golden_decode():
     idx, K_out, V_out = golden_index()
-    Kc = np.concatenate([K_out, bits(GOLD_K[10:])])
-    Vc = np.concatenate([V_out, bits(GOLD_V[10:])])
-    r = wo.decode_group(bits([[1, 0, 0, 0]]), Kc, Vc, idx, L0=10, L=11, n_sink=1, n_recent=1,
-                        n_retrieve=1)
-    assert r.selected.tolist() == [0]
-    assert r.score[0].tolist() == [1.0, 0.375]
-    assert r.out[0] == pytest.approx([4.143251575005814, 1.0, 0.0, -1.0], rel=1e-13, abs=1e-13)
-    assert r.lse[0] == pytest.approx(3.072351847528056, rel=1e-13)
-    full, lse_full = wo.full_attention(bits([[1, 0, 0, 0]]), Kc, Vc, 11)
-    assert full[0, 0] == pytest.approx(3.735741576864432, rel=1e-13)
-    assert lse_full[0] == pytest.approx(3.146492167457256, rel=1e-13)
+    i = GOLD["inputs"]
+    L0, dec = i["L0"], i["decode"]
+    Kc = np.concatenate([K_out, bits(GOLD_K[L0:])])
+    Vc = np.concatenate([V_out, bits(GOLD_V[L0:])])
+    q = bits(dec["q"])
+    r = wo.decode_group(q, Kc, Vc, idx, L0=L0, L=dec["L"], n_sink=i["n_sink"],
+                        n_recent=i["n_recent"], n_retrieve=dec["n_retrieve"])
+    assert r.selected.tolist() == GX["selected"]
+    assert r.score[0].tolist() == GX["score"]
+    assert r.out[0] == pytest.approx(GX["out"], rel=1e-13, abs=1e-13)
+    assert r.lse[0] == pytest.approx(GX["lse"], rel=1e-13)
+    full, lse_full = wo.full_attention(q, Kc, Vc, dec["L"])
+    assert full[0, 0] == pytest.approx(GX["full_out_0"], rel=1e-13)
+    assert lse_full[0] == pytest.approx(GX["full_lse"], rel=1e-13)
 
 
 # ------------------------------------------------------------------------------------------
@@ -284,6 +262,84 @@ def test_batch_elements_are_independent():
     Vc1 = np.concatenate([lay1.v_out, V[1:, :, 100:]], axis=2)
     out1, lse1, _, _ = wo.decode_layer(q[1:], Kc1, Vc1, lay1, 100, 102, 1, 2, 3)
     assert np.array_equal(out[1], out1[0]) and np.array_equal(lse[1], lse1[0])
+
+
+def gqa_case(rng, B=2, H=2, G=3, L0=150, steps=2, d=8):
+    """Distinct keys / values per (b, kv-head) (so mixing heads changes every result)."""
+    L = L0 + steps
+    K = np.empty((B, H, L, d), np.uint16)
+    V = np.empty((B, H, L, d), np.uint16)
+    for b in range(B):
+        for g in range(H):
+            K[b, g], V[b, g], _ = random_case(rng, L0=L0, d=d, G=1, steps=steps)
+    q = bits(rng.standard_normal((B, H * G, d)) * 1.5)
+    return K, V, q
+
+
+def gqa_reference(q, K, V, L):
+    """torch's fp64 SDPA with its own grouped-query mapping (query head h reads KV head
+    h // G), and the log-sum-exp of the same logits by torch.logsumexp."""
+    Q = torch.from_numpy(vals(q))[:, :, None, :]                  # [B, Hq, 1, d]
+    Kt = torch.from_numpy(vals(K[:, :, :L]))                      # [B, Hkv, L, d]
+    Vt = torch.from_numpy(vals(V[:, :, :L]))
+    o = torch.nn.functional.scaled_dot_product_attention(Q, Kt, Vt, enable_gqa=True)
+    G = q.shape[1] // K.shape[1]
+    Ke = Kt.repeat_interleave(G, dim=1)
+    logits = (Q @ Ke.transpose(-1, -2))[:, :, 0, :] / math.sqrt(q.shape[2])
+    return o[:, :, 0].numpy(), torch.logsumexp(logits, dim=-1).numpy()
+
+
+@pytest.mark.parametrize("mode", ["retrieve_all", "singletons"])
+def test_layer_drivers_group_query_heads_by_kv_head(mode):
+    """Whole-layer build and decode with B = 2, Hkv = 2, G = 3: query head h uses KV head
+    h // G (the GQA convention; torch's SDPA with enable_gqa fixes it independently). With
+    every cluster retrieved, or with singleton clusters (exact estimate) at budgets 0 and 3,
+    the layer's output and lse equal exact grouped attention over the original cache."""
+    rng = np.random.default_rng(31)
+    B, H, G, L0, steps = 2, 2, 3, 150, 2
+    K, V, q = gqa_case(rng, B, H, G, L0, steps)
+    L = L0 + steps
+    if mode == "retrieve_all":
+        lay = wo.build_layer(K, V, L0, 64, 6, 3, 2, 5)
+        budgets = [10 ** 6]
+    else:
+        lay = wo.build_layer(K, V, L0, 32, 32, 2, 2, 5)
+        budgets = [0, 3]
+    Kc = np.concatenate([lay.k_out, K[:, :, L0:]], axis=2)
+    Vc = np.concatenate([lay.v_out, V[:, :, L0:]], axis=2)
+    ref, ref_lse = gqa_reference(q, K, V, L)
+    for n_r in budgets:
+        out, lse, sel, shat = wo.decode_layer(q, Kc, Vc, lay, L0, L, 2, 5, n_r)
+        assert out.shape == (B, H * G, 8) and shat.shape[:2] == (B, H)
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+    # each (b, kv-head)'s permuted cache holds exactly that head's own rows
+    for b in range(B):
+        for g in range(H):
+            got = sorted(map(bytes, lay.k_out[b, g]))
+            assert got == sorted(map(bytes, K[b, g, :L0]))
+            assert lay.stacked("size")[b, g].sum() == L0 - 7
+
+
+def test_layer_decode_ranks_by_each_groups_own_heads():
+    """Swapping the two query-head groups of a layer swaps the retrieval sets of the two KV
+    heads' decodes only through their own keys: decoding group 1's queries against KV head 0
+    (a layer with the KV heads swapped) gives KV head 0's selection of the swapped layer."""
+    rng = np.random.default_rng(37)
+    B, H, G, L0 = 1, 2, 3, 150
+    K, V, q = gqa_case(rng, B, H, G, L0, 1)
+    lay = wo.build_layer(K, V, L0, 64, 8, 3, 2, 5)
+    Kc = np.concatenate([lay.k_out, K[:, :, L0:]], axis=2)
+    Vc = np.concatenate([lay.v_out, V[:, :, L0:]], axis=2)
+    out, lse, sel, _ = wo.decode_layer(q, Kc, Vc, lay, L0, L0 + 1, 2, 5, 4)
+    Ks, Vs = K[:, ::-1].copy(), V[:, ::-1].copy()
+    qs = np.concatenate([q[:, G:], q[:, :G]], axis=1)
+    lay_s = wo.build_layer(Ks, Vs, L0, 64, 8, 3, 2, 5)
+    Kcs = np.concatenate([lay_s.k_out, Ks[:, :, L0:]], axis=2)
+    Vcs = np.concatenate([lay_s.v_out, Vs[:, :, L0:]], axis=2)
+    out_s, lse_s, sel_s, _ = wo.decode_layer(qs, Kcs, Vcs, lay_s, L0, L0 + 1, 2, 5, 4)
+    assert np.array_equal(sel_s[0][0], sel[0][1]) and np.array_equal(sel_s[0][1], sel[0][0])
+    assert np.array_equal(out_s[0, :G], out[0, G:]) and np.array_equal(lse_s[0, G:], lse[0, :G])
 
 
 # ------------------------------------------------------------------------------------------

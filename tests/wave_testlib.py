@@ -222,3 +222,63 @@ def n_valid(kseg: int, n: int) -> int:
 
 def sqrt_d() -> float:
     return math.sqrt(128)
+
+
+def check_segments(layer: Layer, idx: wi.IndexTensors, picks, objective_heads=()):
+    """Index parity on sampled segments and heads, given the GPU's own labels.
+
+    For each (b, g, s) in picks: labels = the oracle's assignment from the GPU's last
+    centroids (ties within 1e-4); sizes, offsets and permuted K / V rows bit-exact; centroid
+    means and value sums within 1 bf16 ulp (bf16_close). For each (b, g) in objective_heads:
+    the GPU objective equals the oracle's J of the GPU labels over every segment of the head
+    (1e-4 relative). Works segment by segment, so that it stays cheap at 1M tokens."""
+    segs = segment_ranges(layer)
+    k = layer.kseg
+    labels_all = idx.labels.cpu().numpy()
+    for (b, g, s) in picks:
+        lo, hi = segs[s]
+        c0, c1 = s * k, (s + 1) * k
+        loc = labels_all[b, g, lo:hi] - c0
+        Kseg = wo.bf16_to_f64(layer.k_np[b, g, lo:hi])
+        Vseg = wo.bf16_to_f64(layer.v_np[b, g, lo:hi])
+        Xhat = wo.normalise_rows(Kseg)
+        last = to_np16(idx.last_centroids[b, g, c0:c1])
+        check_assignment(Xhat, last, n_valid(k, hi - lo), loc)
+        size, off, order = wo.finalise_segment(lo, loc, k)
+        assert np.array_equal(idx.cluster_size[b, g, c0:c1].cpu().numpy(), size), (b, g, s)
+        assert np.array_equal(idx.cluster_offset[b, g, c0:c1].cpu().numpy(), off), (b, g, s)
+        if hi > lo:
+            assert np.array_equal(to_np16(layer.k_out[b, g, lo:hi]), layer.k_np[b, g, order])
+            assert np.array_equal(to_np16(layer.v_out[b, g, lo:hi]), layer.v_np[b, g, order])
+        cm, vs = wo.cluster_stats(Kseg, Vseg, 0, loc, k)
+        assert bf16_close(to_np16(idx.centroid_mean[b, g, c0:c1]), cm) <= 1, (b, g, s)
+        assert bf16_close(to_np16(idx.value_sum[b, g, c0:c1]), vs) <= 1, (b, g, s)
+    if objective_heads:
+        obj = idx.objective.cpu().numpy()
+        for (b, g) in objective_heads:
+            J = 0.0
+            for s, (lo, hi) in enumerate(segs):
+                loc = labels_all[b, g, lo:hi] - s * k
+                Xhat = wo.normalise_rows(wo.bf16_to_f64(layer.k_np[b, g, lo:hi]))
+                J += wo.kmeans_objective(wo.kmeans_cluster_sums(Xhat, loc, k))
+            assert abs(obj[b, g] - J) <= 1e-4 * abs(J), (b, g, obj[b, g], J)
+
+
+def check_update_step(layer: Layer, idx_prev: wi.IndexTensors, idx_next: wi.IndexTensors,
+                      picks):
+    """One k-means update at full size: idx_prev was built with T - 1 passes and idx_next
+    with T. The unit centroids of idx_next's last pass (mu^(T-1)) must equal the oracle's
+    update of the (T-1)-th pass's labels (idx_prev.labels) from the centroids that pass used
+    (idx_prev.last_centroids, mu^(T-2)), within 1 bf16 ulp, on the sampled (b, g, s)."""
+    segs = segment_ranges(layer)
+    k = layer.kseg
+    for (b, g, s) in picks:
+        lo, hi = segs[s]
+        c0, c1 = s * k, (s + 1) * k
+        loc = idx_prev.labels[b, g, lo:hi].cpu().numpy() - c0
+        Xhat = wo.normalise_rows(wo.bf16_to_f64(layer.k_np[b, g, lo:hi]))
+        mu_prev = to_np16(idx_prev.last_centroids[b, g, c0:c1])
+        u = wo.kmeans_cluster_sums(Xhat, loc, k)
+        ref = wo.kmeans_update(u, np.bincount(loc, minlength=k), mu_prev)
+        got = to_np16(idx_next.last_centroids[b, g, c0:c1])
+        assert bf16_close(got, ref) <= 1, (b, g, s)
