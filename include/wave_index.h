@@ -185,6 +185,24 @@ wave_status wave_decode_attention(const wave_decode_params* p, const void* q,
                                   int32_t* selected, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
+/* Bytes of the library's own decode scratch used by wave_decode_attention_noalloc. */
+#define WAVE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* wave_decode_attention for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same step with
+ * the workspace taken from a scratch array of WAVE_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on, from the code object's load until the process
+ * ends. The call allocates nothing. Arguments as for wave_decode_attention without the
+ * workspace; WAVE_ERR_WORKSPACE when the parameters need more than
+ * WAVE_NOALLOC_SCRATCH_BYTES of workspace (wave_decode_workspace_size reports it), checked
+ * before anything is enqueued. Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and must not be
+ * made; calls on different GPUs do not interfere. */
+wave_status wave_decode_attention_noalloc(const wave_decode_params* p, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          const wave_index* idx, float* out, float* lse,
+                                          int32_t* selected, hipStream_t stream);
+
 /* Dense decode attention over all L rows (the "full attention" the summaries compare
  * against, section 4). Same parameters; the index fields of p are ignored. */
 wave_status wave_dense_decode_attention(const wave_decode_params* p, const void* q,

@@ -20,15 +20,16 @@ __all__ = [
     "wave_status_string", "wave_index_workspace_size", "wave_index_build", "wave_index_extend",
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
     "IndexTensors", "alloc_index", "EXPORTED_SYMBOLS", "LIB_PATH", "wave_trace",
-    "alloc_decode_workspace",
+    "alloc_decode_workspace", "wave_decode_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libwave_index.so")
 EXPORTED_SYMBOLS = (
     "wave_status_string", "wave_index_workspace_size", "wave_index_build", "wave_index_extend",
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
-    "wave_index_build_traced", "wave_decode_attention_traced",
+    "wave_index_build_traced", "wave_decode_attention_traced", "wave_decode_attention_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20   # WAVE_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "WAVE_OK", 1: "WAVE_ERR_INVALID_ARG", 2: "WAVE_ERR_UNSUPPORTED",
           3: "WAVE_ERR_WORKSPACE", 4: "WAVE_ERR_ALIAS", 5: "WAVE_ERR_HIP"}
 
@@ -95,6 +96,8 @@ def library() -> ctypes.CDLL:
                                               vp, vp, vp, vp, sz, vp]
         lib.wave_dense_decode_attention.argtypes = [P(wave_decode_params), vp, vp, vp, vp, vp,
                                                     vp, sz, vp]
+        lib.wave_decode_attention_noalloc.argtypes = [P(wave_decode_params), vp, vp, vp,
+                                                      P(wave_index), vp, vp, vp, vp]
         lib.wave_index_build_traced.argtypes = lib.wave_index_build.argtypes + [P(wave_trace)]
         lib.wave_decode_attention_traced.argtypes = (lib.wave_decode_attention.argtypes
                                                      + [P(wave_trace)])
@@ -227,6 +230,17 @@ def wave_decode_attention(p: wave_decode_params, q, k_cache, v_cache, index: Ind
     _check("wave_decode_attention_traced",
            library().wave_decode_attention_traced(*args, ctypes.byref(tr)))
     return tr.recorded
+
+
+def wave_decode_attention_noalloc(p: wave_decode_params, q, k_cache, v_cache,
+                                  index: IndexTensors, out, lse=None, selected=None,
+                                  stream=None) -> None:
+    """Enqueue one decode step that allocates nothing: the workspace is the library's own
+    per-GPU scratch (see wave_decode_attention_noalloc in include/wave_index.h)."""
+    idx = index.c_struct()
+    _check("wave_decode_attention_noalloc", library().wave_decode_attention_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(idx), _ptr(out),
+        _ptr(lse), _ptr(selected), _stream(stream)))
 
 
 def wave_dense_decode_attention(p: wave_decode_params, q, k_cache, v_cache, out, lse=None,

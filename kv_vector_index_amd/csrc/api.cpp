@@ -10,6 +10,9 @@
 
 #include "wave_kernels.h"
 
+static_assert(wave::kNoAllocScratchBytes == WAVE_NOALLOC_SCRATCH_BYTES,
+              "the scratch size in the header and in the library agree");
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -485,6 +488,21 @@ wave_status wave_decode_attention_traced(const wave_decode_params* p, const void
                                      workspace_bytes, stream, &tr);
   trace->recorded = tr.n;
   return st;
+}
+
+wave_status wave_decode_attention_noalloc(const wave_decode_params* p, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          const wave_index* idx, float* out, float* lse,
+                                          int32_t* selected, hipStream_t stream) {
+  DecodeShape sh;
+  wave_status st = check_decode(p, &sh);
+  if (st != WAVE_OK) return st;
+  const size_t need = layout_decode(p, sh, nullptr, nullptr);
+  if (need > wave::kNoAllocScratchBytes) return WAVE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (wave::noalloc_scratch(&ws) != hipSuccess) return WAVE_ERR_HIP;
+  return decode_impl(p, q, k_cache, v_cache, idx, out, lse, selected, ws, need, stream,
+                     nullptr);
 }
 
 wave_status wave_dense_decode_attention(const wave_decode_params* p, const void* q,

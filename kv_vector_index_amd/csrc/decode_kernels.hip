@@ -35,6 +35,8 @@
 // each K/V row is shared by the G query heads of its group.
 #include <float.h>
 
+#include <mutex>
+
 #include <type_traits>
 
 #include "wave_common.h"
@@ -1972,6 +1974,35 @@ static hipError_t launch_dense_g(const DecodeArgs& a, hipStream_t s, Tracer* tr)
     case 8: return FN<8>(A, S, T);            \
     default: return hipErrorInvalidValue;     \
   }
+
+// ------------------------------------------------------------------------------------
+// scratch of the allocation-free decode entry point
+// ------------------------------------------------------------------------------------
+// One copy per GPU, allocated when the code object is loaded on that device and kept until
+// the process ends. In host code the name stands for a host-side stand-in, not a device
+// address: host code only ever uses the address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   WAVE_DISPATCH_G(launch_decode_g, a, s, tr)

@@ -102,6 +102,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
 // Enqueue dense decode over [0, L): split-K partials (part, nB per head) + merge.
 hipError_t launch_dense_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
 
+// The library's own decode scratch on the current device (a static device array, one copy
+// per GPU, kept until the process ends), for callers that cannot allocate: its address,
+// looked up once per device. Calls that use it on one GPU must not overlap.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // ---------------------------------------------------------------- build
 struct BuildArgs {
   const uint16_t* k;       // [B, Hkv, Lcap, d]

@@ -161,3 +161,19 @@ def test_decode_rejects_null_small_workspace_and_aliasing_before_any_launch():
     dense = lib.wave_dense_decode_attention
     assert dense(ctypes.byref(p), Q, K, V, None, None, WS, ws, None) == 1
     assert dense(ctypes.byref(p), Q, K, V, OUT, None, None, ws, None) == 3
+
+
+def test_noalloc_decode_rejects_a_problem_larger_than_its_scratch_before_any_launch():
+    """The allocation-free entry point checks its fixed scratch size on the host: a problem
+    whose workspace exceeds it is refused (WAVE_ERR_WORKSPACE) before anything is enqueued,
+    and argument errors come first."""
+    lib = wi.library()
+    big = decode_params(batch=64, n_clusters=65536, index_len=1 << 20, seq_len=(1 << 20) + 1,
+                        kv_capacity=(1 << 20) + 16, n_retrieve=1180)
+    assert wi.wave_decode_workspace_size(big) > wi.NOALLOC_SCRATCH_BYTES
+    Q, K, V, OUT = 1 << 40, 2 << 40, 3 << 40, 4 << 40
+    idx = wi.wave_index(6 << 40, 7 << 40, 8 << 40, 9 << 40, None, None, None, None)
+    call = lib.wave_decode_attention_noalloc
+    assert call(ctypes.byref(big), Q, K, V, ctypes.byref(idx), OUT, None, None, None) == 3
+    bad = decode_params(n_retrieve=-1)
+    assert call(ctypes.byref(bad), Q, K, V, ctypes.byref(idx), OUT, None, None, None) == 1
