@@ -107,7 +107,7 @@ size_t layout_build(const wave_build_params* p, const BuildShape& sh, void* base
 // ---------------------------------------------------------------- decode
 
 struct DecodeShape {
-  int G, nS, nSW, nEW, nEC, nStMax, nH, nB, nG, nBDense, rcap;
+  int G, nS, nSW, nEW, nStMax, nH, nB, nG, nBDense, rcap;
   int64_t BH, cache_elems;
 };
 
@@ -153,10 +153,8 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
                       wave::kRowsPerItem, 1, nb_cap);
   // score / estimate workgroups: a few per CU over all (b, kv-heads), looping over chunks
   sh->nSW = clampi(wave::kScoreWGPerCall / bh, 1, sh->nS);
-  // estimate workgroups: two chunks each for groups of four heads (the second staged in
-  // LDS), else one
-  sh->nEC = G == 4 ? 2 : 1;
-  sh->nEW = (sh->nS + sh->nEC - 1) / sh->nEC;
+  // estimate workgroups: kEstChunks chunks each
+  sh->nEW = (sh->nS + wave::kEstChunks - 1) / wave::kEstChunks;
   // retrieve merge groups: one merge of all partials for up to two groups' worth, else
   // groups of about kMergeGroup and a second level
   sh->nG = sh->nB <= 2 * wave::kMergeGroup
@@ -457,7 +455,6 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   a.nSt = (int)((n_steady + wave::kTokChunk - 1) / wave::kTokChunk);
   a.nSW = sh.nSW;
   a.nEW = sh.nEW;
-  a.nEC = sh.nEC;
   a.nH = sh.nH;
   a.hist_kernel = sh.nS * wave::kChunk > wave::kLocalSelectMax ? 1 : 0;
   a.nB = sh.nB;

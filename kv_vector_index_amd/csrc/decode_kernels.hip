@@ -298,8 +298,7 @@ __device__ __forceinline__ float4 part_ld4(const float* p) {
 // first half (M in log2 units, o unnormalised).
 template <int G, bool DEV, int MB, typename Emit>
 __device__ __forceinline__ void merge_block(const float* parts, int p0, int step, int n,
-                                            Emit emit) {
-  __shared__ float xh[128][6];
+                                            float (*xh)[6], Emit emit) {
   const int tid = threadIdx.x, half = tid >> 7, item = tid & 127;
   for (int it0 = 0; it0 < G * 32; it0 += 128) {
     const int it = it0 + item;
@@ -804,17 +803,6 @@ struct FinShared {
   uint32_t base[2];
 };
 
-// LDS of an estimate workgroup's second chunk (groups of four heads), staged by direct
-// global-to-LDS loads: the value sums in the register layout of the first chunk (per wave
-// and step, 4 rows x 256 B, lane l at byte 16 l), then the clusters' four logits and sizes
-// (waves 0-1 fill the first copy, waves 2-3 a second one that is not read: every wave issues
-// the same loads, so none of them sits behind a branch).
-struct EstStage {
-  uint32_t rows[kChunk * kHeadDim / 2];  // 128 rows x 256 B
-  float logit[2][kChunk][4];
-  int32_t size[2][kChunk];
-};
-
 // The cut of a (b, kv-head) of more than kLocalSelectMax clusters: need = min(n_r, finite
 // scores) and the histogram bin b* that holds the need-th largest score (b* = kHistBins when
 // need = 0), from the histogram kernel's histogram of all the head's scores. Every selection
@@ -1099,6 +1087,10 @@ __device__ __forceinline__ void publish_selection(const DecodeArgs& a, int bh, F
   uint32_t V;
   uint32_t pos = scan_excl<NT>(tok, sh.tmp, &V);
   const int nB = a.nB;
+  // retrieve workgroup wi takes virtual rows [wi span, (wi + 1) span) (clipped to V): whole
+  // steps of its four waves
+  constexpr uint32_t kStep = kRetBlock * (kDecThreads / 64);
+  const uint32_t span = kStep * max(1u, (V + kStep * nB - 1) / (kStep * nB));
   auto emit = [&](uint32_t r, int j, int32_t n, int32_t co) {
     const uint32_t te = pos + (uint32_t)n + 1u;
     if (!long_list) sid[r] = j;
@@ -1106,8 +1098,8 @@ __device__ __forceinline__ void publish_selection(const DecodeArgs& a, int bh, F
     sts[r] = (int32_t)pos;
     sco[r] = co;
     // retrieve workgroups whose first virtual row falls in [pos, te)
-    const int w0 = (int)(((uint64_t)pos * nB + V - 1) / V);
-    const int w1 = (int)(((uint64_t)te * nB + V - 1) / V);
+    const int w0 = (int)((pos + span - 1) / span);
+    const int w1 = (int)((te + span - 1) / span);
     for (int wi = w0; wi < w1; ++wi) sh.wgr[wi] = (int32_t)r;
     pos = te;
   };
@@ -1127,11 +1119,12 @@ __device__ __forceinline__ void publish_selection(const DecodeArgs& a, int bh, F
   __syncthreads();
   // per retrieve workgroup: its virtual rows [T0, T1) and listed clusters [r_lo, r_hi)
   for (int wi = tid; wi < nB; wi += NT) {
-    const int T0 = (int)((uint64_t)V * wi / nB), T1 = (int)((uint64_t)V * (wi + 1) / nB);
+    const int T0 = (int)min((uint64_t)V, (uint64_t)span * wi);
+    const int T1 = (int)min((uint64_t)V, (uint64_t)span * (wi + 1));
     int lo = 0, hi = 0;
     if (T0 < T1) {
       lo = sh.wgr[wi];
-      hi = wi + 1 < nB ? min((int)nsel, sh.wgr[wi + 1] + 1) : (int)nsel;
+      hi = T1 < (int)V ? min((int)nsel, sh.wgr[wi + 1] + 1) : (int)nsel;
     }
     reinterpret_cast<int4*>(a.wg_info)[(size_t)bh * kMaxRetrieveWG + wi] = make_int4(T0, T1, lo, hi);
   }
@@ -1455,6 +1448,158 @@ __device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinSha
   publish_selection(a, bh, sh);
 }
 
+// ------------------------------------------------------------------------------------
+// estimate: every non-empty cluster's centroid term, on the matrix cores
+// ------------------------------------------------------------------------------------
+// A workgroup folds kEstChunks chunks of 128 clusters of one (b, kv-head) into one partial
+// state; wave w takes clusters 32 w .. 32 w + 31 of each chunk, one K step of
+// v_mfma_f32_16x16x32_bf16 per 16 output dims. The product is O[r][dim] = sum_j P[r][j]
+// V[j][dim] over the value sums V (exact in bf16): row r < G holds bf16(p) of head r's weight
+// p = 2^(s_j - m) (s_j the head's log2-domain logit, m the wave's largest), row G + r holds
+// bf16(p - bf16(p)), so that their fp32 sum carries p to about 2^-17 relative; rows from 2G
+// are zero. The denominator sum_j n_j p is summed in fp32 from the unrounded p. Lane l holds
+// the A operand of row l % 16 and the B operand of dim l % 16, both for the clusters
+// 8 (l / 16) .. + 7 of its K step. The value-sum rows reach LDS by direct global-to-LDS
+// loads: block e of a wave holds the wave's clusters 8 g + e in slot g (g = 0..3), each row
+// rotated by 2 g 16-byte chunks, so that the operand reads (the 16 lanes of a slot read 32
+// bytes of one row, the four slots of a block the same dims) fall in distinct LDS banks.
+struct EstLds {
+  uint32_t rows[kEstChunks][kDecThreads / 64][8][4][64];  // [chunk][wave][e][slot][256 B]
+};
+struct EstMerge {  // the same LDS after the products: each wave's rows and (m, l) per head
+  float o[kDecThreads / 64][2 * kMaxGroup][kHeadDim];
+  float m[kDecThreads / 64][kMaxGroup], l[kDecThreads / 64][kMaxGroup];
+};
+
+template <int G>
+__device__ __forceinline__ void estimate_mfma(const DecodeArgs& a, int bh, int e, EstLds& st,
+                                              float* __restrict__ dst) {
+  static_assert(2 * G <= 16, "hi and lo rows of every head in one 16-row tile");
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
+  const size_t base = (size_t)bh * a.C;
+  const bool arow = n < 2 * G;
+  const int hrow = n < G ? n : (arow ? n - G : 0);  // the head of this lane's A row
+  // logits and sizes of this lane's clusters (issued first: they are needed first)
+  float sv[kEstChunks][8];
+  float nv[kEstChunks][8];
+#pragma unroll
+  for (int c = 0; c < kEstChunks; ++c) {
+    const int j0 = (e * kEstChunks + c) * kChunk + 32 * w + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + i;
+      const int jc = min(j, a.C - 1);
+      const float s = a.scores[(base + jc) * G + hrow];
+      const int32_t cnt = a.csize[base + jc];
+      const bool ok = arow && j < a.C && cnt > 0;
+      sv[c][i] = ok ? s : kNegInf;
+      nv[c][i] = ok ? (float)cnt : 0.f;
+    }
+  }
+  // the value-sum rows of the wave's clusters: one direct load of four rows per block
+  {
+    const int slot = lane >> 4, pos = lane & 15, cidx = (pos - 2 * slot) & 15;
+#pragma unroll
+    for (int c = 0; c < kEstChunks; ++c) {
+#pragma unroll
+      for (int ei = 0; ei < 8; ++ei) {
+        const int j = (e * kEstChunks + c) * kChunk + 32 * w + 8 * slot + ei;
+        const size_t row = base + min(j, a.C - 1);
+        __builtin_amdgcn_global_load_lds(a.vsum + row * kHeadDim + cidx * 8,
+                                         (lds_ptr)&st.rows[c][w][ei][0][0], 16, 0, 0);
+      }
+    }
+  }
+  // the wave's largest logit per head (lanes of rows h and G + h hold the same)
+  float mx = kNegInf;
+#pragma unroll
+  for (int c = 0; c < kEstChunks; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, sv[c][i]);
+  mx = fmaxf(mx, xor16(mx));
+  mx = fmaxf(mx, xor32(mx));
+  // A operands (hi or lo part of p) and the denominator
+  bf16x8 pa[kEstChunks];
+  float lsum = 0.f;
+#pragma unroll
+  for (int c = 0; c < kEstChunks; ++c) {
+    uint32_t pk[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      uint32_t h2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float s = sv[c][i + u];
+        const float pr = s == kNegInf ? 0.f : fast_exp2(s - mx);
+        lsum += nv[c][i + u] * pr;
+        const uint32_t hi = f2bf(pr);
+        const uint32_t lo = f2bf(pr - __uint_as_float(hi << 16));
+        h2[u] = n < G ? hi : (n < 2 * G ? lo : 0u);
+      }
+      pk[i >> 1] = h2[0] | (h2[1] << 16);
+    }
+    pa[c] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+  }
+  lsum += xor16(lsum);
+  lsum += xor32(lsum);
+  typedef __attribute__((ext_vector_type(4))) float floatx4;
+  floatx4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  drain_vmem();  // (the direct loads have landed in LDS once the wave's loads completed)
+  __syncthreads();
+  const uint16_t* r16 = reinterpret_cast<const uint16_t*>(&st.rows[0][0][0][0][0]);
+#pragma unroll
+  for (int c = 0; c < kEstChunks; ++c) {
+    const uint16_t* wr = r16 + ((size_t)(c * (kDecThreads / 64) + w) * 8) * 512 + g * 128 + (n & 7);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int ch = (2 * t + (n >> 3) + 2 * g) & 15;
+      uint32_t bw[4];
+#pragma unroll
+      for (int i = 0; i < 8; i += 2)
+        bw[i >> 1] = (uint32_t)wr[i * 512 + ch * 8] | ((uint32_t)wr[(i + 1) * 512 + ch * 8] << 16);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          pa[c], __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]}), acc[t], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // (the merge below reuses the staging LDS)
+  EstMerge& mg = *reinterpret_cast<EstMerge*>(&st);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      if (r < 2 * G) mg.o[w][r][16 * t + n] = acc[t][i];
+    }
+  if (g == 0 && n < G) {
+    mg.m[w][n] = mx;
+    mg.l[w][n] = lsum;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kHeadDim; idx += kDecThreads) {
+    const int h = idx >> 7, d = idx & 127;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kDecThreads / 64; ++ww) M = fmaxf(M, mg.m[ww][h]);
+    float o = 0.f, l = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int ww = 0; ww < kDecThreads / 64; ++ww) {
+        const float f = fast_exp2(mg.m[ww][h] - M);
+        o += f * (mg.o[ww][h][d] + mg.o[ww][G + h][d]);
+        l += f * mg.l[ww][h];
+      }
+    }
+    dst[h * kPartStride + d] = o;
+    if (d == 0) {
+      dst[h * kPartStride + 128] = M;
+      dst[h * kPartStride + 129] = l;
+    }
+  }
+}
+
 // One-dimensional grid, by role (so the selection workgroups of every (b, kv-head) are
 // dispatched first): nH per (b, kv-head) select (one for heads of at most kLocalSelectMax
 // clusters, which selects and publishes alone; else one per kSelSpan scores, listing the
@@ -1470,10 +1615,10 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
   // workgroup's staged chunk and the partial exchange of the estimate and steady roles)
   __shared__ union {
     FinShared f;
-    typename std::conditional<G == 4, EstStage, int>::type est;
+    EstLds est;
     float sm[kDecThreads / 64][G][kPartStride];
   } lds;
-  const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, cc = lane & 15;
+  const int lane = tid & 63, wave = tid >> 6, cc = lane & 15;
   // (roles in dispatch order: selection, steady, estimate; x below numbers a head's
   // workgroups as selection [0, nH), estimate [nH, nH + nEW), steady after those)
   int x = blockIdx.x, bh;
@@ -1491,121 +1636,15 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
   }
   if (x >= a.nH) {
     const int b = bh / a.Hkv, g = bh % a.Hkv;
+    if (x < a.nH + a.nEW) {
+      const int e = x - a.nH;
+      estimate_mfma<G>(a, bh, e, lds.est, a.part + ((size_t)bh * a.nP + e) * G * kPartStride);
+      return;
+    }
     Online<G> st;
     st.init();
     int slot;
-    if (x < a.nH + a.nEW) {
-      const int e = x - a.nH;
-      constexpr int R = Rows<G>::R;
-      const size_t base = (size_t)bh * a.C;
-      if constexpr (G == 4) {
-        // ---- estimate: chunks e nEC (and e nEC + 1 when nEC = 2) of 128 clusters. The
-        // first chunk's rows go to registers (4R rows per wave, one step); the second one is
-        // staged in LDS by direct loads issued after them, so folding the first waits for
-        // the first only; then the second is folded from LDS.
-        const int cA = e * a.nEC, cB = min(cA + a.nEC - 1, a.nS - 1);
-        const bool hasB = cB > cA;
-        const int j0 = cA * kChunk + wave * (kChunk / 4);
-        u32x4 vr[R];
-        int32_t n[R];
-        float s2[R][G], w[R], sg[R];
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const int j = j0 + 4 * i + grp;
-          if (j < a.C) {
-            vr[i] = ld16_stream(a.vsum + (base + j) * kHeadDim + cc * 8);
-            n[i] = __builtin_nontemporal_load(a.csize + base + j);
-            const u32x4 l4 = ld16(a.scores + (base + j) * G);
-#pragma unroll
-            for (int h = 0; h < 4; ++h) s2[i][h] = __uint_as_float(l4[h]);
-          } else {
-            vr[i] = u32x4{0, 0, 0, 0};
-            n[i] = 0;
-#pragma unroll
-            for (int h = 0; h < G; ++h) s2[i][h] = kNegInf;
-          }
-        }
-        {
-          // (unconditional: without a second chunk these re-read the first, never folded;
-          // rows past the head clamp to its last cluster and are masked when folded)
-          typedef __attribute__((address_space(3))) void* lds_ptr;
-          const int jb = cB * kChunk + wave * (kChunk / 4);
-#pragma unroll
-          for (int i = 0; i < R; ++i) {
-            const size_t row = base + min(jb + 4 * i + grp, a.C - 1);
-            __builtin_amdgcn_global_load_lds(a.vsum + row * kHeadDim + cc * 8,
-                                             (lds_ptr)&lds.est.rows[(wave * R + i) * 256], 16,
-                                             0, 0);
-          }
-          const int r0 = (wave & 1) * 64;
-          const size_t rc = base + min(cB * kChunk + r0 + lane, a.C - 1);
-          __builtin_amdgcn_global_load_lds(a.scores + rc * G,
-                                           (lds_ptr)&lds.est.logit[wave >> 1][r0][0], 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(a.csize + rc, (lds_ptr)&lds.est.size[wave >> 1][r0],
-                                           4, 0, 0);
-        }
-        auto fold = [&]() {
-#pragma unroll
-          for (int i = 0; i < R; ++i) {
-            const bool ok = n[i] > 0;
-            w[i] = ok ? (float)n[i] : 0.f;
-            sg[i] = 1.f;
-#pragma unroll
-            for (int h = 0; h < G; ++h) s2[i][h] = ok ? s2[i][h] : kNegInf;
-          }
-          fold_rows<G, R>(st, s2, w, vr, sg);
-        };
-        fold();
-        drain_vmem();  // (the staged chunk is in LDS once this wave's loads have completed)
-        __syncthreads();
-        if (hasB) {
-#pragma unroll
-          for (int i = 0; i < R; ++i) {
-            const int rl = wave * (kChunk / 4) + 4 * i + grp, j = cB * kChunk + rl;
-            vr[i] = *reinterpret_cast<const u32x4*>(&lds.est.rows[(wave * R + i) * 256 + lane * 4]);
-            n[i] = j < a.C ? lds.est.size[0][rl] : 0;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) s2[i][h] = lds.est.logit[0][rl][h];
-          }
-          fold();
-        }
-        __syncthreads();  // (the partial exchange below reuses the staging LDS)
-      } else {
-        // ---- estimate: chunk e of 128 clusters, 4R rows per wave and step
-        const int j0 = e * kChunk + wave * (kChunk / 4);
-        for (int t = j0; t < j0 + kChunk / 4; t += 4 * R) {
-          u32x4 vr[R];
-          int32_t n[R];
-          float s2[R][G], w[R], sg[R];
-#pragma unroll
-          for (int i = 0; i < R; ++i) {
-            const int j = t + 4 * i + grp;
-            if (j < a.C) {
-              vr[i] = ld16_stream(a.vsum + (base + j) * kHeadDim + cc * 8);
-              n[i] = __builtin_nontemporal_load(a.csize + base + j);
-              const float* sp = a.scores + (base + j) * G;
-#pragma unroll
-              for (int h = 0; h < G; ++h) s2[i][h] = sp[h];
-            } else {
-              vr[i] = u32x4{0, 0, 0, 0};
-              n[i] = 0;
-#pragma unroll
-              for (int h = 0; h < G; ++h) s2[i][h] = kNegInf;
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < R; ++i) {
-            const bool ok = n[i] > 0;
-            w[i] = ok ? (float)n[i] : 0.f;
-            sg[i] = 1.f;
-#pragma unroll
-            for (int h = 0; h < G; ++h) s2[i][h] = ok ? s2[i][h] : kNegInf;
-          }
-          fold_rows<G, R>(st, s2, w, vr, sg);
-        }
-      }
-      slot = e;
-    } else {
+    {
       // ---- steady: 128 tokens
       const int s = x - a.nH - a.nEW;
       u32x4 q[G];
@@ -1691,74 +1730,266 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
 // kernel 4: retrieve
 // ------------------------------------------------------------------------------------
 
-// Exact attention and estimate removal over the virtual rows [wb, we) of the listed
-// clusters [r_lo, r_hi) (LDS lists: first virtual row ts[] with ts[r_hi] = end, first cache
-// row co[], cluster id id[]). A removal row carries weight -n_j (wt < 0) and the cluster's
-// stored logits.
+// LDS of one retrieve wave: the value rows of its block of 32 virtual rows, staged for the
+// transposing operand reads, the block's logits and its row descriptors.
+//   vrows: block e (of 8) holds rows 8 s + e in slot s (s = 0..3), each row rotated by 2 s
+//   16-byte chunks; blocks 1152 bytes apart. A ds_read_tr16_b64 of lane (g, L) reads 8 bytes
+//   of row 8 g + 4 hf + (L >> 2) and returns that lane's column of four rows, so that two
+//   reads give the B operand (8 rows of one dim); the rotation and the block spacing spread
+//   the 64 lanes' reads over all LDS banks (each bank twice).
+constexpr int kVBlockWords = 288;      // 1024 bytes of rows + 128 bytes of spacing
 template <int G>
-__device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, const u32x4 (&q)[G],
-                                               Online<G>& st, int wb, int we, const int32_t* ts,
-                                               const int32_t* co, const int32_t* id, int r_lo,
-                                               int r_hi) {
-  constexpr int R = Rows<G>::R / 2;  // (register budget: four retrieve workgroups per CU)
-  const int lane = threadIdx.x & 63, grp = lane >> 4, cc = lane & 15;
+struct RetWave {
+  uint32_t vrows[8][kVBlockWords];
+  float lg[G][kRetBlock];              // log2-domain logits [head][row]
+  int32_t krow[kRetBlock];             // cache row of a token row, -1 removal row, -2 padding
+  int32_t clu[kRetBlock];              // cluster id of a removal row
+  float wgt[kRetBlock];                // denominator weight: 1 token, -n_j removal, 0 padding
+};
+template <int G>
+struct RetMerge {  // the same LDS after the attend: each wave's rows and (m, l) per head
+  float o[kDecThreads / 64][2 * G][kHeadDim];
+  float m[kDecThreads / 64][G], l[kDecThreads / 64][G];
+};
+template <int G>
+union RetLds {
+  RetWave<G> w[kDecThreads / 64];
+  RetMerge<G> mg;
+  float xh[128][6];                    // the final merges' exchange (merge_block)
+};
+
+// Running softmax state of a wave on the matrix cores: acc[t] holds D rows 4 (lane / 16) + i
+// of output dims 16 t + lane % 16, where row r < G is the bf16 part of head r's weights and
+// row G + r the remainder; m (log2 units) and l (this lane's rows only) belong to the head
+// of the lane's A row (lane % 16 < 2G).
+struct MfmaState {
+  typedef __attribute__((ext_vector_type(4))) float floatx4;
+  floatx4 acc[8];
+  float m, l;
+};
+
+// Exact attention and estimate removal over the virtual rows [ts, te) of the listed clusters
+// in LDS (first virtual row l_ts[] with l_ts[cnt] = end, first cache row l_co[], cluster id
+// l_id[]), in blocks of 32 rows: block k of the range goes to wave k % 4. Per block: the row
+// descriptors (lanes 0..31), the keys of the token rows as B operands straight from memory
+// (16 rows x 64 bytes per load) and the value rows (or the removed clusters' value sums)
+// into LDS by direct loads; logits q.k on v_mfma_f32_16x16x32_bf16 (A: the group's queries);
+// the removal rows' logits are the score kernel's; then the weights p = 2^(s - m) (negated
+// for removal rows: their value sum leaves the numerator, n_j p the denominator) as the A
+// operand, hi and lo bf16 parts in rows h and G + h, against the value rows read back
+// transposed.
+template <int G>
+__device__ __forceinline__ void attend_virtual_mfma(const DecodeArgs& a, int bh,
+                                                    const bf16x8 (&qa)[4], MfmaState& st,
+                                                    int ts, int te, const int32_t* l_ts,
+                                                    const int32_t* l_co, const int32_t* l_id,
+                                                    int cnt, RetWave<G>& W) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  typedef __attribute__((ext_vector_type(4))) float floatx4;
+  typedef __attribute__((ext_vector_type(4))) short shortx4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
   const size_t kb = (size_t)bh * a.Lcap, cb = (size_t)bh * a.C;
-  // the listed cluster holding this lane's current virtual row: found once by bisection,
-  // then advanced (a lane's rows only increase, and clusters span about 17 rows)
-  int cur = r_lo;
-  {
-    const int t0 = min(wb + grp, we - 1);
-    int hi = r_hi - 1;
-    while (cur < hi) {
-      const int mid = (cur + hi + 1) >> 1;
-      if (ts[mid] <= t0) cur = mid; else hi = mid - 1;
+  const bool arow = n < 2 * G;
+  const int hA = n < G ? n : (arow ? n - G : 0);  // head of this lane's A row
+  for (int t0 = ts + kRetBlock * wave; t0 < te; t0 += kRetBlock * (kDecThreads / 64)) {
+    // ---- descriptors of rows t0 .. t0 + 31 (lanes 0..31), and the removal rows' logits
+    float rl[G];
+    int kr = -2, cl = 0;
+    float wt = 0.f;
+    if (lane < kRetBlock) {
+      const int t = t0 + lane;
+      if (t < te) {
+        int lo = 0, hi = cnt - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (l_ts[mid] <= t) lo = mid; else hi = mid - 1;
+        }
+        const int off = t - l_ts[lo], nj = l_ts[lo + 1] - l_ts[lo] - 1;
+        if (off < nj) {
+          kr = l_co[lo] + off;
+          wt = 1.f;
+        } else {
+          kr = -1;
+          cl = l_id[lo];
+          wt = -(float)nj;
+        }
+      }
+      W.krow[lane] = kr;
+      W.clu[lane] = cl;
+      W.wgt[lane] = wt;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        rl[h] = kr == -1 ? a.scores[(cb + cl) * G + h] : kNegInf;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---- keys (B operands of the logits) and value rows (LDS)
+    u32x4 kbv[2][4];
+    int krow_of[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      krow_of[tau] = W.krow[16 * tau + n];
+      const size_t row = kb + (krow_of[tau] >= 0 ? krow_of[tau] : 0);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        kbv[tau][s4] = ld16_stream(a.k + row * kHeadDim + s4 * 32 + g * 8);
+    }
+    {
+      const int slot = lane >> 4, cidx = (n - 2 * slot) & 15;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * slot + e;
+        const int k2 = W.krow[r];
+        const uint16_t* src = k2 >= 0 ? a.v + (kb + k2) * kHeadDim
+                                      : (k2 == -1 ? a.vsum + (cb + W.clu[r]) * kHeadDim
+                                                  : a.v + kb * kHeadDim);
+        __builtin_amdgcn_global_load_lds(src + cidx * 8, (lds_ptr)&W.vrows[e][0], 16, 0, 0);
+      }
+    }
+    // ---- logits of the token rows (MFMA), the others from the descriptors
+    floatx4 dq[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      dq[tau] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        dq[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qa[s4], __builtin_bit_cast(bf16x8, kbv[tau][s4]), dq[tau], 0, 0, 0);
+    }
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * g + i;
+        if (h < G && krow_of[tau] >= 0) W.lg[h][16 * tau + n] = dq[tau][i] * a.scale_log2;
+      }
+    if (lane < kRetBlock && kr < 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) W.lg[h][lane] = rl[h];
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---- weights of this lane's rows 8 g .. 8 g + 7 for its A row's head
+    float sv[8], wv[8];
+    {
+      const float4* lp = reinterpret_cast<const float4*>(&W.lg[hA][8 * g]);
+      const float4 x0 = lp[0], x1 = lp[1];
+      sv[0] = x0.x; sv[1] = x0.y; sv[2] = x0.z; sv[3] = x0.w;
+      sv[4] = x1.x; sv[5] = x1.y; sv[6] = x1.z; sv[7] = x1.w;
+      const float4* wp = reinterpret_cast<const float4*>(&W.wgt[8 * g]);
+      const float4 y0 = wp[0], y1 = wp[1];
+      wv[0] = y0.x; wv[1] = y0.y; wv[2] = y0.z; wv[3] = y0.w;
+      wv[4] = y1.x; wv[5] = y1.y; wv[6] = y1.z; wv[7] = y1.w;
+    }
+    float mb = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mb = fmaxf(mb, sv[e]);
+    mb = arow ? mb : kNegInf;
+    mb = fmaxf(mb, xor16(mb));
+    mb = fmaxf(mb, xor32(mb));
+    const float mn = fmaxf(st.m, mb);
+    const float alpha = (st.m == kNegInf || mn == kNegInf) ? (mn == kNegInf ? 1.f : 0.f)
+                                                           : fast_exp2(st.m - mn);
+    st.m = mn;
+    float ls = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      uint32_t h2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float x = sv[e + u];
+        const float pr = (x == kNegInf || mn == kNegInf) ? 0.f : fast_exp2(x - mn);
+        ls += wv[e + u] * pr;
+        const float c = wv[e + u] < 0.f ? -pr : pr;
+        const uint32_t hi = f2bf(c);
+        const uint32_t lo = f2bf(c - __uint_as_float(hi << 16));
+        h2[u] = n < G ? hi : (arow ? lo : 0u);
+      }
+      pk[e >> 1] = h2[0] | (h2[1] << 16);
+    }
+    st.l = alpha * st.l + ls;
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+    // accumulator rows 4 g + i belong to the head of A row 4 g + i (lane 4 g + i)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ar = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) st.acc[t][i] *= ar;
+    }
+    // ---- the value rows, read back transposed, against the weights
+    drain_vmem();  // (this wave's direct loads have landed in LDS)
+    __builtin_amdgcn_wave_barrier();
+    const char* vb = reinterpret_cast<const char*>(&W.vrows[0][0]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      shortx4 bh2[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int e = 4 * hf + (n >> 2);
+        const int c = 2 * t + ((n & 3) >> 1);
+        const int off = e * (kVBlockWords * 4) + g * 256 + (((c + 2 * g) & 15) << 4) + ((n & 1) << 3);
+        bh2[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(vb + off));
+      }
+      const u32x4 bw = {(uint32_t)(uint16_t)bh2[0][0] | ((uint32_t)(uint16_t)bh2[0][1] << 16),
+                        (uint32_t)(uint16_t)bh2[0][2] | ((uint32_t)(uint16_t)bh2[0][3] << 16),
+                        (uint32_t)(uint16_t)bh2[1][0] | ((uint32_t)(uint16_t)bh2[1][1] << 16),
+                        (uint32_t)(uint16_t)bh2[1][2] | ((uint32_t)(uint16_t)bh2[1][3] << 16)};
+      st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, bw),
+                                                          st.acc[t], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();  // (the next block rewrites this wave's LDS)
+  }
+}
+
+// The workgroup's waves' states merged with one more partial xp ([G][kPartStride] in LDS,
+// may be null) into the partial dst (device-coherent stores: read by other workgroups of
+// the same kernel). Ends on a barrier.
+template <int G>
+__device__ __forceinline__ void write_mfma_partial(MfmaState& st, const float* xp,
+                                                   float* __restrict__ dst, RetLds<G>& L) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
+  float l = st.l;
+  l += xor16(l);
+  l += xor32(l);
+  __syncthreads();  // (every wave is done with its staging LDS)
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      if (r < 2 * G) L.mg.o[w][r][16 * t + n] = st.acc[t][i];
+    }
+  if (g == 0 && n < G) {
+    L.mg.m[w][n] = st.m;
+    L.mg.l[w][n] = l;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kHeadDim; idx += kDecThreads) {
+    const int h = idx >> 7, d = idx & 127;
+    float M = xp ? xp[h * kPartStride + 128] : kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kDecThreads / 64; ++ww) M = fmaxf(M, L.mg.m[ww][h]);
+    float o = 0.f, ls = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int ww = 0; ww < kDecThreads / 64; ++ww) {
+        const float f = fast_exp2(L.mg.m[ww][h] - M);
+        o += f * (L.mg.o[ww][h][d] + L.mg.o[ww][G + h][d]);
+        ls += f * L.mg.l[ww][h];
+      }
+      if (xp) {
+        const float f = fast_exp2(xp[h * kPartStride + 128] - M);
+        o += f * xp[h * kPartStride + d];
+        ls += f * xp[h * kPartStride + 129];
+      }
+    }
+    st_dev(dst + h * kPartStride + d, o);
+    if (d == 0) {
+      st_dev(dst + h * kPartStride + 128, M);
+      st_dev(dst + h * kPartStride + 129, ls);
     }
   }
-  // every row issues the same loads (no branch, so the R rows' loads are in flight
-  // together): a key row (a token row; for a removal row with G = 4, its cluster's four
-  // logits in the same 16 bytes, else the cluster's first row), a value row (the token's,
-  // or the cluster's value sum) and, for G != 4, the cluster's logits
-  constexpr bool kPacked = G == 4;
-  constexpr int GS = kPacked ? 1 : G;
-  for (int t = wb; t < we; t += 4 * R) {
-    u32x4 kr[R], vr[R];
-    float wt[R], sc[R][GS];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int tt = t + 4 * i + grp;
-      const bool valid = tt < we;
-      if (valid)
-        while (cur + 1 < r_hi && ts[cur + 1] <= tt) ++cur;
-      const int lo = cur;
-      const int off = tt - ts[lo], n = ts[lo + 1] - ts[lo] - 1;
-      const bool token = valid && off < n;
-      const size_t krow = (kb + co[lo] + (token ? off : 0)) * kHeadDim + cc * 8;
-      const size_t j = cb + id[lo];
-      const float* sp = a.scores + j * G;
-      if constexpr (kPacked) {
-        kr[i] = ld16_stream(token ? static_cast<const void*>(a.k + krow)
-                                  : static_cast<const void*>(sp));
-      } else {
-        kr[i] = ld16_stream(a.k + krow);
-#pragma unroll
-        for (int h = 0; h < GS; ++h) sc[i][h] = sp[h];
-      }
-      vr[i] = ld16_stream(token ? a.v + krow : a.vsum + j * kHeadDim + cc * 8);
-      wt[i] = token ? 1.f : (valid ? -(float)n : 0.f);
-    }
-    float s[R][G], sg[R];
-    row_logits<G, R>(q, kr, a.scale_log2, s);
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      sg[i] = wt[i] < 0.f ? -1.f : 1.f;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float rs = kPacked ? __uint_as_float(kr[i][h & 3]) : sc[i][kPacked ? 0 : h];
-        s[i][h] = wt[i] < 0.f ? rs : (wt[i] == 0.f ? kNegInf : s[i][h]);
-      }
-    }
-    fold_rows<G, R>(st, s, wt, vr, sg);
-  }
+  __syncthreads();
 }
 
 // nB workgroups per (b, kv-head): each takes a share of the estimate and steady partials
@@ -1770,11 +2001,12 @@ __device__ __forceinline__ void attend_virtual(const DecodeArgs& a, int bh, cons
 // launches small enough to be resident at three workgroups per CU); else merged element by
 // element before the attend.
 template <int G, bool XM1>
-__global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_retrieve(DecodeArgs a) {
   __shared__ float s_x[G][kPartStride];  // this workgroup's share of the earlier partials
   __shared__ int32_t l_ts[kWinR + 1], l_co[kWinR], l_id[kWinR];
+  __shared__ RetLds<G> lds;
   const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv, w_item = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cc = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nB = a.nB, nSP = a.nEW + a.nSt;
   float* parts = a.part + (size_t)bh * a.nP * G * kPartStride;
   // ---- this workgroup's virtual rows [T0, T1) and listed clusters [r_lo, r_hi)
@@ -1812,10 +2044,23 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
       }
     }
   }
-  u32x4 q[G];
-  load_q<G>(a, b, g, cc, q);
-  Online<G> st;
-  st.init();
+  // A operands of the logits: query head `lane % 16` (zero beyond G), dims 32 s + 8 (lane / 16)
+  bf16x8 qa[4];
+  {
+    const int qh = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      u32x4 v = {0, 0, 0, 0};
+      if (qh < G)
+        v = ld16(a.q + ((size_t)(b * a.Hq + g * G + qh) * kHeadDim + s4 * 32 + kg * 8));
+      qa[s4] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  MfmaState st;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) st.acc[t] = MfmaState::floatx4{0.f, 0.f, 0.f, 0.f};
+  st.m = kNegInf;
+  st.l = 0.f;
   const size_t lb = (size_t)bh * a.rcap;
   for (int rw = r_lo; rw < r_hi; rw += kWinR) {
     const int cnt = min(kWinR, r_hi - rw);
@@ -1829,8 +2074,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
     __syncthreads();
     const int ts = max(T0, l_ts[0]), te = min(T1, l_ts[cnt]);
     if (ts < te)
-      attend_virtual<G>(a, bh, q, st, ts + (te - ts) * wave / 4, ts + (te - ts) * (wave + 1) / 4,
-                        l_ts, l_co, l_id, 0, cnt);
+      attend_virtual_mfma<G>(a, bh, qa, st, ts, te, l_ts, l_co, l_id, cnt, lds.w[wave]);
     __syncthreads();
   }
   if constexpr (XM1) {
@@ -1868,8 +2112,8 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
       }
     }
   }
-  // (the barrier inside makes s_x visible before it is read)
-  write_block_partial<G>(st, &s_x[0][0], parts + (size_t)(nSP + w_item) * G * kPartStride);
+  // (the barriers inside make s_x visible before it is read)
+  write_mfma_partial<G>(st, &s_x[0][0], parts + (size_t)(nSP + w_item) * G * kPartStride, lds);
   uint32_t* ctr = a.counter + (size_t)bh * kCtrStride;
   const int gsz = (nB + a.nG - 1) / a.nG;  // retrieve partials per merge group
   const int grp = w_item / gsz, g0 = grp * gsz, gn = min(gsz, nB - g0);
@@ -1884,10 +2128,10 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
     if (d4 == 0 && a.lse) a.lse[bq + h] = (M + log2f(L)) * kLn2;
   };
   if (single) {
-    merge_block<G, true, kMergeBatch>(parts, nSP + g0, 1, gn, write_out);
+    merge_block<G, true, kMergeBatch>(parts, nSP + g0, 1, gn, lds.xh, write_out);
     return;
   }
-  merge_block<G, true, kMergeBatch>(parts, nSP + g0, 1, gn,
+  merge_block<G, true, kMergeBatch>(parts, nSP + g0, 1, gn, lds.xh,
                                     [&](int h, int d4, float M, float L, float4 o) {
     float* q = gp + h * kPartStride + d4;
     st_dev(q, o.x);
@@ -1900,7 +2144,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_retrieve(DecodeArgs a) {
     }
   });
   if (!arrive_last(ctr + kCtrFinal, (uint32_t)a.nG)) return;
-  merge_block<G, true, kMergeBatch>(parts, nSP + nB, 1, a.nG, write_out);
+  merge_block<G, true, kMergeBatch>(parts, nSP + nB, 1, a.nG, lds.xh, write_out);
 }
 
 // ------------------------------------------------------------------------------------

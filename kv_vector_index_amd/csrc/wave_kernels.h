@@ -24,6 +24,7 @@ struct Tracer {
 constexpr int kDecThreads = 256;      // every decode workgroup: 4 waves
 constexpr int kChunk = 128;           // clusters per score / estimate workgroup (32 per wave)
 constexpr int kTokChunk = 128;        // steady tokens per steady workgroup
+constexpr int kEstChunks = 1;         // chunks of 128 clusters per estimate workgroup
 constexpr int kPartStride = 132;      // floats per (partial, head): o[128], m, l, 2 pad
 constexpr int kSelSpan = 2048;        // group scores listed per selection workgroup
 constexpr int kHistBins = 4096;       // value-range histogram of the group scores
@@ -37,10 +38,11 @@ constexpr int kMaxClusters = 65536;   // clusters per (b, kv-head) supported by 
 constexpr int kMaxRetrieveWG = 256;   // retrieve workgroups per (b, kv-head)
 constexpr int kMergeGroup = 16;       // retrieve partials per first-level merge (about)
 constexpr int kMergeBatch = 14;       // partials per half-workgroup and round of loads in a merge
-constexpr int kWinR = 1024;           // listed clusters staged per LDS window of a retrieve WG
+constexpr int kWinR = 256;            // listed clusters staged per LDS window of a retrieve WG
+constexpr int kRetBlock = 32;         // virtual rows per retrieve wave and step (one K step)
 constexpr int kRowsPerItem = 128;     // retrieved rows per retrieve workgroup (target)
 constexpr int kCUs = 256;              // compute units of an MI355X
-constexpr int kRetrieveWGPerCall = 1024;  // retrieve workgroups of one call (at most, about)
+constexpr int kRetrieveWGPerCall = 768;   // retrieve workgroups of one call (at most, about)
 // score workgroups of one call (about): three resident per CU, one round
 constexpr int kScoreWGPerCall = 768;
 // per (b, kv-head) counters, cleared by the score kernel in every call
@@ -90,7 +92,6 @@ struct DecodeArgs {
   // chunk), steady workgroups, selection workgroups, retrieve workgroups, their
   // merge groups, partial slots (estimate, steady, retrieve, merge)
   int nS, nSW, nEW, nSt, nH, nB, nG, nP;
-  int nEC;                 // chunks per estimate workgroup (2 for groups of four heads)
   float scale, scale_log2;
   int hist_kernel;         // 1: the histogram kernel runs (Cp > kLocalSelectMax)
 };
