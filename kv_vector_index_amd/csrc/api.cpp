@@ -151,8 +151,8 @@ wave_status check_decode(const wave_decode_params* p, DecodeShape* sh) {
   const int nb_cap = clampi(wave::kRetrieveWGPerCall / bh, 1, wave::kMaxRetrieveWG);
   sh->nB = clampi(((int64_t)p->n_retrieve * (avg + 1) * 3 / 2 + wave::kRowsPerItem - 1) /
                       wave::kRowsPerItem, 1, nb_cap);
-  // score / estimate workgroups: a few per CU over all (b, kv-heads), looping over chunks
-  sh->nSW = clampi(wave::kScoreWGPerCall / bh, 1, sh->nS);
+  // score workgroups: one per chunk of 128 clusters
+  sh->nSW = sh->nS;
   // estimate workgroups: kEstChunks chunks each
   sh->nEW = (sh->nS + wave::kEstChunks - 1) / wave::kEstChunks;
   // retrieve merge groups: one merge of all partials for up to two groups' worth, else

@@ -607,29 +607,20 @@ struct Binner {
 // ------------------------------------------------------------------------------------
 // kernel 1: score (centroid logits of every cluster)
 // ------------------------------------------------------------------------------------
-// Clusters [c0, c1) of a workgroup, a contiguous share of the nS chunks of 128 clusters of
-// its (b, kv-head) split over nw workgroups.
-struct Share {
-  int c0, c1;
-};
-__device__ __forceinline__ Share chunk_share(int nS, int nw, int w) {
-  const int k0 = (int)((int64_t)nS * w / nw), k1 = (int)((int64_t)nS * (w + 1) / nw);
-  return {k0 * kChunk, k1 * kChunk};
-}
-
-// nSW workgroups per (b, kv-head), each over a share of the clusters in steps of 128 (32 per
-// wave), the centroids of the next step loaded while the current step is scored. The logits
-// of the G heads are a dense product [16 x 128] . [128 x 16] per 16 clusters on
-// v_mfma_f32_16x16x32_bf16 (A: the group's query rows, zero beyond G; B: 16 centroids, four
-// lanes of 16 bytes per 64 bytes of a row; D: lane l < 16 holds heads 0..3 of cluster l,
-// lane 16 + l heads 4..7). Every query head's log2-domain logit goes to scores[], the group
-// mean (natural units) to shat[] (-inf for empty and padding clusters), and the
-// workgroup's finite min / max to smm[]. Workgroup 0 of each (b, kv-head) also clears its
-// counters (and its histogram, for the histogram kernel).
+// One workgroup per chunk of 128 clusters of a (b, kv-head) (the dispatcher balances the
+// stream), 32 clusters per wave. The logits of the G heads are a dense product
+// [16 x 128] . [128 x 16] per 16 clusters on v_mfma_f32_16x16x32_bf16 (A: the group's query
+// rows, zero beyond G; B: 16 centroids, four lanes of 16 bytes per 64 bytes of a row, read
+// from the rows staged in LDS; D: lane l < 16 holds heads 0..3 of cluster l, lane 16 + l
+// heads 4..7). Every query head's log2-domain logit goes to scores[], the group mean
+// (natural units) to shat[] (-inf for empty and padding clusters), and the workgroup's
+// finite min / max to smm[]. Workgroup 0 of each (b, kv-head) also clears its counters (and
+// its histogram, for the histogram kernel).
 template <int G>
 __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
   typedef __attribute__((ext_vector_type(4))) float floatx4;
   __shared__ float s_mm[kDecThreads / 64][2];
+  __shared__ uint32_t s_rows[kDecThreads / 64][8][256];  // per wave: 8 loads of 4 rows
   const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, kg = lane >> 4;  // MFMA column (cluster) and k group
@@ -652,66 +643,58 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
   const size_t base = (size_t)bh * a.C;
   float* shat = a.shat + (size_t)bh * a.Cp;
   const float sl2 = a.scale_log2, gmean = a.scale / (float)G;
-  const Share sh = chunk_share(a.nS, a.nSW, blockIdx.x);
-  // B operands of the wave's 32 clusters of a step (two groups of 16): row t + 16 u + col,
-  // dims 32 s + 8 kg, and the clusters' sizes; unconditional loads from a clamped row (rows
-  // past the share re-read its last row, already cached), issued a step ahead and in the
-  // order they are used, so the compiler waits for exactly the step in use
-  const int jmax = min(a.C, sh.c1) - 1;
-  auto load = [&](int t, u32x4 (&kb)[2][4], int32_t (&n)[2]) {
+  // the wave's 32 centroid rows, whole, into LDS: direct load i brings rows 4 i .. 4 i + 3
+  // (slot s = lane / 16), each row rotated by 4 s 16-byte chunks so that the operand reads
+  // below (16 rows, one 16-byte column chunk each) spread over all banks
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int t = blockIdx.x * kChunk + wave * 32;  // this wave's first cluster
+  {
+    const int slot = lane >> 4, cidx = ((lane & 15) - 4 * slot) & 15;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const size_t row = base + min(t + 16 * u + col, jmax);
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        kb[u][st] = ld16_stream(a.cmean + row * kHeadDim + st * 32 + kg * 8);
+    for (int i = 0; i < 8; ++i) {
+      const size_t row = base + min(t + 4 * i + slot, a.C - 1);
+      __builtin_amdgcn_global_load_lds(a.cmean + row * kHeadDim + cidx * 8,
+                                       (lds_ptr)&s_rows[wave][i][0], 16, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      n[u] = __builtin_nontemporal_load(a.csize + base + min(t + 16 * u + col, jmax));
-  };
-  float mn = kPosInf, mx = kNegInf;
-  u32x4 kb[2][4];
+  }
   int32_t n[2];
-  int t = sh.c0 + wave * 32;  // this wave's first cluster of each step
-  load(t, kb, n);
-  for (; t < sh.c1; t += 128) {
-    u32x4 kn[2][4];
-    int32_t nn[2];
-    load(t + 128, kn, nn);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      floatx4 d = {0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 2; ++u)
+    n[u] = __builtin_nontemporal_load(a.csize + base + min(t + 16 * u + col, a.C - 1));
+  float mn = kPosInf, mx = kNegInf;
+  drain_vmem();  // (this wave's direct loads have landed in LDS)
+  __builtin_amdgcn_wave_barrier();
+  const char* wr = reinterpret_cast<const char*>(&s_rows[wave][0][0]);
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], __builtin_bit_cast(bf16x8, kb[u][st]),
-                                                    d, 0, 0, 0);
-      // lane kg * 16 + col: heads 4 kg + i of cluster t + 16 u + col
-      const int j = t + 16 * u + col;
-      float sum = 0.f;
+  for (int u = 0; u < 2; ++u) {
+    const int r = 16 * u + col, blk = r >> 2, sl = r & 3;
+    floatx4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sum += (4 * kg + i < G) ? d[i] : 0.f;
-      if (G > 4) sum += __shfl_xor(sum, 16);  // heads 4..7 from lane col + 16
-      if (j < a.C && kg < (G + 3) / 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * kg + i < G) a.scores[(base + j) * G + 4 * kg + i] = d[i] * sl2;
-      }
-      if (kg == 0) {
-        const float mean = sum * gmean;
-        const bool ok = j < a.C && n[u] > 0;
-        if (ok) {
-          mn = fminf(mn, mean);
-          mx = fmaxf(mx, mean);
-        }
-        shat[j] = ok ? mean : kNegInf;
-      }
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 kb = *reinterpret_cast<const u32x4*>(
+          wr + blk * 1024 + sl * 256 + (((4 * st + kg + 4 * sl) & 15) << 4));
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], __builtin_bit_cast(bf16x8, kb), d, 0,
+                                                  0, 0);
     }
+    // lane kg * 16 + col: heads 4 kg + i of cluster t + 16 u + col
+    const int j = t + 16 * u + col;
+    float sum = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      n[u] = nn[u];
+    for (int i = 0; i < 4; ++i) sum += (4 * kg + i < G) ? d[i] : 0.f;
+    if (G > 4) sum += __shfl_xor(sum, 16);  // heads 4..7 from lane col + 16
+    if (j < a.C && kg < (G + 3) / 4) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) kb[u][st] = kn[u][st];
+      for (int i = 0; i < 4; ++i)
+        if (4 * kg + i < G) a.scores[(base + j) * G + 4 * kg + i] = d[i] * sl2;
+    }
+    if (kg == 0) {
+      const float mean = sum * gmean;
+      const bool ok = j < a.C && n[u] > 0;
+      if (ok) {
+        mn = fminf(mn, mean);
+        mx = fmaxf(mx, mean);
+      }
+      shat[j] = ok ? mean : kNegInf;
     }
   }
   mn = wave_reduce(mn, [](float x, float y) { return fminf(x, y); });
@@ -1460,11 +1443,12 @@ __device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinSha
 // are zero. The denominator sum_j n_j p is summed in fp32 from the unrounded p. Lane l holds
 // the A operand of row l % 16 and the B operand of dim l % 16, both for the clusters
 // 8 (l / 16) .. + 7 of its K step. The value-sum rows reach LDS by direct global-to-LDS
-// loads: block e of a wave holds the wave's clusters 8 g + e in slot g (g = 0..3), each row
-// rotated by 2 g 16-byte chunks, so that the operand reads (the 16 lanes of a slot read 32
-// bytes of one row, the four slots of a block the same dims) fall in distinct LDS banks.
+// loads in the layout of the retrieve's value rows (block e of a wave holds the wave's
+// clusters 8 g + e in slot g, each row rotated by 2 g 16-byte chunks, blocks 1152 bytes
+// apart) and come back as B operands through transposing reads (ds_read_tr16_b64).
 struct EstLds {
-  uint32_t rows[kEstChunks][kDecThreads / 64][8][4][64];  // [chunk][wave][e][slot][256 B]
+  // [chunk][wave][e][slot][256 B] with blocks e 1152 bytes apart (as the retrieve's value rows)
+  uint32_t rows[kEstChunks][kDecThreads / 64][8][288];
 };
 struct EstMerge {  // the same LDS after the products: each wave's rows and (m, l) per head
   float o[kDecThreads / 64][2 * kMaxGroup][kHeadDim];
@@ -1507,7 +1491,7 @@ __device__ __forceinline__ void estimate_mfma(const DecodeArgs& a, int bh, int e
         const int j = (e * kEstChunks + c) * kChunk + 32 * w + 8 * slot + ei;
         const size_t row = base + min(j, a.C - 1);
         __builtin_amdgcn_global_load_lds(a.vsum + row * kHeadDim + cidx * 8,
-                                         (lds_ptr)&st.rows[c][w][ei][0][0], 16, 0, 0);
+                                         (lds_ptr)&st.rows[c][w][ei][0], 16, 0, 0);
       }
     }
   }
@@ -1549,19 +1533,28 @@ __device__ __forceinline__ void estimate_mfma(const DecodeArgs& a, int bh, int e
   for (int t = 0; t < 8; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   drain_vmem();  // (the direct loads have landed in LDS once the wave's loads completed)
   __syncthreads();
-  const uint16_t* r16 = reinterpret_cast<const uint16_t*>(&st.rows[0][0][0][0][0]);
+  typedef __attribute__((ext_vector_type(4))) short shortx4;
 #pragma unroll
   for (int c = 0; c < kEstChunks; ++c) {
-    const uint16_t* wr = r16 + ((size_t)(c * (kDecThreads / 64) + w) * 8) * 512 + g * 128 + (n & 7);
+    const char* vb = reinterpret_cast<const char*>(&st.rows[c][w][0][0]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int ch = (2 * t + (n >> 3) + 2 * g) & 15;
-      uint32_t bw[4];
+      // two transposing reads: rows 8 g + 4 hf .. + 3 of dim 16 t + n (see the retrieve)
+      shortx4 bh2[2];
 #pragma unroll
-      for (int i = 0; i < 8; i += 2)
-        bw[i >> 1] = (uint32_t)wr[i * 512 + ch * 8] | ((uint32_t)wr[(i + 1) * 512 + ch * 8] << 16);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          pa[c], __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]}), acc[t], 0, 0, 0);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int eb = 4 * hf + (n >> 2);
+        const int ch = 2 * t + ((n & 3) >> 1);
+        const int off = eb * 1152 + g * 256 + (((ch + 2 * g) & 15) << 4) + ((n & 1) << 3);
+        bh2[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(vb + off));
+      }
+      const u32x4 bw = {(uint32_t)(uint16_t)bh2[0][0] | ((uint32_t)(uint16_t)bh2[0][1] << 16),
+                        (uint32_t)(uint16_t)bh2[0][2] | ((uint32_t)(uint16_t)bh2[0][3] << 16),
+                        (uint32_t)(uint16_t)bh2[1][0] | ((uint32_t)(uint16_t)bh2[1][1] << 16),
+                        (uint32_t)(uint16_t)bh2[1][2] | ((uint32_t)(uint16_t)bh2[1][3] << 16)};
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[c], __builtin_bit_cast(bf16x8, bw),
+                                                       acc[t], 0, 0, 0);
     }
   }
   __syncthreads();  // (the merge below reuses the staging LDS)

@@ -43,8 +43,6 @@ constexpr int kRetBlock = 32;         // virtual rows per retrieve wave and step
 constexpr int kRowsPerItem = 128;     // retrieved rows per retrieve workgroup (target)
 constexpr int kCUs = 256;              // compute units of an MI355X
 constexpr int kRetrieveWGPerCall = 768;   // retrieve workgroups of one call (at most, about)
-// score workgroups of one call (about): three resident per CU, one round
-constexpr int kScoreWGPerCall = 768;
 // per (b, kv-head) counters, cleared by the score kernel in every call
 constexpr int kCtrStride = 32;
 constexpr int kCtrGather = 1;         // select workgroups of the gather kernel arrived
