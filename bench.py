@@ -2,12 +2,12 @@
 """Benchmark of the wave-index hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input: build the index
-of the layer (segmented spherical k-means, finalise, permuted K/V) and run the workload's
-decode steps against it (score, select, exact + estimate, merge). Inputs are resident in HBM
-before timing starts. Before each decode call a 512 MiB buffer is read (a reduction) so that
-the call finds its data in HBM rather than in the 256 MB Infinity Cache, as it would after
-the other layers of a model; the per-kernel figures come from HIP events that the library
-records between its kernels (the flush lies outside them).
+of the Llama-shaped 128K layer (segmented spherical k-means, finalise, permuted K/V) and run
+the workload's 64 decode steps against it (score, select, exact + estimate, merge). Inputs
+are resident in HBM before timing starts. Before each decode call a 512 MiB buffer is read (a
+reduction) so that the call finds its data in HBM rather than in the 256 MB Infinity Cache, as
+it would after the other layers of a model; the per-kernel figures come from HIP events that
+the library records between its kernels (the flush lies outside them).
 
 The timed steps run the plain entry points with HIP events around each call (call time =
 first kernel start to last kernel end, as the stream sees it); one more step runs the traced
@@ -17,16 +17,18 @@ time). A 256 MiB device-to-device copy runs once before the warmup: its FETCH_SI
 WRITE_SIZE counters calibrate the HBM-traffic figures taken from rocprofv3 runs of this
 script.
 
-Prints one JSON line. `value` is decode-attention tokens/s of the layer (batch / median time
-of one decode call); the index-build rate and achieved HBM bandwidth are extra fields, with
-p10 / p90 of the call time and, as a reference, the bandwidth of a streaming read on the same
-GPU (torch's reduction over the flush buffer). A batched leg (default: batch 8 at 122 880
-tokens) builds that layer's index once and times wave decode calls and dense flash-decode
-calls over the same resident KV (`batched`, with the speedup). A long-context leg (default:
-the 1M-token layer) then builds that layer's index once and times 16 decode calls the same
-way (`long_context`: call time, HBM bandwidth on the algorithmic bytes, build time). An
-extension leg (default: the 128K layer) times the extension of an index built for one
-segment fewer tokens to the full context against a full build (`extend`).
+Prints one JSON line. `value` is decode-attention tokens/s of the 128K layer (batch / median
+time of one decode call); the index-build rate and achieved HBM bandwidth are extra fields,
+with p10 / p90 of the call time. Further legs in the same line:
+  * extend: the extension of an index built for one segment fewer tokens, against a full build;
+  * stack_b8: the 32-layer Llama-shaped stack at batch 8 and 122 880 tokens, every layer's
+    cache and index resident: the build over the stack, decode steps of one call per layer,
+    and dense flash-decode steps over the same caches (the speedup);
+  * stack_1m: the 32-layer stack at 1M tokens (about 150 GB resident): the build over the
+    whole context, decode steps;
+  * sweep: the 28-layer Qwen-shaped stack at batch 4 and 256K over cluster sizes 8/16/32 and
+    budgets 0.5/1/1.8/4 %: step throughput and the error against exact attention per point;
+  * cpu_baseline: the CPU oracle on the host cores, one thread and all cores.
 """
 from __future__ import annotations
 
@@ -55,18 +57,20 @@ def parse():
                     help="decode calls per step (default: the workload's)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-decode-steps", type=int, default=3)
-    ap.add_argument("--long-context", default="llama1m",
-                    help="also time decode calls at this workload's context ('none': skip)")
-    ap.add_argument("--accuracy", default="qwen256k",
-                    help="error of the wave decode against exact (dense) attention over this "
-                         "workload's cluster-size x budget grid ('none': skip)")
+    ap.add_argument("--cpu-decode-steps", type=int, default=16)
     ap.add_argument("--extend", default="llama128k",
                     help="time the extension of this workload's index by one segment of new "
                          "tokens against a full build ('none': skip)")
-    ap.add_argument("--batched", default="llama122k_b8",
-                    help="also time wave and dense decode calls of this (batched) workload on "
-                         "the same resident KV ('none': skip)")
+    ap.add_argument("--stack8", default="llama122k_b8",
+                    help="resident multi-layer stack with dense flash-decode beside it: layer "
+                         "loops of wave and dense decode calls ('none': skip)")
+    ap.add_argument("--stack1m", default="llama1m",
+                    help="resident multi-layer stack at a long context: the build over the "
+                         "whole stack and layer loops of decode calls ('none': skip)")
+    ap.add_argument("--sweep", default="qwen256k",
+                    help="resident stack over cluster sizes x retrieval budgets: throughput "
+                         "and error against exact attention at each point ('none': skip)")
+    ap.add_argument("--stack-steps", type=int, default=8)
     return ap.parse_args()
 
 
@@ -271,19 +275,6 @@ def main():
         "roofline_by_kernel": roofs,
         "roofline_decode_call": roof_call,
     }
-    if flush is not None:
-        # a streaming-read reference on this GPU: torch's reduction over the flush buffer
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
-        for e in sev:
-            e[0].record()
-            flush.sum()
-            e[1].record()
-        torch.cuda.synchronize()
-        st_ms = med([e[0].elapsed_time(e[1]) for e in sev[1:]])
-        st_gbs = flush.numel() * 4 / (st_ms * 1e-3) / 1e9
-        res["stream_read"] = {"kernel": "torch sum over 512 MiB (one read)",
-                              "GBps": round(st_gbs, 1),
-                              "decode_hbm_frac_of_stream": round(call_gbs / st_gbs, 4)}
     cs = sorted(call_ms)
     res["decode_call_us_p10_p90"] = [round(cs[int(0.1 * (len(cs) - 1))] * 1e3, 2),
                                      round(cs[int(0.9 * (len(cs) - 1))] * 1e3, 2)]
@@ -292,14 +283,15 @@ def main():
     if args.extend != "none":
         res["extend"] = extend_leg(args.extend, 5)
         torch.cuda.empty_cache()
-    if args.batched != "none":
-        res["batched"] = batched_vs_dense(args.batched, 8, 2, not args.no_flush)
+    if args.stack8 != "none":
+        res["stack_b8"] = stack_leg(args.stack8, args.stack_steps, 2, dense=True)
         torch.cuda.empty_cache()
-    if args.accuracy != "none":
-        res["accuracy"] = accuracy_grid(args.accuracy, 4)
+    if args.stack1m != "none":
+        res["stack_1m"] = stack_leg(args.stack1m, args.stack_steps, 2, dense=False)
         torch.cuda.empty_cache()
-    if args.long_context != "none":
-        res["long_context"] = long_context(args.long_context, 16, 2, not args.no_flush)
+    if args.sweep != "none":
+        res["sweep"] = sweep_leg(args.sweep, 3, 1)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_decode_steps)
     print(json.dumps(res), flush=True)
@@ -372,48 +364,6 @@ def decode_call_bytes(w, E):
     return (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d) * BH
 
 
-def long_context(name, n_calls, n_warm, use_flush):
-    """Decode at a long context: one build of the index, then n_calls timed decode calls
-    (HIP events around each call; cache flush before each, as in the main measurement)."""
-    import torch
-
-    import kv_vector_index_amd as wi
-    import synth
-
-    w = synth.WORKLOADS[name].with_(steps=n_warm + n_calls)
-    nds = n_warm + n_calls
-    x, k, v, q, k_out, v_out, bp, bws, idx, dps, dws, out, lse, sel = setup(w, nds)
-    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda") if use_flush else None
-    ev = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
-    wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws)     # warm
-    be = ev()
-    be[0].record()
-    wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws)
-    be[1].record()
-    calls = [ev() for _ in range(nds)]
-    for s in range(nds):
-        if flush is not None:
-            flush.sum()
-        calls[s][0].record()
-        wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, out, lse, sel[s], dws)
-        calls[s][1].record()
-    torch.cuda.synchronize()
-    build_ms = be[0].elapsed_time(be[1])
-    call_ms = statistics.median(c[0].elapsed_time(c[1]) for c in calls[n_warm:])
-    E, Er = exact_rows(w, idx, sel, nds)
-    nbytes = decode_call_bytes(w, E)
-    gbs = nbytes / (call_ms * 1e-3) / 1e9
-    return {"workload": w.name, "batch": w.batch, "context": w.context,
-            "clusters": w.n_clusters, "n_retrieve": w.n_retrieve,
-            "steady": [w.n_sink, w.n_recent], "decode_calls": n_calls,
-            "decode_call_us": round(call_ms * 1e3, 2),
-            "decode_tok_s": round(w.batch / (call_ms * 1e-3), 1),
-            "decode_bytes_per_call": nbytes, "decode_hbm_GBps": round(gbs, 1),
-            "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "retrieved_tokens_per_kv_head": round(Er, 1),
-            "index_build_ms": round(build_ms, 3),
-            "index_build_tok_s": round(w.batch * w.context / (build_ms * 1e-3), 1)}
-
 def extend_leg(name, n_rep):
     """Index extension: a workload's index built for its context minus one segment, then
     extended to the full context (wave_index_extend: the last, partly indexed segment and
@@ -469,153 +419,6 @@ def extend_leg(name, n_rep):
             "new_tok_s": round(B * (L0 - prev_len) / (ext_ms * 1e-3), 1)}
 
 
-def batched_vs_dense(name, n_calls, n_warm, use_flush):
-    """A batched workload's decode against dense flash-decode over the same resident KV: one
-    index build, then n_calls timed wave calls and n_calls timed dense calls (all L rows of
-    every head; HIP events around each call, cache flush before each)."""
-    import torch
-
-    import kv_vector_index_amd as wi
-    import synth
-
-    w = synth.WORKLOADS[name].with_(steps=n_warm + n_calls)
-    nds = n_warm + n_calls
-    x, k, v, q, k_out, v_out, bp, bws, idx, dps, dws, out, lse, sel = setup(w, nds)
-    print(f"[bench] batched leg {w.name}: B={w.batch} L0={w.context} C={w.n_clusters} "
-          f"n_r={w.n_retrieve}", file=sys.stderr, flush=True)
-    be = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    be[0].record()
-    wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws)
-    be[1].record()
-    torch.cuda.synchronize()
-    del x, k, v, bws
-    torch.cuda.empty_cache()
-    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda") if use_flush else None
-    ev = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
-
-    def timed(call):
-        pairs = [ev() for _ in range(nds)]
-        for s in range(nds):
-            if flush is not None:
-                flush.sum()
-            pairs[s][0].record()
-            call(s)
-            pairs[s][1].record()
-        torch.cuda.synchronize()
-        return statistics.median(p[0].elapsed_time(p[1]) for p in pairs[n_warm:])
-
-    wave_ms = timed(lambda s: wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, out,
-                                                       lse, sel[s], dws))
-    dense_ms = timed(lambda s: wi.wave_dense_decode_attention(dps[s], q[s], k_out, v_out, out,
-                                                              lse, dws))
-    E, Er = exact_rows(w, idx, sel, nds)
-    nbytes = decode_call_bytes(w, E)
-    BH, G, d = w.batch * w.n_kv_heads, w.group, 128
-    L_mid = w.context + (nds + 1) / 2
-    dense_bytes = (4 * d * L_mid + 2 * G * d + 4 * G * d) * BH
-    gbs, dgbs = nbytes / (wave_ms * 1e-3) / 1e9, dense_bytes / (dense_ms * 1e-3) / 1e9
-    build_ms = be[0].elapsed_time(be[1])
-    return {"workload": w.name, "batch": w.batch, "context": w.context,
-            "clusters": w.n_clusters, "n_retrieve": w.n_retrieve, "decode_calls": n_calls,
-            "decode_call_us": round(wave_ms * 1e3, 2),
-            "decode_tok_s": round(w.batch / (wave_ms * 1e-3), 1),
-            "decode_bytes_per_call": nbytes, "decode_hbm_GBps": round(gbs, 1),
-            "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "dense_call_us": round(dense_ms * 1e3, 2),
-            "dense_tok_s": round(w.batch / (dense_ms * 1e-3), 1),
-            "dense_bytes_per_call": dense_bytes, "dense_hbm_GBps": round(dgbs, 1),
-            "dense_hbm_frac": round(dgbs / HBM_PEAK_GBS, 4),
-            "speedup_vs_dense": round(dense_ms / wave_ms, 2),
-            "index_build_ms": round(build_ms, 3),
-            "index_build_tok_s": round(w.batch * w.context / (build_ms * 1e-3), 1)}
-
-
-def accuracy_grid(name, nds, cluster_sizes=(8, 16, 32),
-                  budgets=(0.005, 0.01, 0.018, 0.04, 1.0)):
-    """Error of the wave decode against exact attention (the dense decode over all L rows,
-    itself checked against the oracle's full attention in the tests) on one layer of the
-    workload, for each cluster size (one index build each) and retrieval budget: relative
-    l2 error ||o - o_exact|| / ||o_exact|| per (b, q head, step), mean / p99 / max (budget
-    1.0 retrieves every cluster: exact up to rounding, a check of the comparison). With it,
-    the share of the exact softmax mass that falls on the exactly attended rows (steady and
-    retrieved), for the first KV group of batch element 0 at the first step. An accuracy
-    report of the approximation, not a parity claim."""
-    import numpy as np
-    import torch
-
-    import kv_vector_index_amd as wi
-    import synth
-
-    base = synth.WORKLOADS[name].with_(steps=nds)
-    B, H, Hq, d = base.batch, base.n_kv_heads, base.n_q_heads, 128
-    L0 = base.context
-    t = time.time()
-    x = synth.generate_layer(base)
-    print(f"[bench] accuracy leg {name}: generated inputs in {time.time() - t:.1f}s",
-          file=sys.stderr, flush=True)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
-        torch.bfloat16).cuda()
-    k, v, q = dev(x.k), dev(x.v), dev(x.q)
-    del x
-    k_out, v_out = torch.zeros_like(k), torch.zeros_like(v)
-    k_out[:, :, L0:] = k[:, :, L0:]
-    v_out[:, :, L0:] = v[:, :, L0:]
-    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
-    ref = torch.empty(nds, B, Hq, d, dtype=torch.float32, device="cuda")
-    scale = 1.0 / math.sqrt(d)
-    grid = []
-    for cs in cluster_sizes:
-        w = base.with_(cluster_size=cs)
-        C = w.n_clusters
-        bp = wi.wave_build_params(B, Hq, H, d, L0, w.capacity, w.segment_size,
-                                  w.clusters_per_segment, w.n_iters, w.n_sink, w.n_recent)
-        bws = torch.empty(wi.wave_index_workspace_size(bp), dtype=torch.uint8, device="cuda")
-        idx = wi.alloc_index(B, H, C, L0, optional=False)
-        wi.wave_index_build(bp, k, v, k_out, v_out, idx, bws)
-        del bws
-        for s in range(nds):
-            p = wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
-                                      w.n_recent, 0, scale)
-            ws = wi.alloc_decode_workspace(p)
-            wi.wave_dense_decode_attention(p, q[s], k_out, v_out, ref[s], None, ws)
-        G = Hq // H
-        for beta in budgets:
-            nr = int(math.ceil(beta * C - 1e-9))
-            errs = []
-            sel = torch.empty(B, H, nr, dtype=torch.int32, device="cuda")
-            for s in range(nds):
-                p = wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
-                                          w.n_recent, nr, scale)
-                ws = wi.alloc_decode_workspace(p)
-                wi.wave_decode_attention(p, q[s], k_out, v_out, idx, out, None,
-                                         sel if s == 0 else None, ws)
-                e = (out - ref[s]).norm(dim=-1) / ref[s].norm(dim=-1)
-                errs.append(e.flatten())
-            e = torch.cat(errs).double().cpu().numpy()
-            # exact softmax mass on the exactly attended rows: batch 0, KV group 0, step 0
-            L = L0 + 1
-            m_np = np.zeros(L, dtype=bool)  # (built on the host, copied once)
-            m_np[:w.n_sink] = True
-            m_np[L0 - w.n_recent:L] = True
-            ids = sel[0, 0].cpu().numpy()
-            off = idx.cluster_offset[0, 0].cpu().numpy()
-            size = idx.cluster_size[0, 0].cpu().numpy()
-            for j in ids[ids >= 0]:
-                m_np[int(off[j]):int(off[j]) + int(size[j])] = True
-            mask = torch.from_numpy(m_np).cuda()
-            logits = (k_out[0, 0, :L].float() @ q[0][0, :G].float().T) * scale  # [L, G]
-            mass = torch.softmax(logits, dim=0)[mask].sum(dim=0).mean().item()
-            grid.append({"cluster_size": cs, "clusters": C, "budget": beta, "n_retrieve": nr,
-                         "rel_l2_mean": float(f"{e.mean():.3e}"),
-                         "rel_l2_p99": float(f"{np.percentile(e, 99):.3e}"),
-                         "rel_l2_max": float(f"{e.max():.3e}"),
-                         "exact_zone_mass": round(mass, 4)})
-        del idx
-        torch.cuda.empty_cache()
-    return {"workload": name, "batch": B, "context": L0, "n_q_heads": Hq, "n_kv_heads": H,
-            "decode_steps": nds, "reference": "dense decode over all L rows", "grid": grid}
-
-
 def kernel_sources_hash() -> str:
     """Hash of the HIP sources: traffic figures are only valid for the kernels they measured."""
     import hashlib
@@ -640,44 +443,357 @@ def load_traffic() -> dict:
     return t.get("bytes_per_launch", {})
 
 
-def cpu_baseline(w, x, n_steps):
-    """The oracle, untuned, on a bounded sample of the same workload (host cores)."""
+def stack_leg(name, n_steps, n_warm, dense):
+    """A whole model's attention layers resident in HBM: n_layers layers of the workload,
+    each with its own permuted K/V cache and index (distinct buffers; the contents of layer 0
+    replicated, since drawing every layer on the host would take minutes), built from the
+    raw cache one layer after the other (the build timed over the whole stack), then decode
+    steps of one call per layer (a model is layer-sequential; the other layers evict the
+    caches, so no flush). Layer l decodes step s with the queries of step (s + l) mod steps
+    so that the layers select different clusters. HIP events around each step's layer loop;
+    with `dense`, the same steps with dense flash-decode over every layer's whole cache."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    import torch
 
+    import kv_vector_index_amd as wi
+    import synth
+
+    nq = n_steps + n_warm
+    w = synth.WORKLOADS[name].with_(steps=nq)
+    nL = w.n_layers
+    B, H, Hq, G, d = w.batch, w.n_kv_heads, w.n_q_heads, w.group, 128
+    L0, C, nr = w.context, w.n_clusters, w.n_retrieve
+    t = time.time()
+    x = synth.generate_layer(w)
+    print(f"[bench] stack leg {name}: {nL} layers, B={B} L0={L0} C={C} n_r={nr}; generated "
+          f"inputs in {time.time() - t:.1f}s", file=sys.stderr, flush=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    k, v, q = dev(x.k), dev(x.v), dev(x.q)
+    del x
+    bp = wi.wave_build_params(B, Hq, H, d, L0, w.capacity, w.segment_size,
+                              w.clusters_per_segment, w.n_iters, w.n_sink, w.n_recent)
+    bws = torch.empty(wi.wave_index_workspace_size(bp), dtype=torch.uint8, device="cuda")
+    layers = []
+    for _ in range(nL):
+        ko, vo = torch.empty_like(k), torch.empty_like(v)
+        ko[:, :, L0:] = k[:, :, L0:]                       # decode-appended rows
+        vo[:, :, L0:] = v[:, :, L0:]
+        layers.append((ko, vo, wi.alloc_index(B, H, C, L0, optional=False)))
+    ev = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
+    be = [ev() for _ in range(nL)]
+    torch.cuda.synchronize()
+    for l, (ko, vo, idx) in enumerate(layers):
+        be[l][0].record()
+        wi.wave_index_build(bp, k, v, ko, vo, idx, bws)
+        be[l][1].record()
+    torch.cuda.synchronize()
+    build_ms = [e[0].elapsed_time(e[1]) for e in be]
+    stack_build_ms = be[0][0].elapsed_time(be[-1][1])
+    del k, v, bws
+    torch.cuda.empty_cache()
+    scale = 1.0 / math.sqrt(d)
+    dps = [wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
+                                 w.n_recent, nr, scale) for s in range(nq)]
+    dws = wi.alloc_decode_workspace(dps[0])
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+    sel = torch.empty(nL, nq, B, H, max(nr, 1), dtype=torch.int32, device="cuda")
+
+    def steps(call):
+        step_ev = [ev() for _ in range(nq)]
+        l0_ev = [ev() for _ in range(nq)]
+        for s in range(nq):
+            step_ev[s][0].record()
+            for l in range(nL):
+                if l == 0:
+                    l0_ev[s][0].record()
+                call(s, l)
+                if l == 0:
+                    l0_ev[s][1].record()
+            step_ev[s][1].record()
+        torch.cuda.synchronize()
+        st = sorted(e[0].elapsed_time(e[1]) for e in step_ev[n_warm:])
+        l0 = statistics.median(e[0].elapsed_time(e[1]) for e in l0_ev[n_warm:])
+        return st, l0
+
+    def wave_call(s, l):
+        ko, vo, idx = layers[l]
+        wi.wave_decode_attention(dps[s], q[(s + l) % nq], ko, vo, idx, out, lse, sel[l, s], dws)
+
+    st, l0_ms = steps(wave_call)
+    med = statistics.median(st)
+    # algorithmic bytes of every timed (layer, step) call, from the selections
+    csize = [layers[l][2].cluster_size.cpu().numpy() for l in range(nL)]
+    selh = sel.cpu().numpy()
+    step_bytes = []
+    for s in range(n_warm, nq):
+        tot = 0.0
+        for l in range(nL):
+            ids = selh[l, s, :, :, :nr]
+            E = 0.0
+            for b in range(B):
+                for g in range(H):
+                    i = ids[b, g]
+                    E += w.n_sink + w.n_recent + s + 1 + float(csize[l][b, g, i[i >= 0]].sum())
+            tot += decode_call_bytes(w, E / (B * H))
+        step_bytes.append(tot)
+    nbytes = float(np.mean(step_bytes))
+    gbs = nbytes / (med * 1e-3) / 1e9
+    # per-kernel times of one traced call (layer 0, last step)
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for e in kev:
+        e.record()
+    ko, vo, idx = layers[0]
+    n_ev = wi.wave_decode_attention(dps[-1], q[-1], ko, vo, idx, out, lse, sel[0, -1], dws,
+                                    events=[e.cuda_event for e in kev])
+    torch.cuda.synchronize()
+    names = ["score", "hist", "gather", "retrieve"] if n_ev == 8 else ["score", "gather",
+                                                                        "retrieve"]
+    kernel_us = {nm: round(kev[2 * i].elapsed_time(kev[2 * i + 1]) * 1e3, 2)
+                 for i, nm in enumerate(names)}
+    res = {"workload": w.name, "layers": nL, "batch": B, "context": L0, "n_q_heads": Hq,
+           "n_kv_heads": H, "clusters": C, "n_retrieve": nr, "steady": [w.n_sink, w.n_recent],
+           "layer_contents": "layer 0 replicated into every layer's own buffers; layer l "
+                             "decodes with the queries of step (s + l) mod steps",
+           "decode_steps": n_steps, "warmup_steps": n_warm,
+           "step_ms": round(med, 4),
+           "step_ms_p10_p90": [round(st[int(0.1 * (len(st) - 1))], 4),
+                               round(st[int(0.9 * (len(st) - 1))], 4)],
+           "decode_tok_s": round(B / (med * 1e-3), 1),
+           "decode_bytes_per_step": nbytes, "decode_hbm_GBps": round(gbs, 1),
+           "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "layer0_call_us": round(l0_ms * 1e3, 2),
+           "step_vs_layers_x_layer0_call": round(med / (nL * l0_ms), 3),
+           "kernel_us_one_call": kernel_us,
+           "index_build_ms_stack": round(stack_build_ms, 3),
+           "index_build_ms_per_layer": round(statistics.median(build_ms), 3),
+           "index_build_tok_s_stack": round(B * L0 * nL / (stack_build_ms * 1e-3), 1)}
+    if dense:
+        def dense_call(s, l):
+            ko, vo, _ = layers[l]
+            wi.wave_dense_decode_attention(dps[s], q[(s + l) % nq], ko, vo, out, lse, dws)
+        dst, _ = steps(dense_call)
+        dmed = statistics.median(dst)
+        L_mid = L0 + (n_warm + 1 + nq) / 2
+        dense_bytes = (4 * d * L_mid + 2 * G * d + 4 * G * d) * B * H * nL
+        dgbs = dense_bytes / (dmed * 1e-3) / 1e9
+        res.update({"dense_step_ms": round(dmed, 4),
+                    "dense_tok_s": round(B / (dmed * 1e-3), 1),
+                    "dense_bytes_per_step": dense_bytes, "dense_hbm_GBps": round(dgbs, 1),
+                    "dense_hbm_frac": round(dgbs / HBM_PEAK_GBS, 4),
+                    "speedup_vs_dense": round(dmed / med, 2)})
+    del layers, dws
+    torch.cuda.empty_cache()
+    return res
+
+
+def sweep_leg(name, n_steps, n_warm, cluster_sizes=(8, 16, 32),
+              budgets=(0.005, 0.01, 0.018, 0.04), err_steps=4):
+    """The Qwen-shaped stack (28 resident layers, layer 0 replicated as in stack_leg) over
+    cluster sizes x retrieval budgets: per point, the decode step time of the layer loop
+    (tokens/s, HBM GB/s on algorithmic bytes) and the error of layer 0's wave decode against
+    exact attention (dense decode over all L rows, itself checked against the oracle's full
+    attention in the tests): relative l2 error per (b, q head) over err_steps steps (mean /
+    p99 / max), and the share of the exact softmax mass on the exactly attended rows (batch
+    element 0, KV group 0, first step). Budget 1.0 (every cluster retrieved) is also run on
+    layer 0 as a check of the comparison (rounding-level error)."""
+    import numpy as np
+    import torch
+
+    import kv_vector_index_amd as wi
+    import synth
+
+    nq = max(n_steps + n_warm, err_steps)
+    base = synth.WORKLOADS[name].with_(steps=nq)
+    nL, B, H, Hq, G, d = base.n_layers, base.batch, base.n_kv_heads, base.n_q_heads, base.group, 128
+    L0 = base.context
+    t = time.time()
+    x = synth.generate_layer(base)
+    print(f"[bench] sweep leg {name}: {nL} layers; generated inputs in {time.time() - t:.1f}s",
+          file=sys.stderr, flush=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    k, v, q = dev(x.k), dev(x.v), dev(x.q)
+    del x
+    scale = 1.0 / math.sqrt(d)
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    ref = torch.empty(err_steps, B, Hq, d, dtype=torch.float32, device="cuda")
+    ev = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
+    grid = []
+    for cs in cluster_sizes:
+        w = base.with_(cluster_size=cs)
+        C = w.n_clusters
+        bp = wi.wave_build_params(B, Hq, H, d, L0, w.capacity, w.segment_size,
+                                  w.clusters_per_segment, w.n_iters, w.n_sink, w.n_recent)
+        bws = torch.empty(wi.wave_index_workspace_size(bp), dtype=torch.uint8, device="cuda")
+        layers = []
+        be = ev()
+        for l in range(nL):
+            ko, vo = torch.empty_like(k), torch.empty_like(v)
+            ko[:, :, L0:] = k[:, :, L0:]
+            vo[:, :, L0:] = v[:, :, L0:]
+            idx = wi.alloc_index(B, H, C, L0, optional=False)
+            if l == 0:
+                be[0].record()
+            wi.wave_index_build(bp, k, v, ko, vo, idx, bws)
+            layers.append((ko, vo, idx))
+        be[1].record()
+        del bws
+        # exact reference of layer 0
+        ko0, vo0, idx0 = layers[0]
+        for s in range(err_steps):
+            p = wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
+                                      w.n_recent, 0, scale)
+            wi.wave_dense_decode_attention(p, q[s], ko0, vo0, ref[s], None,
+                                           wi.alloc_decode_workspace(p))
+        torch.cuda.synchronize()
+        build_ms = be[0].elapsed_time(be[1])
+        for beta in tuple(budgets) + (1.0,):
+            nr = int(math.ceil(beta * C - 1e-9))
+            dps = [wi.wave_decode_params(B, Hq, H, d, L0 + s + 1, L0, w.capacity, C, w.n_sink,
+                                         w.n_recent, nr, scale) for s in range(nq)]
+            dws = wi.alloc_decode_workspace(dps[0])
+            sel = torch.empty(nq, B, H, nr, dtype=torch.int32, device="cuda")
+            point = {"cluster_size": cs, "clusters": C, "budget": beta, "n_retrieve": nr}
+            if beta < 1.0:
+                step_ev = [ev() for _ in range(nq)]
+                for s in range(nq):
+                    step_ev[s][0].record()
+                    for l in range(nL):
+                        ko, vo, idx = layers[l]
+                        wi.wave_decode_attention(dps[s], q[(s + l) % nq], ko, vo, idx, out,
+                                                 None, sel[s] if l == 0 else None, dws)
+                    step_ev[s][1].record()
+                torch.cuda.synchronize()
+                med = statistics.median(e[0].elapsed_time(e[1]) for e in step_ev[n_warm:])
+                csz = idx0.cluster_size.cpu().numpy()
+                selh = sel.cpu().numpy()
+                E = np.mean([w.n_sink + w.n_recent + s + 1 +
+                             float(csz[b, g, selh[s, b, g][selh[s, b, g] >= 0]].sum())
+                             for s in range(n_warm, nq) for b in range(B) for g in range(H)])
+                nbytes = decode_call_bytes(w, E) * nL
+                gbs = nbytes / (med * 1e-3) / 1e9
+                point.update({"step_ms": round(med, 4), "decode_tok_s": round(B / (med * 1e-3), 1),
+                              "decode_bytes_per_step": nbytes, "decode_hbm_GBps": round(gbs, 1),
+                              "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+            errs = []
+            for s in range(err_steps):
+                wi.wave_decode_attention(dps[s], q[s], ko0, vo0, idx0, out, None, sel[s], dws)
+                errs.append(((out - ref[s]).norm(dim=-1) / ref[s].norm(dim=-1)).flatten())
+            e = torch.cat(errs).double().cpu().numpy()
+            # exact softmax mass on the exactly attended rows: batch 0, KV group 0, step 0
+            L = L0 + 1
+            m_np = np.zeros(L, dtype=bool)
+            m_np[:w.n_sink] = True
+            m_np[L0 - w.n_recent:L] = True
+            ids = sel[0, 0, 0].cpu().numpy()
+            off = idx0.cluster_offset[0, 0].cpu().numpy()
+            size = idx0.cluster_size[0, 0].cpu().numpy()
+            for j in ids[ids >= 0]:
+                m_np[int(off[j]):int(off[j]) + int(size[j])] = True
+            mask = torch.from_numpy(m_np).cuda()
+            logits = (ko0[0, 0, :L].float() @ q[0][0, :G].float().T) * scale  # [L, G]
+            mass = torch.softmax(logits, dim=0)[mask].sum(dim=0).mean().item()
+            point.update({"rel_l2_mean": float(f"{e.mean():.3e}"),
+                          "rel_l2_p99": float(f"{np.percentile(e, 99):.3e}"),
+                          "rel_l2_max": float(f"{e.max():.3e}"),
+                          "exact_zone_mass": round(mass, 4),
+                          "index_build_ms_stack": round(build_ms, 3)})
+            grid.append(point)
+            del dws, sel
+        del layers, idx0, ko0, vo0
+        torch.cuda.empty_cache()
+    return {"workload": name, "layers": nL, "batch": B, "context": L0, "n_q_heads": Hq,
+            "n_kv_heads": H, "decode_steps": n_steps, "warmup_steps": n_warm,
+            "error_steps": err_steps,
+            "layer_contents": "layer 0 replicated into every layer's own buffers; layer l "
+                              "decodes with the queries of step (s + l) mod steps",
+            "reference": "dense decode over all L rows (layer 0)", "grid": grid}
+
+
+def cpu_baseline(w, x, n_dec_steps=16):
+    """The oracle, untuned, on the host cores: with one thread and with all of them
+    (os.sched_getaffinity; BLAS threads limited by threadpoolctl, the oracle's own loops
+    being single-threaded).
+      * the 128K layer (w, inputs x): build = two segments (KV head 0 segment 0, KV head 1
+        the middle segment) through all passes, extrapolated to the layer by the exact work
+        ratio (segments x KV heads);
+        decode = n_dec_steps steps of KV head 0 (its index built by the oracle with one pass,
+        untimed: decode work does not depend on the pass count), extrapolated to all KV heads;
+      * the 4K layer ('tiny'): the whole build (all heads, all passes) and all its decode
+        steps, measured whole.
+    `value` is the 128K decode rate at all cores (tokens/s), like the GPU's."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
     from oracle import wave_oracle as wo
 
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    print("[bench] cpu baseline: oracle build of one (head, segment)", file=sys.stderr,
-          flush=True)
+    cores = len(os.sched_getaffinity(0))
     g = 0
-    lo, hi = wo.segment_ranges(w.context, w.segment_size, w.n_sink, w.n_recent)[0]
-    K0 = wo.bf16_to_f64(x.k[0, g, lo:hi])
-    t = time.perf_counter()
-    wo.cluster_segment(K0, w.clusters_per_segment, w.n_iters)
-    t_seg = time.perf_counter() - t
-    build_tok_s = (hi - lo) / t_seg
-    # decode sample: one KV head, index built by the oracle with one pass (decode cost does
-    # not depend on the pass count), a few steps, scaled to all KV heads of the batch
-    print("[bench] cpu baseline: oracle decode sample", file=sys.stderr, flush=True)
-    hidx, ko, vo = wo.build_head(x.k[0, g], x.v[0, g], w.context, w.segment_size,
-                                 w.clusters_per_segment, 1, w.n_sink, w.n_recent)
+    segs = wo.segment_ranges(w.context, w.segment_size, w.n_sink, w.n_recent)
+    picks = [(0, 0), (1, len(segs) // 2)]
+    Ks = [wo.bf16_to_f64(x.k[0, gg, segs[ss][0]:segs[ss][1]]) for gg, ss in picks]
+    n_pts = sum(K.shape[0] for K in Ks)
+    print("[bench] cpu baseline: oracle index of KV head 0 (decode input, untimed)",
+          file=sys.stderr, flush=True)
+    with threadpool_limits(cores):
+        hidx, ko, vo = wo.build_head(x.k[0, g], x.v[0, g], w.context, w.segment_size,
+                                     w.clusters_per_segment, 1, w.n_sink, w.n_recent)
     kc = np.concatenate([ko, x.k[0, g, w.context:]])
     vc = np.concatenate([vo, x.v[0, g, w.context:]])
     G = w.group
-    t = time.perf_counter()
-    for s in range(n_steps):
-        wo.decode_group(x.q[s][0, g * G:(g + 1) * G], kc, vc, hidx, w.context,
-                        w.context + s + 1, w.n_sink, w.n_recent, w.n_retrieve)
-    t_head = (time.perf_counter() - t) / n_steps
-    step_s = t_head * w.n_kv_heads * w.batch
-    return {"value": round(1.0 / step_s, 3), "unit": "tokens/s", "cores": threads,
+    n_dec = min(n_dec_steps, x.q.shape[0])
+    tw = synth.WORKLOADS["tiny"]
+    tx = synth.generate_layer(tw)
+    runs = {}
+    for threads in (1, cores):
+        print(f"[bench] cpu baseline: {threads} thread(s)", file=sys.stderr, flush=True)
+        with threadpool_limits(threads):
+            t = time.perf_counter()
+            for K in Ks:
+                wo.cluster_segment(K, w.clusters_per_segment, w.n_iters)
+            t_seg = (time.perf_counter() - t) / len(Ks)
+            t = time.perf_counter()
+            for s in range(n_dec):
+                wo.decode_group(x.q[s][0, g * G:(g + 1) * G], kc, vc, hidx, w.context,
+                                w.context + s + 1, w.n_sink, w.n_recent, w.n_retrieve)
+            t_head = (time.perf_counter() - t) / n_dec
+            t = time.perf_counter()
+            tlay = wo.build_layer(tx.k, tx.v, tw.context, tw.segment_size,
+                                  tw.clusters_per_segment, tw.n_iters, tw.n_sink, tw.n_recent)
+            t_tiny_build = time.perf_counter() - t
+            kct = np.concatenate([tlay.k_out, tx.k[:, :, tw.context:]], axis=2)
+            vct = np.concatenate([tlay.v_out, tx.v[:, :, tw.context:]], axis=2)
+            t = time.perf_counter()
+            for s in range(tw.steps):
+                wo.decode_layer(tx.q[s], kct, vct, tlay, tw.context, tw.context + s + 1,
+                                tw.n_sink, tw.n_recent, tw.n_retrieve)
+            t_tiny_dec = (time.perf_counter() - t) / tw.steps
+        n_units = w.batch * w.n_kv_heads
+        runs[threads] = {
+            "threads": threads,
+            "llama128k_decode_tok_s": round(w.batch / (t_head * n_units), 3),
+            "llama128k_decode_step_s": round(t_head * n_units, 4),
+            "llama128k_index_build_tok_s": round(n_pts / len(Ks) / t_seg, 1),
+            "llama128k_index_build_s": round(t_seg * len(segs) * n_units, 2),
+            "tiny_index_build_s": round(t_tiny_build, 3),
+            "tiny_index_build_tok_s": round(tw.batch * tw.context / t_tiny_build, 1),
+            "tiny_decode_step_s": round(t_tiny_dec, 4),
+            "tiny_decode_tok_s": round(tw.batch / t_tiny_dec, 3)}
+    allc = runs[cores]
+    return {"value": allc["llama128k_decode_tok_s"], "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": (f"decode: {n_steps} steps of KV head 0 (index built by the oracle, 1 "
-                       f"pass), scaled x{w.n_kv_heads * w.batch} to all KV heads; build: one "
-                       f"{hi - lo}-token segment, {w.n_iters} passes"),
-            "index_build_tok_s": round(build_tok_s, 1)}
-
+            "sample": (f"128K layer: decode {n_dec} steps of KV head 0 (index by the oracle, 1 "
+                       f"pass, untimed), extrapolated x{w.batch * w.n_kv_heads} to every KV "
+                       f"head; build two segments ({n_pts} tokens) x {w.n_iters} passes, "
+                       f"extrapolated x{len(segs) * w.batch * w.n_kv_heads / 2:g} (segments x "
+                       f"KV heads / 2); 4K layer: whole build and all {tw.steps} decode steps, "
+                       f"measured"),
+            "extrapolated": {"llama128k_decode": w.batch * w.n_kv_heads,
+                             "llama128k_index_build": len(segs) * w.batch * w.n_kv_heads / 2},
+            "one_thread": runs[1], "all_cores": allc}
 
 if __name__ == "__main__":
     main()
