@@ -20,7 +20,10 @@ script.
 Prints one JSON line. `value` is decode-attention tokens/s of the 128K layer (batch / median
 time of one decode call); the index-build rate and achieved HBM bandwidth are extra fields,
 with p10 / p90 of the call time. Further legs in the same line:
-  * extend: the extension of an index built for one segment fewer tokens, against a full build;
+  * extend: the extension of an index built for one segment fewer tokens, against a full
+    build, with decode calls before and after it;
+  * prefill_fused_build: the index built chunk by chunk (one segment of new tokens at a time)
+    on a second stream beside a prefill stand-in, serial against overlapped;
   * stack_b8: the 32-layer Llama-shaped stack at batch 8 and 122 880 tokens, every layer's
     cache and index resident: the build over the stack, decode steps of one call per layer,
     and dense flash-decode steps over the same caches (the speedup);
@@ -61,6 +64,9 @@ def parse():
     ap.add_argument("--extend", default="llama128k",
                     help="time the extension of this workload's index by one segment of new "
                          "tokens against a full build ('none': skip)")
+    ap.add_argument("--prefill", default="llama128k",
+                    help="prefill-fused build of this workload's index, chunk by chunk on a "
+                         "second stream beside a prefill stand-in ('none': skip)")
     ap.add_argument("--stack8", default="llama122k_b8",
                     help="resident multi-layer stack with dense flash-decode beside it: layer "
                          "loops of wave and dense decode calls ('none': skip)")
@@ -283,6 +289,9 @@ def main():
     if args.extend != "none":
         res["extend"] = extend_leg(args.extend, 5)
         torch.cuda.empty_cache()
+    if args.prefill != "none":
+        res["prefill_fused_build"] = prefill_leg(args.prefill)
+        torch.cuda.empty_cache()
     if args.stack8 != "none":
         res["stack_b8"] = stack_leg(args.stack8, args.stack_steps, 2, dense=True)
         torch.cuda.empty_cache()
@@ -365,10 +374,13 @@ def decode_call_bytes(w, E):
 
 
 def extend_leg(name, n_rep):
-    """Index extension: a workload's index built for its context minus one segment, then
+    """Index extension in a decode loop: a workload's index built for its context minus one
+    segment while that segment's tokens were generated (they sit in the recent zone), then
     extended to the full context (wave_index_extend: the last, partly indexed segment and
     the new one are clustered, the rest is copied), against a full build of the same
-    context. Median of n_rep timed calls each (HIP events), after one untimed call."""
+    context; with the decode call before the extension (on the earlier index, the generated
+    tokens attended exactly) and after it. Median of n_rep timed calls each (HIP events),
+    after one untimed call."""
     import numpy as np
     import torch
 
@@ -382,7 +394,7 @@ def extend_leg(name, n_rep):
     x = synth.generate_layer(w, rows=L0 + 1)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
         torch.bfloat16).cuda()
-    k, v = dev(x.k), dev(x.v)
+    k, v, q = dev(x.k), dev(x.v), dev(x.q[0])
     del x
     k_out, v_out = torch.zeros_like(k), torch.zeros_like(v)
 
@@ -396,6 +408,15 @@ def extend_leg(name, n_rep):
     prev = wi.alloc_index(B, H, C_prev, prev_len, optional=False)
     idx = wi.alloc_index(B, H, C, L0, optional=False)
     wi.wave_index_build(bp_prev, k, v, k_out, v_out, prev, ws)
+    k_out[:, :, prev_len:] = k[:, :, prev_len:]            # the tokens generated since
+    v_out[:, :, prev_len:] = v[:, :, prev_len:]
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    nr_prev, nr = (int(math.ceil(w.budget * c - 1e-9)) for c in (C_prev, C))
+    # decode with the earlier index while S generated tokens sit in the recent zone
+    dp_before = wi.wave_decode_params(B, Hq, H, d, L0, prev_len, L0 + 1, C_prev, w.n_sink,
+                                      w.n_recent, nr_prev, scale)
+    dws = wi.alloc_decode_workspace(dp_before)
 
     def timed(call):
         call()
@@ -407,8 +428,15 @@ def extend_leg(name, n_rep):
         torch.cuda.synchronize()
         return statistics.median(e[0].elapsed_time(e[1]) for e in ev)
 
+    before_us = timed(lambda: wi.wave_decode_attention(dp_before, q, k_out, v_out, prev, out,
+                                                       None, None, dws)) * 1e3
     ext_ms = timed(lambda: wi.wave_index_extend(bp, prev_len, k, v, k_out, v_out, prev, idx,
                                                 ws))
+    dp_after = wi.wave_decode_params(B, Hq, H, d, L0 + 1, L0, L0 + 1, C, w.n_sink, w.n_recent,
+                                     nr, scale)
+    dws = wi.alloc_decode_workspace(dp_after)
+    after_us = timed(lambda: wi.wave_decode_attention(dp_after, q, k_out, v_out, idx, out, None,
+                                                      None, dws)) * 1e3
     k_full, v_full = torch.zeros_like(k), torch.zeros_like(v)
     full_ms = timed(lambda: wi.wave_index_build(bp, k, v, k_full, v_full, idx, ws))
     s0 = (prev_len - w.n_recent) // S
@@ -416,7 +444,119 @@ def extend_leg(name, n_rep):
             "segments_built": -(-L0 // S) - s0, "segments_total": -(-L0 // S),
             "extend_ms": round(ext_ms, 3), "full_build_ms": round(full_ms, 3),
             "speedup_vs_full_build": round(full_ms / ext_ms, 2),
-            "new_tok_s": round(B * (L0 - prev_len) / (ext_ms * 1e-3), 1)}
+            "new_tok_s": round(B * (L0 - prev_len) / (ext_ms * 1e-3), 1),
+            "decode_call_us_before": round(before_us, 2),
+            "decode_call_us_after": round(after_us, 2),
+            "extend_cost_per_generated_token_us": round(ext_ms * 1e3 / (L0 - prev_len), 4)}
+
+
+def prefill_leg(name, standin_calls=8):
+    """Prefill-fused index build: the context arrives one segment of S tokens at a time, and
+    after each chunk the index is extended from the previous length (wave_index_extend; the
+    first chunk is a plain build) on a second stream, while the first stream runs a stand-in
+    for the chunk's prefill attention (standin_calls dense decode calls over the prefix that
+    has arrived). Both streams keep the default priority; a chunk's extension waits for that
+    chunk's stand-in (an event). Reported: the same work serially on one stream against the
+    two streams, and whether the final index and cache equal one full build bit for bit."""
+    import numpy as np
+    import torch
+
+    import kv_vector_index_amd as wi
+    import synth
+
+    w = synth.WORKLOADS[name]
+    B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, 128
+    L0, S, K = w.context, w.segment_size, w.clusters_per_segment
+    x = synth.generate_layer(w, rows=L0 + 1)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    k, v, q = dev(x.k), dev(x.v), dev(x.q[0])
+    del x
+    lens = list(range(S, L0, S)) + [L0]
+    Lcap = L0 + 1
+
+    def params(n):
+        return wi.wave_build_params(B, Hq, H, d, n, Lcap, S, K, w.n_iters, w.n_sink, w.n_recent)
+
+    ws = torch.empty(wi.wave_index_workspace_size(params(L0)), dtype=torch.uint8, device="cuda")
+    idxs = [wi.alloc_index(B, H, -(-n // S) * K, n) for n in lens]
+    for i in idxs:
+        i.objective = None
+    # (the shortest prefix needs the largest workspace: its partial count grows with the
+    # rows past the index)
+    dp = wi.wave_decode_params(B, Hq, H, d, lens[0], lens[0], Lcap, 1, 0, 0, 0,
+                               1.0 / math.sqrt(d))
+    dws = wi.alloc_decode_workspace(dp)
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    k_out, v_out = torch.zeros_like(k), torch.zeros_like(v)
+    main_s = torch.cuda.current_stream()
+    build_s = torch.cuda.Stream()
+
+    def standin(n):
+        p = wi.wave_decode_params(B, Hq, H, d, n, n, Lcap, 1, 0, 0, 0, 1.0 / math.sqrt(d))
+        for _ in range(standin_calls):
+            wi.wave_dense_decode_attention(p, q, k, v, out, None, dws)
+
+    def build(c, stream):
+        if c == 0:
+            wi.wave_index_build(params(lens[0]), k, v, k_out, v_out, idxs[0], ws, stream)
+        else:
+            wi.wave_index_extend(params(lens[c]), lens[c - 1], k, v, k_out, v_out, idxs[c - 1],
+                                 idxs[c], ws, stream)
+
+    def run(overlap):
+        t0, t1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        torch.cuda.synchronize()
+        t0.record(main_s)
+        build_s.wait_event(t0)
+        for c, n in enumerate(lens):
+            standin(n)
+            if overlap:
+                e = torch.cuda.Event()
+                e.record(main_s)
+                build_s.wait_event(e)
+                build(c, build_s)
+            else:
+                build(c, main_s)
+        if overlap:
+            e = torch.cuda.Event()
+            e.record(build_s)
+            main_s.wait_event(e)
+        t1.record(main_s)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    run(True)                                          # warm
+    serial_ms = statistics.median(run(False) for _ in range(3))
+    overlap_ms = statistics.median(run(True) for _ in range(3))
+    t0, t1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    t0.record()
+    for n in lens:
+        standin(n)
+    t1.record()
+    torch.cuda.synchronize()
+    standin_ms = t0.elapsed_time(t1)
+    full = wi.alloc_index(B, H, -(-L0 // S) * K, L0)
+    full.objective = None
+    k_full, v_full = torch.zeros_like(k), torch.zeros_like(v)
+    wi.wave_index_build(params(L0), k, v, k_full, v_full, full, ws)
+    torch.cuda.synchronize()
+    same = all(torch.equal(getattr(idxs[-1], f).view(torch.int16) if getattr(full, f).dtype ==
+                           torch.bfloat16 else getattr(idxs[-1], f),
+                           getattr(full, f).view(torch.int16) if getattr(full, f).dtype ==
+                           torch.bfloat16 else getattr(full, f))
+               for f in ("centroid_mean", "value_sum", "cluster_size", "cluster_offset",
+                         "labels", "perm", "last_centroids"))
+    same = same and torch.equal(k_out[:, :, :L0].view(torch.int16),
+                                k_full[:, :, :L0].view(torch.int16))
+    build_ms = max(0.0, serial_ms - standin_ms)
+    return {"workload": name, "chunks": len(lens), "chunk_tokens": S,
+            "standin": f"{standin_calls} dense decode calls over the arrived prefix per chunk",
+            "standin_ms": round(standin_ms, 3), "serial_ms": round(serial_ms, 3),
+            "overlapped_ms": round(overlap_ms, 3),
+            "chunked_build_ms_serial": round(build_ms, 3),
+            "build_hidden_frac": round((serial_ms - overlap_ms) / build_ms, 3) if build_ms else None,
+            "equal_to_full_build": bool(same)}
 
 
 def kernel_sources_hash() -> str:

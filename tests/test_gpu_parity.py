@@ -409,6 +409,96 @@ def test_extension_by_nothing_without_a_steady_zone():
     extend_and_check(full, idx_full, 1024, q=q)
 
 
+def test_chained_extensions_equal_the_full_build():
+    """The prefill-fused build: an index extended one segment of new tokens at a time, from
+    an empty index (only the steady zone) to the whole context, equals the index built in one
+    call, bit for bit, and matches the oracle on every segment and one decode step."""
+    t = tl.torch()
+    rng = np.random.default_rng(27)
+    full, q = tl.ragged_layer(rng, B=1, H=2, Hq=8, L0=2600, steps=1, S=512, kseg=32, T=3,
+                              n_sink=3, n_recent=17)
+    idx_full = full.build()
+    idx_full.objective = None
+    lens = [full.n_sink + full.n_recent] + list(range(512, full.L0, 512)) + [full.L0]
+    cur = tl.Layer(full.k_np, full.v_np, lens[0], full.S, full.kseg, full.T, full.n_sink,
+                   full.n_recent, full.Hq)
+    idx = cur.build()
+    idx.objective = None
+    for n0, n1 in zip(lens[:-1], lens[1:]):
+        say(f"[chained extension] {n0} -> {n1}")
+        nxt = tl.Layer(full.k_np, full.v_np, n1, full.S, full.kseg, full.T, full.n_sink,
+                       full.n_recent, full.Hq)
+        new = wi.alloc_index(full.B, full.H, nxt.C, n1)
+        new.objective = None
+        p = nxt.build_params()
+        ws = t.empty(wi.wave_index_workspace_size(p), dtype=t.uint8, device="cuda")
+        wi.wave_index_extend(p, n0, full.k, full.v, cur.k_out, cur.v_out, idx, new, ws)
+        t.cuda.synchronize()
+        idx = new
+    for f in ("centroid_mean", "value_sum", "cluster_size", "cluster_offset", "labels", "perm",
+              "last_centroids"):
+        a, b = getattr(idx, f), getattr(idx_full, f)
+        assert t.equal(a.view(t.int16) if a.dtype == t.bfloat16 else a,
+                       b.view(t.int16) if b.dtype == t.bfloat16 else b), f
+    L0 = full.L0
+    assert t.equal(cur.k_out[:, :, :L0].view(t.int16), full.k_out[:, :, :L0].view(t.int16))
+    assert t.equal(cur.v_out[:, :, :L0].view(t.int16), full.v_out[:, :, :L0].view(t.int16))
+    ext = tl.Layer.__new__(tl.Layer)
+    ext.__dict__.update(full.__dict__)
+    ext.k_out, ext.v_out = cur.k_out, cur.v_out
+    tl.check_segments(ext, idx, [(0, g, s) for g in range(full.H) for s in range(full.nseg)])
+    out, lse, sel = ext.decode(idx, q[0], L0 + 1, 9)
+    tl.oracle_decode_check(ext, idx, q[0], L0 + 1, 9, out, lse, sel)
+
+
+def test_decode_continues_after_an_extension():
+    """A decode loop across an index extension: decode with the index of 1100 tokens while
+    500 generated tokens accumulate in the recent zone, extend the index to the 1600 tokens
+    (three segments clustered again), and decode on. Before the extension, against the
+    oracle on the earlier index; after it, against the oracle's own index built for 1600
+    tokens (same labels as the extended index) and against the oracle on the extended index."""
+    t = tl.torch()
+    rng = np.random.default_rng(29)
+    full, q = tl.ragged_layer(rng, B=1, H=2, Hq=8, L0=1600, steps=2, S=512, kseg=32, T=3,
+                              n_sink=3, n_recent=17)
+    prev = tl.Layer(full.k_np, full.v_np, 1100, full.S, full.kseg, full.T, full.n_sink,
+                    full.n_recent, full.Hq)
+    idx_prev = prev.build()
+    n_r = 6
+    L = 1400
+    say(f"[decode loop] decode at L={L} on the index of {prev.L0} tokens")
+    out, lse, sel = prev.decode(idx_prev, q[0], L, n_r)
+    tl.oracle_decode_check(prev, idx_prev, q[0], L, n_r, out, lse, sel)
+    say("[decode loop] extend to 1600 tokens")
+    idx_new = wi.alloc_index(full.B, full.H, full.C, full.L0)
+    idx_new.objective = None
+    p = full.build_params()
+    ws = t.empty(wi.wave_index_workspace_size(p), dtype=t.uint8, device="cuda")
+    wi.wave_index_extend(p, prev.L0, full.k, full.v, prev.k_out, prev.v_out, idx_prev, idx_new,
+                         ws)
+    t.cuda.synchronize()
+    ext = tl.Layer.__new__(tl.Layer)
+    ext.__dict__.update(full.__dict__)
+    ext.k_out, ext.v_out = prev.k_out, prev.v_out
+    L = full.L0 + 1
+    n_r = 9
+    say(f"[decode loop] decode at L={L} on the extended index (C={full.C})")
+    out, lse, sel = ext.decode(idx_new, q[1], L, n_r)
+    tl.oracle_decode_check(ext, idx_new, q[1], L, n_r, out, lse, sel)
+    lay = wo.build_layer(full.k_np, full.v_np, full.L0, full.S, full.kseg, full.T, full.n_sink,
+                         full.n_recent)
+    assert np.array_equal(lay.stacked("labels"), idx_new.labels.cpu().numpy()), \
+        "the oracle's own clustering differs from the extended index"
+    kc = np.concatenate([lay.k_out, full.k_np[:, :, full.L0:]], axis=2)
+    vc = np.concatenate([lay.v_out, full.v_np[:, :, full.L0:]], axis=2)
+    G = full.Hq // full.H
+    for g in range(full.H):
+        r = wo.decode_group(q[1][0, g * G:(g + 1) * G], kc[0, g], vc[0, g], lay.heads[0][g],
+                            full.L0, L, full.n_sink, full.n_recent, n_r)
+        assert tl.row_rel_err(out[0, g * G:(g + 1) * G], r.out) <= tl.OUT_TOL
+        assert np.all(np.abs(lse[0, g * G:(g + 1) * G] - r.lse) <= tl.OUT_TOL)
+
+
 def test_extension_with_tiled_assignment():
     """The extension through the other assignment kernel (k_seg > 512 centroids per segment:
     LDS tiles of 128 centroids) and a group of seven query heads."""
