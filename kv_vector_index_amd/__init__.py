@@ -23,7 +23,9 @@ __all__ = [
     "alloc_decode_workspace", "wave_decode_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libwave_index.so")
+# WAVE_INDEX_LIB selects another build of the library (e.g. the sanitized host-only one)
+LIB_PATH = os.environ.get("WAVE_INDEX_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libwave_index.so")
 EXPORTED_SYMBOLS = (
     "wave_status_string", "wave_index_workspace_size", "wave_index_build", "wave_index_extend",
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",

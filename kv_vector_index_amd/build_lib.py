@@ -12,6 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libwave_index.so")
+SAN_LIB = os.path.join(LIBDIR, "libwave_index_san.so")
 SOURCES = ["api.cpp", "build_kernels.hip", "decode_kernels.hip"]
 HEADERS = ["wave_common.h", "wave_kernels.h"]
 
@@ -60,6 +61,25 @@ def build(verbose: bool = False) -> str:
          verbose)
     os.replace(tmp, LIB)
     return LIB
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The C ABI's host side alone (argument validation, workspace layout; kernel launchers
+    replaced by host_stubs.cpp, which report that nothing can run), built by the host
+    compiler with AddressSanitizer and UndefinedBehaviorSanitizer. Load it with the ASan
+    runtime preloaded (`g++ -print-file-name=libasan.so`)."""
+    os.makedirs(LIBDIR, exist_ok=True)
+    cxx = shutil.which("g++")
+    if not cxx:
+        raise RuntimeError("g++ not found")
+    tmp = SAN_LIB + ".tmp"
+    cmd = [cxx, "-std=c++17", "-O1", "-g", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "host_stubs.cpp"), "-o", tmp]
+    _run(cmd, verbose)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
 
 
 if __name__ == "__main__":
