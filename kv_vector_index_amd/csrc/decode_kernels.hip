@@ -764,6 +764,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_hist(DecodeArgs a) {
 // ------------------------------------------------------------------------------------
 // kernel 3: gather (the selection) and estimate (every cluster's centroid term)
 // ------------------------------------------------------------------------------------
+constexpr int kTieLds = 1024;  // cut-bin clusters staged in LDS by the finishing workgroup
 struct FinShared {
   union {
     struct {
@@ -774,7 +775,10 @@ struct FinShared {
     uint32_t full[kHistBins + 1 + kHistBins / 16 + 1];  // all the head's scores (+ a spare
                                                         // bin; padded)
   } u;
-  int32_t lst[kMaxClusters / 32];      // the first kMaxClusters / 32 listed ids
+  int32_t lst[kMaxClusters / 32];      // the first kMaxClusters / 32 listed ids (before the
+                                       // publishing: the clusters above the cut bin)
+  float tk[kTieLds];                   // the clusters of the cut bin: scores and ids
+  int32_t ti[kTieLds];
   float ck[kCand];
   int32_t ci[kCand];
   int32_t wgr[kMaxRetrieveWG + 1];
@@ -867,12 +871,13 @@ __device__ __forceinline__ int nth_bit(FinShared& sh, int nwords, uint32_t need)
 }
 
 // The need-th lowest id among the n listed clusters whose score equals v (need >= 1).
-__device__ int nth_id_with_score(const float* tk, const int32_t* ti, uint32_t n, float v,
-                                 uint32_t need, FinShared& sh) {
+template <typename LK, typename LI>
+__device__ int nth_id_with_score(LK tk, LI ti, uint32_t n, float v, uint32_t need,
+                                 FinShared& sh) {
   for (int i = threadIdx.x; i < kMaxClusters / 32; i += kDecThreads) sh.u.bits[i] = 0u;
   __syncthreads();
   for (uint32_t k = threadIdx.x; k < n; k += kDecThreads)
-    if (ld_dev(tk + k) == v) mark(sh, ld_dev(ti + k));
+    if (tk(k) == v) mark(sh, ti(k));
   __syncthreads();
   return nth_bit(sh, kMaxClusters / 32, need);
 }
@@ -880,13 +885,15 @@ __device__ int nth_id_with_score(const float* tk, const int32_t* ti, uint32_t n,
 // (Tkey, Tid): the need-th pair (score descending, id ascending) among the n listed
 // clusters of the cut bin (1 <= need < n). Value-range histograms narrow the range until
 // the bin holding the pair has at most kCand scores, which are then ranked exactly.
-__device__ void cut_pair(const float* tk, const int32_t* ti, uint32_t n, uint32_t need,
-                         FinShared& sh, float& Tkey, int& Tid) {
+// tk(k), ti(k): the k-th listed score and id (global memory or LDS).
+template <typename LK, typename LI>
+__device__ void cut_pair(LK tk, LI ti, uint32_t n, uint32_t need, FinShared& sh, float& Tkey,
+                         int& Tid) {
   constexpr int NT = kDecThreads, BPT = kNarrowBins / NT;
   const int tid = threadIdx.x;
   Red3 r{kPosInf, kNegInf, 0u};
   for (uint32_t k = tid; k < n; k += NT) {
-    const float v = ld_dev(tk + k);
+    const float v = tk(k);
     r.mn = fminf(r.mn, v);
     r.mx = fmaxf(r.mx, v);
   }
@@ -906,7 +913,7 @@ __device__ void cut_pair(const float* tk, const int32_t* ti, uint32_t n, uint32_
     __syncthreads();
     for (uint32_t k0 = 0; k0 < n; k0 += NT) {
       const uint32_t k = k0 + tid;
-      const float v = k < n ? ld_dev(tk + k) : kNegInf;
+      const float v = k < n ? tk(k) : kNegInf;
       const bool in = k < n && v >= lo && v <= hi;
       hist_add<10, kNarrowPad>(sh.u.hist, in ? bin(v) : 0, in);
     }
@@ -934,11 +941,11 @@ __device__ void cut_pair(const float* tk, const int32_t* ti, uint32_t n, uint32_
     const uint32_t need2 = need - sh.v[1], cnt = sh.u.hist[padded<kNarrowPad>(bstar)];
     if (cnt <= (uint32_t)kCand) {
       for (uint32_t k = tid; k < n; k += NT) {
-        const float v = ld_dev(tk + k);
+        const float v = tk(k);
         if (v >= lo && v <= hi && bin(v) == bstar) {
           const uint32_t c = atomicAdd(&sh.v[2], 1u);
           sh.ck[c] = v;
-          sh.ci[c] = ld_dev(ti + k);
+          sh.ci[c] = ti(k);
         }
       }
       __syncthreads();
@@ -963,7 +970,7 @@ __device__ void cut_pair(const float* tk, const int32_t* ti, uint32_t n, uint32_
     }
     Red3 rb{kPosInf, kNegInf, 0u};
     for (uint32_t k = tid; k < n; k += NT) {
-      const float v = ld_dev(tk + k);
+      const float v = tk(k);
       if (v >= lo && v <= hi && bin(v) == bstar) {
         rb.mn = fminf(rb.mn, v);
         rb.mx = fmaxf(rb.mx, v);
@@ -1126,17 +1133,39 @@ __device__ __forceinline__ void finish_select(const DecodeArgs& a, int bh, uint3
   const uint32_t ntie = min(ld_dev(ctr + kCtrTie), (uint32_t)a.C);
   const float* tk = a.tie_key + cb;
   const int32_t* ti = a.tie_id + cb;
+  const int32_t* su = a.sure + (size_t)bh * a.rcap;
   float Tkey = kNegInf;  // default: every listed cluster of the cut bin
   int Tid = 0x7fffffff;
-  if (need > nsure && need - nsure < ntie) cut_pair(tk, ti, ntie, need - nsure, sh, Tkey, Tid);
+  // the lists in LDS when they fit (one round of loads for both), so that the ranking and
+  // the marking below read them from there
+  const bool staged = ntie <= (uint32_t)kTieLds && nsure <= (uint32_t)(kMaxClusters / 32);
+  if (staged) {
+    for (uint32_t k = tid; k < ntie; k += NT) {
+      sh.tk[k] = ld_dev(tk + k);
+      sh.ti[k] = ld_dev(ti + k);
+    }
+    for (uint32_t k = tid; k < nsure; k += NT) sh.lst[k] = ld_dev(su + k);
+    __syncthreads();
+    if (need > nsure && need - nsure < ntie)
+      cut_pair([&](uint32_t k) { return sh.tk[k]; }, [&](uint32_t k) { return sh.ti[k]; }, ntie,
+               need - nsure, sh, Tkey, Tid);
+  } else if (need > nsure && need - nsure < ntie) {
+    cut_pair([&](uint32_t k) { return ld_dev(tk + k); }, [&](uint32_t k) { return ld_dev(ti + k); },
+             ntie, need - nsure, sh, Tkey, Tid);
+  }
   for (int i = tid; i < (a.C + 31) / 32; i += NT) sh.u.bits[i] = 0u;
   __syncthreads();
   if (need > 0) {
-    const int32_t* su = a.sure + (size_t)bh * a.rcap;
-    for (uint32_t k = tid; k < nsure; k += NT) mark(sh, ld_dev(su + k));
-    for (uint32_t k = tid; k < ntie; k += NT) {
-      const int j = ld_dev(ti + k);
-      if (is_selected(ld_dev(tk + k), j, Tkey, Tid)) mark(sh, j);
+    if (staged) {
+      for (uint32_t k = tid; k < nsure; k += NT) mark(sh, sh.lst[k]);
+      for (uint32_t k = tid; k < ntie; k += NT)
+        if (is_selected(sh.tk[k], sh.ti[k], Tkey, Tid)) mark(sh, sh.ti[k]);
+    } else {
+      for (uint32_t k = tid; k < nsure; k += NT) mark(sh, ld_dev(su + k));
+      for (uint32_t k = tid; k < ntie; k += NT) {
+        const int j = ld_dev(ti + k);
+        if (is_selected(ld_dev(tk + k), j, Tkey, Tid)) mark(sh, j);
+      }
     }
   }
   __syncthreads();
@@ -1734,10 +1763,6 @@ constexpr int kVBlockWords = 288;      // 1024 bytes of rows + 128 bytes of spac
 template <int G>
 struct RetWave {
   uint32_t vrows[8][kVBlockWords];
-  float lg[G][kRetBlock];              // log2-domain logits [head][row]
-  int32_t krow[kRetBlock];             // cache row of a token row, -1 removal row, -2 padding
-  int32_t clu[kRetBlock];              // cluster id of a removal row
-  float wgt[kRetBlock];                // denominator weight: 1 token, -n_j removal, 0 padding
 };
 template <int G>
 struct RetMerge {  // the same LDS after the attend: each wave's rows and (m, l) per head
@@ -1761,84 +1786,89 @@ struct MfmaState {
   float m, l;
 };
 
-// Exact attention and estimate removal over the virtual rows [ts, te) of the listed clusters
-// in LDS (first virtual row l_ts[] with l_ts[cnt] = end, first cache row l_co[], cluster id
-// l_id[]), in blocks of 32 rows: block k of the range goes to wave k % 4. Per block: the row
-// descriptors (lanes 0..31), the keys of the token rows as B operands straight from memory
-// (16 rows x 64 bytes per load) and the value rows (or the removed clusters' value sums)
-// into LDS by direct loads; logits q.k on v_mfma_f32_16x16x32_bf16 (A: the group's queries);
-// the removal rows' logits are the score kernel's; then the weights p = 2^(s - m) (negated
-// for removal rows: their value sum leaves the numerator, n_j p the denominator) as the A
-// operand, hi and lo bf16 parts in rows h and G + h, against the value rows read back
-// transposed.
+// Descriptors of the virtual rows [c0, c0 + n) (n <= kDecThreads) of the listed clusters in
+// LDS (first virtual row l_ts[] with l_ts[cnt] = end, first cache row l_co[], cluster id
+// l_id[]), one row per thread: src = the cache row of a token row, or -1 - j for the removal
+// row of cluster j (its centroid key and value sum); wgt = the row's denominator weight (1 for
+// a token, -n_j for a removal row). Rows from n on are padding: src 0, wgt 0.
+__device__ __forceinline__ void describe_rows(int c0, int n, const int32_t* l_ts,
+                                              const int32_t* l_co, const int32_t* l_id, int cnt,
+                                              int32_t* d_src, float* d_wgt) {
+  const int tid = threadIdx.x, t = c0 + tid;
+  int32_t src = 0;
+  float wgt = 0.f;
+  if (tid < n) {
+    int lo = 0, hi = cnt - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (l_ts[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int off = t - l_ts[lo], nj = l_ts[lo + 1] - l_ts[lo] - 1;
+    if (off < nj) {
+      src = l_co[lo] + off;
+      wgt = 1.f;
+    } else {
+      src = -1 - l_id[lo];
+      wgt = -(float)nj;
+    }
+  }
+  d_src[tid] = src;
+  d_wgt[tid] = wgt;
+}
+
+// Exact attention and estimate removal over the described rows [0, nrows) (d_src, d_wgt in
+// LDS), in blocks of 32 rows: block k goes to wave k % 4. Per block: the logits as the
+// transposed product S^T = K Q^T on v_mfma_f32_16x16x32_bf16, A = the key rows straight from
+// memory (a removal row's key is its cluster's centroid, so that its logit is the cluster's
+// score), B = the group's queries (column c holds head c mod G for c < 2G, zero beyond).
+// Tile tau puts table row 8 (m >> 2) + 4 tau + (m & 3) in its row m, so that lane (g, c) ends
+// with the logits of rows 8 g .. 8 g + 7 for its column's head: the A operand layout of the
+// weights, without an exchange. The value rows (or value sums) go to LDS by direct loads;
+// the weights p = 2^(s - m) (negated for removal rows: their value sum leaves the numerator,
+// n_j p the denominator) form the A operand, hi and lo bf16 parts in rows h and G + h,
+// against the value rows read back transposed.
 template <int G>
-__device__ __forceinline__ void attend_virtual_mfma(const DecodeArgs& a, int bh,
-                                                    const bf16x8 (&qa)[4], MfmaState& st,
-                                                    int ts, int te, const int32_t* l_ts,
-                                                    const int32_t* l_co, const int32_t* l_id,
-                                                    int cnt, RetWave<G>& W) {
+__device__ __forceinline__ void attend_rows_mfma(const DecodeArgs& a, int bh,
+                                                 const bf16x8 (&qb)[4], MfmaState& st,
+                                                 int nrows, const int32_t* d_src,
+                                                 const float* d_wgt, RetWave<G>& W) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
   typedef __attribute__((ext_vector_type(4))) float floatx4;
   typedef __attribute__((ext_vector_type(4))) short shortx4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
   const size_t kb = (size_t)bh * a.Lcap, cb = (size_t)bh * a.C;
   const bool arow = n < 2 * G;
-  const int hA = n < G ? n : (arow ? n - G : 0);  // head of this lane's A row
-  for (int t0 = ts + kRetBlock * wave; t0 < te; t0 += kRetBlock * (kDecThreads / 64)) {
-    // ---- descriptors of rows t0 .. t0 + 31 (lanes 0..31), and the removal rows' logits
-    float rl[G];
-    int kr = -2, cl = 0;
-    float wt = 0.f;
-    if (lane < kRetBlock) {
-      const int t = t0 + lane;
-      if (t < te) {
-        int lo = 0, hi = cnt - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (l_ts[mid] <= t) lo = mid; else hi = mid - 1;
-        }
-        const int off = t - l_ts[lo], nj = l_ts[lo + 1] - l_ts[lo] - 1;
-        if (off < nj) {
-          kr = l_co[lo] + off;
-          wt = 1.f;
-        } else {
-          kr = -1;
-          cl = l_id[lo];
-          wt = -(float)nj;
-        }
-      }
-      W.krow[lane] = kr;
-      W.clu[lane] = cl;
-      W.wgt[lane] = wt;
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        rl[h] = kr == -1 ? a.scores[(cb + cl) * G + h] : kNegInf;
-    }
-    __builtin_amdgcn_wave_barrier();
-    // ---- keys (B operands of the logits) and value rows (LDS)
-    u32x4 kbv[2][4];
-    int krow_of[2];
+  for (int r0 = kRetBlock * wave; r0 < nrows; r0 += kRetBlock * (kDecThreads / 64)) {
+    // ---- key rows (A operands of the two tiles), straight from memory
+    u32x4 ka[2][4];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      krow_of[tau] = W.krow[16 * tau + n];
-      const size_t row = kb + (krow_of[tau] >= 0 ? krow_of[tau] : 0);
+      const int32_t src = d_src[r0 + 8 * (n >> 2) + 4 * tau + (n & 3)];
+      const uint16_t* kp = src >= 0 ? a.k + (kb + src) * kHeadDim
+                                    : a.cmean + (cb + (-1 - src)) * kHeadDim;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        kbv[tau][s4] = ld16_stream(a.k + row * kHeadDim + s4 * 32 + g * 8);
+      for (int s4 = 0; s4 < 4; ++s4) ka[tau][s4] = ld16_stream(kp + s4 * 32 + g * 8);
     }
+    // ---- value rows (or value sums) into LDS
     {
       const int slot = lane >> 4, cidx = (n - 2 * slot) & 15;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int r = 8 * slot + e;
-        const int k2 = W.krow[r];
-        const uint16_t* src = k2 >= 0 ? a.v + (kb + k2) * kHeadDim
-                                      : (k2 == -1 ? a.vsum + (cb + W.clu[r]) * kHeadDim
-                                                  : a.v + kb * kHeadDim);
-        __builtin_amdgcn_global_load_lds(src + cidx * 8, (lds_ptr)&W.vrows[e][0], 16, 0, 0);
+        const int32_t src = d_src[r0 + 8 * slot + e];
+        const uint16_t* vp = src >= 0 ? a.v + (kb + src) * kHeadDim
+                                      : a.vsum + (cb + (-1 - src)) * kHeadDim;
+        __builtin_amdgcn_global_load_lds(vp + cidx * 8, (lds_ptr)&W.vrows[e][0], 16, 0, 0);
       }
     }
-    // ---- logits of the token rows (MFMA), the others from the descriptors
+    // ---- denominator weights of this lane's rows 8 g .. 8 g + 7
+    float wv[8];
+    {
+      const float4* wp = reinterpret_cast<const float4*>(d_wgt + r0 + 8 * g);
+      const float4 y0 = wp[0], y1 = wp[1];
+      wv[0] = y0.x; wv[1] = y0.y; wv[2] = y0.z; wv[3] = y0.w;
+      wv[4] = y1.x; wv[5] = y1.y; wv[6] = y1.z; wv[7] = y1.w;
+    }
+    // ---- logits: lane (g, c) gets rows 8 g + 4 tau + i of its column's head
     floatx4 dq[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
@@ -1846,32 +1876,14 @@ __device__ __forceinline__ void attend_virtual_mfma(const DecodeArgs& a, int bh,
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
         dq[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            qa[s4], __builtin_bit_cast(bf16x8, kbv[tau][s4]), dq[tau], 0, 0, 0);
+            __builtin_bit_cast(bf16x8, ka[tau][s4]), qb[s4], dq[tau], 0, 0, 0);
     }
+    float sv[8];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 4 * g + i;
-        if (h < G && krow_of[tau] >= 0) W.lg[h][16 * tau + n] = dq[tau][i] * a.scale_log2;
-      }
-    if (lane < kRetBlock && kr < 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) W.lg[h][lane] = rl[h];
-    }
-    __builtin_amdgcn_wave_barrier();
-    // ---- weights of this lane's rows 8 g .. 8 g + 7 for its A row's head
-    float sv[8], wv[8];
-    {
-      const float4* lp = reinterpret_cast<const float4*>(&W.lg[hA][8 * g]);
-      const float4 x0 = lp[0], x1 = lp[1];
-      sv[0] = x0.x; sv[1] = x0.y; sv[2] = x0.z; sv[3] = x0.w;
-      sv[4] = x1.x; sv[5] = x1.y; sv[6] = x1.z; sv[7] = x1.w;
-      const float4* wp = reinterpret_cast<const float4*>(&W.wgt[8 * g]);
-      const float4 y0 = wp[0], y1 = wp[1];
-      wv[0] = y0.x; wv[1] = y0.y; wv[2] = y0.z; wv[3] = y0.w;
-      wv[4] = y1.x; wv[5] = y1.y; wv[6] = y1.z; wv[7] = y1.w;
-    }
+      for (int i = 0; i < 4; ++i)
+        sv[4 * tau + i] = wv[4 * tau + i] != 0.f ? dq[tau][i] * a.scale_log2 : kNegInf;
     float mb = kNegInf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) mb = fmaxf(mb, sv[e]);
@@ -1997,6 +2009,8 @@ template <int G, bool XM1>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_retrieve(DecodeArgs a) {
   __shared__ float s_x[G][kPartStride];  // this workgroup's share of the earlier partials
   __shared__ int32_t l_ts[kWinR + 1], l_co[kWinR], l_id[kWinR];
+  __shared__ int32_t d_src[kDecThreads];  // the current rows' descriptors (describe_rows)
+  __shared__ __align__(16) float d_wgt[kDecThreads];
   __shared__ RetLds<G> lds;
   const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv, w_item = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -2037,16 +2051,17 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
       }
     }
   }
-  // A operands of the logits: query head `lane % 16` (zero beyond G), dims 32 s + 8 (lane / 16)
-  bf16x8 qa[4];
+  // B operands of the logits: column c = lane % 16 holds query head c mod G for c < 2G (zero
+  // beyond), dims 32 s + 8 (lane / 16)
+  bf16x8 qb[4];
   {
-    const int qh = lane & 15, kg = lane >> 4;
+    const int qc = lane & 15, kg = lane >> 4, qh = qc < G ? qc : qc - G;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       u32x4 v = {0, 0, 0, 0};
-      if (qh < G)
+      if (qc < 2 * G)
         v = ld16(a.q + ((size_t)(b * a.Hq + g * G + qh) * kHeadDim + s4 * 32 + kg * 8));
-      qa[s4] = __builtin_bit_cast(bf16x8, v);
+      qb[s4] = __builtin_bit_cast(bf16x8, v);
     }
   }
   MfmaState st;
@@ -2066,8 +2081,13 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
     }
     __syncthreads();
     const int ts = max(T0, l_ts[0]), te = min(T1, l_ts[cnt]);
-    if (ts < te)
-      attend_virtual_mfma<G>(a, bh, qa, st, ts, te, l_ts, l_co, l_id, cnt, lds.w[wave]);
+    for (int c0 = ts; c0 < te; c0 += kDecThreads) {
+      const int nr = min(kDecThreads, te - c0);
+      describe_rows(c0, nr, l_ts, l_co, l_id, cnt, d_src, d_wgt);
+      __syncthreads();
+      attend_rows_mfma<G>(a, bh, qb, st, nr, d_src, d_wgt, lds.w[wave]);
+      __syncthreads();
+    }
     __syncthreads();
   }
   if constexpr (XM1) {
