@@ -1460,6 +1460,20 @@ __device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinSha
   publish_selection(a, bh, sh);
 }
 
+// Two weights c0, c1 as one bf16 pair of an A operand row: the bf16 parts (round to nearest
+// even, one v_cvt_pk_bf16_f32) in rows n < G, the remainders c - bf16(c) in rows G <= n < 2G
+// (so that the two rows' fp32 sum carries c to about 2^-17 relative), zero beyond.
+template <int G>
+__device__ __forceinline__ uint32_t hi_lo_bf16(float c0, float c1, int n) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const uint32_t hi = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)c0, (__bf16)c1});
+  const float r0 = c0 - __uint_as_float(hi << 16), r1 = c1 - __uint_as_float(hi & 0xffff0000u);
+  const uint32_t lo = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)r0, (__bf16)r1});
+  return n < G ? hi : (n < 2 * G ? lo : 0u);
+}
+
+constexpr float kLazyMax = 8.f;  // log2 headroom of a retrieve wave's running maximum
+
 // ------------------------------------------------------------------------------------
 // estimate: every non-empty cluster's centroid term, on the matrix cores
 // ------------------------------------------------------------------------------------
@@ -1540,17 +1554,14 @@ __device__ __forceinline__ void estimate_mfma(const DecodeArgs& a, int bh, int e
     uint32_t pk[4];
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      uint32_t h2[2];
+      float pr[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const float s = sv[c][i + u];
-        const float pr = s == kNegInf ? 0.f : fast_exp2(s - mx);
-        lsum += nv[c][i + u] * pr;
-        const uint32_t hi = f2bf(pr);
-        const uint32_t lo = f2bf(pr - __uint_as_float(hi << 16));
-        h2[u] = n < G ? hi : (n < 2 * G ? lo : 0u);
+        pr[u] = s == kNegInf ? 0.f : fast_exp2(s - mx);
+        lsum += nv[c][i + u] * pr[u];
       }
-      pk[i >> 1] = h2[0] | (h2[1] << 16);
+      pk[i >> 1] = hi_lo_bf16<G>(pr[0], pr[1], n);
     }
     pa[c] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
   }
@@ -1890,35 +1901,36 @@ __device__ __forceinline__ void attend_rows_mfma(const DecodeArgs& a, int bh,
     mb = arow ? mb : kNegInf;
     mb = fmaxf(mb, xor16(mb));
     mb = fmaxf(mb, xor32(mb));
-    const float mn = fmaxf(st.m, mb);
-    const float alpha = (st.m == kNegInf || mn == kNegInf) ? (mn == kNegInf ? 1.f : 0.f)
-                                                           : fast_exp2(st.m - mn);
+    // the running maximum moves only when the block's exceeds it by more than kLazyMax (the
+    // weights stay below 2^kLazyMax), so that most blocks leave the accumulators unscaled
+    const bool raise = mb > st.m + kLazyMax || (st.m == kNegInf && mb != kNegInf);
+    const float mn = raise ? mb : st.m;
+    const float alpha = raise ? (st.m == kNegInf ? 0.f : fast_exp2(st.m - mn)) : 1.f;
     st.m = mn;
     float ls = 0.f;
     uint32_t pk[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      uint32_t h2[2];
+      float c[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const float x = sv[e + u];
         const float pr = (x == kNegInf || mn == kNegInf) ? 0.f : fast_exp2(x - mn);
         ls += wv[e + u] * pr;
-        const float c = wv[e + u] < 0.f ? -pr : pr;
-        const uint32_t hi = f2bf(c);
-        const uint32_t lo = f2bf(c - __uint_as_float(hi << 16));
-        h2[u] = n < G ? hi : (arow ? lo : 0u);
+        c[u] = wv[e + u] < 0.f ? -pr : pr;
       }
-      pk[e >> 1] = h2[0] | (h2[1] << 16);
+      pk[e >> 1] = hi_lo_bf16<G>(c[0], c[1], n);
     }
     st.l = alpha * st.l + ls;
     const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
     // accumulator rows 4 g + i belong to the head of A row 4 g + i (lane 4 g + i)
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ar = __shfl(alpha, 4 * g + i);
+      for (int i = 0; i < 4; ++i) {
+        const float ar = __shfl(alpha, 4 * g + i);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) st.acc[t][i] *= ar;
+        for (int t = 0; t < 8; ++t) st.acc[t][i] *= ar;
+      }
     }
     // ---- the value rows, read back transposed, against the weights
     drain_vmem();  // (this wave's direct loads have landed in LDS)
@@ -2026,6 +2038,24 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int IPT = XM1 ? (G * 128 + kDecThreads - 1) / kDecThreads : 1;
   constexpr int XB = 4;
   float xm[IPT][XB], xl[IPT][XB], xo[IPT][XB];
+  // XM1: the next XB2 partials (w_item + (XB + k) nB) go to LDS by direct loads issued here,
+  // in 16-byte chunks, one wave instruction per 64 chunks (the area is padded to whole
+  // instructions); they land during the attend
+  // (groups of at most four heads: the larger groups' registers and LDS are full already)
+  constexpr int XB2 = XM1 && G <= 4 ? 2 : 0;
+  constexpr int kPartChunks = G * kPartStride / 4;  // 16-byte chunks of one partial
+  constexpr int kX2Chunks = XB2 > 0 ? (XB2 * kPartChunks + 63) / 64 * 64 : 1;
+  __shared__ __align__(16) float s_x2[kX2Chunks * 4];
+  if constexpr (XB2 > 0) {
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const int lane = tid & 63;
+    for (int c0 = wave * 64; c0 < kX2Chunks; c0 += kDecThreads) {
+      const int c = min(c0 + lane, XB2 * kPartChunks - 1);
+      const int k = c / kPartChunks, pk = min(w_item + (XB + k) * nB, nSP - 1);
+      __builtin_amdgcn_global_load_lds(parts + (size_t)pk * G * kPartStride + (c - k * kPartChunks) * 4,
+                                       (lds_ptr)&s_x2[c0 * 4], 16, 0, 0);
+    }
+  }
   if constexpr (XM1) {
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
@@ -2091,6 +2121,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
     __syncthreads();
   }
   if constexpr (XM1) {
+    drain_vmem();  // (the staged partials have landed: every wave's own loads, then all)
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int idx = tid + i * kDecThreads;
@@ -2106,10 +2138,24 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
           Ls += f * xl[i][k];
         }
       }
-      if (w_item + XB * nB < nSP) {  // more than XB partials for this workgroup
+      {
+        const int h = min(idx, G * 128 - 1) >> 7, d = idx & 127;
+#pragma unroll
+        for (int k = 0; k < XB2; ++k) {  // the partials staged in LDS
+          if (w_item + (XB + k) * nB < nSP) {
+            const float* xp = &s_x2[(k * G + h) * kPartStride];
+            float a1, a2, mn;
+            lse_pair(M, xp[128], a1, a2, mn);
+            O = a1 * O + a2 * xp[d];
+            Ls = a1 * Ls + a2 * xp[129];
+            M = mn;
+          }
+        }
+      }
+      if (w_item + (XB + XB2) * nB < nSP) {  // still more partials for this workgroup
         float M2, L2, O2, a1, a2, mn;
-        merge_partials<false, 4>(parts, G, min(idx, G * 128 - 1), w_item + XB * nB, nB, nSP, M2,
-                                 L2, O2);
+        merge_partials<false, 4>(parts, G, min(idx, G * 128 - 1), w_item + (XB + XB2) * nB, nB,
+                                 nSP, M2, L2, O2);
         lse_pair(M, M2, a1, a2, mn);
         O = a1 * O + a2 * O2;
         Ls = a1 * Ls + a2 * L2;
