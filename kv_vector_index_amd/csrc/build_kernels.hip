@@ -355,28 +355,20 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
   };
   // Blocks b0 + wave go to the waves first; every later block goes to whichever wave asks
   // next (a counter in LDS), so the waves of the workgroup, and with them the SIMDs, stay
-  // busy until its last block. A wave claims its next block when it starts the current one,
-  // and one plain load per 128-byte line of that next block, consumed only after the current
-  // block is scored, brings its keys into L2 meanwhile.
+  // busy until its last block. A wave claims its next block when it starts the current one.
+  // (Its keys are loaded after the current block is scored: the other wave on the SIMD keeps
+  // the matrix core busy meanwhile.)
   auto claim = [&]() {
     int v = 0;
     if (lane == 0) v = atomicAdd(s_next, 1);
     return (int64_t)__shfl(v, 0);
   };
-  uint32_t touch = 0;
   while (blk < b1) {
     const int64_t nxt = claim();
-    const int64_t pn = min(nxt * 64 + lane, n - 1);
-    const uint32_t* nrow =
-        reinterpret_cast<const uint32_t*>(a.k + ((size_t)bh * a.Lcap + sg.lo + pn) * kHeadDim);
-    const uint32_t t0 = nrow[0], t1 = nrow[32];
     score_block(blk, bq, inv);
-    touch ^= t0 ^ t1;
     blk = nxt;
     if (blk < b1) load_block(blk, bq, inv);
   }
-  // (never true, nsplit >= 1: keeps the touching loads)
-  if (nsplit <= 0 && touch == 1u) a.lab[0] = 0;
 }
 
 // ------------------------------------------------------------------------------------
