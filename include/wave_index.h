@@ -211,6 +211,59 @@ wave_status wave_dense_decode_attention(const wave_decode_params* p, const void*
                                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Host-memory tier: the cache in host memory behind a device block cache
+ * ------------------------------------------------------------------------------------
+ * The wave buffer of RetroInfer (gist.science de section 2B "Wave Buffer", fr section 2B,
+ * zh section 2B) keeps the bulk of the KV cache in CPU memory and a cache of hot blocks on
+ * the GPU, exploiting that successive decode steps retrieve largely the same clusters. Here
+ * the index (centroids, value sums, sizes, offsets) and the steady zone stay in device
+ * memory; the index's layout of the cache (k_out / v_out of the build) lives in pinned host
+ * memory; a device cache of n_slots slots holds blocks of 32 consecutive cache rows (K and V,
+ * 16 KiB a slot). A decode step selects clusters as wave_decode_attention does, reads each
+ * retrieved row from its block's slot when the block is cached and from host memory
+ * otherwise, and then copies the blocks it read from host memory into slots that the step
+ * did not use (the next slots in a rotating order: a second-chance replacement); blocks that
+ * find no such slot stay in host memory. The result is bit-identical to
+ * wave_decode_attention on the same rows; only where the rows are read from differs.
+ */
+typedef struct {
+  const void* host_k;    /* pinned host memory (hipHostMalloc), bf16 [B, Hkv, Lcap, d]: the
+                            cache in the index's layout (rows of the indexed zone are read) */
+  const void* host_v;
+  const void* steady_k;  /* device, bf16 [B, Hkv, S_rows, d]: rows [0, n_sink) of the cache,
+                            then rows [L0 - n_recent, L) (decode tokens appended in order);
+                            S_rows = n_sink + n_recent + Lcap - L0 */
+  const void* steady_v;
+  void* cache;           /* device, n_slots * 16384 bytes: the block cache */
+  void* state;           /* device, wave_tier_state_size bytes: block table, slot owners and
+                            stamps, counters; wave_tier_reset sets it up */
+  int32_t n_slots;       /* >= 1 */
+} wave_tier;
+
+/* Bytes of tier state for these decode parameters and n_slots (host only). */
+wave_status wave_tier_state_size(const wave_decode_params* p, int32_t n_slots, size_t* bytes);
+
+/* Empty the block cache: no block cached, step counters and totals zero (enqueued on
+ * stream). Needed once before the first tiered step, and after host_k / host_v change. */
+wave_status wave_tier_reset(const wave_decode_params* p, const wave_tier* tier,
+                            hipStream_t stream);
+
+/* One decode step with the cache in the tier (arguments otherwise as for
+ * wave_decode_attention; the workspace is the same size). Steps that share a tier are
+ * ordered on one stream. */
+wave_status wave_decode_attention_tiered(const wave_decode_params* p, const void* q,
+                                         const wave_tier* tier, const wave_index* idx,
+                                         float* out, float* lse, int32_t* selected,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/* Totals since the last reset, copied to the host (synchronizes stream): retrieved token rows
+ * read from the block cache, read from host memory, blocks copied into the cache, blocks
+ * left out for want of a free slot. */
+wave_status wave_tier_counters(const wave_decode_params* p, const wave_tier* tier,
+                               uint64_t counters[4], hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Tracing: per-kernel timing events
  * ------------------------------------------------------------------------------------
  * The *_traced variants behave exactly like their plain counterparts and additionally time
@@ -222,7 +275,7 @@ wave_status wave_dense_decode_attention(const wave_decode_params* p, const void*
  * Kernel order, build: key norms (if any indexed token), seeds, then per pass: assign,
  * sort, and (all passes but the last) update; then finalise, steady-row copy (if
  * n_sink + n_recent > 0), objective (if requested). Decode: score, histogram (only when
- * n_clusters > 8192), gather, retrieve.
+ * n_clusters > 8192), gather, retrieve (tiered: then fill).
  * Dense decode: partial, merge.
  */
 typedef struct {

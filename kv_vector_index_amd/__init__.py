@@ -21,6 +21,8 @@ __all__ = [
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
     "IndexTensors", "alloc_index", "EXPORTED_SYMBOLS", "LIB_PATH", "wave_trace",
     "alloc_decode_workspace", "wave_decode_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "wave_tier", "TierTensors", "alloc_tier", "wave_tier_state_size", "wave_tier_reset",
+    "wave_decode_attention_tiered", "wave_tier_counters", "TIER_BLOCK",
 ]
 
 # WAVE_INDEX_LIB selects another build of the library (e.g. the sanitized host-only one)
@@ -30,7 +32,10 @@ EXPORTED_SYMBOLS = (
     "wave_status_string", "wave_index_workspace_size", "wave_index_build", "wave_index_extend",
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
     "wave_index_build_traced", "wave_decode_attention_traced", "wave_decode_attention_noalloc",
+    "wave_tier_state_size", "wave_tier_reset", "wave_decode_attention_tiered",
+    "wave_tier_counters",
 )
+TIER_BLOCK = 32                    # cache rows per block of the host-memory tier
 NOALLOC_SCRATCH_BYTES = 64 << 20   # WAVE_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "WAVE_OK", 1: "WAVE_ERR_INVALID_ARG", 2: "WAVE_ERR_UNSUPPORTED",
           3: "WAVE_ERR_WORKSPACE", 4: "WAVE_ERR_ALIAS", 5: "WAVE_ERR_HIP"}
@@ -68,6 +73,13 @@ class wave_decode_params(ctypes.Structure):
                 ("n_retrieve", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
+class wave_tier(ctypes.Structure):
+    _fields_ = [("host_k", ctypes.c_void_p), ("host_v", ctypes.c_void_p),
+                ("steady_k", ctypes.c_void_p), ("steady_v", ctypes.c_void_p),
+                ("cache", ctypes.c_void_p), ("state", ctypes.c_void_p),
+                ("n_slots", ctypes.c_int32)]
+
+
 class wave_trace(ctypes.Structure):
     _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", ctypes.c_int32),
                 ("recorded", ctypes.c_int32)]
@@ -100,6 +112,12 @@ def library() -> ctypes.CDLL:
                                                     vp, sz, vp]
         lib.wave_decode_attention_noalloc.argtypes = [P(wave_decode_params), vp, vp, vp,
                                                       P(wave_index), vp, vp, vp, vp]
+        lib.wave_tier_state_size.argtypes = [P(wave_decode_params), ctypes.c_int32, P(sz)]
+        lib.wave_tier_reset.argtypes = [P(wave_decode_params), P(wave_tier), vp]
+        lib.wave_decode_attention_tiered.argtypes = [P(wave_decode_params), vp, P(wave_tier),
+                                                     P(wave_index), vp, vp, vp, vp, sz, vp]
+        lib.wave_tier_counters.argtypes = [P(wave_decode_params), P(wave_tier),
+                                           P(ctypes.c_uint64), vp]
         lib.wave_index_build_traced.argtypes = lib.wave_index_build.argtypes + [P(wave_trace)]
         lib.wave_decode_attention_traced.argtypes = (lib.wave_decode_attention.argtypes
                                                      + [P(wave_trace)])
@@ -256,3 +274,76 @@ def wave_dense_decode_attention(p: wave_decode_params, q, k_cache, v_cache, out,
 
 def default_scale(head_dim: int = 128) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+# ------------------------------------------------------------------------------------
+# host-memory tier
+# ------------------------------------------------------------------------------------
+@dataclass
+class TierTensors:
+    """One layer's host-memory tier: the cache in pinned host memory, the steady zone and the
+    block cache in device memory, and the tier state (see wave_tier in include/wave_index.h)."""
+    host_k: object     # pinned host bf16 [B, Hkv, Lcap, d]
+    host_v: object
+    steady_k: object   # device bf16 [B, Hkv, n_sink + n_recent + Lcap - L0, d]
+    steady_v: object
+    cache: object      # device uint8 [n_slots * 16384]
+    state: object      # device uint8 [wave_tier_state_size]
+    n_slots: int
+
+    def c_struct(self) -> wave_tier:
+        return wave_tier(_ptr(self.host_k), _ptr(self.host_v), _ptr(self.steady_k),
+                         _ptr(self.steady_v), _ptr(self.cache), _ptr(self.state),
+                         int(self.n_slots))
+
+
+def wave_tier_state_size(p: wave_decode_params, n_slots: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("wave_tier_state_size", library().wave_tier_state_size(ctypes.byref(p), int(n_slots),
+                                                                   ctypes.byref(n)))
+    return n.value
+
+
+def alloc_tier(p: wave_decode_params, n_slots: int, device="cuda") -> TierTensors:
+    """Host and device buffers of a tier for these decode parameters (contents unset: copy the
+    cache rows in, then wave_tier_reset)."""
+    import torch
+    B, H, Lcap, d = p.batch, p.n_kv_heads, p.kv_capacity, 128
+    rows = p.n_sink + p.n_recent + (p.kv_capacity - p.index_len)
+    hk = torch.empty(B, H, Lcap, d, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty(B, H, Lcap, d, dtype=torch.bfloat16, pin_memory=True)
+    sk = torch.empty(B, H, rows, d, dtype=torch.bfloat16, device=device)
+    sv = torch.empty(B, H, rows, d, dtype=torch.bfloat16, device=device)
+    cache = torch.empty(n_slots * 2 * TIER_BLOCK * d * 2, dtype=torch.uint8, device=device)
+    state = torch.empty(wave_tier_state_size(p, n_slots), dtype=torch.uint8, device=device)
+    return TierTensors(hk, hv, sk, sv, cache, state, n_slots)
+
+
+def wave_tier_reset(p: wave_decode_params, tier: TierTensors, stream=None) -> None:
+    """Enqueue the emptying of the tier's block cache."""
+    t = tier.c_struct()
+    _check("wave_tier_reset", library().wave_tier_reset(ctypes.byref(p), ctypes.byref(t),
+                                                         _stream(stream)))
+
+
+def wave_decode_attention_tiered(p: wave_decode_params, q, tier: TierTensors,
+                                 index: IndexTensors, out, lse=None, selected=None,
+                                 workspace=None, stream=None) -> None:
+    """Enqueue one decode step with the cache in the host-memory tier."""
+    t, idx = tier.c_struct(), index.c_struct()
+    _check("wave_decode_attention_tiered", library().wave_decode_attention_tiered(
+        ctypes.byref(p), _ptr(q), ctypes.byref(t), ctypes.byref(idx), _ptr(out), _ptr(lse),
+        _ptr(selected), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def wave_tier_counters(p: wave_decode_params, tier: TierTensors, stream=None) -> dict:
+    """Totals since the last reset (synchronizes the stream): token rows read from the block
+    cache and from host memory, blocks admitted to and left out of the cache."""
+    t = tier.c_struct()
+    c = (ctypes.c_uint64 * 4)()
+    _check("wave_tier_counters", library().wave_tier_counters(ctypes.byref(p), ctypes.byref(t),
+                                                               c, _stream(stream)))
+    return {"rows_cached": c[0], "rows_host": c[1], "blocks_admitted": c[2],
+            "blocks_refused": c[3]}

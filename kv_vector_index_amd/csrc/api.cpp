@@ -408,13 +408,62 @@ wave_status wave_decode_workspace_size(const wave_decode_params* p, size_t* byte
 
 namespace {
 
+// Tier state: counters, block table, slot owners and stamps, the request list.
+struct TierShape {
+  int64_t nblk, steady_rows;
+  int64_t reqcap;
+};
+wave_status check_tier(const wave_decode_params* p, const DecodeShape& sh, int32_t n_slots,
+                       TierShape* ts) {
+  if (n_slots < 1) return WAVE_ERR_INVALID_ARG;
+  if (n_slots > (1 << 24)) return WAVE_ERR_UNSUPPORTED;
+  ts->nblk = (p->kv_capacity + wave::kTierBlock - 1) / wave::kTierBlock;
+  ts->steady_rows = (int64_t)p->n_sink + p->n_recent + (p->kv_capacity - p->index_len);
+  ts->reqcap = sh.BH * ts->nblk;
+  if (ts->reqcap > INT32_MAX) return WAVE_ERR_UNSUPPORTED;
+  return WAVE_OK;
+}
+size_t layout_tier(const DecodeShape& sh, const TierShape& ts, int32_t n_slots, void* base,
+                   wave::DecodeArgs* a) {
+  Carver cv(base);
+  uint32_t* tctr = cv.take<uint32_t>(wave::kTcWords);
+  int32_t* tab = cv.take<int32_t>((size_t)sh.BH * ts.nblk);
+  int32_t* owner = cv.take<int32_t>((size_t)n_slots);
+  int32_t* stamp = cv.take<int32_t>((size_t)n_slots);
+  int32_t* req = cv.take<int32_t>((size_t)ts.reqcap);
+  if (a) {
+    a->tctr = tctr;
+    a->tab = tab;
+    a->owner = owner;
+    a->stamp = stamp;
+    a->req = req;
+    a->nslots = n_slots;
+    a->nblk = (int)ts.nblk;
+    a->reqcap = (int)ts.reqcap;
+    a->Ls = ts.steady_rows;
+  }
+  return cv.off;
+}
+
+// tier: null for the cache in device memory (k_cache, v_cache), else the host-memory tier
+// (k_cache, v_cache unused).
 wave_status decode_impl(const wave_decode_params* p, const void* q, const void* k_cache,
                         const void* v_cache, const wave_index* idx, float* out, float* lse,
                         int32_t* selected, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, wave::Tracer* tr) {
+                        hipStream_t stream, wave::Tracer* tr, const wave_tier* tier = nullptr) {
   DecodeShape sh;
   wave_status st = check_decode(p, &sh);
   if (st != WAVE_OK) return st;
+  TierShape ts{};
+  if (tier) {
+    st = check_tier(p, sh, tier->n_slots, &ts);
+    if (st != WAVE_OK) return st;
+    if (!tier->host_k || !tier->host_v || !tier->steady_k || !tier->steady_v || !tier->cache ||
+        !tier->state)
+      return WAVE_ERR_INVALID_ARG;
+    k_cache = tier->host_k;
+    v_cache = tier->host_v;
+  }
   if (!q || !k_cache || !v_cache || !idx || !idx->centroid_mean || !idx->value_sum ||
       !idx->cluster_size || !idx->cluster_offset || !out)
     return WAVE_ERR_INVALID_ARG;
@@ -423,22 +472,37 @@ wave_status decode_impl(const wave_decode_params* p, const void* q, const void* 
   const size_t BH = (size_t)sh.BH, C = (size_t)p->n_clusters;
   const size_t cache_bytes = (size_t)sh.cache_elems * 2;
   const size_t qb = (size_t)p->batch * p->n_q_heads * wave::kHeadDim;
+  const size_t steady_bytes = BH * (size_t)ts.steady_rows * wave::kHeadDim * 2;
   const void* ins[] = {q, k_cache, v_cache, idx->centroid_mean, idx->value_sum,
-                       idx->cluster_size, idx->cluster_offset};
+                       idx->cluster_size, idx->cluster_offset,
+                       tier ? tier->steady_k : nullptr, tier ? tier->steady_v : nullptr};
   const size_t in_sz[] = {qb * 2, cache_bytes, cache_bytes, BH * C * wave::kHeadDim * 2,
-                          BH * C * wave::kHeadDim * 2, BH * C * 4, BH * C * 4};
-  const void* outs[] = {out, lse, selected, workspace};
+                          BH * C * wave::kHeadDim * 2, BH * C * 4, BH * C * 4, steady_bytes,
+                          steady_bytes};
+  const void* outs[] = {out, lse, selected, workspace, tier ? tier->cache : nullptr,
+                        tier ? tier->state : nullptr};
   const size_t out_sz[] = {qb * 4, (size_t)p->batch * p->n_q_heads * 4,
-                           BH * (size_t)p->n_retrieve * 4, workspace_bytes};
-  for (int i = 0; i < 4; ++i) {
+                           BH * (size_t)p->n_retrieve * 4, workspace_bytes,
+                           tier ? (size_t)tier->n_slots * 2 * wave::kTierBlock * wave::kRowBytes : 0,
+                           tier ? layout_tier(sh, ts, tier->n_slots, nullptr, nullptr) : 0};
+  for (int i = 0; i < 6; ++i) {
     if (!outs[i]) continue;
-    for (int j = 0; j < 7; ++j)
-      if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return WAVE_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = 0; j < 9; ++j)
+      if (ins[j] && overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return WAVE_ERR_ALIAS;
+    for (int j = i + 1; j < 6; ++j)
       if (outs[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return WAVE_ERR_ALIAS;
   }
   wave::DecodeArgs a{};
   layout_decode(p, sh, workspace, &a);
+  if (tier) {
+    layout_tier(sh, ts, tier->n_slots, tier->state, &a);
+    a.tier = 1;
+    a.hk = static_cast<const uint16_t*>(tier->host_k);
+    a.hv = static_cast<const uint16_t*>(tier->host_v);
+    a.sk = static_cast<const uint16_t*>(tier->steady_k);
+    a.sv = static_cast<const uint16_t*>(tier->steady_v);
+    a.cache = static_cast<uint16_t*>(tier->cache);
+  }
   fill_decode_shape(p, sh, &a);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_cache);
@@ -500,6 +564,58 @@ wave_status wave_decode_attention_noalloc(const wave_decode_params* p, const voi
   if (wave::noalloc_scratch(&ws) != hipSuccess) return WAVE_ERR_HIP;
   return decode_impl(p, q, k_cache, v_cache, idx, out, lse, selected, ws, need, stream,
                      nullptr);
+}
+
+wave_status wave_tier_state_size(const wave_decode_params* p, int32_t n_slots, size_t* bytes) {
+  if (!bytes) return WAVE_ERR_INVALID_ARG;
+  DecodeShape sh;
+  wave_status st = check_decode(p, &sh);
+  if (st != WAVE_OK) return st;
+  TierShape ts;
+  st = check_tier(p, sh, n_slots, &ts);
+  if (st != WAVE_OK) return st;
+  *bytes = layout_tier(sh, ts, n_slots, nullptr, nullptr);
+  return WAVE_OK;
+}
+
+wave_status wave_tier_reset(const wave_decode_params* p, const wave_tier* tier,
+                            hipStream_t stream) {
+  DecodeShape sh;
+  wave_status st = check_decode(p, &sh);
+  if (st != WAVE_OK) return st;
+  if (!tier || !tier->state) return WAVE_ERR_INVALID_ARG;
+  TierShape ts;
+  st = check_tier(p, sh, tier->n_slots, &ts);
+  if (st != WAVE_OK) return st;
+  wave::DecodeArgs a{};
+  fill_decode_shape(p, sh, &a);
+  layout_tier(sh, ts, tier->n_slots, tier->state, &a);
+  return wave::launch_tier_reset(a, stream) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
+}
+
+wave_status wave_decode_attention_tiered(const wave_decode_params* p, const void* q,
+                                         const wave_tier* tier, const wave_index* idx,
+                                         float* out, float* lse, int32_t* selected,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  if (!tier) return WAVE_ERR_INVALID_ARG;
+  return decode_impl(p, q, nullptr, nullptr, idx, out, lse, selected, workspace,
+                     workspace_bytes, stream, nullptr, tier);
+}
+
+wave_status wave_tier_counters(const wave_decode_params* p, const wave_tier* tier,
+                               uint64_t counters[4], hipStream_t stream) {
+  DecodeShape sh;
+  wave_status st = check_decode(p, &sh);
+  if (st != WAVE_OK) return st;
+  if (!tier || !tier->state || !counters) return WAVE_ERR_INVALID_ARG;
+  uint32_t c[wave::kTcWords];
+  if (wave::tier_counters_copy(c, tier->state, stream) != hipSuccess) return WAVE_ERR_HIP;
+  counters[0] = c[wave::kTcRowsCached];
+  counters[1] = c[wave::kTcRowsHost];
+  counters[2] = c[wave::kTcAdmitted];
+  counters[3] = c[wave::kTcRefused];
+  return WAVE_OK;
 }
 
 wave_status wave_dense_decode_attention(const wave_decode_params* p, const void* q,

@@ -387,13 +387,14 @@ __device__ __forceinline__ int64_t steady_row(const DecodeArgs& a, int64_t t) {
   return t < a.n_sink ? t : a.L0 - a.n_recent + (t - a.n_sink);
 }
 
-// Exact attention over the cache rows row_of(t), t in [wb, we).
+// Exact attention over the rows base + row_of(t), t in [wb, we), of the arrays kc, vc.
 template <int G, typename RowOf>
-__device__ __forceinline__ void attend_rows(const DecodeArgs& a, int bh, const u32x4 (&q)[G],
-                                            Online<G>& st, int64_t wb, int64_t we, RowOf row_of) {
+__device__ __forceinline__ void attend_rows(const DecodeArgs& a, const uint16_t* kc,
+                                            const uint16_t* vc, size_t base,
+                                            const u32x4 (&q)[G], Online<G>& st, int64_t wb,
+                                            int64_t we, RowOf row_of) {
   constexpr int R = Rows<G>::R;
   const int lane = threadIdx.x & 63, grp = lane >> 4, cc = lane & 15;
-  const size_t base = (size_t)bh * a.Lcap;
   for (int64_t t = wb; t < we; t += 4 * R) {
     u32x4 kr[R], vr[R];
     float wt[R], sg[R];
@@ -403,8 +404,8 @@ __device__ __forceinline__ void attend_rows(const DecodeArgs& a, int bh, const u
       sg[i] = 1.f;
       if (tt < we) {
         const size_t row = (base + row_of(tt)) * kHeadDim + cc * 8;
-        kr[i] = ld16_stream(a.k + row);
-        vr[i] = ld16_stream(a.v + row);
+        kr[i] = ld16_stream(kc + row);
+        vr[i] = ld16_stream(vc + row);
         wt[i] = 1.f;
       } else {
         kr[i] = vr[i] = u32x4{0, 0, 0, 0};
@@ -1685,7 +1686,12 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
       const int64_t n_steady = (int64_t)a.n_sink + a.n_recent + (a.L - a.L0);
       const int64_t wbeg = (int64_t)s * kTokChunk + wave * (kTokChunk / 4);
       const int64_t wend = min(n_steady, wbeg + kTokChunk / 4);
-      attend_rows<G>(a, bh, q, st, wbeg, wend, [&](int64_t t) { return steady_row(a, t); });
+      if (a.tier)  // (the steady zone's own buffer holds its rows in order)
+        attend_rows<G>(a, a.sk, a.sv, (size_t)bh * a.Ls, q, st, wbeg, wend,
+                       [](int64_t t) { return t; });
+      else
+        attend_rows<G>(a, a.k, a.v, (size_t)bh * a.Lcap, q, st, wbeg, wend,
+                       [&](int64_t t) { return steady_row(a, t); });
       slot = a.nEW + s;
     }
     write_block_partial_in<G, false>(st, nullptr,
@@ -1801,13 +1807,25 @@ struct MfmaState {
 // LDS (first virtual row l_ts[] with l_ts[cnt] = end, first cache row l_co[], cluster id
 // l_id[]), one row per thread: src = the cache row of a token row, or -1 - j for the removal
 // row of cluster j (its centroid key and value sum); wgt = the row's denominator weight (1 for
-// a token, -n_j for a removal row). Rows from n on are padding: src 0, wgt 0.
-__device__ __forceinline__ void describe_rows(int c0, int n, const int32_t* l_ts,
-                                              const int32_t* l_co, const int32_t* l_id, int cnt,
-                                              int32_t* d_src, float* d_wgt) {
+// a token, -n_j for a removal row). Rows from n on are padding: src -1, wgt 0 (cluster 0's
+// removal row, which the build always writes: the padding's zero weights meet finite values in
+// the products, never an unwritten cache slot whose contents could be NaN).
+//
+// TIER: a token row's source is its block's cache slot, src = slot * kTierBlock + row %
+// kTierBlock, when the block is cached (the slot is stamped with the step), else the row in
+// host memory, src = kHostRow | row (the block is requested for the fill kernel, once: the
+// table entry goes from -1 to -2). Returns 1 for a token row read from the cache, 2 for one
+// read from host memory, else 0.
+constexpr int32_t kHostRow = 1 << 30;
+template <bool TIER>
+__device__ __forceinline__ int describe_rows(const DecodeArgs& a, int bh, int c0, int n,
+                                             const int32_t* l_ts, const int32_t* l_co,
+                                             const int32_t* l_id, int cnt, int32_t* d_src,
+                                             float* d_wgt) {
   const int tid = threadIdx.x, t = c0 + tid;
-  int32_t src = 0;
+  int32_t src = -1;
   float wgt = 0.f;
+  int cls = 0;
   if (tid < n) {
     int lo = 0, hi = cnt - 1;
     while (lo < hi) {
@@ -1818,6 +1836,26 @@ __device__ __forceinline__ void describe_rows(int c0, int n, const int32_t* l_ts
     if (off < nj) {
       src = l_co[lo] + off;
       wgt = 1.f;
+      if constexpr (TIER) {
+        const int32_t id = bh * a.nblk + src / kTierBlock;
+        int32_t e = a.tab[id];
+        if (e >= a.nslots) e = -3;  // (never set by the fill: a state not reset; not cached)
+        // (one thread per block and cluster run does the block's bookkeeping)
+        const bool lead = (src % kTierBlock) == 0 || off == 0 || tid == 0;
+        if (e >= 0) {
+          if (lead) a.stamp[e] = (int32_t)a.tctr[kTcStep];
+          src = e * kTierBlock + src % kTierBlock;
+          cls = 1;
+        } else {
+          if (lead && e == -1 && atomicCAS(a.tab + id, -1, -2) == -1) {
+            const uint32_t r = atomicAdd(a.tctr + kTcReq, 1u);
+            if (r < (uint32_t)a.reqcap) a.req[r] = id;
+            else atomicExch(a.tab + id, -1);  // (the request list is full: no fill)
+          }
+          src = kHostRow | src;
+          cls = 2;
+        }
+      }
     } else {
       src = -1 - l_id[lo];
       wgt = -(float)nj;
@@ -1825,6 +1863,7 @@ __device__ __forceinline__ void describe_rows(int c0, int n, const int32_t* l_ts
   }
   d_src[tid] = src;
   d_wgt[tid] = wgt;
+  return cls;
 }
 
 // Exact attention and estimate removal over the described rows [0, nrows) (d_src, d_wgt in
@@ -1838,7 +1877,7 @@ __device__ __forceinline__ void describe_rows(int c0, int n, const int32_t* l_ts
 // the weights p = 2^(s - m) (negated for removal rows: their value sum leaves the numerator,
 // n_j p the denominator) form the A operand, hi and lo bf16 parts in rows h and G + h,
 // against the value rows read back transposed.
-template <int G>
+template <int G, bool TIER>
 __device__ __forceinline__ void attend_rows_mfma(const DecodeArgs& a, int bh,
                                                  const bf16x8 (&qb)[4], MfmaState& st,
                                                  int nrows, const int32_t* d_src,
@@ -1855,8 +1894,13 @@ __device__ __forceinline__ void attend_rows_mfma(const DecodeArgs& a, int bh,
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int32_t src = d_src[r0 + 8 * (n >> 2) + 4 * tau + (n & 3)];
-      const uint16_t* kp = src >= 0 ? a.k + (kb + src) * kHeadDim
-                                    : a.cmean + (cb + (-1 - src)) * kHeadDim;
+      const uint16_t* kp;
+      if constexpr (TIER)
+        kp = src < 0 ? a.cmean + (cb + (-1 - src)) * kHeadDim
+             : (src & kHostRow) ? a.hk + (kb + (src & ~kHostRow)) * kHeadDim
+             : a.cache + ((size_t)(src / kTierBlock) * 2 * kTierBlock + src % kTierBlock) * kHeadDim;
+      else
+        kp = src >= 0 ? a.k + (kb + src) * kHeadDim : a.cmean + (cb + (-1 - src)) * kHeadDim;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) ka[tau][s4] = ld16_stream(kp + s4 * 32 + g * 8);
     }
@@ -1866,9 +1910,26 @@ __device__ __forceinline__ void attend_rows_mfma(const DecodeArgs& a, int bh,
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int32_t src = d_src[r0 + 8 * slot + e];
-        const uint16_t* vp = src >= 0 ? a.v + (kb + src) * kHeadDim
-                                      : a.vsum + (cb + (-1 - src)) * kHeadDim;
-        __builtin_amdgcn_global_load_lds(vp + cidx * 8, (lds_ptr)&W.vrows[e][0], 16, 0, 0);
+        if constexpr (TIER) {
+          const bool host = src >= 0 && (src & kHostRow);
+          const uint16_t* vp =
+              src < 0 ? a.vsum + (cb + (-1 - src)) * kHeadDim
+              : host  ? a.hv + (kb + (src & ~kHostRow)) * kHeadDim
+                      : a.cache + ((size_t)(src / kTierBlock) * 2 * kTierBlock + kTierBlock +
+                                   src % kTierBlock) * kHeadDim;
+          // a row in host memory anywhere in this load's four rows: plain loads by every lane,
+          // written where the direct load would put them (a direct load is issued by all lanes
+          // or by none)
+          if (__ballot(host)) {
+            *reinterpret_cast<u32x4*>(&W.vrows[e][4 * lane]) = ld16_stream(vp + cidx * 8);
+          } else {
+            __builtin_amdgcn_global_load_lds(vp + cidx * 8, (lds_ptr)&W.vrows[e][0], 16, 0, 0);
+          }
+        } else {
+          const uint16_t* vp = src >= 0 ? a.v + (kb + src) * kHeadDim
+                                        : a.vsum + (cb + (-1 - src)) * kHeadDim;
+          __builtin_amdgcn_global_load_lds(vp + cidx * 8, (lds_ptr)&W.vrows[e][0], 16, 0, 0);
+        }
       }
     }
     // ---- denominator weights of this lane's rows 8 g .. 8 g + 7
@@ -2017,7 +2078,7 @@ __device__ __forceinline__ void write_mfma_partial(MfmaState& st, const float* x
 // (head, dim) element of a thread before the attend and merged after it (more registers, for
 // launches small enough to be resident at three workgroups per CU); else merged element by
 // element before the attend.
-template <int G, bool XM1>
+template <int G, bool XM1, bool TIER>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_retrieve(DecodeArgs a) {
   __shared__ float s_x[G][kPartStride];  // this workgroup's share of the earlier partials
   __shared__ int32_t l_ts[kWinR + 1], l_co[kWinR], l_id[kWinR];
@@ -2113,9 +2174,17 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
     const int ts = max(T0, l_ts[0]), te = min(T1, l_ts[cnt]);
     for (int c0 = ts; c0 < te; c0 += kDecThreads) {
       const int nr = min(kDecThreads, te - c0);
-      describe_rows(c0, nr, l_ts, l_co, l_id, cnt, d_src, d_wgt);
-      __syncthreads();
-      attend_rows_mfma<G>(a, bh, qb, st, nr, d_src, d_wgt, lds.w[wave]);
+      const int cls = describe_rows<TIER>(a, bh, c0, nr, l_ts, l_co, l_id, cnt, d_src, d_wgt);
+      if constexpr (TIER) {
+        const int nc = __syncthreads_count(cls == 1), nh = __syncthreads_count(cls == 2);
+        if (tid == 0) {
+          if (nc) atomicAdd(a.tctr + kTcRowsCached, (uint32_t)nc);
+          if (nh) atomicAdd(a.tctr + kTcRowsHost, (uint32_t)nh);
+        }
+      } else {
+        __syncthreads();
+      }
+      attend_rows_mfma<G, TIER>(a, bh, qb, st, nr, d_src, d_wgt, lds.w[wave]);
       __syncthreads();
     }
     __syncthreads();
@@ -2207,6 +2276,86 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
 }
 
 // ------------------------------------------------------------------------------------
+// host-memory tier: fill and reset
+// ------------------------------------------------------------------------------------
+// After the retrieve of a step: kFillWG workgroups take the blocks it requested (blocks of
+// retrieved rows it read from host memory) in turn. A block gets the next slot in the hand's
+// order that nothing of this step used (stamp below the step; claimed by a compare-and-swap of
+// the stamp, so that no two blocks take one slot): the slot's old block leaves the table, the
+// new block's K and V rows come from host memory, and then the table points to the slot. A
+// block that finds no such slot within nslots tries stays uncached. The last workgroup to
+// finish clears the request count and moves to the next step.
+__global__ __launch_bounds__(kDecThreads) void k_tier_fill(DecodeArgs a) {
+  __shared__ int32_t s_slot;
+  const int tid = threadIdx.x;
+  const int32_t step = (int32_t)a.tctr[kTcStep];
+  const uint32_t nreq = min(a.tctr[kTcReq], (uint32_t)a.reqcap);
+  const int32_t nid = (a.B * a.Hkv) * a.nblk;
+  for (uint32_t i = blockIdx.x; i < nreq; i += gridDim.x) {
+    const int32_t id = a.req[i];
+    if (id < 0 || id >= nid) continue;  // (only from a state that was not reset)
+    if (tid == 0) {
+      int32_t got = -1;
+      for (int tries = 0; tries < a.nslots && got < 0; ++tries) {
+        const int32_t sl = (int32_t)(atomicAdd(a.tctr + kTcHand, 1u) % (uint32_t)a.nslots);
+        const int32_t old = ld_dev(a.stamp + sl);
+        if (old < step && atomicCAS(a.stamp + sl, old, step) == old) got = sl;
+      }
+      s_slot = got;
+    }
+    __syncthreads();
+    const int32_t sl = s_slot;
+    __syncthreads();
+    if (sl < 0) {
+      if (tid == 0) {
+        a.tab[id] = -1;
+        atomicAdd(a.tctr + kTcRefused, 1u);
+      }
+      continue;
+    }
+    if (tid == 0) {
+      const int32_t prev = a.owner[sl];
+      if (prev >= 0 && prev < nid) a.tab[prev] = -1;
+      a.owner[sl] = id;
+    }
+    // 2 kTierBlock rows of 256 bytes (K, then V): 16-byte chunks, four per thread
+    const int bh = id / a.nblk, blk = id % a.nblk;
+    const size_t r0 = (size_t)bh * a.Lcap + (size_t)blk * kTierBlock;
+    uint16_t* dst = a.cache + (size_t)sl * 2 * kTierBlock * kHeadDim;
+    for (int c = tid; c < 2 * kTierBlock * 16; c += kDecThreads) {
+      const int half = c / (kTierBlock * 16), r = (c >> 4) % kTierBlock, ch = c & 15;
+      if ((int64_t)blk * kTierBlock + r < a.Lcap) {
+        const uint16_t* src = (half ? a.hv : a.hk) + (r0 + r) * kHeadDim + ch * 8;
+        st16(dst + ((size_t)half * kTierBlock + r) * kHeadDim + ch * 8, ld16_stream(src));
+      }
+    }
+    // (the next step's retrieve, a later launch, reads the table and the rows)
+    if (tid == 0) {
+      a.tab[id] = sl;
+      atomicAdd(a.tctr + kTcAdmitted, 1u);
+    }
+  }
+  if (arrive_last(a.tctr + kTcFillDone, gridDim.x) && tid == 0) {
+    a.tctr[kTcReq] = 0u;
+    a.tctr[kTcFillDone] = 0u;
+    a.tctr[kTcStep] = (uint32_t)step + 1u;
+  }
+}
+
+// Empty cache: no block cached or requested, no slot owned or stamped, step 1.
+__global__ __launch_bounds__(kDecThreads) void k_tier_reset(DecodeArgs a) {
+  const size_t i0 = (size_t)blockIdx.x * kDecThreads + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * kDecThreads;
+  const size_t ntab = (size_t)a.B * a.Hkv * a.nblk;
+  for (size_t i = i0; i < ntab; i += stride) a.tab[i] = -1;
+  for (size_t i = i0; i < (size_t)a.nslots; i += stride) {
+    a.owner[i] = -1;
+    a.stamp[i] = -1;
+  }
+  if (i0 < (size_t)kTcWords) a.tctr[i0] = i0 == (size_t)kTcStep ? 1u : 0u;
+}
+
+// ------------------------------------------------------------------------------------
 // dense decode (full attention over [0, L)): split-K partials + merge
 // ------------------------------------------------------------------------------------
 template <int G>
@@ -2221,7 +2370,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dense_partial(DecodeArgs a) {
   const int nB = a.nB, w = blockIdx.x;
   const int64_t t0 = a.L * w / nB, t1 = a.L * (w + 1) / nB;
   const int64_t wb = t0 + (t1 - t0) * wave / 4, we = t0 + (t1 - t0) * (wave + 1) / 4;
-  attend_rows<G>(a, bh, q, st, wb, we, [](int64_t t) { return t; });
+  attend_rows<G>(a, a.k, a.v, (size_t)bh * a.Lcap, q, st, wb, we, [](int64_t t) { return t; });
   write_block_partial<G>(st, nullptr, a.part + ((size_t)bh * nB + w) * G * kPartStride);
 }
 
@@ -2252,9 +2401,16 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr
   e = launch(tr, k_dec_gather<G>, dim3((a.nH + a.nEW + a.nSt) * BH), dim3(kDecThreads), 0, s,
              a);
   if (e != hipSuccess) return e;
+  if (a.tier) {
+    e = a.nB * BH <= 3 * kCUs
+            ? launch(tr, k_dec_retrieve<G, true, true>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a)
+            : launch(tr, k_dec_retrieve<G, false, true>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
+    if (e != hipSuccess) return e;
+    return launch(tr, k_tier_fill, dim3(kFillWG), dim3(kDecThreads), 0, s, a);
+  }
   if (a.nB * BH <= 3 * kCUs)
-    return launch(tr, k_dec_retrieve<G, true>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
-  return launch(tr, k_dec_retrieve<G, false>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
+    return launch(tr, k_dec_retrieve<G, true, false>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
+  return launch(tr, k_dec_retrieve<G, false, false>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
 }
 
 template <int G>
@@ -2312,6 +2468,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
 }
 hipError_t launch_dense_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   WAVE_DISPATCH_G(launch_dense_g, a, s, tr)
+}
+hipError_t tier_counters_copy(uint32_t* c, const void* state, hipStream_t s) {
+  const hipError_t e = hipMemcpyAsync(c, state, kTcWords * sizeof(uint32_t),
+                                      hipMemcpyDeviceToHost, s);
+  return e != hipSuccess ? e : hipStreamSynchronize(s);
+}
+hipError_t launch_tier_reset(const DecodeArgs& a, hipStream_t s) {
+  const size_t n = std::max((size_t)a.B * a.Hkv * a.nblk, (size_t)a.nslots);
+  const int nb = (int)std::min<size_t>((n + kDecThreads - 1) / kDecThreads, 4096);
+  return launch(nullptr, k_tier_reset, dim3(std::max(nb, 1)), dim3(kDecThreads), 0, s, a);
 }
 
 }  // namespace wave

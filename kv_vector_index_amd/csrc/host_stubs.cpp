@@ -14,6 +14,8 @@ hipError_t launch_copy_blocks(const CopyArgs&, hipStream_t, Tracer*) {
   return hipErrorNotSupported;
 }
 hipError_t launch_build(const BuildArgs&, hipStream_t, Tracer*) { return hipErrorNotSupported; }
+hipError_t launch_tier_reset(const DecodeArgs&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t tier_counters_copy(uint32_t*, const void*, hipStream_t) { return hipErrorNotSupported; }
 hipError_t noalloc_scratch(void** ptr) {
   *ptr = nullptr;
   return hipErrorNotSupported;

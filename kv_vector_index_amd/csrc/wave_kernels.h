@@ -92,12 +92,46 @@ struct DecodeArgs {
   int nS, nSW, nEW, nSt, nH, nB, nG, nP;
   float scale, scale_log2;
   int hist_kernel;         // 1: the histogram kernel runs (Cp > kLocalSelectMax)
+  // host-memory tier (tier != 0): the cache's rows live in host memory (hk, hv, the same
+  // layout as k, v), the steady zone in a compact device buffer (sk, sv: [BH, Ls, d], rows
+  // [0, n_sink) then [L0 - n_recent, Lcap)), and a device block cache of nslots slots of
+  // kTierBlock K rows then kTierBlock V rows holds recently retrieved blocks of kTierBlock
+  // consecutive cache rows
+  int tier;
+  const uint16_t* hk;
+  const uint16_t* hv;
+  const uint16_t* sk;
+  const uint16_t* sv;
+  int64_t Ls;
+  uint16_t* cache;         // [nslots, 2, kTierBlock, d]
+  int32_t* tab;            // [BH, nblk] slot of each block, -1 none, -2 requested this step
+  int32_t* owner;          // [nslots] block (bh * nblk + block) held, -1 none
+  int32_t* stamp;          // [nslots] last step that read the slot or filled it
+  uint32_t* tctr;          // kTc* counters
+  int32_t* req;            // [reqcap] blocks requested this step
+  int nslots, nblk, reqcap;
 };
 
+// host-memory tier
+constexpr int kTierBlock = 32;        // cache rows per block (one slot)
+constexpr int kTcStep = 0;            // the current step (from 1; stamps below it are older)
+constexpr int kTcHand = 1;            // replacement hand (slots are tried in its order)
+constexpr int kTcReq = 2;             // blocks requested this step
+constexpr int kTcFillDone = 3;        // fill workgroups finished this step
+constexpr int kTcRowsCached = 4;      // retrieved token rows read from the block cache (total)
+constexpr int kTcRowsHost = 5;        // retrieved token rows read from host memory (total)
+constexpr int kTcAdmitted = 6;        // blocks copied into the cache (total)
+constexpr int kTcRefused = 7;         // requested blocks left out: no free slot (total)
+constexpr int kTcWords = 16;
+constexpr int kFillWG = 256;          // fill kernel workgroups
+
 // Enqueue one tripartite decode step (score, histogram for large heads, gather, retrieve
-// kernels). Returns
-// the first launch error.
+// kernels; with the host-memory tier, then the fill kernel). Returns the first launch error.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
+// Empty the host-memory tier's block cache (table, owners, stamps, counters).
+hipError_t launch_tier_reset(const DecodeArgs& a, hipStream_t stream);
+// Copy the tier's kTcWords counters (the start of its state) to host memory c, synchronously.
+hipError_t tier_counters_copy(uint32_t* c, const void* state, hipStream_t stream);
 // Enqueue dense decode over [0, L): split-K partials (part, nB per head) + merge.
 hipError_t launch_dense_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
 

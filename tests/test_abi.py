@@ -177,3 +177,48 @@ def test_noalloc_decode_rejects_a_problem_larger_than_its_scratch_before_any_lau
     assert call(ctypes.byref(big), Q, K, V, ctypes.byref(idx), OUT, None, None, None) == 3
     bad = decode_params(n_retrieve=-1)
     assert call(ctypes.byref(bad), Q, K, V, ctypes.byref(idx), OUT, None, None, None) == 1
+
+
+def test_tier_validates_before_any_launch():
+    """The host-memory tier's checks run on the host before anything is enqueued: slot count,
+    missing buffers, a block cache overlapping the tier state or an output."""
+    lib = wi.library()
+    p = decode_params()
+    n = ctypes.c_size_t(0)
+    assert lib.wave_tier_state_size(ctypes.byref(p), 0, ctypes.byref(n)) == 1
+    assert lib.wave_tier_state_size(ctypes.byref(p), 64, ctypes.byref(n)) == 0
+    st_bytes = n.value
+    assert st_bytes > 0
+    assert lib.wave_tier_state_size(ctypes.byref(p), 128, ctypes.byref(n)) == 0
+    assert n.value > st_bytes                   # owners and stamps per slot
+    ws = wi.wave_decode_workspace_size(p)
+    Q, OUT, WS = 1 << 40, 4 << 40, 5 << 40
+    HK, HV, SK, SV, CA, STT = 20 << 40, 21 << 40, 22 << 40, 23 << 40, 24 << 40, 25 << 40
+    idx = wi.wave_index(6 << 40, 7 << 40, 8 << 40, 9 << 40, None, None, None, None)
+    call = lib.wave_decode_attention_tiered
+
+    def tier(**kw):
+        base = dict(host_k=HK, host_v=HV, steady_k=SK, steady_v=SV, cache=CA, state=STT,
+                    n_slots=64)
+        base.update(kw)
+        return wi.wave_tier(**base)
+    assert call(ctypes.byref(p), Q, None, ctypes.byref(idx), OUT, None, None, WS, ws, None) == 1
+    for f in ("host_k", "host_v", "steady_k", "steady_v", "cache", "state"):
+        t = tier(**{f: None})
+        assert call(ctypes.byref(p), Q, ctypes.byref(t), ctypes.byref(idx), OUT, None, None, WS,
+                    ws, None) == 1, f
+    t = tier(n_slots=0)
+    assert call(ctypes.byref(p), Q, ctypes.byref(t), ctypes.byref(idx), OUT, None, None, WS, ws,
+                None) == 1
+    t = tier(state=CA + 4096)                   # the cache (64 x 16 KiB) covers the state
+    assert call(ctypes.byref(p), Q, ctypes.byref(t), ctypes.byref(idx), OUT, None, None, WS, ws,
+                None) == 4
+    t = tier(cache=OUT)                         # the cache over out
+    assert call(ctypes.byref(p), Q, ctypes.byref(t), ctypes.byref(idx), OUT, None, None, WS, ws,
+                None) == 4
+    t = tier()
+    assert call(ctypes.byref(p), Q, ctypes.byref(t), ctypes.byref(idx), OUT, None, None, WS,
+                ws - 256, None) == 3
+    assert lib.wave_tier_reset(ctypes.byref(p), None, None) == 1
+    c = (ctypes.c_uint64 * 4)()
+    assert lib.wave_tier_counters(ctypes.byref(p), None, c, None) == 1

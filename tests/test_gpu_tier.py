@@ -1,0 +1,154 @@
+"""Host-memory tier (the wave buffer of RetroInfer: gist.science de section 2B "Wave Buffer"):
+the cache in pinned host memory behind a device block cache. Every tiered decode step must
+give the same out, lse and selection as wave_decode_attention on the same rows, bit for bit,
+whatever the cache holds; the block cache must hold exactly the host rows of the blocks its
+table names; and the row counters must add up to the retrieved rows."""
+import numpy as np
+import pytest
+
+import kv_vector_index_amd as wi
+import synth
+import wave_testlib as tl
+
+pytestmark = pytest.mark.gpu
+
+ALIGN = 256                     # the library's sub-buffer alignment
+TC_WORDS = 16
+
+
+def tier_views(layer, p, n_slots, state):
+    """(counters, table, owners, stamps) views of the tier state."""
+    t = tl.torch()
+    BH = layer.B * layer.H
+    nblk = -(-layer.Lcap // wi.TIER_BLOCK)
+    up = lambda x: -(-x // ALIGN) * ALIGN  # noqa: E731
+    o_tab = up(4 * TC_WORDS)
+    o_own = o_tab + up(4 * BH * nblk)
+    o_stamp = o_own + up(4 * n_slots)
+    i32 = state.view(t.int32)
+    return (i32[:TC_WORDS], i32[o_tab // 4:o_tab // 4 + BH * nblk].view(BH, nblk),
+            i32[o_own // 4:o_own // 4 + n_slots], i32[o_stamp // 4:o_stamp // 4 + n_slots])
+
+
+def make_tier(layer, p, n_slots):
+    t = tl.torch()
+    tier = wi.alloc_tier(p, n_slots)
+    # slots the fill has not written hold NaN (bf16 0xffff): a read of one, even under a zero
+    # weight, turns the output to NaN
+    tier.cache.fill_(0xFF)
+    # written by the device (a DMA copy on the stream), as a caller offloading its cache
+    # would: the device's reads of host memory need not see host-side writes still held in the
+    # CPU's caches
+    tier.host_k.copy_(layer.k_out)
+    tier.host_v.copy_(layer.v_out)
+    ns, nr = layer.n_sink, layer.n_recent
+    tier.steady_k.copy_(t.cat([layer.k_out[:, :, :ns], layer.k_out[:, :, layer.L0 - nr:]], dim=2))
+    tier.steady_v.copy_(t.cat([layer.v_out[:, :, :ns], layer.v_out[:, :, layer.L0 - nr:]], dim=2))
+    wi.wave_tier_reset(p, tier)
+    return tier
+
+
+def check_cache_contents(layer, p, tier):
+    """Every block the table names: the slot's K and V rows are the host rows; owners and the
+    table agree."""
+    t = tl.torch()
+    ctr, tab, owner, stamp = tier_views(layer, p, tier.n_slots, tier.state)
+    tab, owner = tab.cpu().numpy(), owner.cpu().numpy()
+    assert (tab >= -1).all(), "a block left requested after a step"
+    cache = tier.cache.view(t.bfloat16).view(tier.n_slots, 2, wi.TIER_BLOCK, 128).cpu()
+    hk = tier.host_k.view(layer.B * layer.H, layer.Lcap, 128)
+    hv = tier.host_v.view(layer.B * layer.H, layer.Lcap, 128)
+    nblk = tab.shape[1]
+    n_cached = 0
+    for bh, b in zip(*np.nonzero(tab >= 0)):
+        s = int(tab[bh, b])
+        assert owner[s] == bh * nblk + b, (bh, b, s, owner[s])
+        r0, r1 = b * wi.TIER_BLOCK, min((b + 1) * wi.TIER_BLOCK, layer.Lcap)
+        assert t.equal(cache[s, 0, :r1 - r0], hk[bh, r0:r1]), (bh, b)
+        assert t.equal(cache[s, 1, :r1 - r0], hv[bh, r0:r1]), (bh, b)
+        n_cached += 1
+    for s in np.nonzero(owner >= 0)[0]:
+        bh, b = divmod(int(owner[s]), nblk)
+        assert tab[bh, b] == s, "an owner whose block does not point back"
+    return n_cached
+
+
+def retrieved_rows(idx, sel):
+    """Token rows of the selected clusters, summed over (b, kv-head)."""
+    size = idx.cluster_size.cpu().numpy()
+    tot = 0
+    for b in range(sel.shape[0]):
+        for g in range(sel.shape[1]):
+            j = sel[b, g][sel[b, g] >= 0]
+            tot += int(size[b, g, j].sum())
+    return tot
+
+
+@pytest.fixture(scope="module")
+def layer4k():
+    w = synth.WORKLOADS["tiny"]
+    x = synth.generate_layer(w)
+    layer = tl.Layer(x.k, x.v, w.context, w.segment_size, w.clusters_per_segment, w.n_iters,
+                     w.n_sink, w.n_recent, w.n_q_heads)
+    idx = layer.build()
+    return w, x, layer, idx
+
+
+@pytest.mark.parametrize("n_slots", [4096, 64, 3])
+def test_tiered_steps_equal_the_resident_steps(layer4k, n_slots):
+    """16 decode steps through the tier (a cache of every block, a small one that must
+    replace, one too small for a step's blocks) against the resident decode: out, lse and the
+    selection bit for bit at every step; the cache's contents after every step; the counters
+    add up."""
+    t = tl.torch()
+    w, x, layer, idx = layer4k
+    n_r = w.n_retrieve
+    p_last = layer.decode_params(layer.L0 + w.steps, n_r)
+    tier = make_tier(layer, p_last, n_slots)
+    ws = wi.alloc_decode_workspace(p_last)
+    total_rows = 0
+    for s in range(w.steps):
+        L = layer.L0 + s + 1
+        p = layer.decode_params(L, n_r)
+        out_r, lse_r, sel_r = layer.decode(idx, x.q[s], L, n_r)
+        q = tl.to_dev(x.q[s])
+        out = t.empty(layer.B, layer.Hq, 128, dtype=t.float32, device="cuda")
+        lse = t.empty(layer.B, layer.Hq, dtype=t.float32, device="cuda")
+        sel = t.full((layer.B, layer.H, n_r), -7, dtype=t.int32, device="cuda")
+        wi.wave_decode_attention_tiered(p, q, tier, idx, out, lse, sel, ws)
+        t.cuda.synchronize()
+        assert np.array_equal(sel.cpu().numpy(), sel_r), f"step {s}: selection"
+        assert np.array_equal(out.cpu().numpy(), out_r), f"step {s}: out"
+        assert np.array_equal(lse.cpu().numpy(), lse_r), f"step {s}: lse"
+        n_cached = check_cache_contents(layer, p, tier)
+        assert n_cached <= n_slots
+        total_rows += retrieved_rows(idx, sel_r)
+    c = wi.wave_tier_counters(p_last, tier)
+    assert c["rows_cached"] + c["rows_host"] == total_rows, (c, total_rows)
+    if n_slots >= 4096:       # every block fits: each is read from host memory once at most
+        assert c["blocks_refused"] == 0
+        assert c["rows_cached"] > 0
+    if n_slots == 3:
+        assert c["blocks_refused"] > 0
+
+
+def test_tier_reset_empties_the_cache(layer4k):
+    """After a reset nothing is cached: the next step reads every retrieved row from host
+    memory and still equals the resident step."""
+    t = tl.torch()
+    w, x, layer, idx = layer4k
+    n_r = w.n_retrieve
+    L = layer.L0 + 1
+    p = layer.decode_params(L, n_r)
+    tier = make_tier(layer, p, 512)
+    ws = wi.alloc_decode_workspace(p)
+    q = tl.to_dev(x.q[0])
+    out = t.empty(layer.B, layer.Hq, 128, dtype=t.float32, device="cuda")
+    for _ in range(2):
+        wi.wave_decode_attention_tiered(p, q, tier, idx, out, None, None, ws)
+    wi.wave_tier_reset(p, tier)
+    wi.wave_decode_attention_tiered(p, q, tier, idx, out, None, None, ws)
+    c = wi.wave_tier_counters(p, tier)
+    out_r, _, sel_r = layer.decode(idx, x.q[0], L, n_r)
+    assert np.array_equal(out.cpu().numpy(), out_r)
+    assert c["rows_cached"] == 0 and c["rows_host"] == retrieved_rows(idx, sel_r), c
