@@ -31,6 +31,9 @@ with p10 / p90 of the call time. Further legs in the same line:
     whole context, decode steps;
   * sweep: the 28-layer Qwen-shaped stack at batch 4 and 256K over cluster sizes 8/16/32 and
     budgets 0.5/1/1.8/4 %: step throughput and the error against exact attention per point;
+  * tier: the same layer's decode steps with the cache in pinned host memory behind a device
+    block cache of a fraction of the layer's blocks (the wave buffer): call time against the
+    resident call, the share of retrieved rows found in the block cache, bytes over the bus;
   * cpu_baseline: the CPU oracle on the host cores, one thread and all cores.
 """
 from __future__ import annotations
@@ -77,6 +80,9 @@ def parse():
                     help="resident stack over cluster sizes x retrieval budgets: throughput "
                          "and error against exact attention at each point ('none': skip)")
     ap.add_argument("--stack-steps", type=int, default=8)
+    ap.add_argument("--tier", default="1,0.05,0.01",
+                    help="device block-cache sizes of the host-memory tier leg, as fractions "
+                         "of the layer's 32-row blocks ('none' to skip)")
     return ap.parse_args()
 
 
@@ -284,6 +290,10 @@ def main():
     cs = sorted(call_ms)
     res["decode_call_us_p10_p90"] = [round(cs[int(0.1 * (len(cs) - 1))] * 1e3, 2),
                                      round(cs[int(0.9 * (len(cs) - 1))] * 1e3, 2)]
+    if args.tier != "none":
+        res["tier"] = tier_leg(w, nds, k_out, v_out, q, idx, dps, dws, out, lse, flush,
+                               [float(f) for f in args.tier.split(",")], med(call_ms))
+        torch.cuda.empty_cache()
     del k, v, q, k_out, v_out, bws, idx, dws, flush, calib
     torch.cuda.empty_cache()
     if args.extend != "none":
@@ -371,6 +381,64 @@ def decode_call_bytes(w, E):
     C, nr, G, d = w.n_clusters, w.n_retrieve, w.group, 128
     BH = w.batch * w.n_kv_heads
     return (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d) * BH
+
+
+def tier_leg(w, nds, k_out, v_out, q, idx, dps, dws, out, lse, flush, fracs, resident_ms):
+    """The decode steps of the main leg through the host-memory tier: K/V in pinned host
+    memory, the steady zone in its own device buffer, a device block cache of `frac` of the
+    layer's 32-row blocks. Per cache size, after a reset: the first call (every retrieved row
+    read over the bus), then the median call over the steps after the first quarter (in which
+    the cache warms), the share of retrieved rows read from the block cache there, and the
+    bytes that crossed the bus per call (rows read from host memory, blocks copied in)."""
+    import torch
+
+    import kv_vector_index_amd as wi
+
+    L0, ns, nr = w.context, w.n_sink, w.n_recent
+    p_last = dps[-1]
+    blocks = w.batch * w.n_kv_heads * -(-w.capacity // wi.TIER_BLOCK)
+    block_bytes = 2 * wi.TIER_BLOCK * 128 * 2
+    n_warm = max(1, nds // 4)
+    pts = []
+    for frac in fracs:
+        n_slots = max(1, int(round(frac * blocks)))
+        tier = wi.alloc_tier(p_last, n_slots)
+        tier.host_k.copy_(k_out)
+        tier.host_v.copy_(v_out)
+        tier.steady_k.copy_(torch.cat([k_out[:, :, :ns], k_out[:, :, L0 - nr:]], dim=2))
+        tier.steady_v.copy_(torch.cat([v_out[:, :, :ns], v_out[:, :, L0 - nr:]], dim=2))
+        wi.wave_tier_reset(p_last, tier)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nds)]
+        c0 = None
+        for s in range(nds):
+            if s == n_warm:
+                c0 = wi.wave_tier_counters(p_last, tier)     # (synchronizes)
+            if flush is not None:
+                flush.sum()
+            ev[s][0].record()
+            wi.wave_decode_attention_tiered(dps[s], q[s], tier, idx, out, lse, None, dws)
+            ev[s][1].record()
+        c1 = wi.wave_tier_counters(p_last, tier)
+        ms = [a.elapsed_time(b) for a, b in ev]
+        d = {key: c1[key] - c0[key] for key in c1}
+        n_t = nds - n_warm
+        rows = d["rows_cached"] + d["rows_host"]
+        bus = (d["rows_host"] * 4 * 128 + d["blocks_admitted"] * block_bytes) / n_t
+        m = statistics.median(ms[n_warm:])
+        pts.append({"block_cache_frac": frac, "slots": n_slots,
+                    "block_cache_MiB": round(n_slots * block_bytes / 2**20, 1),
+                    "first_call_us": round(ms[0] * 1e3, 1),
+                    "call_us": round(m * 1e3, 1),
+                    "resident_call_us": round(resident_ms * 1e3, 1),
+                    "slowdown": round(m / resident_ms, 2),
+                    "cached_row_share": round(d["rows_cached"] / max(rows, 1), 4),
+                    "bus_MB_per_call": round(bus / 1e6, 3),
+                    "bus_GBps": round(bus / (m * 1e-3) / 1e9, 1),
+                    "blocks_admitted_per_call": round(d["blocks_admitted"] / n_t, 1),
+                    "blocks_refused_per_call": round(d["blocks_refused"] / n_t, 1)})
+        print(f"[bench] tier {frac}: {pts[-1]}", file=sys.stderr, flush=True)
+        del tier
+    return {"workload": w.name, "timed_steps": nds - n_warm, "points": pts}
 
 
 def extend_leg(name, n_rep):

@@ -2282,22 +2282,27 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
 // retrieved rows it read from host memory) in turn. A block gets the next slot in the hand's
 // order that nothing of this step used (stamp below the step; claimed by a compare-and-swap of
 // the stamp, so that no two blocks take one slot): the slot's old block leaves the table, the
-// new block's K and V rows come from host memory, and then the table points to the slot. A
-// block that finds no such slot within nslots tries stays uncached. The last workgroup to
-// finish clears the request count and moves to the next step.
+// new block's K and V rows come from host memory, and then the table points to the slot. The
+// hand makes one revolution per step at most: a stamp never falls within a step, so once every
+// slot has been tried none is left, and the remaining blocks stay uncached at the cost of one
+// atomic each. The last workgroup to finish clears the request count, notes where the hand
+// stopped and moves to the next step.
 __global__ __launch_bounds__(kDecThreads) void k_tier_fill(DecodeArgs a) {
   __shared__ int32_t s_slot;
   const int tid = threadIdx.x;
   const int32_t step = (int32_t)a.tctr[kTcStep];
   const uint32_t nreq = min(a.tctr[kTcReq], (uint32_t)a.reqcap);
+  const uint32_t h0 = a.tctr[kTcHandStart];
   const int32_t nid = (a.B * a.Hkv) * a.nblk;
   for (uint32_t i = blockIdx.x; i < nreq; i += gridDim.x) {
     const int32_t id = a.req[i];
     if (id < 0 || id >= nid) continue;  // (only from a state that was not reset)
     if (tid == 0) {
       int32_t got = -1;
-      for (int tries = 0; tries < a.nslots && got < 0; ++tries) {
-        const int32_t sl = (int32_t)(atomicAdd(a.tctr + kTcHand, 1u) % (uint32_t)a.nslots);
+      while (got < 0) {
+        const uint32_t h = atomicAdd(a.tctr + kTcHand, 1u);
+        if (h - h0 >= (uint32_t)a.nslots) break;  // (the revolution is over: no slot left)
+        const int32_t sl = (int32_t)(h % (uint32_t)a.nslots);
         const int32_t old = ld_dev(a.stamp + sl);
         if (old < step && atomicCAS(a.stamp + sl, old, step) == old) got = sl;
       }
@@ -2338,6 +2343,7 @@ __global__ __launch_bounds__(kDecThreads) void k_tier_fill(DecodeArgs a) {
   if (arrive_last(a.tctr + kTcFillDone, gridDim.x) && tid == 0) {
     a.tctr[kTcReq] = 0u;
     a.tctr[kTcFillDone] = 0u;
+    a.tctr[kTcHandStart] = ld_dev(a.tctr + kTcHand);
     a.tctr[kTcStep] = (uint32_t)step + 1u;
   }
 }

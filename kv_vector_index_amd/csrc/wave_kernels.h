@@ -122,6 +122,7 @@ constexpr int kTcRowsCached = 4;      // retrieved token rows read from the bloc
 constexpr int kTcRowsHost = 5;        // retrieved token rows read from host memory (total)
 constexpr int kTcAdmitted = 6;        // blocks copied into the cache (total)
 constexpr int kTcRefused = 7;         // requested blocks left out: no free slot (total)
+constexpr int kTcHandStart = 8;       // the hand when this step's fill began
 constexpr int kTcWords = 16;
 constexpr int kFillWG = 256;          // fill kernel workgroups
 
