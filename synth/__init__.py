@@ -25,6 +25,11 @@ Recipe, per batch element b, layer l, KV head g, query head h:
     with xi ~ N(0, I) fresh per (b, l, h, s), delta_h ~ N(0, 0.5 I) fixed per
     (l, h), z* = z_{t*} with t* uniform over the indexed positions, drawn per
     (b, l, g, s).
+  * training queries of KV head g (the prefill queries an attention-aware vector index
+    learns the query distribution from): at each of the last n_pos prefill positions
+    p = L0 - n_pos + i, one query per head h of the group, q = RoPE(p) (0.8 mu_{z*} + xi
+    + delta_h) as above (delta_h the same fixed shift), with z* = z_{t*}, t* uniform over
+    the indexed positions, drawn per (b, l, g, i); ordered i-major, head-minor.
   * RoPE: half-split pairs (i, i + d/2), theta_i = base^(-2i/d), angles in fp64.
   * numbers are drawn in fp32/fp64 with numpy PCG64 seeded by
     SeedSequence(seed, spawn_key=(b, l, head, kind)) and rounded to bf16
@@ -39,11 +44,11 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "LayerInputs", "generate_layer", "f32_to_bf16_bits",
-           "bf16_bits_to_f32"]
+__all__ = ["Workload", "WORKLOADS", "LayerInputs", "generate_layer", "training_queries",
+           "f32_to_bf16_bits", "bf16_bits_to_f32"]
 
 # spawn-key "kind" tags, one per independent random stream
-_TOPIC, _CENTRES, _KEYNOISE, _VALUES, _QTARGET, _QNOISE, _QSHIFT = range(7)
+_TOPIC, _CENTRES, _KEYNOISE, _VALUES, _QTARGET, _QNOISE, _QSHIFT, _TTARGET, _TNOISE = range(9)
 N_TOPICS = 64
 
 
@@ -249,3 +254,27 @@ def generate_layer(w: Workload, layer: int = 0, threads: int | None = None,
     for b in range(B):
         q[:, b] = _queries(w, zs[b], b, layer)
     return LayerInputs(w, layer, k, v, q)
+
+
+def training_queries(w: Workload, n_pos: int, layer: int = 0) -> np.ndarray:
+    """Training queries [B, Hkv, n_pos * G, d] (bf16 bits): for each KV head, the queries of
+    its G heads at the last n_pos prefill positions (t = i * G + hh for position
+    L0 - n_pos + i and head g * G + hh)."""
+    B, H, G, d = w.batch, w.n_kv_heads, w.group, w.head_dim
+    out = np.empty((B, H, n_pos * G, d), dtype=np.uint16)
+    pos = w.context - n_pos + np.arange(n_pos)
+    lo, hi = w.n_sink, w.context - w.n_recent
+    if hi <= lo:
+        lo, hi = 0, w.context
+    for b in range(B):
+        z = topic_sequence(w, b)
+        for g in range(H):
+            mu = topic_centres(w, layer, g)
+            tstar = _rng(w, b, layer, g, _TTARGET).integers(lo, hi, size=n_pos)
+            for hh in range(G):
+                h = g * G + hh
+                xi = _rng(w, b, layer, h, _TNOISE).standard_normal((n_pos, d))
+                delta = np.sqrt(0.5) * _rng(w, 0, layer, h, _QSHIFT).standard_normal(d)
+                x = 0.8 * mu[z[tstar]] + xi + delta[None, :]
+                out[b, g, hh::G] = f32_to_bf16_bits(_rope(x, pos, w.rope_base).astype(np.float32))
+    return out
