@@ -45,6 +45,7 @@ def test_train_lists_equal_the_exact_rational_ranking(rng):
     values), ties to the lower id; duplicate keys make exact ties."""
     N, n_t, d, M = 40, 6, 8, 7
     K = bits(rng.standard_normal((N, d)))
+    K[3] = bits(4 * vals(K[3]))   # long enough to rank first for a query along it
     K[7] = K[3]          # exact ties
     K[30] = K[3]
     T = bits(rng.standard_normal((n_t, d)))
