@@ -264,6 +264,86 @@ wave_status wave_tier_counters(const wave_decode_params* p, const wave_tier* tie
                                uint64_t counters[4], hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Attention-aware vector search: a second retrieval zone
+ * ------------------------------------------------------------------------------------
+ * RetrievalAttention (jarxiv.com, "RetrievalAttention: Accelerating Long-Context LLM
+ * Inference via Vector Retrieval", abstract) retrieves, at each decode step, the keys most
+ * relevant to the query from an approximate-nearest-neighbour index over the KV vectors, and
+ * attends to the retrieved tokens; because decode queries and keys follow different
+ * distributions, its index adapts to the distribution of the queries. Here, per (b, KV head),
+ * the nodes are the keys of the indexed zone [n_sink, L0 - n_recent) of the cache (node x =
+ * position n_sink + x; the cache is in position order, not the wave index's layout):
+ *   build: each of n_train training queries (the caller's, e.g. prefill queries of the
+ *     group's heads) lists its list_len nodes of largest inner product, best first (ties to
+ *     the lower id). The list's first node is linked to every other node of the list, and
+ *     each of them back to it. A node keeps at most `degree` neighbours, taken without
+ *     repeats in the order of (its place in a list, the list's index): where it heads a
+ *     list, the list's other nodes in order, else the list's head. The list heads are the
+ *     training queries' entries.
+ *   search (per step): u = the fp32 sum of the group's query rows (head order); a node's
+ *     score is the fp32 dot product of u with its key, accumulated over the dims in order,
+ *     each product and sum rounded (no fused multiply-add); ties to the lower id. The pool
+ *     starts with the entries of the n_entry training queries of largest score; each round
+ *     expands the `expand` best unexpanded pool entries (their unvisited neighbours are
+ *     scored) and the pool keeps its `pool` best entries, until no entry is left to expand
+ *     or max_rounds rounds have run. The n_retrieve best pool entries are retrieved.
+ *   attention: softmax over the steady zone [0, n_sink) U [L0 - n_recent, L) and the
+ *     retrieved tokens, scale * q . k logits, fp32 accumulation (no estimate of the rest).
+ */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;  /* head_dim must be 128; G <= 8 */
+  int64_t seq_len;       /* L (decode): rows [0, L) exist; index_len <= L <= kv_capacity */
+  int64_t index_len;     /* L0: the graph covers positions [n_sink, L0 - n_recent) */
+  int64_t kv_capacity;   /* Lcap: row stride of the caches */
+  int32_t n_sink, n_recent;   /* n_sink + n_recent <= L0 */
+  int32_t n_train;       /* 1..16384 training queries per (b, KV head) */
+  int32_t list_len;      /* 1..64 nodes per training list */
+  int32_t degree;        /* 1..64 neighbours per node */
+  int32_t n_entry;       /* 1..64 training queries that seed a search */
+  int32_t pool;          /* 1..1024 pool entries kept */
+  int32_t expand;        /* 1..64 entries expanded per round; expand * degree <= 2048 */
+  int32_t n_retrieve;    /* 1..pool nodes retrieved */
+  int32_t max_rounds;    /* >= 0 */
+  float scale;           /* > 0 (decode), usually 1/sqrt(d) */
+} wave_anns_params;
+
+typedef struct {
+  const void* train;     /* bf16 [B, Hkv, n_train, d] training queries (build and search) */
+  int32_t* graph;        /* [B, Hkv, N, degree] neighbours, -1 padded (N = L0 - n_sink -
+                            n_recent; may be NULL when N = 0) */
+  int32_t* entry;        /* [B, Hkv, n_train] each training query's first node (-1: none) */
+  int32_t* lists;        /* [B, Hkv, n_train, list_len] training lists, -1 padded (written by
+                            the build; the search does not read them) */
+} wave_anns_index;
+
+/* Bytes of build workspace (host only; no clearing needed). The visited set of a search
+ * lives on chip: N is limited to about a million nodes at pool = 1024 (WAVE_ERR_UNSUPPORTED
+ * beyond). */
+wave_status wave_anns_build_workspace_size(const wave_anns_params* p, size_t* bytes);
+
+/* Build the graph from the cache's keys (k_cache bf16 [B, Hkv, Lcap, d], rows [n_sink,
+ * L0 - n_recent) are read) and idx->train; writes graph, entry and lists. */
+wave_status wave_anns_build(const wave_anns_params* p, const void* k_cache,
+                            const wave_anns_index* idx, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Bytes of decode workspace (host only; no clearing needed; independent of seq_len). */
+wave_status wave_anns_decode_workspace_size(const wave_anns_params* p, size_t* bytes);
+
+/* One decode step: search, then attention.
+ *   q          bf16 [B, Hq, d]
+ *   k_cache, v_cache  bf16 [B, Hkv, Lcap, d], decode tokens appended at rows [L0, L)
+ *   out        fp32 [B, Hq, d];  lse  optional fp32 [B, Hq]
+ *   retrieved  optional int32 [B, Hkv, n_retrieve]: retrieved positions, best first, -1
+ *              padded
+ *   stats      optional int32 [B, Hkv, 2]: rounds run, nodes scored. */
+wave_status wave_anns_decode_attention(const wave_anns_params* p, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const wave_anns_index* idx, float* out, float* lse,
+                                       int32_t* retrieved, int32_t* stats, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Tracing: per-kernel timing events
  * ------------------------------------------------------------------------------------
  * The *_traced variants behave exactly like their plain counterparts and additionally time
@@ -276,7 +356,8 @@ wave_status wave_tier_counters(const wave_decode_params* p, const wave_tier* tie
  * sort, and (all passes but the last) update; then finalise, steady-row copy (if
  * n_sink + n_recent > 0), objective (if requested). Decode: score, histogram (only when
  * n_clusters > 8192), gather, retrieve (tiered: then fill).
- * Dense decode: partial, merge.
+ * Dense decode: partial, merge. Vector-search build: lists, zero (if N > 0), count, and
+ * if N > 0 scan, scatter, link. Vector-search decode: search, partial, merge.
  */
 typedef struct {
   hipEvent_t* events;   /* capacity events created by the caller (hipEventCreate) */
@@ -295,6 +376,18 @@ wave_status wave_decode_attention_traced(const wave_decode_params* p, const void
                                          int32_t* selected, void* workspace,
                                          size_t workspace_bytes, hipStream_t stream,
                                          wave_trace* trace);
+
+wave_status wave_anns_build_traced(const wave_anns_params* p, const void* k_cache,
+                                   const wave_anns_index* idx, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream,
+                                   wave_trace* trace);
+
+wave_status wave_anns_decode_attention_traced(const wave_anns_params* p, const void* q,
+                                              const void* k_cache, const void* v_cache,
+                                              const wave_anns_index* idx, float* out,
+                                              float* lse, int32_t* retrieved, int32_t* stats,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream, wave_trace* trace);
 
 /* Static, human-readable name of a status code. */
 const char* wave_status_string(wave_status s);

@@ -23,6 +23,9 @@ __all__ = [
     "alloc_decode_workspace", "wave_decode_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
     "wave_tier", "TierTensors", "alloc_tier", "wave_tier_state_size", "wave_tier_reset",
     "wave_decode_attention_tiered", "wave_tier_counters", "TIER_BLOCK",
+    "wave_anns_params", "wave_anns_index", "AnnsTensors", "alloc_anns_index",
+    "wave_anns_build_workspace_size", "wave_anns_build", "wave_anns_decode_workspace_size",
+    "wave_anns_decode_attention",
 ]
 
 # WAVE_INDEX_LIB selects another build of the library (e.g. the sanitized host-only one)
@@ -33,7 +36,9 @@ EXPORTED_SYMBOLS = (
     "wave_decode_workspace_size", "wave_decode_attention", "wave_dense_decode_attention",
     "wave_index_build_traced", "wave_decode_attention_traced", "wave_decode_attention_noalloc",
     "wave_tier_state_size", "wave_tier_reset", "wave_decode_attention_tiered",
-    "wave_tier_counters",
+    "wave_tier_counters", "wave_anns_build_workspace_size", "wave_anns_build",
+    "wave_anns_decode_workspace_size", "wave_anns_decode_attention", "wave_anns_build_traced",
+    "wave_anns_decode_attention_traced",
 )
 TIER_BLOCK = 32                    # cache rows per block of the host-memory tier
 NOALLOC_SCRATCH_BYTES = 64 << 20   # WAVE_NOALLOC_SCRATCH_BYTES
@@ -80,6 +85,23 @@ class wave_tier(ctypes.Structure):
                 ("n_slots", ctypes.c_int32)]
 
 
+class wave_anns_params(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("seq_len", ctypes.c_int64), ("index_len", ctypes.c_int64),
+                ("kv_capacity", ctypes.c_int64), ("n_sink", ctypes.c_int32),
+                ("n_recent", ctypes.c_int32), ("n_train", ctypes.c_int32),
+                ("list_len", ctypes.c_int32), ("degree", ctypes.c_int32),
+                ("n_entry", ctypes.c_int32), ("pool", ctypes.c_int32),
+                ("expand", ctypes.c_int32), ("n_retrieve", ctypes.c_int32),
+                ("max_rounds", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class wave_anns_index(ctypes.Structure):
+    _fields_ = [("train", ctypes.c_void_p), ("graph", ctypes.c_void_p),
+                ("entry", ctypes.c_void_p), ("lists", ctypes.c_void_p)]
+
+
 class wave_trace(ctypes.Structure):
     _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", ctypes.c_int32),
                 ("recorded", ctypes.c_int32)]
@@ -118,6 +140,15 @@ def library() -> ctypes.CDLL:
                                                      P(wave_index), vp, vp, vp, vp, sz, vp]
         lib.wave_tier_counters.argtypes = [P(wave_decode_params), P(wave_tier),
                                            P(ctypes.c_uint64), vp]
+        lib.wave_anns_build_workspace_size.argtypes = [P(wave_anns_params), P(sz)]
+        lib.wave_anns_build.argtypes = [P(wave_anns_params), vp, P(wave_anns_index), vp, sz, vp]
+        lib.wave_anns_decode_workspace_size.argtypes = [P(wave_anns_params), P(sz)]
+        lib.wave_anns_decode_attention.argtypes = [P(wave_anns_params), vp, vp, vp,
+                                                   P(wave_anns_index), vp, vp, vp, vp, vp, sz,
+                                                   vp]
+        lib.wave_anns_build_traced.argtypes = lib.wave_anns_build.argtypes + [P(wave_trace)]
+        lib.wave_anns_decode_attention_traced.argtypes = (
+            lib.wave_anns_decode_attention.argtypes + [P(wave_trace)])
         lib.wave_index_build_traced.argtypes = lib.wave_index_build.argtypes + [P(wave_trace)]
         lib.wave_decode_attention_traced.argtypes = (lib.wave_decode_attention.argtypes
                                                      + [P(wave_trace)])
@@ -347,3 +378,79 @@ def wave_tier_counters(p: wave_decode_params, tier: TierTensors, stream=None) ->
                                                                c, _stream(stream)))
     return {"rows_cached": c[0], "rows_host": c[1], "blocks_admitted": c[2],
             "blocks_refused": c[3]}
+
+
+# ------------------------------------------------------------------------------------
+# attention-aware vector search (a second retrieval zone)
+# ------------------------------------------------------------------------------------
+@dataclass
+class AnnsTensors:
+    """One layer's vector-search index (see wave_anns_index in include/wave_index.h)."""
+    train: object      # bf16 [B, Hkv, n_train, d]
+    graph: object      # int32 [B, Hkv, N, degree]
+    entry: object      # int32 [B, Hkv, n_train]
+    lists: object      # int32 [B, Hkv, n_train, list_len]
+
+    def c_struct(self) -> wave_anns_index:
+        return wave_anns_index(_ptr(self.train), _ptr(self.graph), _ptr(self.entry),
+                               _ptr(self.lists))
+
+
+def alloc_anns_index(p: wave_anns_params, train, device="cuda") -> AnnsTensors:
+    """Buffers of the graph for these parameters around the training queries `train`."""
+    import torch
+    B, H = p.batch, p.n_kv_heads
+    N = max(p.index_len - p.n_sink - p.n_recent, 0)
+    e = dict(device=device, dtype=torch.int32)
+    return AnnsTensors(train, torch.empty(B, H, N, p.degree, **e),
+                       torch.empty(B, H, p.n_train, **e),
+                       torch.empty(B, H, p.n_train, p.list_len, **e))
+
+
+def wave_anns_build_workspace_size(p: wave_anns_params) -> int:
+    n = ctypes.c_size_t(0)
+    _check("wave_anns_build_workspace_size",
+           library().wave_anns_build_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def wave_anns_decode_workspace_size(p: wave_anns_params) -> int:
+    n = ctypes.c_size_t(0)
+    _check("wave_anns_decode_workspace_size",
+           library().wave_anns_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def wave_anns_build(p: wave_anns_params, k_cache, index: AnnsTensors, workspace, stream=None,
+                    events=None) -> int:
+    """Enqueue the graph build (see wave_anns_build in include/wave_index.h); `events` as for
+    wave_index_build."""
+    idx = index.c_struct()
+    args = (ctypes.byref(p), _ptr(k_cache), ctypes.byref(idx), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    if events is None:
+        _check("wave_anns_build", library().wave_anns_build(*args))
+        return 0
+    tr, keep = _trace(events)
+    _check("wave_anns_build_traced", library().wave_anns_build_traced(*args, ctypes.byref(tr)))
+    return tr.recorded
+
+
+def wave_anns_decode_attention(p: wave_anns_params, q, k_cache, v_cache, index: AnnsTensors,
+                               out, lse=None, retrieved=None, stats=None, workspace=None,
+                               stream=None, events=None) -> int:
+    """Enqueue one decode step through the vector search (see wave_anns_decode_attention in
+    include/wave_index.h); `events` as for wave_index_build."""
+    idx = index.c_struct()
+    args = (ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(idx),
+            _ptr(out), _ptr(lse), _ptr(retrieved), _ptr(stats), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    if events is None:
+        _check("wave_anns_decode_attention", library().wave_anns_decode_attention(*args))
+        return 0
+    tr, keep = _trace(events)
+    _check("wave_anns_decode_attention_traced",
+           library().wave_anns_decode_attention_traced(*args, ctypes.byref(tr)))
+    return tr.recorded

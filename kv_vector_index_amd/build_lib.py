@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libwave_index.so")
 SAN_LIB = os.path.join(LIBDIR, "libwave_index_san.so")
-SOURCES = ["api.cpp", "build_kernels.hip", "decode_kernels.hip"]
+SOURCES = ["api.cpp", "build_kernels.hip", "decode_kernels.hip", "anns_kernels.hip"]
 HEADERS = ["wave_common.h", "wave_kernels.h"]
 
 HIPCC_FLAGS = [

@@ -655,3 +655,279 @@ wave_status wave_dense_decode_attention(const wave_decode_params* p, const void*
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- attention-aware vector search
+
+namespace {
+
+struct AnnsShape {
+  int G;
+  int64_t N;        // nodes: the indexed zone [n_sink, L0 - n_recent)
+  int64_t BH;
+  int nB;           // attention workgroups per (b, kv-head)
+};
+
+// Checks shared by the build and the decode (decode = 1 also checks seq_len and scale).
+wave_status check_anns(const wave_anns_params* p, int decode, AnnsShape* sh) {
+  if (!p) return WAVE_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->n_kv_heads < 1 || p->n_q_heads < 1 ||
+      p->n_q_heads % p->n_kv_heads != 0)
+    return WAVE_ERR_INVALID_ARG;
+  if (p->head_dim != wave::kHeadDim) return WAVE_ERR_UNSUPPORTED;
+  sh->G = p->n_q_heads / p->n_kv_heads;
+  if (sh->G > wave::kMaxGroup) return WAVE_ERR_UNSUPPORTED;
+  if (p->n_sink < 0 || p->n_recent < 0 || p->index_len < 0 ||
+      (int64_t)p->n_sink + p->n_recent > p->index_len || p->index_len > p->kv_capacity ||
+      p->kv_capacity > ((int64_t)1 << 40))
+    return WAVE_ERR_INVALID_ARG;
+  if (decode && (p->seq_len < p->index_len || p->seq_len > p->kv_capacity || !(p->scale > 0.f)))
+    return WAVE_ERR_INVALID_ARG;
+  if (p->n_train < 1 || p->n_train > wave::kAnnsMaxTrain || p->list_len < 1 ||
+      p->list_len > wave::kAnnsMaxList || p->degree < 1 || p->degree > wave::kAnnsMaxDegree ||
+      p->n_entry < 1 || p->n_entry > wave::kAnnsMaxEntry || p->pool < 1 ||
+      p->pool > wave::kAnnsMaxPool || p->expand < 1 || p->expand > wave::kAnnsMaxExpand ||
+      p->expand * p->degree > wave::kAnnsMaxCand || p->n_retrieve < 1 ||
+      p->n_retrieve > p->pool || p->max_rounds < 0)
+    return WAVE_ERR_INVALID_ARG;
+  sh->N = p->index_len - p->n_sink - p->n_recent;
+  sh->BH = (int64_t)p->batch * p->n_kv_heads;
+  if (sh->N >= ((int64_t)1 << 30) ||
+      wave::anns_search_lds(sh->N, p->pool) > wave::kAnnsMaxLds)   // (visited bitmap in LDS)
+    return WAVE_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!mul_ok(sh->BH, sh->N, &t) || !mul_ok(t, p->degree, &t) || t > ((int64_t)1 << 40))
+    return WAVE_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)p->n_sink + p->n_recent + (p->kv_capacity - p->index_len) +
+                       p->n_retrieve;
+  sh->nB = (int)std::min<int64_t>(std::max<int64_t>((rows + 127) / 128, 1), 64);
+  return WAVE_OK;
+}
+
+size_t anns_graph_bytes(const wave_anns_params* p, const AnnsShape& sh) {
+  return (size_t)sh.BH * sh.N * p->degree * 4;
+}
+size_t anns_entry_bytes(const wave_anns_params* p, const AnnsShape& sh) {
+  return (size_t)sh.BH * p->n_train * 4;
+}
+size_t anns_lists_bytes(const wave_anns_params* p, const AnnsShape& sh) {
+  return (size_t)sh.BH * p->n_train * p->list_len * 4;
+}
+
+size_t layout_anns_build(const wave_anns_params* p, const AnnsShape& sh, void* base,
+                         wave::AnnsArgs* a) {
+  Carver c(base);
+  int32_t* cnt = c.take<int32_t>((size_t)sh.BH * sh.N);
+  int32_t* off = c.take<int32_t>((size_t)sh.BH * (sh.N + 1));
+  int32_t* post = c.take<int32_t>((size_t)sh.BH * p->n_train * p->list_len);
+  if (a) {
+    a->cnt = cnt;
+    a->off = off;
+    a->post = post;
+  }
+  return c.off;
+}
+
+size_t layout_anns_decode(const wave_anns_params* p, const AnnsShape& sh, void* base,
+                          wave::AnnsArgs* a, wave::DecodeArgs* d) {
+  Carver c(base);
+  int32_t* pos = c.take<int32_t>((size_t)sh.BH * p->n_retrieve);
+  int32_t* n = c.take<int32_t>((size_t)sh.BH);
+  float* part = c.take<float>((size_t)sh.BH * sh.nB * sh.G * wave::kPartStride);
+  if (a) {
+    a->found_pos = pos;
+    a->found_n = n;
+  }
+  if (d) {
+    d->rows_pos = pos;
+    d->rows_n = n;
+    d->part = part;
+  }
+  return c.off;
+}
+
+void fill_anns_shape(const wave_anns_params* p, const AnnsShape& sh, wave::AnnsArgs* a) {
+  a->B = p->batch;
+  a->Hq = p->n_q_heads;
+  a->Hkv = p->n_kv_heads;
+  a->G = sh.G;
+  a->Lcap = p->kv_capacity;
+  a->L0 = p->index_len;
+  a->n_sink = p->n_sink;
+  a->n_recent = p->n_recent;
+  a->N = (int)sh.N;
+  a->n_t = p->n_train;
+  a->M = p->list_len;
+  a->R = p->degree;
+  a->n_entry = p->n_entry;
+  a->ef = p->pool;
+  a->W = p->expand;
+  a->n_ret = p->n_retrieve;
+  a->max_rounds = p->max_rounds;
+  a->search_lds = (uint32_t)wave::anns_search_lds(sh.N, p->pool);
+}
+
+wave_status anns_build_impl(const wave_anns_params* p, const void* k_cache,
+                            const wave_anns_index* idx, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream, wave::Tracer* tr) {
+  AnnsShape sh;
+  wave_status st = check_anns(p, 0, &sh);
+  if (st != WAVE_OK) return st;
+  if (!k_cache || !idx || !idx->train || (!idx->graph && sh.N > 0) || !idx->entry ||
+      !idx->lists)
+    return WAVE_ERR_INVALID_ARG;
+  const size_t need = layout_anns_build(p, sh, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return WAVE_ERR_WORKSPACE;
+  const size_t cache_bytes = (size_t)sh.BH * p->kv_capacity * wave::kHeadDim * 2;
+  const size_t train_bytes = (size_t)sh.BH * p->n_train * wave::kHeadDim * 2;
+  const void* ins[] = {k_cache, idx->train};
+  const size_t in_sz[] = {cache_bytes, train_bytes};
+  const void* outs[] = {idx->graph, idx->entry, idx->lists, workspace};
+  const size_t out_sz[] = {anns_graph_bytes(p, sh), anns_entry_bytes(p, sh),
+                           anns_lists_bytes(p, sh), workspace_bytes};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 2; ++j)
+      if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return WAVE_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return WAVE_ERR_ALIAS;
+  }
+  wave::AnnsArgs a{};
+  fill_anns_shape(p, sh, &a);
+  layout_anns_build(p, sh, workspace, &a);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.train = static_cast<const uint16_t*>(idx->train);
+  a.graph = idx->graph;
+  a.entry = idx->entry;
+  a.lists = idx->lists;
+  return wave::launch_anns_build(a, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
+}
+
+wave_status anns_decode_impl(const wave_anns_params* p, const void* q, const void* k_cache,
+                             const void* v_cache, const wave_anns_index* idx, float* out,
+                             float* lse, int32_t* retrieved, int32_t* stats, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, wave::Tracer* tr) {
+  AnnsShape sh;
+  wave_status st = check_anns(p, 1, &sh);
+  if (st != WAVE_OK) return st;
+  if (!q || !k_cache || !v_cache || !idx || !idx->train || (!idx->graph && sh.N > 0) ||
+      !idx->entry || !out)
+    return WAVE_ERR_INVALID_ARG;
+  const size_t need = layout_anns_decode(p, sh, nullptr, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return WAVE_ERR_WORKSPACE;
+  const size_t cache_bytes = (size_t)sh.BH * p->kv_capacity * wave::kHeadDim * 2;
+  const size_t qn = (size_t)p->batch * p->n_q_heads;
+  const void* ins[] = {q, k_cache, v_cache, idx->train, idx->graph, idx->entry};
+  const size_t in_sz[] = {qn * wave::kHeadDim * 2, cache_bytes, cache_bytes,
+                          (size_t)sh.BH * p->n_train * wave::kHeadDim * 2,
+                          anns_graph_bytes(p, sh), anns_entry_bytes(p, sh)};
+  const void* outs[] = {out, lse, retrieved, stats, workspace};
+  const size_t out_sz[] = {qn * wave::kHeadDim * 4, qn * 4,
+                           (size_t)sh.BH * p->n_retrieve * 4, (size_t)sh.BH * 8,
+                           workspace_bytes};
+  for (int i = 0; i < 5; ++i) {
+    if (!outs[i]) continue;
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return WAVE_ERR_ALIAS;
+    for (int j = i + 1; j < 5; ++j)
+      if (outs[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return WAVE_ERR_ALIAS;
+  }
+  wave::AnnsArgs a{};
+  wave::DecodeArgs d{};
+  fill_anns_shape(p, sh, &a);
+  layout_anns_decode(p, sh, workspace, &a, &d);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.train = static_cast<const uint16_t*>(idx->train);
+  a.q = static_cast<const uint16_t*>(q);
+  a.graph = idx->graph;
+  a.entry = idx->entry;
+  a.stats = stats;
+  d.q = a.q;
+  d.k = a.k;
+  d.v = static_cast<const uint16_t*>(v_cache);
+  d.out = out;
+  d.lse = lse;
+  d.B = p->batch;
+  d.Hq = p->n_q_heads;
+  d.Hkv = p->n_kv_heads;
+  d.G = sh.G;
+  d.L = p->seq_len;
+  d.L0 = p->index_len;
+  d.Lcap = p->kv_capacity;
+  d.n_sink = p->n_sink;
+  d.n_recent = p->n_recent;
+  d.scale = p->scale;
+  d.scale_log2 = p->scale * wave::kLog2eHost;
+  d.nB = sh.nB;
+  d.nP = sh.nB;
+  d.rows_k = p->n_retrieve;
+  if (retrieved) {   // (the search writes the caller's buffer, and the attention reads it)
+    a.found_pos = retrieved;
+    d.rows_pos = retrieved;
+  }
+  if (wave::launch_anns_search(a, stream, tr) != hipSuccess) return WAVE_ERR_HIP;
+  return wave::launch_listed_attention(d, stream, tr) == hipSuccess ? WAVE_OK : WAVE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+wave_status wave_anns_build_workspace_size(const wave_anns_params* p, size_t* bytes) {
+  AnnsShape sh;
+  const wave_status st = check_anns(p, 0, &sh);
+  if (st != WAVE_OK) return st;
+  if (!bytes) return WAVE_ERR_INVALID_ARG;
+  *bytes = layout_anns_build(p, sh, nullptr, nullptr);
+  return WAVE_OK;
+}
+
+wave_status wave_anns_build(const wave_anns_params* p, const void* k_cache,
+                            const wave_anns_index* idx, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return anns_build_impl(p, k_cache, idx, workspace, workspace_bytes, stream, nullptr);
+}
+
+wave_status wave_anns_build_traced(const wave_anns_params* p, const void* k_cache,
+                                   const wave_anns_index* idx, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream,
+                                   wave_trace* trace) {
+  if (!trace || (trace->capacity > 0 && !trace->events)) return WAVE_ERR_INVALID_ARG;
+  wave::Tracer tr{trace->events, trace->capacity, 0};
+  const wave_status st = anns_build_impl(p, k_cache, idx, workspace, workspace_bytes, stream,
+                                         &tr);
+  trace->recorded = tr.n;
+  return st;
+}
+
+wave_status wave_anns_decode_workspace_size(const wave_anns_params* p, size_t* bytes) {
+  AnnsShape sh;
+  const wave_status st = check_anns(p, 0, &sh);
+  if (st != WAVE_OK) return st;
+  if (!bytes) return WAVE_ERR_INVALID_ARG;
+  *bytes = layout_anns_decode(p, sh, nullptr, nullptr, nullptr);
+  return WAVE_OK;
+}
+
+wave_status wave_anns_decode_attention(const wave_anns_params* p, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const wave_anns_index* idx, float* out, float* lse,
+                                       int32_t* retrieved, int32_t* stats, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  return anns_decode_impl(p, q, k_cache, v_cache, idx, out, lse, retrieved, stats, workspace,
+                          workspace_bytes, stream, nullptr);
+}
+
+wave_status wave_anns_decode_attention_traced(const wave_anns_params* p, const void* q,
+                                              const void* k_cache, const void* v_cache,
+                                              const wave_anns_index* idx, float* out,
+                                              float* lse, int32_t* retrieved, int32_t* stats,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream, wave_trace* trace) {
+  if (!trace || (trace->capacity > 0 && !trace->events)) return WAVE_ERR_INVALID_ARG;
+  wave::Tracer tr{trace->events, trace->capacity, 0};
+  const wave_status st = anns_decode_impl(p, q, k_cache, v_cache, idx, out, lse, retrieved,
+                                          stats, workspace, workspace_bytes, stream, &tr);
+  trace->recorded = tr.n;
+  return st;
+}
+
+}  // extern "C"

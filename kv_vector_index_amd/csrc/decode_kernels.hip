@@ -426,48 +426,6 @@ __device__ __forceinline__ void attend_rows(const DecodeArgs& a, const uint16_t*
 // ------------------------------------------------------------------------------------
 // block-wide helpers for NT-thread workgroups
 // ------------------------------------------------------------------------------------
-template <int NT>
-struct ScanTmp {
-  uint32_t w[NT / 64];
-};
-
-// Inclusive scan over the 64 lanes of a wave: four DPP row shifts (lanes shifted in from
-// outside the 16-lane row read 0) scan each row, then the three lower rows' totals are read
-// back as scalars and added to the rows above them.
-__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
-  auto shr = [](uint32_t v, auto ctrl) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, decltype(ctrl)::value, 0xF, 0xF,
-                                                 true);
-  };
-  x += shr(x, std::integral_constant<int, 0x111>{});  // row_shr:1
-  x += shr(x, std::integral_constant<int, 0x112>{});  // row_shr:2
-  x += shr(x, std::integral_constant<int, 0x114>{});  // row_shr:4
-  x += shr(x, std::integral_constant<int, 0x118>{});  // row_shr:8
-  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
-  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
-  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
-}
-
-// exclusive scan over the block; *total = block sum
-template <int NT>
-__device__ __forceinline__ uint32_t scan_excl(uint32_t x, ScanTmp<NT>& tmp, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t v = wave_scan_incl(x);
-  if (lane == 63) tmp.w[wave] = v;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const uint32_t t = tmp.w[w];
-    before += (w < wave) ? t : 0u;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + v - x;
-}
 
 // Exclusive prefix of small counts c in [0, 7] over the lanes of a wave (ballot bit planes).
 __device__ __forceinline__ uint32_t wave_prefix_small(uint32_t c, uint32_t& wave_total) {
@@ -2395,6 +2353,32 @@ __global__ __launch_bounds__(kDecThreads) void k_dense_merge(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// attention over the steady zone and listed cache rows (the vector-search retrieval zone):
+// virtual rows [0, n_steady) are the steady zone, then rows_pos[bh][0 .. rows_n[bh]);
+// split-K partials over nB workgroups per head, then the dense merge
+// ------------------------------------------------------------------------------------
+template <int G>
+__global__ __launch_bounds__(kDecThreads) void k_listed_partial(DecodeArgs a) {
+  const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15;
+  u32x4 q[G];
+  load_q<G>(a, b, g, c, q);
+  Online<G> st;
+  st.init();
+  const int64_t n_steady = (int64_t)a.n_sink + a.n_recent + (a.L - a.L0);
+  const int32_t* pos = a.rows_pos + (size_t)bh * a.rows_k;
+  const int64_t n = n_steady + min(max(a.rows_n[bh], 0), a.rows_k);
+  const int nB = a.nB, w = blockIdx.x;
+  const int64_t t0 = n * w / nB, t1 = n * (w + 1) / nB;
+  const int64_t wb = t0 + (t1 - t0) * wave / 4, we = t0 + (t1 - t0) * (wave + 1) / 4;
+  attend_rows<G>(a, a.k, a.v, (size_t)bh * a.Lcap, q, st, wb, we, [&](int64_t t) {
+    return t < n_steady ? steady_row(a, t) : (int64_t)pos[t - n_steady];
+  });
+  write_block_partial<G>(st, nullptr, a.part + ((size_t)bh * nB + w) * G * kPartStride);
+}
+
+// ------------------------------------------------------------------------------------
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   const int BH = a.B * a.Hkv;
@@ -2423,6 +2407,14 @@ template <int G>
 static hipError_t launch_dense_g(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   const int BH = a.B * a.Hkv;
   hipError_t e = launch(tr, k_dense_partial<G>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
+  if (e != hipSuccess) return e;
+  return launch(tr, k_dense_merge<G>, dim3(BH), dim3(kDecThreads), 0, s, a);
+}
+
+template <int G>
+static hipError_t launch_listed_g(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
+  const int BH = a.B * a.Hkv;
+  hipError_t e = launch(tr, k_listed_partial<G>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
   return launch(tr, k_dense_merge<G>, dim3(BH), dim3(kDecThreads), 0, s, a);
 }
@@ -2474,6 +2466,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
 }
 hipError_t launch_dense_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   WAVE_DISPATCH_G(launch_dense_g, a, s, tr)
+}
+hipError_t launch_listed_attention(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
+  WAVE_DISPATCH_G(launch_listed_g, a, s, tr)
 }
 hipError_t tier_counters_copy(uint32_t* c, const void* state, hipStream_t s) {
   const hipError_t e = hipMemcpyAsync(c, state, kTcWords * sizeof(uint32_t),

@@ -15,6 +15,13 @@ hipError_t launch_copy_blocks(const CopyArgs&, hipStream_t, Tracer*) {
 }
 hipError_t launch_build(const BuildArgs&, hipStream_t, Tracer*) { return hipErrorNotSupported; }
 hipError_t launch_tier_reset(const DecodeArgs&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_listed_attention(const DecodeArgs&, hipStream_t, Tracer*) {
+  return hipErrorNotSupported;
+}
+hipError_t launch_anns_build(const AnnsArgs&, hipStream_t, Tracer*) { return hipErrorNotSupported; }
+hipError_t launch_anns_search(const AnnsArgs&, hipStream_t, Tracer*) {
+  return hipErrorNotSupported;
+}
 hipError_t tier_counters_copy(uint32_t*, const void*, hipStream_t) { return hipErrorNotSupported; }
 hipError_t noalloc_scratch(void** ptr) {
   *ptr = nullptr;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "wave_kernels.h"
 
 namespace wave {
@@ -85,6 +87,50 @@ __device__ __forceinline__ void st_dev(T* p, T v) {
 // Wait until this wave's earlier vector-memory operations have completed (device-coherent
 // stores acknowledged); also a compiler barrier for memory accesses.
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---- block-wide scans for NT-thread workgroups
+template <int NT>
+struct ScanTmp {
+  uint32_t w[NT / 64];
+};
+
+// Inclusive scan over the 64 lanes of a wave: four DPP row shifts (lanes shifted in from
+// outside the 16-lane row read 0) scan each row, then the three lower rows' totals are read
+// back as scalars and added to the rows above them.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+  auto shr = [](uint32_t v, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, decltype(ctrl)::value, 0xF, 0xF,
+                                                 true);
+  };
+  x += shr(x, std::integral_constant<int, 0x111>{});  // row_shr:1
+  x += shr(x, std::integral_constant<int, 0x112>{});  // row_shr:2
+  x += shr(x, std::integral_constant<int, 0x114>{});  // row_shr:4
+  x += shr(x, std::integral_constant<int, 0x118>{});  // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// exclusive scan over the block; *total = block sum
+template <int NT>
+__device__ __forceinline__ uint32_t scan_excl(uint32_t x, ScanTmp<NT>& tmp, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t v = wave_scan_incl(x);
+  if (lane == 63) tmp.w[wave] = v;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t t = tmp.w[w];
+    before += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + v - x;
+}
 
 // Enqueue a kernel; with a tracer that has room, its next two events time this kernel
 // (recorded at the start and the end of its execution). Returns the launch status.

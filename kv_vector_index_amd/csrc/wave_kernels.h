@@ -110,6 +110,11 @@ struct DecodeArgs {
   uint32_t* tctr;          // kTc* counters
   int32_t* req;            // [reqcap] blocks requested this step
   int nslots, nblk, reqcap;
+  // attention over the steady zone and listed rows (the vector-search retrieval zone):
+  // rows_pos [BH, rows_k] cache rows (-1 padded after rows_n[bh] entries)
+  const int32_t* rows_pos;
+  const int32_t* rows_n;
+  int rows_k;
 };
 
 // host-memory tier
@@ -135,6 +140,9 @@ hipError_t launch_tier_reset(const DecodeArgs& a, hipStream_t stream);
 hipError_t tier_counters_copy(uint32_t* c, const void* state, hipStream_t stream);
 // Enqueue dense decode over [0, L): split-K partials (part, nB per head) + merge.
 hipError_t launch_dense_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
+// Enqueue attention over the steady zone and the rows listed in rows_pos / rows_n:
+// split-K partials (part, nB per head) + merge.
+hipError_t launch_listed_attention(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
 
 // The library's own decode scratch on the current device (a static device array, one copy
 // per GPU, kept until the process ends), for callers that cannot allocate: its address,
@@ -188,5 +196,53 @@ struct CopyArgs {
 hipError_t launch_copy_blocks(const CopyArgs& c, hipStream_t stream, Tracer* tr);
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream, Tracer* tr);
+
+// ---------------------------------------------------------------- attention-aware vector search
+constexpr int kAnnsListQueries = 64;   // training queries per list workgroup (one wave)
+constexpr int kAnnsListCap = 96;       // candidate entries per training query in LDS
+constexpr int kAnnsMaxList = 64;       // M
+constexpr int kAnnsMaxDegree = 64;     // R
+constexpr int kAnnsSearchThreads = 1024;
+constexpr int kAnnsMaxPool = 1024;     // ef
+constexpr int kAnnsMaxCand = 2048;     // W * R (neighbours examined per round)
+constexpr int kAnnsMaxExpand = 64;     // W
+constexpr int kAnnsMaxEntry = 64;      // n_entry
+constexpr int kAnnsMaxTrain = 16384;   // training queries per (b, kv-head)
+constexpr int kAnnsPlaceShift = 24;    // posting key: place << 24 | list
+constexpr uint32_t kAnnsMaxLds = 160u * 1024u;   // LDS of one workgroup
+
+struct AnnsArgs {
+  const uint16_t* k;       // [B, Hkv, Lcap, d] the cache (positions)
+  const uint16_t* train;   // [B, Hkv, n_t, d] training queries
+  const uint16_t* q;       // [B, Hq, d] decode queries
+  int32_t* graph;          // [BH, N, R] neighbours, -1 padded
+  int32_t* entry;          // [BH, n_t] each training query's first node
+  int32_t* lists;          // [BH, n_t, M] training lists (node ids, -1 padded)
+  // build workspace
+  int32_t* cnt;            // [BH, N] postings per node, then the scatter cursor
+  int32_t* off;            // [BH, N + 1] first posting of each node
+  int32_t* post;           // [BH, n_t * M] postings: place << 24 | list
+  // search outputs
+  int32_t* found_pos;      // [BH, n_ret] retrieved cache rows, best first, -1 padded
+  int32_t* found_n;        // [BH]
+  int32_t* stats;          // [BH, 2] rounds, nodes scored (or null)
+  int B, Hq, Hkv, G;
+  int64_t Lcap, L0;
+  int n_sink, n_recent, N;
+  int n_t, M, R, n_entry, ef, W, n_ret, max_rounds;   // n_ret: k, the nodes retrieved
+  uint32_t search_lds;     // dynamic LDS bytes of the search workgroup
+};
+// LDS of the search workgroup, in this order: the search vector (d floats), the expanded
+// nodes (kAnnsMaxExpand), 32 counters, the round's candidates (scores, then ids), two pools
+// of ef entries (scores, then ids, each), the visited bitmap (one bit per node).
+constexpr uint32_t kAnnsLdsFixed = kHeadDim * 4 + kAnnsMaxExpand * 4 + 32 * 4 + kAnnsMaxCand * 8;
+constexpr uint32_t anns_pool_stride(int ef) { return (uint32_t)((ef + 3) / 4 * 4); }
+constexpr uint64_t anns_search_lds(int64_t N, int ef) {
+  return kAnnsLdsFixed + 16ull * anns_pool_stride(ef) + (uint64_t)((N + 127) / 128) * 16;
+}
+// Enqueue the graph build: training lists, postings, links, entries.
+hipError_t launch_anns_build(const AnnsArgs& a, hipStream_t stream, Tracer* tr);
+// Enqueue the search of one decode step (found_pos, found_n, stats).
+hipError_t launch_anns_search(const AnnsArgs& a, hipStream_t stream, Tracer* tr);
 
 }  // namespace wave

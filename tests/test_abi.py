@@ -222,3 +222,57 @@ def test_tier_validates_before_any_launch():
     assert lib.wave_tier_reset(ctypes.byref(p), None, None) == 1
     c = (ctypes.c_uint64 * 4)()
     assert lib.wave_tier_counters(ctypes.byref(p), None, c, None) == 1
+
+
+def anns_params(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, seq_len=4097,
+                index_len=4096, kv_capacity=4112, n_sink=4, n_recent=64, n_train=256,
+                list_len=32, degree=32, n_entry=16, pool=512, expand=32, n_retrieve=256,
+                max_rounds=100, scale=128 ** -0.5)
+    base.update(kw)
+    return wi.wave_anns_params(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), 2), (dict(n_q_heads=30), 1), (dict(n_q_heads=72, n_kv_heads=8), 2),
+    (dict(n_train=0), 1), (dict(n_train=16385), 1), (dict(list_len=65), 1),
+    (dict(degree=0), 1), (dict(n_entry=65), 1), (dict(pool=1025), 1), (dict(expand=0), 1),
+    (dict(expand=64, degree=64), 1), (dict(n_retrieve=513), 1), (dict(max_rounds=-1), 1),
+    (dict(n_sink=3000, n_recent=2000), 1), (dict(index_len=5000), 1),
+    # a visited set larger than the workgroup's LDS
+    (dict(index_len=2_000_000, kv_capacity=2_000_016, seq_len=2_000_001), 2),
+])
+def test_anns_validation(kw, code):
+    p = anns_params(**kw)
+    n = ctypes.c_size_t(0)
+    assert wi.library().wave_anns_build_workspace_size(ctypes.byref(p), ctypes.byref(n)) == code
+
+
+def test_anns_validates_before_any_launch():
+    """The vector search's checks run on the host before anything is enqueued: missing
+    buffers, a small workspace, an output over an input or another output, the step's own
+    length and scale."""
+    lib = wi.library()
+    p = anns_params()
+    bws, dws = wi.wave_anns_build_workspace_size(p), wi.wave_anns_decode_workspace_size(p)
+    assert bws > 0 and dws > 0
+    K, V, Q, TR, GR, EN, LI, WS, OUT = (i << 40 for i in range(1, 10))
+    idx = wi.wave_anns_index(TR, GR, EN, LI)
+    build = lambda i, ws=WS, n=bws: lib.wave_anns_build(  # noqa: E731
+        ctypes.byref(p), K, ctypes.byref(i), ws, n, None)
+    assert build(wi.wave_anns_index(TR, GR, EN, None)) == 1
+    assert build(wi.wave_anns_index(None, GR, EN, LI)) == 1
+    assert build(idx, n=bws - 256) == 3
+    assert build(idx, ws=None) == 3
+    assert build(wi.wave_anns_index(TR, K + 4096, EN, LI)) == 4       # graph over the cache
+    assert build(wi.wave_anns_index(TR, GR, GR + 64, LI)) == 4        # entry over the graph
+    dec = lambda pp=p, out=OUT, lse=None, ret=None, st=None, n=dws: (  # noqa: E731
+        lib.wave_anns_decode_attention(ctypes.byref(pp), Q, K, V, ctypes.byref(idx), out, lse,
+                                       ret, st, WS, n, None))
+    assert dec(out=None) == 1
+    assert dec(n=dws - 256) == 3
+    assert dec(out=Q) == 4                                             # out over q
+    assert dec(ret=GR + 128) == 4                                      # retrieved over the graph
+    assert dec(lse=OUT + 256) == 4                                     # lse over out
+    assert dec(pp=anns_params(seq_len=4095)) == 1                      # L below L0
+    assert dec(pp=anns_params(scale=0.0)) == 1
