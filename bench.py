@@ -31,6 +31,11 @@ with p10 / p90 of the call time. Further legs in the same line:
     whole context, decode steps;
   * sweep: the 28-layer Qwen-shaped stack at batch 4 and 256K over cluster sizes 8/16/32 and
     budgets 0.5/1/1.8/4 %: step throughput and the error against exact attention per point;
+  * anns: the same layer's decode steps through the attention-aware vector search (a graph
+    over the keys built from 4096 training queries; beam search; attention over the steady
+    zone and the retrieved tokens): build time, call time with its kernels, the recall of the
+    exact top-k, nodes scored, and the error against dense attention beside the wave
+    index's;
   * tier: the same layer's decode steps with the cache in pinned host memory behind a device
     block cache of a fraction of the layer's blocks (the wave buffer): call time against the
     resident call, the share of retrieved rows found in the block cache, bytes over the bus;
@@ -80,6 +85,8 @@ def parse():
                     help="resident stack over cluster sizes x retrieval budgets: throughput "
                          "and error against exact attention at each point ('none': skip)")
     ap.add_argument("--stack-steps", type=int, default=8)
+    ap.add_argument("--anns", default="llama128k",
+                    help="workload of the vector-search leg ('none' to skip)")
     ap.add_argument("--tier", default="1,0.05,0.01",
                     help="device block-cache sizes of the host-memory tier leg, as fractions "
                          "of the layer's 32-row blocks ('none' to skip)")
@@ -290,6 +297,9 @@ def main():
     cs = sorted(call_ms)
     res["decode_call_us_p10_p90"] = [round(cs[int(0.1 * (len(cs) - 1))] * 1e3, 2),
                                      round(cs[int(0.9 * (len(cs) - 1))] * 1e3, 2)]
+    if args.anns != "none" and args.anns == w.name:
+        res["anns"] = anns_leg(w, nds, x, k, v, q, k_out, v_out, idx, dps, dws, flush)
+        torch.cuda.empty_cache()
     if args.tier != "none":
         res["tier"] = tier_leg(w, nds, k_out, v_out, q, idx, dps, dws, out, lse, flush,
                                [float(f) for f in args.tier.split(",")], med(call_ms))
@@ -381,6 +391,135 @@ def decode_call_bytes(w, E):
     C, nr, G, d = w.n_clusters, w.n_retrieve, w.group, 128
     BH = w.batch * w.n_kv_heads
     return (2 * C * d + 4 * C + 2 * (C - nr) * d + 4 * d * E + 2 * G * d + 4 * G * d) * BH
+
+
+def anns_leg(w, nds, x, k, v, q, k_out, v_out, idx, dps, dws, flush, n_pos=1024, M=32, R=32,
+             E=16, ef=512, W=64, n_ret=256, err_steps=8):
+    """The decode steps of the main leg through the attention-aware vector search on the raw
+    (position-ordered) cache: the graph of the group's prefill queries at the last n_pos
+    positions (n_pos * G training queries per KV head), then per step the search and the
+    attention over the steady zone and the n_ret retrieved tokens. Reports the build, the
+    call (median, cache flushed before each call as in the main leg) and its kernels, the
+    rounds and nodes scored per search, the recall of the exact top-n_ret by the fp32 score,
+    and the relative l2 error against dense attention per (b, q head) beside the wave
+    index's error on the same steps."""
+    import numpy as np
+    import torch
+
+    import kv_vector_index_amd as wi
+    import synth
+
+    B, H, Hq, G, d = w.batch, w.n_kv_heads, w.n_q_heads, w.group, 128
+    L0, ns, nr = w.context, w.n_sink, w.n_recent
+    N = L0 - ns - nr
+    T = synth.training_queries(w, n_pos)
+    t_dev = torch.from_numpy(T.view(np.int16)).view(torch.bfloat16).cuda()
+    mk = lambda L: wi.wave_anns_params(B, Hq, H, d, L, L0, w.capacity, ns, nr, n_pos * G, M,  # noqa: E731
+                                       R, E, ef, W, n_ret, 100000, 1.0 / math.sqrt(d))
+    p0 = mk(L0)
+    index = wi.alloc_anns_index(p0, t_dev)
+    bws = torch.empty(wi.wave_anns_build_workspace_size(p0), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(wi.wave_anns_decode_workspace_size(p0), dtype=torch.uint8, device="cuda")
+    ev = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
+    bt = []
+    for _ in range(3):
+        e = ev()
+        e[0].record()
+        wi.wave_anns_build(p0, k, index, bws)
+        e[1].record()
+        bt.append(e)
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(16)]
+    for e in kev:
+        e.record()
+    n_bk = wi.wave_anns_build(p0, k, index, bws, events=[e.cuda_event for e in kev])
+    torch.cuda.synchronize()
+    build_ms = statistics.median(a.elapsed_time(b) for a, b in bt[1:])
+    names = ["lists", "zero", "count", "scan", "scatter", "link"][:n_bk // 2]
+    build_k = {nm: round(kev[2 * i].elapsed_time(kev[2 * i + 1]) * 1e3, 1)
+               for i, nm in enumerate(names)}
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    ret = torch.empty(nds, B, H, n_ret, dtype=torch.int32, device="cuda")
+    st = torch.empty(nds, B, H, 2, dtype=torch.int32, device="cuda")
+    ps = [mk(p.seq_len) for p in dps]
+    for s in range(min(4, nds)):                                   # warm-up
+        wi.wave_anns_decode_attention(ps[s], q[s], k, v, index, out, None, ret[s], st[s], aws)
+    cev = [ev() for _ in range(nds)]
+    for s in range(nds):
+        if flush is not None:
+            flush.sum()
+        cev[s][0].record()
+        wi.wave_anns_decode_attention(ps[s], q[s], k, v, index, out, None, ret[s], st[s], aws)
+        cev[s][1].record()
+    dk = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(nds)]
+    for s in range(nds):
+        if flush is not None:
+            flush.sum()
+        for e in dk[s]:
+            e.record()
+        wi.wave_anns_decode_attention(ps[s], q[s], k, v, index, out, None, ret[s], st[s], aws,
+                                      events=[e.cuda_event for e in dk[s]])
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in cev]
+    kern = lambda i: statistics.mean(dk[s][2 * i].elapsed_time(dk[s][2 * i + 1])  # noqa: E731
+                                     for s in range(nds))
+    stats = st.cpu().numpy()
+    # recall of the exact best n_ret nodes by the group-sum score (fp32 products on the GPU)
+    kn = k[:, :, ns:L0 - nr].float()
+    rec = []
+    for s in range(nds):
+        u = q[s].float().view(B, H, G, d).sum(dim=2)                   # [B, H, d]
+        sc = torch.matmul(kn, u.unsqueeze(-1)).squeeze(-1)             # fp32 [B, H, N]
+        best = sc.topk(n_ret, dim=-1).indices + ns
+        got = ret[s].long()
+        hit = (best.unsqueeze(-1) == got.unsqueeze(-2)).any(-1).float().mean(-1)
+        rec.append(hit.mean().item())
+    # error against dense attention, beside the wave index's, over err_steps steps
+    ref = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    wout = torch.empty_like(ref)
+    lse_ref = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+    lse_a = torch.empty_like(lse_ref)
+    dws_dense = torch.empty(wi.wave_decode_workspace_size(dps[0]), dtype=torch.uint8,
+                            device="cuda")
+    ea, ew, mass = [], [], []
+    for s in range(min(err_steps, nds)):
+        wi.wave_dense_decode_attention(dps[s], q[s], k, v, ref, lse_ref, dws_dense)
+        wi.wave_anns_decode_attention(ps[s], q[s], k, v, index, out, lse_a, None, None, aws)
+        mass.append(torch.exp(lse_a - lse_ref).flatten())
+        wi.wave_decode_attention(dps[s], q[s], k_out, v_out, idx, wout, None, None, dws)
+        den = ref.norm(dim=-1)
+        ea.append(((out - ref).norm(dim=-1) / den).flatten())
+        ew.append(((wout - ref).norm(dim=-1) / den).flatten())
+    ea, ew, mass = torch.cat(ea), torch.cat(ew), torch.cat(mass)
+    rounds, visited = stats[..., 0].astype(float), stats[..., 1].astype(float)
+    # bytes a search touches: the scored key rows and the expanded rows' neighbour lists (the
+    # seed kernel reads the training queries); the attention: K and V of the steady zone and
+    # the retrieved rows
+    search_bytes = float(np.mean(visited * 256 + rounds * W * R * 4)) * B * H
+    n_steady = ns + nr + (nds + 1) / 2
+    attn_bytes = (n_steady + n_ret) * 512 * B * H
+    t_seed, t_search, t_part, t_merge = kern(0), kern(1), kern(2), kern(3)
+    r = {"workload": w.name, "training_queries": n_pos * G, "list_len": M, "degree": R,
+         "n_entry": E, "pool": ef, "expand": W, "retrieved": n_ret, "nodes": N,
+         "build_ms": round(build_ms, 3), "build_kernel_us": build_k,
+         "call_us": round(statistics.median(call_ms) * 1e3, 2),
+         "decode_tok_s": round(B / (statistics.median(call_ms) * 1e-3), 1),
+         "kernel_us": {"seed": round(t_seed * 1e3, 2), "search": round(t_search * 1e3, 2),
+                       "partial": round(t_part * 1e3, 2),
+                       "merge": round(t_merge * 1e3, 2)},
+         "rounds_mean": round(float(rounds.mean()), 1),
+         "nodes_scored_mean": round(float(visited.mean()), 1),
+         "nodes_scored_frac": round(float(visited.mean()) / N, 4),
+         "recall_at_k": round(float(np.mean(rec)), 4),
+         "search_GBps": round(search_bytes / (t_search * 1e-3) / 1e9, 1),
+         "search_bytes_per_launch": round(search_bytes),
+         "attention_GBps": round(attn_bytes / ((t_part + t_merge) * 1e-3) / 1e9, 1),
+         "softmax_mass_on_attended_rows": round(mass.mean().item(), 4),
+         "rel_l2_err_vs_dense": {"anns_mean": round(ea.mean().item(), 4),
+                                 "anns_max": round(ea.max().item(), 4),
+                                 "wave_mean": round(ew.mean().item(), 4),
+                                 "wave_max": round(ew.max().item(), 4)}}
+    print(f"[bench] anns: {r}", file=sys.stderr, flush=True)
+    return r
 
 
 def tier_leg(w, nds, k_out, v_out, q, idx, dps, dws, out, lse, flush, fracs, resident_ms):

@@ -281,8 +281,9 @@ wave_status wave_tier_counters(const wave_decode_params* p, const wave_tier* tie
  *     list, the list's other nodes in order, else the list's head. The list heads are the
  *     training queries' entries.
  *   search (per step): u = the fp32 sum of the group's query rows (head order); a node's
- *     score is the fp32 dot product of u with its key, accumulated over the dims in order,
- *     each product and sum rounded (no fused multiply-add); ties to the lower id. The pool
+ *     score is the fp32 dot product of u with its key in a fixed order: each block of 8
+ *     dims summed in dim order, then the 16 block sums pairwise, neighbours first; each
+ *     product and sum rounded (no fused multiply-add); ties to the lower id. The pool
  *     starts with the entries of the n_entry training queries of largest score; each round
  *     expands the `expand` best unexpanded pool entries (their unvisited neighbours are
  *     scored) and the pool keeps its `pool` best entries, until no entry is left to expand
@@ -357,7 +358,7 @@ wave_status wave_anns_decode_attention(const wave_anns_params* p, const void* q,
  * n_sink + n_recent > 0), objective (if requested). Decode: score, histogram (only when
  * n_clusters > 8192), gather, retrieve (tiered: then fill).
  * Dense decode: partial, merge. Vector-search build: lists, zero (if N > 0), count, and
- * if N > 0 scan, scatter, link. Vector-search decode: search, partial, merge.
+ * if N > 0 scan, scatter, link. Vector-search decode: seed, search, partial, merge.
  */
 typedef struct {
   hipEvent_t* events;   /* capacity events created by the caller (hipEventCreate) */

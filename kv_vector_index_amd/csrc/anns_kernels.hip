@@ -6,17 +6,19 @@
 // Build, per (b, kv-head), over the N keys of the indexed zone (node x = position n_sink + x):
 //   1. k_anns_lists: each training query's M best nodes by inner product, best first (ties
 //      to the lower id). The scores come from v_mfma_f32_16x16x32_bf16 (keys as A rows,
-//      64 training queries as four B column tiles); every training query keeps its candidates
-//      above its current M-th score in LDS and sorts them down to M when the buffer fills.
+//      64 training queries as four B column tiles, 128 nodes per batch with the next batch's
+//      loads in flight, last position first); every training query keeps its candidates
+//      that reach its current M-th score in LDS and sorts them down to M when the buffer
+//      fills.
 //   2. k_anns_count / k_anns_scan / k_anns_scatter: the postings of every node (its place in
 //      each list that holds it, with the list), grouped by node.
 //   3. k_anns_link: each node's neighbours, at most R without repeats, in the order of its
 //      postings by (place, list): where it heads a list, the list's other nodes in list
 //      order, else the list's head. Each list's head is also the training query's entry.
 // Search, one 1024-thread workgroup per (b, kv-head) (k_anns_search): the search vector is
-// the fp32 sum of the group's query rows; every score is an fp32 dot product accumulated over
-// the dims in order without fused multiply-adds, so that each decision is reproducible
-// exactly. The pool starts from the entries of the n_entry training queries nearest the
+// the fp32 sum of the group's query rows; every score is an fp32 dot product in a fixed order
+// (blocks of 8 dims in order, then a pairwise tree of the block sums) without fused
+// multiply-adds, so that each decision is reproducible exactly. The pool starts from the entries of the n_entry training queries nearest the
 // search vector and each round expands the W best unexpanded pool entries: their unvisited
 // neighbours are scored, sorted and merged into the pool, which keeps its ef best entries.
 #include "wave_common.h"
@@ -28,9 +30,10 @@ namespace {
 
 constexpr int kAnnsListSortN = 128;    // a training query's candidates sort as 128 entries
 
-// best-first order: higher score, then lower id
+// best-first order: higher score, then lower id (no short-circuit: both operands are
+// evaluated, so the compiler keeps the comparisons free of branches)
 __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
-  return sa > sb || (sa == sb && ia < ib);
+  return (sa > sb) | ((sa == sb) & (ia < ib));
 }
 
 // ------------------------------------------------------------------------------------
@@ -102,8 +105,11 @@ __global__ __launch_bounds__(64) void k_anns_lists(AnnsArgs a) {
   typedef __attribute__((ext_vector_type(4))) float floatx4;
   __shared__ ListLds L;
   const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
-  const int bh = blockIdx.y;
-  const int t0 = blockIdx.x * kAnnsListQueries;
+  // (workgroups are dealt to the eight XCDs in turn: with bh = index mod BH, the workgroups
+  // of one (b, kv-head) share an XCD and its L2 while they stream the same keys)
+  const int BH = a.B * a.Hkv;
+  const int bh = blockIdx.x % BH;
+  const int t0 = (blockIdx.x / BH) * kAnnsListQueries;
   const int N = a.N, M = a.M;
   // B operands: training query t0 + 16 c + n, dims 32 s4 + 8 g .. + 7
   bf16x8 qb[4][4];
@@ -116,58 +122,84 @@ __global__ __launch_bounds__(64) void k_anns_lists(AnnsArgs a) {
           bf16x8, t < a.n_t ? ld16(a.train + ((size_t)bh * a.n_t + t) * kHeadDim + s4 * 32 + g * 8)
                             : u32x4{0, 0, 0, 0});
   }
+  // (a column past the last training query never takes a candidate)
   L.cnt[lane] = 0;
-  L.theta[lane] = kNegInf;
+  L.theta[lane] = t0 + lane < a.n_t ? kNegInf : __builtin_huge_valf();
   __syncthreads();
-  float th[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+  float th[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) th[c] = L.theta[16 * c + n];
   const uint16_t* kb = a.k + ((size_t)bh * a.Lcap + a.n_sink) * kHeadDim;
-  // A operands: node base + n, dims 32 s4 + 8 g .. + 7 (one tile of 16 nodes, loaded a tile
-  // ahead)
-  u32x4 ka[4], kn[4];
+  // A operands: node N - 1 - (base + n), dims 32 s4 + 8 g .. + 7, in batches of TB tiles of
+  // 16 nodes; the next batch's loads are in flight while a batch is scored. The nodes stream
+  // from the last position back (the training queries' best keys tend to lie near their own
+  // positions at the end, so the thresholds rise early); every new node then has a lower id
+  // than the nodes held, so it enters exactly when its score reaches the threshold.
+  constexpr int TB = 8;
+  u32x4 ka[TB][4], kn[TB][4];
+  auto load_batch = [&](int base, u32x4 (&dst)[TB][4]) {
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4)
-    ka[s4] = n < N ? ld16(kb + (size_t)n * kHeadDim + s4 * 32 + g * 8) : u32x4{0, 0, 0, 0};
-  for (int base = 0; base < N; base += 16) {
-    const int xn = base + 16 + n;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
-      kn[s4] = xn < N ? ld16(kb + (size_t)xn * kHeadDim + s4 * 32 + g * 8) : u32x4{0, 0, 0, 0};
-    floatx4 d[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      d[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TB; ++j) {
+      const int xr = base + 16 * j + n;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
-        d[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s4]),
-                                                       qb[c][s4], d[c], 0, 0, 0);
+        dst[j][s4] = xr < N ? ld16(kb + (size_t)(N - 1 - xr) * kHeadDim + s4 * 32 + g * 8)
+                            : u32x4{0, 0, 0, 0};
     }
-    // lane (g, n) holds nodes base + 4 g + i against training queries 16 c + n
+  };
+  load_batch(0, ka);
+  for (int base = 0; base < N; base += 16 * TB) {
+    load_batch(base + 16 * TB, kn);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int j = 0; j < TB; ++j) {
+      const int tb = base + 16 * j;
+      if (tb >= N) break;
+      floatx4 d[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int x = base + 4 * g + i;
-        if (x < N && t0 + 16 * c + n < a.n_t && d[c][i] > th[c]) {
-          const int qq = 16 * c + n;
-          const int p = atomicAdd(&L.cnt[qq], 1);
-          L.s[qq][p] = d[c][i];
-          L.id[qq][p] = x;
+      for (int c = 0; c < 4; ++c) {
+        d[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          d[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[j][s4]),
+                                                         qb[c][s4], d[c], 0, 0, 0);
+      }
+      // lane (g, n) holds nodes N - 1 - (tb + 4 g + i) against training queries 16 c + n;
+      // once the lists are full most tiles reach no threshold and skip the bookkeeping
+      bool hit = false;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hit |= tb + 4 * g + i < N && d[c][i] >= th[c];
+      if (!__ballot(hit)) continue;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int xr = tb + 4 * g + i;
+          if (xr < N && d[c][i] >= th[c]) {
+            const int qq = 16 * c + n;
+            const int p = atomicAdd(&L.cnt[qq], 1);
+            L.s[qq][p] = d[c][i];
+            L.id[qq][p] = N - 1 - xr;
+          }
         }
-      }
-    __syncthreads();
-    // a buffer that might not take the next tile's 16 is sorted down to M
-    uint64_t need = __ballot(L.cnt[lane] > kAnnsListCap - 16);
-    if (need) {
-      while (need) {
-        const int qq = __builtin_ctzll(need);
-        need &= need - 1;
-        compact_list(L, qq, M);
-      }
+      __syncthreads();
+      // a buffer that might not take the next tile's 16 is sorted down to M
+      uint64_t need = __ballot(L.cnt[lane] > kAnnsListCap - 16);
+      if (need) {
+        while (need) {
+          const int qq = __builtin_ctzll(need);
+          need &= need - 1;
+          compact_list(L, qq, M);
+        }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) th[c] = L.theta[16 * c + n];
+        for (int c = 0; c < 4; ++c) th[c] = L.theta[16 * c + n];
+      }
     }
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) ka[s4] = kn[s4];
+    for (int j = 0; j < TB; ++j)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) ka[j][s4] = kn[j][s4];
   }
   for (int qq = 0; qq < kAnnsListQueries && t0 + qq < a.n_t; ++qq) {
     compact_list(L, qq, M);
@@ -286,53 +318,165 @@ __global__ void k_anns_link(AnnsArgs a) {
 // ------------------------------------------------------------------------------------
 // search
 // ------------------------------------------------------------------------------------
-// fp32 dot product of u (d floats in LDS) with a bf16 row: products and sums rounded to
-// fp32 one at a time, over the dims in order
-__device__ __noinline__ float seq_dot(const float* u, const uint16_t* row) {
+// Dot product of u with a bf16 row by the 16 lanes of a DPP row: lane j holds u's dims
+// 8 j .. 8 j + 7 (uj) and the row's 16 bytes at the same dims (r). Its 8 products are summed
+// in dim order, then the 16 block sums pairwise, neighbours first (lane ^ 1, lane ^ 2, then the
+// half-row and row mirrors); every product and sum is rounded to fp32 (no fused
+// multiply-add), and every lane of the row receives the score.
+__device__ __forceinline__ float group_dot(const float (&uj)[8], const u32x4& r) {
 #pragma clang fp contract(off)
-  u32x4 r[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) r[c] = ld16(row + c * 8);
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
   float acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = u[c * 8 + 2 * e] * bf_lo(w[e]);
-      acc = acc + p0;
-      const float p1 = u[c * 8 + 2 * e + 1] * bf_hi(w[e]);
-      acc = acc + p1;
-    }
+  for (int e = 0; e < 4; ++e) {
+    const float p0 = uj[2 * e] * bf_lo(w[e]);
+    acc = acc + p0;
+    const float p1 = uj[2 * e + 1] * bf_hi(w[e]);
+    acc = acc + p1;
   }
-  return acc;
+  return sum16(acc);
 }
 
-// bitonic sort of (s, id)[0, n) best first, n padded to a power of two P with worst entries
-// (whole workgroup)
-__device__ void block_sort(float* s, int32_t* id, int n) {
-  int P = 2;
-  while (P < n) P <<= 1;
-  for (int i = n + threadIdx.x; i < P; i += blockDim.x) {
-    s[i] = kNegInf;
-    id[i] = INT_MAX;
-  }
-  __syncthreads();
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int pi = threadIdx.x; pi < P / 2; pi += blockDim.x) {
-        const int lo = 2 * pi - (pi & (j - 1)), hi = lo + j;
-        const bool up = (lo & k) == 0;   // an ascending block: the lower position is better
-        const float sl = s[lo], sh = s[hi];
-        const int il = id[lo], ih = id[hi];
-        if (better(sh, ih, sl, il) == up) {
-          s[lo] = sh; s[hi] = sl;
-          id[lo] = ih; id[hi] = il;
-        }
+// Scores of the rows base + ids[c] * d for c < n into sc[c], by the 16-lane groups of the
+// workgroup, U rows per group at a time (their loads in flight together). With adj, each
+// node's neighbour list (R entries from adj + id * R) is read too, so that it is in the
+// cache if the node is expanded in a later round; the values fold into *sink.
+template <int NT, int U>
+__device__ __forceinline__ void score_rows(const float (&uj)[8], const uint16_t* base,
+                                           const int32_t* ids, float* sc, int n,
+                                           const int32_t* adj = nullptr, int R = 0,
+                                           int32_t* sink = nullptr) {
+  constexpr int kG = NT / 16;
+  const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
+  for (int c0 = grp; c0 < n; c0 += U * kG) {
+    u32x4 r[U];
+    int32_t nb[U];
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+      const int c = c0 + m * kG;
+      const int id = c < n ? (ids ? ids[c] : c) : 0;
+      r[m] = c < n ? ld16(base + (size_t)id * kHeadDim + 8 * j) : u32x4{0, 0, 0, 0};
+      nb[m] = adj && c < n ? adj[(size_t)id * R + min(4 * j, R - 1)] : 0;
+    }
+    if (adj) {
+#pragma unroll
+      for (int m = 0; m < U; ++m) *sink ^= nb[m];
+    }
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+      const int c = c0 + m * kG;
+      if (c < n) {
+        const float v = group_dot(uj, r[m]);
+        if (j == 0) sc[c] = v;
       }
-      __syncthreads();
     }
   }
+}
+
+// Sort entries [c0, c0 + 64) of (es, ei) best first across the lanes of one wave (entries
+// from n on count as worst and stay unwritten): a bitonic network over lane exchanges.
+__device__ __forceinline__ void wave_sort64(float* es, int32_t* ei, int c0, int n) {
+  const int lane = threadIdx.x & 63, p = c0 + lane;
+  float v = p < n ? es[p] : kNegInf;
+  int i = p < n ? ei[p] : INT_MAX;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float pv = __shfl_xor(v, j);
+      const int pi = __shfl_xor(i, j);
+      const bool lower = (lane & j) == 0, up = (lane & k) == 0;
+      // the lower lane of an ascending block keeps the better entry
+      if ((lower == up) != better(v, i, pv, pi)) {
+        v = pv;
+        i = pi;
+      }
+    }
+  }
+  if (p < n) {
+    es[p] = v;
+    ei[p] = i;
+  }
+}
+
+// The number of entries of the sorted run (es, ei)[c0, c0 + m) better than (s, id).
+__device__ __forceinline__ int count_better_sorted(const float* es, const int32_t* ei, int c0,
+                                                   int m, float s, int id) {
+  int lo = 0, hi = m;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (better(es[c0 + mid], ei[c0 + mid], s, id)) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// The entries of (es, ei)[0, n), made of sorted runs of `run` entries, better than (s, id),
+// leaving out the run that starts at `skip` (none when skip < 0).
+__device__ __forceinline__ int count_better_runs(const float* es, const int32_t* ei, int n,
+                                                 int run, int skip, float s, int id) {
+  int cnt = 0;
+  for (int c0 = 0; c0 < n; c0 += run)
+    if (c0 != skip) cnt += count_better_sorted(es, ei, c0, min(run, n - c0), s, id);
+  return cnt;
+}
+
+// The rank of entry e of (es, ei)[0, n), made of sorted runs of `run` entries: its place in
+// its own run plus the entries better than it in each other run.
+__device__ __forceinline__ int rank_in_runs(const float* es, const int32_t* ei, int n, int run,
+                                            int e) {
+  return e % run + count_better_runs(es, ei, n, run, e - e % run, es[e], ei[e]);
+}
+
+// the search vector u of (b, kv-head): the group's query rows summed in fp32, head by head;
+// this lane's 8 dims (8 (lane & 15) ..) into uj. Needs 128 floats of LDS and a barrier.
+__device__ __forceinline__ void search_vector(const AnnsArgs& a, int bh, float* u,
+                                              float (&uj)[8]) {
+  const int b = bh / a.Hkv, g = bh % a.Hkv;
+  if (threadIdx.x < kHeadDim) {
+    const uint16_t* q = a.q + (size_t)(b * a.Hq + g * a.G) * kHeadDim + threadIdx.x;
+    float v = __uint_as_float((uint32_t)q[0] << 16);
+    for (int h = 1; h < a.G; ++h) v = v + __uint_as_float((uint32_t)q[(size_t)h * kHeadDim] << 16);
+    u[threadIdx.x] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 8; ++e) uj[e] = u[8 * (threadIdx.x & 15) + e];
+}
+
+// ---- seeds: workgroup x of (b, kv-head) scores training queries [x chunk, (x + 1) chunk)
+// and keeps its n_entry best, best first (score descending, id ascending; -inf / INT_MAX
+// pads)
+constexpr int kSeedThreads = 256;
+__global__ __launch_bounds__(kSeedThreads) void k_anns_seed(AnnsArgs a) {
+  __shared__ float u[kHeadDim];
+  __shared__ float sc[kAnnsMaxTrain / kAnnsMaxSeedWG];
+  __shared__ int32_t sid[kAnnsMaxTrain / kAnnsMaxSeedWG];
+  const int bh = blockIdx.y, x = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float uj[8];
+  search_vector(a, bh, u, uj);
+  const int t0 = x * a.seed_chunk, n = max(0, min(a.n_t - t0, a.seed_chunk));
+  score_rows<kSeedThreads, 8>(uj, a.train + ((size_t)bh * a.n_t + t0) * kHeadDim, nullptr, sc,
+                              n);
+  for (int c = threadIdx.x; c < n; c += kSeedThreads) sid[c] = t0 + c;
+  __syncthreads();
+  for (int c0 = 64 * wave; c0 < n; c0 += kSeedThreads) wave_sort64(sc, sid, c0, n);
+  __syncthreads();
+  // the n_entry best by rank among the sorted runs of 64; padding where n < n_entry
+  float* out_s = a.seed_s + ((size_t)bh * kAnnsMaxSeedWG + x) * a.n_entry;
+  int32_t* out_i = a.seed_i + ((size_t)bh * kAnnsMaxSeedWG + x) * a.n_entry;
+  for (int c = threadIdx.x; c < n; c += kSeedThreads) {
+    const int r = rank_in_runs(sc, sid, n, 64, c);
+    if (r < a.n_entry) {
+      out_s[r] = sc[c];
+      out_i[r] = sid[c];
+    }
+  }
+  for (int r = n + threadIdx.x; r < a.n_entry; r += kSeedThreads) {
+    out_s[r] = kNegInf;
+    out_i[r] = INT_MAX;
+  }
+  (void)lane;
 }
 
 constexpr int32_t kExpanded = (int32_t)0x80000000;   // pool id flag: expanded
@@ -353,107 +497,87 @@ __global__ __launch_bounds__(kAnnsSearchThreads) void k_anns_search(AnnsArgs a) 
                     reinterpret_cast<int32_t*>(lds + kAnnsLdsFixed + 12 * ps)};
   uint32_t* vis = reinterpret_cast<uint32_t*>(lds + kAnnsLdsFixed + 16 * ps);
   static_assert(kAnnsSearchThreads / 64 <= 16, "scan words fit the counters");
+  static_assert(kAnnsMaxSeedWG * kAnnsMaxEntry <= kAnnsMaxCand, "seed candidates fit");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bh = blockIdx.x, b = bh / a.Hkv, g = bh % a.Hkv;
-  const int N = a.N;
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int N = a.N, E = a.n_entry;
   const uint16_t* kb = a.k + ((size_t)bh * a.Lcap + a.n_sink) * kHeadDim;
 
-  // search vector: the group's query rows summed in fp32, head by head
-  if (tid < kHeadDim) {
-    const uint16_t* q = a.q + (size_t)(b * a.Hq + g * a.G) * kHeadDim + tid;
-    float v = __uint_as_float((uint32_t)q[0] << 16);
-    for (int h = 1; h < a.G; ++h) v = v + __uint_as_float((uint32_t)q[(size_t)h * kHeadDim] << 16);
-    u[tid] = v;
-  }
   for (int i = tid; i < (N + 31) / 32; i += kAnnsSearchThreads) vis[i] = 0u;
   if (tid < kCtrScan) ctr[tid] = 0;
-  __syncthreads();
-
-  // ---- seeds: each wave's n_entry nearest training queries by repeated wave argmax, then
-  // the best n_entry of those; their entries are scored
-  constexpr int kTPT = kAnnsMaxTrain / kAnnsSearchThreads;   // training queries per thread
-  const int E = a.n_entry;
-  {
-    float ts[kTPT];
-#pragma unroll
-    for (int j = 0; j < kTPT; ++j) {
-      const int t = tid + j * kAnnsSearchThreads;
-      ts[j] = t < a.n_t ? seq_dot(u, a.train + ((size_t)bh * a.n_t + t) * kHeadDim) : kNegInf;
-    }
-    uint32_t used = 0;
-    for (int e = 0; e < E; ++e) {
-      float bs = kNegInf;
-      int bi = INT_MAX, bj = -1;
-#pragma unroll
-      for (int j = 0; j < kTPT; ++j) {
-        const int t = tid + j * kAnnsSearchThreads;
-        if (!((used >> j) & 1u) && t < a.n_t && better(ts[j], t, bs, bi)) {
-          bs = ts[j];
-          bi = t;
-          bj = j;
-        }
-      }
-      float ws = bs;
-      int wi = bi;
-#pragma unroll
-      for (int m = 32; m > 0; m >>= 1) {
-        const float os = __shfl_xor(ws, m);
-        const int oi = __shfl_xor(wi, m);
-        if (better(os, oi, ws, wi)) {
-          ws = os;
-          wi = oi;
-        }
-      }
-      if (bj >= 0 && bi == wi) used |= 1u << bj;
-      if (lane == 0) {
-        cs[wave * E + e] = ws;
-        ci[wave * E + e] = wi;
-      }
-    }
+  // the seed workgroups' candidates
+  const int ns = a.nseed * E;
+  for (int i = tid; i < ns; i += kAnnsSearchThreads) {
+    const int w = i / E, e = i - w * E;
+    cs[i] = a.seed_s[((size_t)bh * kAnnsMaxSeedWG + w) * E + e];
+    ci[i] = a.seed_i[((size_t)bh * kAnnsMaxSeedWG + w) * E + e];
+  }
+  float uj[8];
+  search_vector(a, bh, u, uj);          // (its barrier also publishes the candidates)
+  // ---- seeds: the entries of the n_entry best training queries (rank among the candidates)
+  int seed_t = INT_MAX;
+  if (tid < ns) {   // (each seed workgroup's list is a sorted run of E)
+    if (rank_in_runs(cs, ci, ns, E, tid) < E) seed_t = ci[tid];
   }
   __syncthreads();
-  block_sort(cs, ci, (kAnnsSearchThreads / 64) * E);
-  const int tseed = tid < E ? ci[tid] : INT_MAX;
-  __syncthreads();
-  if (tid < E && tseed < a.n_t) {
-    const int x = a.entry[(size_t)bh * a.n_t + tseed];
+  if (seed_t < a.n_t) {
+    const int x = a.entry[(size_t)bh * a.n_t + seed_t];
     if (x >= 0 && x < N) {
       const uint32_t bit = 1u << (x & 31);
-      if (!(atomicOr(&vis[x >> 5], bit) & bit)) {
-        const float sc = seq_dot(u, kb + (size_t)x * kHeadDim);
-        const int p = atomicAdd(&ctr[kCtrCand], 1);
-        cs[p] = sc;
-        ci[p] = x;
-      }
+      if (!(atomicOr(&vis[x >> 5], bit) & bit)) ci[atomicAdd(&ctr[kCtrCand], 1)] = x;
     }
   }
   __syncthreads();
 
   int cur = 0, psize = 0, rounds = 0;
+  int32_t sink = 0;
   for (;;) {
-    // ---- the round's new nodes (ctr[kCtrCand] of them in cs, ci): sort, merge into the pool
+    // ---- the listed new nodes ci[0, nc): scored, sorted in runs of 64 (one wave each), then
+    // merged into the pool by rank (a pool entry moves down by the new nodes better than it;
+    // a new node lands after the pool entries and the new nodes better than it); the pool
+    // keeps its ef best
     const int nc = ctr[kCtrCand];
     if (nc > 0) {
-      block_sort(cs, ci, nc);
-      const int out = min(a.ef, psize + nc);
+      score_rows<kAnnsSearchThreads, 4>(uj, kb, ci, cs, nc, a.graph + (size_t)bh * N * a.R,
+                                        a.R, &sink);
+      __syncthreads();
+      for (int c0 = 64 * (tid >> 6); c0 < nc; c0 += kAnnsSearchThreads) wave_sort64(cs, ci, c0, nc);
+      __syncthreads();
       const float* S = pS[cur];
       const int32_t* I = pI[cur];
-      for (int o = tid; o < out; o += kAnnsSearchThreads) {
-        // co-rank: i pool entries and o - i new nodes precede output o
-        int lo = max(0, o - nc), hi = min(o, psize);
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1, j = o - mid;
-          if (better(S[mid], I[mid] & INT_MAX, cs[j - 1], ci[j - 1])) lo = mid + 1;
-          else hi = mid;
+      float* S2 = pS[cur ^ 1];
+      int32_t* I2 = pI[cur ^ 1];
+      for (int e = tid; e < psize + nc; e += kAnnsSearchThreads) {
+        float sv;
+        int32_t iv, id;
+        int rank;
+        if (e < psize) {
+          sv = S[e];
+          iv = I[e];
+          id = iv & INT_MAX;
+          rank = e;
+        } else {
+          sv = cs[e - psize];
+          iv = id = ci[e - psize];
+          int lo = 0, hi = psize;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (better(S[mid], I[mid] & INT_MAX, sv, id)) lo = mid + 1;
+            else hi = mid;
+          }
+          rank = lo;
         }
-        const int i = lo, j = o - lo;
-        const bool from_pool = i < psize && (j >= nc || better(S[i], I[i] & INT_MAX, cs[j], ci[j]));
-        pS[cur ^ 1][o] = from_pool ? S[i] : cs[j];
-        pI[cur ^ 1][o] = from_pool ? I[i] : ci[j];
+        // the new nodes better than it: sorted runs of 64 (its own run: its place)
+        rank += count_better_runs(cs, ci, nc, 64, e < psize ? -1 : (e - psize) & ~63, sv, id) +
+                (e < psize ? 0 : (e - psize) & 63);
+        if (rank < a.ef) {
+          S2[rank] = sv;
+          I2[rank] = iv;
+        }
       }
       cur ^= 1;
-      psize = out;
+      psize = min(a.ef, psize + nc);
     }
     if (tid == 0) ctr[kCtrVisited] += nc;
     __syncthreads();
@@ -472,23 +596,21 @@ __global__ __launch_bounds__(kAnnsSearchThreads) void k_anns_search(AnnsArgs a) 
     __syncthreads();
     if (nsel == 0) break;
     ++rounds;
-    // ---- their unvisited neighbours, scored
+    // ---- their unvisited neighbours, listed
     for (int s = tid; s < nsel * a.R; s += kAnnsSearchThreads) {
       const int src = sel[s / a.R];
       const int y = a.graph[((size_t)bh * N + src) * a.R + s % a.R];
       if (y < 0 || y >= N) continue;
       const uint32_t bit = 1u << (y & 31);
       if (atomicOr(&vis[y >> 5], bit) & bit) continue;
-      const float sc = seq_dot(u, kb + (size_t)y * kHeadDim);
-      const int p = atomicAdd(&ctr[kCtrCand], 1);
-      cs[p] = sc;
-      ci[p] = y;
+      ci[atomicAdd(&ctr[kCtrCand], 1)] = y;
     }
     __syncthreads();
   }
   // ---- the k best pool entries
   for (int o = tid; o < a.n_ret; o += kAnnsSearchThreads)
     a.found_pos[(size_t)bh * a.n_ret + o] = o < psize ? (pI[cur][o] & INT_MAX) + a.n_sink : -1;
+  atomicXor(&ctr[kCtrScan - 1], sink);   // (keeps every thread's neighbour-list reads)
   if (tid == 0) {
     a.found_n[bh] = min(a.n_ret, psize);
     if (a.stats) {
@@ -503,7 +625,7 @@ __global__ __launch_bounds__(kAnnsSearchThreads) void k_anns_search(AnnsArgs a) 
 hipError_t launch_anns_build(const AnnsArgs& a, hipStream_t s, Tracer* tr) {
   const int BH = a.B * a.Hkv;
   hipError_t e = launch(tr, k_anns_lists,
-                        dim3((a.n_t + kAnnsListQueries - 1) / kAnnsListQueries, BH), dim3(64), 0,
+                        dim3((a.n_t + kAnnsListQueries - 1) / kAnnsListQueries * BH), dim3(64), 0,
                         s, a);
   if (e != hipSuccess) return e;
   const size_t nodes = (size_t)BH * a.N, entries = (size_t)BH * a.n_t * a.M;
@@ -523,9 +645,11 @@ hipError_t launch_anns_build(const AnnsArgs& a, hipStream_t s, Tracer* tr) {
 }
 
 hipError_t launch_anns_search(const AnnsArgs& a, hipStream_t s, Tracer* tr) {
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_anns_search),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)a.search_lds);
+  hipError_t e = launch(tr, k_anns_seed, dim3(a.nseed, a.B * a.Hkv), dim3(kSeedThreads), 0, s,
+                        a);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_anns_search),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)a.search_lds);
   if (e != hipSuccess) return e;
   return launch(tr, k_anns_search, dim3(a.B * a.Hkv), dim3(kAnnsSearchThreads), a.search_lds,
                 s, a);

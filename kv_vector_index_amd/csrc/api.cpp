@@ -692,14 +692,14 @@ wave_status check_anns(const wave_anns_params* p, int decode, AnnsShape* sh) {
   sh->N = p->index_len - p->n_sink - p->n_recent;
   sh->BH = (int64_t)p->batch * p->n_kv_heads;
   if (sh->N >= ((int64_t)1 << 30) ||
-      wave::anns_search_lds(sh->N, p->pool) > wave::kAnnsMaxLds)   // (visited bitmap in LDS)
+      wave::anns_search_lds(sh->N, p->pool) > wave::kAnnsMaxLds)   // (visited set on chip)
     return WAVE_ERR_UNSUPPORTED;
   int64_t t;
   if (!mul_ok(sh->BH, sh->N, &t) || !mul_ok(t, p->degree, &t) || t > ((int64_t)1 << 40))
     return WAVE_ERR_INVALID_ARG;
   const int64_t rows = (int64_t)p->n_sink + p->n_recent + (p->kv_capacity - p->index_len) +
                        p->n_retrieve;
-  sh->nB = (int)std::min<int64_t>(std::max<int64_t>((rows + 127) / 128, 1), 64);
+  sh->nB = (int)std::min<int64_t>(std::max<int64_t>((rows + 31) / 32, 1), 64);
   return WAVE_OK;
 }
 
@@ -733,9 +733,13 @@ size_t layout_anns_decode(const wave_anns_params* p, const AnnsShape& sh, void* 
   int32_t* pos = c.take<int32_t>((size_t)sh.BH * p->n_retrieve);
   int32_t* n = c.take<int32_t>((size_t)sh.BH);
   float* part = c.take<float>((size_t)sh.BH * sh.nB * sh.G * wave::kPartStride);
+  float* seed_s = c.take<float>((size_t)sh.BH * wave::kAnnsMaxSeedWG * p->n_entry);
+  int32_t* seed_i = c.take<int32_t>((size_t)sh.BH * wave::kAnnsMaxSeedWG * p->n_entry);
   if (a) {
     a->found_pos = pos;
     a->found_n = n;
+    a->seed_s = seed_s;
+    a->seed_i = seed_i;
   }
   if (d) {
     d->rows_pos = pos;
@@ -764,6 +768,8 @@ void fill_anns_shape(const wave_anns_params* p, const AnnsShape& sh, wave::AnnsA
   a->n_ret = p->n_retrieve;
   a->max_rounds = p->max_rounds;
   a->search_lds = (uint32_t)wave::anns_search_lds(sh.N, p->pool);
+  a->nseed = std::min(wave::kAnnsMaxSeedWG, (p->n_train + 255) / 256);
+  a->seed_chunk = (p->n_train + a->nseed - 1) / a->nseed;
 }
 
 wave_status anns_build_impl(const wave_anns_params* p, const void* k_cache,

@@ -208,6 +208,7 @@ constexpr int kAnnsMaxCand = 2048;     // W * R (neighbours examined per round)
 constexpr int kAnnsMaxExpand = 64;     // W
 constexpr int kAnnsMaxEntry = 64;      // n_entry
 constexpr int kAnnsMaxTrain = 16384;   // training queries per (b, kv-head)
+constexpr int kAnnsMaxSeedWG = 16;     // seed workgroups per (b, kv-head)
 constexpr int kAnnsPlaceShift = 24;    // posting key: place << 24 | list
 constexpr uint32_t kAnnsMaxLds = 160u * 1024u;   // LDS of one workgroup
 
@@ -226,6 +227,9 @@ struct AnnsArgs {
   int32_t* found_pos;      // [BH, n_ret] retrieved cache rows, best first, -1 padded
   int32_t* found_n;        // [BH]
   int32_t* stats;          // [BH, 2] rounds, nodes scored (or null)
+  float* seed_s;           // [BH, kAnnsMaxSeedWG, n_entry] each seed workgroup's best training
+  int32_t* seed_i;         //   queries: scores and indices
+  int nseed, seed_chunk;   // seed workgroups per (b, kv-head), training queries per one
   int B, Hq, Hkv, G;
   int64_t Lcap, L0;
   int n_sink, n_recent, N;
@@ -233,16 +237,17 @@ struct AnnsArgs {
   uint32_t search_lds;     // dynamic LDS bytes of the search workgroup
 };
 // LDS of the search workgroup, in this order: the search vector (d floats), the expanded
-// nodes (kAnnsMaxExpand), 32 counters, the round's candidates (scores, then ids), two pools
+// nodes (kAnnsMaxExpand), 32 counters, the round's new nodes (scores, then ids), two pools
 // of ef entries (scores, then ids, each), the visited bitmap (one bit per node).
 constexpr uint32_t kAnnsLdsFixed = kHeadDim * 4 + kAnnsMaxExpand * 4 + 32 * 4 + kAnnsMaxCand * 8;
-constexpr uint32_t anns_pool_stride(int ef) { return (uint32_t)((ef + 3) / 4 * 4); }
+constexpr uint32_t anns_pool_stride(int n) { return (uint32_t)((n + 3) / 4 * 4); }
 constexpr uint64_t anns_search_lds(int64_t N, int ef) {
   return kAnnsLdsFixed + 16ull * anns_pool_stride(ef) + (uint64_t)((N + 127) / 128) * 16;
 }
 // Enqueue the graph build: training lists, postings, links, entries.
 hipError_t launch_anns_build(const AnnsArgs& a, hipStream_t stream, Tracer* tr);
-// Enqueue the search of one decode step (found_pos, found_n, stats).
+// Enqueue the search of one decode step: the seed kernel (nseed workgroups per head), then
+// the search (found_pos, found_n, stats).
 hipError_t launch_anns_search(const AnnsArgs& a, hipStream_t stream, Tracer* tr);
 
 }  // namespace wave

@@ -32,8 +32,11 @@ abstract gives no algorithm; these readings fill it in (each is listed in the de
       the pool keeps its ef best entries, until every pool entry is expanded or max_rounds
       rounds have run. The k best pool entries are retrieved.
   A6  precision of the search's decisions: the search vector is the fp32 sum of the bf16
-      query rows in head order; a score is the fp32 sum over dims 0..d-1 in order of the
-      fp32 products, with no fused multiply-add. Ties go to the lower id.
+      query rows in head order. A score is an fp32 inner product in a fixed order: the
+      fp32 products of each block of 8 consecutive dims are summed in dim order, and the
+      d/8 block sums are combined by a balanced pairwise tree (neighbours first); every
+      product and sum is rounded to fp32, with no fused multiply-add. Ties go to the lower
+      id.
   A7  attention runs over the steady zone and the retrieved tokens only (no estimate of
       the rest), one softmax, in fp64.
 
@@ -146,14 +149,28 @@ def group_vector(q: np.ndarray) -> np.ndarray:
     return s
 
 
+SCORE_BLOCK = 8   # dims summed in order before the pairwise tree (A6)
+
+
 def scores_f32(u: np.ndarray, rows: np.ndarray) -> np.ndarray:
-    """fp32 inner products of u (float32 [d]) with bf16 rows [n, d], accumulated over dims in
-    order, each product and each sum rounded to fp32 (A6)."""
+    """fp32 inner products of u (float32 [d]) with bf16 rows [n, d] in the order of A6: each
+    block of 8 dims (the whole row when d < 8) summed in dim order, then the block sums
+    combined pairwise, neighbours first; every product and sum rounded to fp32. The number
+    of blocks must be a power of two."""
     X = bf16_to_f32(rows)
-    acc = np.zeros(X.shape[0], dtype=np.float32)
-    for i in range(X.shape[1]):
-        acc = (acc + (u[i] * X[:, i]).astype(np.float32)).astype(np.float32)
-    return acc
+    n, d = X.shape
+    blk = min(SCORE_BLOCK, d)
+    nb = d // blk
+    assert nb * blk == d and nb & (nb - 1) == 0, "d / 8 must be a power of two"
+    sums = []
+    for b in range(nb):
+        acc = np.zeros(n, dtype=np.float32)
+        for i in range(b * blk, (b + 1) * blk):
+            acc = (acc + (u[i] * X[:, i]).astype(np.float32)).astype(np.float32)
+        sums.append(acc)
+    while len(sums) > 1:
+        sums = [(sums[j] + sums[j + 1]).astype(np.float32) for j in range(0, len(sums), 2)]
+    return sums[0]
 
 
 def best_first(score: np.ndarray, ids: np.ndarray, n: int) -> np.ndarray:

@@ -124,13 +124,33 @@ def test_link_prefers_the_nodes_own_lists_then_the_best_places():
 # fp32 scores in a fixed order (A6)
 # ------------------------------------------------------------------------------------------
 
-def test_scores_accumulate_in_dim_order():
+def test_scores_accumulate_a_block_in_dim_order():
     """1 + 2^24 rounds to 2^24 in fp32 (tie to even), so the sum over dims in order of
-    (2^24, 1, -2^24, 1) is 1; any other order or an exact sum gives 2."""
+    (2^24, 1, -2^24, 1) is 1; the reverse order, or an exact sum, gives 2."""
     u = np.ones(4, dtype=np.float32)
     row = bits([[2.0 ** 24, 1.0, -(2.0 ** 24), 1.0]])
     assert ao.scores_f32(u, row).tolist() == [1.0]
     assert ao.scores_f32(u, row[:, ::-1].copy()).tolist() == [2.0]
+
+
+def test_scores_combine_blocks_pairwise():
+    """Four blocks of 8 dims whose sums are (1, 2^24, 1, -2^24): pairwise, (1 + 2^24) rounds
+    to 2^24 and (1 - 2^24) is exact, so the score is 1; a sum of the blocks in order would
+    give 0 (2^24 + 1 rounds back to 2^24), the exact sum is 2."""
+    u = np.ones(32, dtype=np.float32)
+    x = np.zeros(32)
+    x[0], x[8], x[16], x[24] = 1.0, 2.0 ** 24, 1.0, -(2.0 ** 24)
+    assert ao.scores_f32(u, bits([x])).tolist() == [1.0]
+    # 16 blocks (d = 128): the same four sums in blocks 0, 1, 2, 3 meet first in pairs (0,1)
+    # and (2,3), then in the pair of pairs; blocks 4..15 are zero
+    u = np.ones(128, dtype=np.float32)
+    x = np.zeros(128)
+    x[0], x[8], x[16], x[24] = 1.0, 2.0 ** 24, 1.0, -(2.0 ** 24)
+    assert ao.scores_f32(u, bits([x])).tolist() == [1.0]
+    # moved to blocks 0, 2, 1, 3 the pairs are (1, 1) and (2^24, -2^24): exact, 2
+    x = np.zeros(128)
+    x[0], x[16], x[8], x[24] = 1.0, 2.0 ** 24, 1.0, -(2.0 ** 24)
+    assert ao.scores_f32(u, bits([x])).tolist() == [2.0]
 
 
 def test_scores_round_each_product():
