@@ -528,7 +528,8 @@ def tier_leg(w, nds, k_out, v_out, q, idx, dps, dws, out, lse, flush, fracs, res
     layer's 32-row blocks. Per cache size, after a reset: the first call (every retrieved row
     read over the bus), then the median call over the steps after the first quarter (in which
     the cache warms), the share of retrieved rows read from the block cache there, and the
-    bytes that crossed the bus per call (rows read from host memory, blocks copied in)."""
+    bytes that crossed the bus per call (the rows read from host memory: a row read over the
+    bus is written into the cache on the device, not fetched again)."""
     import torch
 
     import kv_vector_index_amd as wi
@@ -562,7 +563,7 @@ def tier_leg(w, nds, k_out, v_out, q, idx, dps, dws, out, lse, flush, fracs, res
         d = {key: c1[key] - c0[key] for key in c1}
         n_t = nds - n_warm
         rows = d["rows_cached"] + d["rows_host"]
-        bus = (d["rows_host"] * 4 * 128 + d["blocks_admitted"] * block_bytes) / n_t
+        bus = d["rows_host"] * 4 * 128 / n_t
         m = statistics.median(ms[n_warm:])
         pts.append({"block_cache_frac": frac, "slots": n_slots,
                     "block_cache_MiB": round(n_slots * block_bytes / 2**20, 1),
@@ -573,8 +574,9 @@ def tier_leg(w, nds, k_out, v_out, q, idx, dps, dws, out, lse, flush, fracs, res
                     "cached_row_share": round(d["rows_cached"] / max(rows, 1), 4),
                     "bus_MB_per_call": round(bus / 1e6, 3),
                     "bus_GBps": round(bus / (m * 1e-3) / 1e9, 1),
-                    "blocks_admitted_per_call": round(d["blocks_admitted"] / n_t, 1),
-                    "blocks_refused_per_call": round(d["blocks_refused"] / n_t, 1)})
+                    "rows_written_per_call": round(d["rows_written"] / n_t, 1),
+                    "slots_claimed_per_call": round(d["blocks_admitted"] / n_t, 1),
+                    "claims_refused_per_call": round(d["blocks_refused"] / n_t, 1)})
         print(f"[bench] tier {frac}: {pts[-1]}", file=sys.stderr, flush=True)
         del tier
     return {"workload": w.name, "timed_steps": nds - n_warm, "points": pts}

@@ -218,13 +218,14 @@ wave_status wave_dense_decode_attention(const wave_decode_params* p, const void*
  * the GPU, exploiting that successive decode steps retrieve largely the same clusters. Here
  * the index (centroids, value sums, sizes, offsets) and the steady zone stay in device
  * memory; the index's layout of the cache (k_out / v_out of the build) lives in pinned host
- * memory; a device cache of n_slots slots holds blocks of 32 consecutive cache rows (K and V,
- * 16 KiB a slot). A decode step selects clusters as wave_decode_attention does, reads each
- * retrieved row from its block's slot when the block is cached and from host memory
- * otherwise, and then copies the blocks it read from host memory into slots that the step
- * did not use (the next slots in a rotating order: a second-chance replacement); blocks that
- * find no such slot stay in host memory. The result is bit-identical to
- * wave_decode_attention on the same rows; only where the rows are read from differs.
+ * memory; a device cache of n_slots slots holds rows of blocks of 32 consecutive cache rows
+ * (K and V, 16 KiB a slot). A decode step selects clusters as wave_decode_attention does and
+ * reads each retrieved row from its block's slot when the slot holds the row, else from host
+ * memory; a row read from host memory is also written into its block's slot (a slot is
+ * claimed for a block that has none: the next slot in a rotating order that the step has not
+ * used, a second-chance replacement; a block that finds none stays in host memory). The
+ * result is bit-identical to wave_decode_attention on the same rows; only where the rows are
+ * read from differs.
  */
 typedef struct {
   const void* host_k;    /* pinned host memory (hipHostMalloc), bf16 [B, Hkv, Lcap, d]: the
@@ -258,10 +259,10 @@ wave_status wave_decode_attention_tiered(const wave_decode_params* p, const void
                                          hipStream_t stream);
 
 /* Totals since the last reset, copied to the host (synchronizes stream): retrieved token rows
- * read from the block cache, read from host memory, blocks copied into the cache, blocks
- * left out for want of a free slot. */
+ * read from the block cache, read from host memory, slots claimed for a block, claims that
+ * found no free slot, rows read from host memory and written into the cache. */
 wave_status wave_tier_counters(const wave_decode_params* p, const wave_tier* tier,
-                               uint64_t counters[4], hipStream_t stream);
+                               uint64_t counters[5], hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Attention-aware vector search: a second retrieval zone
@@ -356,7 +357,7 @@ wave_status wave_anns_decode_attention(const wave_anns_params* p, const void* q,
  * Kernel order, build: key norms (if any indexed token), seeds, then per pass: assign,
  * sort, and (all passes but the last) update; then finalise, steady-row copy (if
  * n_sink + n_recent > 0), objective (if requested). Decode: score, histogram (only when
- * n_clusters > 8192), gather, retrieve (tiered: then fill).
+ * n_clusters > 8192), gather, retrieve (tiered: then step).
  * Dense decode: partial, merge. Vector-search build: lists, zero (if N > 0), count, and
  * if N > 0 scan, scatter, link. Vector-search decode: seed, search, partial, merge.
  */

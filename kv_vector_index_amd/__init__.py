@@ -371,13 +371,14 @@ def wave_decode_attention_tiered(p: wave_decode_params, q, tier: TierTensors,
 
 def wave_tier_counters(p: wave_decode_params, tier: TierTensors, stream=None) -> dict:
     """Totals since the last reset (synchronizes the stream): token rows read from the block
-    cache and from host memory, blocks admitted to and left out of the cache."""
+    cache and from host memory, slots claimed and claims refused, rows written into the
+    cache."""
     t = tier.c_struct()
-    c = (ctypes.c_uint64 * 4)()
+    c = (ctypes.c_uint64 * 5)()
     _check("wave_tier_counters", library().wave_tier_counters(ctypes.byref(p), ctypes.byref(t),
                                                                c, _stream(stream)))
     return {"rows_cached": c[0], "rows_host": c[1], "blocks_admitted": c[2],
-            "blocks_refused": c[3]}
+            "blocks_refused": c[3], "rows_written": c[4]}
 
 
 # ------------------------------------------------------------------------------------

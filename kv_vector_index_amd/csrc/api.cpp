@@ -411,7 +411,6 @@ namespace {
 // Tier state: counters, block table, slot owners and stamps, the request list.
 struct TierShape {
   int64_t nblk, steady_rows;
-  int64_t reqcap;
 };
 wave_status check_tier(const wave_decode_params* p, const DecodeShape& sh, int32_t n_slots,
                        TierShape* ts) {
@@ -419,8 +418,7 @@ wave_status check_tier(const wave_decode_params* p, const DecodeShape& sh, int32
   if (n_slots > (1 << 24)) return WAVE_ERR_UNSUPPORTED;
   ts->nblk = (p->kv_capacity + wave::kTierBlock - 1) / wave::kTierBlock;
   ts->steady_rows = (int64_t)p->n_sink + p->n_recent + (p->kv_capacity - p->index_len);
-  ts->reqcap = sh.BH * ts->nblk;
-  if (ts->reqcap > INT32_MAX) return WAVE_ERR_UNSUPPORTED;
+  if (sh.BH * ts->nblk >= INT32_MAX) return WAVE_ERR_UNSUPPORTED;   // (block ids are int32)
   return WAVE_OK;
 }
 size_t layout_tier(const DecodeShape& sh, const TierShape& ts, int32_t n_slots, void* base,
@@ -428,18 +426,15 @@ size_t layout_tier(const DecodeShape& sh, const TierShape& ts, int32_t n_slots, 
   Carver cv(base);
   uint32_t* tctr = cv.take<uint32_t>(wave::kTcWords);
   int32_t* tab = cv.take<int32_t>((size_t)sh.BH * ts.nblk);
-  int32_t* owner = cv.take<int32_t>((size_t)n_slots);
-  int32_t* stamp = cv.take<int32_t>((size_t)n_slots);
-  int32_t* req = cv.take<int32_t>((size_t)ts.reqcap);
+  uint64_t* slotw = cv.take<uint64_t>((size_t)n_slots);
+  uint32_t* valid = cv.take<uint32_t>((size_t)n_slots);
   if (a) {
     a->tctr = tctr;
     a->tab = tab;
-    a->owner = owner;
-    a->stamp = stamp;
-    a->req = req;
+    a->slotw = slotw;
+    a->valid = valid;
     a->nslots = n_slots;
     a->nblk = (int)ts.nblk;
-    a->reqcap = (int)ts.reqcap;
     a->Ls = ts.steady_rows;
   }
   return cv.off;
@@ -604,7 +599,7 @@ wave_status wave_decode_attention_tiered(const wave_decode_params* p, const void
 }
 
 wave_status wave_tier_counters(const wave_decode_params* p, const wave_tier* tier,
-                               uint64_t counters[4], hipStream_t stream) {
+                               uint64_t counters[5], hipStream_t stream) {
   DecodeShape sh;
   wave_status st = check_decode(p, &sh);
   if (st != WAVE_OK) return st;
@@ -615,6 +610,7 @@ wave_status wave_tier_counters(const wave_decode_params* p, const wave_tier* tie
   counters[1] = c[wave::kTcRowsHost];
   counters[2] = c[wave::kTcAdmitted];
   counters[3] = c[wave::kTcRefused];
+  counters[4] = c[wave::kTcRowsWritten];
   return WAVE_OK;
 }
 

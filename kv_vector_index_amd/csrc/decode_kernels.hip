@@ -1769,21 +1769,81 @@ struct MfmaState {
 // removal row, which the build always writes: the padding's zero weights meet finite values in
 // the products, never an unwritten cache slot whose contents could be NaN).
 //
-// TIER: a token row's source is its block's cache slot, src = slot * kTierBlock + row %
-// kTierBlock, when the block is cached (the slot is stamped with the step), else the row in
-// host memory, src = kHostRow | row (the block is requested for the fill kernel, once: the
-// table entry goes from -1 to -2). Returns 1 for a token row read from the cache, 2 for one
-// read from host memory, else 0.
+// TIER (the cache in host memory): a token row is read from its block's slot when the slot
+// holds the block, is pinned for this step and has the row (src = slot * kTierBlock + row %
+// kTierBlock); else from host memory (src = kHostRow | row), and when the block has a slot
+// (pinned, or claimed in this step), the row read over the bus is also written into it (dst =
+// slot * 2 kTierBlock + row % kTierBlock, the K row; -1: not written). A slot word holds the
+// owner block (low half) and 2 step + claimed (high half): pinning moves a slot of the block
+// to this step by compare-and-swap, and a claim takes a slot that nothing of this step pinned
+// or claimed, so no slot changes hands while a step reads it. The first row of each run of
+// rows of one block pins or claims for the run (t_blk, t_res in LDS), the other rows use its
+// result. Rows written in a step are read from the next step on (each row is retrieved once
+// a step); a slot claimed in this step is not read at all in it. Returns 1 for a row read
+// from a slot, 2 from host memory, 3 from host memory and written into a slot, else 0.
 constexpr int32_t kHostRow = 1 << 30;
+
+// Pin slot e for block id in this step: 1 if the slot holds the block and was not claimed in
+// this step (it is then stamped with the step: readable and writable), 2 if it was claimed in
+// this step for the block (writable only), 0 if it holds another block.
+__device__ __forceinline__ int tier_pin(const DecodeArgs& a, int e, int32_t id, uint32_t step) {
+  const uint64_t mine = ((uint64_t)(2u * step) << 32) | (uint32_t)id;
+  uint64_t w = ld_dev(a.slotw + e);
+  for (int tries = 0; tries < 4; ++tries) {
+    if ((uint32_t)w != (uint32_t)id) return 0;                // another block holds it now
+    const uint32_t hs = (uint32_t)(w >> 32);
+    if (hs == 2u * step + 1u) return 2;                       // claimed in this step
+    if (hs == 2u * step) return 1;                            // pinned in this step already
+    const uint64_t old = atomicCAS(reinterpret_cast<unsigned long long*>(a.slotw + e),
+                                   (unsigned long long)w, (unsigned long long)mine);
+    if (old == w) return 1;
+    w = old;
+  }
+  return 0;
+}
+
+// Claim a slot for block id in this step (the table entry is -2, held by this thread): the
+// next slot in the hand's order that nothing of this step pinned or claimed; the hand goes
+// round at most once per step. The old block leaves the table, the slot holds no row yet, and
+// the table points to the slot. Returns the slot, or -1 (the table entry goes back to -1).
+__device__ __forceinline__ int tier_claim(const DecodeArgs& a, int32_t id, uint32_t step) {
+  const uint32_t h0 = ld_dev(a.tctr + kTcHandStart);
+  const int32_t nid = a.B * a.Hkv * a.nblk;
+  const uint64_t want = ((uint64_t)(2u * step + 1u) << 32) | (uint32_t)id;
+  for (;;) {
+    const uint32_t h = atomicAdd(a.tctr + kTcHand, 1u);
+    if (h - h0 >= (uint32_t)a.nslots) break;                  // the revolution is over
+    const int s = (int)(h % (uint32_t)a.nslots);
+    const uint64_t w = ld_dev(a.slotw + s);
+    if ((uint32_t)(w >> 32) >= 2u * step) continue;          // pinned or claimed this step
+    if (atomicCAS(reinterpret_cast<unsigned long long*>(a.slotw + s), (unsigned long long)w,
+                  (unsigned long long)want) != w)
+      continue;
+    const int32_t prev = (int32_t)(uint32_t)w;
+    if (prev >= 0 && prev < nid) atomicCAS(a.tab + prev, s, -1);
+    // (a row of the block that another workgroup marks in the mask before this reset is
+    // written but not marked: it is only not reused)
+    atomicExch(a.valid + s, 0u);
+    atomicExch(a.tab + id, s);
+    atomicAdd(a.tctr + kTcAdmitted, 1u);
+    return s;
+  }
+  atomicExch(a.tab + id, -1);
+  atomicAdd(a.tctr + kTcRefused, 1u);
+  return -1;
+}
+
 template <bool TIER>
 __device__ __forceinline__ int describe_rows(const DecodeArgs& a, int bh, int c0, int n,
                                              const int32_t* l_ts, const int32_t* l_co,
                                              const int32_t* l_id, int cnt, int32_t* d_src,
-                                             float* d_wgt) {
+                                             float* d_wgt, int32_t* d_dst, int32_t* t_blk,
+                                             int32_t* t_res) {
   const int tid = threadIdx.x, t = c0 + tid;
-  int32_t src = -1;
+  int32_t src = -1, dst = -1;
   float wgt = 0.f;
   int cls = 0;
+  bool token = false;
   if (tid < n) {
     int lo = 0, hi = cnt - 1;
     while (lo < hi) {
@@ -1794,30 +1854,58 @@ __device__ __forceinline__ int describe_rows(const DecodeArgs& a, int bh, int c0
     if (off < nj) {
       src = l_co[lo] + off;
       wgt = 1.f;
-      if constexpr (TIER) {
-        const int32_t id = bh * a.nblk + src / kTierBlock;
-        int32_t e = a.tab[id];
-        if (e >= a.nslots) e = -3;  // (never set by the fill: a state not reset; not cached)
-        // (one thread per block and cluster run does the block's bookkeeping)
-        const bool lead = (src % kTierBlock) == 0 || off == 0 || tid == 0;
-        if (e >= 0) {
-          if (lead) a.stamp[e] = (int32_t)a.tctr[kTcStep];
-          src = e * kTierBlock + src % kTierBlock;
-          cls = 1;
-        } else {
-          if (lead && e == -1 && atomicCAS(a.tab + id, -1, -2) == -1) {
-            const uint32_t r = atomicAdd(a.tctr + kTcReq, 1u);
-            if (r < (uint32_t)a.reqcap) a.req[r] = id;
-            else atomicExch(a.tab + id, -1);  // (the request list is full: no fill)
-          }
-          src = kHostRow | src;
-          cls = 2;
-        }
-      }
+      token = true;
     } else {
       src = -1 - l_id[lo];
       wgt = -(float)nj;
     }
+  }
+  if constexpr (TIER) {
+    // the rows of one block are consecutive among the token rows (clusters are contiguous
+    // runs of the cache, listed in ascending order; one removal row follows each cluster)
+    const int32_t id = token ? bh * a.nblk + src / kTierBlock : -1;
+    t_blk[tid] = id;
+    t_res[tid] = INT32_MIN;   // (not the first row of a run; a run's first row overwrites it)
+    __syncthreads();
+    int j = tid - 1;
+    if (j >= 0 && t_blk[j] < 0) --j;
+    const bool lead = token && (j < 0 || t_blk[j] != id);
+    const uint32_t step = ld_dev(a.tctr + kTcStep);
+    if (lead) {   // slot and state for the run: (slot << 2) | 1 readable, 2 claimed here, 0 none
+      int32_t e = ld_dev(a.tab + id);
+      if (e >= a.nslots) e = -3;  // (never set by a claim: a state not reset; not cached)
+      int32_t res = 0;
+      if (e >= 0) {
+        const int pin = tier_pin(a, e, id, step);
+        if (pin != 0) res = (e << 2) | pin;
+      } else if (e == -1 && atomicCAS(a.tab + id, -1, -2) == -1) {
+        const int sl = tier_claim(a, id, step);
+        if (sl >= 0) res = (sl << 2) | 2;
+      }
+      t_res[tid] = res;
+    }
+    __syncthreads();
+    if (token) {
+      // the run's first row: the nearest row at or before this one that carries a result
+      // (between them lie only rows of this block and removal rows)
+      int k = tid;
+      while (t_res[k] == INT32_MIN) --k;
+      const int32_t res = t_res[k];
+      const int e = res >> 2, pin = res & 3, r = src % kTierBlock;
+      const uint32_t bit = 1u << r;
+      if (pin == 1 && (ld_dev(a.valid + e) & bit)) {
+        src = e * kTierBlock + r;
+        cls = 1;
+      } else {
+        if (pin != 0) {
+          atomicOr(a.valid + e, bit);
+          dst = e * 2 * kTierBlock + r;
+        }
+        src = kHostRow | src;
+        cls = pin != 0 ? 3 : 2;
+      }
+    }
+    d_dst[tid] = dst;
   }
   d_src[tid] = src;
   d_wgt[tid] = wgt;
@@ -1839,7 +1927,8 @@ template <int G, bool TIER>
 __device__ __forceinline__ void attend_rows_mfma(const DecodeArgs& a, int bh,
                                                  const bf16x8 (&qb)[4], MfmaState& st,
                                                  int nrows, const int32_t* d_src,
-                                                 const float* d_wgt, RetWave<G>& W) {
+                                                 const float* d_wgt, const int32_t* d_dst,
+                                                 RetWave<G>& W) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
   typedef __attribute__((ext_vector_type(4))) float floatx4;
   typedef __attribute__((ext_vector_type(4))) short shortx4;
@@ -1861,6 +1950,14 @@ __device__ __forceinline__ void attend_rows_mfma(const DecodeArgs& a, int bh,
         kp = src >= 0 ? a.k + (kb + src) * kHeadDim : a.cmean + (cb + (-1 - src)) * kHeadDim;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) ka[tau][s4] = ld16_stream(kp + s4 * 32 + g * 8);
+      if constexpr (TIER) {   // a row read over the bus goes into its slot as well
+        const int32_t dst = d_dst[r0 + 8 * (n >> 2) + 4 * tau + (n & 3)];
+        if (dst >= 0) {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+            st16(a.cache + (size_t)dst * kHeadDim + s4 * 32 + g * 8, ka[tau][s4]);
+        }
+      }
     }
     // ---- value rows (or value sums) into LDS
     {
@@ -1879,7 +1976,10 @@ __device__ __forceinline__ void attend_rows_mfma(const DecodeArgs& a, int bh,
           // written where the direct load would put them (a direct load is issued by all lanes
           // or by none)
           if (__ballot(host)) {
-            *reinterpret_cast<u32x4*>(&W.vrows[e][4 * lane]) = ld16_stream(vp + cidx * 8);
+            const u32x4 v = ld16_stream(vp + cidx * 8);
+            *reinterpret_cast<u32x4*>(&W.vrows[e][4 * lane]) = v;
+            const int32_t dst = d_dst[r0 + 8 * slot + e];
+            if (dst >= 0) st16(a.cache + ((size_t)dst + kTierBlock) * kHeadDim + cidx * 8, v);
           } else {
             __builtin_amdgcn_global_load_lds(vp + cidx * 8, (lds_ptr)&W.vrows[e][0], 16, 0, 0);
           }
@@ -2042,6 +2142,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
   __shared__ int32_t l_ts[kWinR + 1], l_co[kWinR], l_id[kWinR];
   __shared__ int32_t d_src[kDecThreads];  // the current rows' descriptors (describe_rows)
   __shared__ __align__(16) float d_wgt[kDecThreads];
+  __shared__ int32_t d_dst[TIER ? kDecThreads : 1];
+  __shared__ int32_t t_blk[TIER ? kDecThreads : 1], t_res[TIER ? kDecThreads : 1];
   __shared__ RetLds<G> lds;
   const int bh = blockIdx.y, b = bh / a.Hkv, g = bh % a.Hkv, w_item = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -2132,17 +2234,21 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
     const int ts = max(T0, l_ts[0]), te = min(T1, l_ts[cnt]);
     for (int c0 = ts; c0 < te; c0 += kDecThreads) {
       const int nr = min(kDecThreads, te - c0);
-      const int cls = describe_rows<TIER>(a, bh, c0, nr, l_ts, l_co, l_id, cnt, d_src, d_wgt);
+      const int cls =
+          describe_rows<TIER>(a, bh, c0, nr, l_ts, l_co, l_id, cnt, d_src, d_wgt, d_dst, t_blk,
+                              t_res);
       if constexpr (TIER) {
-        const int nc = __syncthreads_count(cls == 1), nh = __syncthreads_count(cls == 2);
+        const int nc = __syncthreads_count(cls == 1), nh = __syncthreads_count(cls >= 2),
+                  nw = __syncthreads_count(cls == 3);
         if (tid == 0) {
           if (nc) atomicAdd(a.tctr + kTcRowsCached, (uint32_t)nc);
           if (nh) atomicAdd(a.tctr + kTcRowsHost, (uint32_t)nh);
+          if (nw) atomicAdd(a.tctr + kTcRowsWritten, (uint32_t)nw);
         }
       } else {
         __syncthreads();
       }
-      attend_rows_mfma<G, TIER>(a, bh, qb, st, nr, d_src, d_wgt, lds.w[wave]);
+      attend_rows_mfma<G, TIER>(a, bh, qb, st, nr, d_src, d_wgt, d_dst, lds.w[wave]);
       __syncthreads();
     }
     __syncthreads();
@@ -2234,87 +2340,26 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
 }
 
 // ------------------------------------------------------------------------------------
-// host-memory tier: fill and reset
+// host-memory tier: step and reset
 // ------------------------------------------------------------------------------------
-// After the retrieve of a step: kFillWG workgroups take the blocks it requested (blocks of
-// retrieved rows it read from host memory) in turn. A block gets the next slot in the hand's
-// order that nothing of this step used (stamp below the step; claimed by a compare-and-swap of
-// the stamp, so that no two blocks take one slot): the slot's old block leaves the table, the
-// new block's K and V rows come from host memory, and then the table points to the slot. The
-// hand makes one revolution per step at most: a stamp never falls within a step, so once every
-// slot has been tried none is left, and the remaining blocks stay uncached at the cost of one
-// atomic each. The last workgroup to finish clears the request count, notes where the hand
-// stopped and moves to the next step.
-__global__ __launch_bounds__(kDecThreads) void k_tier_fill(DecodeArgs a) {
-  __shared__ int32_t s_slot;
-  const int tid = threadIdx.x;
-  const int32_t step = (int32_t)a.tctr[kTcStep];
-  const uint32_t nreq = min(a.tctr[kTcReq], (uint32_t)a.reqcap);
-  const uint32_t h0 = a.tctr[kTcHandStart];
-  const int32_t nid = (a.B * a.Hkv) * a.nblk;
-  for (uint32_t i = blockIdx.x; i < nreq; i += gridDim.x) {
-    const int32_t id = a.req[i];
-    if (id < 0 || id >= nid) continue;  // (only from a state that was not reset)
-    if (tid == 0) {
-      int32_t got = -1;
-      while (got < 0) {
-        const uint32_t h = atomicAdd(a.tctr + kTcHand, 1u);
-        if (h - h0 >= (uint32_t)a.nslots) break;  // (the revolution is over: no slot left)
-        const int32_t sl = (int32_t)(h % (uint32_t)a.nslots);
-        const int32_t old = ld_dev(a.stamp + sl);
-        if (old < step && atomicCAS(a.stamp + sl, old, step) == old) got = sl;
-      }
-      s_slot = got;
-    }
-    __syncthreads();
-    const int32_t sl = s_slot;
-    __syncthreads();
-    if (sl < 0) {
-      if (tid == 0) {
-        a.tab[id] = -1;
-        atomicAdd(a.tctr + kTcRefused, 1u);
-      }
-      continue;
-    }
-    if (tid == 0) {
-      const int32_t prev = a.owner[sl];
-      if (prev >= 0 && prev < nid) a.tab[prev] = -1;
-      a.owner[sl] = id;
-    }
-    // 2 kTierBlock rows of 256 bytes (K, then V): 16-byte chunks, four per thread
-    const int bh = id / a.nblk, blk = id % a.nblk;
-    const size_t r0 = (size_t)bh * a.Lcap + (size_t)blk * kTierBlock;
-    uint16_t* dst = a.cache + (size_t)sl * 2 * kTierBlock * kHeadDim;
-    for (int c = tid; c < 2 * kTierBlock * 16; c += kDecThreads) {
-      const int half = c / (kTierBlock * 16), r = (c >> 4) % kTierBlock, ch = c & 15;
-      if ((int64_t)blk * kTierBlock + r < a.Lcap) {
-        const uint16_t* src = (half ? a.hv : a.hk) + (r0 + r) * kHeadDim + ch * 8;
-        st16(dst + ((size_t)half * kTierBlock + r) * kHeadDim + ch * 8, ld16_stream(src));
-      }
-    }
-    // (the next step's retrieve, a later launch, reads the table and the rows)
-    if (tid == 0) {
-      a.tab[id] = sl;
-      atomicAdd(a.tctr + kTcAdmitted, 1u);
-    }
-  }
-  if (arrive_last(a.tctr + kTcFillDone, gridDim.x) && tid == 0) {
-    a.tctr[kTcReq] = 0u;
-    a.tctr[kTcFillDone] = 0u;
+// After the retrieve of a step: the next step begins, and the hand's position is noted (a
+// step's claims go round the slots once at most).
+__global__ void k_tier_step(DecodeArgs a) {
+  if (threadIdx.x == 0) {
     a.tctr[kTcHandStart] = ld_dev(a.tctr + kTcHand);
-    a.tctr[kTcStep] = (uint32_t)step + 1u;
+    a.tctr[kTcStep] = ld_dev(a.tctr + kTcStep) + 1u;
   }
 }
 
-// Empty cache: no block cached or requested, no slot owned or stamped, step 1.
+// Empty cache: no block cached, no slot owned (owner -1, step 0), step 1, counters zero.
 __global__ __launch_bounds__(kDecThreads) void k_tier_reset(DecodeArgs a) {
   const size_t i0 = (size_t)blockIdx.x * kDecThreads + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * kDecThreads;
   const size_t ntab = (size_t)a.B * a.Hkv * a.nblk;
   for (size_t i = i0; i < ntab; i += stride) a.tab[i] = -1;
   for (size_t i = i0; i < (size_t)a.nslots; i += stride) {
-    a.owner[i] = -1;
-    a.stamp[i] = -1;
+    a.slotw[i] = 0xffffffffull;
+    a.valid[i] = 0u;
   }
   if (i0 < (size_t)kTcWords) a.tctr[i0] = i0 == (size_t)kTcStep ? 1u : 0u;
 }
@@ -2396,7 +2441,7 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr
             ? launch(tr, k_dec_retrieve<G, true, true>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a)
             : launch(tr, k_dec_retrieve<G, false, true>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);
     if (e != hipSuccess) return e;
-    return launch(tr, k_tier_fill, dim3(kFillWG), dim3(kDecThreads), 0, s, a);
+    return launch(tr, k_tier_step, dim3(1), dim3(64), 0, s, a);
   }
   if (a.nB * BH <= 3 * kCUs)
     return launch(tr, k_dec_retrieve<G, true, false>, dim3(a.nB, BH), dim3(kDecThreads), 0, s, a);

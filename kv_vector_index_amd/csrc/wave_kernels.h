@@ -95,8 +95,8 @@ struct DecodeArgs {
   // host-memory tier (tier != 0): the cache's rows live in host memory (hk, hv, the same
   // layout as k, v), the steady zone in a compact device buffer (sk, sv: [BH, Ls, d], rows
   // [0, n_sink) then [L0 - n_recent, Lcap)), and a device block cache of nslots slots of
-  // kTierBlock K rows then kTierBlock V rows holds recently retrieved blocks of kTierBlock
-  // consecutive cache rows
+  // kTierBlock K rows then kTierBlock V rows holds rows of recently retrieved blocks of
+  // kTierBlock consecutive cache rows
   int tier;
   const uint16_t* hk;
   const uint16_t* hv;
@@ -104,12 +104,12 @@ struct DecodeArgs {
   const uint16_t* sv;
   int64_t Ls;
   uint16_t* cache;         // [nslots, 2, kTierBlock, d]
-  int32_t* tab;            // [BH, nblk] slot of each block, -1 none, -2 requested this step
-  int32_t* owner;          // [nslots] block (bh * nblk + block) held, -1 none
-  int32_t* stamp;          // [nslots] last step that read the slot or filled it
+  int32_t* tab;            // [BH, nblk] slot of each block, -1 none, -2 being claimed
+  uint64_t* slotw;         // [nslots] owner block (bh * nblk + block; low half, -1 none) and
+                           //   2 * (last step that pinned or claimed it) + claimed (high half)
+  uint32_t* valid;         // [nslots] rows of the owner block held (bit r: row r of the block)
   uint32_t* tctr;          // kTc* counters
-  int32_t* req;            // [reqcap] blocks requested this step
-  int nslots, nblk, reqcap;
+  int nslots, nblk;
   // attention over the steady zone and listed rows (the vector-search retrieval zone):
   // rows_pos [BH, rows_k] cache rows (-1 padded after rows_n[bh] entries)
   const int32_t* rows_pos;
@@ -121,18 +121,16 @@ struct DecodeArgs {
 constexpr int kTierBlock = 32;        // cache rows per block (one slot)
 constexpr int kTcStep = 0;            // the current step (from 1; stamps below it are older)
 constexpr int kTcHand = 1;            // replacement hand (slots are tried in its order)
-constexpr int kTcReq = 2;             // blocks requested this step
-constexpr int kTcFillDone = 3;        // fill workgroups finished this step
+constexpr int kTcRowsWritten = 2;     // rows read over the bus and written into a slot (total)
 constexpr int kTcRowsCached = 4;      // retrieved token rows read from the block cache (total)
 constexpr int kTcRowsHost = 5;        // retrieved token rows read from host memory (total)
-constexpr int kTcAdmitted = 6;        // blocks copied into the cache (total)
-constexpr int kTcRefused = 7;         // requested blocks left out: no free slot (total)
-constexpr int kTcHandStart = 8;       // the hand when this step's fill began
+constexpr int kTcAdmitted = 6;        // slots claimed for a block (total)
+constexpr int kTcRefused = 7;         // claims that found no slot (total)
+constexpr int kTcHandStart = 8;       // the hand when this step began
 constexpr int kTcWords = 16;
-constexpr int kFillWG = 256;          // fill kernel workgroups
 
 // Enqueue one tripartite decode step (score, histogram for large heads, gather, retrieve
-// kernels; with the host-memory tier, then the fill kernel). Returns the first launch error.
+// kernels; with the host-memory tier, then the step kernel). Returns the first launch error.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, Tracer* tr);
 // Empty the host-memory tier's block cache (table, owners, stamps, counters).
 hipError_t launch_tier_reset(const DecodeArgs& a, hipStream_t stream);

@@ -220,7 +220,7 @@ def test_tier_validates_before_any_launch():
     assert call(ctypes.byref(p), Q, ctypes.byref(t), ctypes.byref(idx), OUT, None, None, WS,
                 ws - 256, None) == 3
     assert lib.wave_tier_reset(ctypes.byref(p), None, None) == 1
-    c = (ctypes.c_uint64 * 4)()
+    c = (ctypes.c_uint64 * 5)()
     assert lib.wave_tier_counters(ctypes.byref(p), None, c, None) == 1
 
 

@@ -1,8 +1,9 @@
 """Host-memory tier (the wave buffer of RetroInfer: gist.science de section 2B "Wave Buffer"):
 the cache in pinned host memory behind a device block cache. Every tiered decode step must
 give the same out, lse and selection as wave_decode_attention on the same rows, bit for bit,
-whatever the cache holds; the block cache must hold exactly the host rows of the blocks its
-table names; and the row counters must add up to the retrieved rows."""
+whatever the cache holds; every row a slot marks as held must equal the host row of the block
+its owner names, and the table and the owners must agree; and the row counters must add up
+to the retrieved rows."""
 import numpy as np
 import pytest
 
@@ -17,17 +18,18 @@ TC_WORDS = 16
 
 
 def tier_views(layer, p, n_slots, state):
-    """(counters, table, owners, stamps) views of the tier state."""
+    """(counters, table, slot owners, slot steps, slot row masks) of the tier state."""
     t = tl.torch()
     BH = layer.B * layer.H
     nblk = -(-layer.Lcap // wi.TIER_BLOCK)
     up = lambda x: -(-x // ALIGN) * ALIGN  # noqa: E731
     o_tab = up(4 * TC_WORDS)
-    o_own = o_tab + up(4 * BH * nblk)
-    o_stamp = o_own + up(4 * n_slots)
+    o_word = o_tab + up(4 * BH * nblk)
+    o_valid = o_word + up(8 * n_slots)
     i32 = state.view(t.int32)
+    words = state[o_word:o_word + 8 * n_slots].view(t.int32).view(n_slots, 2)
     return (i32[:TC_WORDS], i32[o_tab // 4:o_tab // 4 + BH * nblk].view(BH, nblk),
-            i32[o_own // 4:o_own // 4 + n_slots], i32[o_stamp // 4:o_stamp // 4 + n_slots])
+            words[:, 0], words[:, 1], i32[o_valid // 4:o_valid // 4 + n_slots])
 
 
 def make_tier(layer, p, n_slots):
@@ -49,28 +51,33 @@ def make_tier(layer, p, n_slots):
 
 
 def check_cache_contents(layer, p, tier):
-    """Every block the table names: the slot's K and V rows are the host rows; owners and the
-    table agree."""
+    """Every block the table names: its slot's owner is the block, and every row the slot
+    marks as held equals the host row (K and V); every owned slot's block points back.
+    Returns (blocks cached, rows held)."""
     t = tl.torch()
-    ctr, tab, owner, stamp = tier_views(layer, p, tier.n_slots, tier.state)
+    ctr, tab, owner, step, valid = tier_views(layer, p, tier.n_slots, tier.state)
     tab, owner = tab.cpu().numpy(), owner.cpu().numpy()
-    assert (tab >= -1).all(), "a block left requested after a step"
+    valid = valid.cpu().numpy().view(np.uint32)
+    assert (tab >= -1).all(), "a block left being claimed after a step"
     cache = tier.cache.view(t.bfloat16).view(tier.n_slots, 2, wi.TIER_BLOCK, 128).cpu()
     hk = tier.host_k.view(layer.B * layer.H, layer.Lcap, 128)
     hv = tier.host_v.view(layer.B * layer.H, layer.Lcap, 128)
     nblk = tab.shape[1]
-    n_cached = 0
+    n_cached = n_rows = 0
     for bh, b in zip(*np.nonzero(tab >= 0)):
         s = int(tab[bh, b])
         assert owner[s] == bh * nblk + b, (bh, b, s, owner[s])
-        r0, r1 = b * wi.TIER_BLOCK, min((b + 1) * wi.TIER_BLOCK, layer.Lcap)
-        assert t.equal(cache[s, 0, :r1 - r0], hk[bh, r0:r1]), (bh, b)
-        assert t.equal(cache[s, 1, :r1 - r0], hv[bh, r0:r1]), (bh, b)
+        rows = [r for r in range(wi.TIER_BLOCK) if (int(valid[s]) >> r) & 1]
+        assert all(b * wi.TIER_BLOCK + r < layer.Lcap for r in rows), (bh, b)
+        for r in rows:
+            assert t.equal(cache[s, 0, r], hk[bh, b * wi.TIER_BLOCK + r]), (bh, b, r)
+            assert t.equal(cache[s, 1, r], hv[bh, b * wi.TIER_BLOCK + r]), (bh, b, r)
         n_cached += 1
+        n_rows += len(rows)
     for s in np.nonzero(owner >= 0)[0]:
         bh, b = divmod(int(owner[s]), nblk)
         assert tab[bh, b] == s, "an owner whose block does not point back"
-    return n_cached
+    return n_cached, n_rows
 
 
 def retrieved_rows(idx, sel):
@@ -120,14 +127,16 @@ def test_tiered_steps_equal_the_resident_steps(layer4k, n_slots):
         assert np.array_equal(sel.cpu().numpy(), sel_r), f"step {s}: selection"
         assert np.array_equal(out.cpu().numpy(), out_r), f"step {s}: out"
         assert np.array_equal(lse.cpu().numpy(), lse_r), f"step {s}: lse"
-        n_cached = check_cache_contents(layer, p, tier)
+        n_cached, n_rows = check_cache_contents(layer, p, tier)
         assert n_cached <= n_slots
         total_rows += retrieved_rows(idx, sel_r)
     c = wi.wave_tier_counters(p_last, tier)
     assert c["rows_cached"] + c["rows_host"] == total_rows, (c, total_rows)
-    if n_slots >= 4096:       # every block fits: each is read from host memory once at most
+    assert 0 < c["rows_written"] <= c["rows_host"], c
+    if n_slots >= 4096:       # every block fits: no claim is refused and rows are reused
         assert c["blocks_refused"] == 0
         assert c["rows_cached"] > 0
+        assert n_rows <= c["rows_written"]
     if n_slots == 3:
         assert c["blocks_refused"] > 0
 
