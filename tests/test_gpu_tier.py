@@ -161,3 +161,47 @@ def test_tier_reset_empties_the_cache(layer4k):
     out_r, _, sel_r = layer.decode(idx, x.q[0], L, n_r)
     assert np.array_equal(out.cpu().numpy(), out_r)
     assert c["rows_cached"] == 0 and c["rows_host"] == retrieved_rows(idx, sel_r), c
+
+
+TIER_EDGE = {
+    # name: (B, H, Hq, L0, steps, S, kseg, n_sink, n_recent, n_r, n_slots)
+    "g7_batch2_partial_last_block": (2, 2, 14, 1500, 4, 512, 32, 3, 17, 9, 16),
+    "mha": (1, 4, 4, 1200, 3, 256, 24, 4, 20, 7, 12),
+    "no_steady_zone": (1, 2, 8, 1024, 3, 256, 16, 0, 0, 6, 8),
+    "one_slot": (1, 2, 8, 900, 4, 300, 20, 2, 11, 5, 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TIER_EDGE))
+def test_tier_shapes_and_edge_cases(name):
+    """Other shapes through the tier: seven query heads per KV head at batch 2 with a partly
+    filled last block, MHA, no steady zone, a single slot; every step bit for bit equal to the
+    resident decode, the cache's rows checked after every step."""
+    import zlib
+    B, H, Hq, L0, steps, S, kseg, ns, nr, n_r, n_slots = TIER_EDGE[name]
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    print(f"[tier] edge case {name}", flush=True)
+    layer, q = tl.ragged_layer(rng, B=B, H=H, Hq=Hq, L0=L0, steps=steps, S=S, kseg=kseg,
+                               n_sink=ns, n_recent=nr)
+    idx = layer.build()
+    t = tl.torch()
+    p_last = layer.decode_params(layer.L0 + steps, n_r)
+    tier = make_tier(layer, p_last, n_slots)
+    ws = wi.alloc_decode_workspace(p_last)
+    total = 0
+    for s in range(steps):
+        L = layer.L0 + s + 1
+        p = layer.decode_params(L, n_r)
+        out_r, lse_r, sel_r = layer.decode(idx, q[s], L, n_r)
+        out = t.empty(layer.B, layer.Hq, 128, dtype=t.float32, device="cuda")
+        lse = t.empty(layer.B, layer.Hq, dtype=t.float32, device="cuda")
+        sel = t.full((layer.B, layer.H, n_r), -7, dtype=t.int32, device="cuda")
+        wi.wave_decode_attention_tiered(p, tl.to_dev(q[s]), tier, idx, out, lse, sel, ws)
+        t.cuda.synchronize()
+        assert np.array_equal(sel.cpu().numpy(), sel_r), (name, s)
+        assert np.array_equal(out.cpu().numpy(), out_r), (name, s)
+        assert np.array_equal(lse.cpu().numpy(), lse_r), (name, s)
+        check_cache_contents(layer, p, tier)
+        total += retrieved_rows(idx, sel_r)
+    c = wi.wave_tier_counters(p_last, tier)
+    assert c["rows_cached"] + c["rows_host"] == total, (name, c, total)
