@@ -411,6 +411,21 @@ __device__ __forceinline__ int count_better_sorted(const float* es, const int32_
   return lo;
 }
 
+// The entries among (es, ei)[0, n) (in any order) better than (s, id): four per LDS read.
+__device__ __forceinline__ int count_better_all(const float* es, const int32_t* ei, int n,
+                                                float s, int id) {
+  int cnt = 0, c = 0;
+#pragma unroll 4
+  for (; c + 4 <= n; c += 4) {
+    const float4 s4 = *reinterpret_cast<const float4*>(es + c);
+    const int4 i4 = *reinterpret_cast<const int4*>(ei + c);
+    cnt += (int)better(s4.x, i4.x, s, id) + (int)better(s4.y, i4.y, s, id) +
+           (int)better(s4.z, i4.z, s, id) + (int)better(s4.w, i4.w, s, id);
+  }
+  for (; c < n; ++c) cnt += (int)better(es[c], ei[c], s, id);
+  return cnt;
+}
+
 // The entries of (es, ei)[0, n), made of sorted runs of `run` entries, better than (s, id),
 // leaving out the run that starts at `skip` (none when skip < 0).
 __device__ __forceinline__ int count_better_runs(const float* es, const int32_t* ei, int n,
@@ -537,13 +552,52 @@ __global__ __launch_bounds__(kAnnsSearchThreads) void k_anns_search(AnnsArgs a) 
     // merged into the pool by rank (a pool entry moves down by the new nodes better than it;
     // a new node lands after the pool entries and the new nodes better than it); the pool
     // keeps its ef best
-    const int nc = ctr[kCtrCand];
-    if (nc > 0) {
-      score_rows<kAnnsSearchThreads, 4>(uj, kb, ci, cs, nc, a.graph + (size_t)bh * N * a.R,
+    const int nv = ctr[kCtrCand];   // nodes scored this round
+    int nc = nv;
+    if (nv > 0) {
+      score_rows<kAnnsSearchThreads, 4>(uj, kb, ci, cs, nv, a.graph + (size_t)bh * N * a.R,
                                         a.R, &sink);
       __syncthreads();
-      for (int c0 = 64 * (tid >> 6); c0 < nc; c0 += kAnnsSearchThreads) wave_sort64(cs, ci, c0, nc);
-      __syncthreads();
+      if (psize == a.ef) {
+        // a full pool keeps only nodes better than its last entry: the others are dropped
+        // before the sort (they stay visited)
+        const float ws = pS[cur][a.ef - 1];
+        const int wid = pI[cur][a.ef - 1] & INT_MAX;
+        float v0 = kNegInf, v1 = kNegInf;
+        int i0 = 0, i1 = 0;
+        uint32_t f0 = 0, f1 = 0;
+        if (tid < nv) {
+          v0 = cs[tid];
+          i0 = ci[tid];
+          f0 = better(v0, i0, ws, wid) ? 1u : 0u;
+        }
+        if (tid + kAnnsSearchThreads < nv) {
+          v1 = cs[tid + kAnnsSearchThreads];
+          i1 = ci[tid + kAnnsSearchThreads];
+          f1 = better(v1, i1, ws, wid) ? 1u : 0u;
+        }
+        uint32_t total;
+        const uint32_t at = scan_excl<kAnnsSearchThreads>(f0 + f1, scan, &total);
+        if (f0) {
+          cs[at] = v0;
+          ci[at] = i0;
+        }
+        if (f1) {
+          cs[at + f0] = v1;
+          ci[at + f0] = i1;
+        }
+        nc = (int)total;
+        __syncthreads();
+      }
+    }
+    if (nc > 0) {
+      // more than 64 new nodes: sorted runs of 64 and binary searches; else plain counts
+      const bool runs = nc > 64;
+      if (runs) {
+        for (int c0 = 64 * (tid >> 6); c0 < nc; c0 += kAnnsSearchThreads)
+          wave_sort64(cs, ci, c0, nc);
+        __syncthreads();
+      }
       const float* S = pS[cur];
       const int32_t* I = pI[cur];
       float* S2 = pS[cur ^ 1];
@@ -568,9 +622,10 @@ __global__ __launch_bounds__(kAnnsSearchThreads) void k_anns_search(AnnsArgs a) 
           }
           rank = lo;
         }
-        // the new nodes better than it: sorted runs of 64 (its own run: its place)
-        rank += count_better_runs(cs, ci, nc, 64, e < psize ? -1 : (e - psize) & ~63, sv, id) +
-                (e < psize ? 0 : (e - psize) & 63);
+        // the new nodes better than it (sorted runs of 64: its own run gives its place)
+        rank += !runs ? count_better_all(cs, ci, nc, sv, id)
+                      : count_better_runs(cs, ci, nc, 64, e < psize ? -1 : (e - psize) & ~63,
+                                          sv, id) + (e < psize ? 0 : (e - psize) & 63);
         if (rank < a.ef) {
           S2[rank] = sv;
           I2[rank] = iv;
@@ -579,7 +634,7 @@ __global__ __launch_bounds__(kAnnsSearchThreads) void k_anns_search(AnnsArgs a) 
       cur ^= 1;
       psize = min(a.ef, psize + nc);
     }
-    if (tid == 0) ctr[kCtrVisited] += nc;
+    if (tid == 0) ctr[kCtrVisited] += nv;
     __syncthreads();
     if (rounds >= a.max_rounds) break;
     // ---- the W best unexpanded pool entries, in pool order
