@@ -21,6 +21,7 @@
 // cluster-contiguous permutation of K and V (each row read once, written once), so that
 // decode reads a retrieved cluster as one contiguous run of rows.
 #include <algorithm>
+#include <cfloat>
 
 #include "wave_common.h"
 #include "wave_kernels.h"
@@ -192,8 +193,9 @@ __global__ __launch_bounds__(256) void k_assign(BuildArgs a, const uint16_t* __r
 // Segment-resident variant (k_seg <= kA2MaxK): a 512-thread workgroup stages all centroids
 // of its segment in LDS once (k_seg x 272 B) and each wave loops over 64-point blocks of its
 // share of the segment's points. Per 32-centroid row block the argmax takes a max3 tree of
-// the 16 scores a lane holds and looks for the index only when that beats its running best
-// (rows in increasing id order, so a strict '>' still keeps the lowest id on ties).
+// the 16 scores a lane holds, each carrying its row in its low mantissa bits, and keeps it
+// when it beats the running best (rows in increasing id order, so a strict '>' keeps the
+// earlier block on equal keys).
 constexpr int kA2Threads = 512;
 constexpr int kA2Waves = kA2Threads / 64;
 constexpr int kA2MaxK = 512;
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
   // segment are scored but never written)
   const int64_t nblk = (n + 63) / 64;
   const int64_t b0 = nblk * split / nsplit, b1 = nblk * (split + 1) / nsplit;
-  auto load_block = [&](int64_t blk, bf16x8 (&bq)[2][8], float (&inv)[2]) {
+  auto load_block = [&](int64_t blk, bf16x8 (&bq)[2][8]) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int64_t p = min(blk * 64 + nb * 32 + col, n - 1);
@@ -222,15 +224,13 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         bq[nb][kk] = __builtin_bit_cast(bf16x8, ld16_stream(row + kk * 16 + half * 8));
-      inv[nb] = a.inv_norm[(size_t)bh * a.L0 + sg.lo + p];
     }
   };
   // the wave's first key block is loaded before the centroids are staged, so that both
   // take one memory round trip
   int64_t blk = b0 + wave;
   bf16x8 bq[2][8];
-  float inv[2];
-  if (blk < b1) load_block(blk, bq, inv);
+  if (blk < b1) load_block(blk, bq);
   // the centroids: 16-byte chunks, up to 16 per thread with all their loads in flight
   // together (rows clamp to the last valid one, padding rows are written as zero)
   for (int q0 = 0; q0 < kpad * 16; q0 += 16 * kA2Threads) {
@@ -256,18 +256,14 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
     const unsigned char* r = s_mu2 + min(m0 + col, kpad - 1) * kAsgLdsStride + half * 16;
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(r + kk * 32));
   };
-  // The products k . mu of a point with unit centroids lie within +-||k|| (1 + 2^-8 for bf16
-  // rounding of mu), so starting the accumulation from 2 ||k|| makes every score a positive
-  // float whose bit pattern orders like its value. The low 4 bits of each score are then
-  // replaced by 15 - i for accumulator element i (rows ascend with i), so one unsigned max
-  // over a point's scores picks its best row and, among scores equal above those bits, the
-  // lowest row. The winner's cosine is thereby within 2^-17 of the best one (16 ulps of a
-  // value below 4 ||k||); only which of such near-equal centroids wins can change.
-  auto score_block = [&](int64_t blk, const bf16x8 (&bq)[2][8], const float (&inv)[2]) {
-    float bias[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) bias[nb] = inv[nb] > 0.f ? 2.f / inv[nb] : 1.f;
-    uint32_t best[2] = {0u, 0u};
+  // The low 4 mantissa bits of each score are replaced by 15 - i for accumulator element i
+  // (rows ascend with i), and a float max over a point's scores then picks its best row.
+  // Whatever the sign of the best score, the replaced bits move a score by under 16 ulps, so
+  // the winner's score is within 16 ulps of the best one (a relative 2^-19, far below the
+  // bf16 rounding of the operands); only which of such near-equal centroids wins can change
+  // (among exactly equal positive scores, the lowest row).
+  auto score_block = [&](int64_t blk, const bf16x8 (&bq)[2][8]) {
+    float best[2] = {kNegInf, kNegInf};
     int bblk[2] = {0, 0};
     bf16x8 am[8];
 #pragma unroll
@@ -275,40 +271,39 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
     // products of row block m0; each A operand is refilled with the next row block's once
     // its products are issued
     auto products = [&](int m0, floatx16 (&acc)[2]) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[nb][i] = bias[nb];
+      const floatx16 zero = {};
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[kk], bq[nb][kk], acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[kk], bq[nb][kk],
+                                                            kk == 0 ? zero : acc[nb], 0, 0, 0);
         am[kk] = a_row(m0 + 32, kk);
       }
     };
     // best row of row block m0 per point; element i holds row m0 + 8 * (i / 4) + 4 * half +
-    // i % 4, and in the last block rows >= nvalid get key 0, below every biased score
+    // i % 4, and in the last block rows >= nvalid get -FLT_MAX, below every score
     auto pick = [&](int m0, const floatx16 (&acc)[2], bool last) {
       const int lim = nvalid - m0 - 4 * half;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        uint32_t key[16];
+        float key[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) key[i] = (__float_as_uint(acc[nb][i]) & ~15u) | (15u - i);
+        for (int i = 0; i < 16; ++i)
+          key[i] = __uint_as_float((__float_as_uint(acc[nb][i]) & ~15u) | (15u - i));
         if (last) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (8 * (i >> 2) + (i & 3) >= lim) key[i] = 0u;
+            if (8 * (i >> 2) + (i & 3) >= lim) key[i] = -FLT_MAX;
         }
-        uint32_t bm = max(max(key[0], key[1]), key[2]);
-        bm = max(max(bm, key[3]), key[4]);
-        bm = max(max(bm, key[5]), key[6]);
-        bm = max(max(bm, key[7]), key[8]);
-        bm = max(max(bm, key[9]), key[10]);
-        bm = max(max(bm, key[11]), key[12]);
-        bm = max(max(bm, key[13]), key[14]);
-        bm = max(bm, key[15]);
+        float bm = fmaxf(fmaxf(key[0], key[1]), key[2]);
+        bm = fmaxf(fmaxf(bm, key[3]), key[4]);
+        bm = fmaxf(fmaxf(bm, key[5]), key[6]);
+        bm = fmaxf(fmaxf(bm, key[7]), key[8]);
+        bm = fmaxf(fmaxf(bm, key[9]), key[10]);
+        bm = fmaxf(fmaxf(bm, key[11]), key[12]);
+        bm = fmaxf(fmaxf(bm, key[13]), key[14]);
+        bm = fmaxf(bm, key[15]);
         // strict: an equal key in a later block has a higher row
         if (bm > best[nb]) {
           best[nb] = bm;
@@ -343,10 +338,11 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
     // the two half-waves hold disjoint centroid rows of the same points
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int i = 15 - (int)(best[nb] & 15u);
-      const uint32_t tv = best[nb] & ~15u;
+      const uint32_t bb = __float_as_uint(best[nb]);
+      const int i = 15 - (int)(bb & 15u);
+      const float tv = __uint_as_float(bb & ~15u);
       const int idx = bblk[nb] + 8 * (i >> 2) + 4 * half + (i & 3);
-      const uint32_t ov = __shfl_xor(tv, 32);
+      const float ov = __shfl_xor(tv, 32);
       const int oi = __shfl_xor(idx, 32);
       const int pick = (ov > tv || (ov == tv && oi < idx)) ? oi : idx;
       const int64_t p = blk * 64 + nb * 32 + col;
@@ -365,9 +361,9 @@ __global__ __launch_bounds__(kA2Threads) void k_assign_seg(BuildArgs a, const ui
   };
   while (blk < b1) {
     const int64_t nxt = claim();
-    score_block(blk, bq, inv);
+    score_block(blk, bq);
     blk = nxt;
-    if (blk < b1) load_block(blk, bq, inv);
+    if (blk < b1) load_block(blk, bq);
   }
 }
 
