@@ -68,7 +68,7 @@ def parse():
                     help="decode calls per step (default: the workload's)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-decode-steps", type=int, default=16)
+    ap.add_argument("--cpu-decode-steps", type=int, default=64)
     ap.add_argument("--extend", default="llama128k",
                     help="time the extension of this workload's index by one segment of new "
                          "tokens against a full build ('none': skip)")
@@ -1061,13 +1061,13 @@ def sweep_leg(name, n_steps, n_warm, cluster_sizes=(8, 16, 32),
             "reference": "dense decode over all L rows (layer 0)", "grid": grid}
 
 
-def cpu_baseline(w, x, n_dec_steps=16):
+def cpu_baseline(w, x, n_dec_steps=64):
     """The oracle, untuned, on the host cores: with one thread and with all of them
     (os.sched_getaffinity; BLAS threads limited by threadpoolctl, the oracle's own loops
     being single-threaded).
-      * the 128K layer (w, inputs x): build = two segments (KV head 0 segment 0, KV head 1
-        the middle segment) through all passes, extrapolated to the layer by the exact work
-        ratio (segments x KV heads);
+      * the 128K layer (w, inputs x): build = 24 segments (sample i: KV head i mod H, segment
+        2 i + i // H mod the segments, three distinct segments per KV head) through all passes,
+        extrapolated to the layer by the exact work ratio (segments x KV heads / 24);
         decode = n_dec_steps steps of KV head 0 (its index built by the oracle with one pass,
         untimed: decode work does not depend on the pass count), extrapolated to all KV heads;
       * the 4K layer ('tiny'): the whole build (all heads, all passes) and all its decode
@@ -1082,7 +1082,8 @@ def cpu_baseline(w, x, n_dec_steps=16):
     cores = len(os.sched_getaffinity(0))
     g = 0
     segs = wo.segment_ranges(w.context, w.segment_size, w.n_sink, w.n_recent)
-    picks = [(0, 0), (1, len(segs) // 2)]
+    H = w.n_kv_heads
+    picks = [(i % H, (2 * i + i // H) % len(segs)) for i in range(3 * H)]
     Ks = [wo.bf16_to_f64(x.k[0, gg, segs[ss][0]:segs[ss][1]]) for gg, ss in picks]
     n_pts = sum(K.shape[0] for K in Ks)
     print("[bench] cpu baseline: oracle index of KV head 0 (decode input, untimed)",
@@ -1136,12 +1137,12 @@ def cpu_baseline(w, x, n_dec_steps=16):
             "kind": "oracle",
             "sample": (f"128K layer: decode {n_dec} steps of KV head 0 (index by the oracle, 1 "
                        f"pass, untimed), extrapolated x{w.batch * w.n_kv_heads} to every KV "
-                       f"head; build two segments ({n_pts} tokens) x {w.n_iters} passes, "
-                       f"extrapolated x{len(segs) * w.batch * w.n_kv_heads / 2:g} (segments x "
-                       f"KV heads / 2); 4K layer: whole build and all {tw.steps} decode steps, "
-                       f"measured"),
+                       f"head; build {len(picks)} segments ({n_pts} tokens) x {w.n_iters} "
+                       f"passes, extrapolated x{len(segs) * w.batch * w.n_kv_heads / len(picks):g} "
+                       f"(segments x KV heads / {len(picks)}); 4K layer: whole build and all "
+                       f"{tw.steps} decode steps, measured"),
             "extrapolated": {"llama128k_decode": w.batch * w.n_kv_heads,
-                             "llama128k_index_build": len(segs) * w.batch * w.n_kv_heads / 2},
+                             "llama128k_index_build": len(segs) * w.batch * w.n_kv_heads / len(picks)},
             "one_thread": runs[1], "all_cores": allc}
 
 if __name__ == "__main__":
