@@ -648,7 +648,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_score(DecodeArgs a) {
     }
     if (kg == 0) {
       const float mean = sum * gmean;
-      const bool ok = j < a.C && n[u] > 0;
+      const bool ok = (j < a.C) & (n[u] > 0);
       if (ok) {
         mn = fminf(mn, mean);
         mx = fmaxf(mx, mean);
@@ -1359,7 +1359,7 @@ __device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinSha
       for (int k = 0; k < kLocalV; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          m |= (k < nk && bin_of(k, e) == bstar) ? 1u << (4 * k + e) : 0u;
+          m |= ((k < nk) & (bin_of(k, e) == bstar)) ? 1u << (4 * k + e) : 0u;
       while (m) {
         const int q = __builtin_ctz(m);
         m &= m - 1u;
@@ -1380,7 +1380,8 @@ __device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinSha
         uint32_t rank = 0;
         for (uint32_t c = 0; c < cnt; ++c) {
           const float cv = sh.ck[c];
-          rank += (cv > mv || (cv == mv && sh.ci[c] < mj)) ? 1u : 0u;
+          const int cj = sh.ci[c];
+          rank += ((cv > mv) | ((cv == mv) & (cj < mj))) ? 1u : 0u;
         }
         if (rank == need2 - 1) {
           sh.tkey = mv;
@@ -1414,7 +1415,9 @@ __device__ __forceinline__ void select_local(const DecodeArgs& a, int bh, FinSha
     }
   }
   __syncthreads();
-  local_bitmap(v, nk, sh, [&](float x, int j) { return x > Tkey || (x == Tkey && j <= Tid); });
+  // (the comparisons combined bitwise, here and in the exact rank above: a short-circuit form
+  // compiles to exec-mask branches per score)
+  local_bitmap(v, nk, sh, [&](float x, int j) { return (x > Tkey) | ((x == Tkey) & (j <= Tid)); });
   __syncthreads();
   publish_selection(a, bh, sh);
 }
@@ -1599,8 +1602,11 @@ __device__ __forceinline__ void estimate_mfma(const DecodeArgs& a, int bh, int e
 // then nSt per (b, kv-head) attend exactly to 128 steady tokens each, into partial slot
 // nEW + s; then nEW = nS per (b, kv-head) fold the centroid estimate of a chunk of 128
 // clusters each (weight n_j, logit s_j, value sum V_j) into partial slot e. The value-sum
-// stream of the estimate does not depend on the selection and runs beside it.
-template <int G>
+// stream of the estimate does not depend on the selection and runs beside it. HIST: the
+// selection of heads of more than kLocalSelectMax clusters (after the histogram kernel);
+// each instance holds only its own selection path, so that neither path's code (and its
+// placement) depends on the other's.
+template <int G, bool HIST>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 1))) void k_dec_gather(DecodeArgs a) {
   const int BH = a.B * a.Hkv, tid = threadIdx.x;
   // (roles use different workgroups: one LDS block serves the selection, an estimate
@@ -1661,7 +1667,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(G <
   // estimate and steady waves that share their SIMDs
   __builtin_amdgcn_s_setprio(3);
   FinShared& sh = lds.f;
-  if (!a.hist_kernel) {
+  if constexpr (!HIST) {
     select_local(a, bh, sh);
     return;
   }
@@ -2433,8 +2439,9 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s, Tracer* tr
     e = launch(tr, k_dec_hist, dim3(a.nH, BH), dim3(kDecThreads), 0, s, a);
     if (e != hipSuccess) return e;
   }
-  e = launch(tr, k_dec_gather<G>, dim3((a.nH + a.nEW + a.nSt) * BH), dim3(kDecThreads), 0, s,
-             a);
+  const dim3 ggrid((a.nH + a.nEW + a.nSt) * BH);
+  e = a.hist_kernel ? launch(tr, k_dec_gather<G, true>, ggrid, dim3(kDecThreads), 0, s, a)
+                    : launch(tr, k_dec_gather<G, false>, ggrid, dim3(kDecThreads), 0, s, a);
   if (e != hipSuccess) return e;
   if (a.tier) {
     e = a.nB * BH <= 3 * kCUs
