@@ -842,14 +842,35 @@ __device__ int nth_id_with_score(LK tk, LI ti, uint32_t n, float v, uint32_t nee
 }
 
 // (Tkey, Tid): the need-th pair (score descending, id ascending) among the n listed
-// clusters of the cut bin (1 <= need < n). Value-range histograms narrow the range until
-// the bin holding the pair has at most kCand scores, which are then ranked exactly.
-// tk(k), ti(k): the k-th listed score and id (global memory or LDS).
+// clusters of the cut bin (1 <= need < n). At most kCand of them are ranked exactly at once;
+// more, and value-range histograms narrow the range until the bin holding the pair has at
+// most kCand scores, which are then ranked exactly. tk(k), ti(k): the k-th listed score and
+// id (global memory or LDS).
 template <typename LK, typename LI>
 __device__ void cut_pair(LK tk, LI ti, uint32_t n, uint32_t need, FinShared& sh, float& Tkey,
                          int& Tid) {
   constexpr int NT = kDecThreads, BPT = kNarrowBins / NT;
   const int tid = threadIdx.x;
+  if (n <= (uint32_t)kCand) {
+    if (tid < (int)n) {
+      const float mv = tk(tid);
+      const int mj = ti(tid);
+      uint32_t rank = 0;
+      for (uint32_t c = 0; c < n; ++c) {
+        const float cv = tk(c);
+        rank += (cv > mv || (cv == mv && ti(c) < mj)) ? 1u : 0u;
+      }
+      if (rank == need - 1) {
+        sh.tkey = mv;
+        sh.tid = mj;
+      }
+    }
+    __syncthreads();
+    Tkey = sh.tkey;
+    Tid = sh.tid;
+    __syncthreads();
+    return;
+  }
   Red3 r{kPosInf, kNegInf, 0u};
   for (uint32_t k = tid; k < n; k += NT) {
     const float v = tk(k);
