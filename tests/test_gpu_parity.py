@@ -651,6 +651,45 @@ def test_crowded_cut_bin_is_ranked_exactly(C, skew):
         tl.oracle_decode_check(layer, idx, q[0], layer.L0 + 1, n_r, out, lse, sel)
 
 
+def test_assignment_with_negative_best_scores():
+    """Points whose dot product with every centroid of their segment is negative still get
+    the oracle's assignment (ties within 1e-4): the first pass's centroids are the seeds, the
+    unit keys at local positions j floor(n / kseg), all near +8 e0, while the keys halfway
+    between seed positions lie near -8 e0, so that their best score is about -0.65 (66 such
+    points); the argmax compares fp32 scores of either sign. Checked after one pass and after
+    three."""
+    rng = np.random.default_rng(1907)
+    d, L0, S, kseg, n_sink, n_recent = 128, 1100, 512, 32, 4, 16
+    L = L0 + 1
+    base = np.zeros(d)
+    base[0] = 8.0
+    kf = base + 0.5 * rng.standard_normal((L, d))
+    neg = []
+    for lo, hi in wo.segment_ranges(L0, S, n_sink, n_recent):
+        step = (hi - lo) // kseg
+        if step >= 2:
+            neg.extend(range(lo + step // 2, hi, step))
+    kf[neg] = -base + 0.5 * rng.standard_normal((len(neg), d))
+    layer = tl.Layer(tl.f32_bits(kf[None, None]), tl.f32_bits(rng.standard_normal((1, 1, L, d))),
+                     L0, S, kseg, 3, n_sink, n_recent, 2)
+    K = wo.bf16_to_f64(layer.k_np)
+    for T in (1, 3):
+        say(f"[negative scores] n_iters={T}")
+        idx = layer.build(T=T)
+        mu = tl.to_np16(idx.last_centroids)
+        labels = idx.labels.cpu().numpy()
+        n_negative = 0
+        for s, (lo, hi) in enumerate(tl.segment_ranges(layer)):
+            Xhat = wo.normalise_rows(K[0, 0, lo:hi])
+            mus = mu[0, 0, s * kseg:(s + 1) * kseg]
+            nv = tl.n_valid(kseg, hi - lo)
+            best = (Xhat @ wo.bf16_to_f64(mus)[:nv].T).max(axis=1)
+            n_negative += int((best < 0).sum())
+            tl.check_assignment(Xhat, mus, nv, labels[0, 0, lo:hi] - s * kseg)
+        if T == 1:
+            assert n_negative >= 60, n_negative  # (the case this test is for)
+
+
 def test_traced_calls_time_each_kernel_and_match_the_plain_calls(tiny):
     """The traced variants give bit-identical results and time every kernel with one
     start / end event pair (build: norms, seeds, passes x (assign, sort) + (passes - 1) x
