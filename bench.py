@@ -259,6 +259,18 @@ def main():
     roof_call = roof("decode call", "hbm", call_bytes, call_ms,
                      {"median_launch_us": round(med(call_ms) * 1e3, 2)})
     roof_call.pop("traffic")
+    # The call is a chain of dependent kernels: at 128K its bytes take a few microseconds at
+    # the peak while the chain's steps (kernel launches, memory round trips, the one-workgroup
+    # selection) take most of the call. Each kernel's median traced time, what remains of the
+    # untraced call between them, and the call's bytes at the HBM peak.
+    chain = {"k_dec_score": med(score_ms) * 1e3}
+    if has_hist:
+        chain["k_dec_hist"] = med(hist_ms) * 1e3
+    chain.update({"k_dec_gather": med(gather_ms) * 1e3, "k_dec_retrieve": med(retrieve_ms) * 1e3})
+    roof_call["latency_chain_us"] = {
+        **{k: round(v, 2) for k, v in chain.items()},
+        "between_kernels": round(med(call_ms) * 1e3 - sum(chain.values()), 2),
+        "bytes_at_peak": round(call_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}
 
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s at 128K/1M ctx; index-build tok/s",
