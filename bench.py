@@ -333,6 +333,15 @@ def main():
     if args.sweep != "none":
         res["sweep"] = sweep_leg(args.sweep, 3, 1)
         torch.cuda.empty_cache()
+    if "stack_b8" in res and res["stack_b8"].get("dense_hbm_GBps"):
+        # a measured streaming reference: the library's dense flash-decode over the batch-8
+        # stack (every K and V row read once, in order)
+        ref = res["stack_b8"]["dense_hbm_GBps"]
+        res["decode_frac_of_stream"] = {
+            "reference": "dense flash-decode of the batch-8 stack", "reference_GBps": ref,
+            w.name: round(res["decode_hbm_GBps"] / ref, 4),
+            **{res[k]["workload"]: round(res[k]["decode_hbm_GBps"] / ref, 4)
+               for k in ("stack_b8", "stack_1m") if k in res}}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_decode_steps)
     print(json.dumps(res), flush=True)
