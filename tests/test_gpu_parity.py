@@ -589,11 +589,12 @@ def host_index_layer(rng, C, n_distinct, Hq=4, n_sink=3, n_recent=9, steps=1, p_
     return layer, idx, q, size
 
 
-@pytest.mark.parametrize("C", [3000, 8192, 12000, 65536])
+@pytest.mark.parametrize("C", [3000, 8192, 8193, 10241, 12000, 65536])
 def test_exact_score_ties_select_lowest_ids(C):
     """Exactly tied group scores are broken towards the lower cluster id, both where one
     workgroup selects a whole head from registers (C <= 8192) and where several workgroups
-    per head list candidates and the last ranks them (larger C); the budgets put the cut
+    per head list candidates and the last ranks them (larger C, down to 8193, where the last
+    of 65 chunks holds one cluster, and 10241, a ragged last chunk); the budgets put the cut
     inside a block of ties thousands of clusters wide, and past the number of non-empty
     clusters."""
     rng = np.random.default_rng(C)
@@ -611,7 +612,8 @@ def test_exact_score_ties_select_lowest_ids(C):
         tl.oracle_decode_check(layer, idx, q[0], layer.L0 + 1, n_r, out, lse, sel)
 
 
-@pytest.mark.parametrize("C,skew", [(6000, 0.0), (8192, 0.93), (30000, 0.0), (65536, 0.93)])
+@pytest.mark.parametrize("C,skew", [(6000, 0.0), (8192, 0.93), (8193, 0.93), (30000, 0.0),
+                                    (65536, 0.93)])
 def test_crowded_cut_bin_is_ranked_exactly(C, skew):
     """Thousands of distinct group scores in the cut bin, so the cut pair is found after one
     to three narrowing rounds (C <= 8192: from one workgroup's registers; larger C: from the
