@@ -401,34 +401,92 @@ __device__ __forceinline__ uint32_t scan1024_excl(uint32_t x, uint32_t* s_tmp, u
   return v - x + before;
 }
 
+// Wave w ranks the points of its contiguous chunk [w cs, (w + 1) cs) of the segment, 64 at a
+// time in position order: lanes holding the same label find each other by ballots over the
+// label bits, and the wave's running count of each label (a row of s_cnt, read by every lane
+// and then advanced by the label's first lane: one wave's LDS operations complete in order)
+// gives each point its rank among the chunk's points of that label. The counts then become,
+// label by label, the number of points of that label in earlier chunks, and the scan of the
+// label totals gives each label's first slot, so that a point's slot is its label's first
+// slot + its chunk's base + its rank: the stable order by (label, position), with three
+// workgroup barriers besides the scan's.
+constexpr int kSortBlocks = kMaxSeg / kSortWaves / 64;  // 64-point blocks per chunk, at most
+
 __global__ __launch_bounds__(kSortThreads) void k_sort(BuildArgs a) {
   const int s = a.seg0 + blockIdx.x, bh = blockIdx.y;
   const Seg sg = seg_range(a, s);
   const int n = (int)(sg.hi - sg.lo);
   const int K = a.kseg;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ uint16_t s_lab[kMaxSeg];
-  __shared__ uint16_t s_hist[kSortWaves][kMaxKseg];
+  __shared__ uint16_t s_cnt[kSortWaves][kMaxKseg];  // per chunk: running count, then base
   __shared__ uint32_t s_start[kMaxKseg + 1];
-  __shared__ uint32_t s_run[kMaxKseg];
   __shared__ uint32_t s_tmp[32];
 
   const int32_t* lab = a.lab + (size_t)bh * a.L0 + sg.lo;
-  for (int i = tid; i < n; i += kSortThreads) s_lab[i] = (uint16_t)lab[i];
-  for (int j = tid; j < K; j += kSortThreads) {
-    s_run[j] = 0u;
-    s_start[j] = 0u;
+  {
+    // every label load issued before the first LDS write (one round trip, not one per
+    // 1024 labels)
+    constexpr int kL = kMaxSeg / kSortThreads;
+    uint32_t lv[kL];
+#pragma unroll
+    for (int k = 0; k < kL; ++k)
+      if (k * kSortThreads < n) lv[k] = (uint32_t)lab[min(k * kSortThreads + tid, n - 1)];
+#pragma unroll
+    for (int k = 0; k < kL; ++k) {
+      const int i = k * kSortThreads + tid;
+      if (k * kSortThreads < n && i < n) s_lab[i] = (uint16_t)lv[k];
+    }
   }
-  for (int q = tid; q < kSortWaves * K; q += kSortThreads) s_hist[q / K][q % K] = 0;
+  {
+    uint32_t* z = reinterpret_cast<uint32_t*>(&s_cnt[0][0]);
+    for (int q = tid; q < kSortWaves * kMaxKseg / 2; q += kSortThreads) z[q] = 0u;
+  }
   __syncthreads();
-  for (int i = tid; i < n; i += kSortThreads) atomicAdd(&s_start[s_lab[i]], 1u);
+  // ---- ranks within the wave's chunk (no workgroup barrier)
+  const int cs = (n + 64 * kSortWaves - 1) / (64 * kSortWaves) * 64;  // chunk length
+  const int nblk = cs / 64;
+  const int nbits = 32 - __clz(max(K - 1, 1));
+  uint32_t packed[kSortBlocks];  // label | rank in the chunk << 16 (all ones: no point)
+  uint16_t* cnt = &s_cnt[wave][0];
+#pragma unroll
+  for (int k = 0; k < kSortBlocks; ++k) {
+    packed[k] = 0xffffffffu;
+    if (k < nblk) {
+      const int i = wave * cs + 64 * k + lane;
+      const bool ok = i < n;
+      const uint32_t l = ok ? s_lab[i] : 0u;
+      uint64_t peers = __ballot(ok);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const uint64_t bb = __ballot(ok && ((l >> bit) & 1u));
+        peers &= ((l >> bit) & 1u) ? bb : ~bb;
+      }
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+      const uint32_t prev = ok ? cnt[l] : 0u;
+      if (ok && rank == 0) cnt[l] = (uint16_t)(prev + (uint32_t)__popcll(peers));
+      if (ok) packed[k] = l | ((prev + rank) << 16);
+    }
+    __builtin_amdgcn_wave_barrier();  // (the next block's reads stay after this write)
+  }
   __syncthreads();
-  // exclusive scan of the counts; thread t owns clusters [t*per, (t+1)*per)
+  // ---- per label: counts -> bases of the chunks, totals -> first slots; thread t owns
+  // labels [t per, (t + 1) per)
   {
     const int per = (K + kSortThreads - 1) / kSortThreads;
     const int j0 = min(K, tid * per), j1 = min(K, j0 + per);
     uint32_t loc = 0;
-    for (int j = j0; j < j1; ++j) loc += s_start[j];
+    for (int j = j0; j < j1; ++j) {
+      uint32_t run = 0;
+#pragma unroll
+      for (int w = 0; w < kSortWaves; ++w) {
+        const uint32_t c = s_cnt[w][j];
+        s_cnt[w][j] = (uint16_t)run;
+        run += c;
+      }
+      s_start[j] = run;
+      loc += run;
+    }
     uint32_t total;
     uint32_t run = scan1024_excl(loc, s_tmp, total);
     for (int j = j0; j < j1; ++j) {
@@ -441,35 +499,13 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(BuildArgs a) {
   __syncthreads();
   int32_t* cst = a.cstart + ((size_t)bh * a.nseg + s) * (K + 1);
   for (int j = tid; j <= K; j += kSortThreads) cst[j] = (int32_t)s_start[j];
-
   int32_t* order = a.order + (size_t)bh * a.L0 + sg.lo;
-  const int nbits = 32 - __clz(max(K - 1, 1));
-  for (int r0 = 0; r0 < n; r0 += kSortThreads) {
-    const int i = r0 + tid;
-    const bool ok = i < n;
-    const uint32_t l = ok ? s_lab[i] : 0u;
-    // lanes of this wave holding the same label (ballot over the label bits)
-    uint64_t peers = __ballot(ok);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const uint64_t bb = __ballot(ok && ((l >> bit) & 1u));
-      peers &= ((l >> bit) & 1u) ? bb : ~bb;
+#pragma unroll
+  for (int k = 0; k < kSortBlocks; ++k) {
+    if (packed[k] != 0xffffffffu) {
+      const uint32_t l = packed[k] & 0xffffu;
+      order[s_start[l] + s_cnt[wave][l] + (packed[k] >> 16)] = wave * cs + 64 * k + lane;
     }
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
-    const uint32_t cnt = (uint32_t)__popcll(peers);
-    if (ok && rank == 0) s_hist[wave][l] = (uint16_t)cnt;
-    __syncthreads();
-    if (ok) {
-      uint32_t pos = s_start[l] + s_run[l] + rank;
-      for (int w = 0; w < wave; ++w) pos += s_hist[w][l];
-      order[pos] = i;
-    }
-    __syncthreads();
-    if (ok && rank == 0) {
-      atomicAdd(&s_run[l], cnt);
-      s_hist[wave][l] = 0;
-    }
-    __syncthreads();
   }
 }
 
