@@ -222,6 +222,11 @@ CASES = {
     # 32 (b, kv-head) x 28 retrieve workgroups: more than three per CU, so the retrieve
     # kernel merges its share of the earlier partials element by element
     "wide_retrieve_grid": (dict(B=4, H=8, Hq=32, L0=3000, S=1024, kseg=64, steps=1), (150,)),
+    # the largest segment and cluster count the library takes (S = 16384, k_seg = 2048): a
+    # first segment of 16381 points (every 64-point block of the sort's per-wave chunks),
+    # a ragged second one of 9003
+    "max_segment_and_clusters": (dict(H=1, Hq=4, L0=25404, S=16384, kseg=2048, T=2, steps=1),
+                                 (40, 2048)),
 }
 
 
