@@ -211,6 +211,11 @@ CASES = {
     # name: (ragged_layer kwargs, decode budgets)
     "gqa4_ragged": (dict(), (0, 5, 40)),
     "mha_g1": (dict(H=2, Hq=2), (3,)),
+    # every other group size the kernels are instantiated for, up to the largest (G = 8)
+    "gqa3": (dict(H=2, Hq=6), (5,)),
+    "gqa5_batch2": (dict(B=2, H=1, Hq=5), (0, 9)),
+    "gqa6": (dict(H=2, Hq=12), (40,)),
+    "gqa8": (dict(H=2, Hq=16), (0, 5, 40)),
     "qwen_g7_batch2": (dict(B=2, H=2, Hq=14, L0=600, S=200, kseg=13), (4, 26)),
     "short_last_segment": (dict(L0=530, S=256, kseg=40, n_recent=3), (7,)),
     "no_steady_zone": (dict(n_sink=0, n_recent=0, steps=1), (2,)),

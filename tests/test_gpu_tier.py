@@ -169,13 +169,16 @@ TIER_EDGE = {
     "mha": (1, 4, 4, 1200, 3, 256, 24, 4, 20, 7, 12),
     "no_steady_zone": (1, 2, 8, 1024, 3, 256, 16, 0, 0, 6, 8),
     "one_slot": (1, 2, 8, 900, 4, 300, 20, 2, 11, 5, 1),
+    "g5": (1, 1, 5, 800, 3, 256, 20, 2, 9, 6, 6),
+    "g8": (1, 2, 16, 1100, 3, 256, 24, 3, 17, 8, 10),
 }
 
 
 @pytest.mark.parametrize("name", sorted(TIER_EDGE))
 def test_tier_shapes_and_edge_cases(name):
     """Other shapes through the tier: seven query heads per KV head at batch 2 with a partly
-    filled last block, MHA, no steady zone, a single slot; every step bit for bit equal to the
+    filled last block, MHA, five and eight query heads per KV head, no steady zone, a single
+    slot; every step bit for bit equal to the
     resident decode, the cache's rows checked after every step."""
     import zlib
     B, H, Hq, L0, steps, S, kseg, ns, nr, n_r, n_slots = TIER_EDGE[name]
