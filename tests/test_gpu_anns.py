@@ -199,6 +199,8 @@ EDGE = {
     "wide_rounds": (1, 4, 1, 3000, 2, 4, 64, 100, dict(M=64, R=32, E=64, ef=1024, W=64, k=512)),
     "mha_batch2": (2, 4, 4, 900, 2, 4, 32, 20, dict(M=24, R=20, E=6, ef=80, W=5, k=50)),
     "g7": (1, 14, 2, 900, 2, 4, 32, 10, dict(M=16, R=16, E=8, ef=64, W=8, k=32)),
+    "g3": (1, 6, 2, 800, 2, 4, 32, 12, dict(M=16, R=16, E=8, ef=64, W=8, k=32)),
+    "g8": (1, 16, 2, 900, 2, 4, 32, 10, dict(M=16, R=16, E=8, ef=64, W=8, k=32)),
     "duplicate_keys": (1, 8, 2, 600, 2, 4, 16, 16, dict(M=16, R=16, E=8, ef=64, W=8, k=32)),
 }
 
